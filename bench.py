@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward on one MI355X.
+
+Headline: the chunked forward on the long-context workload (B=1, T=8192, H=16 q/k heads,
+HV=32 value heads, K=V=128, bf16 q/k/v/beta, fp32 log2 gates clamped at -5, no initial
+state, no final state): tokens/s over K timed steps with inputs resident in HBM, plus
+the fraction of bf16 matrix-core peak its flops represent. A step is one call of
+kda_chunk_fwd (scheduler-free dense mode: Stage 1+2 kernel, then the Stage 3+4 scan).
+
+Also reported on the same JSON line:
+  * roofline  -- the dominant kernel (the one with the largest average duration, timed
+                 live with HIP events recorded by kda_chunk_fwd_timed on the library's
+                 stream) against HBM peak, with that kernel's algorithmic bytes;
+  * path      -- the whole step against the HBM floor of the workload's own inputs and
+                 outputs (336.1 MB), and the matrix-core fractions;
+  * decode    -- the per-token recurrent forward on 4096 sequences x 32 heads (one token
+                 each, fp32 states in and out): state GB/s and fraction of HBM peak;
+  * cpu_baseline -- the fp64 CPU oracle on the full headline workload, host threads.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak
+
+
+def hip_runtime():
+    """The HIP runtime already loaded in this process (torch's), for event timing."""
+    for line in open("/proc/self/maps"):
+        path = line.split()[-1]
+        if "libamdhip64" in path and os.path.exists(path):
+            lib = ctypes.CDLL(path)
+            break
+    else:
+        lib = ctypes.CDLL("libamdhip64.so.7")
+    vp = ctypes.c_void_p
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+    lib.hipEventRecord.argtypes = [vp, vp]
+    lib.hipEventSynchronize.argtypes = [vp]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+    lib.hipEventDestroy.argtypes = [vp]
+    return lib
+
+
+class Events:
+    def __init__(self, hip, n):
+        self.hip = hip
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev[i] = e
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) == 0
+        return float(out.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def record_bytes(K, V, elem):
+    """Algorithmic bytes of one Stage 2 record (see the workspace layout in the library):
+    w, qg(hi, lo), kg^T(hi, lo), Aqk(hi, lo) in the operand type, u and 2^G in fp32."""
+    ns = 2 if elem == 2 else 1
+    return 64 * K * elem + ns * (2 * 64 * K * elem + 64 * 64 * elem) + 64 * V * 4 + K * 4
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("kda_chunk.hip", "kda_device.h"):
+        h.update(open(os.path.join(ROOT, "gated_delta_rule_64_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, when it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_c3.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("bytes_per_launch", {}).get(kernel_key)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(sequences and heads shard across GPUs with no communication; run one "
+              "process per GPU on its own share)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_64_amd import _lib
+    if not os.path.exists(_lib.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    import gated_delta_rule_64_amd as kda
+    from gated_delta_rule_64_amd import inputs
+
+    lib = kda.load_library()
+    hip = hip_runtime()
+    vp = ctypes.c_void_p
+    lib.kda_chunk_fwd_timed.restype = ctypes.c_int
+    lib.kda_chunk_fwd_timed.argtypes = list(lib.kda_chunk_fwd.argtypes) + [vp]
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS["c3"]
+    d = inputs.make(w, device=dev)
+    B, T, H, HV, K, V = w.B, w.T, w.H, w.HV, w.K, w.V
+    N = B
+    ws_bytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, N, 0, kda.KDA_BF16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(d["v"])
+    stream = torch.cuda.current_stream(dev)
+    sptr = vp(stream.cuda_stream)
+
+    def call(events_ptr):
+        rc = lib.kda_chunk_fwd_timed(
+            vp(d["q"].data_ptr()), vp(d["k"].data_ptr()), vp(d["v"].data_ptr()),
+            vp(d["g"].data_ptr()), vp(d["beta"].data_ptr()), None, None, N,
+            vp(out.data_ptr()), None, B, T, H, HV, K, V, kda.KDA_BF16, kda.KDA_BF16,
+            0.0, 64, vp(ws.data_ptr()), ws_bytes, None, sptr, events_ptr)
+        if rc != 0:
+            raise RuntimeError(lib.kda_last_error().decode())
+
+    for _ in range(args.warmup):
+        call(None)
+    torch.cuda.synchronize()
+    steps = args.steps
+    ev = Events(hip, 4 * steps)
+    outer = Events(hip, 2)
+    torch.cuda.synchronize()
+    hip.hipEventRecord(outer.ev[0], sptr)
+    for s in range(steps):
+        call(ctypes.cast(ctypes.byref(ev.ev, 4 * s * ctypes.sizeof(vp)), vp))
+    hip.hipEventRecord(outer.ev[1], sptr)
+    torch.cuda.synchronize()
+    total_ms = outer.ms(0, 1)
+    intra_ms = sum(ev.ms(4 * s + 1, 4 * s + 2) for s in range(steps)) / steps
+    scan_ms = sum(ev.ms(4 * s + 2, 4 * s + 3) for s in range(steps)) / steps
+    ev.close()
+    outer.close()
+    ms_per_step = total_ms / steps
+    tokens = B * T
+    tok_s = tokens / (ms_per_step * 1e-3)
+
+    # algorithmic quantities of the workload (inputs + outputs once, flops of the method)
+    path_bytes = (2 * B * T * H * K * 2 + B * T * HV * V * 2 * 2 + B * T * HV * K * 4 + B * T * HV * 2)
+    flops_exact = 141013.0 * B * T * HV
+    flops_dense = 180224.0 * B * T * HV
+    nchunks = B * ((T + 63) // 64)
+    rec = record_bytes(K, V, 2) * nchunks * HV
+    intra_bytes = path_bytes - B * T * HV * V * 2 + rec     # reads inputs, writes records
+    scan_bytes = rec + B * T * HV * V * 2                    # reads records, writes o
+    kern = {"intra": (intra_ms, intra_bytes), "scan": (scan_ms, scan_bytes)}
+    dom = max(kern, key=lambda k_: kern[k_][0])
+    dom_ms, dom_bytes = kern[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(dom)
+
+    # decode: 4096 sequences x 32 heads, one token each, fp32 states in and out
+    del ws, out
+    dd = inputs.make("dec", device=dev)
+    dout = torch.empty_like(dd["v"])
+    dstate = torch.empty_like(dd["initial_state"])
+
+    def dcall():
+        kda.kda_recurrent_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["initial_state"],
+                              dd["cu_seqlens"], output_final_state=True, out=dout, final_state=dstate)
+    for _ in range(2):
+        dcall()
+    torch.cuda.synchronize()
+    dev_ev = Events(hip, 2)
+    hip.hipEventRecord(dev_ev.ev[0], sptr)
+    for _ in range(args.decode_steps):
+        dcall()
+    hip.hipEventRecord(dev_ev.ev[1], sptr)
+    torch.cuda.synchronize()
+    dec_ms = dev_ev.ms(0, 1) / args.decode_steps
+    dev_ev.close()
+    dec_bytes = (2 * dd["initial_state"].numel() * 4 + 3 * dd["q"].numel() * 2 + dd["g"].numel() * 4
+                 + dd["beta"].numel() * 2 + dout.numel() * 2)
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    del dd, dout, dstate
+
+    result = {
+        "metric": "KDA fwd tokens/s + % bf16 MFMA peak at T=8192; decode state GB/s % HBM",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=log2(sigmoid(N(2,1))) >= -5, beta=sigmoid(N(0,1)))",
+        "config": {"workload": "chunk_kda fwd B=1 T=8192 H=16 HV=32 K=V=128 bf16, h0=None, no final state",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": dom_bytes, "avg_launch_ms": dom_ms,
+                     "kernels_ms": {"intra": intra_ms, "scan": scan_ms}},
+        "path": {"hbm_floor_bytes": path_bytes, "achieved_GBs": path_bytes / (ms_per_step * 1e-3) / 1e9,
+                 "hbm_frac": path_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "mfma_frac_exact_flops": flops_exact / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                 "mfma_frac_dense_tile_flops": flops_dense / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "decode": {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
+                   "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
+                   "bytes": dec_bytes},
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        host = inputs.make(w)   # same recipe on the host (the oracle's cost does not depend on values)
+        threads = oracle.default_threads()
+        t0 = time.time()
+        oracle.recurrent(host["q"], host["k"], host["v"], host["g"], host["beta"], None, None,
+                         None, nthreads=threads)
+        cpu_s = time.time() - t0
+        result["cpu_baseline"] = {"value": tokens / cpu_s, "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": "the full headline workload (8192 tokens x 32 value heads), fp64 token recurrence, one thread per (sequence, head) chain",
+                                  "seconds": cpu_s}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

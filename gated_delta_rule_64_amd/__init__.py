@@ -1,0 +1,34 @@
+"""KDA (Kimi Delta Attention) forward on MI355X: a thin Python binding over libkda.so.
+
+The binding only marshals arguments: it checks shapes and dtypes, allocates outputs
+and the workspace with PyTorch (device memory), and passes raw pointers plus the
+current HIP stream to the C ABI declared in ``include/kda.h``. Every arithmetic step
+runs in the library's HIP kernels. There is no CPU fallback: without the built
+library on a GPU every call raises.
+
+Entry points (same names as the C ABI):
+  kda_chunk_fwd(q, k, v, g, beta, ...)      chunked prefill forward
+  kda_recurrent_fwd(q, k, v, g, beta, ...)  per-token recurrent forward (decode)
+  kda_chunk_fwd_workspace_bytes(...)         workspace size query
+  kda_last_error()                           reason for the last failure
+"""
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    KDA_BF16,
+    KDA_DEV_BAD_CU_SEQLENS,
+    KDA_F32,
+    KdaError,
+    kda_chunk_fwd,
+    kda_chunk_fwd_workspace_bytes,
+    kda_last_error,
+    kda_recurrent_fwd,
+    library_path,
+    load_library,
+)
+
+__all__ = [
+    "kda_chunk_fwd", "kda_recurrent_fwd", "kda_chunk_fwd_workspace_bytes", "kda_last_error",
+    "KdaError", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
+    "library_path",
+]

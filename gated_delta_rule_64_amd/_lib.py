@@ -1,0 +1,188 @@
+"""ctypes binding of libkda.so (see ``include/kda.h`` for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32 = 0
+KDA_BF16 = 1
+KDA_DEV_BAD_CU_SEQLENS = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class KdaError(RuntimeError):
+    """A non-zero status from the library, with its reason string."""
+
+    def __init__(self, code: int, reason: str):
+        super().__init__(f"kda error {code}: {reason}")
+        self.code = code
+        self.reason = reason
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load the built library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m gated_delta_rule_64_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.kda_chunk_fwd.restype = i32
+        lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                      i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                      vp, sz, vp, vp]
+        lib.kda_recurrent_fwd.restype = i32
+        lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                          i32, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp]
+        lib.kda_chunk_fwd_workspace_bytes.restype = sz
+        lib.kda_chunk_fwd_workspace_bytes.argtypes = [i32] * 9
+        lib.kda_last_error.restype = ctypes.c_char_p
+        lib.kda_last_error.argtypes = []
+        lib.kda_abi_version.restype = i32
+        lib.kda_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def kda_last_error() -> str:
+    return load_library().kda_last_error().decode()
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"{what} must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_device(tensors):
+    dev = None
+    for name, t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    return dev
+
+
+def _common(q, k, v, g, beta, initial_state, cu_seqlens):
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k must be [B, T, H, K] and v [B, T, HV, V]")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    if tuple(k.shape) != tuple(q.shape):
+        raise ValueError(f"q and k must match, got {tuple(q.shape)} vs {tuple(k.shape)}")
+    if tuple(v.shape[:2]) != (B, T):
+        raise ValueError("v must share B and T with q")
+    if tuple(g.shape) != (B, T, HV, K):
+        raise ValueError(f"g must be {[B, T, HV, K]}, got {list(g.shape)}")
+    if tuple(beta.shape) != (B, T, HV):
+        raise ValueError(f"beta must be {[B, T, HV]}, got {list(beta.shape)}")
+    if g.dtype != torch.float32:
+        raise TypeError("g must be float32 (per-token log2 decay)")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    qkv = _dtype_code(q, "q")
+    bdt = _dtype_code(beta, "beta")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+        if B != 1:
+            raise ValueError("packed sequences (cu_seqlens) need B == 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        if initial_state.dtype != torch.float32:
+            raise TypeError("initial_state must be float32")
+        if tuple(initial_state.shape) != (N, HV, K, V):
+            raise ValueError(f"initial_state must be {[N, HV, K, V]}, got {list(initial_state.shape)}")
+    dev = _check_device([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+                         ("initial_state", initial_state), ("cu_seqlens", cu_seqlens)])
+    return B, T, H, HV, K, V, N, qkv, bdt, dev
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, N, packed, dtype=KDA_BF16) -> int:
+    if isinstance(dtype, torch.dtype):
+        dtype = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load_library().kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, N, int(bool(packed)), int(dtype)))
+
+
+def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                  output_final_state=False, scale=None, *, out=None, final_state=None,
+                  workspace=None, dev_status=None):
+    """Chunked KDA forward. Returns ``(o, final_state or None)``.
+
+    ``out`` / ``final_state`` / ``workspace`` may be given to reuse buffers;
+    ``dev_status`` (int32 [1] GPU tensor) receives device-side check flags.
+    ``final_state`` may be ``initial_state`` itself (in place).
+    """
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens)
+    if out is None:
+        out = torch.empty_like(v)
+    if output_final_state and final_state is None:
+        final_state = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev)
+    if not output_final_state:
+        final_state = None
+    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, N, int(cu_seqlens is not None), qkv)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), N, _ptr(out), _ptr(final_state), B, T, H, HV, K, V,
+                           qkv, bdt, float(scale or 0.0), 64, _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _ptr(dev_status),
+                           _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    return out, final_state
+
+
+def kda_recurrent_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                      output_final_state=False, scale=None, *, out=None, final_state=None,
+                      dev_status=None):
+    """Per-token recurrent KDA forward. Returns ``(o, final_state or None)``."""
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens)
+    if out is None:
+        out = torch.empty_like(v)
+    if output_final_state and final_state is None:
+        final_state = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev)
+    if not output_final_state:
+        final_state = None
+    rc = lib.kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                               _ptr(cu_seqlens), N, _ptr(out), _ptr(final_state), B, T, H, HV, K, V,
+                               qkv, bdt, float(scale or 0.0), _ptr(dev_status), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    return out, final_state

@@ -1,0 +1,161 @@
+// C ABI of the KDA library: argument validation, error strings and dispatch to the
+// kernel launchers. Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Checks shared by both entry points. Returns KDA_OK or an error code (with the reason).
+int check_common(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                 const float* initial_state, const int32_t* cu_seqlens, int N, const void* o,
+                 const float* final_state, int B, int T, int H, int HV, int K, int V,
+                 int qkv_dtype, int beta_dtype) {
+    if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32)
+        return fail(KDA_ERR_DTYPE, "qkv_dtype must be KDA_BF16 (1) or KDA_F32 (0), got %d", qkv_dtype);
+    if (beta_dtype != KDA_BF16 && beta_dtype != KDA_F32)
+        return fail(KDA_ERR_DTYPE, "beta_dtype must be KDA_BF16 (1) or KDA_F32 (0), got %d", beta_dtype);
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0 || N < 0)
+        return fail(KDA_ERR_SHAPE, "sizes must be non-negative (H, HV, K, V positive): B=%d T=%d H=%d HV=%d K=%d V=%d N=%d",
+                    B, T, H, HV, K, V, N);
+    if (HV % H != 0)
+        return fail(KDA_ERR_SHAPE, "HV=%d must be a multiple of H=%d", HV, H);
+    if (cu_seqlens) {
+        if (B != 1) return fail(KDA_ERR_SHAPE, "packed sequences (cu_seqlens given) need B == 1, got B=%d", B);
+    } else if (N != B) {
+        return fail(KDA_ERR_SHAPE, "without cu_seqlens N must equal B (N=%d, B=%d)", N, B);
+    }
+    const long long rows = (long long)B * T;
+    if (rows > 0x7fffffffLL)
+        return fail(KDA_ERR_SHAPE, "B*T=%lld exceeds 2^31-1 rows", rows);
+    if ((long long)N * HV > 0x7fffffffLL / 4)
+        return fail(KDA_ERR_SHAPE, "N*HV=%lld too large", (long long)N * HV);
+    if (rows > 0) {
+        if (!q || !k || !v || !g || !beta || !o)
+            return fail(KDA_ERR_NULL, "q, k, v, g, beta and o must be non-NULL");
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
+        !aligned16(initial_state) || !aligned16(final_state))
+        return fail(KDA_ERR_SHAPE, "q, k, v, g, o and the states must be 16-byte aligned");
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_last_error(void) { return g_last_error; }
+
+int kda_abi_version(void) { return 1; }
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
+                                     int packed, int qkv_dtype) {
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || N < 0 || (K != 64 && K != 128) ||
+        (V != 64 && V != 128) || (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32))
+        return 0;
+    kda::ChunkLayout L;
+    if (!kda::chunk_layout(B, T, HV, K, V, packed ? N : B, packed != 0, qkv_dtype, &L)) return 0;
+    return L.total;
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                  float* final_state, int B, int T, int H, int HV, int K, int V, int qkv_dtype,
+                  int beta_dtype, float scale, int chunk_size, void* workspace,
+                  size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+    return kda_chunk_fwd_timed(q, k, v, g, beta, initial_state, cu_seqlens, N, o, final_state, B,
+                               T, H, HV, K, V, qkv_dtype, beta_dtype, scale, chunk_size,
+                               workspace, workspace_bytes, dev_status, stream, nullptr);
+}
+
+int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int N, void* o, float* final_state, int B,
+                        int T, int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
+                        float scale, int chunk_size, void* workspace, size_t workspace_bytes,
+                        int32_t* dev_status, hipStream_t stream, hipEvent_t* events) {
+    clear_error();
+    int rc = check_common(q, k, v, g, beta, initial_state, cu_seqlens, N, o, final_state, B, T,
+                          H, HV, K, V, qkv_dtype, beta_dtype);
+    if (rc != KDA_OK) return rc;
+    if (chunk_size != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64, got %d", chunk_size);
+    if (K != 64 && K != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "K must be 64 or 128, got %d", K);
+    if (V != 64 && V != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "V must be 64 or 128, got %d", V);
+    if (cu_seqlens && (long long)T / 64 + N > 0x7fffffffLL / HV)
+        return fail(KDA_ERR_SHAPE, "too many chunks");
+    kda::ChunkLayout L;
+    kda::chunk_layout(B, T, HV, K, V, N, cu_seqlens != nullptr, qkv_dtype, &L);
+    if (N == 0) return KDA_OK;
+    if (L.total > 0) {
+        if (!workspace)
+            return fail(KDA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+        if (workspace_bytes < L.total)
+            return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, L.total);
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+            return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
+    a.o = o; a.final_state = final_state;
+    a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype;
+    a.scale = scale == 0.0f ? 1.0f / sqrtf((float)K) : scale;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.dev_status = dev_status; a.stream = stream; a.events = events;
+    hipError_t err = kda::launch_chunk(a, L);
+    if (err != hipSuccess)
+        return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return KDA_OK;
+}
+
+int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* g,
+                      const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                      int N, void* o, float* final_state, int B, int T, int H, int HV, int K,
+                      int V, int qkv_dtype, int beta_dtype, float scale, int32_t* dev_status,
+                      hipStream_t stream) {
+    clear_error();
+    int rc = check_common(q, k, v, g, beta, initial_state, cu_seqlens, N, o, final_state, B, T,
+                          H, HV, K, V, qkv_dtype, beta_dtype);
+    if (rc != KDA_OK) return rc;
+    if (K != 64 && K != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "K must be 64 or 128, got %d", K);
+    if (V % 64 != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "V must be a multiple of 64, got %d", V);
+    if ((long long)N * HV * (V / 64) > 0x7fffffffLL * 4LL)
+        return fail(KDA_ERR_SHAPE, "grid too large");
+    if (N == 0) return KDA_OK;
+    kda::RecurrentArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
+    a.o = o; a.final_state = final_state;
+    a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype;
+    a.scale = scale == 0.0f ? 1.0f / sqrtf((float)K) : scale;
+    a.dev_status = dev_status; a.stream = stream;
+    hipError_t err = kda::launch_recurrent(a);
+    if (err != hipSuccess)
+        return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return KDA_OK;
+}
+
+}  // extern "C"

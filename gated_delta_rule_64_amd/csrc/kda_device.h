@@ -1,0 +1,109 @@
+// Device-side building blocks shared by the KDA kernels (gfx950 / CDNA4).
+//
+//  * element types: inputs are fp32 or bf16 (__bf16, converted with the hardware
+//    round-to-nearest-even instruction);
+//  * 16x16 MFMA tiles: bf16 uses v_mfma_f32_16x16x32_bf16 (8 bf16 per lane, K step 32),
+//    fp32 uses v_mfma_f32_16x16x4_f32 (1 fp32 per lane, K step 4). In both, lane l feeds
+//    row/column (l % 16) at contraction offset (l / 16) * per_lane, and receives
+//    D[4 * (l / 16) + r][l % 16] in accumulator register r;
+//  * LDS tiles of 16-byte chunks whose chunk index is XOR-swizzled with (row & 7), so
+//    that MFMA fragment reads (16 rows, same column) and transposed 4-row writes do not
+//    pile onto the same banks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// 2^x with the hardware transcendental (v_exp_f32); x <= 0 in every use below, results
+// under 2^-126 flush to zero, which is below anything the outputs can resolve.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------------
+// MFMA 16x16 tile products: C[16x16] += A[16 x Kc] * B[16 x Kc]^T, both operands with
+// the contraction index contiguous.
+// ---------------------------------------------------------------------------------
+template <typename TW> struct Mma;
+
+template <> struct Mma<__bf16> {
+    static constexpr int KS = 32;   // contraction covered by one instruction
+    static constexpr int KPL = 8;   // contraction elements held by one lane
+    typedef bf16x8 frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int KS = 4;
+    static constexpr int KPL = 1;
+    typedef float frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// ---------------------------------------------------------------------------------
+// Swizzled LDS tile: ROWS x COLS elements of TW, 16-byte chunks, chunk ^= (row & 7).
+// ---------------------------------------------------------------------------------
+template <typename TW, int ROWS, int COLS> struct Tile {
+    static constexpr int EPC = 16 / (int)sizeof(TW);   // elements per chunk
+    static constexpr int NCH = COLS / EPC;             // chunks per row
+    static_assert(COLS % EPC == 0, "row must be whole chunks");
+    static_assert(NCH % 8 == 0, "swizzle needs at least 8 chunks per row");
+    static constexpr int ELEMS = ROWS * COLS;
+    static constexpr int BYTES = ELEMS * (int)sizeof(TW);
+
+    __device__ __forceinline__ static int idx(int row, int col) {
+        const int ch = col / EPC;
+        return row * COLS + ((ch ^ (row & 7)) * EPC) + (col % EPC);
+    }
+    // MFMA operand fragment: row `row`, contraction offset kbase + (lane/16)*KPL
+    __device__ __forceinline__ static typename Mma<TW>::frag frag(const TW* t, int row, int k) {
+        return *reinterpret_cast<const typename Mma<TW>::frag*>(t + idx(row, k));
+    }
+};
+
+// Product of a 16-row band of A (rows a_row0..+15) with a 16-row band of B (rows
+// b_row0..+15) over contraction [k0, k1), accumulated into acc.
+template <typename TW, typename TA, typename TB>
+__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const TW* A, int a_row0, const TW* B,
+                                          int b_row0, int k0, int k1, int lane) {
+    const int r = lane & 15;
+    const int ko = (lane >> 4) * Mma<TW>::KPL;
+    for (int k = k0; k < k1; k += Mma<TW>::KS) {
+        auto a = TA::frag(A, a_row0 + r, k + ko);
+        auto b = TB::frag(B, b_row0 + r, k + ko);
+        acc = Mma<TW>::mma(a, b, acc);
+    }
+    return acc;
+}
+
+// Store 4 consecutive rows (row0..row0+3) of one column from accumulator registers into
+// a transposed tile T[col][row0..row0+3] (row0 % 4 == 0).
+template <typename TW, typename TT>
+__device__ __forceinline__ void store_col4(TW* t, int col, int row0, f32x4 v) {
+    TW* p = t + TT::idx(col, row0);
+    p[0] = from_f32<TW>(v[0]);
+    p[1] = from_f32<TW>(v[1]);
+    p[2] = from_f32<TW>(v[2]);
+    p[3] = from_f32<TW>(v[3]);
+}
+
+// Block-wide OR of a flag (256-thread blocks).
+__device__ __forceinline__ int block_any(int pred) { return __syncthreads_or(pred); }
+
+}  // namespace kda

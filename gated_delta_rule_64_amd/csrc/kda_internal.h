@@ -1,0 +1,77 @@
+// Host-side launch descriptors shared by the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+
+struct RecurrentArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    const float* initial_state;
+    const int32_t* cu_seqlens;
+    void* o;
+    float* final_state;
+    int N, B, T, H, HV, K, V;
+    int qkv_dtype, beta_dtype;
+    float scale;
+    int32_t* dev_status;
+    hipStream_t stream;
+};
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    const float* initial_state;
+    const int32_t* cu_seqlens;
+    void* o;
+    float* final_state;
+    int N, B, T, H, HV, K, V;
+    int qkv_dtype, beta_dtype;
+    float scale;
+    void* workspace;
+    size_t workspace_bytes;
+    int32_t* dev_status;
+    hipStream_t stream;
+    hipEvent_t* events;   // optional: 4 events recorded around the kernels
+};
+
+// Workspace layout of the chunked forward (all offsets 256-byte aligned):
+//   [sched]  packed mode only: int32 first_chunk[N], int32 end_chunk[N],
+//            int32 slot_ok[N], int32 n_chunks[1], int2 chunk_table[NCmax] (row start,
+//            length)
+//   [inter]  per (value head hv, chunk c), one record of the Stage 2 results, in order:
+//              w      [64][K]       element type of the compute path (TW)
+//              qg     [NS][64][K]   TW, scale folded in
+//              kgT    [NS][K][64]   TW, transposed
+//              Aqk    [NS][64][64]  TW, scale folded in, zero above the diagonal
+//              u      [64][V]       fp32
+//              eG     [K]           fp32, 2^(chunk's total log2 decay)
+//            NS = 2 on the bf16 path (tile 1 holds x - bf16(x) rounded to bf16, so
+//            hi + lo carries about 16 significant bits), NS = 1 on the fp32 path.
+//            records are ordered hv-major: record(hv, c) = hv * NCmax + c.
+struct ChunkLayout {
+    int NCmax;            // chunk slots (dense: B * ceil(T/64); packed: T/64 + N)
+    size_t elem;          // bytes per intermediate element (2 bf16, 4 fp32)
+    size_t off_w, off_u, off_qg, off_kgT, off_aqk, off_eg, rec_bytes;
+    size_t sched_bytes;   // bytes of the packed-mode schedule (0 in dense mode)
+    size_t total;
+};
+
+bool chunk_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qkv_dtype,
+                  ChunkLayout* out);
+
+hipError_t launch_recurrent(const RecurrentArgs& a);
+hipError_t launch_chunk(const ChunkArgs& a, const ChunkLayout& L);
+
+}  // namespace kda

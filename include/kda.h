@@ -1,0 +1,147 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * KDA is the gated delta rule with one base-2 decay per key channel. For each sequence
+ * n and value head hv (q/k head h = hv / (HV / H)), with S an fp32 [K, V] state:
+ *
+ *     S <- Diag(2^g_t) S                      decay every key row d by 2^g_t[d]
+ *     S <- S + beta_t k_t (v_t - S^T k_t)^T    delta-rule erase + write
+ *     o_t = scale * S^T q_t                    read the updated state
+ *
+ * Source: "kernel-fun 0.2.0.dev1 sdist", ALGORITHM.md (intro and section Forward:
+ * base-2 gates <= 0, GVA head map h = hv // (HV // H), scale = K^-0.5, the chunk
+ * stages); "Add fused recurrent_kda for decode and inference prefill" (attention-gym
+ * PR #317, description: per-token log2 gate, packed int32 offsets, empty slots, state
+ * per logical sequence, fp32 state and compute).
+ *
+ * Conventions for every entry point
+ *   - Tensors are device pointers to contiguous row-major arrays (last index fastest),
+ *     owned by the caller. The library never allocates, frees or synchronises; all
+ *     work is enqueued on `stream` (NULL = the default stream).
+ *   - Layouts: q, k [B, T, H, K]; v [B, T, HV, V]; g fp32 [B, T, HV, K] (per-token
+ *     log2 decay, expected <= 0); beta [B, T, HV]; states fp32 [N, HV, K, V];
+ *     o [B, T, HV, V] in the q/k/v dtype.
+ *   - Dense mode (cu_seqlens == NULL): N must equal B; sequence n is row b = n, all T
+ *     tokens. Packed mode (cu_seqlens != NULL): B must be 1; cu_seqlens is an int32
+ *     device array [N + 1]; sequence n is tokens cu_seqlens[n] .. cu_seqlens[n+1]-1.
+ *     Repeated offsets are empty slots: their final state is their initial state
+ *     copied bitwise (zeros without an initial state). Rows at or past cu_seqlens[N]
+ *     are neither read nor written.
+ *   - initial_state == NULL means zeros. final_state == NULL means no final state is
+ *     wanted: nothing is stored. final_state may equal initial_state (in place).
+ *     o must not alias any input.
+ *   - scale == 0.0f selects K^-0.5.
+ *   - Return value: KDA_OK or a negative kda_status; kda_last_error() then gives a
+ *     reason (thread-local, valid until the next call on the same thread). Argument
+ *     errors are detected on the host before anything is enqueued.
+ *   - Device-side checks never fault: a packed slot whose offsets break
+ *     0 = cu[0] <= cu[n] <= cu[n+1] <= T is skipped (its rows of o and its final state
+ *     are left untouched) and KDA_DEV_BAD_CU_SEQLENS is OR-ed into *dev_status when
+ *     dev_status != NULL. The check runs on every call, including graph replays.
+ *     Offsets that decrease always fail some slot's check; slots that pass may then
+ *     overlap, and their shared rows of o are unspecified. kda_chunk_fwd also skips
+ *     and flags any slot whose chunks would exceed its chunk table (T/64 + N chunks),
+ *     which only overlapping slots can reach.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,         /* a required pointer is NULL */
+    KDA_ERR_SHAPE = -2,        /* inconsistent or non-positive sizes, HV % H != 0, ... */
+    KDA_ERR_DTYPE = -3,        /* unknown dtype code */
+    KDA_ERR_UNSUPPORTED = -4,  /* K, V or chunk size outside what the kernels cover */
+    KDA_ERR_WORKSPACE = -5,    /* workspace missing, too small or misaligned */
+    KDA_ERR_HIP = -6           /* a kernel launch failed */
+};
+
+enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+};
+
+/* bit flags written into *dev_status by device-side checks */
+#define KDA_DEV_BAD_CU_SEQLENS 1
+
+/*
+ * Chunked forward (prefill). The method of "kernel-fun 0.2.0.dev1 sdist",
+ * ALGORITHM.md, section Forward: chunks of 64 tokens (restarting at every sequence
+ * start), chunk-local log2 cumsum of the gate (Stage 1), intra-chunk Aqk / WY
+ * transform (Stage 2, 16-row sub-chunks), then the serial state scan with the output
+ * read-out (Stage 3+4).
+ *
+ *   qkv_dtype  KDA_BF16: bf16 q, k, v, o; bf16 matrix-core operands, fp32 accumulation
+ *              and fp32 state. KDA_F32: fp32 everywhere.
+ *   beta_dtype KDA_BF16 or KDA_F32 (independent of qkv_dtype).
+ *   K          64 or 128.  V: 64 or 128.  chunk_size: must be 64.
+ *   workspace  device buffer of at least kda_chunk_fwd_workspace_bytes(...) bytes,
+ *              256-byte aligned, owned by the caller; it holds the per-chunk
+ *              intermediates of one call and must not be shared by calls that may
+ *              run concurrently.
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                  const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                  int N, void* o, float* final_state, int B, int T, int H, int HV, int K,
+                  int V, int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                  void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                  hipStream_t stream);
+
+/*
+ * kda_chunk_fwd with in-place timing: identical arguments, results and errors, plus
+ * `events`, an array of four HIP events created by the caller. They are recorded on
+ * `stream` before the first kernel (events[0]), after the packed-mode scheduler
+ * (events[1]; same point as events[0] in dense mode), after the Stage 1+2 kernel
+ * (events[2]) and after the Stage 3+4 scan (events[3]), so the caller can read each
+ * kernel's duration with hipEventElapsedTime. events == NULL behaves like kda_chunk_fwd.
+ * For profiling callers (benchmarks); nothing is synchronised.
+ */
+int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int N, void* o, float* final_state, int B,
+                        int T, int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
+                        float scale, int chunk_size, void* workspace, size_t workspace_bytes,
+                        int32_t* dev_status, hipStream_t stream, hipEvent_t* events);
+
+/*
+ * Workspace bytes kda_chunk_fwd needs for these sizes (packed != 0 for packed mode,
+ * N sequences). Returns 0 for invalid sizes.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
+                                     int packed, int qkv_dtype);
+
+/*
+ * Per-token recurrent forward (decode, or a token-by-token prefill): the contract of
+ * "Add fused recurrent_kda for decode and inference prefill" (attention-gym PR #317):
+ * each (sequence, value head, 64-column slice of V) walks its tokens in order with
+ * its fp32 state slice in registers; fp32 arithmetic whatever the input dtype; one
+ * flat 1-D grid, so N * HV may exceed 65,535.
+ *
+ *   qkv_dtype, beta_dtype  KDA_BF16 or KDA_F32.   K: 64 or 128.   V: a multiple of 64.
+ */
+int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* g,
+                      const void* beta, const float* initial_state,
+                      const int32_t* cu_seqlens, int N, void* o, float* final_state, int B,
+                      int T, int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
+                      float scale, int32_t* dev_status, hipStream_t stream);
+
+/* Reason for the last non-KDA_OK return on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/* ABI version of this header (bumped on any signature change). */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

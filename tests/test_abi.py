@@ -1,0 +1,157 @@
+"""The C ABI library without a GPU: it loads, exports every declared entry point, sizes
+its workspace as documented, and rejects bad arguments on the host before enqueueing
+anything (no test here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_64_amd import _lib
+    if not os.path.exists(_lib.library_path()):
+        from gated_delta_rule_64_amd import build
+        build.build()
+    return _lib.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kda_chunk_fwd", "kda_recurrent_fwd", "kda_chunk_fwd_workspace_bytes",
+              "kda_last_error", "kda_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from gated_delta_rule_64_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_abi_version(lib):
+    assert lib.kda_abi_version() == 1
+
+
+def _rec_bytes(K, V, elem):
+    # w, qg, kg^T in the compute type; u fp32; Aqk (plus its bf16 residual); 2^G fp32
+    b = 64 * K * elem * 3 + 64 * V * 4 + 64 * 64 * elem * (2 if elem == 2 else 1) + 4 * K
+    return (b + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("K,V,dt,elem", [(128, 128, 1, 2), (64, 64, 0, 4), (128, 64, 1, 2)])
+def test_workspace_bytes_dense(lib, K, V, dt, elem):
+    B, T, H, HV = 2, 4096 + 17, 4, 8
+    nt = (T + 63) // 64
+    got = lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, dt)
+    assert got == HV * B * nt * _rec_bytes(K, V, elem)
+
+
+def test_workspace_bytes_packed(lib):
+    N, T, HV = 64, 33000, 16
+    got = lib.kda_chunk_fwd_workspace_bytes(1, T, 16, HV, 128, 128, N, 1, 1)
+    ncmax = T // 64 + N
+    sched = ((3 * N + 1) * 4 + 15) // 16 * 16 + ncmax * 8
+    sched = (sched + 255) // 256 * 256
+    assert got == sched + HV * ncmax * _rec_bytes(128, 128, 2)
+
+
+def test_workspace_bytes_invalid(lib):
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 96, 128, 1, 0, 1) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 128, 128, 1, 0, 7) == 0
+
+
+FAKE = 0x10000  # aligned non-NULL host value: every call below fails validation first
+
+
+def _chunk(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, N=1, o=FAKE, ht=None,
+             B=1, T=64, H=2, HV=2, K=128, V=128, qd=1, bd=1, scale=0.0, cs=64,
+             ws=FAKE, wsb=1 << 40, st=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["N"],
+                             a["o"], a["ht"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"],
+                             a["qd"], a["bd"], a["scale"], a["cs"], a["ws"], a["wsb"], a["st"],
+                             a["stream"])
+
+
+def _rec(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, N=1, o=FAKE, ht=None,
+             B=1, T=1, H=2, HV=2, K=128, V=128, qd=1, bd=1, scale=0.0, st=None, stream=None)
+    a.update(kw)
+    return lib.kda_recurrent_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"],
+                                 a["N"], a["o"], a["ht"], a["B"], a["T"], a["H"], a["HV"], a["K"],
+                                 a["V"], a["qd"], a["bd"], a["scale"], a["st"], a["stream"])
+
+
+CASES = [
+    ("null q", dict(q=None), -1),
+    ("HV % H", dict(H=3, HV=4), -2),
+    ("negative T", dict(T=-1), -2),
+    ("B != N dense", dict(B=2, N=1), -2),
+    ("packed needs B == 1", dict(B=2, N=1, cu=FAKE), -2),
+    ("dtype", dict(qd=5), -3),
+    ("beta dtype", dict(bd=2), -3),
+    ("misaligned q", dict(q=FAKE + 4), -2),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", CASES, ids=[c[0] for c in CASES])
+def test_chunk_rejects(lib, name, kw, code):
+    assert _chunk(lib, **kw) == code
+    assert lib.kda_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("name,kw,code", CASES, ids=[c[0] for c in CASES])
+def test_recurrent_rejects(lib, name, kw, code):
+    assert _rec(lib, **kw) == code
+    assert lib.kda_last_error().decode() != ""
+
+
+def test_chunk_specific_rejects(lib):
+    assert _chunk(lib, cs=32) == -4
+    assert b"chunk_size" in lib.kda_last_error()
+    assert _chunk(lib, K=96) == -4
+    assert _chunk(lib, V=256) == -4
+    assert _chunk(lib, ws=None) == -5
+    assert _chunk(lib, wsb=16) == -5
+    assert _chunk(lib, ws=FAKE + 16) == -5
+
+
+def test_recurrent_specific_rejects(lib):
+    assert _rec(lib, K=32) == -4
+    assert _rec(lib, V=96) == -4
+
+
+def test_empty_problem_is_a_noop(lib):
+    # N = 0 sequences: nothing to do, nothing enqueued
+    assert _chunk(lib, cu=FAKE, N=0, T=0) == 0
+    assert _rec(lib, cu=FAKE, N=0, T=0) == 0
+    assert lib.kda_last_error().decode() == ""
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    from gated_delta_rule_64_amd import kda_chunk_fwd
+    q = torch.zeros(1, 64, 2, 128)
+    with pytest.raises(ValueError):
+        kda_chunk_fwd(q, q, torch.zeros(1, 64, 2, 128), torch.zeros(1, 64, 2, 128),
+                      torch.zeros(1, 64, 2))
+    with pytest.raises(TypeError):
+        kda_chunk_fwd(q, q, torch.zeros(1, 64, 2, 128), torch.zeros(1, 64, 2, 128, dtype=torch.float64),
+                      torch.zeros(1, 64, 2))

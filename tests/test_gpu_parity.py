@@ -1,0 +1,334 @@
+"""Parity of the HIP library with the fp64 oracle on MI355X (marked gpu).
+
+Every case feeds the oracle the exact tensors the GPU received (copied back to host),
+and compares element by element: max|err| <= 1e-4 for fp32 inputs, <= 2e-2 * RMS of
+the oracle output for bf16 inputs; integer-exact items (empty-slot state, rows outside
+every sequence, NULL state vs zeros) are compared bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import chunked as chunked_ref
+from gated_delta_rule_64_amd import inputs
+from tests.util import check, log, to64, to_device, valid_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import gated_delta_rule_64_amd as kda
+    kda.load_library()   # raises loudly when the HIP library is missing
+    assert torch.cuda.is_available()
+    yield
+
+
+def run(path, d, final=True, scale=None, **kw):
+    import gated_delta_rule_64_amd as kda
+    fn = kda.kda_chunk_fwd if path == "chunk" else kda.kda_recurrent_fwd
+    o, ht = fn(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], d["cu_seqlens"],
+               output_final_state=final, scale=scale, **kw)
+    torch.cuda.synchronize()
+    return o, ht
+
+
+def oracle_of(d, scale=None):
+    return oracle.recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                            d["cu_seqlens"], scale)
+
+
+def small(B, T, H, HV, K, V, dtype, seed, h0=True, gate_lo=None, clamp=-5.0):
+    """A seeded case drawn with the workload recipe at custom sizes."""
+    w = inputs.Workload("custom", B, T, H, HV, K, V, dtype, dtype, seed, clamp,
+                        0.05 if h0 else None, True)
+    d = inputs.make(w)
+    if gate_lo is not None:
+        d["g"] = torch.empty_like(d["g"]).uniform_(gate_lo, 0.0, generator=torch.Generator().manual_seed(seed + 99))
+    return to_device(d)
+
+
+# ------------------------------------------------------------------------------------
+# tiny (fp32): both paths, NULL state vs explicit zeros
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_tiny_fp32(path):
+    d = to_device(inputs.make("tiny"))
+    log(f"[tiny fp32 {path}] B=1 T=256 H=HV=2 K=V=64")
+    o, ht = run(path, d)
+    o_ref, ht_ref = oracle_of(d)
+    check("o", o, o_ref, torch.float32)
+    check("final_state", ht, ht_ref, torch.float32)
+    z = dict(d, initial_state=torch.zeros(1, 2, 64, 64, device=DEV))
+    o2, ht2 = run(path, z)
+    assert torch.equal(o, o2) and torch.equal(ht, ht2), "NULL state must equal explicit zeros bitwise"
+
+
+# ------------------------------------------------------------------------------------
+# full-size bf16 configurations
+# ------------------------------------------------------------------------------------
+def test_chunk_c2_full():
+    d = to_device(inputs.make("c2"))
+    log("[c2 chunk] B=2 T=4096 H=HV=16 K=V=128 bf16, h0 ~ N(0, 0.05)")
+    o, ht = run("chunk", d)
+    o_ref, ht_ref = oracle_of(d)
+    check("o", o, o_ref, torch.bfloat16)
+    check("final_state", ht, ht_ref, torch.bfloat16)
+
+
+def test_chunk_c3_full():
+    d = to_device(inputs.make("c3"))
+    log("[c3 chunk] B=1 T=8192 H=16 HV=32 K=V=128 bf16, h0 = None, no final state")
+    o, ht = run("chunk", d, final=False)
+    assert ht is None
+    o_ref, _ = oracle_of(d)
+    check("o", o, o_ref, torch.bfloat16)
+
+
+def test_chunk_varlen_full():
+    d = to_device(inputs.make("vl"))
+    cu = d["cu_seqlens"].cpu()
+    T = d["q"].shape[1]
+    log(f"[vl chunk] 64 slots, {int(cu[-1])} tokens, T_phys={T}, H=HV=16 K=V=128 bf16")
+    sentinel = torch.full_like(d["v"], float("nan"))
+    h0 = d["initial_state"]
+    o, ht = run("chunk", d, out=sentinel)
+    o_ref, ht_ref = oracle_of(d)
+    m = valid_rows(cu, T)
+    check("o", o[:, m], o_ref[:, m], torch.bfloat16)
+    check("final_state", ht, ht_ref, torch.bfloat16)
+    lens = (cu[1:] - cu[:-1]).numpy()
+    empty = np.nonzero(lens == 0)[0]
+    assert len(empty) == 4
+    for n in empty:
+        assert torch.equal(ht[n], h0[n]), f"empty slot {n} state must pass through bitwise"
+    tail = o[:, ~m]
+    assert tail.numel() > 0 and torch.isnan(tail).all(), "rows past the last offset must stay untouched"
+
+
+def test_recurrent_decode_full_sampled():
+    """The decode workload at full size (4096 sequences x 32 heads: a flat grid of
+    262,144 waves), checked against the oracle on 96 sampled sequences (all heads)."""
+    d = inputs.make("dec", device=DEV)
+    log("[dec recurrent] N=4096 HV=32 K=V=128, 1 token each, fp32 states")
+    o, ht = run("recurrent", d)
+    o2, ht2 = run("recurrent", d)
+    assert torch.equal(o, o2) and torch.equal(ht, ht2), "decode must be deterministic"
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(4096, size=96, replace=False))
+    idx = torch.as_tensor(sample, device=DEV)
+    sub = dict(q=d["q"][0, idx].unsqueeze(1), k=d["k"][0, idx].unsqueeze(1), v=d["v"][0, idx].unsqueeze(1),
+               g=d["g"][0, idx].unsqueeze(1), beta=d["beta"][0, idx].unsqueeze(1),
+               initial_state=d["initial_state"][idx], cu_seqlens=None)
+    o_ref, ht_ref = oracle_of(sub)
+    check("o (sampled)", o[0, idx].unsqueeze(1), o_ref, torch.bfloat16)
+    check("final_state (sampled)", ht[idx], ht_ref, torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------------
+# cross-checks and exact properties
+# ------------------------------------------------------------------------------------
+def test_chunk_vs_recurrent_bf16():
+    d = small(2, 1000, 4, 8, 128, 128, torch.bfloat16, seed=11)
+    o1, s1 = run("chunk", d)
+    o2, s2 = run("recurrent", d)
+    o_ref, s_ref = oracle_of(d)
+    check("chunk o", o1, o_ref, torch.bfloat16)
+    check("recurrent o", o2, o_ref, torch.bfloat16)
+    check("chunk vs recurrent", o1, to64(o2), torch.bfloat16)
+    check("chunk state", s1, s_ref, torch.bfloat16)
+    check("recurrent state", s2, s_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_retrieval_identity_c3_scale(path):
+    """beta = 1, q = k: o_t = scale * v_t whatever the history -- an indexing check at the
+    long-context size that needs no oracle run."""
+    d = to_device(inputs.make("c3"))
+    d["q"] = d["k"]
+    d["beta"] = torch.ones_like(d["beta"])
+    o, _ = run(path, d, final=False)
+    want = to64(d["v"]) * 128 ** -0.5
+    check("o vs scale*v", o, want, torch.bfloat16)
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_gva_equals_repeated_heads(path):
+    d = small(1, 300, 2, 6, 128, 128, torch.bfloat16, seed=5)
+    o1, s1 = run(path, d)
+    r = dict(d, q=d["q"].repeat_interleave(3, dim=2).contiguous(),
+             k=d["k"].repeat_interleave(3, dim=2).contiguous())
+    o2, s2 = run(path, r)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_ragged_dense(path, dtype):
+    """T not a multiple of 64 (short last chunk), several batch rows."""
+    for T in (1, 63, 65, 130):
+        d = small(3, T, 2, 4, 64, 128, dtype, seed=T)
+        o, s = run(path, d)
+        o_ref, s_ref = oracle_of(d)
+        check(f"T={T} o", o, o_ref, dtype)
+        check(f"T={T} state", s, s_ref, dtype)
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_packed_edge_lengths(path, dtype):
+    lens = [1, 63, 64, 0, 65, 130, 0, 2]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    T = int(cu[-1]) + 40
+    d = small(1, T, 2, 2, 128, 64, dtype, seed=3)
+    d["cu_seqlens"] = cu.to(DEV)
+    h0 = torch.randn(len(lens), 2, 128, 64, generator=torch.Generator().manual_seed(1)).to(DEV) * 0.05
+    d["initial_state"] = h0
+    out = torch.full_like(d["v"], float("nan"))
+    o, s = run(path, d, out=out)
+    o_ref, s_ref = oracle_of(d)
+    m = valid_rows(cu, T)
+    check("o", o[:, m], o_ref[:, m], dtype)
+    check("state", s, s_ref, dtype)
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert torch.equal(s[n], h0[n])
+    assert torch.isnan(o[:, ~m]).all()
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_packed_equals_dense_runs(path):
+    lens = [200, 64, 17]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    d = small(1, int(cu[-1]), 4, 4, 128, 128, torch.bfloat16, seed=8)
+    d["cu_seqlens"] = cu.to(DEV)
+    d["initial_state"] = torch.randn(3, 4, 128, 128, generator=torch.Generator().manual_seed(2)).to(DEV) * 0.05
+    o, s = run(path, d)
+    for n in range(3):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sub = dict(q=d["q"][:, a:b].contiguous(), k=d["k"][:, a:b].contiguous(), v=d["v"][:, a:b].contiguous(),
+                   g=d["g"][:, a:b].contiguous(), beta=d["beta"][:, a:b].contiguous(),
+                   initial_state=d["initial_state"][n:n + 1].contiguous(), cu_seqlens=None)
+        od, sd = run(path, sub)
+        # chunks restart at every sequence start, so packed and dense runs do the same work
+        assert torch.equal(o[:, a:b], od), n
+        assert torch.equal(s[n], sd[0]), n
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_invalid_cu_seqlens_flagged_not_faulting(path):
+    import gated_delta_rule_64_amd as kda
+    T = 300
+    d = small(1, T, 2, 2, 128, 128, torch.bfloat16, seed=4)
+    h0 = torch.randn(3, 2, 128, 128, generator=torch.Generator().manual_seed(3)).to(DEV) * 0.05
+    d["initial_state"] = h0
+    for bad in ([0, 100, 50, 200], [5, 100, 150, 200], [0, 100, 200, 400], [0, -7, 100, 200]):
+        d["cu_seqlens"] = torch.tensor(bad, dtype=torch.int32, device=DEV)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        fs = torch.full((3, 2, 128, 128), 7.0, device=DEV)
+        run(path, d, dev_status=status, final_state=fs)
+        assert int(status.item()) & kda.KDA_DEV_BAD_CU_SEQLENS, bad
+        for n in range(3):
+            a, b = bad[n], bad[n + 1]
+            if not (0 <= a <= b <= T and (n > 0 or a == 0)):
+                assert (fs[n] == 7.0).all(), f"slot {n} of {bad} must be left untouched"
+    good = torch.tensor([0, 100, 150, 300], dtype=torch.int32, device=DEV)
+    d["cu_seqlens"] = good
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    run(path, d, dev_status=status)
+    assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_inplace_state_and_null_final(path):
+    d = small(2, 129, 2, 2, 128, 128, torch.bfloat16, seed=6)
+    o1, s1 = run(path, d)
+    st = d["initial_state"].clone()
+    o2, s2 = run(path, dict(d, initial_state=st), final_state=st)
+    assert s2.data_ptr() == st.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(s1, st)
+    o3, s3 = run(path, d, final=False)
+    assert s3 is None and torch.equal(o1, o3)
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_deterministic(path):
+    d = small(2, 700, 4, 8, 128, 128, torch.bfloat16, seed=9)
+    a = run(path, d)
+    b = run(path, d)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_split_resume(path):
+    d = small(1, 512, 2, 4, 128, 128, torch.bfloat16, seed=12)
+    o, s = run(path, d)
+    t1 = 192
+
+    def part(a, b, h0):
+        return dict(q=d["q"][:, a:b].contiguous(), k=d["k"][:, a:b].contiguous(),
+                    v=d["v"][:, a:b].contiguous(), g=d["g"][:, a:b].contiguous(),
+                    beta=d["beta"][:, a:b].contiguous(), initial_state=h0, cu_seqlens=None)
+    oa, sa = run(path, part(0, t1, d["initial_state"]))
+    ob, sb = run(path, part(t1, 512, sa))
+    check("resumed o", torch.cat([oa, ob], 1), to64(o), torch.bfloat16)
+    check("resumed state", sb, to64(s), torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_extreme_decay(path, dtype):
+    """Per-token gates down to -15 (mixed with mild ones): the chunk path's steep-decay
+    branch (exact diagonal blocks) must stay finite and within tolerance."""
+    d = small(1, 256, 2, 2, 128, 128, dtype, seed=13, gate_lo=-15.0)
+    g = d["g"].clone()
+    g[:, 64:128] = -15.0
+    d["g"] = g
+    o, s = run(path, d)
+    o_ref, s_ref = oracle_of(d)
+    check("o", o, o_ref, dtype)
+    check("state", s, s_ref, dtype)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_chunk_stage2_records_fp32(seed):
+    """The intra kernel's per-chunk records (Aqk, w, u, qg, kg^T, 2^G) against the fp64
+    chunk algebra, fp32 inputs."""
+    import gated_delta_rule_64_amd as kda
+    d = small(1, 128 + 37, 2, 2, 64, 64, torch.float32, seed=seed)
+    B, T, H, K = d["q"].shape
+    HV, V = 2, 64
+    nbytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, torch.float32)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    run("chunk", d, workspace=ws)
+    _, _, stages = chunked_ref.chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                       None, None, return_stages=True)
+    rec = (64 * K * 4 * 3 + 64 * V * 4 + 64 * 64 * 4 + 4 * K + 255) // 256 * 256
+    raw = ws.cpu()
+    NT = (T + 63) // 64
+    for st in stages:
+        hv, c = st["hv"], st["start"] // 64
+        base = (hv * NT + c) * rec
+        L = st["length"]
+
+        def arr(off, shape):
+            n = int(np.prod(shape))
+            return raw[base + off: base + off + 4 * n].view(torch.float32).reshape(shape).double().numpy()
+        # record layout (fp32 path): w | qg | kg^T | Aqk | u | 2^G
+        off = 0
+        w = arr(off, (64, K)); off += 64 * K * 4
+        qg = arr(off, (64, K)); off += 64 * K * 4
+        kgT = arr(off, (K, 64)); off += K * 64 * 4
+        aqk = arr(off, (64, 64)); off += 64 * 64 * 4
+        u = arr(off, (64, V)); off += 64 * V * 4
+        eg = arr(off, (K,))
+        scale = K ** -0.5
+        for name, got, want in (("Aqk", aqk[:L, :L], st["Aqk"]), ("w", w[:L], st["w"]),
+                                ("u", u[:L], st["u"]), ("qg", qg[:L], scale * st["qg"]),
+                                ("kgT", kgT[:, :L], st["kg"].T), ("2^G", eg, np.exp2(st["G"]))):
+            err = np.abs(got - want).max()
+            assert err <= 2e-5 * max(1.0, np.abs(want).max()), (name, hv, c, err)
+        assert np.abs(aqk[L:]).max(initial=0) == 0 and np.abs(w[L:]).max(initial=0) == 0
