@@ -49,8 +49,10 @@ def test_abi_version(lib):
 
 
 def _rec_bytes(K, V, elem):
-    # w, qg, kg^T in the compute type; u fp32; Aqk (plus its bf16 residual); 2^G fp32
-    b = 64 * K * elem * 3 + 64 * V * 4 + 64 * 64 * elem * (2 if elem == 2 else 1) + 4 * K
+    # w in the compute type; qg, kg^T and Aqk each with a bf16 residual tile on the bf16
+    # path; u and 2^G in fp32
+    ns = 2 if elem == 2 else 1
+    b = 64 * K * elem + ns * (2 * 64 * K * elem + 64 * 64 * elem) + 64 * V * 4 + 4 * K
     return (b + 255) // 256 * 256
 
 
