@@ -1,9 +1,9 @@
 // Chunked KDA forward for gfx950: the chunk algebra of "kernel-fun 0.2.0.dev1 sdist",
 // ALGORITHM.md, section Forward, in three kernels.
 //
-//  sched   (packed mode only, one block) validates the int32 offsets per slot and lays
-//          out the chunks: each slot is cut into 64-row chunks starting at its first
-//          row, the last one short.
+//  sched   (one block) validates the int32 offsets per slot (packed mode) and lays out
+//          the chunks: each sequence is cut into 64-row chunks starting at its first
+//          row, the last one short; dense mode is N = B sequences of T rows.
 //  intra   one block per (chunk, value head): Stage 1 (chunk-local cumsum of the log2
 //          gate) and Stage 2 (Aqk, the WY inverse (I + L)^-1 with beta in L, and
 //          w, u, qg, kg, 2^G), written as one record per (value head, chunk).
@@ -21,6 +21,8 @@
 // 100 log2 units (2^100 stays far from fp32 overflow), switches that chunk to block-
 // boundary anchors (all factors <= 1: safe at any gate magnitude) for the off-diagonal
 // blocks and an exact one-sided 2^(G_i - G_j) per (i, j, channel) for the diagonal ones.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -32,7 +34,7 @@ constexpr int C = 64;            // chunk rows
 constexpr int NTHREADS = 256;
 constexpr float SPREAD_LIMIT = 100.0f;
 
-// byte offset of the chunk table inside the packed-mode schedule
+// byte offset of the chunk table inside the schedule
 inline size_t sched_table_offset(int N) { return ((size_t)(3 * (size_t)N + 1) * 4 + 15) / 16 * 16; }
 
 __device__ __forceinline__ int xcd_remap(int b, int G) {
@@ -43,7 +45,8 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
 }
 
 // ------------------------------------------------------------------------------------
-// sched: per-slot validation, chunk offsets and the chunk table (packed mode)
+// sched: per-slot validation, chunk offsets and the chunk table (dense mode: N = B
+// sequences of T rows each, all valid)
 // ------------------------------------------------------------------------------------
 // Each slot is checked on its own (0 <= bos <= eos <= T, slot 0 starts at 0). Offsets that
 // decrease always break some slot's check; the slots that pass may then overlap, so the
@@ -67,9 +70,10 @@ __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* __restrict__
         const int n = base + tid;
         int bos = 0, len = 0, cnt = 0, ok = 0;
         if (n < N) {
-            bos = cu[n];
-            const int eos = cu[n + 1];
-            ok = bos >= 0 && bos <= eos && eos <= T && (n != 0 || bos == 0);
+            // dense mode (no offsets): sequence n is row block n*T .. n*T+T-1
+            bos = cu ? cu[n] : n * T;
+            const int eos = cu ? cu[n + 1] : bos + T;
+            ok = cu ? (bos >= 0 && bos <= eos && eos <= T && (n != 0 || bos == 0)) : 1;
             if (ok) {
                 len = eos - bos;
                 cnt = (len + C - 1) / C;
@@ -117,239 +121,324 @@ struct IntraParams {
     const void* v;
     const float* g;
     const void* beta;
-    const int32_t* nchunks;   // packed mode: device chunk count (else NULL)
-    const int2* table;        // packed mode: chunk table
+    const int32_t* nchunks;   // device chunk count (from the schedule)
+    const int2* table;        // chunk table: (first row, rows)
     char* rec;                // record base
     size_t rec_bytes, off_w, off_u, off_qg, off_kgT, off_aqk, off_eg;
     int T, H, HV, NT, NCmax;
     float scale;
 };
 
+// Thread mapping for the elementwise work: thread (cg, rg) owns columns 8cg .. 8cg+7 of
+// rows rg*RPT .. rg*RPT+RPT-1, so every global access is a 16- or 32-byte vector. The
+// Stage 2 products run on fp32 matrix cores (v_mfma_f32_16x16x4_f32) in two K-halves to
+// keep the LDS footprint under 80 KB (two blocks per CU). All record tiles are written
+// in the scan's fragment order.
 template <int K, int V, typename TIn, typename TB>
-__global__ __launch_bounds__(NTHREADS) void intra_kernel(IntraParams p) {
-    typedef TIn TW;                        // intermediate / operand type
-    constexpr int RG = NTHREADS / K;       // row groups of the elementwise mapping
-    constexpr int RPT = C / RG;            // rows per thread (16 or 32)
-    constexpr int RGV = NTHREADS / V;
-    constexpr int RPTV = C / RGV;
-    typedef Tile<TW, 16, K> TQ;            // one 16-row block of q-side / k-row operands
-    typedef Tile<TW, C, K> TKC;            // k-column operands of a block row
+__global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
+    typedef TIn TW;                        // operand type of the record
+    constexpr bool SPLIT = sizeof(TW) == 2;
+    constexpr int CG = K / 8, RG = NTHREADS / CG, RPT = C / RG;
+    constexpr int CGV = V / 8, RGV = NTHREADS / CGV, RPTV = C / RGV;
+    static_assert(RPT >= 1 && RPTV >= 1 && 16 % RPT == 0, "row groups must tile 16-row blocks");
+    constexpr int KH = K / 2;              // Stage 2 contraction half
+    constexpr int LD = C + 1;              // padded fp32 64x64 matrices
+    typedef Tile<float, 16, KH> TQh;       // q-side / k-row operands of one block row
+    typedef Tile<float, C, KH> TKh;        // k-column operands
     typedef Tile<TW, C, C> TB64;           // T beta
     typedef Tile<TW, K, C> TKD;            // (k 2^G)^T
     typedef Tile<TW, V, C> TVT;            // v^T
-    constexpr int LD = C + 1;              // fp32 64x64 matrices, padded rows
-    // bf16 operands carry a second "lo" tile holding what bf16 rounded away
-    constexpr bool SPLIT = sizeof(TW) == 2;
-    constexpr int NSPLIT = SPLIT ? 2 : 1;
+    typedef Tile<TW, C, K> TWS;            // w staging (rows i, columns d)
+    typedef Tile<float, 64, C> TGS;        // kg^T staging, 64 key rows at a time
+    typedef FragTile<TW, C, K> FA;         // w, qg
+    typedef FragTile<TW, C, C> FQ;         // Aqk
+    typedef FragTile<TW, K, C> FG;         // kg^T
+    typedef Mma<TW> MW;
 
-    constexpr int P2_BYTES = NSPLIT * (2 * TQ::BYTES + TKC::BYTES);
+    constexpr int P2_BYTES = 2 * TQh::BYTES + TKh::BYTES + 16 * LD * 4;
     constexpr int P4_BYTES = TB64::BYTES + TKD::BYTES + TVT::BYTES;
-    constexpr int GM_BYTES = C * K * 4;
-    constexpr int XS_BYTES = 3 * 16 * 17 * 4;
+    constexpr int ST_BYTES = TWS::BYTES;
+    static_assert(TGS::BYTES <= C * LD * 4, "kg^T staging must fit in L's and T's space");
+    constexpr int GM_BYTES = 16 * K * 4;
     constexpr int U1 = P2_BYTES > P4_BYTES ? P2_BYTES : P4_BYTES;
-    constexpr int U2 = U1 > GM_BYTES ? U1 : GM_BYTES;
-    constexpr int UNION_BYTES = U2 > XS_BYTES ? U2 : XS_BYTES;
+    constexpr int U2 = U1 > ST_BYTES ? U1 : ST_BYTES;
+    constexpr int UNION_BYTES = U2 > GM_BYTES ? U2 : GM_BYTES;
+    static_assert(RG * K + 12 * K + 4 * K <= C * LD, "phase-1 scratch must fit in T's space");
 
-    __shared__ float gsum[4][128];
-    __shared__ float anch[4][128];
     __shared__ float Lm[C * LD];
-    __shared__ float Tm[C * LD];
+    __shared__ float Tm[C * LD];           // also phase 1-2 scratch: partial sums, key rows
     __shared__ float betas[C];
     __shared__ __attribute__((aligned(16))) char un[UNION_BYTES];
 
-    TW* QH = reinterpret_cast<TW*>(un);
-    TW* KR = reinterpret_cast<TW*>(un + TQ::BYTES);
-    TW* KC = reinterpret_cast<TW*>(un + 2 * TQ::BYTES);
-    TW* QHl = reinterpret_cast<TW*>(un + (2 * TQ::BYTES + TKC::BYTES));
-    TW* KRl = reinterpret_cast<TW*>(un + (3 * TQ::BYTES + TKC::BYTES));
-    TW* KCl = reinterpret_cast<TW*>(un + (4 * TQ::BYTES + TKC::BYTES));
+    float* part = Tm;                      // [RG][K]   per-row-group column sums
+    float* keyrow = Tm + RG * K;           // [4][3][K] Gamma at rows 16I, 16I+8, 16I+15
+    float* QH = reinterpret_cast<float*>(un);
+    float* KR = reinterpret_cast<float*>(un + TQh::BYTES);
+    float* KC = reinterpret_cast<float*>(un + 2 * TQh::BYTES);
+    float* AS = reinterpret_cast<float*>(un + 2 * TQh::BYTES + TKh::BYTES);   // [16][LD]
+    float* GMI = reinterpret_cast<float*>(un);                                  // [16][K]
+    float* Xs = reinterpret_cast<float*>(un);
     TW* TBs = reinterpret_cast<TW*>(un);
     TW* KDt = reinterpret_cast<TW*>(un + TB64::BYTES);
     TW* VTt = reinterpret_cast<TW*>(un + TB64::BYTES + TKD::BYTES);
-    float* GM = reinterpret_cast<float*>(un);
-    float* Xs = reinterpret_cast<float*>(un);
+    TW* WS = reinterpret_cast<TW*>(un);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
     const int G = p.NCmax * p.HV;
     const int item = xcd_remap(blockIdx.x, G);
     const int hv = item % p.HV;
     const int c = item / p.HV;
     const int h = hv / (p.HV / p.H);
 
-    long long rs;   // first row of the chunk in the [B*T] row space
-    int len;
-    if (p.table) {
-        if (c >= p.nchunks[0]) return;
-        const int2 e = p.table[c];
-        rs = e.x;
-        len = e.y;
-    } else {
-        const int b = c / p.NT, ci = c % p.NT;
-        rs = (long long)b * p.T + (long long)ci * C;
-        len = p.T - ci * C < C ? p.T - ci * C : C;
-    }
+    if (c >= p.nchunks[0]) return;
+    const int2 cpos = p.table[c];
+    const long long rs = cpos.x;   // first row of the chunk in the [B*T] row space
+    const int len = cpos.y;
     const TIn* q = reinterpret_cast<const TIn*>(p.q);
     const TIn* k = reinterpret_cast<const TIn*>(p.k);
     const TIn* v = reinterpret_cast<const TIn*>(p.v);
     const TB* beta = reinterpret_cast<const TB*>(p.beta);
     char* rec = p.rec + ((size_t)hv * p.NCmax + c) * p.rec_bytes;
     TW* out_w = reinterpret_cast<TW*>(rec + p.off_w);
-    float* out_u = reinterpret_cast<float*>(rec + p.off_u);
     TW* out_qg = reinterpret_cast<TW*>(rec + p.off_qg);
     TW* out_kgT = reinterpret_cast<TW*>(rec + p.off_kgT);
     TW* out_aqk = reinterpret_cast<TW*>(rec + p.off_aqk);
-    TW* out_aqk_lo = out_aqk + C * C;             // residual tile (bf16 path)
+    float* out_u = reinterpret_cast<float*>(rec + p.off_u);
     float* out_eg = reinterpret_cast<float*>(rec + p.off_eg);
-    auto put_aqk = [&](int idx, float val) {
-        const TW hi = from_f32<TW>(val);
-        out_aqk[idx] = hi;
-        if constexpr (SPLIT) out_aqk_lo[idx] = from_f32<TW>(val - to_f32(hi));
-    };
-    auto put_split = [&](TW* hi_t, TW* lo_t, int idx, float val) {
-        const TW hi = from_f32<TW>(val);
+
+    // write x as hi (and lo = x - hi on the bf16 path) at element idx of two tiles
+    auto put_split = [&](TW* hi_t, TW* lo_t, int idx, float x) {
+        const TW hi = from_f32<TW>(x);
         hi_t[idx] = hi;
-        if constexpr (SPLIT) lo_t[idx] = from_f32<TW>(val - to_f32(hi));
+        if constexpr (SPLIT) lo_t[idx] = from_f32<TW>(x - to_f32(hi));
+    };
+    // 8 consecutive fp32 values -> one bf16 fragment lane (hi and lo, 16 bytes each)
+    auto put_split8 = [&](TW* hi_t, TW* lo_t, int idx, const float* x) {
+        if constexpr (SPLIT) {
+            bf16x8 hv8, lv8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                hv8[e] = (__bf16)x[e];
+                lv8[e] = (__bf16)(x[e] - (float)hv8[e]);
+            }
+            *reinterpret_cast<bf16x8*>(hi_t + idx) = hv8;
+            *reinterpret_cast<bf16x8*>(lo_t + idx) = lv8;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hi_t[idx + e] = from_f32<TW>(x[e]);
+        }
+    };
+    auto load8 = [&](const TIn* src, float* dst) {
+        if constexpr (SPLIT) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(src);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = (float)x[e];
+        } else {
+            const f32x4 a = reinterpret_cast<const f32x4*>(src)[0];
+            const f32x4 b = reinterpret_cast<const f32x4*>(src)[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { dst[e] = a[e]; dst[4 + e] = b[e]; }
+        }
     };
 
-    // ---- phase 0: clear L and T, stage beta ----
-    for (int i = tid; i < C * LD; i += NTHREADS) {
-        Lm[i] = 0.f;
-        Tm[i] = 0.f;
-    }
+    // ---- phase 0: clear L, stage beta ----
+    for (int i = tid; i < C * LD; i += NTHREADS) Lm[i] = 0.f;
     if (tid < C) betas[tid] = tid < len ? to_f32(beta[(size_t)(rs + tid) * p.HV + hv]) : 0.f;
 
-    // ---- phase 1 (Stage 1): chunk-local cumsum of the log2 gate, column d per thread ----
-    const int d = tid % K;
-    const int rg = tid / K;
-    const int i0 = rg * RPT;
-    float gam[RPT], kk[RPT], qq[RPT];
+    // ---- phase 1 (Stage 1): loads and the chunk-local cumsum of the log2 gate ----
+    const int cg = tid % CG, rg = tid / CG;
+    const int d0 = 8 * cg, i0 = rg * RPT;
+    // q and k stay in their input type in registers (bf16: 4 registers per 8 values)
+    typedef typename std::conditional<SPLIT, bf16x8, f32x8>::type Row8;
+    float gm[RPT][8];
+    Row8 qv[RPT], kv[RPT];
 #pragma unroll
     for (int ii = 0; ii < RPT; ++ii) {
         const int i = i0 + ii;
-        float gv = 0.f, kv = 0.f, qv = 0.f;
         if (i < len) {
             const size_t r = (size_t)(rs + i);
-            gv = p.g[(r * p.HV + hv) * K + d];
-            kv = to_f32(k[(r * p.H + h) * K + d]);
-            qv = to_f32(q[(r * p.H + h) * K + d]);
+            const f32x4* gp = reinterpret_cast<const f32x4*>(p.g + (r * p.HV + hv) * K + d0);
+            const f32x4 g0 = gp[0], g1 = gp[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { gm[ii][e] = g0[e]; gm[ii][4 + e] = g1[e]; }
+            qv[ii] = *reinterpret_cast<const Row8*>(q + (r * p.H + h) * K + d0);
+            kv[ii] = *reinterpret_cast<const Row8*>(k + (r * p.H + h) * K + d0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { gm[ii][e] = 0.f; qv[ii][e] = from_f32<TIn>(0.f); kv[ii][e] = from_f32<TIn>(0.f); }
         }
-        gam[ii] = gv;
-        kk[ii] = kv;
-        qq[ii] = qv;
     }
 #pragma unroll
-    for (int ii = 1; ii < RPT; ++ii) gam[ii] += gam[ii - 1];
-    gsum[rg][d] = gam[RPT - 1];
-    __syncthreads();
-    float pre = 0.f, Gd = 0.f;
+    for (int ii = 1; ii < RPT; ++ii)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gm[ii][e] += gm[ii - 1][e];
+#pragma unroll
+    for (int e = 0; e < 8; e += 4)
+        *reinterpret_cast<f32x4*>(part + rg * K + d0 + e) = f32x4{gm[RPT - 1][e], gm[RPT - 1][e + 1], gm[RPT - 1][e + 2], gm[RPT - 1][e + 3]};
+    lds_barrier();
+    float pre[8], Gd[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { pre[e] = 0.f; Gd[e] = 0.f; }
+#pragma unroll 2
     for (int r2 = 0; r2 < RG; ++r2) {
-        if (r2 < rg) pre += gsum[r2][d];
-        Gd += gsum[r2][d];
+        const f32x4 a = *reinterpret_cast<const f32x4*>(part + r2 * K + d0);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(part + r2 * K + d0 + 4);
+        const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (r2 < rg) pre[e] += x[e];
+            Gd[e] += x[e];
+        }
     }
 #pragma unroll
-    for (int ii = 0; ii < RPT; ++ii) gam[ii] += pre;
-
-    // anchors: midpoint of each 16-row block unless a half-block spans too much decay
+    for (int ii = 0; ii < RPT; ++ii)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gm[ii][e] += pre[e];
+    // Gamma at each 16-row block's first, middle and last rows
+#pragma unroll
+    for (int ii = 0; ii < RPT; ++ii) {
+        const int i = i0 + ii, o16 = i & 15;
+        const int which = o16 == 0 ? 0 : (o16 == 8 ? 1 : (o16 == 15 ? 2 : -1));
+        if (which >= 0) {
+            float* dst = keyrow + ((i >> 4) * 3 + which) * K + d0;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{gm[ii][0], gm[ii][1], gm[ii][2], gm[ii][3]};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{gm[ii][4], gm[ii][5], gm[ii][6], gm[ii][7]};
+        }
+    }
+    lds_barrier();
+    // midpoint anchors unless some half-block spans more decay than SPREAD_LIMIT
     int wide = 0;
-#pragma unroll
-    for (int bl = 0; bl < RPT / 16; ++bl) {
-        const float s0 = gam[bl * 16], sm = gam[bl * 16 + 8], s1 = gam[bl * 16 + 15];
-        wide |= (s0 - sm > SPREAD_LIMIT) || (sm - s1 > SPREAD_LIMIT);
-    }
+#pragma unroll 1
+    for (int I = 0; I < 4; ++I)
+#pragma unroll 2
+        for (int e = 0; e < 8; ++e) {
+            const float s0 = keyrow[(I * 3 + 0) * K + d0 + e];
+            const float sm = keyrow[(I * 3 + 1) * K + d0 + e];
+            const float s1 = keyrow[(I * 3 + 2) * K + d0 + e];
+            wide |= (s0 - sm > SPREAD_LIMIT) || (sm - s1 > SPREAD_LIMIT);
+        }
     const bool exact_diag = block_any(wide) != 0;
-#pragma unroll
-    for (int bl = 0; bl < RPT / 16; ++bl) {
-        const int I = (i0 >> 4) + bl;
-        anch[I][d] = exact_diag ? gam[bl * 16] : gam[bl * 16 + 8];
-    }
-    __syncthreads();
+    const int anchor_slot = exact_diag ? 0 : 1;
 
-    // ---- phase 2 (Stage 2, products): Aqk and L block rows ----
-    const int lr = lane & 15;          // accumulator column
-    const int lq = lane >> 4;          // accumulator row quad
+    // ---- phase 2 (Stage 2 products): Aqk and L, one 16-row block row at a time ----
+#pragma unroll 1
     for (int I = 0; I < 4; ++I) {
-        const float am = anch[I][d];
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 1
+        for (int hh = 0; hh < 2; ++hh) {
+            if (d0 >= hh * KH && d0 < (hh + 1) * KH) {
+                const int dd = d0 - hh * KH;
+                const float* am = keyrow + (I * 3 + anchor_slot) * K + d0;
 #pragma unroll
-        for (int ii = 0; ii < RPT; ++ii) {
-            const int i = i0 + ii;
-            if ((i >> 4) == I) {
-                const float f = exp2_fast(gam[ii] - am);
-                put_split(QH, QHl, TQ::idx(i - 16 * I, d), qq[ii] * f);
-                put_split(KR, KRl, TQ::idx(i - 16 * I, d), kk[ii] * f);
+                for (int ii = 0; ii < RPT; ++ii) {
+                    const int i = i0 + ii, blk = i >> 4;
+                    if (blk == I) {
+                        float fq[8], fk[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float f = exp2_fast(gm[ii][e] - am[e]);
+                            fq[e] = to_f32(qv[ii][e]) * f;
+                            fk[e] = to_f32(kv[ii][e]) * f;
+                        }
+                        float* dq = QH + TQh::idx(i - 16 * I, dd);
+                        float* dk = KR + TQh::idx(i - 16 * I, dd);
+                        *reinterpret_cast<f32x4*>(dq) = f32x4{fq[0], fq[1], fq[2], fq[3]};
+                        *reinterpret_cast<f32x4*>(QH + TQh::idx(i - 16 * I, dd + 4)) = f32x4{fq[4], fq[5], fq[6], fq[7]};
+                        *reinterpret_cast<f32x4*>(dk) = f32x4{fk[0], fk[1], fk[2], fk[3]};
+                        *reinterpret_cast<f32x4*>(KR + TQh::idx(i - 16 * I, dd + 4)) = f32x4{fk[4], fk[5], fk[6], fk[7]};
+                    }
+                    if (blk <= I) {
+                        float fc[8];
+                        const bool zero = exact_diag && blk == I;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) fc[e] = zero ? 0.f : to_f32(kv[ii][e]) * exp2_fast(am[e] - gm[ii][e]);
+                        *reinterpret_cast<f32x4*>(KC + TKh::idx(i, dd)) = f32x4{fc[0], fc[1], fc[2], fc[3]};
+                        *reinterpret_cast<f32x4*>(KC + TKh::idx(i, dd + 4)) = f32x4{fc[4], fc[5], fc[6], fc[7]};
+                    }
+                }
             }
-            if ((i >> 4) <= I) {
-                float kc = 0.f;
-                if (!(exact_diag && (i >> 4) == I)) kc = kk[ii] * exp2_fast(am - gam[ii]);
-                put_split(KC, KCl, TKC::idx(i, d), kc);
+            if (hh == 0)
+                for (int e = tid; e < 16 * LD; e += NTHREADS) AS[e] = 0.f;
+            lds_barrier();
+            // tiles (I, J) for J <= I: even tt = Aqk, odd tt = L; wave w takes tt = w, w+4
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const int tt = wave + 4 * a;
+                const int J = tt >> 1;
+                if (J <= I && !(exact_diag && J == I))
+                    acc[a] = tile_mma<float, TQh, TKh>(acc[a], (tt & 1) ? KR : QH, 0, KC, 16 * J, 0, KH, lane);
             }
+            lds_barrier();
         }
-        __syncthreads();
-        const int ntile = 2 * (I + 1);
-        for (int tt = wave; tt < ntile; tt += 4) {
+        // results: Aqk rows of block I -> AS (scaled, masked); L -> Lm (beta_i, strictly lower)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int tt = wave + 4 * a;
             const int J = tt >> 1;
-            const bool is_qk = (tt & 1) == 0;
-            if (exact_diag && J == I) continue;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = tile_mma<TW, TQ, TKC>(acc, is_qk ? QH : KR, 0, KC, 16 * J, 0, K, lane);
+            if (J <= I && !(exact_diag && J == I)) {
+                const int j = 16 * J + lr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ir = 4 * lq + r, i = 16 * I + ir;
+                    if (tt & 1) Lm[i * LD + j] = i > j ? betas[i] * acc[a][r] : 0.f;
+                    else AS[ir * LD + j] = i >= j ? p.scale * acc[a][r] : 0.f;
+                }
+            }
+        }
+        if (exact_diag) {
+            // diagonal block: one-sided 2^(G_i - G_j) per (i, j, channel), no anchor
+            lds_barrier();
+#pragma unroll
+            for (int ii = 0; ii < RPT; ++ii) {
+                const int i = i0 + ii;
+                if ((i >> 4) == I) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) GMI[(i - 16 * I) * K + d0 + e] = gm[ii][e];
+                }
+            }
+            lds_barrier();
+            {
+                const int ri = tid >> 4, rj = tid & 15;
+                const int i = 16 * I + ri, j = 16 * I + rj;
+                if (rj <= ri && i < len) {
+                    const size_t r_i = (size_t)(rs + i), r_j = (size_t)(rs + j);
+                    float aq = 0.f, ak = 0.f;
+                    for (int dd = 0; dd < K; ++dd) {
+                        const float f = exp2_fast(GMI[ri * K + dd] - GMI[rj * K + dd]);
+                        const float kj = to_f32(k[(r_j * p.H + h) * K + dd]) * f;
+                        aq = fmaf(to_f32(q[(r_i * p.H + h) * K + dd]), kj, aq);
+                        ak = fmaf(to_f32(k[(r_i * p.H + h) * K + dd]), kj, ak);
+                    }
+                    AS[ri * LD + j] = p.scale * aq;
+                    if (i > j) Lm[i * LD + j] = betas[i] * ak;
+                }
+            }
+        }
+        lds_barrier();
+        // Aqk block row I -> record (fragment order, hi and lo)
+        for (int t = tid; t < 64 * FQ::NS; t += NTHREADS) {
+            const int st = t >> 6, l = t & 63;
+            const int row = l & 15, col = st * MW::KS + (l >> 4) * MW::KPL;
+            const int o = FQ::frag(I, st, l);
             if constexpr (SPLIT) {
-                f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
-                acc2 = tile_mma<TW, TQ, TKC>(acc2, is_qk ? QHl : KRl, 0, KC, 16 * J, 0, K, lane);
-                acc2 = tile_mma<TW, TQ, TKC>(acc2, is_qk ? QH : KR, 0, KCl, 16 * J, 0, K, lane);
-                acc += acc2;
-            }
-            const int j = 16 * J + lr;
+                float x[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * I + 4 * lq + r;
-                if (is_qk) {
-                    const float val = i >= j ? p.scale * acc[r] : 0.f;
-                    put_aqk(i * C + j, val);
-                } else {
-                    Lm[i * LD + j] = i > j ? betas[i] * acc[r] : 0.f;
-                }
+                for (int e = 0; e < 8; ++e) x[e] = AS[row * LD + col + e];
+                put_split8(out_aqk, out_aqk + C * C, o, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < MW::KPL; ++e) out_aqk[o + e] = from_f32<TW>(AS[row * LD + col + e]);
             }
         }
-        __syncthreads();
-    }
-    // zero the upper blocks of Aqk
-    for (int e = tid; e < 6 * 256; e += NTHREADS) {
-        const int bi = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-        const int I = bi < 3 ? 0 : (bi < 5 ? 1 : 2);
-        const int J = bi < 3 ? bi + 1 : (bi < 5 ? bi - 1 : 3);
-        put_aqk((16 * I + rr) * C + 16 * J + cc, 0.f);
+        lds_barrier();
     }
 
-    // ---- phase 2b: exact diagonal blocks when the decay is too steep for an anchor ----
-    if (exact_diag) {
-#pragma unroll
-        for (int ii = 0; ii < RPT; ++ii) GM[(i0 + ii) * K + d] = gam[ii];
-        __syncthreads();
-        for (int e = tid; e < 4 * 256; e += NTHREADS) {
-            const int I = e >> 8, ri = (e >> 4) & 15, rj = e & 15;
-            const int i = 16 * I + ri, j = 16 * I + rj;
-            if (rj > ri) {   // above the diagonal: Aqk is zero there
-                put_aqk(i * C + j, 0.f);
-                continue;
-            }
-            float aq = 0.f, ak = 0.f;
-            if (i < len) {
-                const size_t r_i = (size_t)(rs + i), r_j = (size_t)(rs + j);
-                for (int dd = 0; dd < K; ++dd) {
-                    const float f = exp2_fast(GM[i * K + dd] - GM[j * K + dd]);
-                    const float kj = to_f32(k[(r_j * p.H + h) * K + dd]) * f;
-                    aq = fmaf(to_f32(q[(r_i * p.H + h) * K + dd]), kj, aq);
-                    ak = fmaf(to_f32(k[(r_i * p.H + h) * K + dd]), kj, ak);
-                }
-            }
-            put_aqk(i * C + j, p.scale * aq);
-            if (i > j) Lm[i * LD + j] = betas[i] * ak;
-        }
-        __syncthreads();
-    }
-
-    // ---- phase 3: T = (I + L)^-1 by blocks ----
+    // ---- phase 3: T = (I + L)^-1 by blocks (Tm's scratch use is over) ----
+    for (int i = tid; i < C * LD; i += NTHREADS) Tm[i] = 0.f;
+    lds_barrier();
     if (wave == 0) {
         const int I = lane >> 4, cc = lane & 15;
         float x[16];
@@ -363,7 +452,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(IntraParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) Tm[(16 * I + i) * LD + 16 * I + cc] = x[i];
     }
-    __syncthreads();
+    lds_barrier();
     for (int lev = 1; lev < 4; ++lev) {
         const int nb = 4 - lev;
         for (int e = tid; e < nb * 256; e += NTHREADS) {
@@ -376,7 +465,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(IntraParams p) {
                     x = fmaf(Lm[(16 * I + rr) * LD + 16 * M + m], Tm[(16 * M + m) * LD + 16 * J + cc], x);
             Xs[(bi * 16 + rr) * 17 + cc] = x;
         }
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < nb * 256; e += NTHREADS) {
             const int bi = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
             const int I = lev + bi, J = I - lev;
@@ -386,54 +475,115 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(IntraParams p) {
                 t = fmaf(Tm[(16 * I + rr) * LD + 16 * I + m], Xs[(bi * 16 + m) * 17 + cc], t);
             Tm[(16 * I + rr) * LD + 16 * J + cc] = -t;
         }
-        __syncthreads();
+        lds_barrier();
     }
 
-    // ---- phase 4: operands of w and u, and the elementwise outputs ----
+    // ---- phase 4: T beta, (k 2^G)^T, v^T in LDS; qg and 2^G straight to the record;
+    //      kg^T staged in the space of L and T once T beta is built ----
     for (int e = tid; e < C * C; e += NTHREADS) {
         const int i = e / C, j = e % C;
         TBs[TB64::idx(i, j)] = from_f32<TW>(Tm[i * LD + j] * betas[j]);
     }
+    lds_barrier();
+    float* GS0 = Lm;   // kg^T rows 0..63   (Tile<float, 64, 64>, fits in 64 x 65 floats)
+    float* GS1 = Tm;   // kg^T rows 64..127 (K = 128)
 #pragma unroll
     for (int ii = 0; ii < RPT; ++ii) {
         const int i = i0 + ii;
-        const float e = exp2_fast(gam[ii]);
-        KDt[TKD::idx(d, i)] = from_f32<TW>(kk[ii] * e);
-        put_split(out_qg, out_qg + C * K, i * K + d, p.scale * qq[ii] * e);
-        put_split(out_kgT, out_kgT + K * C, d * C + i, kk[ii] * exp2_fast(Gd - gam[ii]));
-    }
-    if (rg == 0) out_eg[d] = exp2_fast(Gd);
-    {
-        const int cv = tid % V;
-        const int i1 = (tid / V) * RPTV;
-#pragma unroll 4
-        for (int ii = 0; ii < RPTV; ++ii) {
-            const int i = i1 + ii;
-            float vv = 0.f;
-            if (i < len) vv = to_f32(v[((size_t)(rs + i) * p.HV + hv) * V + cv]);
-            VTt[TVT::idx(cv, i)] = from_f32<TW>(vv);
+        float qo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ex = exp2_fast(gm[ii][e]);
+            const float kf = to_f32(kv[ii][e]);
+            KDt[TKD::idx(d0 + e, i)] = from_f32<TW>(kf * ex);
+            qo[e] = p.scale * to_f32(qv[ii][e]) * ex;
+            const int dk = d0 + e;
+            (dk < 64 ? GS0 : GS1)[TGS::idx(dk & 63, i)] = kf * exp2_fast(Gd[e] - gm[ii][e]);
+        }
+        if constexpr (SPLIT) {
+            put_split8(out_qg, out_qg + C * K, FA::idx(i, d0), qo);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out_qg[FA::idx(i, d0 + e)] = from_f32<TW>(qo[e]);
         }
     }
-    __syncthreads();
+    if (rg == 0) {
+        *reinterpret_cast<f32x4*>(out_eg + d0) = f32x4{exp2_fast(Gd[0]), exp2_fast(Gd[1]), exp2_fast(Gd[2]), exp2_fast(Gd[3])};
+        *reinterpret_cast<f32x4*>(out_eg + d0 + 4) = f32x4{exp2_fast(Gd[4]), exp2_fast(Gd[5]), exp2_fast(Gd[6]), exp2_fast(Gd[7])};
+    }
+    {
+        const int cgv = tid % CGV, rgv = tid / CGV;
+        const int c0v = 8 * cgv, j0 = rgv * RPTV;
+#pragma unroll
+        for (int jj = 0; jj < RPTV; ++jj) {
+            const int j = j0 + jj;
+            float vv[8];
+            if (j < len) {
+                load8(v + ((size_t)(rs + j) * p.HV + hv) * V + c0v, vv);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vv[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) VTt[TVT::idx(c0v + e, j)] = from_f32<TW>(vv[e]);
+        }
+    }
+    lds_barrier();
 
-    // w = (T beta) (k 2^G)   [64 x K],   u = (T beta) v   [64 x V]
-    constexpr int NTW = K / 16, NTU = V / 16;
-    for (int tt = wave; tt < 4 * (NTW + NTU); tt += 4) {
-        const int mt = tt % 4;
-        const int nt = tt / 4;
-        const int kend = (16 * mt + 16 + Mma<TW>::KS - 1) / Mma<TW>::KS * Mma<TW>::KS;
+    // u = (T beta) v: wave w owns rows 16w.., stored transposed in accumulator order
+    const int kend = (16 * wave + 16 + MW::KS - 1) / MW::KS * MW::KS;
+    const int k1 = kend < C ? kend : C;
+    for (int nu = 0; nu < V / 16; ++nu) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (nt < NTW) {
-            acc = tile_mma<TW, TB64, TKD>(acc, TBs, 16 * mt, KDt, 16 * nt, 0, kend < C ? kend : C, lane);
+        acc = tile_mma<TW, TB64, TVT>(acc, TBs, 16 * wave, VTt, 16 * nu, 0, k1, lane);
+        *reinterpret_cast<f32x4*>(out_u + AccTile::quad(16 * nu + lr, 16 * wave + 4 * lq)) = acc;
+    }
+    // w = (T beta)(k 2^G): kept in registers until the operand tiles are released
+    f32x4 wacc[K / 16];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                out_w[(16 * mt + 4 * lq + r) * K + 16 * nt + lr] = from_f32<TW>(acc[r]);
-        } else {
-            const int nu = nt - NTW;
-            acc = tile_mma<TW, TB64, TVT>(acc, TBs, 16 * mt, VTt, 16 * nu, 0, kend < C ? kend : C, lane);
+    for (int nt = 0; nt < K / 16; ++nt) {
+        wacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        wacc[nt] = tile_mma<TW, TB64, TKD>(wacc[nt], TBs, 16 * wave, KDt, 16 * nt, 0, k1, lane);
+    }
+    lds_barrier();
+    // stage w (rows i, columns d)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                out_u[(16 * mt + 4 * lq + r) * V + 16 * nu + lr] = acc[r];
+    for (int nt = 0; nt < K / 16; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) WS[TWS::idx(16 * wave + 4 * lq + r, 16 * nt + lr)] = from_f32<TW>(wacc[nt][r]);
+    lds_barrier();
+    for (int half = 0; half < K / 64; ++half) {
+        const float* GS = half ? GS1 : GS0;
+        if (half == 0) {
+            // w: fragment lanes of the record
+            for (int t = tid; t < 4 * FA::NS * 64; t += NTHREADS) {
+                const int blk = t >> 6, l = t & 63;
+                const int b = blk / FA::NS, st = blk % FA::NS;
+                const int row = 16 * b + (l & 15), col = st * MW::KS + (l >> 4) * MW::KPL;
+                const int o = FA::frag(b, st, l);
+                if constexpr (SPLIT) {
+                    *reinterpret_cast<bf16x8*>(out_w + o) = *reinterpret_cast<const bf16x8*>(WS + TWS::idx(row, col));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < MW::KPL; ++e) out_w[o + e] = WS[TWS::idx(row, col + e)];
+                }
+            }
+        }
+        // kg^T rows 64*half .. +63: fragment lanes, hi and lo
+        for (int t = tid; t < 4 * FG::NS * 64; t += NTHREADS) {
+            const int blk = t >> 6, l = t & 63;
+            const int b = blk / FG::NS, st = blk % FG::NS;
+            const int row = 16 * b + (l & 15), col = st * MW::KS + (l >> 4) * MW::KPL;
+            const int o = FG::frag(4 * half + b, st, l);
+            if constexpr (SPLIT) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = GS[TGS::idx(row, col + e)];
+                put_split8(out_kgT, out_kgT + K * C, o, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < MW::KPL; ++e) out_kgT[o + e] = from_f32<TW>(GS[TGS::idx(row, col + e)]);
+            }
         }
     }
 }
@@ -447,91 +597,107 @@ struct ScanParams {
     const float* initial_state;
     float* final_state;
     void* o;
-    const int32_t* coff;     // packed: first chunk of each slot [N]
-    const int32_t* cend;     // packed: one past the last chunk of each slot [N]
-    const int32_t* slot_ok;  // packed: slot validity
-    const int2* table;       // packed: chunk table
+    const int32_t* coff;     // first chunk of each sequence [N]
+    const int32_t* cend;     // one past the last chunk of each sequence [N]
+    const int32_t* slot_ok;  // sequence validity (packed offsets checked per slot)
+    const int2* table;       // chunk table: (first row, rows)
     int N, T, HV, NT, NCmax;
 };
 
-// The chunk records stream through registers: the block issues the global loads of
-// chunk c+1 right after chunk c's record is in LDS and only waits for them one step
-// later, so HBM latency overlaps the serial matrix-core work.
+// Scan design. Each of the four waves owns a 16-row band of the chunk (for v' and o)
+// and K/64 16-row bands of the state (for the state update), so the record operands a
+// wave multiplies (w, qg, Aqk rows of its band; kg^T rows of its state bands; u and
+// 2^G entries) are private to it: they go from the record straight into registers in
+// matrix-core fragment layout, one chunk ahead. Only the operands every wave needs --
+// the state S^T and v'^T, both produced inside the block -- pass through LDS. To cover
+// HBM latency beyond one step, every block also touches the record WARM chunks ahead so
+// it is in L2 when its fragments are loaded.
+constexpr int WARM = 4;
+
 template <int K, int V, int BV, typename TW>
-struct RecordRegs {
-    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+struct ScanFrags {
+    typedef Mma<TW> M;
+    typedef typename M::frag frag;
     static constexpr bool SPLIT = sizeof(TW) == 2;
     static constexpr int NS = SPLIT ? 2 : 1;
-    static constexpr int EPC = 16 / (int)sizeof(TW);
-    static constexpr int CW = C * K / EPC / NTHREADS;        // 16-byte chunks per thread: w, qg, kgT
-    static constexpr int CA = C * C / EPC / NTHREADS;        // Aqk
-    static constexpr int CU = C * BV / 4 / NTHREADS;         // u slice (fp32, 4 per chunk)
-    static_assert(CW * NTHREADS * EPC == C * K, "w tile must split evenly");
-    static_assert(CA * NTHREADS * EPC == C * C, "Aqk tile must split evenly");
-    static_assert(CU * NTHREADS * 4 == C * BV, "u slice must split evenly");
-    u32x4 w[CW], q[NS][CW], g[NS][CW], a[NS][CA];
-    f32x4 u[CU], e;
+    static constexpr int NKS = K / M::KS;    // contraction steps over the key dim
+    static constexpr int NJS = C / M::KS;    // contraction steps over the chunk rows
+    static constexpr int NDT = K / 64;       // state bands per wave
+    static constexpr int NNT = BV / 16;      // 16-column tiles of the slice
+    frag w[NKS];
+    frag q[NS][NKS];
+    frag a[NS][NJS];
+    frag g[NDT][NS][NJS];
+    f32x4 u[NNT];
+    f32x4 e[NDT];
+    int2 pos;   // (first row of the chunk, rows in it)
 };
 
 template <int K, int V, int BV, typename TW>
-__device__ __forceinline__ void fetch_record(RecordRegs<K, V, BV, TW>& R, const char* rec,
-                                             const ScanParams& p, int v0, int tid) {
-    typedef RecordRegs<K, V, BV, TW> RR;
-    typedef typename RR::u32x4 u32x4;
-    const u32x4* gw = reinterpret_cast<const u32x4*>(rec + p.off_w);
-    const u32x4* gq = reinterpret_cast<const u32x4*>(rec + p.off_qg);
-    const u32x4* gg = reinterpret_cast<const u32x4*>(rec + p.off_kgT);
-    const u32x4* ga = reinterpret_cast<const u32x4*>(rec + p.off_aqk);
+__device__ __forceinline__ void load_frags(ScanFrags<K, V, BV, TW>& F, const char* rec,
+                                           const ScanParams& p, int c, int wave, int lr,
+                                           int lq, int v0) {
+    // everything below is straight-line code: the compiler then waits for exactly these
+    // loads when they are used, never for later prefetches
+    F.pos = p.table[c];
+    typedef ScanFrags<K, V, BV, TW> SF;
+    typedef typename SF::frag frag;
+    constexpr int KS = SF::M::KS, KPL = SF::M::KPL;
+    const TW* w = reinterpret_cast<const TW*>(rec + p.off_w);
+    const TW* qg = reinterpret_cast<const TW*>(rec + p.off_qg);
+    const TW* aqk = reinterpret_cast<const TW*>(rec + p.off_aqk);
+    const TW* kgT = reinterpret_cast<const TW*>(rec + p.off_kgT);
+    const float* u = reinterpret_cast<const float*>(rec + p.off_u);
+    const float* eg = reinterpret_cast<const float*>(rec + p.off_eg);
+    // record tiles are in fragment order: one contiguous 64-lane block per (band, step)
+    typedef FragTile<TW, C, K> FA;
+    typedef FragTile<TW, C, C> FQ;
+    typedef FragTile<TW, K, C> FG;
+    const int lane = lr + 16 * lq;
 #pragma unroll
-    for (int j = 0; j < RR::CW; ++j) R.w[j] = gw[tid + j * NTHREADS];
+    for (int kk = 0; kk < SF::NKS; ++kk) {
+        F.w[kk] = *reinterpret_cast<const frag*>(w + FA::frag(wave, kk, lane));
 #pragma unroll
-    for (int sx = 0; sx < RR::NS; ++sx)
-#pragma unroll
-        for (int j = 0; j < RR::CW; ++j) {
-            R.q[sx][j] = gq[sx * RR::CW * NTHREADS + tid + j * NTHREADS];
-            R.g[sx][j] = gg[sx * RR::CW * NTHREADS + tid + j * NTHREADS];
-        }
-#pragma unroll
-    for (int sx = 0; sx < RR::NS; ++sx)
-#pragma unroll
-        for (int j = 0; j < RR::CA; ++j) R.a[sx][j] = ga[sx * RR::CA * NTHREADS + tid + j * NTHREADS];
-    const float* gu = reinterpret_cast<const float*>(rec + p.off_u);
-#pragma unroll
-    for (int j = 0; j < RR::CU; ++j) {
-        const int e = tid + j * NTHREADS;
-        const int row = e / (BV / 4), c4 = e % (BV / 4);
-        R.u[j] = *reinterpret_cast<const f32x4*>(gu + row * V + v0 + 4 * c4);
+        for (int sx = 0; sx < SF::NS; ++sx)
+            F.q[sx][kk] = *reinterpret_cast<const frag*>(qg + (size_t)sx * C * K + FA::frag(wave, kk, lane));
     }
-    if (tid < K / 4) R.e = reinterpret_cast<const f32x4*>(rec + p.off_eg)[tid];
+#pragma unroll
+    for (int jj = 0; jj < SF::NJS; ++jj) {
+#pragma unroll
+        for (int sx = 0; sx < SF::NS; ++sx)
+            F.a[sx][jj] = *reinterpret_cast<const frag*>(aqk + (size_t)sx * C * C + FQ::frag(wave, jj, lane));
+#pragma unroll
+        for (int a = 0; a < SF::NDT; ++a)
+#pragma unroll
+            for (int sx = 0; sx < SF::NS; ++sx)
+                F.g[a][sx][jj] = *reinterpret_cast<const frag*>(kgT + (size_t)sx * K * C + FG::frag(wave + 4 * a, jj, lane));
+    }
+#pragma unroll
+    for (int nt = 0; nt < SF::NNT; ++nt)
+        F.u[nt] = *reinterpret_cast<const f32x4*>(u + AccTile::quad(v0 + 16 * nt + lr, 16 * wave + 4 * lq));
+#pragma unroll
+    for (int a = 0; a < SF::NDT; ++a)
+        F.e[a] = *reinterpret_cast<const f32x4*>(eg + 16 * (wave + 4 * a) + 4 * lq);
 }
 
 template <int K, int V, int BV, typename TIn>
 __global__ __launch_bounds__(NTHREADS) void scan_kernel(ScanParams p) {
     typedef TIn TW;
-    typedef Tile<TW, C, K> TA;       // w, qg   [64][K]
-    typedef Tile<TW, K, C> TG;       // kg^T    [K][64]
-    typedef Tile<TW, C, C> TQK;      // Aqk     [64][64]
+    typedef ScanFrags<K, V, BV, TW> SF;
+    typedef typename SF::frag frag;
+    typedef typename SF::M M;
     typedef Tile<TW, BV, K> TS;      // S^T     [BV][K]
     typedef Tile<TW, BV, C> TV;      // v'^T    [BV][64]
-    typedef RecordRegs<K, V, BV, TW> RR;
-    typedef typename RR::u32x4 u32x4;
-    // bf16 path: the state, v', qg, kg and Aqk operands are each a pair hi + lo of bf16
-    // tiles, lo holding what rounding hi to bf16 lost; products use hi*hi + lo*hi + hi*lo.
-    constexpr bool SPLIT = RR::SPLIT;
-    constexpr int NS = RR::NS;
-    constexpr int EPC = RR::EPC;
+    constexpr bool SPLIT = SF::SPLIT;
+    constexpr int NS = SF::NS;
+    constexpr int NKS = SF::NKS, NJS = SF::NJS, NDT = SF::NDT, NNT = SF::NNT;
+    constexpr int KS = M::KS, KPL = M::KPL;
     constexpr int NVT = V / BV;
-    constexpr int NNT = BV / 16;     // 16-column tiles of the slice
-    constexpr int NDT = K / 64;      // 16-row state tiles per wave (K/16 tiles over 4 waves)
 
-    __shared__ __attribute__((aligned(16))) TW Wt[TA::ELEMS];
-    __shared__ __attribute__((aligned(16))) TW Qt[NS][TA::ELEMS];
-    __shared__ __attribute__((aligned(16))) TW Gt[NS][TG::ELEMS];
-    __shared__ __attribute__((aligned(16))) TW At[NS][TQK::ELEMS];
-    __shared__ __attribute__((aligned(16))) TW St[2][NS][TS::ELEMS];
+    // bf16 path: S, v', qg, kg and Aqk are each a pair hi + lo of bf16 values (lo holds
+    // what rounding hi lost); products are hi*hi + lo*hi + hi*lo.
+    __shared__ __attribute__((aligned(16))) TW St[NS][TS::ELEMS];
     __shared__ __attribute__((aligned(16))) TW Vt[NS][TV::ELEMS];
-    __shared__ __attribute__((aligned(16))) float Ut[C][BV];
-    __shared__ __attribute__((aligned(16))) float eG[K];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -544,19 +710,14 @@ __global__ __launch_bounds__(NTHREADS) void scan_kernel(ScanParams p) {
     const int hv = chain % p.HV;
     const int n = chain / p.HV;
     const int v0 = vt * BV;
+    // Aqk rows 16*wave.. are zero past column 16*wave+15: fewer contraction steps
+    const int njs_w = (16 * wave + 16 + KS - 1) / KS;
 
-    int c0, c1;
-    if (p.table) {
-        if (!p.slot_ok[n]) return;    // malformed offsets: leave this slot untouched
-        c0 = p.coff[n];
-        c1 = p.cend[n];
-    } else {
-        c0 = n * p.NT;
-        c1 = c0 + p.NT;
-    }
+    if (!p.slot_ok[n]) return;    // malformed offsets: leave this slot untouched
+    const int c0 = p.coff[n];
+    const int c1 = p.cend[n];
     auto record = [&](int c) { return p.rec + ((size_t)hv * p.NCmax + c) * p.rec_bytes; };
 
-    // store an accumulator column block (4 rows) as hi (+ lo) into a pair of tiles
     auto put4 = [&](TW* hi, TW* lo, int col, int row0, f32x4 x, auto tile_tag) {
         typedef decltype(tile_tag) TT;
         const int base = TT::idx(col, row0);
@@ -568,10 +729,28 @@ __global__ __launch_bounds__(NTHREADS) void scan_kernel(ScanParams p) {
         }
     };
 
-    RR R;
-    if (c0 < c1) fetch_record<K, V, BV, TW>(R, record(c0), p, v0, tid);
+    // L2 warming: one dword per 128-byte line of a record, spread over the block
+    const int warm_lines = (int)(p.rec_bytes / 128);
+    uint32_t warm_acc = 0;
+    uint32_t warm_val[4] = {0u, 0u, 0u, 0u};
+    auto warm = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) warm_acc ^= warm_val[i];
+        const uint32_t* base = reinterpret_cast<const uint32_t*>(record(c < c1 ? c : c1 - 1));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int line = tid + i * NTHREADS;
+            warm_val[i] = base[(line < warm_lines ? line : 0) * 32];
+        }
+    };
 
-    // state tiles owned by this wave: dt = wave + 4 * a
+    ScanFrags<K, V, BV, TW> F0, F1;
+    if (c0 < c1) {
+        for (int c = c0; c < c0 + WARM; ++c) warm(c);
+        load_frags<K, V, BV, TW>(F0, record(c0), p, c0, wave, lr, lq, v0);
+    }
+
+    // state bands owned by this wave: dt = wave + 4 * a
     f32x4 S[NDT][NNT];
     const size_t sbase = ((size_t)n * p.HV + hv) * (size_t)K * V;
     if (p.initial_state) {
@@ -590,123 +769,122 @@ __global__ __launch_bounds__(NTHREADS) void scan_kernel(ScanParams p) {
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt) S[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    int cur = 0;
 #pragma unroll
     for (int a = 0; a < NDT; ++a)
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt)
-            put4(St[0][0], St[0][NS - 1], 16 * nt + lr, 16 * (wave + 4 * a) + 4 * lq, S[a][nt], TS());
+            put4(St[0], St[NS - 1], 16 * nt + lr, 16 * (wave + 4 * a) + 4 * lq, S[a][nt], TS());
+    lds_barrier();
 
     TIn* o = reinterpret_cast<TIn*>(p.o);
-    for (int c = c0; c < c1; ++c) {
-        long long rs;
-        int len;
-        if (p.table) {
-            const int2 e = p.table[c];
-            rs = e.x;
-            len = e.y;
-        } else {
-            const int ci = c - c0;
-            rs = (long long)n * p.T + (long long)ci * C;
-            len = p.T - ci * C < C ? p.T - ci * C : C;
-        }
-        // ---- commit the prefetched record of chunk c to LDS, start fetching c+1 ----
+    auto step = [&](SF& F) {
+        const long long rs = F.pos.x;
+        const int len = F.pos.y;
+        // S^T fragments (hi, lo) for v' and o
+        frag sb[NNT][NS][NKS];
 #pragma unroll
-        for (int j = 0; j < RR::CW; ++j) {
-            const int e = tid + j * NTHREADS;
-            const int row = e / (K / EPC), col = (e % (K / EPC)) * EPC;
-            *reinterpret_cast<u32x4*>(&Wt[TA::idx(row, col)]) = R.w[j];
+        for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
             for (int sx = 0; sx < NS; ++sx)
-                *reinterpret_cast<u32x4*>(&Qt[sx][TA::idx(row, col)]) = R.q[sx][j];
-            const int grow = e / (C / EPC), gcol = (e % (C / EPC)) * EPC;
 #pragma unroll
-            for (int sx = 0; sx < NS; ++sx)
-                *reinterpret_cast<u32x4*>(&Gt[sx][TG::idx(grow, gcol)]) = R.g[sx][j];
-        }
-#pragma unroll
-        for (int j = 0; j < RR::CA; ++j) {
-            const int e = tid + j * NTHREADS;
-            const int row = e / (C / EPC), col = (e % (C / EPC)) * EPC;
-#pragma unroll
-            for (int sx = 0; sx < NS; ++sx)
-                *reinterpret_cast<u32x4*>(&At[sx][TQK::idx(row, col)]) = R.a[sx][j];
-        }
-#pragma unroll
-        for (int j = 0; j < RR::CU; ++j) {
-            const int e = tid + j * NTHREADS;
-            const int row = e / (BV / 4), c4 = e % (BV / 4);
-            *reinterpret_cast<f32x4*>(&Ut[row][4 * c4]) = R.u[j];
-        }
-        if (tid < K / 4) *reinterpret_cast<f32x4*>(&eG[4 * tid]) = R.e;
-        __syncthreads();
-        if (c + 1 < c1) fetch_record<K, V, BV, TW>(R, record(c + 1), p, v0, tid);
-
-        // ---- v' = u - w S ----
-        const TW* Sh = St[cur][0];
-        const TW* Sl = St[cur][NS - 1];
+                for (int kk = 0; kk < NKS; ++kk)
+                    sb[nt][sx][kk] = TS::frag(St[sx], 16 * nt + lr, kk * KS + lq * KPL);
+        // v' = u - w S
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = tile_mma<TW, TA, TS>(acc, Wt, 16 * wave, Sh, 16 * nt, 0, K, lane);
-            if constexpr (SPLIT) acc = tile_mma<TW, TA, TS>(acc, Wt, 16 * wave, Sl, 16 * nt, 0, K, lane);
+#pragma unroll
+            for (int kk = 0; kk < NKS; ++kk) {
+                acc = M::mma(F.w[kk], sb[nt][0][kk], acc);
+                if constexpr (SPLIT) acc = M::mma(F.w[kk], sb[nt][1][kk], acc);
+            }
             f32x4 vn;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vn[r] = Ut[16 * wave + 4 * lq + r][16 * nt + lr] - acc[r];
+            for (int r = 0; r < 4; ++r) vn[r] = F.u[nt][r] - acc[r];
             put4(Vt[0], Vt[NS - 1], 16 * nt + lr, 16 * wave + 4 * lq, vn, TV());
         }
-        __syncthreads();
-
-        // ---- o = qg S + Aqk v'  (rows 16*wave ..) ----
-        {
-            const int kend = (16 * wave + 16 + Mma<TW>::KS - 1) / Mma<TW>::KS * Mma<TW>::KS;
-            const int k1 = kend < C ? kend : C;
+        lds_barrier();
+        frag vb[NNT][NS][NJS];
 #pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = tile_mma<TW, TA, TS>(acc, Qt[0], 16 * wave, Sh, 16 * nt, 0, K, lane);
-                acc = tile_mma<TW, TQK, TV>(acc, At[0], 16 * wave, Vt[0], 16 * nt, 0, k1, lane);
+        for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+            for (int sx = 0; sx < NS; ++sx)
+#pragma unroll
+                for (int jj = 0; jj < NJS; ++jj)
+                    vb[nt][sx][jj] = TV::frag(Vt[sx], 16 * nt + lr, jj * KS + lq * KPL);
+        // o = qg S + Aqk v'
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NKS; ++kk) {
+                acc = M::mma(F.q[0][kk], sb[nt][0][kk], acc);
                 if constexpr (SPLIT) {
-                    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
-                    acc2 = tile_mma<TW, TA, TS>(acc2, Qt[NS - 1], 16 * wave, Sh, 16 * nt, 0, K, lane);
-                    acc2 = tile_mma<TW, TA, TS>(acc2, Qt[0], 16 * wave, Sl, 16 * nt, 0, K, lane);
-                    acc2 = tile_mma<TW, TQK, TV>(acc2, At[NS - 1], 16 * wave, Vt[0], 16 * nt, 0, k1, lane);
-                    acc2 = tile_mma<TW, TQK, TV>(acc2, At[0], 16 * wave, Vt[NS - 1], 16 * nt, 0, k1, lane);
-                    acc += acc2;
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * wave + 4 * lq + r;
-                    if (i < len)
-                        o[((size_t)(rs + i) * p.HV + hv) * V + v0 + 16 * nt + lr] = from_f32<TIn>(acc[r]);
+                    acc2 = M::mma(F.q[1][kk], sb[nt][0][kk], acc2);
+                    acc2 = M::mma(F.q[0][kk], sb[nt][1][kk], acc2);
                 }
             }
+#pragma unroll
+            for (int jj = 0; jj < NJS; ++jj) {
+                if (jj < njs_w) {
+                    acc = M::mma(F.a[0][jj], vb[nt][0][jj], acc);
+                    if constexpr (SPLIT) {
+                        acc2 = M::mma(F.a[1][jj], vb[nt][0][jj], acc2);
+                        acc2 = M::mma(F.a[0][jj], vb[nt][1][jj], acc2);
+                    }
+                }
+            }
+            acc += acc2;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * wave + 4 * lq + r;
+                if (i < len)
+                    o[((size_t)(rs + i) * p.HV + hv) * V + v0 + 16 * nt + lr] = from_f32<TIn>(acc[r]);
+            }
         }
-
-        // ---- S = 2^G S + kg^T v' ----
-        const int nxt = cur ^ 1;
+        // S = 2^G S + kg^T v'
 #pragma unroll
         for (int a = 0; a < NDT; ++a) {
             const int dt = wave + 4 * a;
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt) {
                 f32x4 acc = S[a][nt];
+                f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] *= eG[16 * dt + 4 * lq + r];
-                acc = tile_mma<TW, TG, TV>(acc, Gt[0], 16 * dt, Vt[0], 16 * nt, 0, C, lane);
-                if constexpr (SPLIT) {
-                    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
-                    acc2 = tile_mma<TW, TG, TV>(acc2, Gt[NS - 1], 16 * dt, Vt[0], 16 * nt, 0, C, lane);
-                    acc2 = tile_mma<TW, TG, TV>(acc2, Gt[0], 16 * dt, Vt[NS - 1], 16 * nt, 0, C, lane);
-                    acc += acc2;
+                for (int r = 0; r < 4; ++r) acc[r] *= F.e[a][r];
+#pragma unroll
+                for (int jj = 0; jj < NJS; ++jj) {
+                    acc = M::mma(F.g[a][0][jj], vb[nt][0][jj], acc);
+                    if constexpr (SPLIT) {
+                        acc2 = M::mma(F.g[a][1][jj], vb[nt][0][jj], acc2);
+                        acc2 = M::mma(F.g[a][0][jj], vb[nt][1][jj], acc2);
+                    }
                 }
+                acc += acc2;
                 S[a][nt] = acc;
-                put4(St[nxt][0], St[nxt][NS - 1], 16 * nt + lr, 16 * dt + 4 * lq, acc, TS());
+                put4(St[0], St[NS - 1], 16 * nt + lr, 16 * dt + 4 * lq, acc, TS());
             }
         }
-        cur = nxt;
-        __syncthreads();
+        lds_barrier();
+    };
+
+    // two chunks per trip so the prefetch buffers alternate without register copies;
+    // past the end the prefetch re-reads the last chunk (in bounds, unused)
+    for (int c = c0; c < c1; c += 2) {
+        const int c_1 = c + 1 < c1 ? c + 1 : c1 - 1;
+        load_frags<K, V, BV, TW>(F1, record(c_1), p, c_1, wave, lr, lq, v0);
+        warm(c + WARM);
+        step(F0);
+        if (c + 1 >= c1) break;
+        const int c_2 = c + 2 < c1 ? c + 2 : c1 - 1;
+        load_frags<K, V, BV, TW>(F0, record(c_2), p, c_2, wave, lr, lq, v0);
+        warm(c + 1 + WARM);
+        step(F1);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) warm_acc ^= warm_val[i];
+    if (p.NCmax < 0) o[0] = from_f32<TIn>((float)warm_acc);   // never true: keeps the warming loads
 
     if (p.final_state) {
 #pragma unroll
@@ -732,15 +910,14 @@ hipError_t launch_scan(const ChunkArgs& a, const ScanParams& sp);
 template <int K, int V, typename TIn, typename TB>
 hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     char* ws = reinterpret_cast<char*>(a.workspace);
-    const bool packed = a.cu_seqlens != nullptr;
-    const int NT = packed ? 0 : (a.T + C - 1) / C;
+    const int NT = 0;   // chunk positions always come from the schedule
     int32_t *coff = nullptr, *cend = nullptr, *slot_ok = nullptr, *nch = nullptr;
     int2* table = nullptr;
     if (a.events) {
         hipError_t err = hipEventRecord(a.events[0], a.stream);
         if (err != hipSuccess) return err;
     }
-    if (packed) {
+    {
         coff = reinterpret_cast<int32_t*>(ws);
         cend = coff + a.N;
         slot_ok = cend + a.N;
@@ -824,6 +1001,7 @@ bool chunk_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qk
         L.NCmax = T / C + N;
     } else {
         L.NCmax = B * ((T + C - 1) / C);
+        N = B;
     }
     L.elem = qkv_dtype == KDA_BF16 ? 2 : 4;
     // bf16 path: qg, kg^T and Aqk carry a second tile with their bf16 rounding residual
@@ -833,11 +1011,10 @@ bool chunk_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qk
     L.off_qg = off;  off += ns * C * K * L.elem;
     L.off_kgT = off; off += ns * K * C * L.elem;
     L.off_aqk = off; off += ns * C * C * L.elem;
-    L.off_u = off;   off += (size_t)C * V * 4;        // u stays fp32 (used outside the MFMAs)
+    L.off_u = off;   off += (size_t)C * V * 4;        // u^T [V][64], fp32 (used outside the MFMAs)
     L.off_eg = off;  off += (size_t)K * 4;
     L.rec_bytes = align256(off);
-    L.sched_bytes = 0;
-    if (packed) {
+    {
         size_t s = sched_table_offset(N);                      // coff, cend, slot_ok, n_chunks
         s += (size_t)L.NCmax * 8;                              // chunk table
         L.sched_bytes = align256(s);

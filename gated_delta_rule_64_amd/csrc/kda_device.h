@@ -20,6 +20,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
@@ -77,6 +78,37 @@ template <typename TW, int ROWS, int COLS> struct Tile {
     }
 };
 
+// ---------------------------------------------------------------------------------
+// Fragment-order tile in global memory: an R x KC matrix stored as 64-lane blocks, one
+// per (16-row band b, contraction step s), band-major; lane l of block (b, s) holds row
+// 16b + (l % 16), columns s*KS + (l / 16)*KPL .. +KPL contiguously. A wave reads one
+// MFMA operand fragment of a band with one contiguous 64 x 16-byte (bf16) load.
+// ---------------------------------------------------------------------------------
+template <typename TW, int R, int KC> struct FragTile {
+    typedef Mma<TW> M;
+    static constexpr int NS = KC / M::KS;
+    static constexpr int ELEMS = R * KC;
+    static_assert(R % 16 == 0 && KC % M::KS == 0, "whole bands and steps");
+    __device__ __forceinline__ static int idx(int row, int col) {
+        const int b = row >> 4, st = col / M::KS;
+        const int l = (row & 15) + 16 * ((col % M::KS) / M::KPL);
+        return ((b * NS + st) * 64 + l) * M::KPL + (col % M::KPL);
+    }
+    __device__ __forceinline__ static int frag(int b, int st, int lane) {
+        return ((b * NS + st) * 64 + lane) * M::KPL;
+    }
+};
+
+// Accumulator-order tile of fp32 values [R][64] read back as four consecutive rows of
+// one column: block (column tile ct = col/16, row band rb = row/16), lane
+// l = (col % 16) + 16 * ((row % 16) / 4) holds rows 16rb + 4(l/16) .. +3 of column
+// 16ct + (l % 16) -- the layout a 16x16 MFMA result has in its four accumulator registers.
+struct AccTile {
+    __device__ __forceinline__ static int quad(int col, int row) {   // offset of the 4-row group
+        return (((col >> 4) * 4 + (row >> 4)) * 64 + (col & 15) + 16 * ((row & 15) >> 2)) * 4;
+    }
+};
+
 // Product of a 16-row band of A (rows a_row0..+15) with a 16-row band of B (rows
 // b_row0..+15) over contraction [k0, k1), accumulated into acc.
 template <typename TW, typename TA, typename TB>
@@ -101,6 +133,16 @@ __device__ __forceinline__ void store_col4(TW* t, int col, int row0, f32x4 v) {
     p[1] = from_f32<TW>(v[1]);
     p[2] = from_f32<TW>(v[2]);
     p[3] = from_f32<TW>(v[3]);
+}
+
+// Barrier for blocks that exchange data only through LDS: the fences are restricted to
+// the LDS address space, so outstanding global loads (prefetches) and stores stay in
+// flight across it (a full __syncthreads() must also drain global stores, and on gfx9
+// one counter covers loads and stores, which would wait for every prefetch too).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Block-wide OR of a flag (256-thread blocks).

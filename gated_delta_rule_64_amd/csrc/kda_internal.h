@@ -47,15 +47,15 @@ struct ChunkArgs {
 };
 
 // Workspace layout of the chunked forward (all offsets 256-byte aligned):
-//   [sched]  packed mode only: int32 first_chunk[N], int32 end_chunk[N],
-//            int32 slot_ok[N], int32 n_chunks[1], int2 chunk_table[NCmax] (row start,
-//            length)
+//   [sched]  int32 first_chunk[N], int32 end_chunk[N], int32 slot_ok[N],
+//            int32 n_chunks[1], int2 chunk_table[NCmax] (first row, rows); dense mode
+//            uses it too (N = B sequences of T rows)
 //   [inter]  per (value head hv, chunk c), one record of the Stage 2 results, in order:
 //              w      [64][K]       element type of the compute path (TW)
 //              qg     [NS][64][K]   TW, scale folded in
 //              kgT    [NS][K][64]   TW, transposed
 //              Aqk    [NS][64][64]  TW, scale folded in, zero above the diagonal
-//              u      [64][V]       fp32
+//              uT     [V][64]       fp32, transposed
 //              eG     [K]           fp32, 2^(chunk's total log2 decay)
 //            NS = 2 on the bf16 path (tile 1 holds x - bf16(x) rounded to bf16, so
 //            hi + lo carries about 16 significant bits), NS = 1 on the fp32 path.
@@ -64,7 +64,7 @@ struct ChunkLayout {
     int NCmax;            // chunk slots (dense: B * ceil(T/64); packed: T/64 + N)
     size_t elem;          // bytes per intermediate element (2 bf16, 4 fp32)
     size_t off_w, off_u, off_qg, off_kgT, off_aqk, off_eg, rec_bytes;
-    size_t sched_bytes;   // bytes of the packed-mode schedule (0 in dense mode)
+    size_t sched_bytes;   // bytes of the chunk schedule
     size_t total;
 };
 

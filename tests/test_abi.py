@@ -56,21 +56,25 @@ def _rec_bytes(K, V, elem):
     return (b + 255) // 256 * 256
 
 
+def _sched_bytes(N, ncmax):
+    # first/end chunk and validity per sequence, chunk count, then the chunk table
+    s = ((3 * N + 1) * 4 + 15) // 16 * 16 + ncmax * 8
+    return (s + 255) // 256 * 256
+
+
 @pytest.mark.parametrize("K,V,dt,elem", [(128, 128, 1, 2), (64, 64, 0, 4), (128, 64, 1, 2)])
 def test_workspace_bytes_dense(lib, K, V, dt, elem):
     B, T, H, HV = 2, 4096 + 17, 4, 8
     nt = (T + 63) // 64
     got = lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, dt)
-    assert got == HV * B * nt * _rec_bytes(K, V, elem)
+    assert got == _sched_bytes(B, B * nt) + HV * B * nt * _rec_bytes(K, V, elem)
 
 
 def test_workspace_bytes_packed(lib):
     N, T, HV = 64, 33000, 16
     got = lib.kda_chunk_fwd_workspace_bytes(1, T, 16, HV, 128, 128, N, 1, 1)
     ncmax = T // 64 + N
-    sched = ((3 * N + 1) * 4 + 15) // 16 * 16 + ncmax * 8
-    sched = (sched + 255) // 256 * 256
-    assert got == sched + HV * ncmax * _rec_bytes(128, 128, 2)
+    assert got == _sched_bytes(N, ncmax) + HV * ncmax * _rec_bytes(128, 128, 2)
 
 
 def test_workspace_bytes_invalid(lib):

@@ -12,7 +12,7 @@ import torch
 import oracle
 from oracle import chunked as chunked_ref
 from gated_delta_rule_64_amd import inputs
-from tests.util import check, log, to64, to_device, valid_rows
+from tests.util import acc_tile_index, check, frag_tile_index, log, to64, to_device, valid_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -309,22 +309,26 @@ def test_chunk_stage2_records_fp32(seed):
     rec = (64 * K * 4 * 3 + 64 * V * 4 + 64 * 64 * 4 + 4 * K + 255) // 256 * 256
     raw = ws.cpu()
     NT = (T + 63) // 64
+    sched = (((3 * B + 1) * 4 + 15) // 16 * 16 + B * NT * 8 + 255) // 256 * 256
     for st in stages:
         hv, c = st["hv"], st["start"] // 64
-        base = (hv * NT + c) * rec
+        base = sched + (hv * NT + c) * rec
         L = st["length"]
 
-        def arr(off, shape):
-            n = int(np.prod(shape))
-            return raw[base + off: base + off + 4 * n].view(torch.float32).reshape(shape).double().numpy()
-        # record layout (fp32 path): w | qg | kg^T | Aqk | u | 2^G
+        def flat(off, n):
+            return raw[base + off: base + off + 4 * n].view(torch.float32).double().numpy()
+
+        def frag(off, R, KC):   # fp32 path: 4-wide contraction steps, 1 value per lane
+            return flat(off, R * KC)[frag_tile_index(R, KC, 4, 1)]
+        # record layout (fp32 path): w | qg | kg^T | Aqk (fragment order) | u (accumulator
+        # order) | 2^G, after the schedule
         off = 0
-        w = arr(off, (64, K)); off += 64 * K * 4
-        qg = arr(off, (64, K)); off += 64 * K * 4
-        kgT = arr(off, (K, 64)); off += K * 64 * 4
-        aqk = arr(off, (64, 64)); off += 64 * 64 * 4
-        u = arr(off, (64, V)); off += 64 * V * 4
-        eg = arr(off, (K,))
+        w = frag(off, 64, K); off += 64 * K * 4
+        qg = frag(off, 64, K); off += 64 * K * 4
+        kgT = frag(off, K, 64); off += K * 64 * 4
+        aqk = frag(off, 64, 64); off += 64 * 64 * 4
+        u = flat(off, 64 * V)[acc_tile_index(64, V)]; off += 64 * V * 4
+        eg = flat(off, K)
         scale = K ** -0.5
         for name, got, want in (("Aqk", aqk[:L, :L], st["Aqk"]), ("w", w[:L], st["w"]),
                                 ("u", u[:L], st["u"]), ("qg", qg[:L], scale * st["qg"]),

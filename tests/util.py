@@ -77,3 +77,22 @@ def to_device(d, device="cuda"):
     for k, v in d.items():
         out[k] = v.to(device) if isinstance(v, torch.Tensor) else v
     return out
+
+
+def frag_tile_index(R, KC, ks, kpl):
+    """Element offsets of a fragment-order tile (see the record layout in the library):
+    64-lane blocks per (16-row band b, contraction step st), band-major; lane
+    l = row % 16 + 16 * ((col % ks) // kpl) holds kpl consecutive columns."""
+    row = np.arange(R)[:, None]
+    col = np.arange(KC)[None, :]
+    b, st = row // 16, col // ks
+    lane = row % 16 + 16 * ((col % ks) // kpl)
+    return ((b * (KC // ks) + st) * 64 + lane) * kpl + col % kpl
+
+
+def acc_tile_index(R, NCOL):
+    """Element offsets of an accumulator-order fp32 tile holding x[row][col] for rows
+    0..R-1 (R = 64) and columns 0..NCOL-1, four consecutive rows of one column per lane."""
+    row = np.arange(R)[:, None]
+    col = np.arange(NCOL)[None, :]
+    return (((col // 16) * 4 + row // 16) * 64 + col % 16 + 16 * ((row % 16) // 4)) * 4 + row % 4
