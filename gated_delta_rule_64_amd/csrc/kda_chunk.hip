@@ -364,12 +364,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
                 for (int e = tid; e < 16 * LD; e += NTHREADS) AS[e] = 0.f;
             lds_barrier();
             // tiles (I, J) for J <= I: even tt = Aqk, odd tt = L; wave w takes tt = w, w+4
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const int tt = wave + 4 * a;
-                const int J = tt >> 1;
-                if (J <= I && !(exact_diag && J == I))
-                    acc[a] = tile_mma<float, TQh, TKh>(acc[a], (tt & 1) ? KR : QH, 0, KC, 16 * J, 0, KH, lane);
+            {
+                const int J0 = wave >> 1, J1 = (wave + 4) >> 1;
+                const bool do0 = J0 <= I && !(exact_diag && J0 == I);
+                const bool do1 = J1 <= I && !(exact_diag && J1 == I);
+                tile_mma2<float, TQh, TKh, KH>(acc[0], (wave & 1) ? KR : QH, 0, KC, 16 * J0, do0,
+                                               acc[1], (wave & 1) ? KR : QH, 0, KC, 16 * J1, do1, lane);
             }
             lds_barrier();
         }
@@ -487,19 +487,31 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
     lds_barrier();
     float* GS0 = Lm;   // kg^T rows 0..63   (Tile<float, 64, 64>, fits in 64 x 65 floats)
     float* GS1 = Tm;   // kg^T rows 64..127 (K = 128)
+    {
+        // (k 2^G)^T and kg^T: this thread's RPT consecutive rows j of each column d are
+        // contiguous in the transposed tiles, so each column is one vector write
+        float kd_run[8][RPT], kg_run[8][RPT];
+#pragma unroll
+        for (int ii = 0; ii < RPT; ++ii)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kf = to_f32(kv[ii][e]);
+                kd_run[e][ii] = kf * exp2_fast(gm[ii][e]);
+                kg_run[e][ii] = kf * exp2_fast(Gd[e] - gm[ii][e]);
+            }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int dk = d0 + e;
+            store_run<TW, RPT>(KDt + TKD::idx(dk, i0), kd_run[e]);
+            store_run<float, RPT>((dk < 64 ? GS0 : GS1) + TGS::idx(dk & 63, i0), kg_run[e]);
+        }
+    }
 #pragma unroll
     for (int ii = 0; ii < RPT; ++ii) {
         const int i = i0 + ii;
         float qo[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float ex = exp2_fast(gm[ii][e]);
-            const float kf = to_f32(kv[ii][e]);
-            KDt[TKD::idx(d0 + e, i)] = from_f32<TW>(kf * ex);
-            qo[e] = p.scale * to_f32(qv[ii][e]) * ex;
-            const int dk = d0 + e;
-            (dk < 64 ? GS0 : GS1)[TGS::idx(dk & 63, i)] = kf * exp2_fast(Gd[e] - gm[ii][e]);
-        }
+        for (int e = 0; e < 8; ++e) qo[e] = p.scale * to_f32(qv[ii][e]) * exp2_fast(gm[ii][e]);
         if constexpr (SPLIT) {
             put_split8(out_qg, out_qg + C * K, FA::idx(i, d0), qo);
         } else {
@@ -514,6 +526,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
     {
         const int cgv = tid % CGV, rgv = tid / CGV;
         const int c0v = 8 * cgv, j0 = rgv * RPTV;
+        float vrun[8][RPTV];
 #pragma unroll
         for (int jj = 0; jj < RPTV; ++jj) {
             const int j = j0 + jj;
@@ -525,25 +538,31 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
                 for (int e = 0; e < 8; ++e) vv[e] = 0.f;
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) VTt[TVT::idx(c0v + e, j)] = from_f32<TW>(vv[e]);
+            for (int e = 0; e < 8; ++e) vrun[e][jj] = vv[e];
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) store_run<TW, RPTV>(VTt + TVT::idx(c0v + e, j0), vrun[e]);
     }
     lds_barrier();
 
     // u = (T beta) v: wave w owns rows 16w.., stored transposed in accumulator order
-    const int kend = (16 * wave + 16 + MW::KS - 1) / MW::KS * MW::KS;
-    const int k1 = kend < C ? kend : C;
-    for (int nu = 0; nu < V / 16; ++nu) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_mma<TW, TB64, TVT>(acc, TBs, 16 * wave, VTt, 16 * nu, 0, k1, lane);
-        *reinterpret_cast<f32x4*>(out_u + AccTile::quad(16 * nu + lr, 16 * wave + 4 * lq)) = acc;
+    // (the contraction runs over all 64 columns; T is zero above its diagonal)
+#pragma unroll
+    for (int nu = 0; nu < V / 16; nu += 2) {
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        tile_mma2<TW, TB64, TVT, C>(a0, TBs, 16 * wave, VTt, 16 * nu, true,
+                                    a1, TBs, 16 * wave, VTt, 16 * nu + 16, true, lane);
+        *reinterpret_cast<f32x4*>(out_u + AccTile::quad(16 * nu + lr, 16 * wave + 4 * lq)) = a0;
+        *reinterpret_cast<f32x4*>(out_u + AccTile::quad(16 * nu + 16 + lr, 16 * wave + 4 * lq)) = a1;
     }
     // w = (T beta)(k 2^G): kept in registers until the operand tiles are released
     f32x4 wacc[K / 16];
 #pragma unroll
-    for (int nt = 0; nt < K / 16; ++nt) {
+    for (int nt = 0; nt < K / 16; nt += 2) {
         wacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        wacc[nt] = tile_mma<TW, TB64, TKD>(wacc[nt], TBs, 16 * wave, KDt, 16 * nt, 0, k1, lane);
+        wacc[nt + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        tile_mma2<TW, TB64, TKD, C>(wacc[nt], TBs, 16 * wave, KDt, 16 * nt, true,
+                                    wacc[nt + 1], TBs, 16 * wave, KDt, 16 * nt + 16, true, lane);
     }
     lds_barrier();
     // stage w (rows i, columns d)
@@ -585,6 +604,471 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
                 for (int e = 0; e < MW::KPL; ++e) out_kgT[o + e] = from_f32<TW>(GS[TGS::idx(row, col + e)]);
             }
         }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// intra, bf16 inputs: Stage 1 + 2 with each wave owning one 16-row block of the chunk
+// ------------------------------------------------------------------------------------
+// Wave w holds rows 16w .. 16w+15 in matrix-core operand layout: lane l has row
+// 16w + (l % 16) and columns 32s + 8(l / 16) .. +7 of q, k, g and v for every 32-column
+// step s, so q, k and the gate scaled by their decays feed the 16x16x32 products with no
+// LDS round trip, the gate cumsum runs down each 16-lane row with DPP, and the qg record
+// is stored straight from registers.
+//
+// Anchors. Block row w of Aqk and L uses the block boundary P_w (Gamma of the row just
+// before the block) for every block pair: row operands x_i 2^(Gamma_i - P_w) <= |x_i|, and
+// column operands k_j 2^(P_w - Gamma_j), which are <= |k_j| for the earlier blocks (the
+// boundary separates i from j) and at most 2^(block decay) for the diagonal block. When a
+// block decays by more than SPREAD_LIMIT in some channel, that diagonal block is computed
+// exactly with one one-sided 2^(Gamma_i - Gamma_j) per (i, j, channel) instead. All
+// exponents are local: Gamma_i - P_w is the block-local cumsum, and the boundary-to-
+// boundary factors 2^(P_w - P_J) are tabulated once per chunk in LDS.
+//
+// Products run on hi/lo bf16 splits (three products) and give fp32-level Aqk and L. The
+// WY inverse is blocked: each wave inverts its 16x16 diagonal block by substitution, and
+// the off-diagonal blocks follow in three dependency levels of 16x16x16 split products.
+// Transposes that the records need (kg^T, w, Aqk in fragment order) come from products
+// with a selection matrix and lane swaps, not from LDS staging.
+// Per-chunk factor table, one row per channel vector: 2^(sum of the block totals bt_b over
+// a range of blocks), or 2^(-bt_w). Rows: 0-2 the boundary-to-boundary factors of block
+// pairs (2,0) (3,0) (3,1); 3-5 2^(P_w) for w = 1..3; 6-8 2^(G - P_(w+1)) for w = 0..2; 9
+// 2^G; 10-13 2^(-bt_w); 14 ones (the factors that are empty products).
+constexpr int NTAB = 15;
+constexpr int TAB_ONE = 14;
+__device__ __forceinline__ int tab_pair(int w, int J) { return J == w - 1 ? TAB_ONE : (w == 2 ? 0 : 1 + J); }
+__device__ __forceinline__ int tab_ew(int w) { return w == 0 ? TAB_ONE : 2 + w; }
+__device__ __forceinline__ int tab_kg(int w) { return w == 3 ? TAB_ONE : 6 + w; }
+constexpr int TAB_EG = 9;
+__device__ __forceinline__ int tab_dg(int w) { return 10 + w; }
+
+template <int K, int V, typename TB>
+__global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) {
+    typedef __bf16 TW;
+    constexpr int NKS = K / 32, NVS = V / 32;   // 32-column steps of q/k/g and of v
+    typedef Tile<TW, C, C> TB64;                // T beta
+    typedef Tile<TW, K, C> TKD;                 // (k 2^Gamma)^T
+    typedef Tile<TW, V, C> TVT;                 // v^T
+    typedef FragTile<TW, C, K> FA;              // w, qg
+    typedef FragTile<TW, C, C> FQ;              // Aqk
+    typedef FragTile<TW, K, C> FG;              // kg^T
+
+    // LDS
+    //  R1  factor table [NTAB][K] and the published column operands kap[3][NKS][2][64][4]
+    //      (Stage 2), then T [64][64] and T tiles in accumulator layout [6][64][4] (solve)
+    //  R2  block totals of the gate [4][K] (Stage 1), L [64][64] (Stage 2 and solve),
+    //      T beta as a bf16 tile (products)
+    //  R4  (k 2^Gamma)^T and v^T bf16 tiles
+    constexpr int TAB_F = NTAB * K;
+    constexpr int KAP_F = 3 * NKS * 2 * 64 * 4;
+    constexpr int R1_F = (TAB_F + KAP_F) > (C * C + 6 * 256) ? (TAB_F + KAP_F) : (C * C + 6 * 256);
+    constexpr int R2_F = C * C;
+    static_assert(4 * K <= R2_F && TB64::BYTES <= R2_F * 4, "R2 holds the block totals and T beta");
+    __shared__ __attribute__((aligned(16))) float R1[R1_F];
+    __shared__ __attribute__((aligned(16))) float R2[R2_F];
+    __shared__ __attribute__((aligned(16))) TW KDt[K * C];
+    __shared__ __attribute__((aligned(16))) TW VTt[V * C];
+    __shared__ __attribute__((aligned(16))) float betas[C];
+    float* table = R1;
+    float* kap = R1 + TAB_F;
+    float* Tm = R1;
+    float* TA = R1 + C * C;
+    float* bt = R2;
+    float* Lm = R2;
+    TW* TBs = reinterpret_cast<TW*>(R2);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int lr = lane & 15, lq = lane >> 4;
+    const int G = p.NCmax * p.HV;
+    const int item = xcd_remap(blockIdx.x, G);
+    const int hv = item % p.HV;
+    const int c = item / p.HV;
+    const int h = hv / (p.HV / p.H);
+
+    if (c >= p.nchunks[0]) return;
+    const int2 cpos = p.table[c];
+    const long long rs = cpos.x;
+    const int len = cpos.y;
+    char* rec = p.rec + ((size_t)hv * p.NCmax + c) * p.rec_bytes;
+    TW* out_w = reinterpret_cast<TW*>(rec + p.off_w);
+    TW* out_qg = reinterpret_cast<TW*>(rec + p.off_qg);
+    TW* out_kgT = reinterpret_cast<TW*>(rec + p.off_kgT);
+    TW* out_aqk = reinterpret_cast<TW*>(rec + p.off_aqk);
+    float* out_u = reinterpret_cast<float*>(rec + p.off_u);
+    float* out_eg = reinterpret_cast<float*>(rec + p.off_eg);
+
+    // swizzled fp32 64 x 64: 16-byte chunk index XOR (row % 16)
+    auto sw = [](int row, int col) { return row * C + ((((col >> 2) ^ (row & 15))) << 2) + (col & 3); };
+
+    // ---- Stage 1: loads (row i = 16w + lr) and the block-local cumsum of the gate ----
+    const int i_row = 16 * w + lr;
+    const bool live = i_row < len;
+    const size_t r_g = (size_t)(rs + i_row);
+    bf16x8 qv[NKS], kv[NKS], vv[NVS];
+    float loc[NKS][8];
+    float beta_i = 0.f;
+    if (live) {
+        beta_i = to_f32(reinterpret_cast<const TB*>(p.beta)[r_g * p.HV + hv]);
+        const TW* qp = reinterpret_cast<const TW*>(p.q) + (r_g * p.H + h) * K + 8 * lq;
+        const TW* kp = reinterpret_cast<const TW*>(p.k) + (r_g * p.H + h) * K + 8 * lq;
+        const TW* vp = reinterpret_cast<const TW*>(p.v) + (r_g * p.HV + hv) * V + 8 * lq;
+        const float* gp = p.g + (r_g * p.HV + hv) * K + 8 * lq;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            qv[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+            kv[s] = *reinterpret_cast<const bf16x8*>(kp + 32 * s);
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp + 32 * s);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(gp + 32 * s + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { loc[s][e] = g0[e]; loc[s][4 + e] = g1[e]; }
+        }
+#pragma unroll
+        for (int s = 0; s < NVS; ++s) vv[s] = *reinterpret_cast<const bf16x8*>(vp + 32 * s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { qv[s][e] = (__bf16)0.f; kv[s][e] = (__bf16)0.f; loc[s][e] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < NVS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[s][e] = (__bf16)0.f;
+    }
+    if (lq == 0) betas[i_row] = beta_i;
+
+    // Gamma_i - P_w (inclusive, down the 16 rows of the block); the block total is the
+    // value of the block's last row
+    int wide = 0;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            loc[s][e] = row_scan(loc[s][e]);
+            wide |= -row_bcast<15>(loc[s][e]) > SPREAD_LIMIT;
+        }
+    if (lr == 15) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            float* dst = bt + w * K + 32 * s + 8 * lq;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{loc[s][0], loc[s][1], loc[s][2], loc[s][3]};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{loc[s][4], loc[s][5], loc[s][6], loc[s][7]};
+        }
+    }
+    const bool exact_diag = __builtin_amdgcn_ballot_w64(wide) != 0;   // wave-uniform
+
+    // v^T into LDS: the selection products turn each lane's 8 columns of one row into
+    // 4 consecutive rows of one column
+#pragma unroll
+    for (int s = 0; s < NVS; ++s)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const f32x4 x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[s], eye_frag(lane, hh),
+                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const int col = 32 * s + 16 * hh + lr;
+            *reinterpret_cast<bf16x4*>(VTt + TVT::idx(col, 16 * w + 4 * lq)) =
+                bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+        }
+
+    // diagonal block, exact one-sided decays (blocks that decay too fast for an anchor)
+    f32x4 aqk_d = {0.f, 0.f, 0.f, 0.f}, lt_d = {0.f, 0.f, 0.f, 0.f};
+    if (exact_diag) {
+#pragma unroll 1
+        for (int jj = 0; jj < 16; ++jj) {
+            const int src = (lane & 48) | jj;
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float kf = to_f32(kv[s][e]);
+                    const float kj = __shfl(kf, src);
+                    const float lj = __shfl(loc[s][e], src);
+                    const float f = kj * exp2_fast(fminf(loc[s][e] - lj, 0.f));
+                    sq = fmaf(to_f32(qv[s][e]), f, sq);
+                    sk = fmaf(kf, f, sk);
+                }
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            sk += __shfl_xor(sk, 16);
+            sk += __shfl_xor(sk, 32);
+            // this lane keeps (row i = lr, column j = 4 lq + r) of the transposed tile
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (jj == 4 * lq + r) { aqk_d[r] = sq; lt_d[r] = sk; }
+        }
+    }
+    // operands: row side x 2^(Gamma_i - P_w) and the column side k 2^(P_(w+1) - Gamma_j),
+    // which later blocks read from LDS (and scale by 2^(P_w' - P_(w+1))) and this block
+    // scales by 2^(P_w - P_(w+1)) for its diagonal block
+    bf16x8 qh[NKS], ql[NKS], kh[NKS], kl[NKS];
+    float kap_own[NKS][8];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        float xq[8], xk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float kf = to_f32(kv[s][e]);
+            const float bi = exp2_fast(loc[s][e]);
+            xq[e] = to_f32(qv[s][e]) * bi;
+            xk[e] = kf * bi;
+            kap_own[s][e] = kf * exp2_fast(row_bcast<15>(loc[s][e]) - loc[s][e]);
+        }
+        split8(xq, qh[s], ql[s]);
+        split8(xk, kh[s], kl[s]);
+    }
+    if (w < 3) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                *reinterpret_cast<f32x4*>(kap + (((w * NKS + s) * 2 + half) * 64 + lane) * 4) =
+                    f32x4{kap_own[s][4 * half], kap_own[s][4 * half + 1], kap_own[s][4 * half + 2], kap_own[s][4 * half + 3]};
+    }
+    lds_barrier();
+
+    // ---- factor table: 2^(sum of block totals over a range of blocks), per channel ----
+    for (int t = tid; t < NTAB * K; t += NTHREADS) {
+        const int row = t / K, d = t % K;
+        int lo, hi;                                            // blocks lo .. hi-1
+        if (row < 3) { lo = row == 2 ? 2 : 1; hi = row == 0 ? 2 : 3; }   // pairs (2,0) (3,0) (3,1)
+        else if (row < 6) { lo = 0; hi = row - 2; }            // 2^(P_w), w = row - 2
+        else if (row < 9) { lo = row - 5; hi = 4; }            // 2^(G - P_(w+1)), w = row - 6
+        else if (row == TAB_EG) { lo = 0; hi = 4; }            // 2^G
+        else if (row < TAB_ONE) { lo = row - 10; hi = row - 9; }   // 2^(-bt_w), w = row - 10
+        else { lo = 0; hi = 0; }
+        float ex = 0.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (b >= lo && b < hi) ex += bt[b * K + d];
+        if (row >= 10 && row < TAB_ONE) ex = -ex;
+        table[t] = exp2_fast(ex);
+    }
+    lds_barrier();
+
+    // ---- records from registers: qg, kg^T, eG; (k 2^Gamma)^T into LDS ----
+    const float* ew = table + tab_ew(w) * K + 8 * lq;
+    const float* kgf = table + tab_kg(w) * K + 8 * lq;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(ew + 32 * s);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(ew + 32 * s + 4);
+        const f32x4 f0 = *reinterpret_cast<const f32x4*>(kgf + 32 * s);
+        const f32x4 f1 = *reinterpret_cast<const f32x4*>(kgf + 32 * s + 4);
+        const float ewv[8] = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+        const float kgv[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+        float xq[8], xg[8];
+        bf16x8 kd;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            xq[e] = p.scale * ((float)qh[s][e] + (float)ql[s][e]) * ewv[e];
+            kd[e] = (__bf16)(((float)kh[s][e] + (float)kl[s][e]) * ewv[e]);
+            xg[e] = kap_own[s][e] * kgv[e];
+        }
+        bf16x8 hi8, lo8;
+        split8(xq, hi8, lo8);
+        *reinterpret_cast<bf16x8*>(out_qg + FA::frag(w, s, lane)) = hi8;
+        *reinterpret_cast<bf16x8*>(out_qg + C * K + FA::frag(w, s, lane)) = lo8;
+        // (k 2^Gamma)^T: four consecutive rows of one column per lane
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const f32x4 x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kd, eye_frag(lane, hh),
+                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            *reinterpret_cast<bf16x4*>(KDt + TKD::idx(32 * s + 16 * hh + lr, 16 * w + 4 * lq)) =
+                bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+        }
+        // kg^T in fragment order (rows = channels, contraction = rows of the chunk):
+        // selection products give 4 consecutive rows per lane, the lane swaps 8
+        split8(xg, hi8, lo8);
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            const bf16x8 a = part ? lo8 : hi8;
+            const f32x4 x0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, eye_frag(lane, 0), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const f32x4 x1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, eye_frag(lane, 1), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            float o8[8];
+            acc_pair_to_frag(x0, x1, o8);
+            bf16x8 ov;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ov[e] = (__bf16)o8[e];
+            // lanes lq 0-1 hold channel 32s + lr, lanes lq 2-3 channel 32s + 16 + lr; rows
+            // 16w + 8(lq & 1) .. +7 of the chunk
+            const int band = 2 * s + (lq >> 1);
+            const int fl = lr + 16 * (2 * (w & 1) + (lq & 1));
+            *reinterpret_cast<bf16x8*>(out_kgT + part * K * C + FG::frag(band, w >> 1, fl)) = ov;
+        }
+    }
+    for (int t = tid; t < K / 4; t += NTHREADS)
+        *reinterpret_cast<f32x4*>(out_eg + 4 * t) = *reinterpret_cast<const f32x4*>(table + TAB_EG * K + 4 * t);
+
+    // ---- Aqk and L, block row w: transposed tiles D'[j][i] (A = column side) ----
+    f32x4 aqk[3], lt[3];
+#pragma unroll
+    for (int J = 0; J < 3; ++J) {
+        aqk[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lt[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (J < w) {
+            const float* fj = table + tab_pair(w, J) * K + 8 * lq;
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(kap + (((J * NKS + s) * 2 + 0) * 64 + lane) * 4);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(kap + (((J * NKS + s) * 2 + 1) * 64 + lane) * 4);
+                const f32x4 f0 = *reinterpret_cast<const f32x4*>(fj + 32 * s);
+                const f32x4 f1 = *reinterpret_cast<const f32x4*>(fj + 32 * s + 4);
+                const float x[8] = {a0[0] * f0[0], a0[1] * f0[1], a0[2] * f0[2], a0[3] * f0[3],
+                                    a1[0] * f1[0], a1[1] * f1[1], a1[2] * f1[2], a1[3] * f1[3]};
+                bf16x8 ah, al;
+                split8(x, ah, al);
+                aqk[J] = mma3(ah, al, qh[s], ql[s], aqk[J]);
+                lt[J] = mma3(ah, al, kh[s], kl[s], lt[J]);
+            }
+        }
+    }
+    if (!exact_diag) {
+        const float* dg = table + tab_dg(w) * K + 8 * lq;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const f32x4 f0 = *reinterpret_cast<const f32x4*>(dg + 32 * s);
+            const f32x4 f1 = *reinterpret_cast<const f32x4*>(dg + 32 * s + 4);
+            const float x[8] = {kap_own[s][0] * f0[0], kap_own[s][1] * f0[1], kap_own[s][2] * f0[2], kap_own[s][3] * f0[3],
+                                kap_own[s][4] * f1[0], kap_own[s][5] * f1[1], kap_own[s][6] * f1[2], kap_own[s][7] * f1[3]};
+            bf16x8 ah, al;
+            split8(x, ah, al);
+            aqk_d = mma3(ah, al, qh[s], ql[s], aqk_d);
+            lt_d = mma3(ah, al, kh[s], kl[s], lt_d);
+        }
+    }
+    // lane (lq, lr) holds rows j = 16J + 4lq + r, column i = 16w + lr of the transposed tile
+    auto tile_aqk = [&](int J, int r) -> float {
+        if (J < w) return p.scale * (J == 0 ? aqk[0][r] : (J == 1 ? aqk[1][r] : aqk[2][r]));
+        if (J == w) return lr >= 4 * lq + r ? p.scale * aqk_d[r] : 0.f;
+        return 0.f;
+    };
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        f32x4 x, y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { x[r] = tile_aqk(2 * s, r); y[r] = tile_aqk(2 * s + 1, r); }
+        float o8[8];
+        acc_pair_to_frag(x, y, o8);
+        bf16x8 hi8, lo8;
+        split8(o8, hi8, lo8);
+        *reinterpret_cast<bf16x8*>(out_aqk + FQ::frag(w, s, lane)) = hi8;
+        *reinterpret_cast<bf16x8*>(out_aqk + C * C + FQ::frag(w, s, lane)) = lo8;
+    }
+    // L rows of block w (beta_i, strictly lower) -> LDS
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        if (J <= w) {
+            f32x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float val = J < w ? (J == 0 ? lt[0][r] : (J == 1 ? lt[1][r] : lt[2][r]))
+                                        : (lr > 4 * lq + r ? lt_d[r] : 0.f);
+                x[r] = beta_i * val;
+            }
+            *reinterpret_cast<f32x4*>(Lm + sw(16 * w + lr, 16 * J + 4 * lq)) = x;
+        }
+    }
+    lds_barrier();
+
+    // ---- WY inverse T = (I + L)^-1 by 16-row blocks ----
+    // diagonal blocks: lane (lq, lr) solves column lr of (I + L_ww) x = e_lr
+    {
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float srow[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 t4 = *reinterpret_cast<const f32x4*>(Lm + sw(16 * w + i, 16 * w + 4 * q4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) srow[4 * q4 + e] = t4[e];
+            }
+            float acc = (i == lr) ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < i; ++j) acc = fmaf(-srow[j], x[j], acc);
+            x[i] = acc;
+        }
+        // (R1 is free: the table and the column operands were last read before the barrier)
+        if (lq == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Tm[sw(16 * w + i, 16 * w + lr)] = x[i];
+        }
+        if (w < 3) {
+            f32x4 t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                t[r] = lq == 0 ? x[r] : (lq == 1 ? x[4 + r] : (lq == 2 ? x[8 + r] : x[12 + r]));
+            *reinterpret_cast<f32x4*>(TA + (w * 64 + lane) * 4) = t;   // slots 0..2: T_00, T_11, T_22
+        }
+    }
+    lds_barrier();
+    // level l: T_(w, w-l) = -T_ww sum_(M = w-l .. w-1) L_wM T_(M, w-l)
+    auto ta_slot = [](int M, int J) { return M == J ? M : (M - J == 1 ? 2 + M : 5); };
+#pragma unroll 1
+    for (int l = 1; l < 4; ++l) {
+        if (w >= l) {
+            const int J = w - l;
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int M = J; M < w; ++M) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(Lm + sw(16 * w + lr, 16 * M + 4 * lq));
+                const f32x4 b = *reinterpret_cast<const f32x4*>(TA + (ta_slot(M, J) * 64 + lane) * 4);
+                y = mma16x3(a, b, y);
+            }
+            const f32x4 a = *reinterpret_cast<const f32x4*>(Tm + sw(16 * w + lr, 16 * w + 4 * lq));
+            f32x4 t = mma16x3(a, y, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                t[r] = -t[r];
+                Tm[sw(16 * w + 4 * lq + r, 16 * J + lr)] = t[r];
+            }
+            if (w < 3) *reinterpret_cast<f32x4*>(TA + (ta_slot(w, J) * 64 + lane) * 4) = t;
+        }
+        lds_barrier();
+    }
+
+    // ---- T beta (bf16, lower blocks only) ----
+    for (int t = tid; t < C * C / 8; t += NTHREADS) {
+        const int i = t >> 3, j0 = (t & 7) * 8;
+        bf16x8 o;
+        if ((j0 >> 4) <= (i >> 4)) {
+            const f32x4 t0 = *reinterpret_cast<const f32x4*>(Tm + sw(i, j0));
+            const f32x4 t1 = *reinterpret_cast<const f32x4*>(Tm + sw(i, j0 + 4));
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(betas + j0);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(betas + j0 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { o[e] = (__bf16)(t0[e] * b0[e]); o[4 + e] = (__bf16)(t1[e] * b1[e]); }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (__bf16)0.f;
+        }
+        *reinterpret_cast<bf16x8*>(TBs + TB64::idx(i, j0)) = o;
+    }
+    lds_barrier();
+
+    // ---- u = (T beta) v (accumulator order) and w = (T beta)(k 2^Gamma) (fragment order) ----
+#pragma unroll
+    for (int nu = 0; nu < V / 16; nu += 2) {
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        tile_mma2<TW, TB64, TVT, C>(a0, TBs, 16 * w, VTt, 16 * nu, true,
+                                    a1, TBs, 16 * w, VTt, 16 * nu + 16, true, lane);
+        *reinterpret_cast<f32x4*>(out_u + AccTile::quad(16 * nu + lr, 16 * w + 4 * lq)) = a0;
+        *reinterpret_cast<f32x4*>(out_u + AccTile::quad(16 * nu + 16 + lr, 16 * w + 4 * lq)) = a1;
+    }
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        // transposed tiles D'[d][i] for channels 32s .. 32s+31, rows i of block w
+        f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+        tile_mma2<TW, TKD, TB64, C>(x, KDt, 32 * s, TBs, 16 * w, true,
+                                    y, KDt, 32 * s + 16, TBs, 16 * w, true, lane);
+        float o8[8];
+        acc_pair_to_frag(x, y, o8);
+        bf16x8 ov;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ov[e] = (__bf16)o8[e];
+        *reinterpret_cast<bf16x8*>(out_w + FA::frag(w, s, lane)) = ov;
     }
 }
 
@@ -943,8 +1427,12 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     ip.scale = a.scale;
     const long long nintra = (long long)L.NCmax * a.HV;
     if (nintra > 0) {
-        hipLaunchKernelGGL((intra_kernel<K, V, TIn, TB>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
-                           a.stream, ip);
+        if constexpr (sizeof(TIn) == 2)
+            hipLaunchKernelGGL((intra_bf16_kernel<K, V, TB>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
+                               a.stream, ip);
+        else
+            hipLaunchKernelGGL((intra_kernel<K, V, TIn, TB>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
+                               a.stream, ip);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

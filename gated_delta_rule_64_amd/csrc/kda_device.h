@@ -124,6 +124,57 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const TW* A, int a_row0, co
     return acc;
 }
 
+// Two independent tile products over the same compile-time contraction [0, NK): all
+// fragments of a step are loaded before its MFMAs, and the two accumulation chains
+// interleave, so LDS latency and MFMA latency overlap. A2/B2 may alias A1/B1.
+template <typename TW, typename TA, typename TB, int NK>
+__device__ __forceinline__ void tile_mma2(f32x4& acc1, const TW* A1, int a1_row0, const TW* B1,
+                                          int b1_row0, bool do1, f32x4& acc2, const TW* A2,
+                                          int a2_row0, const TW* B2, int b2_row0, bool do2,
+                                          int lane) {
+    const int r = lane & 15;
+    const int ko = (lane >> 4) * Mma<TW>::KPL;
+#pragma unroll
+    for (int k = 0; k < NK; k += Mma<TW>::KS) {
+        if (do1) {
+            auto a = TA::frag(A1, a1_row0 + r, k + ko);
+            auto b = TB::frag(B1, b1_row0 + r, k + ko);
+            acc1 = Mma<TW>::mma(a, b, acc1);
+        }
+        if (do2) {
+            auto a = TA::frag(A2, a2_row0 + r, k + ko);
+            auto b = TB::frag(B2, b2_row0 + r, k + ko);
+            acc2 = Mma<TW>::mma(a, b, acc2);
+        }
+    }
+}
+
+// Single tile product over a compile-time contraction [0, NK).
+template <typename TW, typename TA, typename TB, int NK>
+__device__ __forceinline__ f32x4 tile_mma_n(f32x4 acc, const TW* A, int a_row0, const TW* B,
+                                            int b_row0, int lane) {
+    const int r = lane & 15;
+    const int ko = (lane >> 4) * Mma<TW>::KPL;
+#pragma unroll
+    for (int k = 0; k < NK; k += Mma<TW>::KS) {
+        auto a = TA::frag(A, a_row0 + r, k + ko);
+        auto b = TB::frag(B, b_row0 + r, k + ko);
+        acc = Mma<TW>::mma(a, b, acc);
+    }
+    return acc;
+}
+
+// Store N consecutive elements (converted from fp32) with one vector write; the
+// destination must be aligned to N elements and not cross a 16-byte chunk.
+template <typename TW, int N>
+__device__ __forceinline__ void store_run(TW* dst, const float* x) {
+    typedef __attribute__((ext_vector_type(N))) TW vec;
+    vec v;
+#pragma unroll
+    for (int e = 0; e < N; ++e) v[e] = from_f32<TW>(x[e]);
+    *reinterpret_cast<vec*>(dst) = v;
+}
+
 // Store 4 consecutive rows (row0..row0+3) of one column from accumulator registers into
 // a transposed tile T[col][row0..row0+3] (row0 % 4 == 0).
 template <typename TW, typename TT>
@@ -133,6 +184,99 @@ __device__ __forceinline__ void store_col4(TW* t, int col, int row0, f32x4 v) {
     p[1] = from_f32<TW>(v[1]);
     p[2] = from_f32<TW>(v[2]);
     p[3] = from_f32<TW>(v[3]);
+}
+
+// ---------------------------------------------------------------------------------
+// Cross-lane building blocks. A 64-lane wave is four DPP rows of 16 lanes.
+// ---------------------------------------------------------------------------------
+// x of lane (l - N) within this lane's 16-lane row; 0 for the first N lanes of the row
+template <int N> __device__ __forceinline__ float row_shr(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x110 + N, 0xf, 0xf, true));
+}
+// x of lane N of this lane's 16-lane row (row_newbcast)
+template <int N> __device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x150 + N, 0xf, 0xf, false));
+}
+// inclusive prefix sum over the 16 lanes of each row (Hillis-Steele, four steps)
+__device__ __forceinline__ float row_scan(float x) {
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    return x;
+}
+
+// Two 16x16 accumulator tiles X and Y (lane l holds M[4(l/16) + r][l % 16], r = 0..3) are
+// the top and bottom halves of a 32 x 16 matrix Z = [X; Y]. Afterwards lane l holds the
+// eight consecutive rows Z[8(l/16) + e][l % 16], e = 0..7: the operand-fragment layout of
+// the 16 x 32 matrix Z^T. Two lane-swap steps per register, no LDS.
+__device__ __forceinline__ void acc_pair_to_frag(f32x4 x, f32x4 y, float out[8]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        // {X0 X1 Y0 Y1}, {X2 X3 Y2 Y3}  (Xg = rows 4g..4g+3 of X, one 16-lane row each)
+        // (scalar copies: __builtin_bit_cast of a vector element reads element 0)
+        const float xr = x[r], yr = y[r];
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(xr), __float_as_uint(yr), false, false);
+        const unsigned s0 = s[0], s1 = s[1];
+        // {X0 X2 Y0 Y2}, {X1 X3 Y1 Y3}
+        const auto t = __builtin_amdgcn_permlane16_swap(s0, s1, false, false);
+        const unsigned t0 = t[0], t1 = t[1];
+        out[r] = __uint_as_float(t0);
+        out[4 + r] = __uint_as_float(t1);
+    }
+}
+
+// bf16 hi/lo split of 8 fp32 values: x = hi + lo to about 16 significant bits
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = (__bf16)x[e];
+        lo[e] = (__bf16)(x[e] - (float)hi[e]);
+    }
+}
+__device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)x[e];
+        lo[e] = (__bf16)(x[e] - (float)hi[e]);
+    }
+}
+
+// hi*hi + lo*hi + hi*lo on the 16x16x32 bf16 matrix cores (the lo*lo term is below fp32
+// rounding of the result)
+__device__ __forceinline__ f32x4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+}
+
+// 16x16x16 bf16 product (lane l: row l % 16, contraction 4(l/16) .. +3), same split
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16x3(f32x4 a, f32x4 b, f32x4 c) {
+    bf16x4 ah, al, bh, bl;
+    split4(a, ah, al);
+    split4(b, bh, bl);
+    c = mma16(ah, bl, c);
+    c = mma16(al, bh, c);
+    return mma16(ah, bh, c);
+}
+
+// B operand of a 16x16x32 product that selects contraction columns 16h .. 16h+15:
+// B[n][k] = (k == n + 16h). With it, an A fragment (row m, eight consecutive columns per
+// lane) comes out as A[m][16h + n] in accumulator layout -- four consecutive rows per lane.
+// Exact: every product is x * 1 or x * 0.
+__device__ __forceinline__ bf16x8 eye_frag(int lane, int h) {
+    const int n = lane & 15, k0 = 8 * (lane >> 4);
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (__bf16)((k0 + e == n + 16 * h) ? 1.f : 0.f);
+    return b;
 }
 
 // Barrier for blocks that exchange data only through LDS: the fences are restricted to

@@ -336,3 +336,70 @@ def test_chunk_stage2_records_fp32(seed):
             err = np.abs(got - want).max()
             assert err <= 2e-5 * max(1.0, np.abs(want).max()), (name, hv, c, err)
         assert np.abs(aqk[L:]).max(initial=0) == 0 and np.abs(w[L:]).max(initial=0) == 0
+
+
+@pytest.mark.parametrize("steep", [False, True])
+def test_chunk_stage2_records_bf16(steep):
+    """The bf16 intra kernel's records against the fp64 chunk algebra of the same (bf16)
+    inputs, K = V = 128, GVA 2 -> 4 value heads, a short last chunk. Each stored quantity
+    is decoded from its layout (hi + lo where it carries a residual tile). ``steep``
+    puts gates down to -15 into the second chunk so its diagonal blocks take the exact
+    one-sided branch."""
+    import gated_delta_rule_64_amd as kda
+    K = V = 128
+    d = small(1, 128 + 37, 2, 4, K, V, torch.bfloat16, seed=21)
+    if steep:
+        g = d["g"].clone()
+        g[:, 64:128, 1] = -15.0
+        d["g"] = g
+    B, T, H, _ = d["q"].shape
+    HV = 4
+    nbytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, torch.bfloat16)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    run("chunk", d, workspace=ws)
+    _, _, stages = chunked_ref.chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                       None, None, return_stages=True)
+    e2 = 2
+    rec = (64 * K * e2 * 5 + 64 * 64 * e2 * 2 + 64 * V * 4 + 4 * K + 255) // 256 * 256
+    raw = ws.cpu()
+    NT = (T + 63) // 64
+    sched = (((3 * B + 1) * 4 + 15) // 16 * 16 + B * NT * 8 + 255) // 256 * 256
+    scale = K ** -0.5
+    # relative bounds: single-bf16 tiles (w) and the fp32 u built from the bf16 T beta
+    # carry bf16 rounding; the hi + lo tiles and 2^G are fp32-level
+    bounds = {"Aqk": 2e-5, "w": 1e-2, "u": 1e-2, "qg": 2e-5, "kgT": 2e-5, "2^G": 2e-5}
+    worst = {}
+    for st in stages:
+        hv, c = st["hv"], st["start"] // 64
+        base = sched + (hv * NT + c) * rec
+        L = st["length"]
+
+        def bf(off, n):
+            return raw[base + off: base + off + 2 * n].view(torch.bfloat16).double().numpy()
+
+        def frag(off, R, KC, split):
+            x = bf(off, R * KC)
+            if split:
+                x = x + bf(off + 2 * R * KC, R * KC)
+            return x[frag_tile_index(R, KC, 32, 8)]
+        off = 0
+        w = frag(off, 64, K, False); off += 64 * K * 2
+        qg = frag(off, 64, K, True); off += 2 * 64 * K * 2
+        kgT = frag(off, K, 64, True); off += 2 * K * 64 * 2
+        aqk = frag(off, 64, 64, True); off += 2 * 64 * 64 * 2
+        u = raw[base + off: base + off + 4 * 64 * V].view(torch.float32).double().numpy()[acc_tile_index(64, V)]
+        off += 64 * V * 4
+        eg = raw[base + off: base + off + 4 * K].view(torch.float32).double().numpy()
+        for name, got, want in (("Aqk", aqk[:L, :L], st["Aqk"]), ("w", w[:L], st["w"]),
+                                ("u", u[:L], st["u"]), ("qg", qg[:L], scale * st["qg"]),
+                                ("kgT", kgT[:, :L], st["kg"].T), ("2^G", eg, np.exp2(st["G"]))):
+            rel = np.abs(got - want).max() / max(1e-30, np.abs(want).max())
+            worst[name] = max(worst.get(name, 0.0), rel)
+            if rel > bounds[name]:
+                bad = np.unravel_index(np.argmax(np.abs(got - want)), got.shape)
+                log(f"  {name} hv={hv} chunk={c}: rel err {rel:.3e} at {bad}: got {got[bad]:.6e} want {want[bad]:.6e}")
+        assert np.abs(aqk[L:]).max(initial=0) == 0 and np.abs(w[L:]).max(initial=0) == 0
+        assert np.abs(qg[L:]).max(initial=0) == 0 and np.abs(kgT[:, L:]).max(initial=0) == 0
+    log("  worst relative error per record: " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    for name, b in bounds.items():
+        assert worst[name] <= b, (name, worst[name], b)
