@@ -109,6 +109,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also launch one plain elementwise kernel that reads and writes 1 GiB "
+                         "(torch.neg on fp32), outside the timed region: the reference for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -151,6 +155,13 @@ def main():
         if rc != 0:
             raise RuntimeError(lib.kda_last_error().decode())
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)          # 1 GiB read + 1 GiB written by one plain kernel
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         call(None)
     torch.cuda.synchronize()

@@ -1092,11 +1092,12 @@ struct ScanParams {
 // and K/64 16-row bands of the state (for the state update), so the record operands a
 // wave multiplies (w, qg, Aqk rows of its band; kg^T rows of its state bands; u and
 // 2^G entries) are private to it: they go from the record straight into registers in
-// matrix-core fragment layout, one chunk ahead. Only the operands every wave needs --
-// the state S^T and v'^T, both produced inside the block -- pass through LDS. To cover
-// HBM latency beyond one step, every block also touches the record WARM chunks ahead so
-// it is in L2 when its fragments are loaded.
-constexpr int WARM = 4;
+// matrix-core fragment layout, PREFETCH chunks ahead (a ring of register buffers, so a
+// step never waits on data requested less than PREFETCH steps earlier). Only the
+// operands every wave needs -- the state S^T and v'^T, both produced inside the block
+// -- pass through LDS. o is formed transposed, so each lane stores four consecutive
+// columns of one row.
+constexpr int PREFETCH = 3;
 
 template <int K, int V, int BV, typename TW>
 struct ScanFrags {
@@ -1165,7 +1166,7 @@ __device__ __forceinline__ void load_frags(ScanFrags<K, V, BV, TW>& F, const cha
 }
 
 template <int K, int V, int BV, typename TIn>
-__global__ __launch_bounds__(NTHREADS) void scan_kernel(ScanParams p) {
+__global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
     typedef TIn TW;
     typedef ScanFrags<K, V, BV, TW> SF;
     typedef typename SF::frag frag;
@@ -1202,36 +1203,31 @@ __global__ __launch_bounds__(NTHREADS) void scan_kernel(ScanParams p) {
     const int c1 = p.cend[n];
     auto record = [&](int c) { return p.rec + ((size_t)hv * p.NCmax + c) * p.rec_bytes; };
 
+    // four consecutive rows row0.. of column col of a transposed tile, one vector write
+    // per part (hi and, on the bf16 path, lo)
     auto put4 = [&](TW* hi, TW* lo, int col, int row0, f32x4 x, auto tile_tag) {
         typedef decltype(tile_tag) TT;
+        typedef __attribute__((ext_vector_type(4))) TW vec4;
         const int base = TT::idx(col, row0);
+        vec4 h, l;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const TW h = from_f32<TW>(x[r]);
-            hi[base + r] = h;
-            if constexpr (SPLIT) lo[base + r] = from_f32<TW>(x[r] - to_f32(h));
+            h[r] = from_f32<TW>(x[r]);
+            if constexpr (SPLIT) l[r] = from_f32<TW>(x[r] - to_f32(h[r]));
         }
+        *reinterpret_cast<vec4*>(hi + base) = h;
+        if constexpr (SPLIT) *reinterpret_cast<vec4*>(lo + base) = l;
     };
 
-    // L2 warming: one dword per 128-byte line of a record, spread over the block
-    const int warm_lines = (int)(p.rec_bytes / 128);
-    uint32_t warm_acc = 0;
-    uint32_t warm_val[4] = {0u, 0u, 0u, 0u};
-    auto warm = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) warm_acc ^= warm_val[i];
-        const uint32_t* base = reinterpret_cast<const uint32_t*>(record(c < c1 ? c : c1 - 1));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int line = tid + i * NTHREADS;
-            warm_val[i] = base[(line < warm_lines ? line : 0) * 32];
-        }
-    };
-
-    ScanFrags<K, V, BV, TW> F0, F1;
+    // prefetch ring: buffer b holds chunk c0 + b, c0 + b + PREFETCH, ...; past the end a
+    // buffer re-reads the last chunk (in bounds, never used)
+    static_assert(PREFETCH == 3, "the loop below is unrolled for three buffers");
+    auto clampc = [&](int c) { return c < c1 ? c : c1 - 1; };
+    ScanFrags<K, V, BV, TW> F0, F1, F2;
     if (c0 < c1) {
-        for (int c = c0; c < c0 + WARM; ++c) warm(c);
         load_frags<K, V, BV, TW>(F0, record(c0), p, c0, wave, lr, lq, v0);
+        load_frags<K, V, BV, TW>(F1, record(clampc(c0 + 1)), p, clampc(c0 + 1), wave, lr, lq, v0);
+        load_frags<K, V, BV, TW>(F2, record(clampc(c0 + 2)), p, clampc(c0 + 2), wave, lr, lq, v0);
     }
 
     // state bands owned by this wave: dt = wave + 4 * a
@@ -1296,35 +1292,38 @@ __global__ __launch_bounds__(NTHREADS) void scan_kernel(ScanParams p) {
 #pragma unroll
                 for (int jj = 0; jj < NJS; ++jj)
                     vb[nt][sx][jj] = TV::frag(Vt[sx], 16 * nt + lr, jj * KS + lq * KPL);
-        // o = qg S + Aqk v'
+        // o^T = S^T qg^T + v'^T Aqk^T: lane (lq, lr) gets row 16 wave + lr, columns
+        // 16 nt + 4 lq .. +3
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < NKS; ++kk) {
-                acc = M::mma(F.q[0][kk], sb[nt][0][kk], acc);
+                acc = M::mma(sb[nt][0][kk], F.q[0][kk], acc);
                 if constexpr (SPLIT) {
-                    acc2 = M::mma(F.q[1][kk], sb[nt][0][kk], acc2);
-                    acc2 = M::mma(F.q[0][kk], sb[nt][1][kk], acc2);
+                    acc2 = M::mma(sb[nt][0][kk], F.q[1][kk], acc2);
+                    acc2 = M::mma(sb[nt][1][kk], F.q[0][kk], acc2);
                 }
             }
 #pragma unroll
             for (int jj = 0; jj < NJS; ++jj) {
                 if (jj < njs_w) {
-                    acc = M::mma(F.a[0][jj], vb[nt][0][jj], acc);
+                    acc = M::mma(vb[nt][0][jj], F.a[0][jj], acc);
                     if constexpr (SPLIT) {
-                        acc2 = M::mma(F.a[1][jj], vb[nt][0][jj], acc2);
-                        acc2 = M::mma(F.a[0][jj], vb[nt][1][jj], acc2);
+                        acc2 = M::mma(vb[nt][0][jj], F.a[1][jj], acc2);
+                        acc2 = M::mma(vb[nt][1][jj], F.a[0][jj], acc2);
                     }
                 }
             }
             acc += acc2;
+            const int i = 16 * wave + lr;
+            if (i < len) {
+                typedef __attribute__((ext_vector_type(4))) TIn ovec;
+                ovec ov;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * wave + 4 * lq + r;
-                if (i < len)
-                    o[((size_t)(rs + i) * p.HV + hv) * V + v0 + 16 * nt + lr] = from_f32<TIn>(acc[r]);
+                for (int r = 0; r < 4; ++r) ov[r] = from_f32<TIn>(acc[r]);
+                *reinterpret_cast<ovec*>(o + ((size_t)(rs + i) * p.HV + hv) * V + v0 + 16 * nt + 4 * lq) = ov;
             }
         }
         // S = 2^G S + kg^T v'
@@ -1353,22 +1352,18 @@ __global__ __launch_bounds__(NTHREADS) void scan_kernel(ScanParams p) {
         lds_barrier();
     };
 
-    // two chunks per trip so the prefetch buffers alternate without register copies;
-    // past the end the prefetch re-reads the last chunk (in bounds, unused)
-    for (int c = c0; c < c1; c += 2) {
-        const int c_1 = c + 1 < c1 ? c + 1 : c1 - 1;
-        load_frags<K, V, BV, TW>(F1, record(c_1), p, c_1, wave, lr, lq, v0);
-        warm(c + WARM);
+    // three chunks per trip so the ring buffers rotate without register copies; each
+    // buffer is refilled right after its step, PREFETCH chunks ahead
+    for (int c = c0; c < c1; c += 3) {
         step(F0);
+        load_frags<K, V, BV, TW>(F0, record(clampc(c + 3)), p, clampc(c + 3), wave, lr, lq, v0);
         if (c + 1 >= c1) break;
-        const int c_2 = c + 2 < c1 ? c + 2 : c1 - 1;
-        load_frags<K, V, BV, TW>(F0, record(c_2), p, c_2, wave, lr, lq, v0);
-        warm(c + 1 + WARM);
         step(F1);
+        load_frags<K, V, BV, TW>(F1, record(clampc(c + 4)), p, clampc(c + 4), wave, lr, lq, v0);
+        if (c + 2 >= c1) break;
+        step(F2);
+        load_frags<K, V, BV, TW>(F2, record(clampc(c + 5)), p, clampc(c + 5), wave, lr, lq, v0);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) warm_acc ^= warm_val[i];
-    if (p.NCmax < 0) o[0] = from_f32<TIn>((float)warm_acc);   // never true: keeps the warming loads
 
     if (p.final_state) {
 #pragma unroll
