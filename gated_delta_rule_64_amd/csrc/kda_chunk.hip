@@ -1413,12 +1413,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
 constexpr int SCAN8_THREADS = 512;
 constexpr int ROW_PREFETCH = 2;     // row waves: chunks in flight
 constexpr int STATE_PREFETCH = 3;   // state waves: chunks in flight
-// L2 warming: the records come from HBM, and at HBM latency the misses a CU can keep in
-// flight cap its fetch rate. The state waves touch one line per thread of the record
-// WARM_AHEAD chunks ahead (each of a chain's slice blocks a different eighth of the
-// lines), so the fragment loads that follow hit L2. The touched values are consumed
-// only when their ring buffer is refilled, three steps later, so no step waits on them.
-constexpr int WARM_AHEAD = 8;
 
 template <int K, int BV>
 struct RowFrags {
@@ -1435,7 +1429,6 @@ struct StateFrags {
     static constexpr int NDT = K / 64, NJS = C / 32;
     bf16x8 g[NDT][2][NJS]; // kg^T hi, lo of the wave's state bands
     f32x4 e[NDT];          // 2^G of those bands
-    uint32_t warm;         // one dword of a record further ahead (L2 warming)
 };
 
 // Row operands are loaded in two parts, each as soon as the previous chunk's values of
@@ -1477,14 +1470,11 @@ __device__ __forceinline__ void load_row_a(RowFrags<K, BV>& F, const char* rec, 
                                    : bf16x8{};
 }
 
-// State operands in two parts: 2^G (used by the decay, before the v' barrier) and kg^T;
-// the first part also touches line `line` of the record `wrec` (warming).
+// State operands in two parts: 2^G (used by the decay, before the v' barrier) and kg^T.
 template <int K, int BV>
 __device__ __forceinline__ void load_state_e(StateFrags<K, BV>& F, const char* rec, const ScanParams& p,
-                                             int sw, int lane, const char* wrec, int line, uint32_t& sink) {
+                                             int sw, int lane) {
     const int lq = lane >> 4;
-    sink ^= F.warm;
-    F.warm = *reinterpret_cast<const uint32_t*>(wrec + (size_t)line * 128);
     const float* eg = reinterpret_cast<const float*>(rec + p.off_eg);
 #pragma unroll
     for (int a = 0; a < StateFrags<K, BV>::NDT; ++a)
@@ -1643,18 +1633,12 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
         const size_t sbase = ((size_t)n * p.HV + hv) * (size_t)K * V;
         StateFrags<K, BV> G0, G1, G2;
         static_assert(STATE_PREFETCH == 3, "the state loop is unrolled for three buffers");
-        // warming lines of this block: vt, vt + 8, ... (this thread: vt + 8 (tid - 256))
-        const int nlines = (int)(p.rec_bytes / 128);
-        const int wline0 = vt % 8 + 8 * (tid - 256);
-        const int wline = wline0 < nlines ? wline0 : vt % 8;
-        uint32_t wsink = 0;
-        G0.warm = G1.warm = G2.warm = 0u;
         if (c0 < c1) {
-            load_state_e<K, BV>(G0, record(c0), p, sw, lane, record(c0 + WARM_AHEAD), wline, wsink);
+            load_state_e<K, BV>(G0, record(c0), p, sw, lane);
             load_state_g<K, BV>(G0, record(c0), p, sw, lane);
-            load_state_e<K, BV>(G1, record(c0 + 1), p, sw, lane, record(c0 + 1 + WARM_AHEAD), wline, wsink);
+            load_state_e<K, BV>(G1, record(c0 + 1), p, sw, lane);
             load_state_g<K, BV>(G1, record(c0 + 1), p, sw, lane);
-            load_state_e<K, BV>(G2, record(c0 + 2), p, sw, lane, record(c0 + 2 + WARM_AHEAD), wline, wsink);
+            load_state_e<K, BV>(G2, record(c0 + 2), p, sw, lane);
             load_state_g<K, BV>(G2, record(c0 + 2), p, sw, lane);
         }
 #pragma unroll
@@ -1683,7 +1667,7 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                 for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) S[a][nt][r] *= F.e[a][r];
-            load_state_e<K, BV>(F, record(cn), p, sw, lane, record(cn + WARM_AHEAD), wline, wsink);
+            load_state_e<K, BV>(F, record(cn), p, sw, lane);
             lds_barrier();   // A: v' complete
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt) {
@@ -1721,8 +1705,6 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
         }
         if (nsteps % 3 >= 1) step(G0, c + 3);
         if (nsteps % 3 >= 2) step(G1, c + 4);
-        wsink ^= G0.warm ^ G1.warm ^ G2.warm;
-        if (p.NCmax < 0) reinterpret_cast<uint32_t*>(p.o)[0] = wsink;   // never true: keeps the warming loads
         if (p.final_state) {
 #pragma unroll
             for (int a = 0; a < NDT; ++a)
