@@ -37,6 +37,16 @@ constexpr float SPREAD_LIMIT = 100.0f;
 // byte offset of the chunk table inside the schedule
 inline size_t sched_table_offset(int N) { return ((size_t)(3 * (size_t)N + 1) * 4 + 15) / 16 * 16; }
 
+// Chunk c as (first row in the [B*T] row space, rows). Dense mode (no offsets): chunk c
+// is chunk c % NT of sequence c / NT, computed here; packed mode: the schedule's table.
+__device__ __forceinline__ int2 chunk_pos(bool dense, int NT, int T, const int2* table, int c) {
+    if (dense) {
+        const int ci = c % NT;
+        return make_int2((c / NT) * T + ci * C, T - ci * C < C ? T - ci * C : C);
+    }
+    return table[c];
+}
+
 __device__ __forceinline__ int xcd_remap(int b, int G) {
     // blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous run of
     // work items so neighbouring items (same chain, same chunk) share an L2
@@ -194,8 +204,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
     const int c = item / p.HV;
     const int h = hv / (p.HV / p.H);
 
-    if (c >= p.nchunks[0]) return;
-    const int2 cpos = p.table[c];
+    if (!p.dense && c >= p.nchunks[0]) return;
+    const int2 cpos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
     const long long rs = cpos.x;   // first row of the chunk in the [B*T] row space
     const int len = cpos.y;
     const TIn* q = reinterpret_cast<const TIn*>(p.q);
@@ -690,18 +700,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
 
     // chunk position: computed in dense mode (no dependent loads before the inputs),
     // else from the schedule's table
-    long long rs;
-    int len;
-    if (p.dense) {
-        const int ci = c % p.NT;
-        rs = (long long)(c / p.NT) * p.T + (long long)ci * C;
-        len = p.T - ci * C < C ? p.T - ci * C : C;
-    } else {
-        if (c >= p.nchunks[0]) return;
-        const int2 cpos = p.table[c];
-        rs = cpos.x;
-        len = cpos.y;
-    }
+    if (!p.dense && c >= p.nchunks[0]) return;
+    const int2 cpos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
+    const long long rs = cpos.x;
+    const int len = cpos.y;
     char* rec = p.rec + ((size_t)hv * p.NCmax + c) * p.rec_bytes;
     TW* out_w = reinterpret_cast<TW*>(rec + p.off_w);
     TW* out_qg = reinterpret_cast<TW*>(rec + p.off_qg);
@@ -1106,6 +1108,7 @@ struct ScanParams {
     const int32_t* slot_ok;  // sequence validity (packed offsets checked per slot)
     const int2* table;       // chunk table: (first row, rows)
     int N, T, HV, NT, NCmax;
+    int dense;               // no offsets: sequence n is chunks n NT .. n NT + NT - 1, no schedule
 };
 
 // Scan design. Each of the four waves owns a 16-row band of the chunk (for v' and o)
@@ -1144,7 +1147,7 @@ __device__ __forceinline__ void load_frags(ScanFrags<K, V, BV, TW>& F, const cha
                                            int lq, int v0) {
     // everything below is straight-line code: the compiler then waits for exactly these
     // loads when they are used, never for later prefetches
-    F.pos = p.table[c];
+    F.pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
     typedef ScanFrags<K, V, BV, TW> SF;
     typedef typename SF::frag frag;
     constexpr int KS = SF::M::KS, KPL = SF::M::KPL;
@@ -1218,9 +1221,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
     // Aqk rows 16*wave.. are zero past column 16*wave+15: fewer contraction steps
     const int njs_w = (16 * wave + 16 + KS - 1) / KS;
 
-    if (!p.slot_ok[n]) return;    // malformed offsets: leave this slot untouched
-    const int c0 = p.coff[n];
-    const int c1 = p.cend[n];
+    if (!p.dense && !p.slot_ok[n]) return;    // malformed offsets: leave this slot untouched
+    const int c0 = p.dense ? n * p.NT : p.coff[n];
+    const int c1 = p.dense ? c0 + p.NT : p.cend[n];
     auto record = [&](int c) { return p.rec + ((size_t)hv * p.NCmax + c) * p.rec_bytes; };
 
     // four consecutive rows row0.. of column col of a transposed tile, one vector write
@@ -1458,7 +1461,7 @@ template <int K, int BV>
 __device__ __forceinline__ void load_row_a(RowFrags<K, BV>& F, const char* rec, const ScanParams& p,
                                            int c, int b, int lane) {
     typedef FragTile<__bf16, C, C> FQ;
-    F.pos = p.table[c];
+    F.pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
     const __bf16* aqk = reinterpret_cast<const __bf16*>(rec + p.off_aqk);
     // band b of the lower-triangular Aqk has nonzero columns only below 16b + 16
     const int njs = (16 * b + 16 + 31) / 32;
@@ -1519,9 +1522,9 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
     const int n = chain / p.HV;
     const int v0 = vt * BV;
 
-    if (!p.slot_ok[n]) return;    // malformed offsets: leave this slot untouched
-    const int c0 = p.coff[n];
-    const int c1 = p.cend[n];
+    if (!p.dense && !p.slot_ok[n]) return;    // malformed offsets: leave this slot untouched
+    const int c0 = p.dense ? n * p.NT : p.coff[n];
+    const int c1 = p.dense ? c0 + p.NT : p.cend[n];
     auto record = [&](int c) { return p.rec + ((size_t)hv * p.NCmax + (c < c1 ? c : c1 - 1)) * p.rec_bytes; };
     auto clampc = [&](int c) { return c < c1 ? c : c1 - 1; };
 
@@ -1728,14 +1731,17 @@ hipError_t launch_scan(const ChunkArgs& a, const ScanParams& sp);
 template <int K, int V, typename TIn, typename TB>
 hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     char* ws = reinterpret_cast<char*>(a.workspace);
-    const int NT = 0;   // chunk positions always come from the schedule
+    // dense mode (no offsets): B sequences of T rows, NT = ceil(T / 64) chunks each; every
+    // kernel computes chunk positions itself and the schedule kernel is not launched
+    const bool dense = a.cu_seqlens == nullptr;
+    const int NT = (a.T + C - 1) / C;
     int32_t *coff = nullptr, *cend = nullptr, *slot_ok = nullptr, *nch = nullptr;
     int2* table = nullptr;
     if (a.events) {
         hipError_t err = hipEventRecord(a.events[0], a.stream);
         if (err != hipSuccess) return err;
     }
-    {
+    if (!dense) {
         coff = reinterpret_cast<int32_t*>(ws);
         cend = coff + a.N;
         slot_ok = cend + a.N;
@@ -1758,9 +1764,8 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     ip.rec_bytes = L.rec_bytes; ip.off_w = L.off_w; ip.off_u = L.off_u; ip.off_qg = L.off_qg;
     ip.off_kgT = L.off_kgT; ip.off_aqk = L.off_aqk; ip.off_eg = L.off_eg;
     ip.T = a.T; ip.H = a.H; ip.HV = a.HV; ip.NCmax = L.NCmax;
-    // dense mode: NCmax = B * ceil(T / 64) chunks, all present
-    ip.dense = a.cu_seqlens == nullptr;
-    ip.NT = (a.T + C - 1) / C;
+    ip.dense = dense;   // then NCmax = B * NT chunks, all present
+    ip.NT = NT;
     ip.scale = a.scale;
     const long long nintra = (long long)L.NCmax * a.HV;
     if (nintra > 0) {
@@ -1780,6 +1785,7 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     sp.initial_state = a.initial_state; sp.final_state = a.final_state; sp.o = a.o;
     sp.coff = coff; sp.cend = cend; sp.slot_ok = slot_ok; sp.table = table;
     sp.N = a.N; sp.T = a.T; sp.HV = a.HV; sp.NT = NT; sp.NCmax = L.NCmax;
+    sp.dense = dense;
     if (a.events) {
         hipError_t err = hipEventRecord(a.events[2], a.stream);
         if (err != hipSuccess) return err;
