@@ -10,6 +10,8 @@ Contents
   * ``chunked``    -- the chunk decomposition of the same recurrence, written in numpy
                       fp64 with a free chunk size (``chunked.py``); used for stage-level
                       checks and pinned against ``recurrent``.
+  * ``gate_activation`` -- the fused gate activation (raw gate input -> per-token log2
+                      decay), numpy fp64 (``gate.py``).
 
 All inputs are converted to float64 exactly (bf16 and fp32 values are exactly
 representable), so the oracle sees the very values the GPU sees.
@@ -137,3 +139,4 @@ def recurrent(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None,
 
 
 from . import chunked  # noqa: E402  (numpy only; no dependency on the library above)
+from .gate import gate_activation  # noqa: E402,F401  (numpy only)
