@@ -13,6 +13,8 @@ Also reported on the same JSON line:
                  stream) against HBM peak, with that kernel's algorithmic bytes;
   * path      -- the whole step against the HBM floor of the workload's own inputs and
                  outputs (336.1 MB), and the matrix-core fractions;
+  * gated     -- the same forward with the gate activation fused into Stage 1 (raw bf16
+                 gate input instead of the fp32 log2 decay);
   * decode    -- the per-token recurrent forward on 4096 sequences x 32 heads (one token
                  each, fp32 states in and out): state GB/s and fraction of HBM peak;
   * cpu_baseline -- the fp64 CPU oracle on the full headline workload, host threads.
@@ -197,6 +199,29 @@ def main():
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(dom)
 
+    # the same forward with the gate activation fused into Stage 1: raw bf16 gate input,
+    # A_log = log(U[1, 2]) per head, dt_bias N(0, 0.5^2) (timed like the headline)
+    gen = torch.Generator().manual_seed(w.seed + 100)
+    g_raw = torch.randn(B, T, HV, K, generator=gen).mul(2.0).to(torch.bfloat16).to(dev)
+    A_log = torch.rand(HV, generator=gen).add(1.0).log().to(dev)
+    dt_bias = torch.randn(HV * K, generator=gen).mul(0.5).to(dev)
+
+    def gcall():
+        kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], g_raw, d["beta"], A_log, dt_bias, None,
+                                None, None, out=out, workspace=ws)
+    for _ in range(args.warmup):
+        gcall()
+    torch.cuda.synchronize()
+    gev = Events(hip, 2)
+    hip.hipEventRecord(gev.ev[0], sptr)
+    for _ in range(steps):
+        gcall()
+    hip.hipEventRecord(gev.ev[1], sptr)
+    torch.cuda.synchronize()
+    gated_ms = gev.ms(0, 1) / steps
+    gev.close()
+    del g_raw, A_log, dt_bias
+
     # decode: 4096 sequences x 32 heads, one token each, fp32 states in and out
     del ws, out
     dd = inputs.make("dec", device=dev)
@@ -245,6 +270,8 @@ def main():
                  "hbm_frac": path_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "mfma_frac_exact_flops": flops_exact / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                  "mfma_frac_dense_tile_flops": flops_dense / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "gated": {"workload": "the headline forward with the gate activation fused into Stage 1 (raw bf16 gate input, A_log, dt_bias)",
+                  "ms_per_step": gated_ms, "tokens_per_s": tokens / (gated_ms * 1e-3)},
         "decode": {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
                    "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
                    "bytes": dec_bytes},

@@ -8,6 +8,8 @@ library on a GPU every call raises.
 
 Entry points (same names as the C ABI):
   kda_chunk_fwd(q, k, v, g, beta, ...)      chunked prefill forward
+  kda_chunk_fwd_gated(q, k, v, g_raw, beta, A_log, ...)
+                                             the same with the gate activation fused in
   kda_recurrent_fwd(q, k, v, g, beta, ...)  per-token recurrent forward (decode)
   kda_chunk_fwd_workspace_bytes(...)         workspace size query
   kda_last_error()                           reason for the last failure
@@ -20,6 +22,7 @@ from ._lib import (  # noqa: F401
     KDA_F32,
     KdaError,
     kda_chunk_fwd,
+    kda_chunk_fwd_gated,
     kda_chunk_fwd_workspace_bytes,
     kda_last_error,
     kda_recurrent_fwd,
@@ -28,7 +31,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "kda_chunk_fwd", "kda_recurrent_fwd", "kda_chunk_fwd_workspace_bytes", "kda_last_error",
-    "KdaError", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
+    "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_recurrent_fwd", "kda_chunk_fwd_workspace_bytes",
+    "kda_last_error", "KdaError", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
     "library_path",
 ]

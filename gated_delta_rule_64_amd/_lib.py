@@ -46,6 +46,10 @@ def load_library():
         lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                       i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                       vp, sz, vp, vp]
+        lib.kda_chunk_fwd_gated.restype = i32
+        lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp,
+                                            vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            i32, ctypes.c_float, i32, vp, sz, vp, vp]
         lib.kda_recurrent_fwd.restype = i32
         lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                           i32, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp]
@@ -91,7 +95,7 @@ def _check_device(tensors):
     return dev
 
 
-def _common(q, k, v, g, beta, initial_state, cu_seqlens):
+def _common(q, k, v, g, beta, initial_state, cu_seqlens, raw_gate=False):
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k must be [B, T, H, K] and v [B, T, HV, V]")
     B, T, H, K = q.shape
@@ -104,8 +108,10 @@ def _common(q, k, v, g, beta, initial_state, cu_seqlens):
         raise ValueError(f"g must be {[B, T, HV, K]}, got {list(g.shape)}")
     if tuple(beta.shape) != (B, T, HV):
         raise ValueError(f"beta must be {[B, T, HV]}, got {list(beta.shape)}")
-    if g.dtype != torch.float32:
+    if not raw_gate and g.dtype != torch.float32:
         raise TypeError("g must be float32 (per-token log2 decay)")
+    if raw_gate and g.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("the raw gate input must be float32 or bfloat16")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
     qkv = _dtype_code(q, "q")
@@ -163,6 +169,46 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
                            qkv, bdt, float(scale or 0.0), 64, _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _ptr(dev_status),
                            _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    return out, final_state
+
+
+def kda_chunk_fwd_gated(q, k, v, g_raw, beta, A_log, dt_bias=None, lower_bound=None,
+                        initial_state=None, cu_seqlens=None, output_final_state=False, scale=None,
+                        *, out=None, final_state=None, workspace=None, dev_status=None):
+    """Chunked KDA forward with the gate activation fused into Stage 1.
+
+    ``g_raw`` is the raw gate input [B, T, HV, K] (bfloat16 or float32); the library forms
+    the per-token log2 decay -exp(A_log[hv]) * softplus(g_raw + dt_bias[hv, d]) / ln 2,
+    the natural-log activation clamped from below at ``lower_bound`` (a negative float)
+    when one is given. ``A_log``: float32 [HV]; ``dt_bias``: float32 [HV * K] or [HV, K],
+    or None for zeros. Returns ``(o, final_state or None)`` like ``kda_chunk_fwd``.
+    """
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g_raw, beta, initial_state, cu_seqlens,
+                                                  raw_gate=True)
+    if A_log.dtype != torch.float32 or A_log.numel() != HV:
+        raise ValueError(f"A_log must be float32 with {HV} elements")
+    if dt_bias is not None and (dt_bias.dtype != torch.float32 or dt_bias.numel() != HV * K):
+        raise ValueError(f"dt_bias must be float32 with {HV * K} elements")
+    _check_device([("g_raw", g_raw), ("A_log", A_log), ("dt_bias", dt_bias)])
+    if out is None:
+        out = torch.empty_like(v)
+    if output_final_state and final_state is None:
+        final_state = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev)
+    if not output_final_state:
+        final_state = None
+    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, N, int(cu_seqlens is not None), qkv)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _dtype_code(g_raw, "g_raw"),
+                                 _ptr(A_log), _ptr(dt_bias), int(lower_bound is not None),
+                                 float(lower_bound if lower_bound is not None else 0.0), _ptr(beta),
+                                 _ptr(initial_state), _ptr(cu_seqlens), N, _ptr(out),
+                                 _ptr(final_state), B, T, H, HV, K, V, qkv, bdt, float(scale or 0.0),
+                                 64, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _ptr(dev_status), _stream(dev))
     if rc != 0:
         raise KdaError(rc, lib.kda_last_error().decode())
     return out, final_state

@@ -84,16 +84,36 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                                workspace, workspace_bytes, dev_status, stream, nullptr);
 }
 
-int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float* g,
-                        const void* beta, const float* initial_state,
-                        const int32_t* cu_seqlens, int N, void* o, float* final_state, int B,
-                        int T, int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
-                        float scale, int chunk_size, void* workspace, size_t workspace_bytes,
-                        int32_t* dev_status, hipStream_t stream, hipEvent_t* events) {
-    clear_error();
-    int rc = check_common(q, k, v, g, beta, initial_state, cu_seqlens, N, o, final_state, B, T,
-                          H, HV, K, V, qkv_dtype, beta_dtype);
+}  // extern "C"
+
+namespace {
+
+// The chunked forward behind every chunk entry point; `gate` describes where the Stage 1
+// loads take the per-token log2 decay from (`g` for GATE_LOG2).
+struct GateSpec {
+    int mode;
+    const void* g_raw;
+    const float* A_log;
+    const float* dt_bias;
+    int has_lower_bound;
+    float lower_bound;
+};
+
+int chunk_impl(const void* q, const void* k, const void* v, const float* g, const GateSpec& gate,
+               const void* beta, const float* initial_state, const int32_t* cu_seqlens, int N,
+               void* o, float* final_state, int B, int T, int H, int HV, int K, int V,
+               int qkv_dtype, int beta_dtype, float scale, int chunk_size, void* workspace,
+               size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
+               hipEvent_t* events) {
+    const float* g_checked = gate.mode == kda::GATE_LOG2 ? g : reinterpret_cast<const float*>(gate.g_raw);
+    int rc = check_common(q, k, v, g_checked, beta, initial_state, cu_seqlens, N, o, final_state, B,
+                          T, H, HV, K, V, qkv_dtype, beta_dtype);
     if (rc != KDA_OK) return rc;
+    if (gate.mode != kda::GATE_LOG2 && (long long)B * T > 0) {
+        if (!gate.A_log) return fail(KDA_ERR_NULL, "A_log must be non-NULL");
+        if (!aligned16(gate.dt_bias))
+            return fail(KDA_ERR_SHAPE, "dt_bias must be 16-byte aligned");
+    }
     if (chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64, got %d", chunk_size);
     if (K != 64 && K != 128)
@@ -115,6 +135,8 @@ int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float
     }
     kda::ChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.g_raw = gate.g_raw; a.gate_mode = gate.mode; a.A_log = gate.A_log; a.dt_bias = gate.dt_bias;
+    a.has_lower_bound = gate.has_lower_bound; a.lower_bound = gate.lower_bound;
     a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
     a.o = o; a.final_state = final_state;
     a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
@@ -126,6 +148,43 @@ int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float
     if (err != hipSuccess)
         return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, int N, void* o, float* final_state, int B,
+                        int T, int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
+                        float scale, int chunk_size, void* workspace, size_t workspace_bytes,
+                        int32_t* dev_status, hipStream_t stream, hipEvent_t* events) {
+    clear_error();
+    const GateSpec gate{kda::GATE_LOG2, nullptr, nullptr, nullptr, 0, 0.0f};
+    return chunk_impl(q, k, v, g, gate, beta, initial_state, cu_seqlens, N, o, final_state, B, T,
+                      H, HV, K, V, qkv_dtype, beta_dtype, scale, chunk_size, workspace,
+                      workspace_bytes, dev_status, stream, events);
+}
+
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* g_raw,
+                        int g_dtype, const float* A_log, const float* dt_bias,
+                        int has_lower_bound, float lower_bound, const void* beta,
+                        const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                        float* final_state, int B, int T, int H, int HV, int K, int V,
+                        int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                        void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                        hipStream_t stream) {
+    clear_error();
+    if (g_dtype != KDA_BF16 && g_dtype != KDA_F32)
+        return fail(KDA_ERR_DTYPE, "g_dtype must be KDA_BF16 (1) or KDA_F32 (0), got %d", g_dtype);
+    if (has_lower_bound && !(lower_bound < 0.0f && isfinite(lower_bound)))
+        return fail(KDA_ERR_SHAPE, "lower_bound must be negative and finite, got %g", (double)lower_bound);
+    const GateSpec gate{g_dtype == KDA_BF16 ? kda::GATE_RAW_BF16 : kda::GATE_RAW_F32, g_raw, A_log,
+                        dt_bias, has_lower_bound ? 1 : 0, lower_bound};
+    return chunk_impl(q, k, v, nullptr, gate, beta, initial_state, cu_seqlens, N, o, final_state,
+                      B, T, H, HV, K, V, qkv_dtype, beta_dtype, scale, chunk_size, workspace,
+                      workspace_bytes, dev_status, stream, nullptr);
 }
 
 int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* g,

@@ -138,7 +138,64 @@ struct IntraParams {
     int T, H, HV, NT, NCmax;
     int dense;                // no offsets: chunk c is chunk c % NT of sequence c / NT
     float scale;
+    // per-token log2 decay: p.g as given (GATE_LOG2), or formed from the raw gate input
+    const void* g_raw;
+    int gate_mode;
+    const float* A_log;       // [HV]
+    const float* dt_bias;     // [HV * K] or null
+    int has_lower_bound;
+    float lower_bound;
 };
+
+// Channels d0 .. d0+7 of the per-token log2 decay at row r, value head hv: loaded as
+// given, or formed from the raw gate input by the fused activation
+// -exp(A_log[hv]) softplus(g_raw + dt_bias[hv, d]) / ln 2, the natural-log value clamped
+// from below at lower_bound when one is set (stage 1 of the chunk algebra, with the gate
+// activation fused into the cumsum's loads).
+template <int K>
+__device__ __forceinline__ void load_gate8(const IntraParams& p, size_t r, int hv, int d0, float* out) {
+    const size_t base = (r * p.HV + hv) * K + d0;
+    if (p.gate_mode == GATE_LOG2) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p.g + base);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(p.g + base + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { out[e] = a[e]; out[4 + e] = b[e]; }
+        return;
+    }
+    float x[8];
+    if (p.gate_mode == GATE_RAW_BF16) {
+        const bf16x8 h = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.g_raw) + base);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
+    } else {
+        const float* gr = static_cast<const float*>(p.g_raw) + base;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(gr);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(gr + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+    }
+    if (p.dt_bias) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)hv * K + d0);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)hv * K + d0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[e] += a[e]; x[4 + e] += b[e]; }
+    }
+    // log2 decay = -e^A softplus(x) / ln 2 = -e^A log2(1 + 2^(x log2 e)); for x > 15 the
+    // softplus is x to fp32 precision. Where 1 + 2^(x log2 e) rounds to 1 (x below about
+    // -17) the result is 0 instead of a value under 6e-8 e^A: a decay factor off by less
+    // than 4e-8 e^A per token.
+    const float amp = -expf(p.A_log[hv]);
+    constexpr float LOG2E = 1.4426950408889634f;
+    const float lb2 = p.lower_bound * LOG2E;   // the bound in log2 units
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float y = x[e] * LOG2E;
+        const float sp2 = x[e] > 15.f ? y : __builtin_amdgcn_logf(1.f + exp2_fast(y));   // softplus / ln 2
+        float g2 = amp * sp2;
+        if (p.has_lower_bound) g2 = fmaxf(g2, lb2);
+        out[e] = g2;
+    }
+}
 
 // Thread mapping for the elementwise work: thread (cg, rg) owns columns 8cg .. 8cg+7 of
 // rows rg*RPT .. rg*RPT+RPT-1, so every global access is a 16- or 32-byte vector. The
@@ -271,10 +328,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
         const int i = i0 + ii;
         if (i < len) {
             const size_t r = (size_t)(rs + i);
-            const f32x4* gp = reinterpret_cast<const f32x4*>(p.g + (r * p.HV + hv) * K + d0);
-            const f32x4 g0 = gp[0], g1 = gp[1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { gm[ii][e] = g0[e]; gm[ii][4 + e] = g1[e]; }
+            load_gate8<K>(p, r, hv, d0, gm[ii]);
             qv[ii] = *reinterpret_cast<const Row8*>(q + (r * p.H + h) * K + d0);
             kv[ii] = *reinterpret_cast<const Row8*>(k + (r * p.H + h) * K + d0);
         } else {
@@ -727,15 +781,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
         const TW* qp = reinterpret_cast<const TW*>(p.q) + (r_g * p.H + h) * K + 8 * lq;
         const TW* kp = reinterpret_cast<const TW*>(p.k) + (r_g * p.H + h) * K + 8 * lq;
         const TW* vp = reinterpret_cast<const TW*>(p.v) + (r_g * p.HV + hv) * V + 8 * lq;
-        const float* gp = p.g + (r_g * p.HV + hv) * K + 8 * lq;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             qv[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
             kv[s] = *reinterpret_cast<const bf16x8*>(kp + 32 * s);
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp + 32 * s);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(gp + 32 * s + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { loc[s][e] = g0[e]; loc[s][4 + e] = g1[e]; }
+            load_gate8<K>(p, r_g, hv, 32 * s + 8 * lq, loc[s]);
         }
 #pragma unroll
         for (int s = 0; s < NVS; ++s) vv[s] = *reinterpret_cast<const bf16x8*>(vp + 32 * s);
@@ -1767,6 +1817,8 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     ip.dense = dense;   // then NCmax = B * NT chunks, all present
     ip.NT = NT;
     ip.scale = a.scale;
+    ip.g_raw = a.g_raw; ip.gate_mode = a.gate_mode; ip.A_log = a.A_log; ip.dt_bias = a.dt_bias;
+    ip.has_lower_bound = a.has_lower_bound; ip.lower_bound = a.lower_bound;
     const long long nintra = (long long)L.NCmax * a.HV;
     if (nintra > 0) {
         if constexpr (sizeof(TIn) == 2)

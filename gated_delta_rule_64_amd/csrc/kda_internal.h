@@ -26,11 +26,24 @@ struct RecurrentArgs {
     hipStream_t stream;
 };
 
+// How the Stage 1 loads obtain the per-token log2 decay.
+enum GateMode {
+    GATE_LOG2 = 0,       // g: fp32 per-token log2 decay, as given
+    GATE_RAW_F32 = 1,    // g_raw fp32: -exp(A_log) softplus(g_raw + dt_bias) / ln 2
+    GATE_RAW_BF16 = 2    // g_raw bf16: same activation
+};
+
 struct ChunkArgs {
     const void* q;
     const void* k;
     const void* v;
     const float* g;
+    const void* g_raw;         // GATE_RAW_*: raw gate input
+    int gate_mode;
+    const float* A_log;        // [HV]
+    const float* dt_bias;      // [HV * K] or NULL
+    int has_lower_bound;
+    float lower_bound;
     const void* beta;
     const float* initial_state;
     const int32_t* cu_seqlens;
@@ -48,15 +61,16 @@ struct ChunkArgs {
 
 // Workspace layout of the chunked forward (all offsets 256-byte aligned):
 //   [sched]  int32 first_chunk[N], int32 end_chunk[N], int32 slot_ok[N],
-//            int32 n_chunks[1], int2 chunk_table[NCmax] (first row, rows); dense mode
-//            uses it too (N = B sequences of T rows)
+//            int32 n_chunks[1], int2 chunk_table[NCmax] (first row, rows); written in
+//            packed mode only (dense mode computes positions), present in both
 //   [inter]  per (value head hv, chunk c), one record of the Stage 2 results, in order:
 //              w      [64][K]       element type of the compute path (TW)
 //              qg     [NS][64][K]   TW, scale folded in
-//              kgT    [NS][K][64]   TW, transposed
+//              kgT    [NS][K][64]   TW (rows = key channels)
 //              Aqk    [NS][64][64]  TW, scale folded in, zero above the diagonal
-//              uT     [V][64]       fp32, transposed
+//              u      [64][V]       fp32, accumulator order (AccTile)
 //              eG     [K]           fp32, 2^(chunk's total log2 decay)
+//            w, qg, kgT and Aqk are in matrix-core fragment order (FragTile).
 //            NS = 2 on the bf16 path (tile 1 holds x - bf16(x) rounded to bf16, so
 //            hi + lo carries about 16 significant bits), NS = 1 on the fp32 path.
 //            records are ordered hv-major: record(hv, c) = hv * NCmax + c.

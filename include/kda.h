@@ -113,6 +113,34 @@ int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float
                         int32_t* dev_status, hipStream_t stream, hipEvent_t* events);
 
 /*
+ * kda_chunk_fwd with the gate activation fused into Stage 1. Instead of the per-token
+ * log2 decay, the caller passes the raw gate input w_g(x) and the activation's
+ * parameters; the Stage 1 loads form, per element,
+ *     log2 decay = -exp(A_log[hv]) * softplus(g_raw[b,t,hv,d] + dt_bias[hv*K + d]) / ln 2
+ * (softplus(x) = log(1 + e^x)) and the chunk cumsum proceeds as in kda_chunk_fwd. The
+ * activation and its place in the cumsum: "kernel-fun 0.2.0.dev1 sdist", the chain
+ * module's gate_cumsum helper (A_log [HV], dt_bias [HV*K]), and ALGORITHM.md, Forward,
+ * on the activation fused into stage 1; the cumsum's 1/ln 2 gives the base-2 gate.
+ *
+ *   g_raw            device [B, T, HV, K], dtype g_dtype (KDA_BF16 or KDA_F32).
+ *   A_log            device fp32 [HV]; required.
+ *   dt_bias          device fp32 [HV * K], or NULL for zeros.
+ *   has_lower_bound  nonzero: the natural-log activation is first clamped from below at
+ *                    lower_bound, which must then be negative and finite (the pages name
+ *                    the option without a formula; a clamp is the reading taken).
+ * Everything else -- arguments, workspace, results, errors -- as kda_chunk_fwd; the
+ * workspace size is the same.
+ */
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* g_raw,
+                        int g_dtype, const float* A_log, const float* dt_bias,
+                        int has_lower_bound, float lower_bound, const void* beta,
+                        const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                        float* final_state, int B, int T, int H, int HV, int K, int V,
+                        int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                        void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                        hipStream_t stream);
+
+/*
  * Workspace bytes kda_chunk_fwd needs for these sizes (packed != 0 for packed mode,
  * N sequences). Returns 0 for invalid sizes.
  */

@@ -32,6 +32,7 @@ def test_header_declares_the_entry_points():
     for n in ("kda_chunk_fwd", "kda_recurrent_fwd", "kda_chunk_fwd_workspace_bytes",
               "kda_last_error", "kda_abi_version"):
         assert n in names
+    assert "kda_chunk_fwd_gated" in names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -105,6 +106,18 @@ def _rec(lib, **kw):
                                  a["V"], a["qd"], a["bd"], a["scale"], a["st"], a["stream"])
 
 
+def _gated(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gd=1, A=FAKE, dt=None, hlb=0, lb=0.0, beta=FAKE,
+             h0=None, cu=None, N=1, o=FAKE, ht=None, B=1, T=64, H=2, HV=2, K=128, V=128, qd=1,
+             bd=1, scale=0.0, cs=64, ws=FAKE, wsb=1 << 40, st=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_gated(a["q"], a["k"], a["v"], a["g"], a["gd"], a["A"], a["dt"],
+                                   a["hlb"], a["lb"], a["beta"], a["h0"], a["cu"], a["N"], a["o"],
+                                   a["ht"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"],
+                                   a["qd"], a["bd"], a["scale"], a["cs"], a["ws"], a["wsb"],
+                                   a["st"], a["stream"])
+
+
 CASES = [
     ("null q", dict(q=None), -1),
     ("HV % H", dict(H=3, HV=4), -2),
@@ -129,6 +142,25 @@ def test_recurrent_rejects(lib, name, kw, code):
     assert lib.kda_last_error().decode() != ""
 
 
+@pytest.mark.parametrize("name,kw,code", CASES, ids=[c[0] for c in CASES])
+def test_gated_rejects_common(lib, name, kw, code):
+    assert _gated(lib, **kw) == code
+    assert lib.kda_last_error().decode() != ""
+
+
+def test_gated_specific_rejects(lib):
+    assert _gated(lib, gd=7) == -3                    # raw gate dtype
+    assert b"g_dtype" in lib.kda_last_error()
+    assert _gated(lib, A=None) == -1                  # A_log required
+    assert _gated(lib, g=None) == -1                  # the raw gate itself
+    assert _gated(lib, dt=FAKE + 4) == -2             # misaligned dt_bias
+    assert _gated(lib, hlb=1, lb=0.5) == -2           # a lower bound must be negative
+    assert _gated(lib, hlb=1, lb=float("nan")) == -2
+    assert _gated(lib, hlb=1, lb=float("-inf")) == -2
+    assert _gated(lib, cs=32) == -4                   # then the chunk checks as usual
+    assert _gated(lib, ws=None) == -5
+
+
 def test_chunk_specific_rejects(lib):
     assert _chunk(lib, cs=32) == -4
     assert b"chunk_size" in lib.kda_last_error()
@@ -148,6 +180,7 @@ def test_empty_problem_is_a_noop(lib):
     # N = 0 sequences: nothing to do, nothing enqueued
     assert _chunk(lib, cu=FAKE, N=0, T=0) == 0
     assert _rec(lib, cu=FAKE, N=0, T=0) == 0
+    assert _gated(lib, cu=FAKE, N=0, T=0) == 0
     assert lib.kda_last_error().decode() == ""
 
 

@@ -403,3 +403,76 @@ def test_chunk_stage2_records_bf16(steep):
     log("  worst relative error per record: " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
     for name, b in bounds.items():
         assert worst[name] <= b, (name, worst[name], b)
+
+
+# ------------------------------------------------------------------------------------
+# gate activation fused into Stage 1 (kda_chunk_fwd_gated)
+# ------------------------------------------------------------------------------------
+def _gate_params(B, T, HV, K, gdt, seed):
+    """Raw gate input N(0, 2^2) in gdt, A_log = log(U[1, 2]) per head, dt_bias N(0, 0.5^2)."""
+    gen = torch.Generator().manual_seed(seed)
+    g_raw = torch.randn(B, T, HV, K, generator=gen).mul(2.0).to(gdt)
+    A_log = torch.rand(HV, generator=gen).add(1.0).log()
+    dt_bias = torch.randn(HV * K, generator=gen).mul(0.5)
+    return g_raw.to(DEV), A_log.to(DEV), dt_bias.to(DEV)
+
+
+def _gated_oracle(d, g_raw, A_log, dt_bias, bound):
+    g2 = oracle.gate_activation(g_raw, A_log, dt_bias, bound)
+    return oracle.recurrent(d["q"], d["k"], d["v"], g2, d["beta"], d["initial_state"], d["cu_seqlens"])
+
+
+@pytest.mark.parametrize("bound", [None, -3.0])
+@pytest.mark.parametrize("gdt", [torch.bfloat16, torch.float32])
+def test_gated_chunk_bf16(gdt, bound):
+    """bf16 q/k/v, raw gates in gdt: the fused activation against the oracle's fp64
+    activation followed by the recurrence (a short last chunk included)."""
+    import gated_delta_rule_64_amd as kda
+    d = small(1, 300, 2, 4, 128, 128, torch.bfloat16, seed=31)
+    g_raw, A_log, dt_bias = _gate_params(1, 300, 4, 128, gdt, seed=77)
+    log(f"[gated chunk] B1 T300 H2 HV4 K=V=128 bf16, raw gate {gdt}, lower_bound={bound}")
+    o, ht = kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], g_raw, d["beta"], A_log, dt_bias, bound,
+                                    d["initial_state"], None, output_final_state=True)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = _gated_oracle(d, g_raw, A_log, dt_bias, bound)
+    check("o", o, o_ref, torch.bfloat16)
+    check("state", ht, ht_ref, torch.bfloat16)
+
+
+def test_gated_chunk_fp32_and_no_dt_bias():
+    """fp32 everything (the fp32 Stage 1+2 kernel), dt_bias omitted: 1e-4 max-abs."""
+    import gated_delta_rule_64_amd as kda
+    d = small(1, 200, 2, 2, 64, 64, torch.float32, seed=32)
+    g_raw, A_log, _ = _gate_params(1, 200, 2, 64, torch.float32, seed=78)
+    o, ht = kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], g_raw, d["beta"], A_log, None, None,
+                                    d["initial_state"], None, output_final_state=True)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = _gated_oracle(d, g_raw, A_log, None, None)
+    check("o", o, o_ref, torch.float32)
+    check("state", ht, ht_ref, torch.float32)
+
+
+def test_gated_chunk_packed():
+    """Packed sequences (one empty slot, a tail) with fused gates: o on valid rows, the
+    tail untouched, every final state."""
+    import gated_delta_rule_64_amd as kda
+    lens = [130, 0, 64, 37, 200]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    Tp = cu[-1] + 40
+    d = small(1, Tp, 2, 4, 128, 128, torch.bfloat16, seed=33)
+    d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    d["initial_state"] = torch.randn(len(lens), 4, 128, 128, generator=torch.Generator().manual_seed(5)).mul(0.05).to(DEV)
+    g_raw, A_log, dt_bias = _gate_params(1, Tp, 4, 128, torch.bfloat16, seed=79)
+    out = torch.full_like(d["v"], float("nan"))
+    o, ht = kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], g_raw, d["beta"], A_log, dt_bias, -6.0,
+                                    d["initial_state"], d["cu_seqlens"], output_final_state=True,
+                                    out=out)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = _gated_oracle(d, g_raw, A_log, dt_bias, -6.0)
+    rows = valid_rows(cu, Tp)
+    check("o", o[0][torch.from_numpy(rows).to(DEV)], o_ref[0][rows], torch.bfloat16)
+    assert torch.isnan(o[0, cu[-1]:].float()).all(), "tail must stay untouched"
+    check("state", ht, ht_ref, torch.bfloat16)
+    assert torch.equal(ht[1], d["initial_state"][1]), "empty slot passes its state bitwise"
