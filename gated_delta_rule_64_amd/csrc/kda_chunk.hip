@@ -834,32 +834,75 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
                 bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
         }
 
-    // diagonal block, exact one-sided decays (blocks that decay too fast for an anchor)
+    // diagonal block, exact at any gate (blocks that decay too fast for one anchor): a
+    // pair j < i is split at the highest bit b where i and j differ; the row
+    // a = (i >> b << b) - 1 lies between them, so 2^(G_i - G_j) = 2^(G_i - G_a) 2^(G_a - G_j)
+    // with both factors <= 1. Level b is one transposed tile whose row side (rows with bit
+    // b set) is x_i 2^(G_i - G_a) and whose column side (bit b clear) is k_j 2^(G_a' - G_j),
+    // a' the last row of j's half; each lane's row sits on one side per level, so one
+    // exp2 per element and level. The diagonal i == j is the plain q_i . k_i.
     f32x4 aqk_d = {0.f, 0.f, 0.f, 0.f}, lt_d = {0.f, 0.f, 0.f, 0.f};
     if (exact_diag) {
-#pragma unroll 1
-        for (int jj = 0; jj < 16; ++jj) {
-            const int src = (lane & 48) | jj;
-            float sq = 0.f, sk = 0.f;
+        f32x4 tq[4], tk[4], td = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < NKS; ++s)
+        for (int b = 0; b < 4; ++b) { tq[b] = f32x4{0.f, 0.f, 0.f, 0.f}; tk[b] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            bf16x8 hq, lqv, hk, lk;
+            {
+                float xq[8], xk[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { xq[e] = to_f32(qv[s][e]); xk[e] = to_f32(kv[s][e]); }
+                split8(xq, hq, lqv);   // bf16 inputs: exact, lo = 0
+                split8(xk, hk, lk);
+                td = mma3(hk, lk, hq, lqv, td);
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const bool rowside = (lr >> b) & 1;
+                float xq[8], xk[8], xc[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
+                    const float x = loc[s][e];
+                    float la;                      // G - P_w at this row's anchor for level b
+                    if (b == 3) {
+                        la = row_bcast<7>(x);
+                    } else if (b == 2) {
+                        const float a3 = row_bcast<3>(x), a11 = row_bcast<11>(x);
+                        la = (lr & 8) ? a11 : a3;
+                    } else if (b == 1) {
+                        const float a1 = row_bcast<1>(x), a5 = row_bcast<5>(x);
+                        const float a9 = row_bcast<9>(x), a13 = row_bcast<13>(x);
+                        la = (lr & 8) ? ((lr & 4) ? a13 : a9) : ((lr & 4) ? a5 : a1);
+                    } else {
+                        // (the DPP read runs in every lane: a lane disabled by a branch
+                        // would return the fill value to its neighbour)
+                        const float prev = row_shr<1>(x);
+                        la = rowside ? prev : x;
+                    }
+                    const float f = exp2_fast(rowside ? x - la : la - x);
                     const float kf = to_f32(kv[s][e]);
-                    const float kj = __shfl(kf, src);
-                    const float lj = __shfl(loc[s][e], src);
-                    const float f = kj * exp2_fast(fminf(loc[s][e] - lj, 0.f));
-                    sq = fmaf(to_f32(qv[s][e]), f, sq);
-                    sk = fmaf(kf, f, sk);
+                    xq[e] = rowside ? to_f32(qv[s][e]) * f : 0.f;
+                    xk[e] = rowside ? kf * f : 0.f;
+                    xc[e] = rowside ? 0.f : kf * f;
                 }
-            sq += __shfl_xor(sq, 16);
-            sq += __shfl_xor(sq, 32);
-            sk += __shfl_xor(sk, 16);
-            sk += __shfl_xor(sk, 32);
-            // this lane keeps (row i = lr, column j = 4 lq + r) of the transposed tile
+                bf16x8 qh1, ql1, kh1, kl1, ch1, cl1;
+                split8(xq, qh1, ql1);
+                split8(xk, kh1, kl1);
+                split8(xc, ch1, cl1);
+                tq[b] = mma3(ch1, cl1, qh1, ql1, tq[b]);
+                tk[b] = mma3(ch1, cl1, kh1, kl1, tk[b]);
+            }
+        }
+        // lane (lq, lr) keeps the pairs (i = lr, j = 4 lq + r) of its level
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (jj == 4 * lq + r) { aqk_d[r] = sq; lt_d[r] = sk; }
+        for (int r = 0; r < 4; ++r) {
+            const int j = 4 * lq + r, x = lr ^ j;
+            const int lvl = x >= 8 ? 3 : (x >= 4 ? 2 : (x >= 2 ? 1 : 0));
+            const float vq = lvl == 3 ? tq[3][r] : (lvl == 2 ? tq[2][r] : (lvl == 1 ? tq[1][r] : tq[0][r]));
+            const float vk = lvl == 3 ? tk[3][r] : (lvl == 2 ? tk[2][r] : (lvl == 1 ? tk[1][r] : tk[0][r]));
+            aqk_d[r] = j < lr ? vq : (j == lr ? td[r] : 0.f);
+            lt_d[r] = j < lr ? vk : 0.f;
         }
     }
     // operands: row side x 2^(Gamma_i - P_w) and the column side k 2^(P_(w+1) - Gamma_j),
