@@ -476,3 +476,21 @@ def test_gated_chunk_packed():
     assert torch.isnan(o[0, cu[-1]:].float()).all(), "tail must stay untouched"
     check("state", ht, ht_ref, torch.bfloat16)
     assert torch.equal(ht[1], d["initial_state"][1]), "empty slot passes its state bitwise"
+
+
+@pytest.mark.parametrize("steep", [False, True])
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_chunk_head_dims(dtype, K, V, steep):
+    """Every (K, V) the chunk kernels are built for, both input precisions; ``steep`` puts
+    per-token gates of -15 on one chunk of one head (the exact diagonal-block path)."""
+    d = small(1, 200, 2, 4, K, V, dtype, seed=40 + K + V)
+    if steep:
+        g = d["g"].clone()
+        g[:, 64:128, 2] = -15.0
+        d["g"] = g
+    log(f"[head dims] K={K} V={V} {dtype} steep={steep}")
+    o, s = run("chunk", d)
+    o_ref, s_ref = oracle_of(d)
+    check("o", o, o_ref, dtype)
+    check("state", s, s_ref, dtype)
