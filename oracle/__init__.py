@@ -12,6 +12,8 @@ Contents
                       checks and pinned against ``recurrent``.
   * ``gate_activation`` -- the fused gate activation (raw gate input -> per-token log2
                       decay), numpy fp64 (``gate.py``).
+  * ``l2norm``, ``beta_sigmoid`` -- the q/k normalisation and beta activation the op can
+                      fuse (``preprocess.py``).
 
 All inputs are converted to float64 exactly (bf16 and fp32 values are exactly
 representable), so the oracle sees the very values the GPU sees.
@@ -140,3 +142,4 @@ def recurrent(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None,
 
 from . import chunked  # noqa: E402  (numpy only; no dependency on the library above)
 from .gate import gate_activation  # noqa: E402,F401  (numpy only)
+from .preprocess import beta_sigmoid, l2norm  # noqa: E402,F401  (numpy only)
