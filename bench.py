@@ -15,6 +15,8 @@ Also reported on the same JSON line:
                  outputs (336.1 MB), and the matrix-core fractions;
   * gated     -- the same forward with the gate activation fused into Stage 1 (raw bf16
                  gate input instead of the fp32 log2 decay);
+  * fused_inputs -- the same with every input fusion on (fused gate, q/k L2 norm, beta
+                 sigmoid x2); the decode line carries the same for the recurrent path;
   * decode    -- the per-token recurrent forward on 4096 sequences x 32 heads (one token
                  each, fp32 states in and out): state GB/s and fraction of HBM peak;
   * cpu_baseline -- the fp64 CPU oracle on the full headline workload, host threads.
@@ -220,6 +222,25 @@ def main():
     torch.cuda.synchronize()
     gated_ms = gev.ms(0, 1) / steps
     gev.close()
+
+    # every input fusion at once: the fused gate as above, q / k L2-normalised in the
+    # loads and beta = 2 sigmoid(beta) (the recipe's q, k and beta serve as the raw inputs)
+    def fcall():
+        kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], g_raw, d["beta"], use_gate_in_kernel=True,
+                             A_log=A_log, dt_bias=dt_bias, use_qk_l2norm_in_kernel=True,
+                             use_beta_sigmoid_in_kernel=True, allow_neg_eigval=True, out=out,
+                             workspace=ws)
+    for _ in range(args.warmup):
+        fcall()
+    torch.cuda.synchronize()
+    fev = Events(hip, 2)
+    hip.hipEventRecord(fev.ev[0], sptr)
+    for _ in range(steps):
+        fcall()
+    hip.hipEventRecord(fev.ev[1], sptr)
+    torch.cuda.synchronize()
+    fused_ms = fev.ms(0, 1) / steps
+    fev.close()
     del g_raw, A_log, dt_bias
 
     # decode: 4096 sequences x 32 heads, one token each, fp32 states in and out
@@ -241,6 +262,23 @@ def main():
     hip.hipEventRecord(dev_ev.ev[1], sptr)
     torch.cuda.synchronize()
     dec_ms = dev_ev.ms(0, 1) / args.decode_steps
+    dev_ev.close()
+    # the same decode with q / k normalisation and beta = sigmoid(beta) fused into the loads
+    def dfcall():
+        kda.kda_recurrent_fwd_ex(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["initial_state"],
+                                 dd["cu_seqlens"], output_final_state=True, out=dout,
+                                 final_state=dstate, use_qk_l2norm_in_kernel=True,
+                                 use_beta_sigmoid_in_kernel=True)
+    for _ in range(2):
+        dfcall()
+    torch.cuda.synchronize()
+    dev_ev = Events(hip, 2)
+    hip.hipEventRecord(dev_ev.ev[0], sptr)
+    for _ in range(args.decode_steps):
+        dfcall()
+    hip.hipEventRecord(dev_ev.ev[1], sptr)
+    torch.cuda.synchronize()
+    dec_fused_ms = dev_ev.ms(0, 1) / args.decode_steps
     dev_ev.close()
     dec_bytes = (2 * dd["initial_state"].numel() * 4 + 3 * dd["q"].numel() * 2 + dd["g"].numel() * 4
                  + dd["beta"].numel() * 2 + dout.numel() * 2)
@@ -272,9 +310,11 @@ def main():
                  "mfma_frac_dense_tile_flops": flops_dense / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "gated": {"workload": "the headline forward with the gate activation fused into Stage 1 (raw bf16 gate input, A_log, dt_bias)",
                   "ms_per_step": gated_ms, "tokens_per_s": tokens / (gated_ms * 1e-3)},
+        "fused_inputs": {"workload": "the headline forward with every input fusion: raw bf16 gate + A_log + dt_bias, q/k L2 norm in the loads, beta = 2 sigmoid(beta)",
+                         "ms_per_step": fused_ms, "tokens_per_s": tokens / (fused_ms * 1e-3)},
         "decode": {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
                    "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
-                   "bytes": dec_bytes},
+                   "bytes": dec_bytes, "fused_inputs_ms": dec_fused_ms},
     }
 
     if not args.no_cpu_baseline:

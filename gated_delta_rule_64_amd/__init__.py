@@ -10,7 +10,10 @@ Entry points (same names as the C ABI):
   kda_chunk_fwd(q, k, v, g, beta, ...)      chunked prefill forward
   kda_chunk_fwd_gated(q, k, v, g_raw, beta, A_log, ...)
                                              the same with the gate activation fused in
+  kda_chunk_fwd_ex(q, k, v, g, beta, ...)   every option: fused gate activation, q/k L2
+                                             norm and beta sigmoid in the loads, timing events
   kda_recurrent_fwd(q, k, v, g, beta, ...)  per-token recurrent forward (decode)
+  kda_recurrent_fwd_ex(q, k, v, g, beta, ...)  the same with the options of kda_chunk_fwd_ex
   kda_chunk_fwd_workspace_bytes(...)         workspace size query
   kda_last_error()                           reason for the last failure
 """
@@ -20,18 +23,29 @@ from ._lib import (  # noqa: F401
     KDA_BF16,
     KDA_DEV_BAD_CU_SEQLENS,
     KDA_F32,
+    KDA_GATE_LOG2,
+    KDA_GATE_RAW_BF16,
+    KDA_GATE_RAW_F32,
+    KDA_PRE_BETA_SIGMOID,
+    KDA_PRE_L2NORM_K,
+    KDA_PRE_L2NORM_Q,
+    KDA_PRE_NEG_EIGVAL,
     KdaError,
     kda_chunk_fwd,
+    kda_chunk_fwd_ex,
     kda_chunk_fwd_gated,
     kda_chunk_fwd_workspace_bytes,
     kda_last_error,
     kda_recurrent_fwd,
+    kda_recurrent_fwd_ex,
     library_path,
     load_library,
 )
 
 __all__ = [
-    "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_recurrent_fwd", "kda_chunk_fwd_workspace_bytes",
+    "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_recurrent_fwd",
+    "kda_recurrent_fwd_ex", "kda_chunk_fwd_workspace_bytes",
     "kda_last_error", "KdaError", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
-    "library_path",
+    "library_path", "KDA_GATE_LOG2", "KDA_GATE_RAW_F32", "KDA_GATE_RAW_BF16", "KDA_PRE_L2NORM_Q",
+    "KDA_PRE_L2NORM_K", "KDA_PRE_BETA_SIGMOID", "KDA_PRE_NEG_EIGVAL",
 ]

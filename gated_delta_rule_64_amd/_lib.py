@@ -13,6 +13,13 @@ _LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_F32 = 0
 KDA_BF16 = 1
 KDA_DEV_BAD_CU_SEQLENS = 1
+KDA_GATE_LOG2 = 0
+KDA_GATE_RAW_F32 = 1
+KDA_GATE_RAW_BF16 = 2
+KDA_PRE_L2NORM_Q = 1
+KDA_PRE_L2NORM_K = 2
+KDA_PRE_BETA_SIGMOID = 4
+KDA_PRE_NEG_EIGVAL = 8
 
 _lock = threading.Lock()
 _lib = None
@@ -50,6 +57,14 @@ def load_library():
         lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp,
                                             vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                             i32, ctypes.c_float, i32, vp, sz, vp, vp]
+        lib.kda_chunk_fwd_ex.restype = i32
+        lib.kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp, vp,
+                                         i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                         f32, i32, vp, sz, vp, vp, vp]
+        lib.kda_recurrent_fwd_ex.restype = i32
+        lib.kda_recurrent_fwd_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp,
+                                             vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             i32, f32, vp, vp]
         lib.kda_recurrent_fwd.restype = i32
         lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                           i32, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp]
@@ -229,6 +244,107 @@ def kda_recurrent_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
     rc = lib.kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                                _ptr(cu_seqlens), N, _ptr(out), _ptr(final_state), B, T, H, HV, K, V,
                                qkv, bdt, float(scale or 0.0), _ptr(dev_status), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    return out, final_state
+
+
+def _options(g, HV, K, use_gate_in_kernel, A_log, dt_bias, lower_bound, use_qk_l2norm_in_kernel,
+             l2norm_q, l2norm_k, use_beta_sigmoid_in_kernel, allow_neg_eigval):
+    """The gate code and preprocessing flags of the _ex entry points, with checks."""
+    if use_gate_in_kernel:
+        gate = KDA_GATE_RAW_BF16 if g.dtype == torch.bfloat16 else KDA_GATE_RAW_F32
+        if A_log is None:
+            raise ValueError("A_log is required with use_gate_in_kernel")
+        if A_log.dtype != torch.float32 or A_log.numel() != HV:
+            raise ValueError(f"A_log must be float32 with {HV} elements")
+        if dt_bias is not None and (dt_bias.dtype != torch.float32 or dt_bias.numel() != HV * K):
+            raise ValueError(f"dt_bias must be float32 with {HV * K} elements")
+        _check_device([("g", g), ("A_log", A_log), ("dt_bias", dt_bias)])
+    else:
+        if A_log is not None or dt_bias is not None or lower_bound is not None:
+            raise ValueError("A_log, dt_bias and lower_bound need use_gate_in_kernel")
+        gate = KDA_GATE_LOG2
+    lq = use_qk_l2norm_in_kernel if l2norm_q is None else l2norm_q
+    lk = use_qk_l2norm_in_kernel if l2norm_k is None else l2norm_k
+    if allow_neg_eigval and not use_beta_sigmoid_in_kernel:
+        raise ValueError("allow_neg_eigval needs use_beta_sigmoid_in_kernel")
+    pre = ((KDA_PRE_L2NORM_Q if lq else 0) | (KDA_PRE_L2NORM_K if lk else 0)
+           | (KDA_PRE_BETA_SIGMOID if use_beta_sigmoid_in_kernel else 0)
+           | (KDA_PRE_NEG_EIGVAL if allow_neg_eigval else 0))
+    return gate, pre
+
+
+def kda_chunk_fwd_ex(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                     output_final_state=False, scale=None, *, use_gate_in_kernel=False,
+                     A_log=None, dt_bias=None, lower_bound=None, use_qk_l2norm_in_kernel=False,
+                     l2norm_q=None, l2norm_k=None, use_beta_sigmoid_in_kernel=False,
+                     allow_neg_eigval=False, out=None, final_state=None, workspace=None,
+                     dev_status=None, events=None):
+    """Chunked KDA forward with every option. Returns ``(o, final_state or None)``.
+
+    ``g`` is the float32 per-token log2 decay, or with ``use_gate_in_kernel`` the raw gate
+    input (bfloat16 or float32) with ``A_log`` / ``dt_bias`` / ``lower_bound`` as in
+    ``kda_chunk_fwd_gated``. ``use_qk_l2norm_in_kernel`` normalises q and k rows in the
+    loads (``l2norm_q`` / ``l2norm_k`` set each one separately); ``beta`` goes through a
+    sigmoid with ``use_beta_sigmoid_in_kernel``, doubled with ``allow_neg_eigval``.
+    ``events``: optional sequence of four HIP event handles (ints), as in the timed entry.
+    """
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens,
+                                                  raw_gate=use_gate_in_kernel)
+    gate, pre = _options(g, HV, K, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                         use_qk_l2norm_in_kernel, l2norm_q, l2norm_k, use_beta_sigmoid_in_kernel,
+                         allow_neg_eigval)
+    if out is None:
+        out = torch.empty_like(v)
+    if output_final_state and final_state is None:
+        final_state = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev)
+    if not output_final_state:
+        final_state = None
+    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, N, int(cu_seqlens is not None), qkv)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * 4)(*[int(e) for e in events])
+    rc = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), gate, _ptr(A_log), _ptr(dt_bias),
+                              int(lower_bound is not None),
+                              float(lower_bound if lower_bound is not None else 0.0), _ptr(beta),
+                              pre, _ptr(initial_state), _ptr(cu_seqlens), N, _ptr(out),
+                              _ptr(final_state), B, T, H, HV, K, V, qkv, bdt, float(scale or 0.0),
+                              64, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _ptr(dev_status), _stream(dev), ev)
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    return out, final_state
+
+
+def kda_recurrent_fwd_ex(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                         output_final_state=False, scale=None, *, use_gate_in_kernel=False,
+                         A_log=None, dt_bias=None, lower_bound=None,
+                         use_qk_l2norm_in_kernel=False, l2norm_q=None, l2norm_k=None,
+                         use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False, out=None,
+                         final_state=None, dev_status=None):
+    """Per-token recurrent KDA forward with the options of ``kda_chunk_fwd_ex``."""
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens,
+                                                  raw_gate=use_gate_in_kernel)
+    gate, pre = _options(g, HV, K, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                         use_qk_l2norm_in_kernel, l2norm_q, l2norm_k, use_beta_sigmoid_in_kernel,
+                         allow_neg_eigval)
+    if out is None:
+        out = torch.empty_like(v)
+    if output_final_state and final_state is None:
+        final_state = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev)
+    if not output_final_state:
+        final_state = None
+    rc = lib.kda_recurrent_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), gate, _ptr(A_log),
+                                  _ptr(dt_bias), int(lower_bound is not None),
+                                  float(lower_bound if lower_bound is not None else 0.0),
+                                  _ptr(beta), pre, _ptr(initial_state), _ptr(cu_seqlens), N,
+                                  _ptr(out), _ptr(final_state), B, T, H, HV, K, V, qkv, bdt,
+                                  float(scale or 0.0), _ptr(dev_status), _stream(dev))
     if rc != 0:
         raise KdaError(rc, lib.kda_last_error().decode())
     return out, final_state

@@ -56,64 +56,53 @@ int check_common(const void* q, const void* k, const void* v, const float* g, co
     return KDA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* kda_last_error(void) { return g_last_error; }
-
-int kda_abi_version(void) { return 1; }
-
-size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
-                                     int packed, int qkv_dtype) {
-    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || N < 0 || (K != 64 && K != 128) ||
-        (V != 64 && V != 128) || (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32))
-        return 0;
-    kda::ChunkLayout L;
-    if (!kda::chunk_layout(B, T, HV, K, V, packed ? N : B, packed != 0, qkv_dtype, &L)) return 0;
-    return L.total;
-}
-
-int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
-                  const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
-                  float* final_state, int B, int T, int H, int HV, int K, int V, int qkv_dtype,
-                  int beta_dtype, float scale, int chunk_size, void* workspace,
-                  size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
-    return kda_chunk_fwd_timed(q, k, v, g, beta, initial_state, cu_seqlens, N, o, final_state, B,
-                               T, H, HV, K, V, qkv_dtype, beta_dtype, scale, chunk_size,
-                               workspace, workspace_bytes, dev_status, stream, nullptr);
-}
-
-}  // extern "C"
-
-namespace {
-
-// The chunked forward behind every chunk entry point; `gate` describes where the Stage 1
-// loads take the per-token log2 decay from (`g` for GATE_LOG2).
-struct GateSpec {
-    int mode;
-    const void* g_raw;
-    const float* A_log;
-    const float* dt_bias;
-    int has_lower_bound;
-    float lower_bound;
-};
-
-int chunk_impl(const void* q, const void* k, const void* v, const float* g, const GateSpec& gate,
-               const void* beta, const float* initial_state, const int32_t* cu_seqlens, int N,
-               void* o, float* final_state, int B, int T, int H, int HV, int K, int V,
-               int qkv_dtype, int beta_dtype, float scale, int chunk_size, void* workspace,
-               size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
-               hipEvent_t* events) {
-    const float* g_checked = gate.mode == kda::GATE_LOG2 ? g : reinterpret_cast<const float*>(gate.g_raw);
-    int rc = check_common(q, k, v, g_checked, beta, initial_state, cu_seqlens, N, o, final_state, B,
-                          T, H, HV, K, V, qkv_dtype, beta_dtype);
-    if (rc != KDA_OK) return rc;
-    if (gate.mode != kda::GATE_LOG2 && (long long)B * T > 0) {
-        if (!gate.A_log) return fail(KDA_ERR_NULL, "A_log must be non-NULL");
-        if (!aligned16(gate.dt_bias))
-            return fail(KDA_ERR_SHAPE, "dt_bias must be 16-byte aligned");
+// Builds the kernels' InputSpec from the gate and preprocessing arguments and checks them
+// (g itself, log2 decay or raw input, goes through the common pointer checks).
+int make_input_spec(const void* g, int gate, const float* A_log, const float* dt_bias,
+                    int has_lower_bound, float lower_bound, int preprocess, bool nonempty,
+                    kda::InputSpec* in) {
+    if (gate != KDA_GATE_LOG2 && gate != KDA_GATE_RAW_F32 && gate != KDA_GATE_RAW_BF16)
+        return fail(KDA_ERR_ARG, "gate must be KDA_GATE_LOG2 (0), KDA_GATE_RAW_F32 (1) or KDA_GATE_RAW_BF16 (2), got %d", gate);
+    if (preprocess & ~(KDA_PRE_L2NORM_Q | KDA_PRE_L2NORM_K | KDA_PRE_BETA_SIGMOID | KDA_PRE_NEG_EIGVAL))
+        return fail(KDA_ERR_ARG, "preprocess has unknown bits: 0x%x", preprocess);
+    if ((preprocess & KDA_PRE_NEG_EIGVAL) && !(preprocess & KDA_PRE_BETA_SIGMOID))
+        return fail(KDA_ERR_ARG, "KDA_PRE_NEG_EIGVAL needs KDA_PRE_BETA_SIGMOID");
+    if (gate == KDA_GATE_LOG2) {
+        if (A_log || dt_bias || has_lower_bound)
+            return fail(KDA_ERR_ARG, "A_log, dt_bias and a lower bound belong to a raw gate input (gate=%d is the log2 decay)", gate);
+    } else {
+        if (has_lower_bound && !(lower_bound < 0.0f && isfinite(lower_bound)))
+            return fail(KDA_ERR_SHAPE, "lower_bound must be negative and finite, got %g", (double)lower_bound);
+        if (nonempty && !A_log) return fail(KDA_ERR_NULL, "A_log must be non-NULL");
+        if (!aligned16(dt_bias)) return fail(KDA_ERR_SHAPE, "dt_bias must be 16-byte aligned");
     }
+    in->gate_mode = gate;
+    in->g_raw = gate == KDA_GATE_LOG2 ? nullptr : g;
+    in->A_log = gate == KDA_GATE_LOG2 ? nullptr : A_log;
+    in->dt_bias = gate == KDA_GATE_LOG2 ? nullptr : dt_bias;
+    in->has_lower_bound = gate != KDA_GATE_LOG2 && has_lower_bound ? 1 : 0;
+    in->lower_bound = lower_bound;
+    in->l2norm_q = (preprocess & KDA_PRE_L2NORM_Q) ? 1 : 0;
+    in->l2norm_k = (preprocess & KDA_PRE_L2NORM_K) ? 1 : 0;
+    in->beta_sig = (preprocess & KDA_PRE_BETA_SIGMOID) ? ((preprocess & KDA_PRE_NEG_EIGVAL) ? 2.0f : 1.0f) : 0.0f;
+    return KDA_OK;
+}
+
+// The chunked forward behind every chunk entry point.
+int chunk_impl(const void* q, const void* k, const void* v, const void* g, int gate,
+               const float* A_log, const float* dt_bias, int has_lower_bound, float lower_bound,
+               const void* beta, int preprocess, const float* initial_state,
+               const int32_t* cu_seqlens, int N, void* o, float* final_state, int B, int T, int H,
+               int HV, int K, int V, int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+               void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
+               hipEvent_t* events) {
+    int rc = check_common(q, k, v, static_cast<const float*>(g), beta, initial_state, cu_seqlens, N,
+                          o, final_state, B, T, H, HV, K, V, qkv_dtype, beta_dtype);
+    if (rc != KDA_OK) return rc;
+    kda::InputSpec in;
+    rc = make_input_spec(g, gate, A_log, dt_bias, has_lower_bound, lower_bound, preprocess,
+                         (long long)B * T > 0, &in);
+    if (rc != KDA_OK) return rc;
     if (chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64, got %d", chunk_size);
     if (K != 64 && K != 128)
@@ -134,9 +123,9 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* g, cons
             return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     }
     kda::ChunkArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-    a.g_raw = gate.g_raw; a.gate_mode = gate.mode; a.A_log = gate.A_log; a.dt_bias = gate.dt_bias;
-    a.has_lower_bound = gate.has_lower_bound; a.lower_bound = gate.lower_bound;
+    a.q = q; a.k = k; a.v = v; a.beta = beta;
+    a.g = gate == KDA_GATE_LOG2 ? static_cast<const float*>(g) : nullptr;
+    a.in = in;
     a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
     a.o = o; a.final_state = final_state;
     a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
@@ -150,9 +139,87 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* g, cons
     return KDA_OK;
 }
 
+// The per-token forward behind both recurrent entry points.
+int recurrent_impl(const void* q, const void* k, const void* v, const void* g, int gate,
+                   const float* A_log, const float* dt_bias, int has_lower_bound,
+                   float lower_bound, const void* beta, int preprocess,
+                   const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                   float* final_state, int B, int T, int H, int HV, int K, int V, int qkv_dtype,
+                   int beta_dtype, float scale, int32_t* dev_status, hipStream_t stream) {
+    int rc = check_common(q, k, v, static_cast<const float*>(g), beta, initial_state, cu_seqlens, N,
+                          o, final_state, B, T, H, HV, K, V, qkv_dtype, beta_dtype);
+    if (rc != KDA_OK) return rc;
+    kda::InputSpec in;
+    rc = make_input_spec(g, gate, A_log, dt_bias, has_lower_bound, lower_bound, preprocess,
+                         (long long)B * T > 0, &in);
+    if (rc != KDA_OK) return rc;
+    if (K != 64 && K != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "K must be 64 or 128, got %d", K);
+    if (V % 64 != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "V must be a multiple of 64, got %d", V);
+    if ((long long)N * HV * (V / 64) > 0x7fffffffLL * 4LL)
+        return fail(KDA_ERR_SHAPE, "grid too large");
+    if (N == 0) return KDA_OK;
+    kda::RecurrentArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta;
+    a.g = gate == KDA_GATE_LOG2 ? static_cast<const float*>(g) : nullptr;
+    a.in = in;
+    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
+    a.o = o; a.final_state = final_state;
+    a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype;
+    a.scale = scale == 0.0f ? 1.0f / sqrtf((float)K) : scale;
+    a.dev_status = dev_status; a.stream = stream;
+    hipError_t err = kda::launch_recurrent(a);
+    if (err != hipSuccess)
+        return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+const char* kda_last_error(void) { return g_last_error; }
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
+                                     int packed, int qkv_dtype) {
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || N < 0 || (K != 64 && K != 128) ||
+        (V != 64 && V != 128) || (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32))
+        return 0;
+    kda::ChunkLayout L;
+    if (!kda::chunk_layout(B, T, HV, K, V, packed ? N : B, packed != 0, qkv_dtype, &L)) return 0;
+    return L.total;
+}
+
+int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
+                     const float* A_log, const float* dt_bias, int has_lower_bound,
+                     float lower_bound, const void* beta, int preprocess,
+                     const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                     float* final_state, int B, int T, int H, int HV, int K, int V,
+                     int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                     void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                     hipStream_t stream, hipEvent_t* events) {
+    clear_error();
+    return chunk_impl(q, k, v, g, gate, A_log, dt_bias, has_lower_bound, lower_bound, beta,
+                      preprocess, initial_state, cu_seqlens, N, o, final_state, B, T, H, HV, K,
+                      V, qkv_dtype, beta_dtype, scale, chunk_size, workspace, workspace_bytes,
+                      dev_status, stream, events);
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                  float* final_state, int B, int T, int H, int HV, int K, int V, int qkv_dtype,
+                  int beta_dtype, float scale, int chunk_size, void* workspace,
+                  size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+    clear_error();
+    return chunk_impl(q, k, v, g, KDA_GATE_LOG2, nullptr, nullptr, 0, 0.0f, beta, 0,
+                      initial_state, cu_seqlens, N, o, final_state, B, T, H, HV, K, V, qkv_dtype,
+                      beta_dtype, scale, chunk_size, workspace, workspace_bytes, dev_status,
+                      stream, nullptr);
+}
 
 int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float* g,
                         const void* beta, const float* initial_state,
@@ -161,10 +228,10 @@ int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float
                         float scale, int chunk_size, void* workspace, size_t workspace_bytes,
                         int32_t* dev_status, hipStream_t stream, hipEvent_t* events) {
     clear_error();
-    const GateSpec gate{kda::GATE_LOG2, nullptr, nullptr, nullptr, 0, 0.0f};
-    return chunk_impl(q, k, v, g, gate, beta, initial_state, cu_seqlens, N, o, final_state, B, T,
-                      H, HV, K, V, qkv_dtype, beta_dtype, scale, chunk_size, workspace,
-                      workspace_bytes, dev_status, stream, events);
+    return chunk_impl(q, k, v, g, KDA_GATE_LOG2, nullptr, nullptr, 0, 0.0f, beta, 0,
+                      initial_state, cu_seqlens, N, o, final_state, B, T, H, HV, K, V, qkv_dtype,
+                      beta_dtype, scale, chunk_size, workspace, workspace_bytes, dev_status,
+                      stream, events);
 }
 
 int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* g_raw,
@@ -178,13 +245,10 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void*
     clear_error();
     if (g_dtype != KDA_BF16 && g_dtype != KDA_F32)
         return fail(KDA_ERR_DTYPE, "g_dtype must be KDA_BF16 (1) or KDA_F32 (0), got %d", g_dtype);
-    if (has_lower_bound && !(lower_bound < 0.0f && isfinite(lower_bound)))
-        return fail(KDA_ERR_SHAPE, "lower_bound must be negative and finite, got %g", (double)lower_bound);
-    const GateSpec gate{g_dtype == KDA_BF16 ? kda::GATE_RAW_BF16 : kda::GATE_RAW_F32, g_raw, A_log,
-                        dt_bias, has_lower_bound ? 1 : 0, lower_bound};
-    return chunk_impl(q, k, v, nullptr, gate, beta, initial_state, cu_seqlens, N, o, final_state,
-                      B, T, H, HV, K, V, qkv_dtype, beta_dtype, scale, chunk_size, workspace,
-                      workspace_bytes, dev_status, stream, nullptr);
+    return chunk_impl(q, k, v, g_raw, g_dtype == KDA_BF16 ? KDA_GATE_RAW_BF16 : KDA_GATE_RAW_F32,
+                      A_log, dt_bias, has_lower_bound, lower_bound, beta, 0, initial_state,
+                      cu_seqlens, N, o, final_state, B, T, H, HV, K, V, qkv_dtype, beta_dtype,
+                      scale, chunk_size, workspace, workspace_bytes, dev_status, stream, nullptr);
 }
 
 int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -193,28 +257,22 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* 
                       int V, int qkv_dtype, int beta_dtype, float scale, int32_t* dev_status,
                       hipStream_t stream) {
     clear_error();
-    int rc = check_common(q, k, v, g, beta, initial_state, cu_seqlens, N, o, final_state, B, T,
-                          H, HV, K, V, qkv_dtype, beta_dtype);
-    if (rc != KDA_OK) return rc;
-    if (K != 64 && K != 128)
-        return fail(KDA_ERR_UNSUPPORTED, "K must be 64 or 128, got %d", K);
-    if (V % 64 != 0)
-        return fail(KDA_ERR_UNSUPPORTED, "V must be a multiple of 64, got %d", V);
-    if ((long long)N * HV * (V / 64) > 0x7fffffffLL * 4LL)
-        return fail(KDA_ERR_SHAPE, "grid too large");
-    if (N == 0) return KDA_OK;
-    kda::RecurrentArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
-    a.o = o; a.final_state = final_state;
-    a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
-    a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype;
-    a.scale = scale == 0.0f ? 1.0f / sqrtf((float)K) : scale;
-    a.dev_status = dev_status; a.stream = stream;
-    hipError_t err = kda::launch_recurrent(a);
-    if (err != hipSuccess)
-        return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
-    return KDA_OK;
+    return recurrent_impl(q, k, v, g, KDA_GATE_LOG2, nullptr, nullptr, 0, 0.0f, beta, 0,
+                          initial_state, cu_seqlens, N, o, final_state, B, T, H, HV, K, V,
+                          qkv_dtype, beta_dtype, scale, dev_status, stream);
+}
+
+int kda_recurrent_fwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
+                         const float* A_log, const float* dt_bias, int has_lower_bound,
+                         float lower_bound, const void* beta, int preprocess,
+                         const float* initial_state, const int32_t* cu_seqlens, int N,
+                         void* o, float* final_state, int B, int T, int H, int HV, int K,
+                         int V, int qkv_dtype, int beta_dtype, float scale,
+                         int32_t* dev_status, hipStream_t stream) {
+    clear_error();
+    return recurrent_impl(q, k, v, g, gate, A_log, dt_bias, has_lower_bound, lower_bound, beta,
+                          preprocess, initial_state, cu_seqlens, N, o, final_state, B, T, H, HV,
+                          K, V, qkv_dtype, beta_dtype, scale, dev_status, stream);
 }
 
 }  // extern "C"

@@ -138,13 +138,9 @@ struct IntraParams {
     int T, H, HV, NT, NCmax;
     int dense;                // no offsets: chunk c is chunk c % NT of sequence c / NT
     float scale;
-    // per-token log2 decay: p.g as given (GATE_LOG2), or formed from the raw gate input
-    const void* g_raw;
-    int gate_mode;
-    const float* A_log;       // [HV]
-    const float* dt_bias;     // [HV * K] or null
-    int has_lower_bound;
-    float lower_bound;
+    // per-token log2 decay: p.g as given (GATE_LOG2), or formed from the raw gate input;
+    // q / k normalisation and the beta activation
+    InputSpec in;
 };
 
 // Channels d0 .. d0+7 of the per-token log2 decay at row r, value head hv: loaded as
@@ -155,7 +151,8 @@ struct IntraParams {
 template <int K>
 __device__ __forceinline__ void load_gate8(const IntraParams& p, size_t r, int hv, int d0, float* out) {
     const size_t base = (r * p.HV + hv) * K + d0;
-    if (p.gate_mode == GATE_LOG2) {
+    const InputSpec& in = p.in;
+    if (in.gate_mode == GATE_LOG2) {
         const f32x4 a = *reinterpret_cast<const f32x4*>(p.g + base);
         const f32x4 b = *reinterpret_cast<const f32x4*>(p.g + base + 4);
 #pragma unroll
@@ -163,38 +160,34 @@ __device__ __forceinline__ void load_gate8(const IntraParams& p, size_t r, int h
         return;
     }
     float x[8];
-    if (p.gate_mode == GATE_RAW_BF16) {
-        const bf16x8 h = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.g_raw) + base);
+    if (in.gate_mode == GATE_RAW_BF16) {
+        const bf16x8 h = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(in.g_raw) + base);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
     } else {
-        const float* gr = static_cast<const float*>(p.g_raw) + base;
+        const float* gr = static_cast<const float*>(in.g_raw) + base;
         const f32x4 a = *reinterpret_cast<const f32x4*>(gr);
         const f32x4 b = *reinterpret_cast<const f32x4*>(gr + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
     }
-    if (p.dt_bias) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)hv * K + d0);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)hv * K + d0 + 4);
+    if (in.dt_bias) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(in.dt_bias + (size_t)hv * K + d0);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(in.dt_bias + (size_t)hv * K + d0 + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) { x[e] += a[e]; x[4 + e] += b[e]; }
     }
-    // log2 decay = -e^A softplus(x) / ln 2 = -e^A log2(1 + 2^(x log2 e)); for x > 15 the
-    // softplus is x to fp32 precision. Where 1 + 2^(x log2 e) rounds to 1 (x below about
-    // -17) the result is 0 instead of a value under 6e-8 e^A: a decay factor off by less
-    // than 4e-8 e^A per token.
-    const float amp = -expf(p.A_log[hv]);
-    constexpr float LOG2E = 1.4426950408889634f;
-    const float lb2 = p.lower_bound * LOG2E;   // the bound in log2 units
+    const float amp = -expf(in.A_log[hv]);
+    const float lb2 = in.lower_bound * LOG2E;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float y = x[e] * LOG2E;
-        const float sp2 = x[e] > 15.f ? y : __builtin_amdgcn_logf(1.f + exp2_fast(y));   // softplus / ln 2
-        float g2 = amp * sp2;
-        if (p.has_lower_bound) g2 = fmaxf(g2, lb2);
-        out[e] = g2;
-    }
+    for (int e = 0; e < 8; ++e) out[e] = gate_log2_from_raw(x[e], amp, in.has_lower_bound, lb2);
+}
+
+// beta of row r, value head hv, with the optional sigmoid
+template <typename TB>
+__device__ __forceinline__ float load_beta(const IntraParams& p, size_t r, int hv) {
+    const float b = to_f32(reinterpret_cast<const TB*>(p.beta)[r * p.HV + hv]);
+    return p.in.beta_sig != 0.f ? beta_from_logit(b, p.in.beta_sig) : b;
 }
 
 // Thread mapping for the elementwise work: thread (cg, rg) owns columns 8cg .. 8cg+7 of
@@ -314,7 +307,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
 
     // ---- phase 0: clear L, stage beta ----
     for (int i = tid; i < C * LD; i += NTHREADS) Lm[i] = 0.f;
-    if (tid < C) betas[tid] = tid < len ? to_f32(beta[(size_t)(rs + tid) * p.HV + hv]) : 0.f;
+    if (tid < C) betas[tid] = tid < len ? load_beta<TB>(p, (size_t)(rs + tid), hv) : 0.f;
 
     // ---- phase 1 (Stage 1): loads and the chunk-local cumsum of the log2 gate ----
     const int cg = tid % CG, rg = tid / CG;
@@ -336,6 +329,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
             for (int e = 0; e < 8; ++e) { gm[ii][e] = 0.f; qv[ii][e] = from_f32<TIn>(0.f); kv[ii][e] = from_f32<TIn>(0.f); }
         }
     }
+    // optional L2 normalisation of the q / k rows: the CG lanes of a row group hold one
+    // row's K channels between them
+    auto l2norm_rows = [&](Row8* x) {
+#pragma unroll
+        for (int ii = 0; ii < RPT; ++ii) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { const float f = to_f32(x[ii][e]); ss = fmaf(f, f, ss); }
+#pragma unroll
+            for (int m = 1; m < CG; m <<= 1) ss += __shfl_xor(ss, m, 64);
+            const float rn = l2norm_rstd(ss);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[ii][e] = from_f32<TIn>(to_f32(x[ii][e]) * rn);
+        }
+    };
+    if (p.in.l2norm_q) l2norm_rows(qv);
+    if (p.in.l2norm_k) l2norm_rows(kv);
 #pragma unroll
     for (int ii = 1; ii < RPT; ++ii)
 #pragma unroll
@@ -707,6 +717,20 @@ __device__ __forceinline__ int tab_kg(int w) { return w == 3 ? TAB_ONE : 6 + w; 
 constexpr int TAB_EG = 9;
 __device__ __forceinline__ int tab_dg(int w) { return 10 + w; }
 
+// Reciprocal L2 norm of rows held in the 16x16x32 operand layout: lane (lq, lr) holds
+// channels 32s + 8lq .. +7 of row lr, so the 4 lane groups lq share each row.
+template <int NS>
+__device__ __forceinline__ float frag_row_rstd(const bf16x8 (&x)[NS]) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { const float f = (float)x[s][e]; ss = fmaf(f, f, ss); }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    return l2norm_rstd(ss);
+}
+
 template <int K, int V, typename TB>
 __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) {
     typedef __bf16 TW;
@@ -722,13 +746,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
     //  R1  factor table [NTAB][K] and the published column operands kap[3][NKS][2][64][4]
     //      (Stage 2), then T [64][64] and T tiles in accumulator layout [6][64][4] (solve)
     //  R2  block totals of the gate [4][K] (Stage 1), L [64][64] (Stage 2 and solve),
-    //      T beta as a bf16 tile (products)
+    //      T beta as two bf16 tiles, hi and lo (products)
     //  R4  (k 2^Gamma)^T and v^T bf16 tiles
     constexpr int TAB_F = NTAB * K;
     constexpr int KAP_F = 3 * NKS * 2 * 64 * 4;
     constexpr int R1_F = (TAB_F + KAP_F) > (C * C + 6 * 256) ? (TAB_F + KAP_F) : (C * C + 6 * 256);
     constexpr int R2_F = C * C;
-    static_assert(4 * K <= R2_F && TB64::BYTES <= R2_F * 4, "R2 holds the block totals and T beta");
+    static_assert(4 * K <= R2_F && 2 * TB64::BYTES <= R2_F * 4, "R2 holds the block totals and T beta");
     __shared__ __attribute__((aligned(16))) float R1[R1_F];
     __shared__ __attribute__((aligned(16))) float R2[R2_F];
     __shared__ __attribute__((aligned(16))) TW KDt[K * C];
@@ -740,7 +764,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
     float* TA = R1 + C * C;
     float* bt = R2;
     float* Lm = R2;
-    TW* TBs = reinterpret_cast<TW*>(R2);
+    TW* TBs = reinterpret_cast<TW*>(R2);                         // T beta, hi
+    TW* TBl = reinterpret_cast<TW*>(reinterpret_cast<char*>(R2) + TB64::BYTES);   // lo
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -777,7 +802,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
     float loc[NKS][8];
     float beta_i = 0.f;
     if (live) {
-        beta_i = to_f32(reinterpret_cast<const TB*>(p.beta)[r_g * p.HV + hv]);
+        beta_i = load_beta<TB>(p, r_g, hv);
         const TW* qp = reinterpret_cast<const TW*>(p.q) + (r_g * p.H + h) * K + 8 * lq;
         const TW* kp = reinterpret_cast<const TW*>(p.k) + (r_g * p.H + h) * K + 8 * lq;
         const TW* vp = reinterpret_cast<const TW*>(p.v) + (r_g * p.HV + hv) * V + 8 * lq;
@@ -800,6 +825,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
             for (int e = 0; e < 8; ++e) vv[s][e] = (__bf16)0.f;
     }
     if (lq == 0) betas[i_row] = beta_i;
+    // optional L2 normalisation of the q / k rows: each lane's row is x * rn, with the row
+    // scale folded into the fp32 products below (the bf16 inputs stay exact)
+    const float rq = p.in.l2norm_q ? frag_row_rstd(qv) : 1.f;
+    const float rk = p.in.l2norm_k ? frag_row_rstd(kv) : 1.f;
 
     // Gamma_i - P_w (inclusive, down the 16 rows of the block); the block total is the
     // value of the block's last row
@@ -852,8 +881,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
             {
                 float xq[8], xk[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) { xq[e] = to_f32(qv[s][e]); xk[e] = to_f32(kv[s][e]); }
-                split8(xq, hq, lqv);   // bf16 inputs: exact, lo = 0
+                for (int e = 0; e < 8; ++e) { xq[e] = to_f32(qv[s][e]) * rq; xk[e] = to_f32(kv[s][e]) * rk; }
+                split8(xq, hq, lqv);   // lo = 0 unless a row scale applies
                 split8(xk, hk, lk);
                 td = mma3(hk, lk, hq, lqv, td);
             }
@@ -881,8 +910,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
                         la = rowside ? prev : x;
                     }
                     const float f = exp2_fast(rowside ? x - la : la - x);
-                    const float kf = to_f32(kv[s][e]);
-                    xq[e] = rowside ? to_f32(qv[s][e]) * f : 0.f;
+                    const float kf = to_f32(kv[s][e]) * rk;
+                    xq[e] = rowside ? (to_f32(qv[s][e]) * rq) * f : 0.f;
                     xk[e] = rowside ? kf * f : 0.f;
                     xc[e] = rowside ? 0.f : kf * f;
                 }
@@ -915,9 +944,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
         float xq[8], xk[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float kf = to_f32(kv[s][e]);
+            const float kf = to_f32(kv[s][e]) * rk;
             const float bi = exp2_fast(loc[s][e]);
-            xq[e] = to_f32(qv[s][e]) * bi;
+            xq[e] = (to_f32(qv[s][e]) * rq) * bi;
             xk[e] = kf * bi;
             kap_own[s][e] = kf * exp2_fast(row_bcast<15>(loc[s][e]) - loc[s][e]);
         }
@@ -1144,22 +1173,28 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
         lds_barrier();
     }
 
-    // ---- T beta (bf16, lower blocks only) ----
+    // ---- T beta as hi + lo bf16 tiles (lower blocks only). A single bf16 T beta is the
+    //      largest rounding left once beta spreads over (0, 2): u and w share it, and its
+    //      error changes the effective erase strength, which does not decay when beta k^T k
+    //      is near 1 or 2 ----
     for (int t = tid; t < C * C / 8; t += NTHREADS) {
         const int i = t >> 3, j0 = (t & 7) * 8;
-        bf16x8 o;
+        float x[8];
         if ((j0 >> 4) <= (i >> 4)) {
             const f32x4 t0 = *reinterpret_cast<const f32x4*>(Tm + sw(i, j0));
             const f32x4 t1 = *reinterpret_cast<const f32x4*>(Tm + sw(i, j0 + 4));
             const f32x4 b0 = *reinterpret_cast<const f32x4*>(betas + j0);
             const f32x4 b1 = *reinterpret_cast<const f32x4*>(betas + j0 + 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { o[e] = (__bf16)(t0[e] * b0[e]); o[4 + e] = (__bf16)(t1[e] * b1[e]); }
+            for (int e = 0; e < 4; ++e) { x[e] = t0[e] * b0[e]; x[4 + e] = t1[e] * b1[e]; }
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = (__bf16)0.f;
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
         }
-        *reinterpret_cast<bf16x8*>(TBs + TB64::idx(i, j0)) = o;
+        bf16x8 hi8, lo8;
+        split8(x, hi8, lo8);
+        *reinterpret_cast<bf16x8*>(TBs + TB64::idx(i, j0)) = hi8;
+        *reinterpret_cast<bf16x8*>(TBl + TB64::idx(i, j0)) = lo8;
     }
     lds_barrier();
 
@@ -1167,6 +1202,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
 #pragma unroll
     for (int nu = 0; nu < V / 16; nu += 2) {
         f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        tile_mma2<TW, TB64, TVT, C>(a0, TBl, 16 * w, VTt, 16 * nu, true,
+                                    a1, TBl, 16 * w, VTt, 16 * nu + 16, true, lane);
         tile_mma2<TW, TB64, TVT, C>(a0, TBs, 16 * w, VTt, 16 * nu, true,
                                     a1, TBs, 16 * w, VTt, 16 * nu + 16, true, lane);
         *reinterpret_cast<f32x4*>(out_u + AccTile::quad(16 * nu + lr, 16 * w + 4 * lq)) = a0;
@@ -1176,6 +1213,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
     for (int s = 0; s < NKS; ++s) {
         // transposed tiles D'[d][i] for channels 32s .. 32s+31, rows i of block w
         f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+        tile_mma2<TW, TKD, TB64, C>(x, KDt, 32 * s, TBl, 16 * w, true,
+                                    y, KDt, 32 * s + 16, TBl, 16 * w, true, lane);
         tile_mma2<TW, TKD, TB64, C>(x, KDt, 32 * s, TBs, 16 * w, true,
                                     y, KDt, 32 * s + 16, TBs, 16 * w, true, lane);
         float o8[8];
@@ -1860,8 +1899,7 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     ip.dense = dense;   // then NCmax = B * NT chunks, all present
     ip.NT = NT;
     ip.scale = a.scale;
-    ip.g_raw = a.g_raw; ip.gate_mode = a.gate_mode; ip.A_log = a.A_log; ip.dt_bias = a.dt_bias;
-    ip.has_lower_bound = a.has_lower_bound; ip.lower_bound = a.lower_bound;
+    ip.in = a.in;
     const long long nintra = (long long)L.NCmax * a.HV;
     if (nintra > 0) {
         if constexpr (sizeof(TIn) == 2)

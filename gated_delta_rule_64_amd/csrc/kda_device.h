@@ -29,9 +29,37 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
-// 2^x with the hardware transcendental (v_exp_f32); x <= 0 in every use below, results
-// under 2^-126 flush to zero, which is below anything the outputs can resolve.
+// 2^x with the hardware transcendental (v_exp_f32): results under 2^-126 flush to zero
+// (below anything the outputs can resolve), large x gives +inf.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------------
+// Fusable input preprocessing (fp32, per element or per row)
+// ---------------------------------------------------------------------------------
+
+// The gate activation: log2 decay = -e^A softplus(x) / ln 2 = amp log2(1 + 2^(x log2 e))
+// with amp = -e^A, and, when has_lb, the natural-log value clamped from below at the bound
+// (lb2 = bound * log2 e, the bound in log2 units). For x > 15 the softplus is x to fp32
+// precision. Where 1 + 2^(x log2 e) rounds to 1 (x below about -17) the result is 0
+// instead of a value under 6e-8 e^A: a decay factor off by less than 4e-8 e^A per token.
+__device__ __forceinline__ float gate_log2_from_raw(float x, float amp, bool has_lb, float lb2) {
+    const float y = x * LOG2E;
+    const float sp2 = x > 15.f ? y : __builtin_amdgcn_logf(1.f + exp2_fast(y));   // softplus / ln 2
+    const float g2 = amp * sp2;
+    return has_lb ? fmaxf(g2, lb2) : g2;
+}
+
+// beta from its pre-activation: bscale * sigmoid(b) = bscale / (1 + 2^(-b log2 e)); below
+// b of about -88 the exponential overflows to +inf and beta is 0.
+__device__ __forceinline__ float beta_from_logit(float b, float bscale) {
+    return bscale / (1.f + exp2_fast(-LOG2E * b));
+}
+
+// Reciprocal norm of a row whose squares sum to ss: 1 / sqrt(ss + 1e-6) (v_rsq_f32).
+constexpr float L2NORM_EPS = 1e-6f;
+__device__ __forceinline__ float l2norm_rstd(float ss) { return __builtin_amdgcn_rsqf(ss + L2NORM_EPS); }
 
 // ---------------------------------------------------------------------------------
 // MFMA 16x16 tile products: C[16x16] += A[16 x Kc] * B[16 x Kc]^T, both operands with

@@ -9,11 +9,31 @@
 
 namespace kda {
 
+// How the loads obtain the per-token log2 decay (the public kda_gate values).
+enum GateMode {
+    GATE_LOG2 = KDA_GATE_LOG2,           // g: fp32 per-token log2 decay, as given
+    GATE_RAW_F32 = KDA_GATE_RAW_F32,     // g_raw fp32: -exp(A_log) softplus(g_raw + dt_bias) / ln 2
+    GATE_RAW_BF16 = KDA_GATE_RAW_BF16    // g_raw bf16: same activation
+};
+
+// Gate source and input preprocessing, as the kernels take them.
+struct InputSpec {
+    int gate_mode;             // GateMode
+    const void* g_raw;         // GATE_RAW_*: raw gate input
+    const float* A_log;        // [HV]
+    const float* dt_bias;      // [HV * K] or NULL
+    int has_lower_bound;
+    float lower_bound;
+    int l2norm_q, l2norm_k;    // normalise q / k rows in the loads
+    float beta_sig;            // 0: beta as given; else beta = beta_sig * sigmoid(beta)
+};
+
 struct RecurrentArgs {
     const void* q;
     const void* k;
     const void* v;
     const float* g;
+    InputSpec in;
     const void* beta;
     const float* initial_state;
     const int32_t* cu_seqlens;
@@ -26,24 +46,12 @@ struct RecurrentArgs {
     hipStream_t stream;
 };
 
-// How the Stage 1 loads obtain the per-token log2 decay.
-enum GateMode {
-    GATE_LOG2 = 0,       // g: fp32 per-token log2 decay, as given
-    GATE_RAW_F32 = 1,    // g_raw fp32: -exp(A_log) softplus(g_raw + dt_bias) / ln 2
-    GATE_RAW_BF16 = 2    // g_raw bf16: same activation
-};
-
 struct ChunkArgs {
     const void* q;
     const void* k;
     const void* v;
     const float* g;
-    const void* g_raw;         // GATE_RAW_*: raw gate input
-    int gate_mode;
-    const float* A_log;        // [HV]
-    const float* dt_bias;      // [HV * K] or NULL
-    int has_lower_bound;
-    float lower_bound;
+    InputSpec in;
     const void* beta;
     const float* initial_state;
     const int32_t* cu_seqlens;

@@ -1,7 +1,9 @@
 // Per-token KDA recurrence (decode and token-by-token prefill) for gfx950.
 //
 // Contract: "Add fused recurrent_kda for decode and inference prefill" (attention-gym
-// PR #317, description): the gate is the per-token log2 decay, the scale is 1/sqrt(K),
+// PR #317, description): the gate is the per-token log2 decay (or, optionally, formed
+// from the raw gate input by the fused activation, with q / k normalisation and the beta
+// sigmoid fused into the loads as in the chunked path), the scale is 1/sqrt(K),
 // compute and state are fp32 whatever the input dtype, packed int32 offsets with empty
 // slots passing their state through bitwise, one state per logical sequence. The update
 // order (decay, delta-rule write, read of the updated state) is the one of KDA's chunk
@@ -75,10 +77,20 @@ __device__ __forceinline__ float sum_row_groups(float x) {
     return x;
 }
 
+template <int R>
+__device__ __forceinline__ void l2norm_rows(float (&x)[R]) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) ss = fmaf(x[i], x[i], ss);
+    const float rn = l2norm_rstd(sum_row_groups(ss));
+#pragma unroll
+    for (int i = 0; i < R; ++i) x[i] *= rn;
+}
+
 template <int K, typename TIn, typename TB>
 __global__ __launch_bounds__(256) void recurrent_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ g, const TB* __restrict__ beta,
+    const float* __restrict__ g, const InputSpec in, const TB* __restrict__ beta,
     const float* initial_state, const int32_t* __restrict__ cu_seqlens,
     TIn* __restrict__ o, float* final_state, int T, int H, int HV, int V, int nvt,
     long long n_items, float scale, int32_t* dev_status) {
@@ -127,14 +139,37 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
             for (int j = 0; j < 4; ++j) S[i][j] = 0.0f;
     }
 
+    const float amp = in.gate_mode != GATE_LOG2 ? -expf(in.A_log[hv]) : 0.f;
+    const float lb2 = in.lower_bound * LOG2E;
     for (int t = bos; t < eos; ++t) {
         const long long r = row0 + t;
         float kk[R], qq[R], ee[R], vv[4];
         load_row_block(k + ((size_t)r * H + h) * K + d0, kk, R);
         load_row_block(q + ((size_t)r * H + h) * K + d0, qq, R);
-        load_row_block(g + ((size_t)r * HV + hv) * K + d0, ee, R);
+        const size_t gofs = ((size_t)r * HV + hv) * K + d0;
+        if (in.gate_mode == GATE_LOG2) {
+            load_row_block(g + gofs, ee, R);
+        } else {
+            // the fused gate activation on the raw gate input
+            if (in.gate_mode == GATE_RAW_BF16)
+                load_row_block(static_cast<const __bf16*>(in.g_raw) + gofs, ee, R);
+            else
+                load_row_block(static_cast<const float*>(in.g_raw) + gofs, ee, R);
+            if (in.dt_bias) {
+                float db[R];
+                load_row_block(in.dt_bias + (size_t)hv * K + d0, db, R);
+#pragma unroll
+                for (int i = 0; i < R; ++i) ee[i] += db[i];
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) ee[i] = gate_log2_from_raw(ee[i], amp, in.has_lower_bound, lb2);
+        }
         load4(v + ((size_t)r * HV + hv) * V + c0, vv);
-        const float b = to_f32(beta[(size_t)r * HV + hv]);
+        float b = to_f32(beta[(size_t)r * HV + hv]);
+        if (in.beta_sig != 0.f) b = beta_from_logit(b, in.beta_sig);
+        // optional L2 normalisation of q / k (the four row groups hold a row between them)
+        if (in.l2norm_q) l2norm_rows(qq);
+        if (in.l2norm_k) l2norm_rows(kk);
 
         float p[4] = {0.f, 0.f, 0.f, 0.f};
         float rq[4] = {0.f, 0.f, 0.f, 0.f};
@@ -181,7 +216,7 @@ hipError_t launch_t(const RecurrentArgs& a) {
     if (n_items == 0) return hipSuccess;
     const long long blocks = (n_items + 3) / 4;
     hipLaunchKernelGGL((recurrent_kernel<K, TIn, TB>), dim3((unsigned)blocks), dim3(256), 0,
-                       a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g,
+                       a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.in,
                        (const TB*)a.beta, a.initial_state, a.cu_seqlens, (TIn*)a.o,
                        a.final_state, a.T, a.H, a.HV, a.V, nvt, n_items, a.scale,
                        a.dev_status);

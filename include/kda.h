@@ -62,7 +62,8 @@ enum kda_status {
     KDA_ERR_DTYPE = -3,        /* unknown dtype code */
     KDA_ERR_UNSUPPORTED = -4,  /* K, V or chunk size outside what the kernels cover */
     KDA_ERR_WORKSPACE = -5,    /* workspace missing, too small or misaligned */
-    KDA_ERR_HIP = -6           /* a kernel launch failed */
+    KDA_ERR_HIP = -6,          /* a kernel launch failed */
+    KDA_ERR_ARG = -7           /* an option outside its documented set (gate, preprocess) */
 };
 
 enum kda_dtype {
@@ -72,6 +73,34 @@ enum kda_dtype {
 
 /* bit flags written into *dev_status by device-side checks */
 #define KDA_DEV_BAD_CU_SEQLENS 1
+
+/* Where the per-token log2 decay comes from (the `gate` argument of the _ex entry points). */
+enum kda_gate {
+    KDA_GATE_LOG2 = 0,      /* g: fp32 per-token log2 decay, used as given */
+    KDA_GATE_RAW_F32 = 1,   /* g: fp32 raw gate input; the activation is fused (see below) */
+    KDA_GATE_RAW_BF16 = 2   /* g: bf16 raw gate input; the same activation */
+};
+
+/*
+ * Input preprocessing fused into the kernels' loads (the `preprocess` argument of the _ex
+ * entry points, a bitwise OR; 0 = inputs used as given). Source: "kernel-fun 0.2.0.dev1
+ * sdist", the autograd Function's forward (use_qk_l2norm: fla's l2norm of q and k before
+ * the gate cumsum) and the chunk_kda wrapper (use_beta_sigmoid_in_kernel: beta through a
+ * sigmoid, times 2 when negative eigenvalues are allowed); the deferred q normalisation
+ * of attention-gym PR #345 (description).
+ *   KDA_PRE_L2NORM_Q     q <- q / sqrt(sum_d q_d^2 + 1e-6), per (token, head); the pages
+ *                        give no epsilon, 1e-6 is the reading taken. The row scale is
+ *                        applied in fp32 (on the bf16 path it is folded into the fp32
+ *                        products that feed the matrix cores, so nothing is re-rounded).
+ *   KDA_PRE_L2NORM_K     the same for k.
+ *   KDA_PRE_BETA_SIGMOID beta <- sigmoid(beta), in fp32.
+ *   KDA_PRE_NEG_EIGVAL   with KDA_PRE_BETA_SIGMOID: beta <- 2 sigmoid(beta), in (0, 2).
+ *                        Invalid without it.
+ */
+#define KDA_PRE_L2NORM_Q 1
+#define KDA_PRE_L2NORM_K 2
+#define KDA_PRE_BETA_SIGMOID 4
+#define KDA_PRE_NEG_EIGVAL 8
 
 /*
  * Chunked forward (prefill). The method of "kernel-fun 0.2.0.dev1 sdist",
@@ -141,6 +170,24 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void*
                         hipStream_t stream);
 
 /*
+ * The chunked forward with every option: the gate source (`gate`, a kda_gate; for
+ * KDA_GATE_LOG2, A_log and dt_bias must be NULL and has_lower_bound 0, otherwise the
+ * activation and its arguments are those of kda_chunk_fwd_gated, with g the raw gate
+ * input), the input preprocessing flags (`preprocess`, KDA_PRE_*), and the optional
+ * `events` of kda_chunk_fwd_timed (NULL for none). Everything else as kda_chunk_fwd;
+ * the workspace size is the same. kda_chunk_fwd, kda_chunk_fwd_timed and
+ * kda_chunk_fwd_gated are this call with gate and preprocess at their plain values.
+ */
+int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
+                     const float* A_log, const float* dt_bias, int has_lower_bound,
+                     float lower_bound, const void* beta, int preprocess,
+                     const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                     float* final_state, int B, int T, int H, int HV, int K, int V,
+                     int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                     void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                     hipStream_t stream, hipEvent_t* events);
+
+/*
  * Workspace bytes kda_chunk_fwd needs for these sizes (packed != 0 for packed mode,
  * N sequences). Returns 0 for invalid sizes.
  */
@@ -162,10 +209,25 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* 
                       int T, int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
                       float scale, int32_t* dev_status, hipStream_t stream);
 
+/*
+ * kda_recurrent_fwd with the gate source and the input preprocessing of kda_chunk_fwd_ex
+ * (the same `gate`, A_log, dt_bias, has_lower_bound, lower_bound and `preprocess`
+ * arguments and rules): the decode-side counterpart of the fused preprocessing.
+ */
+int kda_recurrent_fwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
+                         const float* A_log, const float* dt_bias, int has_lower_bound,
+                         float lower_bound, const void* beta, int preprocess,
+                         const float* initial_state, const int32_t* cu_seqlens, int N,
+                         void* o, float* final_state, int B, int T, int H, int HV, int K,
+                         int V, int qkv_dtype, int beta_dtype, float scale,
+                         int32_t* dev_status, hipStream_t stream);
+
 /* Reason for the last non-KDA_OK return on this thread ("" if none). */
 const char* kda_last_error(void);
 
-/* ABI version of this header (bumped on any signature change). */
+/* ABI version of this header (bumped on any signature change or added entry point);
+ * the library returns the KDA_ABI_VERSION it was built with. */
+#define KDA_ABI_VERSION 2
 int kda_abi_version(void);
 
 #ifdef __cplusplus

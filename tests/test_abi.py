@@ -33,6 +33,23 @@ def test_header_declares_the_entry_points():
               "kda_last_error", "kda_abi_version"):
         assert n in names
     assert "kda_chunk_fwd_gated" in names
+    assert "kda_chunk_fwd_ex" in names and "kda_recurrent_fwd_ex" in names
+
+
+def _header_int(name):
+    m = re.search(r"#define\s+%s\s+(\d+)" % name, open(HEADER).read())
+    if m:
+        return int(m.group(1))
+    m = re.search(r"\b%s\s*=\s*(-?\d+)" % name, open(HEADER).read())
+    return int(m.group(1))
+
+
+def test_binding_constants_match_the_header():
+    from gated_delta_rule_64_amd import _lib
+    for name in ("KDA_F32", "KDA_BF16", "KDA_DEV_BAD_CU_SEQLENS", "KDA_GATE_LOG2",
+                 "KDA_GATE_RAW_F32", "KDA_GATE_RAW_BF16", "KDA_PRE_L2NORM_Q", "KDA_PRE_L2NORM_K",
+                 "KDA_PRE_BETA_SIGMOID", "KDA_PRE_NEG_EIGVAL"):
+        assert getattr(_lib, name) == _header_int(name), name
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -46,7 +63,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == _header_int("KDA_ABI_VERSION")
 
 
 def _rec_bytes(K, V, elem):
@@ -118,6 +135,30 @@ def _gated(lib, **kw):
                                    a["st"], a["stream"])
 
 
+def _ex(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gate=0, A=None, dt=None, hlb=0, lb=0.0, beta=FAKE,
+             pre=0, h0=None, cu=None, N=1, o=FAKE, ht=None, B=1, T=64, H=2, HV=2, K=128, V=128,
+             qd=1, bd=1, scale=0.0, cs=64, ws=FAKE, wsb=1 << 40, st=None, stream=None, ev=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["gate"], a["A"], a["dt"],
+                                a["hlb"], a["lb"], a["beta"], a["pre"], a["h0"], a["cu"], a["N"],
+                                a["o"], a["ht"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"],
+                                a["qd"], a["bd"], a["scale"], a["cs"], a["ws"], a["wsb"],
+                                a["st"], a["stream"], a["ev"])
+
+
+def _rec_ex(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gate=0, A=None, dt=None, hlb=0, lb=0.0, beta=FAKE,
+             pre=0, h0=None, cu=None, N=1, o=FAKE, ht=None, B=1, T=1, H=2, HV=2, K=128, V=128,
+             qd=1, bd=1, scale=0.0, st=None, stream=None)
+    a.update(kw)
+    return lib.kda_recurrent_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["gate"], a["A"], a["dt"],
+                                    a["hlb"], a["lb"], a["beta"], a["pre"], a["h0"], a["cu"],
+                                    a["N"], a["o"], a["ht"], a["B"], a["T"], a["H"], a["HV"],
+                                    a["K"], a["V"], a["qd"], a["bd"], a["scale"], a["st"],
+                                    a["stream"])
+
+
 CASES = [
     ("null q", dict(q=None), -1),
     ("HV % H", dict(H=3, HV=4), -2),
@@ -146,6 +187,42 @@ def test_recurrent_rejects(lib, name, kw, code):
 def test_gated_rejects_common(lib, name, kw, code):
     assert _gated(lib, **kw) == code
     assert lib.kda_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("name,kw,code", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("call", ["chunk_ex", "recurrent_ex"])
+def test_ex_rejects_common(lib, call, name, kw, code):
+    f = _ex if call == "chunk_ex" else _rec_ex
+    assert f(lib, **kw) == code
+    assert lib.kda_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("call", ["chunk_ex", "recurrent_ex"])
+def test_ex_option_rejects(lib, call):
+    f = _ex if call == "chunk_ex" else _rec_ex
+    assert f(lib, gate=3) == -7                       # unknown gate source
+    assert b"gate" in lib.kda_last_error()
+    assert f(lib, pre=16) == -7                       # unknown preprocessing bit
+    assert f(lib, pre=8) == -7                        # doubled beta without the sigmoid
+    assert b"NEG_EIGVAL" in lib.kda_last_error()
+    assert f(lib, A=FAKE) == -7                       # activation arguments with a log2 gate
+    assert f(lib, hlb=1, lb=-1.0) == -7
+    assert f(lib, gate=2, A=None) == -1               # raw gate: A_log required
+    assert f(lib, gate=1, A=FAKE, dt=FAKE + 4) == -2  # misaligned dt_bias
+    assert f(lib, gate=2, A=FAKE, hlb=1, lb=0.0) == -2
+    assert f(lib, gate=2, A=FAKE, g=None) == -1       # the raw gate itself
+    assert f(lib, gate=2, A=FAKE, g=FAKE + 8) == -2
+
+
+def test_chunk_ex_then_chunk_checks(lib):
+    # valid options, then the chunked path's own checks as usual
+    ok = dict(gate=2, A=FAKE, dt=FAKE, hlb=1, lb=-5.0, pre=15)
+    assert _ex(lib, cs=32, **ok) == -4
+    assert _ex(lib, ws=None, **ok) == -5
+    assert _rec_ex(lib, K=32, **ok) == -4
+    assert _ex(lib, cu=FAKE, N=0, T=0, **ok) == 0
+    assert _rec_ex(lib, cu=FAKE, N=0, T=0, **ok) == 0
+    assert lib.kda_last_error().decode() == ""
 
 
 def test_gated_specific_rejects(lib):

@@ -494,3 +494,137 @@ def test_chunk_head_dims(dtype, K, V, steep):
     o_ref, s_ref = oracle_of(d)
     check("o", o, o_ref, dtype)
     check("state", s, s_ref, dtype)
+
+
+# ------------------------------------------------------------------------------------
+# input preprocessing fused into the loads: q / k L2 normalisation, beta sigmoid (x2)
+# ------------------------------------------------------------------------------------
+PRE_CASES = [  # (l2norm_q, l2norm_k, beta sigmoid, allow_neg_eigval)
+    (True, True, True, False),
+    (True, False, True, True),
+    (False, True, False, False),
+    (False, False, True, True),
+]
+
+
+def _raw_inputs(d, seed, lq=True, lk=True, sig=True, zero_rows=True):
+    """Inputs for the preprocessing flags: q (lq) and k (lk) un-normalised, every
+    (token, head) row of the unit-norm draw times 10^U[-3, 3] with about 2% of rows zero;
+    beta (sig) replaced by pre-activations N(0, 2^2) in beta's dtype. Tensors whose
+    preprocessing is off keep the recipe's values (a delta rule on un-normalised keys or
+    beta outside (0, 2) diverges)."""
+    gen = torch.Generator().manual_seed(seed)
+
+    def scaled(x):
+        B, T, H, _ = x.shape
+        s = torch.pow(10.0, torch.empty(B, T, H, 1).uniform_(-3.0, 3.0, generator=gen))
+        y = x.cpu().float() * s
+        if zero_rows:
+            y = torch.where(torch.rand(B, T, H, 1, generator=gen) < 0.02, torch.zeros_like(y), y)
+        return y.to(x.dtype).to(DEV)
+
+    q = scaled(d["q"])
+    k = scaled(d["k"])
+    logits = torch.randn(tuple(d["beta"].shape), generator=gen).mul(2.0).to(d["beta"].dtype).to(DEV)
+    return dict(d, q=q if lq else d["q"], k=k if lk else d["k"], beta=logits if sig else d["beta"])
+
+
+def _pre_oracle(r, lq, lk, sig, neg, g2=None):
+    """The oracle's preprocessing (fp64) followed by the recurrence."""
+    q = oracle.l2norm(r["q"]) if lq else r["q"]
+    k = oracle.l2norm(r["k"]) if lk else r["k"]
+    beta = oracle.beta_sigmoid(r["beta"], neg) if sig else r["beta"]
+    return oracle.recurrent(q, k, r["v"], r["g"] if g2 is None else g2, beta, r["initial_state"],
+                            r["cu_seqlens"])
+
+
+def _run_ex(path, r, lq, lk, sig, neg, **kw):
+    import gated_delta_rule_64_amd as kda
+    fn = kda.kda_chunk_fwd_ex if path == "chunk" else kda.kda_recurrent_fwd_ex
+    o, ht = fn(r["q"], r["k"], r["v"], kw.pop("g", r["g"]), r["beta"], r["initial_state"],
+               r["cu_seqlens"], output_final_state=True, l2norm_q=lq, l2norm_k=lk,
+               use_beta_sigmoid_in_kernel=sig, allow_neg_eigval=neg, **kw)
+    torch.cuda.synchronize()
+    return o, ht
+
+
+@pytest.mark.parametrize("lq,lk,sig,neg", PRE_CASES, ids=lambda x: str(int(x)))
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_preprocess(path, dtype, lq, lk, sig, neg):
+    """Normalisation and beta activation in the loads against the oracle's fp64
+    preprocessing: row scales over six decades, zero rows, a short last chunk."""
+    d = small(1, 230, 2, 4, 128, 128, dtype, seed=50)
+    r = _raw_inputs(d, 51, lq, lk, sig)
+    log(f"[preprocess {path}] {dtype} l2norm_q={lq} l2norm_k={lk} sigmoid={sig} neg_eigval={neg}")
+    o, ht = _run_ex(path, r, lq, lk, sig, neg)
+    o_ref, ht_ref = _pre_oracle(r, lq, lk, sig, neg)
+    check("o", o, o_ref, dtype)
+    check("state", ht, ht_ref, dtype)
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_preprocess_fused_equals_explicit(path):
+    """bf16 inputs with the fused normalisation and beta activation against the explicit
+    route: q / k normalised and beta activated beforehand in fp32 torch, then the plain
+    fp32 call (v widened exactly). Within the bf16 bound of the explicit result."""
+    d = small(1, 200, 2, 4, 128, 128, torch.bfloat16, seed=52)
+    r = _raw_inputs(d, 53)
+    o, ht = _run_ex(path, r, True, True, True, True)
+
+    def norm(x):
+        xf = x.float()
+        return xf / torch.sqrt((xf * xf).sum(-1, keepdim=True) + 1e-6)
+
+    e = dict(r, q=norm(r["q"]), k=norm(r["k"]), v=r["v"].float(),
+             beta=torch.sigmoid(r["beta"].float()) * 2.0)
+    o2, ht2 = run(path, e)
+    check("o vs explicit", o, to64(o2), torch.bfloat16)
+    check("state vs explicit", ht, to64(ht2), torch.bfloat16)
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_preprocess_with_gate_packed(path):
+    """Every option at once in packed mode: raw bf16 gate with dt_bias and a lower bound,
+    both normalisations, beta = 2 sigmoid; an empty slot and a tail of unowned rows."""
+    lens = [130, 0, 64, 37, 200]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    Tp = cu[-1] + 40
+    d = small(1, Tp, 2, 4, 128, 128, torch.bfloat16, seed=54)
+    d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    d["initial_state"] = torch.randn(len(lens), 4, 128, 128, generator=torch.Generator().manual_seed(6)).mul(0.05).to(DEV)
+    r = _raw_inputs(d, 55)
+    g_raw, A_log, dt_bias = _gate_params(1, Tp, 4, 128, torch.bfloat16, seed=80)
+    out = torch.full_like(r["v"], float("nan"))
+    log(f"[preprocess + gate, packed {path}] lens={lens}")
+    o, ht = _run_ex(path, r, True, True, True, True, g=g_raw, use_gate_in_kernel=True,
+                    A_log=A_log, dt_bias=dt_bias, lower_bound=-6.0, out=out)
+    g2 = oracle.gate_activation(g_raw, A_log, dt_bias, -6.0)
+    o_ref, ht_ref = _pre_oracle(r, True, True, True, True, g2=g2)
+    rows = valid_rows(cu, Tp)
+    check("o", o[0][torch.from_numpy(rows).to(DEV)], o_ref[0][rows], torch.bfloat16)
+    assert torch.isnan(o[0, cu[-1]:].float()).all(), "tail must stay untouched"
+    check("state", ht, ht_ref, torch.bfloat16)
+    assert torch.equal(ht[1], d["initial_state"][1]), "empty slot passes its state bitwise"
+
+
+def test_preprocess_c3_full():
+    """The long-context workload (B=1 T=8192 H=16 HV=32 K=V=128 bf16) with every fusion
+    on, as the benchmark's fused-input leg runs it: un-normalised q / k, beta logits,
+    raw bf16 gates with dt_bias. Whole output against the oracle."""
+    import gated_delta_rule_64_amd as kda
+    d = to_device(inputs.make("c3"))
+    r = _raw_inputs(d, 56, zero_rows=False)
+    g_raw, A_log, dt_bias = _gate_params(1, 8192, 32, 128, torch.bfloat16, seed=81)
+    log("[c3 chunk, all input fusions] B=1 T=8192 H=16 HV=32 K=V=128 bf16")
+    o, ht = kda.kda_chunk_fwd_ex(r["q"], r["k"], r["v"], g_raw, r["beta"], None, None,
+                                 use_gate_in_kernel=True, A_log=A_log, dt_bias=dt_bias,
+                                 use_qk_l2norm_in_kernel=True, use_beta_sigmoid_in_kernel=True,
+                                 allow_neg_eigval=True)
+    torch.cuda.synchronize()
+    assert ht is None
+    g2 = oracle.gate_activation(g_raw, A_log, dt_bias, None)
+    o_ref, _ = _pre_oracle(dict(r, initial_state=None, cu_seqlens=None), True, True, True, True, g2=g2)
+    check("o", o, o_ref, torch.bfloat16)
