@@ -65,6 +65,12 @@ def load_library():
         lib.kda_recurrent_fwd_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp,
                                              vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                              i32, f32, vp, vp]
+        lib.kda_chunk_bwd.restype = i32
+        lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+                                      sz, vp, vp]
+        lib.kda_chunk_bwd_workspace_bytes.restype = sz
+        lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32] * 9
         lib.kda_recurrent_fwd.restype = i32
         lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                           i32, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp]
@@ -348,3 +354,43 @@ def kda_recurrent_fwd_ex(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
     if rc != 0:
         raise KdaError(rc, lib.kda_last_error().decode())
     return out, final_state
+
+
+def kda_chunk_bwd(q, k, v, g, beta, do, initial_state=None, cu_seqlens=None, dht=None,
+                  scale=None, *, want_dh0=True, workspace=None, dev_status=None):
+    """Gradients of the chunked forward. ``do`` [B, T, HV, V] in q's dtype is the gradient
+    with respect to o, ``dht`` (float32 [N, HV, K, V] or None) with respect to the final
+    state. Returns ``(dq, dk, dv, dg, dbeta, dh0)``: dq, dk, dv in q's dtype, dg float32
+    (with respect to the per-token log2 decay g), dbeta in beta's dtype, dh0 float32
+    [N, HV, K, V] (None unless ``want_dh0``). Rows outside every sequence are zero."""
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens)
+    if tuple(do.shape) != tuple(v.shape) or do.dtype != q.dtype:
+        raise ValueError("do must match v's shape and q's dtype")
+    if dht is not None and (dht.dtype != torch.float32 or tuple(dht.shape) != (N, HV, K, V)):
+        raise ValueError(f"dht must be float32 {[N, HV, K, V]}")
+    _check_device([("do", do), ("dht", dht)])
+    dq = torch.zeros_like(q)
+    dk = torch.zeros_like(k)
+    dv = torch.zeros_like(v)
+    dg = torch.zeros(B, T, HV, K, dtype=torch.float32, device=dev)
+    dbeta = torch.zeros_like(beta)
+    dh0 = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev) if want_dh0 else None
+    need = lib.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, int(cu_seqlens is not None), qkv)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), N, _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv),
+                           _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, HV, K, V, qkv, bdt,
+                           float(scale or 0.0), 64, _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _ptr(dev_status),
+                           _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+def kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, packed, dtype=KDA_BF16) -> int:
+    if isinstance(dtype, torch.dtype):
+        dtype = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load_library().kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, int(bool(packed)), int(dtype)))

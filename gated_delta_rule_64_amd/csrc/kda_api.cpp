@@ -176,11 +176,74 @@ int recurrent_impl(const void* q, const void* k, const void* v, const void* g, i
     return KDA_OK;
 }
 
+int chunk_bwd_impl(const kda::ChunkBwdArgs& a0, const float* g, int chunk_size) {
+    kda::ChunkBwdArgs a = a0;
+    int rc = check_common(a.q, a.k, a.v, g, a.beta, a.initial_state, a.cu_seqlens, a.N, a.dv,
+                          a.dh0, a.B, a.T, a.H, a.HV, a.K, a.V, a.qkv_dtype, a.beta_dtype);
+    if (rc != KDA_OK) return rc;
+    if ((long long)a.B * a.T > 0 && (!a.dout || !a.dq || !a.dk || !a.dv || !a.dg || !a.dbeta))
+        return fail(KDA_ERR_NULL, "do, dq, dk, dv, dg and dbeta must be non-NULL");
+    if (!aligned16(a.dht))
+        return fail(KDA_ERR_SHAPE, "dht must be 16-byte aligned");
+    if (chunk_size != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64, got %d", chunk_size);
+    if (a.K != 64 && a.K != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "K must be 64 or 128, got %d", a.K);
+    if (a.V != 64 && a.V != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "V must be 64 or 128, got %d", a.V);
+    if (a.cu_seqlens && (long long)a.T / 64 + a.N > 0x7fffffffLL / a.HV)
+        return fail(KDA_ERR_SHAPE, "too many chunks");
+    kda::ChunkBwdLayout L;
+    kda::chunk_bwd_layout(a.B, a.T, a.HV, a.K, a.V, a.N, a.cu_seqlens != nullptr, a.qkv_dtype, &L);
+    if (a.N == 0) return KDA_OK;
+    if (!a.workspace)
+        return fail(KDA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+    if (a.workspace_bytes < L.total)
+        return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", a.workspace_bytes, L.total);
+    if ((reinterpret_cast<uintptr_t>(a.workspace) & 255) != 0)
+        return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    a.g = g;
+    a.scale = a.scale == 0.0f ? 1.0f / sqrtf((float)a.K) : a.scale;
+    hipError_t err = kda::launch_chunk_bwd(a, L);
+    if (err != hipSuccess)
+        return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* kda_last_error(void) { return g_last_error; }
+
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
+                                     int packed, int qkv_dtype) {
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || N < 0 || (K != 64 && K != 128) ||
+        (V != 64 && V != 128) || (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32))
+        return 0;
+    kda::ChunkBwdLayout L;
+    if (!kda::chunk_bwd_layout(B, T, HV, K, V, packed ? N : B, packed != 0, qkv_dtype, &L)) return 0;
+    return L.total;
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, int N, const void* dout,
+                  const float* dht, void* dq, void* dk, void* dv, float* dg, void* dbeta,
+                  float* dh0, int B, int T, int H, int HV, int K, int V, int qkv_dtype,
+                  int beta_dtype, float scale, int chunk_size, void* workspace,
+                  size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+    clear_error();
+    kda::ChunkBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
+    a.dout = dout; a.dht = dht;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype; a.scale = scale;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.dev_status = dev_status; a.stream = stream;
+    return chunk_bwd_impl(a, g, chunk_size);
+}
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 

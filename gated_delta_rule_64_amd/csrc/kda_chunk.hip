@@ -23,6 +23,7 @@
 // blocks and an exact one-sided 2^(G_i - G_j) per (i, j, channel) for the diagonal ones.
 #include <type_traits>
 
+#include "kda_chunk_common.h"
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -30,29 +31,8 @@ namespace kda {
 
 namespace {
 
-constexpr int C = 64;            // chunk rows
 constexpr int NTHREADS = 256;
 constexpr float SPREAD_LIMIT = 100.0f;
-
-// byte offset of the chunk table inside the schedule
-inline size_t sched_table_offset(int N) { return ((size_t)(3 * (size_t)N + 1) * 4 + 15) / 16 * 16; }
-
-// Chunk c as (first row in the [B*T] row space, rows). Dense mode (no offsets): chunk c
-// is chunk c % NT of sequence c / NT, computed here; packed mode: the schedule's table.
-__device__ __forceinline__ int2 chunk_pos(bool dense, int NT, int T, const int2* table, int c) {
-    if (dense) {
-        const int ci = c % NT;
-        return make_int2((c / NT) * T + ci * C, T - ci * C < C ? T - ci * C : C);
-    }
-    return table[c];
-}
-
-__device__ __forceinline__ int xcd_remap(int b, int G) {
-    // blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous run of
-    // work items so neighbouring items (same chain, same chunk) share an L2
-    if (G % 8 != 0) return b;
-    return (b % 8) * (G / 8) + b / 8;
-}
 
 // ------------------------------------------------------------------------------------
 // sched: per-slot validation, chunk offsets and the chunk table (dense mode: N = B
@@ -1241,6 +1221,11 @@ struct ScanParams {
     const int2* table;       // chunk table: (first row, rows)
     int N, T, HV, NT, NCmax;
     int dense;               // no offsets: sequence n is chunks n NT .. n NT + NT - 1, no schedule
+    // checkpoints for the backward (kernels instantiated with CKPT, which write no o),
+    // per (value head, chunk) like the records: the state at the chunk's start [K][V]
+    // and v' [64][V], fp32
+    float* h_out;
+    float* vn_out;
 };
 
 // Scan design. Each of the four waves owns a 16-row band of the chunk (for v' and o)
@@ -1320,7 +1305,7 @@ __device__ __forceinline__ void load_frags(ScanFrags<K, V, BV, TW>& F, const cha
         F.e[a] = *reinterpret_cast<const f32x4*>(eg + 16 * (wave + 4 * a) + 4 * lq);
 }
 
-template <int K, int V, int BV, typename TIn>
+template <int K, int V, int BV, typename TIn, bool CKPT>
 __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
     typedef TIn TW;
     typedef ScanFrags<K, V, BV, TW> SF;
@@ -1412,9 +1397,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
     lds_barrier();
 
     TIn* o = reinterpret_cast<TIn*>(p.o);
-    auto step = [&](SF& F) {
+    auto step = [&](SF& F, int c) {
         const long long rs = F.pos.x;
         const int len = F.pos.y;
+        if constexpr (CKPT) {
+            float* hb = p.h_out + ((size_t)hv * p.NCmax + c) * (size_t)K * V;
+#pragma unroll
+            for (int a = 0; a < NDT; ++a)
+#pragma unroll
+                for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        hb[(size_t)(16 * (wave + 4 * a) + 4 * lq + r) * V + v0 + 16 * nt + lr] = S[a][nt][r];
+        }
         // S^T fragments (hi, lo) for v' and o
         frag sb[NNT][NS][NKS];
 #pragma unroll
@@ -1437,6 +1432,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) vn[r] = F.u[nt][r] - acc[r];
             put4(Vt[0], Vt[NS - 1], 16 * nt + lr, 16 * wave + 4 * lq, vn, TV());
+            if constexpr (CKPT) {
+                float* vb = p.vn_out + ((size_t)hv * p.NCmax + c) * (size_t)C * V;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vb[(size_t)(16 * wave + 4 * lq + r) * V + v0 + 16 * nt + lr] = vn[r];
+            }
         }
         lds_barrier();
         frag vb[NNT][NS][NJS];
@@ -1473,7 +1473,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
             }
             acc += acc2;
             const int i = 16 * wave + lr;
-            if (i < len) {
+            if (!CKPT && i < len) {
                 typedef __attribute__((ext_vector_type(4))) TIn ovec;
                 ovec ov;
 #pragma unroll
@@ -1510,13 +1510,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
     // three chunks per trip so the ring buffers rotate without register copies; each
     // buffer is refilled right after its step, PREFETCH chunks ahead
     for (int c = c0; c < c1; c += 3) {
-        step(F0);
+        step(F0, c);
         load_frags<K, V, BV, TW>(F0, record(clampc(c + 3)), p, clampc(c + 3), wave, lr, lq, v0);
         if (c + 1 >= c1) break;
-        step(F1);
+        step(F1, c + 1);
         load_frags<K, V, BV, TW>(F1, record(clampc(c + 4)), p, clampc(c + 4), wave, lr, lq, v0);
         if (c + 2 >= c1) break;
-        step(F2);
+        step(F2, c + 2);
         load_frags<K, V, BV, TW>(F2, record(clampc(c + 5)), p, clampc(c + 5), wave, lr, lq, v0);
     }
 
@@ -1630,7 +1630,7 @@ __device__ __forceinline__ void load_state_g(StateFrags<K, BV>& F, const char* r
                 F.g[a][sx][jj] = *reinterpret_cast<const bf16x8*>(kgT + (size_t)sx * K * C + FG::frag(sw + 4 * a, jj, lane));
 }
 
-template <int K, int V, int BV>
+template <int K, int V, int BV, bool CKPT>
 __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams p) {
     typedef __bf16 TW;
     typedef Mma<TW> M;
@@ -1689,6 +1689,7 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
         int cur = 0;
         // one chunk; F is refilled with chunk cn as its registers die
         auto step = [&](RowFrags<K, BV>& F, int cn) {
+            const int c = cn - ROW_PREFETCH;   // the chunk F holds
             bf16x8 sb[NNT][2][NKS];
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt)
@@ -1711,6 +1712,11 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) vn[r] = F.u[nt][r] - (xa[r] + xb[r]);
                 put4(Vt[0], Vt[1], TV::idx(16 * nt + lr, 16 * b + 4 * lq), vn);
+                if constexpr (CKPT) {
+                    float* vb = p.vn_out + ((size_t)hv * p.NCmax + c) * (size_t)C * V;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) vb[(size_t)(16 * b + 4 * lq + r) * V + v0 + 16 * nt + lr] = vn[r];
+                }
             }
             // o^T, first part (independent of v'): S^T qg^T
 #pragma unroll
@@ -1742,7 +1748,7 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                     }
                 }
                 const int i = 16 * b + lr;
-                if (i < len) {
+                if (!CKPT && i < len) {
                     vec4 ov;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) ov[r] = (__bf16)(oacc[nt][r] + oacc2[nt][r]);
@@ -1795,6 +1801,16 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
         int cur = 0;
         // one chunk; F is refilled with chunk cn as its registers die
         auto step = [&](StateFrags<K, BV>& F, int cn) {
+            if constexpr (CKPT) {   // the state at the start of the chunk F holds
+                float* hb = p.h_out + ((size_t)hv * p.NCmax + (cn - STATE_PREFETCH)) * (size_t)K * V;
+#pragma unroll
+                for (int a = 0; a < NDT; ++a)
+#pragma unroll
+                    for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            hb[(size_t)(16 * (sw + 4 * a) + 4 * lq + r) * V + v0 + 16 * nt + lr] = S[a][nt][r];
+            }
             // decay first (independent of v')
 #pragma unroll
             for (int a = 0; a < NDT; ++a)
@@ -1919,6 +1935,7 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     sp.coff = coff; sp.cend = cend; sp.slot_ok = slot_ok; sp.table = table;
     sp.N = a.N; sp.T = a.T; sp.HV = a.HV; sp.NT = NT; sp.NCmax = L.NCmax;
     sp.dense = dense;
+    sp.h_out = a.h_out; sp.vn_out = a.vn_out;
     if (a.events) {
         hipError_t err = hipEventRecord(a.events[2], a.stream);
         if (err != hipSuccess) return err;
@@ -1938,14 +1955,21 @@ hipError_t launch_scan(const ChunkArgs& a, const ScanParams& sp) {
     int BV = 16;
     if (sizeof(TIn) == 2 && chains * (V / 32) >= 512) BV = 32;
     const unsigned nscan = (unsigned)(chains * (V / BV));
+    const bool ckpt = sp.h_out != nullptr;   // backward re-scan: checkpoints, no o
     if constexpr (sizeof(TIn) == 2) {
-        if (BV == 32)
-            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 32>), dim3(nscan), dim3(SCAN8_THREADS), 0, a.stream, sp);
+        if (ckpt)
+            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 16, true>), dim3((unsigned)(chains * (V / 16))),
+                               dim3(SCAN8_THREADS), 0, a.stream, sp);
+        else if (BV == 32)
+            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 32, false>), dim3(nscan), dim3(SCAN8_THREADS), 0, a.stream, sp);
         else
-            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 16>), dim3(nscan), dim3(SCAN8_THREADS), 0, a.stream, sp);
+            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 16, false>), dim3(nscan), dim3(SCAN8_THREADS), 0, a.stream, sp);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((scan_kernel<K, V, 16, TIn>), dim3(nscan), dim3(NTHREADS), 0, a.stream, sp);
+    if (ckpt)
+        hipLaunchKernelGGL((scan_kernel<K, V, 16, TIn, true>), dim3(nscan), dim3(NTHREADS), 0, a.stream, sp);
+    else
+        hipLaunchKernelGGL((scan_kernel<K, V, 16, TIn, false>), dim3(nscan), dim3(NTHREADS), 0, a.stream, sp);
     return hipGetLastError();
 }
 

@@ -1,0 +1,771 @@
+// Chunked KDA backward for gfx950: the gradients of the chunked forward with respect to
+// q, k, v, the per-token log2 decay g, beta and the initial state.
+//
+// The method is the backward of "kernel-fun 0.2.0.dev1 sdist", ALGORITHM.md, section
+// Backward: the forward's Stage 1+2 is recomputed (the forward's own kernel writes the
+// per-chunk records), the forward scan runs again and checkpoints the state at every
+// chunk start and v' (its "re-scan"), a reverse scan carries the state gradient and
+// gives dv' per chunk (its "dhu" stage), and per-chunk kernels turn those into the
+// input gradients: the products with the state checkpoints (its wy_dqkg h/dh
+// consumers), the backward of the WY inverse, and the intra-chunk pair terms with a
+// reverse cumsum of the gate gradient folded in (its intra stage and dg cumsum). GVA
+// gradients of q and k are summed over each q/k head's value heads at the end.
+//
+// Per chunk (rows r, s of the chunk, Gamma the chunk-local cumsum of g, G its last
+// row, S the state at the chunk start, dS the gradient at the chunk end, do the output
+// gradient), with the forward's qg = scale q 2^Gamma, kd = k 2^Gamma,
+// kg = k 2^(G - Gamma), Aqk[r,s] = scale sum_d q_r k_s 2^(Gamma_r - Gamma_s) (s <= r),
+// M[r,s] = sum_d k_r k_s 2^(Gamma_r - Gamma_s) (s < r), T = (I + diag(beta) M)^-1,
+// u = T diag(beta) v, w = T diag(beta) kd, v' = u - w S:
+//   dv'  = Aqk^T do + kg dS                 dS_prev = 2^G dS + qg^T do - w^T dv'
+//   dqg  = do S^T   dw = -dv' S^T   dkg = v' dS^T   dAqk = do v'^T (s <= r)
+//   dG  += ln2 2^G sum_v dS S
+//   Gu = T^T dv', Gw = T^T dw: dv = beta Gu, dkd = beta Gw,
+//   dbeta = rowsum(Gu v) + rowsum(Gw kd) + rowsum(dL M),
+//   dT = dv' (beta v)^T + dw (beta kd)^T, dL = -(T^T dT T^T) strictly lower, dM = beta dL
+//   and the pair terms of Aqk and M with one one-sided 2^(Gamma_r - Gamma_s) <= 1 each.
+// All of it in fp32 (fp32 matrix cores for the dense products).
+#include "kda_chunk_common.h"
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int BT = 256;                       // threads per block
+constexpr float LN2F = 0.69314718055994531f;
+
+// fp32 matrix-core tile product over contraction [0, nk): C[16x16] += sum_k A(i, k) B(j, k).
+// Lane (lq, lr) supplies A(lr, k + lq) and B(lr, k + lq) and holds C[4 lq + r][lr] in
+// register r (v_mfma_f32_16x16x4_f32).
+template <class FA, class FB>
+__device__ __forceinline__ f32x4 mma_f32(f32x4 acc, const FA& a, const FB& b, int nk, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+    for (int k = 0; k < nk; k += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(r, k + kq), b(r, k + kq), acc, 0, 0, 0);
+    return acc;
+}
+
+// Sum over the 16 lanes of a DPP row (the lanes that hold one row of a tile product).
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
+// An R x KC record tile (fragment order; on the bf16 path the rounding residual tile
+// follows at + R*KC when `split`) copied into fp32 LDS: dst[row * ld + col].
+template <typename TW, int R, int KC>
+__device__ __forceinline__ void stage_record(const TW* t, bool split, float* dst, int ld, int tid) {
+    typedef Mma<TW> M;
+    constexpr int NS = KC / M::KS;
+    for (int e = tid; e < R * KC; e += BT) {
+        const int x = e % M::KPL;
+        const int l = (e / M::KPL) % 64;
+        const int blk = e / (M::KPL * 64);
+        const int row = 16 * (blk / NS) + (l & 15);
+        const int col = (blk % NS) * M::KS + (l >> 4) * M::KPL + x;
+        float v = to_f32(t[e]);
+        if (split) v += to_f32(t[e + R * KC]);
+        dst[row * ld + col] = v;
+    }
+}
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    const void* dout;
+    const float* dht;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dg;
+    void* dbeta;
+    float* dh0;
+    // schedule (packed mode) or dense positions
+    const int32_t* nchunks;
+    const int2* table;
+    const int32_t* coff;
+    const int32_t* cend;
+    const int32_t* slot_ok;
+    int dense, NT, T, N, H, HV, NCmax;
+    float scale;
+    // forward records
+    const char* rec;
+    size_t rec_bytes, off_w, off_u, off_qg, off_kgT, off_aqk, off_eg;
+    // checkpoints and intermediates, per (value head, chunk): index hv * NCmax + c
+    const float* h;      // [K][V] state at the chunk start
+    const float* vn;     // [64][V] v'
+    float* dh;           // [K][V] gradient at the chunk end
+    float* dvn;          // [64][V] dv'
+    float* gs;           // dqg, dw, dkg [64][K] each, dAqk [64][64], dG [K]
+    float* wy;           // dkd [64][K], dM [64][64]
+    float* dq_hv;        // [B*T][HV][K]
+    float* dk_hv;
+};
+
+template <int K>
+struct GsLayout {
+    static constexpr int DQG = 0, DW = C * K, DKG = 2 * C * K, DA = 3 * C * K, DG = 3 * C * K + C * C;
+    static constexpr int FLOATS = 3 * C * K + C * C + K;
+};
+template <int K>
+struct WyLayout {
+    static constexpr int DKD = 0, DM = C * K;
+    static constexpr int FLOATS = C * K + C * C;
+};
+
+// ------------------------------------------------------------------------------------
+// reverse scan: dS (the state gradient) walks each chain's chunks backwards; per chunk
+// it stores dS (the gradient at the chunk end) and dv'. One block per (chain, 16-column
+// slice of V); wave w owns rows 16w.. of dv' and state bands w, w + 4.
+// ------------------------------------------------------------------------------------
+template <int K, int V, typename TW, typename TIn>
+__global__ __launch_bounds__(BT, 1) void bwd_dscan_kernel(BwdParams p) {
+    constexpr int BV = 16, NVT = V / BV, LB = BV + 1, LA = C + 1, LK = K + 1, NDT = K / 64;
+    constexpr bool SPLIT = sizeof(TW) == 2;
+    constexpr int P1 = C * LA + K * LA, P2 = 2 * C * LK;
+    __shared__ float un[P1 > P2 ? P1 : P2];
+    __shared__ float doL[C * LB];
+    __shared__ float dvL[C * LB];
+    __shared__ float dSL[K * LB];
+    __shared__ float eGL[K];
+    float* aqkL = un;              // Aqk[r][s]
+    float* kgL = un + C * LA;      // kg^T[d][s]
+    float* qgL = un;               // qg[r][d]
+    float* wL = un + C * LK;       // w[r][d]
+
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = p.N * p.HV * NVT;
+    const int item = xcd_remap(blockIdx.x, G);
+    const int vt = item % NVT, chain = item / NVT;
+    const int hv = chain % p.HV, n = chain / p.HV;
+    const int v0 = vt * BV;
+    if (!p.dense && !p.slot_ok[n]) return;
+    const int c0 = p.dense ? n * p.NT : p.coff[n];
+    const int c1 = p.dense ? c0 + p.NT : p.cend[n];
+    const size_t sbase = ((size_t)n * p.HV + hv) * (size_t)K * V;
+    const TIn* dout = reinterpret_cast<const TIn*>(p.dout);
+
+    f32x4 dS[NDT];
+#pragma unroll
+    for (int a = 0; a < NDT; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d = 16 * (wave + 4 * a) + 4 * lq + r;
+            dS[a][r] = p.dht ? p.dht[sbase + (size_t)d * V + v0 + lr] : 0.f;
+            dSL[d * LB + lr] = dS[a][r];
+        }
+    for (int c = c1 - 1; c >= c0; --c) {
+        const int2 pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
+        const char* rec = p.rec + ((size_t)hv * p.NCmax + c) * p.rec_bytes;
+        const size_t ci = (size_t)hv * p.NCmax + c;
+        // the gradient at the chunk end
+        float* dhb = p.dh + ci * (size_t)K * V;
+#pragma unroll
+        for (int a = 0; a < NDT; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dhb[(size_t)(16 * (wave + 4 * a) + 4 * lq + r) * V + v0 + lr] = dS[a][r];
+        stage_record<TW, C, C>(reinterpret_cast<const TW*>(rec + p.off_aqk), SPLIT, aqkL, LA, tid);
+        stage_record<TW, K, C>(reinterpret_cast<const TW*>(rec + p.off_kgT), SPLIT, kgL, LA, tid);
+        for (int e = tid; e < C * BV; e += BT) {
+            const int r = e / BV, vv = e % BV;
+            doL[r * LB + vv] = r < pos.y ? to_f32(dout[((size_t)(pos.x + r) * p.HV + hv) * V + v0 + vv]) : 0.f;
+        }
+        for (int e = tid; e < K; e += BT) eGL[e] = reinterpret_cast<const float*>(rec + p.off_eg)[e];
+        __syncthreads();
+        // dv' = Aqk^T do + kg dS, rows 16 wave ..
+        {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int s0 = 16 * wave;
+            acc = mma_f32(acc, [&](int i, int k) { return aqkL[k * LA + s0 + i]; },
+                          [&](int j, int k) { return doL[k * LB + j]; }, C, lane);
+            acc = mma_f32(acc, [&](int i, int k) { return kgL[k * LA + s0 + i]; },
+                          [&](int j, int k) { return dSL[k * LB + j]; }, K, lane);
+            float* dvb = p.dvn + ci * (size_t)C * V;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = s0 + 4 * lq + r;
+                dvL[s * LB + lr] = acc[r];
+                dvb[(size_t)s * V + v0 + lr] = acc[r];
+            }
+        }
+        __syncthreads();
+        stage_record<TW, C, K>(reinterpret_cast<const TW*>(rec + p.off_qg), SPLIT, qgL, LK, tid);
+        stage_record<TW, C, K>(reinterpret_cast<const TW*>(rec + p.off_w), false, wL, LK, tid);
+        __syncthreads();
+        // dS <- 2^G dS + qg^T do - w^T dv'
+#pragma unroll
+        for (int a = 0; a < NDT; ++a) {
+            const int d0 = 16 * (wave + 4 * a);
+            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = {0.f, 0.f, 0.f, 0.f};
+            aq = mma_f32(aq, [&](int i, int k) { return qgL[k * LK + d0 + i]; },
+                         [&](int j, int k) { return doL[k * LB + j]; }, C, lane);
+            aw = mma_f32(aw, [&](int i, int k) { return wL[k * LK + d0 + i]; },
+                         [&](int j, int k) { return dvL[k * LB + j]; }, C, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = d0 + 4 * lq + r;
+                dS[a][r] = eGL[d] * dS[a][r] + aq[r] - aw[r];
+                dSL[d * LB + lr] = dS[a][r];
+            }
+        }
+        __syncthreads();
+    }
+    if (p.dh0) {
+#pragma unroll
+        for (int a = 0; a < NDT; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                p.dh0[sbase + (size_t)(16 * (wave + 4 * a) + 4 * lq + r) * V + v0 + lr] = dS[a][r];
+    }
+}
+
+// the chunk this block handles, or false when it is past the packed schedule's end
+__device__ __forceinline__ bool bwd_chunk(const BwdParams& p, int& c, int& hv, int2& pos) {
+    const int G = p.NCmax * p.HV;
+    const int item = xcd_remap(blockIdx.x, G);
+    hv = item % p.HV;
+    c = item / p.HV;
+    if (!p.dense && c >= p.nchunks[0]) return false;
+    pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
+    return true;
+}
+
+// ------------------------------------------------------------------------------------
+// products with the state checkpoints, per (chunk, value head): dqg = do S^T,
+// dw = -dv' S^T, dkg = v' dS^T, dAqk = do v'^T (s <= r), dG = ln2 2^G rowsum(dS S).
+// Contraction over V in slices of 32 staged in LDS; wave w owns row band w.
+// ------------------------------------------------------------------------------------
+template <int K, int V, typename TIn>
+__global__ __launch_bounds__(BT, 2) void bwd_state_kernel(BwdParams p) {
+    constexpr int VC = 32, LV = VC + 1, NKT = K / 16;
+    typedef GsLayout<K> GL;
+    __shared__ float hL[K * LV];
+    __shared__ float dhL[K * LV];
+    __shared__ float doL[C * LV];
+    __shared__ float vnL[C * LV];
+    __shared__ float dvL[C * LV];
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int c, hv;
+    int2 pos;
+    if (!bwd_chunk(p, c, hv, pos)) return;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const float* hC = p.h + ci * (size_t)K * V;
+    const float* dhC = p.dh + ci * (size_t)K * V;
+    const float* vnC = p.vn + ci * (size_t)C * V;
+    const float* dvC = p.dvn + ci * (size_t)C * V;
+    const TIn* dout = reinterpret_cast<const TIn*>(p.dout);
+    const int r0 = 16 * wave;
+
+    f32x4 aq[NKT], aw[NKT], ak[NKT], aA[4];
+#pragma unroll
+    for (int j = 0; j < NKT; ++j) { aq[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aw[j] = aq[j]; ak[j] = aq[j]; }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) aA[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dgacc = 0.f;   // thread d < K: sum_v dS[d][v] S[d][v]
+    for (int vb = 0; vb < V; vb += VC) {
+        for (int e = tid; e < K * VC; e += BT) {
+            const int d = e / VC, vv = e % VC;
+            hL[d * LV + vv] = hC[(size_t)d * V + vb + vv];
+            dhL[d * LV + vv] = dhC[(size_t)d * V + vb + vv];
+        }
+        for (int e = tid; e < C * VC; e += BT) {
+            const int r = e / VC, vv = e % VC;
+            doL[r * LV + vv] = r < pos.y ? to_f32(dout[((size_t)(pos.x + r) * p.HV + hv) * V + vb + vv]) : 0.f;
+            vnL[r * LV + vv] = vnC[(size_t)r * V + vb + vv];
+            dvL[r * LV + vv] = dvC[(size_t)r * V + vb + vv];
+        }
+        __syncthreads();
+        if (tid < K)
+            for (int vv = 0; vv < VC; ++vv) dgacc = fmaf(dhL[tid * LV + vv], hL[tid * LV + vv], dgacc);
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+            auto bh = [&](int jj, int k) { return hL[(16 * j + jj) * LV + k]; };
+            auto bdh = [&](int jj, int k) { return dhL[(16 * j + jj) * LV + k]; };
+            aq[j] = mma_f32(aq[j], [&](int i, int k) { return doL[(r0 + i) * LV + k]; }, bh, VC, lane);
+            aw[j] = mma_f32(aw[j], [&](int i, int k) { return dvL[(r0 + i) * LV + k]; }, bh, VC, lane);
+            ak[j] = mma_f32(ak[j], [&](int i, int k) { return vnL[(r0 + i) * LV + k]; }, bdh, VC, lane);
+        }
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+            if (J <= wave)
+                aA[J] = mma_f32(aA[J], [&](int i, int k) { return doL[(r0 + i) * LV + k]; },
+                                [&](int jj, int k) { return vnL[(16 * J + jj) * LV + k]; }, VC, lane);
+        __syncthreads();
+    }
+    float* out = p.gs + ci * (size_t)GL::FLOATS;
+#pragma unroll
+    for (int j = 0; j < NKT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = r0 + 4 * lq + r, d = 16 * j + lr;
+            out[GL::DQG + row * K + d] = aq[j][r];
+            out[GL::DW + row * K + d] = -aw[j][r];
+            out[GL::DKG + row * K + d] = ak[j][r];
+        }
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = r0 + 4 * lq + r, s = 16 * J + lr;
+            out[GL::DA + row * C + s] = (J <= wave && s <= row) ? aA[J][r] : 0.f;
+        }
+    if (tid < K) {
+        const float eg = reinterpret_cast<const float*>(p.rec + ci * p.rec_bytes + p.off_eg)[tid];
+        out[GL::DG + tid] = LN2F * eg * dgacc;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// backward of the WY inverse, per (chunk, value head): recomputes M and T from k, g,
+// beta; writes dv and dbeta (final) and dkd, dM for the pair kernel.
+// ------------------------------------------------------------------------------------
+template <int K, int V, typename TIn, typename TB>
+__global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
+    constexpr int LA = C + 1, LK = K + 1, LX = (K > V ? K : V) + 1, LY = (V > C ? V : C) + 1;
+    typedef GsLayout<K> GL;
+    typedef WyLayout<K> WL;
+    __shared__ float kL[C * LK];     // k, then kd = k 2^Gamma
+    __shared__ float XL[C * LX];     // Gamma, then dv', then dw
+    __shared__ float YL[C * LY];     // v, then T^T dT
+    __shared__ float ML[C * LA];
+    __shared__ float TL[C * LA];
+    __shared__ float dTL[C * LA];
+    __shared__ float bL[C];
+    __shared__ float dbL[C];
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int c, hv;
+    int2 pos;
+    if (!bwd_chunk(p, c, hv, pos)) return;
+    const int h = hv / (p.HV / p.H);
+    const int len = pos.y;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const TIn* kin = reinterpret_cast<const TIn*>(p.k);
+    const TIn* vin = reinterpret_cast<const TIn*>(p.v);
+    const TB* bin = reinterpret_cast<const TB*>(p.beta);
+    const int r0 = 16 * wave;
+
+    // ---- loads and the chunk-local cumsum of g ----
+    for (int e = tid; e < C * K; e += BT) {
+        const int r = e / K, d = e % K;
+        const bool live = r < len;
+        const size_t row = (size_t)(pos.x + r);
+        kL[r * LK + d] = live ? to_f32(kin[(row * p.H + h) * K + d]) : 0.f;
+        XL[r * LX + d] = live ? p.g[(row * p.HV + hv) * K + d] : 0.f;
+    }
+    if (tid < C) {
+        bL[tid] = tid < len ? to_f32(bin[(size_t)(pos.x + tid) * p.HV + hv]) : 0.f;
+        dbL[tid] = 0.f;
+    }
+    __syncthreads();
+    if (tid < K) {
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) { acc += XL[r * LX + tid]; XL[r * LX + tid] = acc; }
+    }
+    __syncthreads();
+    // ---- M[r][s] = sum_d k_r k_s 2^(Gamma_r - Gamma_s), s < r: thread (r, s = sg + 4j) ----
+    {
+        const int r = tid >> 2, sg = tid & 3;
+        float acc[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+        for (int d = 0; d < K; ++d) {
+            const float kr = kL[r * LK + d], gr = XL[r * LX + d];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int s = sg + 4 * j;
+                if (s < r) acc[j] = fmaf(kr * kL[s * LK + d], exp2_fast(gr - XL[s * LX + d]), acc[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int s = sg + 4 * j;
+            ML[r * LA + s] = s < r ? acc[j] : 0.f;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < C * K; e += BT) {
+        const int r = e / K, d = e % K;
+        kL[r * LK + d] *= exp2_fast(XL[r * LX + d]);
+    }
+    // ---- T = (I + diag(beta) M)^-1 by columns (unit lower triangular) ----
+    if (tid < C) {
+        const int j = tid;
+        for (int r = 0; r < C; ++r) TL[r * LA + j] = r == j ? 1.f : 0.f;
+        for (int r = j + 1; r < C; ++r) {
+            float acc = 0.f;
+            for (int s = j; s < r; ++s) acc = fmaf(ML[r * LA + s], TL[s * LA + j], acc);
+            TL[r * LA + j] = -bL[r] * acc;
+        }
+    }
+    __syncthreads();
+    // ---- value side: dv = beta T^T dv', dbeta += rowsum((T^T dv') v), dT = dv' (beta v)^T ----
+    const float* dvC = p.dvn + ci * (size_t)C * V;
+    for (int e = tid; e < C * V; e += BT) {
+        const int r = e / V, vv = e % V;
+        XL[r * LX + vv] = dvC[(size_t)r * V + vv];
+        YL[r * LY + vv] = r < len ? to_f32(vin[((size_t)(pos.x + r) * p.HV + hv) * V + vv]) : 0.f;
+    }
+    __syncthreads();
+    TIn* dvout = reinterpret_cast<TIn*>(p.dv);
+    {
+        float db[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < V / 16; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_f32(acc, [&](int i, int k) { return TL[k * LA + r0 + i]; },
+                          [&](int j, int k) { return XL[k * LX + 16 * nt + j]; }, C, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = r0 + 4 * lq + r, vv = 16 * nt + lr;
+                db[r] = fmaf(acc[r], YL[s * LY + vv], db[r]);
+                if (s < len) dvout[((size_t)(pos.x + s) * p.HV + hv) * V + vv] = from_f32<TIn>(bL[s] * acc[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = sum16(db[r]);
+            if (lr == 0) dbL[r0 + 4 * lq + r] += x;
+        }
+    }
+    f32x4 dT[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        dT[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (J <= wave)
+            dT[J] = mma_f32(dT[J], [&](int i, int k) { return XL[(r0 + i) * LX + k]; },
+                            [&](int j, int k) { return bL[16 * J + j] * YL[(16 * J + j) * LY + k]; }, V, lane);
+    }
+    __syncthreads();
+    // ---- key side: dkd = beta T^T dw, dbeta += rowsum((T^T dw) kd), dT += dw (beta kd)^T ----
+    const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
+    for (int e = tid; e < C * K; e += BT) {
+        const int r = e / K, d = e % K;
+        XL[r * LX + d] = gsC[GL::DW + r * K + d];
+    }
+    __syncthreads();
+    float* wyC = p.wy + ci * (size_t)WL::FLOATS;
+    {
+        float db[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < K / 16; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_f32(acc, [&](int i, int k) { return TL[k * LA + r0 + i]; },
+                          [&](int j, int k) { return XL[k * LX + 16 * nt + j]; }, C, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = r0 + 4 * lq + r, d = 16 * nt + lr;
+                db[r] = fmaf(acc[r], kL[s * LK + d], db[r]);
+                wyC[WL::DKD + s * K + d] = bL[s] * acc[r];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = sum16(db[r]);
+            if (lr == 0) dbL[r0 + 4 * lq + r] += x;
+        }
+    }
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        if (J <= wave)
+            dT[J] = mma_f32(dT[J], [&](int i, int k) { return XL[(r0 + i) * LX + k]; },
+                            [&](int j, int k) { return bL[16 * J + j] * kL[(16 * J + j) * LK + k]; }, K, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = r0 + 4 * lq + r, s = 16 * J + lr;
+            dTL[row * LA + s] = (J <= wave && s < row) ? dT[J][r] : 0.f;
+        }
+    }
+    __syncthreads();
+    // ---- X = T^T dT (all tiles), then dL = -(X T^T) strictly lower ----
+    for (int J = 0; J < 4; ++J) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        x = mma_f32(x, [&](int i, int k) { return TL[k * LA + r0 + i]; },
+                    [&](int j, int k) { return dTL[k * LA + 16 * J + j]; }, C, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) YL[(r0 + 4 * lq + r) * LY + 16 * J + lr] = x[r];
+    }
+    __syncthreads();
+    {
+        float db[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (J <= wave)
+                x = mma_f32(x, [&](int i, int k) { return YL[(r0 + i) * LY + k]; },
+                            [&](int j, int k) { return TL[(16 * J + j) * LA + k]; }, C, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = r0 + 4 * lq + r, s = 16 * J + lr;
+                const float dl = (J <= wave && s < row) ? -x[r] : 0.f;
+                db[r] = fmaf(dl, ML[row * LA + s], db[r]);
+                wyC[WL::DM + row * C + s] = bL[row] * dl;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = sum16(db[r]);
+            if (lr == 0) dbL[r0 + 4 * lq + r] += x;
+        }
+    }
+    __syncthreads();
+    if (tid < len) reinterpret_cast<TB*>(p.dbeta)[(size_t)(pos.x + tid) * p.HV + hv] = from_f32<TB>(dbL[tid]);
+}
+
+// ------------------------------------------------------------------------------------
+// pair terms and the elementwise ones, per (chunk, value head): dq, dk (per value head,
+// summed later) and dg (the chunk-local reverse cumsum of dGamma). Thread (r, d = dg4 +
+// 4 j) sweeps the row side (s <= r) and the column side (r' >= r) of row r; every
+// factor is one one-sided 2^(Gamma_r - Gamma_s) <= 1.
+// ------------------------------------------------------------------------------------
+template <int K, int V, typename TIn>
+__global__ __launch_bounds__(BT, 1) void bwd_pair_kernel(BwdParams p) {
+    constexpr int LA = C + 1, LK = K + 1, NJ = K / 4;
+    typedef GsLayout<K> GL;
+    typedef WyLayout<K> WL;
+    __shared__ float qL[C * LK];     // q, then dGamma
+    __shared__ float kL[C * LK];
+    __shared__ float GmL[C * LK];    // Gamma
+    __shared__ float dAL[C * LA];    // scale dAqk (s <= r)
+    __shared__ float dML[C * LA];    // dM (s < r)
+    __shared__ float dGL[K];
+    const int tid = threadIdx.x;
+    int c, hv;
+    int2 pos;
+    if (!bwd_chunk(p, c, hv, pos)) return;
+    const int h = hv / (p.HV / p.H);
+    const int len = pos.y;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const TIn* qin = reinterpret_cast<const TIn*>(p.q);
+    const TIn* kin = reinterpret_cast<const TIn*>(p.k);
+    const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
+    const float* wyC = p.wy + ci * (size_t)WL::FLOATS;
+
+    for (int e = tid; e < C * K; e += BT) {
+        const int r = e / K, d = e % K;
+        const bool live = r < len;
+        const size_t row = (size_t)(pos.x + r);
+        qL[r * LK + d] = live ? to_f32(qin[(row * p.H + h) * K + d]) : 0.f;
+        kL[r * LK + d] = live ? to_f32(kin[(row * p.H + h) * K + d]) : 0.f;
+        GmL[r * LK + d] = live ? p.g[(row * p.HV + hv) * K + d] : 0.f;
+    }
+    for (int e = tid; e < C * C; e += BT) {
+        const int r = e / C, s = e % C;
+        dAL[r * LA + s] = p.scale * gsC[GL::DA + e];
+        dML[r * LA + s] = wyC[WL::DM + e];
+    }
+    if (tid < K) dGL[tid] = gsC[GL::DG + tid];
+    __syncthreads();
+    if (tid < K) {
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) { acc += GmL[r * LK + tid]; GmL[r * LK + tid] = acc; }
+    }
+    __syncthreads();
+
+    const int r = tid >> 2, dg4 = tid & 3;
+    float gr[NJ], dqi[NJ], dkr[NJ], dkc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        gr[j] = GmL[r * LK + dg4 + 4 * j];
+        dqi[j] = 0.f; dkr[j] = 0.f; dkc[j] = 0.f;
+    }
+    // row side: s <= r
+    for (int s = 0; s <= r; ++s) {
+        const float a = dAL[r * LA + s], m = dML[r * LA + s];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int d = dg4 + 4 * j;
+            const float ek = kL[s * LK + d] * exp2_fast(gr[j] - GmL[s * LK + d]);
+            dqi[j] = fmaf(a, ek, dqi[j]);
+            dkr[j] = fmaf(m, ek, dkr[j]);
+        }
+    }
+    // column side: r2 >= r
+    for (int r2 = r; r2 < C; ++r2) {
+        const float a = dAL[r2 * LA + r], m = dML[r2 * LA + r];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int d = dg4 + 4 * j;
+            const float e = exp2_fast(GmL[r2 * LK + d] - gr[j]);
+            dkc[j] = fmaf(fmaf(a, qL[r2 * LK + d], m * kL[r2 * LK + d]), e, dkc[j]);
+        }
+    }
+    // elementwise terms of qg, kd, kg; dGamma
+    float qv[NJ], kv[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        qv[j] = qL[r * LK + dg4 + 4 * j];
+        kv[j] = kL[r * LK + dg4 + 4 * j];
+    }
+    __syncthreads();   // qL becomes dGamma
+    const bool live = r < len;
+    const size_t row = (size_t)(pos.x + r);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int d = dg4 + 4 * j;
+        const float Gd = GmL[(C - 1) * LK + d];
+        const float e1 = exp2_fast(gr[j]), e2 = exp2_fast(Gd - gr[j]);
+        const float dqg = gsC[GL::DQG + r * K + d];
+        const float dkg = gsC[GL::DKG + r * K + d];
+        const float dkd = wyC[WL::DKD + r * K + d];
+        const float dq = fmaf(p.scale * e1, dqg, dqi[j]);
+        const float dk = dkr[j] + dkc[j] + e1 * dkd + e2 * dkg;
+        const float kge = kv[j] * e2 * dkg;
+        const float dgam = LN2F * (qv[j] * (dqi[j] + p.scale * e1 * dqg) + kv[j] * (dkr[j] - dkc[j] + e1 * dkd) - kge);
+        qL[r * LK + d] = dgam;
+        if (live) atomicAdd(&dGL[d], LN2F * kge);
+        if (live) {
+            p.dq_hv[(row * p.HV + hv) * K + d] = dq;
+            p.dk_hv[(row * p.HV + hv) * K + d] = dk;
+        }
+    }
+    __syncthreads();
+    // dg = reverse cumsum of dGamma over the chunk's rows; dG joins at the last row
+    if (tid < K && len > 0) {
+        float acc = dGL[tid];
+        for (int rr = len - 1; rr >= 0; --rr) {
+            acc += qL[rr * LK + tid];
+            p.dg[((size_t)(pos.x + rr) * p.HV + hv) * K + tid] = acc;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// GVA: dq, dk of a q/k head are the sums over its value heads; per (chunk, q/k head)
+// ------------------------------------------------------------------------------------
+template <int K, typename TIn>
+__global__ __launch_bounds__(BT) void bwd_reduce_kernel(BwdParams p) {
+    const int G = p.NCmax * p.H;
+    const int item = blockIdx.x;
+    if (item >= G) return;
+    const int h = item % p.H, c = item / p.H;
+    if (!p.dense && c >= p.nchunks[0]) return;
+    const int2 pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
+    const int grp = p.HV / p.H;
+    TIn* dq = reinterpret_cast<TIn*>(p.dq);
+    TIn* dk = reinterpret_cast<TIn*>(p.dk);
+    for (int e = threadIdx.x; e < pos.y * K; e += BT) {
+        const int r = e / K, d = e % K;
+        const size_t row = (size_t)(pos.x + r);
+        float sq = 0.f, sk = 0.f;
+        for (int j = 0; j < grp; ++j) {
+            sq += p.dq_hv[(row * p.HV + h * grp + j) * K + d];
+            sk += p.dk_hv[(row * p.HV + h * grp + j) * K + d];
+        }
+        dq[(row * p.H + h) * K + d] = from_f32<TIn>(sq);
+        dk[(row * p.H + h) * K + d] = from_f32<TIn>(sk);
+    }
+}
+
+template <int K, int V, typename TIn, typename TB>
+hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
+    char* ws = reinterpret_cast<char*>(a.workspace);
+    const bool dense = a.cu_seqlens == nullptr;
+    const int NT = (a.T + C - 1) / C;
+    // forward recompute: schedule (packed), records, and the re-scan with checkpoints
+    ChunkArgs f;
+    f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
+    f.in = InputSpec{GATE_LOG2, nullptr, nullptr, nullptr, 0, 0.f, 0, 0, 0.f};
+    f.initial_state = a.initial_state; f.cu_seqlens = a.cu_seqlens;
+    f.o = nullptr; f.final_state = nullptr;
+    f.N = a.N; f.B = a.B; f.T = a.T; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
+    f.qkv_dtype = a.qkv_dtype; f.beta_dtype = a.beta_dtype; f.scale = a.scale;
+    f.workspace = a.workspace; f.workspace_bytes = a.workspace_bytes;
+    f.dev_status = a.dev_status; f.stream = a.stream; f.events = nullptr;
+    f.h_out = reinterpret_cast<float*>(ws + L.off_h);
+    f.vn_out = reinterpret_cast<float*>(ws + L.off_vn);
+    hipError_t err = launch_chunk(f, L.fwd);
+    if (err != hipSuccess) return err;
+
+    BwdParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.dout = a.dout; p.dht = a.dht;
+    p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
+    if (!dense) {
+        const int32_t* coff = reinterpret_cast<const int32_t*>(ws);
+        p.coff = coff; p.cend = coff + a.N; p.slot_ok = coff + 2 * a.N; p.nchunks = coff + 3 * a.N;
+        p.table = reinterpret_cast<const int2*>(ws + sched_table_offset(a.N));
+    } else {
+        p.coff = p.cend = p.slot_ok = p.nchunks = nullptr;
+        p.table = nullptr;
+    }
+    p.dense = dense; p.NT = NT; p.T = a.T; p.N = a.N; p.H = a.H; p.HV = a.HV; p.NCmax = L.fwd.NCmax;
+    p.scale = a.scale;
+    p.rec = ws + L.fwd.sched_bytes;
+    p.rec_bytes = L.fwd.rec_bytes; p.off_w = L.fwd.off_w; p.off_u = L.fwd.off_u; p.off_qg = L.fwd.off_qg;
+    p.off_kgT = L.fwd.off_kgT; p.off_aqk = L.fwd.off_aqk; p.off_eg = L.fwd.off_eg;
+    p.h = reinterpret_cast<const float*>(ws + L.off_h);
+    p.vn = reinterpret_cast<const float*>(ws + L.off_vn);
+    p.dh = reinterpret_cast<float*>(ws + L.off_dh);
+    p.dvn = reinterpret_cast<float*>(ws + L.off_dvn);
+    p.gs = reinterpret_cast<float*>(ws + L.off_gs);
+    p.wy = reinterpret_cast<float*>(ws + L.off_wy);
+    p.dq_hv = reinterpret_cast<float*>(ws + L.off_dq);
+    p.dk_hv = reinterpret_cast<float*>(ws + L.off_dk);
+
+    const long long chains = (long long)a.N * a.HV;
+    const long long nchunk_items = (long long)L.fwd.NCmax * a.HV;
+    if (chains > 0) {
+        // the records are in the input type (bf16 hi/lo pairs, or fp32)
+        hipLaunchKernelGGL((bwd_dscan_kernel<K, V, TIn, TIn>), dim3((unsigned)(chains * (V / 16))),
+                           dim3(BT), 0, a.stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (nchunk_items > 0) {
+        hipLaunchKernelGGL((bwd_state_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((bwd_pair_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((bwd_reduce_kernel<K, TIn>), dim3((unsigned)((long long)L.fwd.NCmax * a.H)), dim3(BT), 0,
+                           a.stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+template <typename TIn, typename TB>
+hipError_t launch_bwd_t(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
+    if (a.K == 128) return a.V == 128 ? launch_bwd_kv<128, 128, TIn, TB>(a, L) : launch_bwd_kv<128, 64, TIn, TB>(a, L);
+    return a.V == 128 ? launch_bwd_kv<64, 128, TIn, TB>(a, L) : launch_bwd_kv<64, 64, TIn, TB>(a, L);
+}
+
+size_t align256b(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+bool chunk_bwd_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qkv_dtype,
+                      ChunkBwdLayout* out) {
+    ChunkBwdLayout L{};
+    if (!chunk_layout(B, T, HV, K, V, N, packed, qkv_dtype, &L.fwd)) return false;
+    const size_t items = (size_t)HV * L.fwd.NCmax;
+    const size_t rows = (size_t)B * T;
+    size_t off = align256b(L.fwd.total);
+    L.off_h = off;   off = align256b(off + items * K * V * 4);
+    L.off_vn = off;  off = align256b(off + items * C * V * 4);
+    L.off_dh = off;  off = align256b(off + items * K * V * 4);
+    L.off_dvn = off; off = align256b(off + items * C * V * 4);
+    L.off_gs = off;  off = align256b(off + items * (size_t)(3 * C * K + C * C + K) * 4);
+    L.off_wy = off;  off = align256b(off + items * (size_t)(C * K + C * C) * 4);
+    L.off_dq = off;  off = align256b(off + rows * HV * K * 4);
+    L.off_dk = off;  off = align256b(off + rows * HV * K * 4);
+    L.total = off;
+    *out = L;
+    return true;
+}
+
+hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
+    if (a.qkv_dtype == KDA_BF16)
+        return a.beta_dtype == KDA_BF16 ? launch_bwd_t<__bf16, __bf16>(a, L) : launch_bwd_t<__bf16, float>(a, L);
+    return a.beta_dtype == KDA_BF16 ? launch_bwd_t<float, __bf16>(a, L) : launch_bwd_t<float, float>(a, L);
+}
+
+}  // namespace kda

@@ -65,6 +65,10 @@ struct ChunkArgs {
     int32_t* dev_status;
     hipStream_t stream;
     hipEvent_t* events;   // optional: 4 events recorded around the kernels
+    // optional checkpoints for the backward (o may then be null): the state at each
+    // chunk's start [HV][NCmax][K][V] and v' [HV][NCmax][64][V], fp32
+    float* h_out = nullptr;
+    float* vn_out = nullptr;
 };
 
 // Workspace layout of the chunked forward (all offsets 256-byte aligned):
@@ -92,6 +96,48 @@ struct ChunkLayout {
 
 bool chunk_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qkv_dtype,
                   ChunkLayout* out);
+
+// The chunked backward: forward inputs, the output gradient and the gradients out.
+struct ChunkBwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    const float* initial_state;
+    const int32_t* cu_seqlens;
+    const void* dout;          // [B, T, HV, V], q's dtype
+    const float* dht;          // [N, HV, K, V] or NULL (zeros)
+    void* dq;                  // [B, T, H, K], q's dtype
+    void* dk;
+    void* dv;                  // [B, T, HV, V]
+    float* dg;                 // [B, T, HV, K]
+    void* dbeta;               // [B, T, HV], beta's dtype
+    float* dh0;                // [N, HV, K, V] or NULL
+    int N, B, T, H, HV, K, V;
+    int qkv_dtype, beta_dtype;
+    float scale;
+    void* workspace;
+    size_t workspace_bytes;
+    int32_t* dev_status;
+    hipStream_t stream;
+};
+
+// Backward workspace: the forward's (schedule + records) first, then per (value head,
+// chunk) fp32 checkpoints and intermediates, then per-value-head dq, dk (all offsets
+// 256-byte aligned):
+//   h [K][V] state at the chunk start, vn [64][V] v', dh [K][V] gradient at the chunk
+//   end, dvn [64][V] dv', gs (dqg, dw, dkg [64][K], dAqk [64][64], dG [K]),
+//   wy (dkd [64][K], dM [64][64]); dq, dk [B*T][HV][K].
+struct ChunkBwdLayout {
+    ChunkLayout fwd;
+    size_t off_h, off_vn, off_dh, off_dvn, off_gs, off_wy, off_dq, off_dk;
+    size_t total;
+};
+
+bool chunk_bwd_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qkv_dtype,
+                      ChunkBwdLayout* out);
+hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, const ChunkBwdLayout& L);
 
 hipError_t launch_recurrent(const RecurrentArgs& a);
 hipError_t launch_chunk(const ChunkArgs& a, const ChunkLayout& L);

@@ -195,6 +195,44 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, 
                                      int packed, int qkv_dtype);
 
 /*
+ * Chunked backward (training): the gradients of kda_chunk_fwd's outputs with respect to
+ * q, k, v, g (the per-token log2 decay), beta and the initial state. The method of
+ * "kernel-fun 0.2.0.dev1 sdist", ALGORITHM.md, section Backward: recompute of the
+ * chunk records, a re-scan that checkpoints the state at every chunk start and v', the
+ * reverse scan of the state gradient (dv' per chunk), then per chunk the products with
+ * the checkpoints, the backward of the WY inverse and the intra-chunk pair terms with
+ * one-sided decay factors only; dg comes out already reverse-cumsummed (it is the
+ * gradient with respect to g itself), and GVA dq, dk are summed over each q/k head's
+ * value heads. All arithmetic is fp32.
+ *
+ *   q, k, v, g, beta, initial_state, cu_seqlens, N, sizes, dtypes, scale, chunk_size:
+ *                as kda_chunk_fwd (the forward being differentiated).
+ *   dout         device [B, T, HV, V] in qkv_dtype: the gradient with respect to o.
+ *   dht          device fp32 [N, HV, K, V]: with respect to the final state, or NULL
+ *                (zeros).
+ *   dq, dk       device [B, T, H, K] in qkv_dtype.   dv  device [B, T, HV, V] in qkv_dtype.
+ *   dg           device fp32 [B, T, HV, K].           dbeta  device [B, T, HV] in beta_dtype.
+ *   dh0          device fp32 [N, HV, K, V], or NULL when not wanted. It is the gradient
+ *                with respect to the initial state (zeros stand in for a NULL one).
+ *   workspace    at least kda_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned;
+ *                one call's intermediates (records, per-chunk fp32 state checkpoints and
+ *                gradients), not shared between calls that may overlap.
+ * Gradients of rows outside every sequence (packed tail, slots that fail the offset
+ * check) are not written. No output may alias an input.
+ */
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                  const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                  int N, const void* dout, const float* dht, void* dq, void* dk, void* dv,
+                  float* dg, void* dbeta, float* dh0, int B, int T, int H, int HV, int K,
+                  int V, int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                  void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                  hipStream_t stream);
+
+/* Workspace bytes kda_chunk_bwd needs for these sizes; 0 for invalid sizes. */
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
+                                     int packed, int qkv_dtype);
+
+/*
  * Per-token recurrent forward (decode, or a token-by-token prefill): the contract of
  * "Add fused recurrent_kda for decode and inference prefill" (attention-gym PR #317):
  * each (sequence, value head, 64-column slice of V) walks its tokens in order with
@@ -227,7 +265,7 @@ const char* kda_last_error(void);
 
 /* ABI version of this header (bumped on any signature change or added entry point);
  * the library returns the KDA_ABI_VERSION it was built with. */
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 int kda_abi_version(void);
 
 #ifdef __cplusplus

@@ -628,3 +628,91 @@ def test_preprocess_c3_full():
     g2 = oracle.gate_activation(g_raw, A_log, dt_bias, None)
     o_ref, _ = _pre_oracle(dict(r, initial_state=None, cu_seqlens=None), True, True, True, True, g2=g2)
     check("o", o, o_ref, torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------------
+# chunked backward: every gradient against the fp64 adjoint oracle
+# ------------------------------------------------------------------------------------
+def _bwd_inputs(d, seed, dht=True):
+    """Output gradient N(0, 1) in q's dtype; final-state gradient N(0, 0.1^2) fp32."""
+    gen = torch.Generator().manual_seed(seed)
+    do = torch.randn(tuple(d["v"].shape), generator=gen).to(d["v"].dtype).to(DEV)
+    N = d["initial_state"].shape[0] if d["initial_state"] is not None else (
+        d["cu_seqlens"].numel() - 1 if d["cu_seqlens"] is not None else d["q"].shape[0])
+    HV, K, V = d["v"].shape[2], d["q"].shape[3], d["v"].shape[3]
+    dht_t = torch.randn(N, HV, K, V, generator=gen).mul(0.1).to(DEV) if dht else None
+    return do, dht_t
+
+
+def _check_bwd(d, do, dht, dtype, rows=None, label=""):
+    import gated_delta_rule_64_amd as kda
+    got = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["initial_state"],
+                            d["cu_seqlens"], dht)
+    torch.cuda.synchronize()
+    ref = oracle.recurrent_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["initial_state"],
+                               d["cu_seqlens"], dht)
+    names = ["dq", "dk", "dv", "dg", "dbeta", "dh0"]
+    for name, x, y in zip(names, got, ref):
+        if rows is not None and name != "dh0":
+            x, y = x[:, rows], y[:, rows]
+        # fp32 gradients (dg, dh0) of bf16 inputs are held to the bf16 bound as well
+        check(f"{label}{name}", x, y, dtype)
+    return got, ref
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_chunk_bwd_dense_gva(dtype):
+    """B=2, T=200 (a short last chunk), H=2, HV=4 (GVA), K=V=128, initial state and a
+    final-state gradient: dq, dk, dv, dg, dbeta, dh0 against the oracle."""
+    d = small(2, 200, 2, 4, 128, 128, dtype, seed=60)
+    do, dht = _bwd_inputs(d, 61)
+    log(f"[bwd dense] B2 T200 H2 HV4 K=V=128 {dtype}")
+    _check_bwd(d, do, dht, dtype)
+
+
+def test_chunk_bwd_packed():
+    """Packed sequences with an empty slot and a tail of unowned rows: gradients on the
+    valid rows, the empty slot's dh0 equal to its dht bitwise, the tail untouched (zero)."""
+    lens = [130, 0, 64, 37, 200]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    Tp = cu[-1] + 40
+    d = small(1, Tp, 2, 4, 128, 128, torch.bfloat16, seed=62)
+    d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    d["initial_state"] = torch.randn(len(lens), 4, 128, 128, generator=torch.Generator().manual_seed(7)).mul(0.05).to(DEV)
+    do, dht = _bwd_inputs(d, 63)
+    log(f"[bwd packed] lens={lens}")
+    rows = valid_rows(cu, Tp)
+    got, _ = _check_bwd(d, do, dht, torch.bfloat16, rows=torch.from_numpy(rows))
+    assert torch.equal(got[5][1], dht[1]), "empty slot passes dht to dh0 bitwise"
+    for x in got[:5]:
+        assert not x[0, cu[-1]:].float().abs().any(), "tail rows must stay untouched"
+
+
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64)])
+def test_chunk_bwd_head_dims(K, V):
+    d = small(1, 150, 2, 2, K, V, torch.bfloat16, seed=64 + K + V)
+    do, dht = _bwd_inputs(d, 65)
+    log(f"[bwd head dims] K={K} V={V}")
+    _check_bwd(d, do, dht, torch.bfloat16)
+
+
+def test_chunk_bwd_steep_gates():
+    """Per-token gates of -15 on one chunk of one head (decay factors down to 2^-945
+    inside a chunk): every factor is one-sided, nothing overflows."""
+    d = small(1, 200, 2, 4, 128, 128, torch.bfloat16, seed=66)
+    g = d["g"].clone()
+    g[:, 64:128, 2] = -15.0
+    d["g"] = g
+    do, dht = _bwd_inputs(d, 67)
+    _check_bwd(d, do, dht, torch.bfloat16)
+
+
+def test_chunk_bwd_c3_full():
+    """The long-context workload (B=1 T=8192 H=16 HV=32 K=V=128 bf16, no initial state,
+    no final-state gradient), every gradient against the oracle."""
+    d = to_device(inputs.make("c3"))
+    do, _ = _bwd_inputs(d, 68, dht=False)
+    log("[bwd c3] B=1 T=8192 H=16 HV=32 K=V=128 bf16")
+    _check_bwd(d, do, None, torch.bfloat16)
