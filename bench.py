@@ -17,6 +17,7 @@ Also reported on the same JSON line:
                  gate input instead of the fp32 log2 decay);
   * fused_inputs -- the same with every input fusion on (fused gate, q/k L2 norm, beta
                  sigmoid x2); the decode line carries the same for the recurrent path;
+  * backward  -- the chunked backward of the headline forward (every input gradient);
   * decode    -- the per-token recurrent forward on 4096 sequences x 32 heads (one token
                  each, fp32 states in and out): state GB/s and fraction of HBM peak;
   * cpu_baseline -- the fp64 CPU oracle on the full headline workload, host threads.
@@ -243,6 +244,39 @@ def main():
     fev.close()
     del g_raw, A_log, dt_bias
 
+    # the chunked backward of the headline forward: do ~ N(0, 1) bf16, no final-state
+    # gradient, no initial state (so no dh0); outputs and workspace allocated up front
+    bws_bytes = kda.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, 0, kda.KDA_BF16)
+    bws = torch.empty(bws_bytes, dtype=torch.uint8, device=dev)
+    gen = torch.Generator().manual_seed(w.seed + 200)
+    dout = torch.randn(tuple(d["v"].shape), generator=gen).to(torch.bfloat16).to(dev)
+    gq, gk, gv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+    gg = torch.empty(B, T, HV, K, dtype=torch.float32, device=dev)
+    gb = torch.empty_like(d["beta"])
+
+    def bcall():
+        rc = lib.kda_chunk_bwd(
+            vp(d["q"].data_ptr()), vp(d["k"].data_ptr()), vp(d["v"].data_ptr()),
+            vp(d["g"].data_ptr()), vp(d["beta"].data_ptr()), None, None, N,
+            vp(dout.data_ptr()), None, vp(gq.data_ptr()), vp(gk.data_ptr()), vp(gv.data_ptr()),
+            vp(gg.data_ptr()), vp(gb.data_ptr()), None, B, T, H, HV, K, V, kda.KDA_BF16,
+            kda.KDA_BF16, 0.0, 64, vp(bws.data_ptr()), bws_bytes, None, sptr)
+        if rc != 0:
+            raise RuntimeError(lib.kda_last_error().decode())
+    bsteps = max(1, steps // 4)
+    for _ in range(2):
+        bcall()
+    torch.cuda.synchronize()
+    bev = Events(hip, 2)
+    hip.hipEventRecord(bev.ev[0], sptr)
+    for _ in range(bsteps):
+        bcall()
+    hip.hipEventRecord(bev.ev[1], sptr)
+    torch.cuda.synchronize()
+    bwd_ms = bev.ms(0, 1) / bsteps
+    bev.close()
+    del bws, dout, gq, gk, gv, gg, gb
+
     # decode: 4096 sequences x 32 heads, one token each, fp32 states in and out
     del ws, out
     dd = inputs.make("dec", device=dev)
@@ -312,6 +346,8 @@ def main():
                   "ms_per_step": gated_ms, "tokens_per_s": tokens / (gated_ms * 1e-3)},
         "fused_inputs": {"workload": "the headline forward with every input fusion: raw bf16 gate + A_log + dt_bias, q/k L2 norm in the loads, beta = 2 sigmoid(beta)",
                          "ms_per_step": fused_ms, "tokens_per_s": tokens / (fused_ms * 1e-3)},
+        "backward": {"workload": "kda_chunk_bwd of the headline forward (dq, dk, dv, dg, dbeta; do ~ N(0,1) bf16, no dht)",
+                     "ms_per_step": bwd_ms, "tokens_per_s": tokens / (bwd_ms * 1e-3), "steps": bsteps},
         "decode": {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
                    "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
                    "bytes": dec_bytes, "fused_inputs_ms": dec_fused_ms},

@@ -121,6 +121,10 @@ struct IntraParams {
     // per-token log2 decay: p.g as given (GATE_LOG2), or formed from the raw gate input;
     // q / k normalisation and the beta activation
     InputSpec in;
+    // checkpoints for the backward (kernels instantiated with CKPT), per record index:
+    // M [64][64] (the key Gram with decay, strictly lower, before beta) and T [64][64]
+    float* m_out;
+    float* t_out;
 };
 
 // Channels d0 .. d0+7 of the per-token log2 decay at row r, value head hv: loaded as
@@ -175,7 +179,7 @@ __device__ __forceinline__ float load_beta(const IntraParams& p, size_t r, int h
 // Stage 2 products run on fp32 matrix cores (v_mfma_f32_16x16x4_f32) in two K-halves to
 // keep the LDS footprint under 80 KB (two blocks per CU). All record tiles are written
 // in the scan's fragment order.
-template <int K, int V, typename TIn, typename TB>
+template <int K, int V, typename TIn, typename TB, bool CKPT>
 __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
     typedef TIn TW;                        // operand type of the record
     constexpr bool SPLIT = sizeof(TW) == 2;
@@ -429,6 +433,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
             lds_barrier();
         }
         // results: Aqk rows of block I -> AS (scaled, masked); L -> Lm (beta_i, strictly lower)
+        float* mrec = CKPT ? p.m_out + ((size_t)hv * p.NCmax + c) * (C * C) : nullptr;
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
             const int tt = wave + 4 * a;
@@ -440,7 +445,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
                     const int ir = 4 * lq + r, i = 16 * I + ir;
                     if (tt & 1) Lm[i * LD + j] = i > j ? betas[i] * acc[a][r] : 0.f;
                     else AS[ir * LD + j] = i >= j ? p.scale * acc[a][r] : 0.f;
+                    if constexpr (CKPT)
+                        if (tt & 1) mrec[i * C + j] = i > j ? acc[a][r] : 0.f;
                 }
+            } else if (CKPT && (tt & 1) && J > I) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mrec[(16 * I + 4 * lq + r) * C + 16 * J + lr] = 0.f;
             }
         }
         if (exact_diag) {
@@ -458,6 +468,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
             {
                 const int ri = tid >> 4, rj = tid & 15;
                 const int i = 16 * I + ri, j = 16 * I + rj;
+                if constexpr (CKPT)
+                    if (!(rj < ri && i < len)) mrec[i * C + j] = 0.f;
                 if (rj <= ri && i < len) {
                     const size_t r_i = (size_t)(rs + i), r_j = (size_t)(rs + j);
                     float aq = 0.f, ak = 0.f;
@@ -467,6 +479,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
                         aq = fmaf(to_f32(q[(r_i * p.H + h) * K + dd]), kj, aq);
                         ak = fmaf(to_f32(k[(r_i * p.H + h) * K + dd]), kj, ak);
                     }
+                    if constexpr (CKPT)
+                        if (rj < ri) mrec[i * C + j] = ak;
                     AS[ri * LD + j] = p.scale * aq;
                     if (i > j) Lm[i * LD + j] = betas[i] * ak;
                 }
@@ -533,6 +547,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
         lds_barrier();
     }
 
+    if constexpr (CKPT) {
+        float* trec = p.t_out + ((size_t)hv * p.NCmax + c) * (C * C);
+        for (int e = tid; e < C * C; e += NTHREADS) trec[e] = Tm[(e / C) * LD + (e % C)];
+    }
     // ---- phase 4: T beta, (k 2^G)^T, v^T in LDS; qg and 2^G straight to the record;
     //      kg^T staged in the space of L and T once T beta is built ----
     for (int e = tid; e < C * C; e += NTHREADS) {
@@ -711,7 +729,7 @@ __device__ __forceinline__ float frag_row_rstd(const bf16x8 (&x)[NS]) {
     return l2norm_rstd(ss);
 }
 
-template <int K, int V, typename TB>
+template <int K, int V, typename TB, bool CKPT>
 __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) {
     typedef __bf16 TW;
     constexpr int NKS = K / 32, NVS = V / 32;   // 32-column steps of q/k/g and of v
@@ -1084,14 +1102,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
         if (J <= w) {
-            f32x4 x;
+            f32x4 x, m;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float val = J < w ? (J == 0 ? lt[0][r] : (J == 1 ? lt[1][r] : lt[2][r]))
                                         : (lr > 4 * lq + r ? lt_d[r] : 0.f);
+                m[r] = val;
                 x[r] = beta_i * val;
             }
             *reinterpret_cast<f32x4*>(Lm + sw(16 * w + lr, 16 * J + 4 * lq)) = x;
+            if constexpr (CKPT)
+                *reinterpret_cast<f32x4*>(p.m_out + ((size_t)hv * p.NCmax + c) * (C * C) + (16 * w + lr) * C + 16 * J + 4 * lq) = m;
+        } else if (CKPT) {
+            *reinterpret_cast<f32x4*>(p.m_out + ((size_t)hv * p.NCmax + c) * (C * C) + (16 * w + lr) * C + 16 * J + 4 * lq) =
+                f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
     lds_barrier();
@@ -1153,6 +1177,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
         lds_barrier();
     }
 
+    if constexpr (CKPT) {   // T, lower blocks (the blocks above them were never written)
+        float* trec = p.t_out + ((size_t)hv * p.NCmax + c) * (C * C);
+        for (int e = tid; e < C * C; e += NTHREADS) {
+            const int i = e / C, j = e % C;
+            trec[e] = (j >> 4) <= (i >> 4) ? Tm[sw(i, j)] : 0.f;
+        }
+    }
     // ---- T beta as hi + lo bf16 tiles (lower blocks only). A single bf16 T beta is the
     //      largest rounding left once beta spreads over (0, 2): u and w share it, and its
     //      error changes the effective erase strength, which does not decay when beta k^T k
@@ -1916,14 +1947,25 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     ip.NT = NT;
     ip.scale = a.scale;
     ip.in = a.in;
+    ip.m_out = a.m_out; ip.t_out = a.t_out;
     const long long nintra = (long long)L.NCmax * a.HV;
     if (nintra > 0) {
-        if constexpr (sizeof(TIn) == 2)
-            hipLaunchKernelGGL((intra_bf16_kernel<K, V, TB>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
-                               a.stream, ip);
-        else
-            hipLaunchKernelGGL((intra_kernel<K, V, TIn, TB>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
-                               a.stream, ip);
+        const bool ckpt = a.m_out != nullptr;
+        if constexpr (sizeof(TIn) == 2) {
+            if (ckpt)
+                hipLaunchKernelGGL((intra_bf16_kernel<K, V, TB, true>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
+                                   a.stream, ip);
+            else
+                hipLaunchKernelGGL((intra_bf16_kernel<K, V, TB, false>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
+                                   a.stream, ip);
+        } else {
+            if (ckpt)
+                hipLaunchKernelGGL((intra_kernel<K, V, TIn, TB, true>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
+                                   a.stream, ip);
+            else
+                hipLaunchKernelGGL((intra_kernel<K, V, TIn, TB, false>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
+                                   a.stream, ip);
+        }
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

@@ -62,15 +62,34 @@ template <typename TW, int R, int KC>
 __device__ __forceinline__ void stage_record(const TW* t, bool split, float* dst, int ld, int tid) {
     typedef Mma<TW> M;
     constexpr int NS = KC / M::KS;
-    for (int e = tid; e < R * KC; e += BT) {
-        const int x = e % M::KPL;
-        const int l = (e / M::KPL) % 64;
-        const int blk = e / (M::KPL * 64);
-        const int row = 16 * (blk / NS) + (l & 15);
-        const int col = (blk % NS) * M::KS + (l >> 4) * M::KPL + x;
-        float v = to_f32(t[e]);
-        if (split) v += to_f32(t[e + R * KC]);
-        dst[row * ld + col] = v;
+    static_assert((R * KC) % (8 * BT) == 0, "whole 8-element groups per thread");
+    // 8 consecutive elements (one 16-byte bf16 or two fp32 vectors) per thread and step
+#pragma unroll 4
+    for (int q = tid; q < R * KC / 8; q += BT) {
+        const int e0 = 8 * q;
+        float v[8];
+        if constexpr (sizeof(TW) == 2) {
+            const bf16x8 h = *reinterpret_cast<const bf16x8*>(t + e0);
+            bf16x8 l8 = {};
+            if (split) l8 = *reinterpret_cast<const bf16x8*>(t + e0 + R * KC);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v[x] = (float)h[x] + (float)l8[x];
+        } else {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(t + e0);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(t + e0 + 4);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { v[x] = a[x]; v[4 + x] = b[x]; }
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int e = e0 + x;
+            const int xi = e % M::KPL;
+            const int l = (e / M::KPL) % 64;
+            const int blk = e / (M::KPL * 64);
+            const int row = 16 * (blk / NS) + (l & 15);
+            const int col = (blk % NS) * M::KS + (l >> 4) * M::KPL + xi;
+            dst[row * ld + col] = v[x];
+        }
     }
 }
 
@@ -102,8 +121,10 @@ struct BwdParams {
     // checkpoints and intermediates, per (value head, chunk): index hv * NCmax + c
     const float* h;      // [K][V] state at the chunk start
     const float* vn;     // [64][V] v'
+    const float* mt;     // M [64][64] per item, then T [64][64] per item (Stage 2)
     float* dh;           // [K][V] gradient at the chunk end
     float* dvn;          // [64][V] dv'
+    float* sops;         // operands of the reverse scan (ScanOps)
     float* gs;           // dqg, dw, dkg [64][K] each, dAqk [64][64], dG [K]
     float* wy;           // dkd [64][K], dM [64][64]
     float* dq_hv;        // [B*T][HV][K]
@@ -121,26 +142,146 @@ struct WyLayout {
     static constexpr int FLOATS = C * K + C * C;
 };
 
+// the chunk this block handles, or false when it is past the packed schedule's end
+__device__ __forceinline__ bool bwd_chunk(const BwdParams& p, int& c, int& hv, int2& pos) {
+    const int G = p.NCmax * p.HV;
+    const int item = xcd_remap(blockIdx.x, G);
+    hv = item % p.HV;
+    c = item / p.HV;
+    if (!p.dense && c >= p.nchunks[0]) return false;
+    pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
+    return true;
+}
+
+// Accumulator order of a K x V fp32 tile (rows d, columns v): block (16-column tile,
+// 16-row band), lane l = (v % 16) + 16 ((d % 16) / 4) holds rows d .. d+3 of column v as
+// one f32x4 -- the layout of a 16x16 matrix-core result, loaded with one 16-byte access.
+template <int K>
+__device__ __forceinline__ int acc_kv(int v, int d) {
+    return (((v >> 4) * (K / 16) + (d >> 4)) * 64 + (v & 15) + 16 * ((d & 15) >> 2)) * 4 + (d & 3);
+}
+
+// Per (value head, chunk) operands of the reverse scan, fp32: kg in fragment order as
+// the A operand of kg dS ([64][K]), w^T in fragment order as the A operand of w^T dv'
+// ([K][64]), P1 = Aqk^T do ([64][V], AccTile order) and P2 = qg^T do ([K][V], acc_kv
+// order). P1 and P2 do not depend on the state gradient, so they are formed in
+// parallel before the scan.
+template <int K, int V>
+struct ScanOps {
+    static constexpr int KG = 0, WT = C * K, P1 = 2 * C * K, P2 = 2 * C * K + C * V;
+    static constexpr int FLOATS = 2 * C * K + C * V + K * V;
+};
+
 // ------------------------------------------------------------------------------------
-// reverse scan: dS (the state gradient) walks each chain's chunks backwards; per chunk
-// it stores dS (the gradient at the chunk end) and dv'. One block per (chain, 16-column
-// slice of V); wave w owns rows 16w.. of dv' and state bands w, w + 4.
+// prep for the reverse scan, per (chunk, value head): P1, P2 and the transposed
+// operands, from the forward records and do.
 // ------------------------------------------------------------------------------------
 template <int K, int V, typename TW, typename TIn>
-__global__ __launch_bounds__(BT, 1) void bwd_dscan_kernel(BwdParams p) {
-    constexpr int BV = 16, NVT = V / BV, LB = BV + 1, LA = C + 1, LK = K + 1, NDT = K / 64;
+__global__ __launch_bounds__(BT, 1) void bwd_prep_kernel(BwdParams p) {
+    constexpr int LA = C + 1, LK = K + 1, LV = V + 1;
     constexpr bool SPLIT = sizeof(TW) == 2;
-    constexpr int P1 = C * LA + K * LA, P2 = 2 * C * LK;
-    __shared__ float un[P1 > P2 ? P1 : P2];
-    __shared__ float doL[C * LB];
-    __shared__ float dvL[C * LB];
-    __shared__ float dSL[K * LB];
-    __shared__ float eGL[K];
-    float* aqkL = un;              // Aqk[r][s]
-    float* kgL = un + C * LA;      // kg^T[d][s]
-    float* qgL = un;               // qg[r][d]
-    float* wL = un + C * LK;       // w[r][d]
+    typedef ScanOps<K, V> SO;
+    typedef FragTile<float, C, K> FKG;
+    typedef FragTile<float, K, C> FWT;
+    __shared__ float R0[C * LK];     // qg [r][d], then w [r][d]
+    __shared__ float R1[K * LA];     // Aqk [r][s], then kg^T [d][s]
+    __shared__ float doL[C * LV];
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int c, hv;
+    int2 pos;
+    if (!bwd_chunk(p, c, hv, pos)) return;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const char* rec = p.rec + ci * p.rec_bytes;
+    const TIn* dout = reinterpret_cast<const TIn*>(p.dout);
+    float* ops = p.sops + ci * (size_t)SO::FLOATS;
 
+    stage_record<TW, C, K>(reinterpret_cast<const TW*>(rec + p.off_qg), SPLIT, R0, LK, tid);
+    stage_record<TW, C, C>(reinterpret_cast<const TW*>(rec + p.off_aqk), SPLIT, R1, LA, tid);
+    for (int e = tid; e < C * V; e += BT) {
+        const int r = e / V, vv = e % V;
+        doL[r * LV + vv] = r < pos.y ? to_f32(dout[((size_t)(pos.x + r) * p.HV + hv) * V + vv]) : 0.f;
+    }
+    __syncthreads();
+    // P1[s][v] = sum_r Aqk[r][s] do[r][v]: wave w owns rows 16w ..
+    for (int nt = 0; nt < V / 16; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_f32(acc, [&](int i, int k) { return R1[k * LA + 16 * wave + i]; },
+                      [&](int j, int k) { return doL[k * LV + 16 * nt + j]; }, C, lane);
+        *reinterpret_cast<f32x4*>(ops + SO::P1 + AccTile::quad(16 * nt + lr, 16 * wave + 4 * lq)) = acc;
+    }
+    // P2[d][v] = sum_r qg[r][d] do[r][v]: wave w owns bands w, w + 4, ..
+    for (int db = wave; db < K / 16; db += 4)
+        for (int nt = 0; nt < V / 16; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_f32(acc, [&](int i, int k) { return R0[k * LK + 16 * db + i]; },
+                          [&](int j, int k) { return doL[k * LV + 16 * nt + j]; }, C, lane);
+            *reinterpret_cast<f32x4*>(ops + SO::P2 + acc_kv<K>(16 * nt + lr, 16 * db + 4 * lq)) = acc;
+        }
+    __syncthreads();
+    stage_record<TW, C, K>(reinterpret_cast<const TW*>(rec + p.off_w), false, R0, LK, tid);
+    stage_record<TW, K, C>(reinterpret_cast<const TW*>(rec + p.off_kgT), SPLIT, R1, LA, tid);
+    __syncthreads();
+    // kg in fragment order (rows s, contraction d) and w^T (rows d, contraction r)
+    for (int e = tid; e < C * K; e += BT) {
+        const int l = e % 64, blk = e / 64;
+        {
+            const int row = 16 * (blk / FKG::NS) + (l & 15), col = 4 * (blk % FKG::NS) + (l >> 4);
+            ops[SO::KG + e] = R1[col * LA + row];
+        }
+        {
+            const int row = 16 * (blk / FWT::NS) + (l & 15), col = 4 * (blk % FWT::NS) + (l >> 4);
+            ops[SO::WT + e] = R0[col * LK + row];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// reverse scan: dS (the state gradient) walks each chain's chunks backwards:
+//   dh_c = dS,  dv' = P1 + kg dS,  dS <- 2^G dS + P2 - w^T dv'
+// One block per (chain, 16-column slice of V); wave w owns rows 16w.. of dv' and state
+// bands w, w + 4. The kg / w^T fragments are loaded straight from memory (fragment
+// order), two chunks ahead; dS^T and dv'^T are shared through LDS.
+// ------------------------------------------------------------------------------------
+template <int K, int V>
+struct DscanFrags {
+    static constexpr int NKS = K / 4, NJS = C / 4, NDT = K / 64;
+    float kg[NKS];
+    float wt[NDT][NJS];
+    f32x4 p1;
+    f32x4 p2[NDT];
+    f32x4 e[NDT];
+};
+
+template <int K, int V>
+__device__ __forceinline__ void load_dscan(DscanFrags<K, V>& F, const BwdParams& p, int hv, int c,
+                                           int wave, int lane, int v0) {
+    typedef ScanOps<K, V> SO;
+    typedef FragTile<float, C, K> FKG;
+    typedef FragTile<float, K, C> FWT;
+    const int lr = lane & 15, lq = lane >> 4;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const float* ops = p.sops + ci * (size_t)SO::FLOATS;
+    const float* eg = reinterpret_cast<const float*>(p.rec + ci * p.rec_bytes + p.off_eg);
+#pragma unroll
+    for (int kk = 0; kk < DscanFrags<K, V>::NKS; ++kk) F.kg[kk] = ops[SO::KG + FKG::frag(wave, kk, lane)];
+#pragma unroll
+    for (int a = 0; a < DscanFrags<K, V>::NDT; ++a) {
+#pragma unroll
+        for (int jj = 0; jj < DscanFrags<K, V>::NJS; ++jj)
+            F.wt[a][jj] = ops[SO::WT + FWT::frag(wave + 4 * a, jj, lane)];
+        F.p2[a] = *reinterpret_cast<const f32x4*>(ops + SO::P2 + acc_kv<K>(v0 + lr, 16 * (wave + 4 * a) + 4 * lq));
+        F.e[a] = *reinterpret_cast<const f32x4*>(eg + 16 * (wave + 4 * a) + 4 * lq);
+    }
+    F.p1 = *reinterpret_cast<const f32x4*>(ops + SO::P1 + AccTile::quad(v0 + lr, 16 * wave + 4 * lq));
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(BT, 1) void bwd_scan_kernel(BwdParams p) {
+    constexpr int BV = 16, NVT = V / BV, LDK = K + 1, LDC = C + 1, NDT = K / 64;
+    typedef DscanFrags<K, V> DF;
+    __shared__ float dSt[BV * LDK];   // dS^T [v][d]
+    __shared__ float dvt[BV * LDC];   // dv'^T [v][r]
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = p.N * p.HV * NVT;
@@ -152,7 +293,6 @@ __global__ __launch_bounds__(BT, 1) void bwd_dscan_kernel(BwdParams p) {
     const int c0 = p.dense ? n * p.NT : p.coff[n];
     const int c1 = p.dense ? c0 + p.NT : p.cend[n];
     const size_t sbase = ((size_t)n * p.HV + hv) * (size_t)K * V;
-    const TIn* dout = reinterpret_cast<const TIn*>(p.dout);
 
     f32x4 dS[NDT];
 #pragma unroll
@@ -161,64 +301,61 @@ __global__ __launch_bounds__(BT, 1) void bwd_dscan_kernel(BwdParams p) {
         for (int r = 0; r < 4; ++r) {
             const int d = 16 * (wave + 4 * a) + 4 * lq + r;
             dS[a][r] = p.dht ? p.dht[sbase + (size_t)d * V + v0 + lr] : 0.f;
-            dSL[d * LB + lr] = dS[a][r];
+            dSt[lr * LDK + d] = dS[a][r];
         }
-    for (int c = c1 - 1; c >= c0; --c) {
-        const int2 pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
-        const char* rec = p.rec + ((size_t)hv * p.NCmax + c) * p.rec_bytes;
+    // two-chunk ring: F0 holds chunk c, F1 chunk c - 1; past the first chunk a buffer
+    // re-reads chunk c0 (in bounds, never used)
+    auto clampc = [&](int c) { return c >= c0 ? c : c0; };
+    DF F0, F1;
+    if (c0 < c1) {
+        load_dscan<K, V>(F0, p, hv, c1 - 1, wave, lane, v0);
+        load_dscan<K, V>(F1, p, hv, clampc(c1 - 2), wave, lane, v0);
+    }
+    __syncthreads();
+    auto step = [&](DF& F, int c) {
         const size_t ci = (size_t)hv * p.NCmax + c;
-        // the gradient at the chunk end
         float* dhb = p.dh + ci * (size_t)K * V;
 #pragma unroll
         for (int a = 0; a < NDT; ++a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) dhb[(size_t)(16 * (wave + 4 * a) + 4 * lq + r) * V + v0 + lr] = dS[a][r];
-        stage_record<TW, C, C>(reinterpret_cast<const TW*>(rec + p.off_aqk), SPLIT, aqkL, LA, tid);
-        stage_record<TW, K, C>(reinterpret_cast<const TW*>(rec + p.off_kgT), SPLIT, kgL, LA, tid);
-        for (int e = tid; e < C * BV; e += BT) {
-            const int r = e / BV, vv = e % BV;
-            doL[r * LB + vv] = r < pos.y ? to_f32(dout[((size_t)(pos.x + r) * p.HV + hv) * V + v0 + vv]) : 0.f;
-        }
-        for (int e = tid; e < K; e += BT) eGL[e] = reinterpret_cast<const float*>(rec + p.off_eg)[e];
-        __syncthreads();
-        // dv' = Aqk^T do + kg dS, rows 16 wave ..
-        {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int s0 = 16 * wave;
-            acc = mma_f32(acc, [&](int i, int k) { return aqkL[k * LA + s0 + i]; },
-                          [&](int j, int k) { return doL[k * LB + j]; }, C, lane);
-            acc = mma_f32(acc, [&](int i, int k) { return kgL[k * LA + s0 + i]; },
-                          [&](int j, int k) { return dSL[k * LB + j]; }, K, lane);
-            float* dvb = p.dvn + ci * (size_t)C * V;
+        // dv' = P1 + kg dS (rows 16 wave + 4 lq + r, column lr of the slice)
+        f32x4 acc = F.p1;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s = s0 + 4 * lq + r;
-                dvL[s * LB + lr] = acc[r];
-                dvb[(size_t)s * V + v0 + lr] = acc[r];
-            }
+        for (int kk = 0; kk < DF::NKS; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(F.kg[kk], dSt[lr * LDK + 4 * kk + lq], acc, 0, 0, 0);
+        float* dvb = p.dvn + ci * (size_t)C * V;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int s = 16 * wave + 4 * lq + r;
+            dvt[lr * LDC + s] = acc[r];
+            dvb[(size_t)s * V + v0 + lr] = acc[r];
         }
         __syncthreads();
-        stage_record<TW, C, K>(reinterpret_cast<const TW*>(rec + p.off_qg), SPLIT, qgL, LK, tid);
-        stage_record<TW, C, K>(reinterpret_cast<const TW*>(rec + p.off_w), false, wL, LK, tid);
-        __syncthreads();
-        // dS <- 2^G dS + qg^T do - w^T dv'
+        // dS <- 2^G dS + P2 - w^T dv'
 #pragma unroll
         for (int a = 0; a < NDT; ++a) {
-            const int d0 = 16 * (wave + 4 * a);
-            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = {0.f, 0.f, 0.f, 0.f};
-            aq = mma_f32(aq, [&](int i, int k) { return qgL[k * LK + d0 + i]; },
-                         [&](int j, int k) { return doL[k * LB + j]; }, C, lane);
-            aw = mma_f32(aw, [&](int i, int k) { return wL[k * LK + d0 + i]; },
-                         [&](int j, int k) { return dvL[k * LB + j]; }, C, lane);
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < DF::NJS; ++jj)
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(F.wt[a][jj], dvt[lr * LDC + 4 * jj + lq], x, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int d = d0 + 4 * lq + r;
-                dS[a][r] = eGL[d] * dS[a][r] + aq[r] - aw[r];
-                dSL[d * LB + lr] = dS[a][r];
+                dS[a][r] = fmaf(F.e[a][r], dS[a][r], F.p2[a][r] - x[r]);
+                dSt[lr * LDK + 16 * (wave + 4 * a) + 4 * lq + r] = dS[a][r];
             }
         }
         __syncthreads();
+    };
+    const int nsteps = c1 - c0;
+    int c = c1 - 1;
+    for (int t = 0; t < nsteps / 2; ++t, c -= 2) {
+        step(F0, c);
+        load_dscan<K, V>(F0, p, hv, clampc(c - 2), wave, lane, v0);
+        step(F1, c - 1);
+        load_dscan<K, V>(F1, p, hv, clampc(c - 3), wave, lane, v0);
     }
+    if (nsteps & 1) step(F0, c);
     if (p.dh0) {
 #pragma unroll
         for (int a = 0; a < NDT; ++a)
@@ -226,17 +363,6 @@ __global__ __launch_bounds__(BT, 1) void bwd_dscan_kernel(BwdParams p) {
             for (int r = 0; r < 4; ++r)
                 p.dh0[sbase + (size_t)(16 * (wave + 4 * a) + 4 * lq + r) * V + v0 + lr] = dS[a][r];
     }
-}
-
-// the chunk this block handles, or false when it is past the packed schedule's end
-__device__ __forceinline__ bool bwd_chunk(const BwdParams& p, int& c, int& hv, int2& pos) {
-    const int G = p.NCmax * p.HV;
-    const int item = xcd_remap(blockIdx.x, G);
-    hv = item % p.HV;
-    c = item / p.HV;
-    if (!p.dense && c >= p.nchunks[0]) return false;
-    pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
-    return true;
 }
 
 // ------------------------------------------------------------------------------------
@@ -326,8 +452,8 @@ __global__ __launch_bounds__(BT, 2) void bwd_state_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------
-// backward of the WY inverse, per (chunk, value head): recomputes M and T from k, g,
-// beta; writes dv and dbeta (final) and dkd, dM for the pair kernel.
+// backward of the WY inverse, per (chunk, value head): with M and T from the recompute,
+// writes dv and dbeta (final) and dkd, dM for the pair kernel.
 // ------------------------------------------------------------------------------------
 template <int K, int V, typename TIn, typename TB>
 __global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
@@ -373,39 +499,20 @@ __global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
         for (int r = 0; r < C; ++r) { acc += XL[r * LX + tid]; XL[r * LX + tid] = acc; }
     }
     __syncthreads();
-    // ---- M[r][s] = sum_d k_r k_s 2^(Gamma_r - Gamma_s), s < r: thread (r, s = sg + 4j) ----
-    {
-        const int r = tid >> 2, sg = tid & 3;
-        float acc[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-        for (int d = 0; d < K; ++d) {
-            const float kr = kL[r * LK + d], gr = XL[r * LX + d];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int s = sg + 4 * j;
-                if (s < r) acc[j] = fmaf(kr * kL[s * LK + d], exp2_fast(gr - XL[s * LX + d]), acc[j]);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int s = sg + 4 * j;
-            ML[r * LA + s] = s < r ? acc[j] : 0.f;
-        }
-    }
-    __syncthreads();
+    // kd = k 2^Gamma; M and T = (I + diag(beta) M)^-1 as Stage 2 of the recompute left them
     for (int e = tid; e < C * K; e += BT) {
         const int r = e / K, d = e % K;
         kL[r * LK + d] *= exp2_fast(XL[r * LX + d]);
     }
-    // ---- T = (I + diag(beta) M)^-1 by columns (unit lower triangular) ----
-    if (tid < C) {
-        const int j = tid;
-        for (int r = 0; r < C; ++r) TL[r * LA + j] = r == j ? 1.f : 0.f;
-        for (int r = j + 1; r < C; ++r) {
-            float acc = 0.f;
-            for (int s = j; s < r; ++s) acc = fmaf(ML[r * LA + s], TL[s * LA + j], acc);
-            TL[r * LA + j] = -bL[r] * acc;
+    {
+        const float* Mg = p.mt + ci * (size_t)(C * C);
+        const float* Tg = p.mt + ((size_t)p.NCmax * p.HV + ci) * (C * C);
+        for (int e = tid; e < C * C / 4; e += BT) {
+            const int r = e / (C / 4), s4 = 4 * (e % (C / 4));
+            const f32x4 m = *reinterpret_cast<const f32x4*>(Mg + r * C + s4);
+            const f32x4 t = *reinterpret_cast<const f32x4*>(Tg + r * C + s4);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { ML[r * LA + s4 + x] = m[x]; TL[r * LA + s4 + x] = t[x]; }
         }
     }
     __syncthreads();
@@ -682,6 +789,8 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
     f.dev_status = a.dev_status; f.stream = a.stream; f.events = nullptr;
     f.h_out = reinterpret_cast<float*>(ws + L.off_h);
     f.vn_out = reinterpret_cast<float*>(ws + L.off_vn);
+    f.m_out = reinterpret_cast<float*>(ws + L.off_mt);                        // [items][64][64]
+    f.t_out = f.m_out + (size_t)L.fwd.NCmax * a.HV * (C * C);                  // [items][64][64]
     hipError_t err = launch_chunk(f, L.fwd);
     if (err != hipSuccess) return err;
 
@@ -703,8 +812,10 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
     p.off_kgT = L.fwd.off_kgT; p.off_aqk = L.fwd.off_aqk; p.off_eg = L.fwd.off_eg;
     p.h = reinterpret_cast<const float*>(ws + L.off_h);
     p.vn = reinterpret_cast<const float*>(ws + L.off_vn);
+    p.mt = reinterpret_cast<const float*>(ws + L.off_mt);
     p.dh = reinterpret_cast<float*>(ws + L.off_dh);
     p.dvn = reinterpret_cast<float*>(ws + L.off_dvn);
+    p.sops = reinterpret_cast<float*>(ws + L.off_sops);
     p.gs = reinterpret_cast<float*>(ws + L.off_gs);
     p.wy = reinterpret_cast<float*>(ws + L.off_wy);
     p.dq_hv = reinterpret_cast<float*>(ws + L.off_dq);
@@ -712,10 +823,13 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
 
     const long long chains = (long long)a.N * a.HV;
     const long long nchunk_items = (long long)L.fwd.NCmax * a.HV;
-    if (chains > 0) {
+    if (nchunk_items > 0) {
         // the records are in the input type (bf16 hi/lo pairs, or fp32)
-        hipLaunchKernelGGL((bwd_dscan_kernel<K, V, TIn, TIn>), dim3((unsigned)(chains * (V / 16))),
-                           dim3(BT), 0, a.stream, p);
+        hipLaunchKernelGGL((bwd_prep_kernel<K, V, TIn, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (chains > 0) {
+        hipLaunchKernelGGL((bwd_scan_kernel<K, V>), dim3((unsigned)(chains * (V / 16))), dim3(BT), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (nchunk_items > 0) {
@@ -751,8 +865,10 @@ bool chunk_bwd_layout(int B, int T, int HV, int K, int V, int N, bool packed, in
     size_t off = align256b(L.fwd.total);
     L.off_h = off;   off = align256b(off + items * K * V * 4);
     L.off_vn = off;  off = align256b(off + items * C * V * 4);
+    L.off_mt = off;  off = align256b(off + items * (size_t)(2 * C * C) * 4);
     L.off_dh = off;  off = align256b(off + items * K * V * 4);
     L.off_dvn = off; off = align256b(off + items * C * V * 4);
+    L.off_sops = off; off = align256b(off + items * (size_t)(2 * C * K + C * V + K * V) * 4);
     L.off_gs = off;  off = align256b(off + items * (size_t)(3 * C * K + C * C + K) * 4);
     L.off_wy = off;  off = align256b(off + items * (size_t)(C * K + C * C) * 4);
     L.off_dq = off;  off = align256b(off + rows * HV * K * 4);

@@ -69,6 +69,10 @@ struct ChunkArgs {
     // chunk's start [HV][NCmax][K][V] and v' [HV][NCmax][64][V], fp32
     float* h_out = nullptr;
     float* vn_out = nullptr;
+    // and from Stage 1+2: M (the key Gram with decay, strictly lower, before beta) and
+    // T = (I + diag(beta) M)^-1, [HV][NCmax][64][64] fp32 each
+    float* m_out = nullptr;
+    float* t_out = nullptr;
 };
 
 // Workspace layout of the chunked forward (all offsets 256-byte aligned):
@@ -126,12 +130,14 @@ struct ChunkBwdArgs {
 // Backward workspace: the forward's (schedule + records) first, then per (value head,
 // chunk) fp32 checkpoints and intermediates, then per-value-head dq, dk (all offsets
 // 256-byte aligned):
-//   h [K][V] state at the chunk start, vn [64][V] v', dh [K][V] gradient at the chunk
-//   end, dvn [64][V] dv', gs (dqg, dw, dkg [64][K], dAqk [64][64], dG [K]),
+//   h [K][V] state at the chunk start, vn [64][V] v', mt (M [64][64] and T [64][64] of
+//   Stage 2), dh [K][V] gradient at the chunk
+//   end, dvn [64][V] dv', sops (the reverse scan's operands: kg, w^T, Aqk^T do, qg^T do),
+//   gs (dqg, dw, dkg [64][K], dAqk [64][64], dG [K]),
 //   wy (dkd [64][K], dM [64][64]); dq, dk [B*T][HV][K].
 struct ChunkBwdLayout {
     ChunkLayout fwd;
-    size_t off_h, off_vn, off_dh, off_dvn, off_gs, off_wy, off_dq, off_dk;
+    size_t off_h, off_vn, off_mt, off_dh, off_dvn, off_sops, off_gs, off_wy, off_dq, off_dk;
     size_t total;
 };
 

@@ -159,6 +159,17 @@ def _rec_ex(lib, **kw):
                                     a["stream"])
 
 
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, N=1, do=FAKE, dht=None,
+             dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, db=FAKE, dh0=None, B=1, T=64, H=2, HV=2, K=128,
+             V=128, qd=1, bd=1, scale=0.0, cs=64, ws=FAKE, wsb=1 << 40, st=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["N"],
+                             a["do"], a["dht"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"],
+                             a["dh0"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["qd"],
+                             a["bd"], a["scale"], a["cs"], a["ws"], a["wsb"], a["st"], a["stream"])
+
+
 CASES = [
     ("null q", dict(q=None), -1),
     ("HV % H", dict(H=3, HV=4), -2),
@@ -271,3 +282,40 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(TypeError):
         kda_chunk_fwd(q, q, torch.zeros(1, 64, 2, 128), torch.zeros(1, 64, 2, 128, dtype=torch.float64),
                       torch.zeros(1, 64, 2))
+
+
+@pytest.mark.parametrize("name,kw,code", CASES, ids=[c[0] for c in CASES])
+def test_bwd_rejects_common(lib, name, kw, code):
+    assert _bwd(lib, **kw) == code
+    assert lib.kda_last_error().decode() != ""
+
+
+def test_bwd_specific_rejects(lib):
+    for out in ("do", "dq", "dk", "dv", "dg", "db"):
+        assert _bwd(lib, **{out: None}) == -1, out
+    assert _bwd(lib, dht=FAKE + 4) == -2
+    assert _bwd(lib, cs=32) == -4
+    assert _bwd(lib, K=96) == -4
+    assert _bwd(lib, V=256) == -4
+    assert _bwd(lib, ws=None) == -5
+    assert _bwd(lib, wsb=16) == -5
+    assert _bwd(lib, ws=FAKE + 16) == -5
+    assert _bwd(lib, cu=FAKE, N=0, T=0) == 0
+    assert lib.kda_last_error().decode() == ""
+
+
+def test_bwd_workspace_bytes(lib):
+    """The forward's workspace, then per (value head, chunk) fp32 checkpoints,
+    reverse-scan operands and intermediates, then per-value-head dq, dk."""
+    B, T, H, HV, K, V = 2, 4096 + 17, 4, 8, 128, 128
+    nt = (T + 63) // 64
+    items = HV * B * nt
+    al = lambda x: (x + 255) // 256 * 256
+    off = al(lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, 1))
+    for per in (K * V, 64 * V, K * V, 64 * V, 2 * 64 * K + 64 * V + K * V,
+                3 * 64 * K + 64 * 64 + K, 64 * K + 64 * 64):
+        off = al(off + items * per * 4)
+    for _ in range(2):
+        off = al(off + B * T * HV * K * 4)
+    assert lib.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, B, 0, 1) == off
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 64, 1, 1, 96, 128, 1, 0, 1) == 0
