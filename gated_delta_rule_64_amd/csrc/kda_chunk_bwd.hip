@@ -93,6 +93,45 @@ __device__ __forceinline__ void stage_record(const TW* t, bool split, float* dst
     }
 }
 
+// Rows [0, R) x columns [0, W) of a row-major fp32 array (row stride `gstride` floats)
+// into LDS dst[r * ld + c]; 16-byte loads, several in flight per thread.
+template <int R, int W>
+__device__ __forceinline__ void stage_f32(const float* src, size_t gstride, float* dst, int ld, int tid) {
+    constexpr int W4 = W / 4;
+#pragma unroll 4
+    for (int q = tid; q < R * W4; q += BT) {
+        const int r = q / W4, c4 = 4 * (q % W4);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + (size_t)r * gstride + c4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[r * ld + c4 + e] = x[e];
+    }
+}
+
+// Rows of an input tensor as fp32 into LDS: row r at src + r * rstride (W contiguous
+// elements of T), zeros from row `len` on.
+template <int R, int W, typename T>
+__device__ __forceinline__ void stage_rows(const T* src, size_t rstride, int len, float* dst, int ld, int tid) {
+    constexpr int W4 = W / 4;
+#pragma unroll 4
+    for (int q = tid; q < R * W4; q += BT) {
+        const int r = q / W4, c4 = 4 * (q % W4);
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (r < len) {
+            if constexpr (sizeof(T) == 2) {
+                const bf16x4 h = *reinterpret_cast<const bf16x4*>(src + (size_t)r * rstride + c4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (float)h[e];
+            } else {
+                const f32x4 f = *reinterpret_cast<const f32x4*>(src + (size_t)r * rstride + c4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = f[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[r * ld + c4 + e] = x[e];
+    }
+}
+
 struct BwdParams {
     const void* q;
     const void* k;
@@ -198,10 +237,7 @@ __global__ __launch_bounds__(BT, 1) void bwd_prep_kernel(BwdParams p) {
 
     stage_record<TW, C, K>(reinterpret_cast<const TW*>(rec + p.off_qg), SPLIT, R0, LK, tid);
     stage_record<TW, C, C>(reinterpret_cast<const TW*>(rec + p.off_aqk), SPLIT, R1, LA, tid);
-    for (int e = tid; e < C * V; e += BT) {
-        const int r = e / V, vv = e % V;
-        doL[r * LV + vv] = r < pos.y ? to_f32(dout[((size_t)(pos.x + r) * p.HV + hv) * V + vv]) : 0.f;
-    }
+    stage_rows<C, V>(dout + ((size_t)pos.x * p.HV + hv) * V, (size_t)p.HV * V, pos.y, doL, LV, tid);
     __syncthreads();
     // P1[s][v] = sum_r Aqk[r][s] do[r][v]: wave w owns rows 16w ..
     for (int nt = 0; nt < V / 16; ++nt) {
@@ -399,17 +435,11 @@ __global__ __launch_bounds__(BT, 2) void bwd_state_kernel(BwdParams p) {
     for (int j = 0; j < 4; ++j) aA[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dgacc = 0.f;   // thread d < K: sum_v dS[d][v] S[d][v]
     for (int vb = 0; vb < V; vb += VC) {
-        for (int e = tid; e < K * VC; e += BT) {
-            const int d = e / VC, vv = e % VC;
-            hL[d * LV + vv] = hC[(size_t)d * V + vb + vv];
-            dhL[d * LV + vv] = dhC[(size_t)d * V + vb + vv];
-        }
-        for (int e = tid; e < C * VC; e += BT) {
-            const int r = e / VC, vv = e % VC;
-            doL[r * LV + vv] = r < pos.y ? to_f32(dout[((size_t)(pos.x + r) * p.HV + hv) * V + vb + vv]) : 0.f;
-            vnL[r * LV + vv] = vnC[(size_t)r * V + vb + vv];
-            dvL[r * LV + vv] = dvC[(size_t)r * V + vb + vv];
-        }
+        stage_f32<K, VC>(hC + vb, V, hL, LV, tid);
+        stage_f32<K, VC>(dhC + vb, V, dhL, LV, tid);
+        stage_rows<C, VC>(dout + ((size_t)pos.x * p.HV + hv) * V + vb, (size_t)p.HV * V, pos.y, doL, LV, tid);
+        stage_f32<C, VC>(vnC + vb, V, vnL, LV, tid);
+        stage_f32<C, VC>(dvC + vb, V, dvL, LV, tid);
         __syncthreads();
         if (tid < K)
             for (int vv = 0; vv < VC; ++vv) dgacc = fmaf(dhL[tid * LV + vv], hL[tid * LV + vv], dgacc);
@@ -482,13 +512,8 @@ __global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
     const int r0 = 16 * wave;
 
     // ---- loads and the chunk-local cumsum of g ----
-    for (int e = tid; e < C * K; e += BT) {
-        const int r = e / K, d = e % K;
-        const bool live = r < len;
-        const size_t row = (size_t)(pos.x + r);
-        kL[r * LK + d] = live ? to_f32(kin[(row * p.H + h) * K + d]) : 0.f;
-        XL[r * LX + d] = live ? p.g[(row * p.HV + hv) * K + d] : 0.f;
-    }
+    stage_rows<C, K>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
+    stage_rows<C, K>(p.g + ((size_t)pos.x * p.HV + hv) * K, (size_t)p.HV * K, len, XL, LX, tid);
     if (tid < C) {
         bL[tid] = tid < len ? to_f32(bin[(size_t)(pos.x + tid) * p.HV + hv]) : 0.f;
         dbL[tid] = 0.f;
@@ -518,11 +543,8 @@ __global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
     __syncthreads();
     // ---- value side: dv = beta T^T dv', dbeta += rowsum((T^T dv') v), dT = dv' (beta v)^T ----
     const float* dvC = p.dvn + ci * (size_t)C * V;
-    for (int e = tid; e < C * V; e += BT) {
-        const int r = e / V, vv = e % V;
-        XL[r * LX + vv] = dvC[(size_t)r * V + vv];
-        YL[r * LY + vv] = r < len ? to_f32(vin[((size_t)(pos.x + r) * p.HV + hv) * V + vv]) : 0.f;
-    }
+    stage_f32<C, V>(dvC, V, XL, LX, tid);
+    stage_rows<C, V>(vin + ((size_t)pos.x * p.HV + hv) * V, (size_t)p.HV * V, len, YL, LY, tid);
     __syncthreads();
     TIn* dvout = reinterpret_cast<TIn*>(p.dv);
     {
@@ -555,10 +577,7 @@ __global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
     __syncthreads();
     // ---- key side: dkd = beta T^T dw, dbeta += rowsum((T^T dw) kd), dT += dw (beta kd)^T ----
     const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
-    for (int e = tid; e < C * K; e += BT) {
-        const int r = e / K, d = e % K;
-        XL[r * LX + d] = gsC[GL::DW + r * K + d];
-    }
+    stage_f32<C, K>(gsC + GL::DW, K, XL, LX, tid);
     __syncthreads();
     float* wyC = p.wy + ci * (size_t)WL::FLOATS;
     {
@@ -641,7 +660,7 @@ __global__ __launch_bounds__(BT, 1) void bwd_pair_kernel(BwdParams p) {
     __shared__ float qL[C * LK];     // q, then dGamma
     __shared__ float kL[C * LK];
     __shared__ float GmL[C * LK];    // Gamma
-    __shared__ float dAL[C * LA];    // scale dAqk (s <= r)
+    __shared__ float dAL[C * LA];    // dAqk (s <= r)
     __shared__ float dML[C * LA];    // dM (s < r)
     __shared__ float dGL[K];
     const int tid = threadIdx.x;
@@ -656,19 +675,11 @@ __global__ __launch_bounds__(BT, 1) void bwd_pair_kernel(BwdParams p) {
     const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
     const float* wyC = p.wy + ci * (size_t)WL::FLOATS;
 
-    for (int e = tid; e < C * K; e += BT) {
-        const int r = e / K, d = e % K;
-        const bool live = r < len;
-        const size_t row = (size_t)(pos.x + r);
-        qL[r * LK + d] = live ? to_f32(qin[(row * p.H + h) * K + d]) : 0.f;
-        kL[r * LK + d] = live ? to_f32(kin[(row * p.H + h) * K + d]) : 0.f;
-        GmL[r * LK + d] = live ? p.g[(row * p.HV + hv) * K + d] : 0.f;
-    }
-    for (int e = tid; e < C * C; e += BT) {
-        const int r = e / C, s = e % C;
-        dAL[r * LA + s] = p.scale * gsC[GL::DA + e];
-        dML[r * LA + s] = wyC[WL::DM + e];
-    }
+    stage_rows<C, K>(qin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, qL, LK, tid);
+    stage_rows<C, K>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
+    stage_rows<C, K>(p.g + ((size_t)pos.x * p.HV + hv) * K, (size_t)p.HV * K, len, GmL, LK, tid);
+    stage_f32<C, C>(gsC + GL::DA, C, dAL, LA, tid);   // dAqk (the scale is applied at use)
+    stage_f32<C, C>(wyC + WL::DM, C, dML, LA, tid);
     if (tid < K) dGL[tid] = gsC[GL::DG + tid];
     __syncthreads();
     if (tid < K) {
@@ -686,7 +697,7 @@ __global__ __launch_bounds__(BT, 1) void bwd_pair_kernel(BwdParams p) {
     }
     // row side: s <= r
     for (int s = 0; s <= r; ++s) {
-        const float a = dAL[r * LA + s], m = dML[r * LA + s];
+        const float a = p.scale * dAL[r * LA + s], m = dML[r * LA + s];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int d = dg4 + 4 * j;
@@ -697,7 +708,7 @@ __global__ __launch_bounds__(BT, 1) void bwd_pair_kernel(BwdParams p) {
     }
     // column side: r2 >= r
     for (int r2 = r; r2 < C; ++r2) {
-        const float a = dAL[r2 * LA + r], m = dML[r2 * LA + r];
+        const float a = p.scale * dAL[r2 * LA + r], m = dML[r2 * LA + r];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int d = dg4 + 4 * j;
