@@ -95,11 +95,11 @@ __device__ __forceinline__ void stage_record(const TW* t, bool split, float* dst
 
 // Rows [0, R) x columns [0, W) of a row-major fp32 array (row stride `gstride` floats)
 // into LDS dst[r * ld + c]; 16-byte loads, several in flight per thread.
-template <int R, int W>
+template <int R, int W, int NTH = BT>
 __device__ __forceinline__ void stage_f32(const float* src, size_t gstride, float* dst, int ld, int tid) {
     constexpr int W4 = W / 4;
 #pragma unroll 4
-    for (int q = tid; q < R * W4; q += BT) {
+    for (int q = tid; q < R * W4; q += NTH) {
         const int r = q / W4, c4 = 4 * (q % W4);
         const f32x4 x = *reinterpret_cast<const f32x4*>(src + (size_t)r * gstride + c4);
 #pragma unroll
@@ -109,11 +109,11 @@ __device__ __forceinline__ void stage_f32(const float* src, size_t gstride, floa
 
 // Rows of an input tensor as fp32 into LDS: row r at src + r * rstride (W contiguous
 // elements of T), zeros from row `len` on.
-template <int R, int W, typename T>
+template <int R, int W, typename T, int NTH = BT>
 __device__ __forceinline__ void stage_rows(const T* src, size_t rstride, int len, float* dst, int ld, int tid) {
     constexpr int W4 = W / 4;
 #pragma unroll 4
-    for (int q = tid; q < R * W4; q += BT) {
+    for (int q = tid; q < R * W4; q += NTH) {
         const int r = q / W4, c4 = 4 * (q % W4);
         float x[4] = {0.f, 0.f, 0.f, 0.f};
         if (r < len) {
@@ -648,13 +648,22 @@ __global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------------------------
 // pair terms and the elementwise ones, per (chunk, value head): dq, dk (per value head,
-// summed later) and dg (the chunk-local reverse cumsum of dGamma). Thread (r, d = dg4 +
-// 4 j) sweeps the row side (s <= r) and the column side (r' >= r) of row r; every
-// factor is one one-sided 2^(Gamma_r - Gamma_s) <= 1.
+// summed later) and dg (the chunk-local reverse cumsum of dGamma).
+//   row side    dq_r  = sum_(s<=r) scale dAqk[r,s] k_s e(r,s),  dkr_r = sum_(s<r) dM[r,s] k_s e(r,s)
+//   column side dkc_s = sum_(r>=s) (scale dAqk[r,s] q_r + dM[r,s] k_r) e(r,s)
+// with e(r,s) = 2^(Gamma_r - Gamma_s) per channel. Pairs in different 16-row blocks run on
+// the matrix cores, factored through a boundary row between them (both factors <= 1): the
+// row side of block I through row 16I - 1, the column side of block J through row
+// 16J + 15. Pairs inside a block keep one one-sided factor each. Wave w owns channel
+// tile w (K / 16 waves); each lane holds its results in the matrix-core layout (rows
+// 16I + 4lq .. +3 of channel 16w + lr) through the elementwise step.
 // ------------------------------------------------------------------------------------
+template <int K>
+constexpr int pair_threads() { return 4 * K; }   // one wave per 16-channel tile
+
 template <int K, int V, typename TIn>
-__global__ __launch_bounds__(BT, 1) void bwd_pair_kernel(BwdParams p) {
-    constexpr int LA = C + 1, LK = K + 1, NJ = K / 4;
+__global__ __launch_bounds__(4 * K, 1) void bwd_pair_kernel(BwdParams p) {
+    constexpr int LA = C + 1, LK = K + 1, NDW = 1, NTH = pair_threads<K>();
     typedef GsLayout<K> GL;
     typedef WyLayout<K> WL;
     __shared__ float qL[C * LK];     // q, then dGamma
@@ -663,7 +672,8 @@ __global__ __launch_bounds__(BT, 1) void bwd_pair_kernel(BwdParams p) {
     __shared__ float dAL[C * LA];    // dAqk (s <= r)
     __shared__ float dML[C * LA];    // dM (s < r)
     __shared__ float dGL[K];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int c, hv;
     int2 pos;
     if (!bwd_chunk(p, c, hv, pos)) return;
@@ -674,12 +684,13 @@ __global__ __launch_bounds__(BT, 1) void bwd_pair_kernel(BwdParams p) {
     const TIn* kin = reinterpret_cast<const TIn*>(p.k);
     const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
     const float* wyC = p.wy + ci * (size_t)WL::FLOATS;
+    const float sc = p.scale;
 
-    stage_rows<C, K>(qin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, qL, LK, tid);
-    stage_rows<C, K>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
-    stage_rows<C, K>(p.g + ((size_t)pos.x * p.HV + hv) * K, (size_t)p.HV * K, len, GmL, LK, tid);
-    stage_f32<C, C>(gsC + GL::DA, C, dAL, LA, tid);   // dAqk (the scale is applied at use)
-    stage_f32<C, C>(wyC + WL::DM, C, dML, LA, tid);
+    stage_rows<C, K, TIn, NTH>(qin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, qL, LK, tid);
+    stage_rows<C, K, TIn, NTH>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
+    stage_rows<C, K, float, NTH>(p.g + ((size_t)pos.x * p.HV + hv) * K, (size_t)p.HV * K, len, GmL, LK, tid);
+    stage_f32<C, C, NTH>(gsC + GL::DA, C, dAL, LA, tid);   // dAqk (the scale is applied at use)
+    stage_f32<C, C, NTH>(wyC + WL::DM, C, dML, LA, tid);
     if (tid < K) dGL[tid] = gsC[GL::DG + tid];
     __syncthreads();
     if (tid < K) {
@@ -688,63 +699,131 @@ __global__ __launch_bounds__(BT, 1) void bwd_pair_kernel(BwdParams p) {
     }
     __syncthreads();
 
-    const int r = tid >> 2, dg4 = tid & 3;
-    float gr[NJ], dqi[NJ], dkr[NJ], dkc[NJ];
+    f32x4 aq[NDW][4], akr[NDW][4], akc[NDW][4];   // [channel tile][row block]
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        gr[j] = GmL[r * LK + dg4 + 4 * j];
-        dqi[j] = 0.f; dkr[j] = 0.f; dkc[j] = 0.f;
-    }
-    // row side: s <= r
-    for (int s = 0; s <= r; ++s) {
-        const float a = p.scale * dAL[r * LA + s], m = dML[r * LA + s];
+    for (int t = 0; t < NDW; ++t)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int d = dg4 + 4 * j;
-            const float ek = kL[s * LK + d] * exp2_fast(gr[j] - GmL[s * LK + d]);
-            dqi[j] = fmaf(a, ek, dqi[j]);
-            dkr[j] = fmaf(m, ek, dkr[j]);
+        for (int I = 0; I < 4; ++I) {
+            aq[t][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+            akr[t][I] = aq[t][I];
+            akc[t][I] = aq[t][I];
+        }
+#pragma unroll
+    for (int t = 0; t < NDW; ++t) {
+        const int d = 16 * (wave + t) + lr;
+        // row side, pairs across blocks: block I against rows s < 16I, through row 16I - 1
+#pragma unroll
+        for (int I = 1; I < 4; ++I) {
+            const float P = GmL[(16 * I - 1) * LK + d];
+            f32x4 yq = {0.f, 0.f, 0.f, 0.f}, yk = {0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < 16 * I; s0 += 4) {
+                const int s = s0 + lq;
+                const float b = kL[s * LK + d] * exp2_fast(P - GmL[s * LK + d]);
+                yq = __builtin_amdgcn_mfma_f32_16x16x4f32(sc * dAL[(16 * I + lr) * LA + s], b, yq, 0, 0, 0);
+                yk = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[(16 * I + lr) * LA + s], b, yk, 0, 0, 0);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const float f = exp2_fast(GmL[(16 * I + 4 * lq + rr) * LK + d] - P);
+                aq[t][I][rr] = fmaf(f, yq[rr], aq[t][I][rr]);
+                akr[t][I][rr] = fmaf(f, yk[rr], akr[t][I][rr]);
+            }
+        }
+        // column side, pairs across blocks: block J against rows r >= 16J + 16, through
+        // row 16J + 15
+#pragma unroll
+        for (int J = 0; J < 3; ++J) {
+            const float Q = GmL[(16 * J + 15) * LK + d];
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            for (int r0 = 16 * (J + 1); r0 < C; r0 += 4) {
+                const int r = r0 + lq;
+                const float e = exp2_fast(GmL[r * LK + d] - Q);
+                z = __builtin_amdgcn_mfma_f32_16x16x4f32(sc * dAL[r * LA + 16 * J + lr], qL[r * LK + d] * e, z, 0, 0, 0);
+                z = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[r * LA + 16 * J + lr], kL[r * LK + d] * e, z, 0, 0, 0);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const float f = exp2_fast(Q - GmL[(16 * J + 4 * lq + rr) * LK + d]);
+                akc[t][J][rr] = fmaf(f, z[rr], akc[t][J][rr]);
+            }
+        }
+        // pairs inside a block: one one-sided factor each. All 16 rows of the block are
+        // visited (fixed trip counts, fully unrolled); pairs on the wrong side of the
+        // diagonal meet a zero dAqk / dM, and their exponent is clamped at 0 so nothing
+        // overflows.
+#pragma unroll 1
+        for (int I = 0; I < 4; ++I) {
+            float kb[16], qb[16], gb[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                kb[j] = kL[(16 * I + j) * LK + d];
+                qb[j] = qL[(16 * I + j) * LK + d];
+                gb[j] = GmL[(16 * I + j) * LK + d];
+            }
+            f32x4 xq4, xk4, xc4;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 16 * I + 4 * lq + rr;
+                const float gr = GmL[r * LK + d];
+                float xq = 0.f, xk = 0.f, xc = 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int s = 16 * I + j;
+                    const float er = exp2_fast(fminf(gr - gb[j], 0.f));   // row side: s <= r
+                    const float ec = exp2_fast(fminf(gb[j] - gr, 0.f));   // column side: s >= r
+                    const float ek = kb[j] * er;
+                    xq = fmaf(dAL[r * LA + s], ek, xq);
+                    xk = fmaf(dML[r * LA + s], ek, xk);
+                    xc = fmaf(fmaf(sc * dAL[s * LA + r], qb[j], dML[s * LA + r] * kb[j]), ec, xc);
+                }
+                xq4[rr] = sc * xq;
+                xk4[rr] = xk;
+                xc4[rr] = xc;
+            }
+#pragma unroll
+            for (int Ib = 0; Ib < 4; ++Ib)
+                if (Ib == I) { aq[t][Ib] += xq4; akr[t][Ib] += xk4; akc[t][Ib] += xc4; }
         }
     }
-    // column side: r2 >= r
-    for (int r2 = r; r2 < C; ++r2) {
-        const float a = p.scale * dAL[r2 * LA + r], m = dML[r2 * LA + r];
+    // elementwise terms of qg, kd, kg; dGamma; dq, dk per value head
+    float dgam[NDW][4][4];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int d = dg4 + 4 * j;
-            const float e = exp2_fast(GmL[r2 * LK + d] - gr[j]);
-            dkc[j] = fmaf(fmaf(a, qL[r2 * LK + d], m * kL[r2 * LK + d]), e, dkc[j]);
-        }
-    }
-    // elementwise terms of qg, kd, kg; dGamma
-    float qv[NJ], kv[NJ];
+    for (int t = 0; t < NDW; ++t) {
+        const int d = 16 * (wave + t) + lr;
+        const float Gd = GmL[(C - 1) * LK + d];
+        float dgk = 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        qv[j] = qL[r * LK + dg4 + 4 * j];
-        kv[j] = kL[r * LK + dg4 + 4 * j];
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 16 * I + 4 * lq + rr;
+                const float qv = qL[r * LK + d], kv = kL[r * LK + d], gr = GmL[r * LK + d];
+                const float e1 = exp2_fast(gr), e2 = exp2_fast(Gd - gr);
+                const float dqg = gsC[GL::DQG + r * K + d];
+                const float dkg = gsC[GL::DKG + r * K + d];
+                const float dkd = wyC[WL::DKD + r * K + d];
+                const float dqi = aq[t][I][rr], dkr = akr[t][I][rr], dkc = akc[t][I][rr];
+                const float dq = fmaf(sc * e1, dqg, dqi);
+                const float dk = dkr + dkc + e1 * dkd + e2 * dkg;
+                const float kge = kv * e2 * dkg;
+                dgam[t][I][rr] = LN2F * (qv * dq + kv * (dkr - dkc + e1 * dkd) - kge);
+                if (r < len) {
+                    dgk += kge;
+                    const size_t row = (size_t)(pos.x + r);
+                    p.dq_hv[(row * p.HV + hv) * K + d] = dq;
+                    p.dk_hv[(row * p.HV + hv) * K + d] = dk;
+                }
+            }
+        atomicAdd(&dGL[d], LN2F * dgk);
     }
     __syncthreads();   // qL becomes dGamma
-    const bool live = r < len;
-    const size_t row = (size_t)(pos.x + r);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int d = dg4 + 4 * j;
-        const float Gd = GmL[(C - 1) * LK + d];
-        const float e1 = exp2_fast(gr[j]), e2 = exp2_fast(Gd - gr[j]);
-        const float dqg = gsC[GL::DQG + r * K + d];
-        const float dkg = gsC[GL::DKG + r * K + d];
-        const float dkd = wyC[WL::DKD + r * K + d];
-        const float dq = fmaf(p.scale * e1, dqg, dqi[j]);
-        const float dk = dkr[j] + dkc[j] + e1 * dkd + e2 * dkg;
-        const float kge = kv[j] * e2 * dkg;
-        const float dgam = LN2F * (qv[j] * (dqi[j] + p.scale * e1 * dqg) + kv[j] * (dkr[j] - dkc[j] + e1 * dkd) - kge);
-        qL[r * LK + d] = dgam;
-        if (live) atomicAdd(&dGL[d], LN2F * kge);
-        if (live) {
-            p.dq_hv[(row * p.HV + hv) * K + d] = dq;
-            p.dk_hv[(row * p.HV + hv) * K + d] = dk;
-        }
-    }
+    for (int t = 0; t < NDW; ++t)
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                qL[(16 * I + 4 * lq + rr) * LK + 16 * (wave + t) + lr] = dgam[t][I][rr];
     __syncthreads();
     // dg = reverse cumsum of dGamma over the chunk's rows; dG joins at the last row
     if (tid < K && len > 0) {
@@ -848,7 +927,8 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL((bwd_pair_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
+        hipLaunchKernelGGL((bwd_pair_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(pair_threads<K>()), 0,
+                           a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((bwd_reduce_kernel<K, TIn>), dim3((unsigned)((long long)L.fwd.NCmax * a.H)), dim3(BT), 0,
                            a.stream, p);
