@@ -483,10 +483,15 @@ __global__ __launch_bounds__(BT, 2) void bwd_state_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------------------------
 // backward of the WY inverse, per (chunk, value head): with M and T from the recompute,
-// writes dv and dbeta (final) and dkd, dM for the pair kernel.
+// writes dv and dbeta (final) and dkd, dM for the pair kernel. Eight waves; every product
+// is split into 16x16 output tiles dealt round-robin to the waves, and the row sums
+// that make dbeta are added into LDS.
 // ------------------------------------------------------------------------------------
+constexpr int WY_THREADS = 512;
+
 template <int K, int V, typename TIn, typename TB>
-__global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
+__global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
+    constexpr int NTH = WY_THREADS, NW = NTH / 64;
     constexpr int LA = C + 1, LK = K + 1, LX = (K > V ? K : V) + 1, LY = (V > C ? V : C) + 1;
     typedef GsLayout<K> GL;
     typedef WyLayout<K> WL;
@@ -509,11 +514,10 @@ __global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
     const TIn* kin = reinterpret_cast<const TIn*>(p.k);
     const TIn* vin = reinterpret_cast<const TIn*>(p.v);
     const TB* bin = reinterpret_cast<const TB*>(p.beta);
-    const int r0 = 16 * wave;
 
     // ---- loads and the chunk-local cumsum of g ----
-    stage_rows<C, K>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
-    stage_rows<C, K>(p.g + ((size_t)pos.x * p.HV + hv) * K, (size_t)p.HV * K, len, XL, LX, tid);
+    stage_rows<C, K, TIn, NTH>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
+    stage_rows<C, K, float, NTH>(p.g + ((size_t)pos.x * p.HV + hv) * K, (size_t)p.HV * K, len, XL, LX, tid);
     if (tid < C) {
         bL[tid] = tid < len ? to_f32(bin[(size_t)(pos.x + tid) * p.HV + hv]) : 0.f;
         dbL[tid] = 0.f;
@@ -525,122 +529,118 @@ __global__ __launch_bounds__(BT, 1) void bwd_wy_kernel(BwdParams p) {
     }
     __syncthreads();
     // kd = k 2^Gamma; M and T = (I + diag(beta) M)^-1 as Stage 2 of the recompute left them
-    for (int e = tid; e < C * K; e += BT) {
+    for (int e = tid; e < C * K; e += NTH) {
         const int r = e / K, d = e % K;
         kL[r * LK + d] *= exp2_fast(XL[r * LX + d]);
     }
     {
         const float* Mg = p.mt + ci * (size_t)(C * C);
         const float* Tg = p.mt + ((size_t)p.NCmax * p.HV + ci) * (C * C);
-        for (int e = tid; e < C * C / 4; e += BT) {
-            const int r = e / (C / 4), s4 = 4 * (e % (C / 4));
-            const f32x4 m = *reinterpret_cast<const f32x4*>(Mg + r * C + s4);
-            const f32x4 t = *reinterpret_cast<const f32x4*>(Tg + r * C + s4);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) { ML[r * LA + s4 + x] = m[x]; TL[r * LA + s4 + x] = t[x]; }
-        }
+        stage_f32<C, C, NTH>(Mg, C, ML, LA, tid);
+        stage_f32<C, C, NTH>(Tg, C, TL, LA, tid);
     }
     __syncthreads();
-    // ---- value side: dv = beta T^T dv', dbeta += rowsum((T^T dv') v), dT = dv' (beta v)^T ----
-    const float* dvC = p.dvn + ci * (size_t)C * V;
-    stage_f32<C, V>(dvC, V, XL, LX, tid);
-    stage_rows<C, V>(vin + ((size_t)pos.x * p.HV + hv) * V, (size_t)p.HV * V, len, YL, LY, tid);
-    __syncthreads();
-    TIn* dvout = reinterpret_cast<TIn*>(p.dv);
-    {
-        float db[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int nt = 0; nt < V / 16; ++nt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_f32(acc, [&](int i, int k) { return TL[k * LA + r0 + i]; },
-                          [&](int j, int k) { return XL[k * LX + 16 * nt + j]; }, C, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s = r0 + 4 * lq + r, vv = 16 * nt + lr;
-                db[r] = fmaf(acc[r], YL[s * LY + vv], db[r]);
-                if (s < len) dvout[((size_t)(pos.x + s) * p.HV + hv) * V + vv] = from_f32<TIn>(bL[s] * acc[r]);
-            }
-        }
+    // row sums over one tile's columns (the 16 lanes of a row), added into dbL
+    auto add_rows = [&](int row0, const float (&x)[4]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float x = sum16(db[r]);
-            if (lr == 0) dbL[r0 + 4 * lq + r] += x;
+            const float y = sum16(x[r]);
+            if (lr == 0) atomicAdd(&dbL[row0 + 4 * lq + r], y);
         }
-    }
-    f32x4 dT[4];
+    };
+    // dT tiles (I, J) owned by this wave: t = wave + NW i, I = t / 4, J = t % 4
+    constexpr int NT_DT = 16 / NW;
+    f32x4 dT[NT_DT];
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-        dT[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (J <= wave)
-            dT[J] = mma_f32(dT[J], [&](int i, int k) { return XL[(r0 + i) * LX + k]; },
+    for (int i = 0; i < NT_DT; ++i) dT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- value side: dv = beta T^T dv', dbeta += rowsum((T^T dv') v), dT = dv' (beta v)^T ----
+    const float* dvC = p.dvn + ci * (size_t)C * V;
+    stage_f32<C, V, NTH>(dvC, V, XL, LX, tid);
+    stage_rows<C, V, TIn, NTH>(vin + ((size_t)pos.x * p.HV + hv) * V, (size_t)p.HV * V, len, YL, LY, tid);
+    __syncthreads();
+    TIn* dvout = reinterpret_cast<TIn*>(p.dv);
+    for (int t = wave; t < 4 * (V / 16); t += NW) {
+        const int sb = t / (V / 16), nt = t % (V / 16);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_f32(acc, [&](int i, int k) { return TL[k * LA + 16 * sb + i]; },
+                      [&](int j, int k) { return XL[k * LX + 16 * nt + j]; }, C, lane);
+        float db[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int s = 16 * sb + 4 * lq + r, vv = 16 * nt + lr;
+            db[r] = acc[r] * YL[s * LY + vv];
+            if (s < len) dvout[((size_t)(pos.x + s) * p.HV + hv) * V + vv] = from_f32<TIn>(bL[s] * acc[r]);
+        }
+        add_rows(16 * sb, db);
+    }
+#pragma unroll
+    for (int i = 0; i < NT_DT; ++i) {
+        const int t = wave + NW * i, I = t / 4, J = t % 4;
+        if (J <= I)
+            dT[i] = mma_f32(dT[i], [&](int ii, int k) { return XL[(16 * I + ii) * LX + k]; },
                             [&](int j, int k) { return bL[16 * J + j] * YL[(16 * J + j) * LY + k]; }, V, lane);
     }
     __syncthreads();
     // ---- key side: dkd = beta T^T dw, dbeta += rowsum((T^T dw) kd), dT += dw (beta kd)^T ----
     const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
-    stage_f32<C, K>(gsC + GL::DW, K, XL, LX, tid);
+    stage_f32<C, K, NTH>(gsC + GL::DW, K, XL, LX, tid);
     __syncthreads();
     float* wyC = p.wy + ci * (size_t)WL::FLOATS;
-    {
-        float db[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int nt = 0; nt < K / 16; ++nt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_f32(acc, [&](int i, int k) { return TL[k * LA + r0 + i]; },
-                          [&](int j, int k) { return XL[k * LX + 16 * nt + j]; }, C, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s = r0 + 4 * lq + r, d = 16 * nt + lr;
-                db[r] = fmaf(acc[r], kL[s * LK + d], db[r]);
-                wyC[WL::DKD + s * K + d] = bL[s] * acc[r];
-            }
-        }
+    for (int t = wave; t < 4 * (K / 16); t += NW) {
+        const int sb = t / (K / 16), nt = t % (K / 16);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_f32(acc, [&](int i, int k) { return TL[k * LA + 16 * sb + i]; },
+                      [&](int j, int k) { return XL[k * LX + 16 * nt + j]; }, C, lane);
+        float db[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float x = sum16(db[r]);
-            if (lr == 0) dbL[r0 + 4 * lq + r] += x;
+            const int s = 16 * sb + 4 * lq + r, d = 16 * nt + lr;
+            db[r] = acc[r] * kL[s * LK + d];
+            wyC[WL::DKD + s * K + d] = bL[s] * acc[r];
         }
+        add_rows(16 * sb, db);
     }
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-        if (J <= wave)
-            dT[J] = mma_f32(dT[J], [&](int i, int k) { return XL[(r0 + i) * LX + k]; },
+    for (int i = 0; i < NT_DT; ++i) {
+        const int t = wave + NW * i, I = t / 4, J = t % 4;
+        if (J <= I)
+            dT[i] = mma_f32(dT[i], [&](int ii, int k) { return XL[(16 * I + ii) * LX + k]; },
                             [&](int j, int k) { return bL[16 * J + j] * kL[(16 * J + j) * LK + k]; }, K, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = r0 + 4 * lq + r, s = 16 * J + lr;
-            dTL[row * LA + s] = (J <= wave && s < row) ? dT[J][r] : 0.f;
+            const int row = 16 * I + 4 * lq + r, s = 16 * J + lr;
+            dTL[row * LA + s] = (J <= I && s < row) ? dT[i][r] : 0.f;
         }
     }
     __syncthreads();
     // ---- X = T^T dT (all tiles), then dL = -(X T^T) strictly lower ----
-    for (int J = 0; J < 4; ++J) {
+#pragma unroll
+    for (int i = 0; i < NT_DT; ++i) {
+        const int t = wave + NW * i, I = t / 4, J = t % 4;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        x = mma_f32(x, [&](int i, int k) { return TL[k * LA + r0 + i]; },
+        x = mma_f32(x, [&](int ii, int k) { return TL[k * LA + 16 * I + ii]; },
                     [&](int j, int k) { return dTL[k * LA + 16 * J + j]; }, C, lane);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) YL[(r0 + 4 * lq + r) * LY + 16 * J + lr] = x[r];
+        for (int r = 0; r < 4; ++r) YL[(16 * I + 4 * lq + r) * LY + 16 * J + lr] = x[r];
     }
     __syncthreads();
-    {
-        float db[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            if (J <= wave)
-                x = mma_f32(x, [&](int i, int k) { return YL[(r0 + i) * LY + k]; },
-                            [&](int j, int k) { return TL[(16 * J + j) * LA + k]; }, C, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = r0 + 4 * lq + r, s = 16 * J + lr;
-                const float dl = (J <= wave && s < row) ? -x[r] : 0.f;
-                db[r] = fmaf(dl, ML[row * LA + s], db[r]);
-                wyC[WL::DM + row * C + s] = bL[row] * dl;
-            }
-        }
+    for (int i = 0; i < NT_DT; ++i) {
+        const int t = wave + NW * i, I = t / 4, J = t % 4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (J <= I)
+            x = mma_f32(x, [&](int ii, int k) { return YL[(16 * I + ii) * LY + k]; },
+                        [&](int j, int k) { return TL[(16 * J + j) * LA + k]; }, C, lane);
+        float db[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float x = sum16(db[r]);
-            if (lr == 0) dbL[r0 + 4 * lq + r] += x;
+            const int row = 16 * I + 4 * lq + r, s = 16 * J + lr;
+            const float dl = (J <= I && s < row) ? -x[r] : 0.f;
+            db[r] = dl * ML[row * LA + s];
+            wyC[WL::DM + row * C + s] = bL[row] * dl;
         }
+        add_rows(16 * I, db);
     }
     __syncthreads();
     if (tid < len) reinterpret_cast<TB*>(p.dbeta)[(size_t)(pos.x + tid) * p.HV + hv] = from_f32<TB>(dbL[tid]);
@@ -925,7 +925,7 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
     if (nchunk_items > 0) {
         hipLaunchKernelGGL((bwd_state_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
+        hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(WY_THREADS), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((bwd_pair_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(pair_threads<K>()), 0,
                            a.stream, p);
