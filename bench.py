@@ -87,7 +87,7 @@ def record_bytes(K, V, elem):
 
 def source_hash():
     h = hashlib.sha256()
-    for f in ("kda_chunk.hip", "kda_device.h"):
+    for f in ("kda_chunk.hip", "kda_chunk_common.h", "kda_device.h"):
         h.update(open(os.path.join(ROOT, "gated_delta_rule_64_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
