@@ -31,6 +31,8 @@ from ._lib import (  # noqa: F401
     KDA_PRE_L2NORM_K,
     KDA_PRE_L2NORM_Q,
     KDA_PRE_NEG_EIGVAL,
+    KDA_STATE_KV,
+    KDA_STATE_VK,
     KdaError,
     kda_chunk_bwd,
     kda_chunk_bwd_workspace_bytes,
@@ -50,5 +52,5 @@ __all__ = [
     "kda_recurrent_fwd_ex", "kda_chunk_fwd_workspace_bytes",
     "kda_last_error", "KdaError", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
     "library_path", "KDA_GATE_LOG2", "KDA_GATE_RAW_F32", "KDA_GATE_RAW_BF16", "KDA_PRE_L2NORM_Q",
-    "KDA_PRE_L2NORM_K", "KDA_PRE_BETA_SIGMOID", "KDA_PRE_NEG_EIGVAL",
+    "KDA_PRE_L2NORM_K", "KDA_PRE_BETA_SIGMOID", "KDA_PRE_NEG_EIGVAL", "KDA_STATE_KV", "KDA_STATE_VK",
 ]

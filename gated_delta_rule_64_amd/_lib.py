@@ -20,6 +20,8 @@ KDA_PRE_L2NORM_Q = 1
 KDA_PRE_L2NORM_K = 2
 KDA_PRE_BETA_SIGMOID = 4
 KDA_PRE_NEG_EIGVAL = 8
+KDA_STATE_KV = 0
+KDA_STATE_VK = 1
 
 _lock = threading.Lock()
 _lib = None
@@ -62,9 +64,9 @@ def load_library():
                                          i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                          f32, i32, vp, sz, vp, vp, vp]
         lib.kda_recurrent_fwd_ex.restype = i32
-        lib.kda_recurrent_fwd_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp,
-                                             vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                                             i32, f32, vp, vp]
+        lib.kda_recurrent_fwd_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, i32,
+                                             vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
+                                             i32, i32, i32, f32, vp, vp]
         lib.kda_chunk_bwd.restype = i32
         lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
@@ -330,29 +332,50 @@ def kda_recurrent_fwd_ex(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
                          output_final_state=False, scale=None, *, use_gate_in_kernel=False,
                          A_log=None, dt_bias=None, lower_bound=None,
                          use_qk_l2norm_in_kernel=False, l2norm_q=None, l2norm_k=None,
-                         use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False, out=None,
-                         final_state=None, dev_status=None):
-    """Per-token recurrent KDA forward with the options of ``kda_chunk_fwd_ex``."""
+                         use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False,
+                         state_layout="kv", output_intermediate_states=False, out=None,
+                         final_state=None, intermediate_states=None, dev_status=None):
+    """Per-token recurrent KDA forward with every decode option: those of
+    ``kda_chunk_fwd_ex``, ``state_layout`` ("kv": states [N, HV, K, V]; "vk": [N, HV, V, K])
+    and ``output_intermediate_states`` (the state after every token, float32
+    [B*T, HV, K, V] or [B*T, HV, V, K] in the states' layout). Returns
+    ``(o, final_state or None)``, plus the intermediate states when requested."""
     lib = load_library()
-    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens,
+    if state_layout not in ("kv", "vk"):
+        raise ValueError("state_layout must be 'kv' or 'vk'")
+    vk = state_layout == "vk"
+    h0 = initial_state
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, None if vk else h0, cu_seqlens,
                                                   raw_gate=use_gate_in_kernel)
+    sshape = (N, HV, V, K) if vk else (N, HV, K, V)
+    if vk and h0 is not None:
+        if h0.dtype != torch.float32 or tuple(h0.shape) != sshape:
+            raise ValueError(f"initial_state must be float32 {list(sshape)}")
+        _check_device([("initial_state", h0)])
     gate, pre = _options(g, HV, K, use_gate_in_kernel, A_log, dt_bias, lower_bound,
                          use_qk_l2norm_in_kernel, l2norm_q, l2norm_k, use_beta_sigmoid_in_kernel,
                          allow_neg_eigval)
     if out is None:
         out = torch.empty_like(v)
     if output_final_state and final_state is None:
-        final_state = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev)
+        final_state = torch.empty(*sshape, dtype=torch.float32, device=dev)
     if not output_final_state:
         final_state = None
+    if output_intermediate_states and intermediate_states is None:
+        intermediate_states = torch.empty(B * T, HV, *sshape[2:], dtype=torch.float32, device=dev)
+    if not output_intermediate_states:
+        intermediate_states = None
     rc = lib.kda_recurrent_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), gate, _ptr(A_log),
                                   _ptr(dt_bias), int(lower_bound is not None),
                                   float(lower_bound if lower_bound is not None else 0.0),
-                                  _ptr(beta), pre, _ptr(initial_state), _ptr(cu_seqlens), N,
-                                  _ptr(out), _ptr(final_state), B, T, H, HV, K, V, qkv, bdt,
+                                  _ptr(beta), pre, KDA_STATE_VK if vk else KDA_STATE_KV, _ptr(h0),
+                                  _ptr(cu_seqlens), N, _ptr(out), _ptr(final_state),
+                                  _ptr(intermediate_states), B, T, H, HV, K, V, qkv, bdt,
                                   float(scale or 0.0), _ptr(dev_status), _stream(dev))
     if rc != 0:
         raise KdaError(rc, lib.kda_last_error().decode())
+    if output_intermediate_states:
+        return out, final_state, intermediate_states
     return out, final_state
 
 

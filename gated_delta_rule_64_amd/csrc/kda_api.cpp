@@ -142,10 +142,11 @@ int chunk_impl(const void* q, const void* k, const void* v, const void* g, int g
 // The per-token forward behind both recurrent entry points.
 int recurrent_impl(const void* q, const void* k, const void* v, const void* g, int gate,
                    const float* A_log, const float* dt_bias, int has_lower_bound,
-                   float lower_bound, const void* beta, int preprocess,
+                   float lower_bound, const void* beta, int preprocess, int state_layout,
                    const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
-                   float* final_state, int B, int T, int H, int HV, int K, int V, int qkv_dtype,
-                   int beta_dtype, float scale, int32_t* dev_status, hipStream_t stream) {
+                   float* final_state, float* inter_states, int B, int T, int H, int HV, int K,
+                   int V, int qkv_dtype, int beta_dtype, float scale, int32_t* dev_status,
+                   hipStream_t stream) {
     int rc = check_common(q, k, v, static_cast<const float*>(g), beta, initial_state, cu_seqlens, N,
                           o, final_state, B, T, H, HV, K, V, qkv_dtype, beta_dtype);
     if (rc != KDA_OK) return rc;
@@ -159,6 +160,10 @@ int recurrent_impl(const void* q, const void* k, const void* v, const void* g, i
         return fail(KDA_ERR_UNSUPPORTED, "V must be a multiple of 64, got %d", V);
     if ((long long)N * HV * (V / 64) > 0x7fffffffLL * 4LL)
         return fail(KDA_ERR_SHAPE, "grid too large");
+    if (state_layout != KDA_STATE_KV && state_layout != KDA_STATE_VK)
+        return fail(KDA_ERR_ARG, "state_layout must be KDA_STATE_KV (0) or KDA_STATE_VK (1), got %d", state_layout);
+    if (!aligned16(inter_states))
+        return fail(KDA_ERR_SHAPE, "intermediate_states must be 16-byte aligned");
     if (N == 0) return KDA_OK;
     kda::RecurrentArgs a;
     a.q = q; a.k = k; a.v = v; a.beta = beta;
@@ -170,6 +175,8 @@ int recurrent_impl(const void* q, const void* k, const void* v, const void* g, i
     a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype;
     a.scale = scale == 0.0f ? 1.0f / sqrtf((float)K) : scale;
     a.dev_status = dev_status; a.stream = stream;
+    a.state_vk = state_layout == KDA_STATE_VK ? 1 : 0;
+    a.inter_states = inter_states;
     hipError_t err = kda::launch_recurrent(a);
     if (err != hipSuccess)
         return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
@@ -321,21 +328,22 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* 
                       hipStream_t stream) {
     clear_error();
     return recurrent_impl(q, k, v, g, KDA_GATE_LOG2, nullptr, nullptr, 0, 0.0f, beta, 0,
-                          initial_state, cu_seqlens, N, o, final_state, B, T, H, HV, K, V,
-                          qkv_dtype, beta_dtype, scale, dev_status, stream);
+                          KDA_STATE_KV, initial_state, cu_seqlens, N, o, final_state, nullptr, B,
+                          T, H, HV, K, V, qkv_dtype, beta_dtype, scale, dev_status, stream);
 }
 
 int kda_recurrent_fwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
                          const float* A_log, const float* dt_bias, int has_lower_bound,
-                         float lower_bound, const void* beta, int preprocess,
+                         float lower_bound, const void* beta, int preprocess, int state_layout,
                          const float* initial_state, const int32_t* cu_seqlens, int N,
-                         void* o, float* final_state, int B, int T, int H, int HV, int K,
-                         int V, int qkv_dtype, int beta_dtype, float scale,
-                         int32_t* dev_status, hipStream_t stream) {
+                         void* o, float* final_state, float* intermediate_states, int B, int T,
+                         int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
+                         float scale, int32_t* dev_status, hipStream_t stream) {
     clear_error();
     return recurrent_impl(q, k, v, g, gate, A_log, dt_bias, has_lower_bound, lower_bound, beta,
-                          preprocess, initial_state, cu_seqlens, N, o, final_state, B, T, H, HV,
-                          K, V, qkv_dtype, beta_dtype, scale, dev_status, stream);
+                          preprocess, state_layout, initial_state, cu_seqlens, N, o, final_state,
+                          intermediate_states, B, T, H, HV, K, V, qkv_dtype, beta_dtype, scale,
+                          dev_status, stream);
 }
 
 }  // extern "C"

@@ -44,6 +44,8 @@ struct RecurrentArgs {
     float scale;
     int32_t* dev_status;
     hipStream_t stream;
+    int state_vk = 0;                // states [V][K] instead of [K][V]
+    float* inter_states = nullptr;   // [B*T][HV][K*V]: the state after every token, or NULL
 };
 
 struct ChunkArgs {

@@ -21,7 +21,9 @@
 // which is o = scale S_t^T q without a second pass over the state.
 //
 // The grid is flat and 1-D (four wavefronts per 256-thread block), so N * HV * V/64 may
-// exceed 65,535. Packed offsets are validated per slot on every call: a slot with
+// exceed 65,535. States may be laid out [K][V] or transposed, [V][K] (fla's state_v_first);
+// the state after every token can be written out as well (fla's
+// return_intermediate_states). Packed offsets are validated per slot on every call: a slot with
 // bos < 0, bos > eos, eos > T, or slot 0 not starting at 0, is skipped and flagged.
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -77,6 +79,43 @@ __device__ __forceinline__ float sum_row_groups(float x) {
     return x;
 }
 
+// The lane's block of a state (rows d0 .. d0+R-1, columns c0 .. c0+3) in either layout:
+// [K][V] (row d at base + d V) or, with vk, [V][K] (column c at base + c K); 16-byte
+// accesses in both.
+template <int R>
+__device__ __forceinline__ void load_state(const float* base, int K, int V, bool vk, int d0, int c0,
+                                           float (&S)[R][4]) {
+    if (!vk) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) load4(base + (size_t)(d0 + i) * V + c0, S[i]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < R; i += 4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(base + (size_t)(c0 + j) * K + d0 + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[i + e][j] = x[e];
+            }
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void store_state(float* base, int K, int V, bool vk, int d0, int c0,
+                                            const float (&S)[R][4]) {
+    if (!vk) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) store4(base + (size_t)(d0 + i) * V + c0, S[i]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < R; i += 4)
+                *reinterpret_cast<f32x4*>(base + (size_t)(c0 + j) * K + d0 + i) =
+                    f32x4{S[i][j], S[i + 1][j], S[i + 2][j], S[i + 3][j]};
+    }
+}
+
 template <int R>
 __device__ __forceinline__ void l2norm_rows(float (&x)[R]) {
     float ss = 0.f;
@@ -92,8 +131,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ g, const InputSpec in, const TB* __restrict__ beta,
     const float* initial_state, const int32_t* __restrict__ cu_seqlens,
-    TIn* __restrict__ o, float* final_state, int T, int H, int HV, int V, int nvt,
-    long long n_items, float scale, int32_t* dev_status) {
+    TIn* __restrict__ o, float* final_state, float* inter_states, int state_vk, int T, int H,
+    int HV, int V, int nvt, long long n_items, float scale, int32_t* dev_status) {
     constexpr int R = K / 4;  // rows per lane
     const int lane = threadIdx.x & 63;
     const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -129,9 +168,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     const size_t sbase = ((size_t)n * HV + hv) * (size_t)K * V;
     float S[R][4];
     if (initial_state) {
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-            load4(initial_state + sbase + (size_t)(d0 + i) * V + c0, S[i]);
+        load_state<R>(initial_state + sbase, K, V, state_vk, d0, c0, S);
     } else {
 #pragma unroll
         for (int i = 0; i < R; ++i)
@@ -200,13 +237,11 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) S[i][j] = fmaf(kk[i], delta[j], S[i][j]);
         if (rg == 0) store4(o + ((size_t)r * HV + hv) * V + c0, out);
+        // the state after this token, in the states' layout
+        if (inter_states) store_state<R>(inter_states + ((size_t)r * HV + hv) * (size_t)K * V, K, V, state_vk, d0, c0, S);
     }
 
-    if (final_state) {
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-            store4(final_state + sbase + (size_t)(d0 + i) * V + c0, S[i]);
-    }
+    if (final_state) store_state<R>(final_state + sbase, K, V, state_vk, d0, c0, S);
 }
 
 template <int K, typename TIn, typename TB>
@@ -218,7 +253,7 @@ hipError_t launch_t(const RecurrentArgs& a) {
     hipLaunchKernelGGL((recurrent_kernel<K, TIn, TB>), dim3((unsigned)blocks), dim3(256), 0,
                        a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.in,
                        (const TB*)a.beta, a.initial_state, a.cu_seqlens, (TIn*)a.o,
-                       a.final_state, a.T, a.H, a.HV, a.V, nvt, n_items, a.scale,
+                       a.final_state, a.inter_states, a.state_vk, a.T, a.H, a.HV, a.V, nvt, n_items, a.scale,
                        a.dev_status);
     return hipGetLastError();
 }

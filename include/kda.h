@@ -247,25 +247,38 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* 
                       int T, int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
                       float scale, int32_t* dev_status, hipStream_t stream);
 
+/* State layouts of the recurrent entry points (the `state_layout` argument). */
+enum kda_state_layout {
+    KDA_STATE_KV = 0,   /* [N, HV, K, V] (the default everywhere) */
+    KDA_STATE_VK = 1    /* [N, HV, V, K]: each state stored transposed */
+};
+
 /*
- * kda_recurrent_fwd with the gate source and the input preprocessing of kda_chunk_fwd_ex
- * (the same `gate`, A_log, dt_bias, has_lower_bound, lower_bound and `preprocess`
- * arguments and rules): the decode-side counterpart of the fused preprocessing.
+ * kda_recurrent_fwd with every decode option: the gate source and the input
+ * preprocessing of kda_chunk_fwd_ex (the same `gate`, A_log, dt_bias, has_lower_bound,
+ * lower_bound and `preprocess` arguments and rules), the layout of initial_state,
+ * final_state and intermediate_states (`state_layout`, a kda_state_layout: the
+ * transposed layout is fla's state_v_first / transpose_state_layout, named on the
+ * "kernel-fun 0.2.0.dev1 sdist" page among the flags its op does not take), and
+ * `intermediate_states`: NULL, or device fp32 [B*T, HV, K*V] receiving the state after
+ * every token of every sequence (fla's return_intermediate_states; row r's entries are
+ * written only for rows inside a sequence). The decode serving path of "Add fused
+ * recurrent_kda for decode and inference prefill" (attention-gym PR #317).
  */
 int kda_recurrent_fwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
                          const float* A_log, const float* dt_bias, int has_lower_bound,
-                         float lower_bound, const void* beta, int preprocess,
+                         float lower_bound, const void* beta, int preprocess, int state_layout,
                          const float* initial_state, const int32_t* cu_seqlens, int N,
-                         void* o, float* final_state, int B, int T, int H, int HV, int K,
-                         int V, int qkv_dtype, int beta_dtype, float scale,
-                         int32_t* dev_status, hipStream_t stream);
+                         void* o, float* final_state, float* intermediate_states, int B, int T,
+                         int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
+                         float scale, int32_t* dev_status, hipStream_t stream);
 
 /* Reason for the last non-KDA_OK return on this thread ("" if none). */
 const char* kda_last_error(void);
 
 /* ABI version of this header (bumped on any signature change or added entry point);
  * the library returns the KDA_ABI_VERSION it was built with. */
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 int kda_abi_version(void);
 
 #ifdef __cplusplus

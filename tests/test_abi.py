@@ -48,7 +48,7 @@ def test_binding_constants_match_the_header():
     from gated_delta_rule_64_amd import _lib
     for name in ("KDA_F32", "KDA_BF16", "KDA_DEV_BAD_CU_SEQLENS", "KDA_GATE_LOG2",
                  "KDA_GATE_RAW_F32", "KDA_GATE_RAW_BF16", "KDA_PRE_L2NORM_Q", "KDA_PRE_L2NORM_K",
-                 "KDA_PRE_BETA_SIGMOID", "KDA_PRE_NEG_EIGVAL"):
+                 "KDA_PRE_BETA_SIGMOID", "KDA_PRE_NEG_EIGVAL", "KDA_STATE_KV", "KDA_STATE_VK"):
         assert getattr(_lib, name) == _header_int(name), name
 
 
@@ -149,14 +149,14 @@ def _ex(lib, **kw):
 
 def _rec_ex(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gate=0, A=None, dt=None, hlb=0, lb=0.0, beta=FAKE,
-             pre=0, h0=None, cu=None, N=1, o=FAKE, ht=None, B=1, T=1, H=2, HV=2, K=128, V=128,
-             qd=1, bd=1, scale=0.0, st=None, stream=None)
+             pre=0, lay=0, h0=None, cu=None, N=1, o=FAKE, ht=None, inter=None, B=1, T=1, H=2, HV=2,
+             K=128, V=128, qd=1, bd=1, scale=0.0, st=None, stream=None)
     a.update(kw)
     return lib.kda_recurrent_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["gate"], a["A"], a["dt"],
-                                    a["hlb"], a["lb"], a["beta"], a["pre"], a["h0"], a["cu"],
-                                    a["N"], a["o"], a["ht"], a["B"], a["T"], a["H"], a["HV"],
-                                    a["K"], a["V"], a["qd"], a["bd"], a["scale"], a["st"],
-                                    a["stream"])
+                                    a["hlb"], a["lb"], a["beta"], a["pre"], a["lay"], a["h0"],
+                                    a["cu"], a["N"], a["o"], a["ht"], a["inter"], a["B"], a["T"],
+                                    a["H"], a["HV"], a["K"], a["V"], a["qd"], a["bd"], a["scale"],
+                                    a["st"], a["stream"])
 
 
 def _bwd(lib, **kw):
@@ -312,10 +312,17 @@ def test_bwd_workspace_bytes(lib):
     items = HV * B * nt
     al = lambda x: (x + 255) // 256 * 256
     off = al(lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, 1))
-    for per in (K * V, 64 * V, K * V, 64 * V, 2 * 64 * K + 64 * V + K * V,
+    for per in (K * V, 64 * V, 2 * 64 * 64, K * V, 64 * V, 2 * 64 * K + 64 * V + K * V,
                 3 * 64 * K + 64 * 64 + K, 64 * K + 64 * 64):
         off = al(off + items * per * 4)
     for _ in range(2):
         off = al(off + B * T * HV * K * 4)
     assert lib.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, B, 0, 1) == off
     assert lib.kda_chunk_bwd_workspace_bytes(1, 64, 1, 1, 96, 128, 1, 0, 1) == 0
+
+
+def test_recurrent_ex_layout_and_intermediate_rejects(lib):
+    assert _rec_ex(lib, lay=2) == -7
+    assert b"state_layout" in lib.kda_last_error()
+    assert _rec_ex(lib, inter=FAKE + 4) == -2
+    assert _rec_ex(lib, lay=1, inter=FAKE, cu=FAKE, N=0, T=0) == 0

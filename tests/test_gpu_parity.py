@@ -716,3 +716,123 @@ def test_chunk_bwd_c3_full():
     do, _ = _bwd_inputs(d, 68, dht=False)
     log("[bwd c3] B=1 T=8192 H=16 HV=32 K=V=128 bf16")
     _check_bwd(d, do, None, torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------------
+# decode serving: transposed state layout, intermediate states, graph replay
+# ------------------------------------------------------------------------------------
+def _packed_case(lens, HV=4, seed=70, dtype=torch.bfloat16):
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    Tp = cu[-1] + 8
+    d = small(1, Tp, 2, HV, 128, 128, dtype, seed=seed)
+    d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    d["initial_state"] = torch.randn(len(lens), HV, 128, 128, generator=torch.Generator().manual_seed(seed + 1)).mul(0.05).to(DEV)
+    return d, cu
+
+
+def test_recurrent_state_layout_vk():
+    """States stored transposed ([V][K] per head): the same outputs and states, bitwise."""
+    import gated_delta_rule_64_amd as kda
+    d, cu = _packed_case([5, 0, 1, 9])
+    o1, s1 = kda.kda_recurrent_fwd_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                      d["cu_seqlens"], output_final_state=True)
+    h0t = d["initial_state"].transpose(-1, -2).contiguous()
+    o2, s2 = kda.kda_recurrent_fwd_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], h0t, d["cu_seqlens"],
+                                      output_final_state=True, state_layout="vk")
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(valid_rows(cu, d["q"].shape[1])).to(DEV)
+    assert torch.equal(o1[0][rows], o2[0][rows])
+    assert torch.equal(s1, s2.transpose(-1, -2))
+
+
+@pytest.mark.parametrize("layout", ["kv", "vk"])
+def test_recurrent_intermediate_states(layout):
+    """The state after every token: equal to the final state at each sequence's last
+    token (bitwise), and to the oracle's final state of the prefix at sampled tokens."""
+    import gated_delta_rule_64_amd as kda
+    lens = [7, 0, 3, 12]
+    d, cu = _packed_case(lens, seed=72)
+    h0 = d["initial_state"] if layout == "kv" else d["initial_state"].transpose(-1, -2).contiguous()
+    o, ht, inter = kda.kda_recurrent_fwd_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], h0, d["cu_seqlens"],
+                                            output_final_state=True, state_layout=layout,
+                                            output_intermediate_states=True)
+    torch.cuda.synchronize()
+    if layout == "vk":
+        inter = inter.transpose(-1, -2)
+        ht = ht.transpose(-1, -2)
+    for n, ln in enumerate(lens):
+        if ln:
+            assert torch.equal(inter[cu[n + 1] - 1], ht[n]), f"sequence {n}: last intermediate != final"
+    for n, t_in in [(0, 0), (0, 4), (2, 1), (3, 11), (3, 6)]:
+        r = cu[n] + t_in
+        sub = dict(q=d["q"][:, cu[n]:r + 1], k=d["k"][:, cu[n]:r + 1], v=d["v"][:, cu[n]:r + 1],
+                   g=d["g"][:, cu[n]:r + 1], beta=d["beta"][:, cu[n]:r + 1],
+                   initial_state=d["initial_state"][n:n + 1], cu_seqlens=None)
+        _, ht_ref = oracle_of(sub)
+        check(f"state after token {t_in} of sequence {n}", inter[r], ht_ref[0], torch.bfloat16)
+
+
+def _graph_variants(N, Tp, seed):
+    """Offsets and histories for successive replays: one token each, repeated offsets
+    (empty slots) with two-token sequences, then a shorter terminal offset."""
+    gen = torch.Generator().manual_seed(seed)
+    a = list(range(N + 1))
+    b = [0]
+    for n in range(N):
+        b.append(b[-1] + (0 if n % 3 == 1 else (2 if n % 3 == 2 else 1)))
+    c = [min(x, Tp // 4) for x in a]
+    out = []
+    for cu in (a, b, c):
+        assert cu[-1] <= Tp
+        out.append((torch.tensor(cu, dtype=torch.int32), torch.randn(N, 4, 128, 128, generator=gen).mul(0.05)))
+    return out
+
+
+@pytest.mark.parametrize("path", ["recurrent", "chunk"])
+def test_graph_replay_mutated_boundaries_and_history(path):
+    """Capture one call in a HIP graph, then replay it with new offsets and new initial
+    states copied into its input buffers (eager work and syncs between replays); every
+    replay must equal an eager call on the same inputs, bitwise."""
+    import gated_delta_rule_64_amd as kda
+    N, Tp = 48, 96
+    d = small(1, Tp, 2, 4, 128, 128, torch.bfloat16, seed=74)
+    variants = _graph_variants(N, Tp, 75)
+    cu_buf = variants[0][0].to(DEV).clone()
+    h0_buf = variants[0][1].to(DEV).clone()
+    out = torch.zeros_like(d["v"])
+    ht = torch.zeros(N, 4, 128, 128, device=DEV)
+    ws = None
+    if path == "chunk":
+        ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(1, Tp, 2, 4, 128, 128, N, 1), dtype=torch.uint8, device=DEV)
+
+    def call(cu, h0, o, s):
+        if path == "chunk":
+            kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, output_final_state=True,
+                              out=o, final_state=s, workspace=ws)
+        else:
+            kda.kda_recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], h0, cu, output_final_state=True,
+                                  out=o, final_state=s)
+
+    call(cu_buf, h0_buf, out, ht)      # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(cu_buf, h0_buf, out, ht)
+    torch.cuda.synchronize()
+    for rep, (cu, h0) in enumerate(variants * 2):
+        cu_buf.copy_(cu.to(DEV))
+        h0_buf.copy_(h0.to(DEV))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_ref = torch.full_like(d["v"], float("nan"))
+        s_ref = torch.zeros_like(ht)
+        call(cu_buf, h0_buf, o_ref, s_ref)      # eager, same inputs
+        torch.cuda.synchronize()
+        used = int(cu[-1])
+        assert torch.equal(out[:, :used], o_ref[:, :used]), f"replay {rep}: o differs"
+        assert torch.equal(ht, s_ref), f"replay {rep}: final state differs"
+        assert torch.isnan(out[:, used:].float()).all(), f"replay {rep}: rows past the last offset were written"
