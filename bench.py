@@ -314,6 +314,26 @@ def main():
     torch.cuda.synchronize()
     dec_fused_ms = dev_ev.ms(0, 1) / args.decode_steps
     dev_ev.close()
+    # the same decode with the states stored transposed ([V][K] per head)
+    h0_vk = dd["initial_state"].transpose(-1, -2).contiguous()
+    dstate_vk = torch.empty_like(h0_vk)
+
+    def dvcall():
+        kda.kda_recurrent_fwd_ex(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], h0_vk,
+                                 dd["cu_seqlens"], output_final_state=True, out=dout,
+                                 final_state=dstate_vk, state_layout="vk")
+    for _ in range(2):
+        dvcall()
+    torch.cuda.synchronize()
+    dev_ev = Events(hip, 2)
+    hip.hipEventRecord(dev_ev.ev[0], sptr)
+    for _ in range(args.decode_steps):
+        dvcall()
+    hip.hipEventRecord(dev_ev.ev[1], sptr)
+    torch.cuda.synchronize()
+    dec_vk_ms = dev_ev.ms(0, 1) / args.decode_steps
+    dev_ev.close()
+    del h0_vk, dstate_vk
     dec_bytes = (2 * dd["initial_state"].numel() * 4 + 3 * dd["q"].numel() * 2 + dd["g"].numel() * 4
                  + dd["beta"].numel() * 2 + dout.numel() * 2)
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
@@ -350,7 +370,7 @@ def main():
                      "ms_per_step": bwd_ms, "tokens_per_s": tokens / (bwd_ms * 1e-3), "steps": bsteps},
         "decode": {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
                    "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
-                   "bytes": dec_bytes, "fused_inputs_ms": dec_fused_ms},
+                   "bytes": dec_bytes, "fused_inputs_ms": dec_fused_ms, "state_vk_ms": dec_vk_ms},
     }
 
     if not args.no_cpu_baseline:
