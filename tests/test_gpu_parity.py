@@ -836,3 +836,47 @@ def test_graph_replay_mutated_boundaries_and_history(path):
         assert torch.equal(out[:, :used], o_ref[:, :used]), f"replay {rep}: o differs"
         assert torch.equal(ht, s_ref), f"replay {rep}: final state differs"
         assert torch.isnan(out[:, used:].float()).all(), f"replay {rep}: rows past the last offset were written"
+
+
+BWD_EDGE = [  # (label, B, T, H, HV, K, V, dtype, h0, dht)
+    ("single_token", 3, 1, 2, 2, 128, 128, torch.bfloat16, True, True),
+    ("one_chunk", 1, 64, 2, 4, 128, 64, torch.bfloat16, True, False),
+    ("chunk_plus_one", 2, 65, 1, 2, 64, 128, torch.float32, False, True),
+    ("fp32_k64", 1, 130, 2, 2, 64, 64, torch.float32, True, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD_EDGE, ids=[c[0] for c in BWD_EDGE])
+def test_chunk_bwd_edges(case):
+    label, B, T, H, HV, K, V, dtype, h0, dht = case
+    d = small(B, T, H, HV, K, V, dtype, seed=80 + T, h0=h0)
+    do, dht_t = _bwd_inputs(d, 81, dht=dht)
+    log(f"[bwd edge {label}] B{B} T{T} H{H} HV{HV} K{K} V{V} {dtype}")
+    _check_bwd(d, do, dht_t, dtype)
+
+
+def test_chunk_bwd_zero_beta_and_short_packed():
+    """beta exactly 0 on a third of the tokens (dbeta then needs M itself, not L = beta M),
+    packed slots of length 1 between empty ones, and no dh0 wanted."""
+    import gated_delta_rule_64_amd as kda
+    lens = [0, 1, 0, 0, 70, 1]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    Tp = cu[-1] + 3
+    d = small(1, Tp, 2, 2, 128, 128, torch.bfloat16, seed=84)
+    d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    d["initial_state"] = torch.randn(len(lens), 2, 128, 128, generator=torch.Generator().manual_seed(85)).mul(0.05).to(DEV)
+    beta = d["beta"].clone()
+    beta[:, ::3] = 0.0
+    d["beta"] = beta
+    do, dht = _bwd_inputs(d, 86)
+    got = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["initial_state"],
+                            d["cu_seqlens"], dht, want_dh0=False)
+    torch.cuda.synchronize()
+    assert got[5] is None
+    ref = oracle.recurrent_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["initial_state"],
+                               d["cu_seqlens"], dht)
+    rows = torch.from_numpy(valid_rows(cu, Tp))
+    for name, x, y in zip(["dq", "dk", "dv", "dg", "dbeta"], got[:5], ref[:5]):
+        check(name, x[:, rows], y[:, rows], torch.bfloat16)
