@@ -15,7 +15,8 @@ Contents
   * ``gate_activation`` -- the fused gate activation (raw gate input -> per-token log2
                       decay), numpy fp64 (``gate.py``).
   * ``l2norm``, ``beta_sigmoid`` -- the q/k normalisation and beta activation the op can
-                      fuse (``preprocess.py``).
+                      fuse (``preprocess.py``); ``gate_activation_bwd``, ``l2norm_bwd``,
+                      ``beta_sigmoid_bwd`` -- their gradients.
 
 All inputs are converted to float64 exactly (bf16 and fp32 values are exactly
 representable), so the oracle sees the very values the GPU sees.
@@ -233,5 +234,5 @@ def recurrent_bwd(q, k, v, g, beta, do, initial_state=None, cu_seqlens=None, dht
 
 
 from . import chunked  # noqa: E402  (numpy only; no dependency on the library above)
-from .gate import gate_activation  # noqa: E402,F401  (numpy only)
-from .preprocess import beta_sigmoid, l2norm  # noqa: E402,F401  (numpy only)
+from .gate import gate_activation, gate_activation_bwd  # noqa: E402,F401  (numpy only)
+from .preprocess import beta_sigmoid, beta_sigmoid_bwd, l2norm, l2norm_bwd  # noqa: E402,F401  (numpy only)
