@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
   kda_recurrent_fwd(q, k, v, g, beta, ...)  per-token recurrent forward (decode)
   kda_recurrent_fwd_ex(q, k, v, g, beta, ...)  the same with the options of kda_chunk_fwd_ex
   kda_chunk_bwd(q, k, v, g, beta, do, ...)  chunked backward: dq, dk, dv, dg, dbeta, dh0
+  kda_chunk_bwd_ex(...)                      the same through the fused input options
+                                             (raw gate -> dA_log, ddt_bias; q/k norm; beta sigmoid)
   kda_chunk_fwd_workspace_bytes(...)         workspace size queries (also _bwd_)
   kda_last_error()                           reason for the last failure
 """
@@ -35,6 +37,7 @@ from ._lib import (  # noqa: F401
     KDA_STATE_VK,
     KdaError,
     kda_chunk_bwd,
+    kda_chunk_bwd_ex,
     kda_chunk_bwd_workspace_bytes,
     kda_chunk_fwd,
     kda_chunk_fwd_ex,
@@ -48,7 +51,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "kda_chunk_fwd", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_recurrent_fwd",
+    "kda_chunk_fwd", "kda_chunk_bwd", "kda_chunk_bwd_ex", "kda_chunk_bwd_workspace_bytes", "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_recurrent_fwd",
     "kda_recurrent_fwd_ex", "kda_chunk_fwd_workspace_bytes",
     "kda_last_error", "KdaError", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
     "library_path", "KDA_GATE_LOG2", "KDA_GATE_RAW_F32", "KDA_GATE_RAW_BF16", "KDA_PRE_L2NORM_Q",

@@ -71,6 +71,12 @@ def load_library():
         lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
                                       sz, vp, vp]
+        lib.kda_chunk_bwd_ex.restype = i32
+        lib.kda_chunk_bwd_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp, vp, i32,
+                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                         i32, i32, i32, i32, f32, i32, vp, sz, vp, vp]
+        lib.kda_chunk_bwd_ex_workspace_bytes.restype = sz
+        lib.kda_chunk_bwd_ex_workspace_bytes.argtypes = [i32] * 9
         lib.kda_chunk_bwd_workspace_bytes.restype = sz
         lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32] * 9
         lib.kda_recurrent_fwd.restype = i32
@@ -417,3 +423,44 @@ def kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, packed, dtype=KDA_BF16) 
     if isinstance(dtype, torch.dtype):
         dtype = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
     return int(load_library().kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, int(bool(packed)), int(dtype)))
+
+
+def kda_chunk_bwd_ex(q, k, v, g, beta, do, initial_state=None, cu_seqlens=None, dht=None,
+                     scale=None, *, use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                     lower_bound=None, use_qk_l2norm_in_kernel=False, l2norm_q=None,
+                     l2norm_k=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False,
+                     want_dh0=True, workspace=None, dev_status=None):
+    """Gradients of ``kda_chunk_fwd_ex`` with the same options, with respect to the raw
+    inputs. Returns ``(dq, dk, dv, dg, dbeta, dh0, dA_log, ddt_bias)``; the last two are
+    None unless the gate is raw (``ddt_bias`` also needs ``dt_bias``)."""
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens,
+                                                  raw_gate=use_gate_in_kernel)
+    gate, pre = _options(g, HV, K, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                         use_qk_l2norm_in_kernel, l2norm_q, l2norm_k, use_beta_sigmoid_in_kernel,
+                         allow_neg_eigval)
+    if tuple(do.shape) != tuple(v.shape) or do.dtype != q.dtype:
+        raise ValueError("do must match v's shape and q's dtype")
+    if dht is not None and (dht.dtype != torch.float32 or tuple(dht.shape) != (N, HV, K, V)):
+        raise ValueError(f"dht must be float32 {[N, HV, K, V]}")
+    _check_device([("do", do), ("dht", dht)])
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    dg = torch.zeros(B, T, HV, K, dtype=torch.float32, device=dev)
+    dbeta = torch.zeros_like(beta)
+    dh0 = torch.empty(N, HV, K, V, dtype=torch.float32, device=dev) if want_dh0 else None
+    dA = torch.empty(HV, dtype=torch.float32, device=dev) if use_gate_in_kernel else None
+    ddt = torch.empty(HV * K, dtype=torch.float32, device=dev) if (use_gate_in_kernel and dt_bias is not None) else None
+    need = lib.kda_chunk_bwd_ex_workspace_bytes(B, T, H, HV, K, V, N, int(cu_seqlens is not None), qkv)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), gate, _ptr(A_log), _ptr(dt_bias),
+                              int(lower_bound is not None),
+                              float(lower_bound if lower_bound is not None else 0.0), _ptr(beta), pre,
+                              _ptr(initial_state), _ptr(cu_seqlens), N, _ptr(do), _ptr(dht), _ptr(dq),
+                              _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(dA), _ptr(ddt),
+                              B, T, H, HV, K, V, qkv, bdt, float(scale or 0.0), 64, _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(dev_status),
+                              _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    return dq, dk, dv, dg, dbeta, dh0, dA, ddt

@@ -221,6 +221,80 @@ int chunk_bwd_impl(const kda::ChunkBwdArgs& a0, const float* g, int chunk_size) 
 
 extern "C" {
 
+size_t kda_chunk_bwd_ex_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
+                                        int packed, int qkv_dtype) {
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || N < 0 || (K != 64 && K != 128) ||
+        (V != 64 && V != 128) || (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32))
+        return 0;
+    kda::ChunkBwdExLayout L;
+    if (!kda::chunk_bwd_ex_layout(B, T, H, HV, K, V, packed ? N : B, packed != 0, qkv_dtype, &L)) return 0;
+    return L.total;
+}
+
+int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
+                     const float* A_log, const float* dt_bias, int has_lower_bound,
+                     float lower_bound, const void* beta, int preprocess,
+                     const float* initial_state, const int32_t* cu_seqlens, int N,
+                     const void* dout, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                     void* dbeta, float* dh0, float* dA_log, float* ddt_bias, int B, int T,
+                     int H, int HV, int K, int V, int qkv_dtype, int beta_dtype, float scale,
+                     int chunk_size, void* workspace, size_t workspace_bytes,
+                     int32_t* dev_status, hipStream_t stream) {
+    clear_error();
+    int rc = check_common(q, k, v, static_cast<const float*>(g), beta, initial_state, cu_seqlens, N,
+                          dv, dh0, B, T, H, HV, K, V, qkv_dtype, beta_dtype);
+    if (rc != KDA_OK) return rc;
+    kda::InputSpec in;
+    const bool nonempty = (long long)B * T > 0;
+    rc = make_input_spec(g, gate, A_log, dt_bias, has_lower_bound, lower_bound, preprocess, nonempty, &in);
+    if (rc != KDA_OK) return rc;
+    if (nonempty && (!dout || !dq || !dk || !dv || !dg || !dbeta))
+        return fail(KDA_ERR_NULL, "do, dq, dk, dv, dg and dbeta must be non-NULL");
+    if (gate != KDA_GATE_LOG2 && nonempty && !dA_log)
+        return fail(KDA_ERR_NULL, "dA_log must be non-NULL with a raw gate");
+    if (gate != KDA_GATE_LOG2 && dt_bias && nonempty && !ddt_bias)
+        return fail(KDA_ERR_NULL, "ddt_bias must be non-NULL when dt_bias is given");
+    if (!aligned16(dht))
+        return fail(KDA_ERR_SHAPE, "dht must be 16-byte aligned");
+    if (chunk_size != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64, got %d", chunk_size);
+    if (K != 64 && K != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "K must be 64 or 128, got %d", K);
+    if (V != 64 && V != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "V must be 64 or 128, got %d", V);
+    if (cu_seqlens && (long long)T / 64 + N > 0x7fffffffLL / HV)
+        return fail(KDA_ERR_SHAPE, "too many chunks");
+    kda::ChunkBwdExLayout L;
+    kda::chunk_bwd_ex_layout(B, T, H, HV, K, V, N, cu_seqlens != nullptr, qkv_dtype, &L);
+    if (N == 0) return KDA_OK;
+    if (!workspace)
+        return fail(KDA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+    if (workspace_bytes < L.total)
+        return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, L.total);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    kda::ChunkBwdExArgs x;
+    kda::ChunkBwdArgs& a = x.core;
+    a.q = q; a.k = k; a.v = v; a.g = static_cast<const float*>(g); a.beta = beta;
+    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
+    a.dout = dout; a.dht = dht;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype;
+    a.scale = scale == 0.0f ? 1.0f / sqrtf((float)K) : scale;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.dev_status = dev_status; a.stream = stream;
+    x.g = g;
+    x.gate_bf16 = gate == KDA_GATE_RAW_BF16 ? 1 : 0;
+    x.in = in;
+    x.dA_log = dA_log;
+    x.ddt_bias = ddt_bias;
+    hipError_t err = kda::launch_chunk_bwd_ex(x, L);
+    if (err != hipSuccess)
+        return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return KDA_OK;
+}
+
 const char* kda_last_error(void) { return g_last_error; }
 
 size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,

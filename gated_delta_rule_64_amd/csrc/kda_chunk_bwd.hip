@@ -168,7 +168,48 @@ struct BwdParams {
     float* wy;           // dkd [64][K], dM [64][64]
     float* dq_hv;        // [B*T][HV][K]
     float* dk_hv;
+    InputSpec in;        // fused options of the forward (applied to the staged inputs)
+    int dbeta_f32;       // dbeta written as fp32
 };
+
+// The fused options applied to staged rows in LDS (64 rows of K, rows >= len zero):
+// the L2 normalisation of each row, in fp32.
+// Thread t in [0, 64) takes row t.
+template <int K>
+__device__ __forceinline__ void l2norm_rows_lds(float* X, int ld, int t) {
+    if (t >= 0 && t < C) {
+        float ss = 0.f;
+        for (int d = 0; d < K; ++d) ss = fmaf(X[t * ld + d], X[t * ld + d], ss);
+        const float rn = l2norm_rstd(ss);
+        for (int d = 0; d < K; ++d) X[t * ld + d] *= rn;
+    }
+}
+
+// The raw gate input staged into X (rows < len) turned into the log2 decay.
+template <int K, int NTH>
+__device__ __forceinline__ void gate_rows_lds(float* X, int ld, int len, const InputSpec& in, int hv, int tid) {
+    const float amp = -expf(in.A_log[hv]);
+    const float lb2 = in.lower_bound * LOG2E;
+    for (int e = tid; e < C * K; e += NTH) {
+        const int r = e / K, d = e % K;
+        if (r < len) {
+            const float x = X[r * ld + d] + (in.dt_bias ? in.dt_bias[(size_t)hv * K + d] : 0.f);
+            X[r * ld + d] = gate_log2_from_raw(x, amp, in.has_lower_bound, lb2);
+        }
+    }
+}
+
+// rows of g (log2 decay, or the raw gate input by the options) into LDS
+template <int K, int NTH>
+__device__ __forceinline__ void stage_gate(const BwdParams& p, int2 pos, int hv, float* X, int ld, int tid) {
+    const size_t o = ((size_t)pos.x * p.HV + hv) * K, st = (size_t)p.HV * K;
+    if (p.in.gate_mode == GATE_RAW_BF16)
+        stage_rows<C, K, __bf16, NTH>(static_cast<const __bf16*>(p.in.g_raw) + o, st, pos.y, X, ld, tid);
+    else if (p.in.gate_mode == GATE_RAW_F32)
+        stage_rows<C, K, float, NTH>(static_cast<const float*>(p.in.g_raw) + o, st, pos.y, X, ld, tid);
+    else
+        stage_rows<C, K, float, NTH>(p.g + o, st, pos.y, X, ld, tid);
+}
 
 template <int K>
 struct GsLayout {
@@ -517,11 +558,16 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
 
     // ---- loads and the chunk-local cumsum of g ----
     stage_rows<C, K, TIn, NTH>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
-    stage_rows<C, K, float, NTH>(p.g + ((size_t)pos.x * p.HV + hv) * K, (size_t)p.HV * K, len, XL, LX, tid);
+    stage_gate<K, NTH>(p, pos, hv, XL, LX, tid);
     if (tid < C) {
-        bL[tid] = tid < len ? to_f32(bin[(size_t)(pos.x + tid) * p.HV + hv]) : 0.f;
+        float b = tid < len ? to_f32(bin[(size_t)(pos.x + tid) * p.HV + hv]) : 0.f;
+        if (p.in.beta_sig != 0.f && tid < len) b = beta_from_logit(b, p.in.beta_sig);
+        bL[tid] = b;
         dbL[tid] = 0.f;
     }
+    __syncthreads();
+    if (p.in.l2norm_k) l2norm_rows_lds<K>(kL, LK, tid);
+    if (p.in.gate_mode != GATE_LOG2) gate_rows_lds<K, NTH>(XL, LX, len, p.in, hv, tid);
     __syncthreads();
     if (tid < K) {
         float acc = 0.f;
@@ -643,7 +689,11 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
         add_rows(16 * I, db);
     }
     __syncthreads();
-    if (tid < len) reinterpret_cast<TB*>(p.dbeta)[(size_t)(pos.x + tid) * p.HV + hv] = from_f32<TB>(dbL[tid]);
+    if (tid < len) {
+        const size_t e = (size_t)(pos.x + tid) * p.HV + hv;
+        if (p.dbeta_f32) reinterpret_cast<float*>(p.dbeta)[e] = dbL[tid];
+        else reinterpret_cast<TB*>(p.dbeta)[e] = from_f32<TB>(dbL[tid]);
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -688,10 +738,14 @@ __global__ __launch_bounds__(4 * K, 1) void bwd_pair_kernel(BwdParams p) {
 
     stage_rows<C, K, TIn, NTH>(qin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, qL, LK, tid);
     stage_rows<C, K, TIn, NTH>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
-    stage_rows<C, K, float, NTH>(p.g + ((size_t)pos.x * p.HV + hv) * K, (size_t)p.HV * K, len, GmL, LK, tid);
+    stage_gate<K, NTH>(p, pos, hv, GmL, LK, tid);
     stage_f32<C, C, NTH>(gsC + GL::DA, C, dAL, LA, tid);   // dAqk (the scale is applied at use)
     stage_f32<C, C, NTH>(wyC + WL::DM, C, dML, LA, tid);
     if (tid < K) dGL[tid] = gsC[GL::DG + tid];
+    __syncthreads();
+    if (p.in.l2norm_q) l2norm_rows_lds<K>(qL, LK, tid);        // threads 0 .. 63
+    if (p.in.l2norm_k) l2norm_rows_lds<K>(kL, LK, tid - C);    // threads 64 .. 127
+    if (p.in.gate_mode != GATE_LOG2) gate_rows_lds<K, NTH>(GmL, LK, len, p.in, hv, tid);
     __syncthreads();
     if (tid < K) {
         float acc = 0.f;
@@ -870,7 +924,7 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
     // forward recompute: schedule (packed), records, and the re-scan with checkpoints
     ChunkArgs f;
     f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
-    f.in = InputSpec{GATE_LOG2, nullptr, nullptr, nullptr, 0, 0.f, 0, 0, 0.f};
+    f.in = a.in;   // the recompute runs with the forward's fused options
     f.initial_state = a.initial_state; f.cu_seqlens = a.cu_seqlens;
     f.o = nullptr; f.final_state = nullptr;
     f.N = a.N; f.B = a.B; f.T = a.T; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
@@ -910,6 +964,8 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
     p.wy = reinterpret_cast<float*>(ws + L.off_wy);
     p.dq_hv = reinterpret_cast<float*>(ws + L.off_dq);
     p.dk_hv = reinterpret_cast<float*>(ws + L.off_dk);
+    p.in = a.in;
+    p.dbeta_f32 = a.dbeta_f32;
 
     const long long chains = (long long)a.N * a.HV;
     const long long nchunk_items = (long long)L.fwd.NCmax * a.HV;
@@ -930,9 +986,11 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
         hipLaunchKernelGGL((bwd_pair_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(pair_threads<K>()), 0,
                            a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL((bwd_reduce_kernel<K, TIn>), dim3((unsigned)((long long)L.fwd.NCmax * a.H)), dim3(BT), 0,
-                           a.stream, p);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if (!a.skip_reduce) {
+            hipLaunchKernelGGL((bwd_reduce_kernel<K, TIn>), dim3((unsigned)((long long)L.fwd.NCmax * a.H)), dim3(BT), 0,
+                               a.stream, p);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
     }
     return hipSuccess;
 }
@@ -944,6 +1002,192 @@ hipError_t launch_bwd_t(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
 }
 
 size_t align256b(size_t x) { return (x + 255) / 256 * 256; }
+
+// ------------------------------------------------------------------------------------
+// backward of the fused input options (gate activation, q/k L2 norm, beta sigmoid): the
+// chunked backward applies the options to the inputs it stages (in fp32, as the fused
+// forward does), and the chain rule of each option is applied to its gradients after.
+// ------------------------------------------------------------------------------------
+struct PostParams {
+    const void* q;           // raw inputs
+    const void* k;
+    const void* g;
+    const void* beta;
+    InputSpec in;
+    int gate_bf16;
+    const float* dq_hv;      // [rows][HV][K] per value head, from the chunked backward
+    const float* dk_hv;
+    const float* dg2;        // [rows][HV][K] with respect to the log2 gate
+    const float* dba;        // [rows][HV] with respect to the activated beta
+    void* dq;                // outputs
+    void* dk;
+    float* dg;
+    void* dbeta;
+    float* part;             // [NCmax][HV][K + 1]: ddt_bias and dA_log partial sums per chunk
+    float* dA_log;
+    float* ddt_bias;
+    const int32_t* nchunks;
+    const int2* table;
+    int dense, NT, T, H, HV, NCmax;
+};
+
+// dq, dk: the sum over each q/k head's value heads, then the L2-norm backward
+// r (dy - y (y . dy)); one wave per (row, head), per chunk
+template <int K, typename TIn>
+__global__ __launch_bounds__(256) void bwd_post_qk_kernel(PostParams p) {
+    constexpr int NE = K / 64;
+    const int c = blockIdx.x / p.H, h = blockIdx.x % p.H;
+    if (!p.dense && c >= p.nchunks[0]) return;
+    const int2 pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = p.HV / p.H;
+    for (int r = wave; r < pos.y; r += 4) {
+        const size_t row = (size_t)(pos.x + r);
+        for (int which = 0; which < 2; ++which) {
+            const float* src = which ? p.dk_hv : p.dq_hv;
+            const TIn* x_in = reinterpret_cast<const TIn*>(which ? p.k : p.q);
+            TIn* out = reinterpret_cast<TIn*>(which ? p.dk : p.dq);
+            const bool norm = which ? p.in.l2norm_k : p.in.l2norm_q;
+            float dy[NE], y[NE];
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                const int d = lane + 64 * e;
+                float acc = 0.f;
+                for (int j = 0; j < grp; ++j) acc += src[(row * p.HV + h * grp + j) * K + d];
+                dy[e] = acc;
+                y[e] = to_f32(x_in[(row * p.H + h) * K + d]);
+                ss = fmaf(y[e], y[e], ss);
+            }
+            if (norm) {
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m, 64);
+                const float rn = l2norm_rstd(ss);
+                float yd = 0.f;
+#pragma unroll
+                for (int e = 0; e < NE; ++e) { y[e] *= rn; yd = fmaf(y[e], dy[e], yd); }
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) yd += __shfl_xor(yd, m, 64);
+#pragma unroll
+                for (int e = 0; e < NE; ++e) dy[e] = rn * (dy[e] - y[e] * yd);
+            }
+#pragma unroll
+            for (int e = 0; e < NE; ++e) out[(row * p.H + h) * K + lane + 64 * e] = from_f32<TIn>(dy[e]);
+        }
+    }
+}
+
+// the raw gate's and beta's gradients per (chunk, value head), with this chunk's partial
+// sums of ddt_bias (per channel) and dA_log
+template <int K, typename TB>
+__global__ __launch_bounds__(K) void bwd_post_gb_kernel(PostParams p) {
+    const int c = blockIdx.x / p.HV, hv = blockIdx.x % p.HV;
+    if (!p.dense && c >= p.nchunks[0]) return;
+    const int2 pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
+    const int d = threadIdx.x;
+    const bool raw = p.in.gate_mode != GATE_LOG2;
+    float sdt = 0.f, sA = 0.f;
+    const float eA = raw ? expf(p.in.A_log[hv]) : 0.f;
+    for (int r = 0; r < pos.y; ++r) {
+        const size_t e = ((size_t)(pos.x + r) * p.HV + hv) * K + d;
+        if (raw) {
+            float x = p.gate_bf16 ? (float)static_cast<const __bf16*>(p.g)[e] : static_cast<const float*>(p.g)[e];
+            if (p.in.dt_bias) x += p.in.dt_bias[(size_t)hv * K + d];
+            const float sp = x > 15.f ? x : log1pf(expf(x));      // softplus
+            const float gn = -eA * sp;                               // natural-log activation
+            const bool clamped = p.in.has_lower_bound && gn < p.in.lower_bound;
+            const float dgn = clamped ? 0.f : p.dg2[e] * LOG2E;      // d/dgn of the log2 value is 1/ln 2
+            const float sig = 1.f / (1.f + expf(-x));
+            const float dx = -eA * sig * dgn;
+            p.dg[e] = dx;
+            sdt += dx;
+            sA = fmaf(dgn, gn, sA);
+        }
+        if (d == 0 && p.in.beta_sig != 0.f) {
+            const size_t eb = (size_t)(pos.x + r) * p.HV + hv;
+            const float b = to_f32(reinterpret_cast<const TB*>(p.beta)[eb]);
+            const float sb = 1.f / (1.f + expf(-b));
+            reinterpret_cast<TB*>(p.dbeta)[eb] = from_f32<TB>(p.dba[eb] * p.in.beta_sig * sb * (1.f - sb));
+        }
+    }
+    if (raw) {
+        float* pp = p.part + ((size_t)c * p.HV + hv) * (K + 1);
+        pp[d] = sdt;
+        // dA_log partial: the block's sum over channels
+        __shared__ float red[K];
+        red[d] = sA;
+        __syncthreads();
+        if (d == 0) {
+            float t = 0.f;
+            for (int i = 0; i < K; ++i) t += red[i];
+            pp[K] = t;
+        }
+    }
+}
+
+// dA_log and ddt_bias: the chunk partials summed in chunk order (deterministic)
+template <int K>
+__global__ __launch_bounds__(K + 1) void bwd_gate_sum_kernel(PostParams p) {
+    const int hv = blockIdx.x, j = threadIdx.x;
+    const int nc = p.dense ? p.NCmax : p.nchunks[0];
+    float t = 0.f;
+    for (int c = 0; c < nc; ++c) t += p.part[((size_t)c * p.HV + hv) * (K + 1) + j];
+    if (j < K) {
+        if (p.ddt_bias) p.ddt_bias[(size_t)hv * K + j] = t;
+    } else {
+        p.dA_log[hv] = t;
+    }
+}
+
+template <int K, typename TIn, typename TB>
+hipError_t launch_bwd_ex_k(const ChunkBwdExArgs& x, const ChunkBwdExLayout& L) {
+    const ChunkBwdArgs& a = x.core;
+    char* ws = reinterpret_cast<char*>(a.workspace);
+    hipError_t err;
+    // the chunked backward with the options applied to its staged inputs, into fp32
+    // gradients where a chain rule follows (dq, dk per value head; the log2 gate's and
+    // the activated beta's gradients)
+    ChunkBwdArgs c = a;
+    c.in = x.in;
+    const bool raw = x.in.gate_mode != GATE_LOG2, sig = x.in.beta_sig != 0.f;
+    c.g = raw ? nullptr : a.g;
+    c.dg = raw ? reinterpret_cast<float*>(ws + L.off_dg2) : a.dg;
+    if (sig) {
+        c.dbeta = ws + L.off_dba;
+        c.dbeta_f32 = true;
+    }
+    c.skip_reduce = true;
+    err = launch_chunk_bwd(c, L.core);
+    if (err != hipSuccess) return err;
+
+    PostParams q;
+    q.q = a.q; q.k = a.k; q.g = x.g; q.beta = a.beta; q.in = x.in; q.gate_bf16 = x.gate_bf16;
+    q.dq_hv = reinterpret_cast<const float*>(ws + L.core.off_dq);
+    q.dk_hv = reinterpret_cast<const float*>(ws + L.core.off_dk);
+    q.dg2 = reinterpret_cast<const float*>(ws + L.off_dg2);
+    q.dba = reinterpret_cast<const float*>(ws + L.off_dba);
+    q.dq = a.dq; q.dk = a.dk; q.dg = a.dg; q.dbeta = a.dbeta;
+    q.part = reinterpret_cast<float*>(ws + L.off_part);
+    q.dA_log = x.dA_log; q.ddt_bias = x.ddt_bias;
+    const bool dense = a.cu_seqlens == nullptr;
+    q.nchunks = dense ? nullptr : reinterpret_cast<const int32_t*>(ws) + 3 * a.N;
+    q.table = dense ? nullptr : reinterpret_cast<const int2*>(ws + sched_table_offset(a.N));
+    q.dense = dense; q.NT = (a.T + C - 1) / C; q.T = a.T; q.H = a.H; q.HV = a.HV; q.NCmax = L.core.fwd.NCmax;
+    const long long nc = (long long)L.core.fwd.NCmax;
+    if (nc > 0) {
+        hipLaunchKernelGGL((bwd_post_qk_kernel<K, TIn>), dim3((unsigned)(nc * a.H)), dim3(256), 0, a.stream, q);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if (raw || sig) {
+            hipLaunchKernelGGL((bwd_post_gb_kernel<K, TB>), dim3((unsigned)(nc * a.HV)), dim3(K), 0, a.stream, q);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        if (raw) {
+            hipLaunchKernelGGL((bwd_gate_sum_kernel<K>), dim3((unsigned)a.HV), dim3(K + 1), 0, a.stream, q);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+    }
+    return hipSuccess;
+}
 
 }  // namespace
 
@@ -967,6 +1211,32 @@ bool chunk_bwd_layout(int B, int T, int HV, int K, int V, int N, bool packed, in
     L.total = off;
     *out = L;
     return true;
+}
+
+bool chunk_bwd_ex_layout(int B, int T, int H, int HV, int K, int V, int N, bool packed, int qkv_dtype,
+                         ChunkBwdExLayout* out) {
+    ChunkBwdExLayout L{};
+    if (!chunk_bwd_layout(B, T, HV, K, V, N, packed, qkv_dtype, &L.core)) return false;
+    const size_t rows = (size_t)B * T;
+    size_t off = align256b(L.core.total);
+    L.off_dg2 = off;  off = align256b(off + rows * HV * K * 4);
+    L.off_dba = off;  off = align256b(off + rows * HV * 4);
+    L.off_part = off; off = align256b(off + (size_t)L.core.fwd.NCmax * HV * (K + 1) * 4);
+    L.total = off;
+    *out = L;
+    return true;
+}
+
+hipError_t launch_chunk_bwd_ex(const ChunkBwdExArgs& x, const ChunkBwdExLayout& L) {
+    const ChunkBwdArgs& a = x.core;
+    if (a.qkv_dtype == KDA_BF16) {
+        if (a.beta_dtype == KDA_BF16)
+            return a.K == 128 ? launch_bwd_ex_k<128, __bf16, __bf16>(x, L) : launch_bwd_ex_k<64, __bf16, __bf16>(x, L);
+        return a.K == 128 ? launch_bwd_ex_k<128, __bf16, float>(x, L) : launch_bwd_ex_k<64, __bf16, float>(x, L);
+    }
+    if (a.beta_dtype == KDA_BF16)
+        return a.K == 128 ? launch_bwd_ex_k<128, float, __bf16>(x, L) : launch_bwd_ex_k<64, float, __bf16>(x, L);
+    return a.K == 128 ? launch_bwd_ex_k<128, float, float>(x, L) : launch_bwd_ex_k<64, float, float>(x, L);
 }
 
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {

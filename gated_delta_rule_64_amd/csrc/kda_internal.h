@@ -127,6 +127,12 @@ struct ChunkBwdArgs {
     size_t workspace_bytes;
     int32_t* dev_status;
     hipStream_t stream;
+    bool skip_reduce = false;   // leave dq, dk per value head (fp32) in the workspace
+    // fused input options of the forward being differentiated (g unused for a raw gate);
+    // the gradients then are with respect to the transformed inputs (q, k normalised,
+    // the log2 gate, the activated beta), the last one written fp32 when dbeta_f32
+    InputSpec in{GATE_LOG2, nullptr, nullptr, nullptr, 0, 0.f, 0, 0, 0.f};
+    bool dbeta_f32 = false;
 };
 
 // Backward workspace: the forward's (schedule + records) first, then per (value head,
@@ -146,6 +152,29 @@ struct ChunkBwdLayout {
 bool chunk_bwd_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qkv_dtype,
                       ChunkBwdLayout* out);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, const ChunkBwdLayout& L);
+
+// The backward with the fused input options: `core` holds the raw inputs (g unused when
+// the gate is raw; then g below is the raw gate) and the final gradient outputs.
+struct ChunkBwdExArgs {
+    ChunkBwdArgs core;
+    const void* g;          // log2 decay (fp32) or the raw gate input
+    int gate_bf16;          // raw gate stored as bf16
+    InputSpec in;
+    float* dA_log;          // [HV] (raw gate)
+    float* ddt_bias;        // [HV * K] or NULL
+};
+
+// the core backward's workspace, then the fp32 gradients of the log2 gate and of the
+// activated beta, and the per-chunk partial sums of the gate parameters' gradients
+struct ChunkBwdExLayout {
+    ChunkBwdLayout core;
+    size_t off_dg2, off_dba, off_part;
+    size_t total;
+};
+
+bool chunk_bwd_ex_layout(int B, int T, int H, int HV, int K, int V, int N, bool packed, int qkv_dtype,
+                         ChunkBwdExLayout* out);
+hipError_t launch_chunk_bwd_ex(const ChunkBwdExArgs& x, const ChunkBwdExLayout& L);
 
 hipError_t launch_recurrent(const RecurrentArgs& a);
 hipError_t launch_chunk(const ChunkArgs& a, const ChunkLayout& L);

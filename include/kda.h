@@ -228,6 +228,38 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                   void* workspace, size_t workspace_bytes, int32_t* dev_status,
                   hipStream_t stream);
 
+/*
+ * kda_chunk_bwd for a forward run with the options of kda_chunk_fwd_ex: the same `g`,
+ * `gate`, A_log, dt_bias, has_lower_bound, lower_bound, beta and `preprocess` arguments
+ * (and rules) as that forward. The gradients are with respect to the raw inputs:
+ *   dq, dk     through the L2 normalisation when KDA_PRE_L2NORM_Q / _K is set
+ *              (dx = r (dy - y (y . dy)), y = x r, r = (sum x^2 + 1e-6)^-1/2);
+ *   dbeta      through the sigmoid when KDA_PRE_BETA_SIGMOID is set (c s (1 - s));
+ *   dg         fp32 [B, T, HV, K]: with respect to g itself (the log2 decay, or the raw
+ *              gate input), through the activation where the lower bound does not clamp;
+ *   dA_log     device fp32 [HV], required with a raw gate (NULL otherwise);
+ *   ddt_bias   device fp32 [HV * K], required when dt_bias is given.
+ * The gate backward is the one of "kernel-fun 0.2.0.dev1 sdist" (the chain module's
+ * gate_backward: dg with respect to the raw input, dA_log, ddt_bias); the normalisation
+ * backward is fla's l2norm_bwd, which that page's autograd Function applies to dq and
+ * dk. The options are applied in fp32 to the inputs each kernel stages, as in the fused
+ * forward; the workspace (kda_chunk_bwd_ex_workspace_bytes) adds the fp32 gradients of
+ * the transformed gate and beta. Everything else as kda_chunk_bwd.
+ */
+int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
+                     const float* A_log, const float* dt_bias, int has_lower_bound,
+                     float lower_bound, const void* beta, int preprocess,
+                     const float* initial_state, const int32_t* cu_seqlens, int N,
+                     const void* dout, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                     void* dbeta, float* dh0, float* dA_log, float* ddt_bias, int B, int T,
+                     int H, int HV, int K, int V, int qkv_dtype, int beta_dtype, float scale,
+                     int chunk_size, void* workspace, size_t workspace_bytes,
+                     int32_t* dev_status, hipStream_t stream);
+
+/* Workspace bytes kda_chunk_bwd_ex needs; 0 for invalid sizes. */
+size_t kda_chunk_bwd_ex_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
+                                        int packed, int qkv_dtype);
+
 /* Workspace bytes kda_chunk_bwd needs for these sizes; 0 for invalid sizes. */
 size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
                                      int packed, int qkv_dtype);
@@ -278,7 +310,7 @@ const char* kda_last_error(void);
 
 /* ABI version of this header (bumped on any signature change or added entry point);
  * the library returns the KDA_ABI_VERSION it was built with. */
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 int kda_abi_version(void);
 
 #ifdef __cplusplus

@@ -507,17 +507,17 @@ PRE_CASES = [  # (l2norm_q, l2norm_k, beta sigmoid, allow_neg_eigval)
 ]
 
 
-def _raw_inputs(d, seed, lq=True, lk=True, sig=True, zero_rows=True):
+def _raw_inputs(d, seed, lq=True, lk=True, sig=True, zero_rows=True, span=3.0):
     """Inputs for the preprocessing flags: q (lq) and k (lk) un-normalised, every
-    (token, head) row of the unit-norm draw times 10^U[-3, 3] with about 2% of rows zero;
-    beta (sig) replaced by pre-activations N(0, 2^2) in beta's dtype. Tensors whose
+    (token, head) row of the unit-norm draw times 10^U[-span, span] with about 2% of rows
+    zero; beta (sig) replaced by pre-activations N(0, 2^2) in beta's dtype. Tensors whose
     preprocessing is off keep the recipe's values (a delta rule on un-normalised keys or
     beta outside (0, 2) diverges)."""
     gen = torch.Generator().manual_seed(seed)
 
     def scaled(x):
         B, T, H, _ = x.shape
-        s = torch.pow(10.0, torch.empty(B, T, H, 1).uniform_(-3.0, 3.0, generator=gen))
+        s = torch.pow(10.0, torch.empty(B, T, H, 1).uniform_(-span, span, generator=gen))
         y = x.cpu().float() * s
         if zero_rows:
             y = torch.where(torch.rand(B, T, H, 1, generator=gen) < 0.02, torch.zeros_like(y), y)
@@ -880,3 +880,64 @@ def test_chunk_bwd_zero_beta_and_short_packed():
     rows = torch.from_numpy(valid_rows(cu, Tp))
     for name, x, y in zip(["dq", "dk", "dv", "dg", "dbeta"], got[:5], ref[:5]):
         check(name, x[:, rows], y[:, rows], torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------------
+# backward through the fused input options
+# ------------------------------------------------------------------------------------
+def _bwd_ex_oracle(r, do, dht, g_raw, A_log, dt_bias, bound, lq, lk, sig, neg):
+    """The oracle composed: the options' forward transforms, the recurrence's gradients,
+    then each option's chain rule."""
+    qn = oracle.l2norm(r["q"]) if lq else r["q"]
+    kn = oracle.l2norm(r["k"]) if lk else r["k"]
+    ba = oracle.beta_sigmoid(r["beta"], neg) if sig else r["beta"]
+    g2 = oracle.gate_activation(g_raw, A_log, dt_bias, bound) if g_raw is not None else r["g"]
+    dq, dk, dv, dg2, dba, dh0 = oracle.recurrent_bwd(qn, kn, r["v"], g2, ba, do, r["initial_state"],
+                                                     r["cu_seqlens"], dht)
+    if lq:
+        dq = oracle.l2norm_bwd(r["q"], dq)
+    if lk:
+        dk = oracle.l2norm_bwd(r["k"], dk)
+    if sig:
+        dba = oracle.beta_sigmoid_bwd(r["beta"], dba, neg)
+    dA = ddt = None
+    dg = dg2
+    if g_raw is not None:
+        dg, dA, ddt = oracle.gate_activation_bwd(g_raw, A_log, dt_bias, bound, dg2)
+    return dq, dk, dv, dg, dba, dh0, dA, ddt
+
+
+BWD_EX = [  # (gate raw, lower bound, l2norm q, l2norm k, sigmoid, neg eigval, dtype)
+    (True, None, True, True, True, False, torch.bfloat16),
+    (True, -4.0, False, True, False, False, torch.bfloat16),
+    (False, None, True, False, True, True, torch.bfloat16),
+    (True, None, True, True, True, True, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", BWD_EX, ids=lambda c: f"gate{int(c[0])}_lb{c[1]}_q{int(c[2])}k{int(c[3])}_sig{int(c[4])}{int(c[5])}_{str(c[6])[6:]}")
+def test_chunk_bwd_ex(case):
+    """Gradients through the fused options with respect to the raw inputs (and A_log,
+    dt_bias) against the composed oracle. Row scales 10^U[-0.5, 0.5]: the normalisation's
+    gradient grows as 1 / |row|, so rows far below unit norm would only test fp32's
+    relative precision against an absolute bound."""
+    import gated_delta_rule_64_amd as kda
+    raw, bound, lq, lk, sig, neg, dtype = case
+    d = small(1, 200, 2, 4, 128, 128, dtype, seed=90)
+    r = _raw_inputs(d, 91, lq, lk, sig, zero_rows=False, span=0.5)
+    g_raw = A_log = dt_bias = None
+    if raw:
+        g_raw, A_log, dt_bias = _gate_params(1, 200, 4, 128, torch.bfloat16 if dtype == torch.bfloat16 else torch.float32, seed=92)
+    do, dht = _bwd_inputs(d, 93)
+    got = kda.kda_chunk_bwd_ex(r["q"], r["k"], r["v"], g_raw if raw else r["g"], r["beta"], do,
+                               r["initial_state"], None, dht, use_gate_in_kernel=raw, A_log=A_log,
+                               dt_bias=dt_bias, lower_bound=bound, l2norm_q=lq, l2norm_k=lk,
+                               use_beta_sigmoid_in_kernel=sig, allow_neg_eigval=neg)
+    torch.cuda.synchronize()
+    ref = _bwd_ex_oracle(r, do, dht, g_raw, A_log, dt_bias, bound, lq, lk, sig, neg)
+    log(f"[bwd ex] gate raw={raw} bound={bound} l2norm q={lq} k={lk} sigmoid={sig} neg={neg} {dtype}")
+    for name, x, y in zip(["dq", "dk", "dv", "dg", "dbeta", "dh0", "dA_log", "ddt_bias"], got, ref):
+        if y is None:
+            assert x is None, name
+            continue
+        check(name, x, np.asarray(y).reshape(tuple(x.shape)), dtype)
