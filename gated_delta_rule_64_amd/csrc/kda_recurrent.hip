@@ -9,45 +9,42 @@
 // order (decay, delta-rule write, read of the updated state) is the one of KDA's chunk
 // algebra in "kernel-fun 0.2.0.dev1 sdist", ALGORITHM.md, section Forward.
 //
-// Work decomposition. One wavefront owns one (sequence n, value head hv, 64-column
-// slice of V) and walks its tokens in order. Lane l holds the state block
-//     rows  d = (l / 16) * (K / 4) + i,   i = 0 .. K/4 - 1
-//     cols  c = v0 + 4 * (l % 16) + j,    j = 0 .. 3
-// in registers (K = 128: 32 x 4 fp32 per lane), so the state is read from HBM once and
+// Work decomposition. One wavefront owns one (sequence n, value head hv, BV-column slice
+// of V) and walks its tokens in order. Its 64 lanes form CG = BV/4 column groups times
+// RG = 64/CG row groups; lane l (column group cg = l % CG, row group rg = l / CG) holds
+// the state block of the R = K/RG rows d(rg, i), i = 0 .. R-1, and the four columns
+// c = v0 + 4 cg + j, j = 0 .. 3, in registers, so the state is read from HBM once and
 // written once with 16-byte accesses. Per token the lane folds the decay into its block,
-// forms partial sums of S~^T k and S~^T q over its rows (S~ = decayed state), and the
-// four row groups combine them with two cross-lane exchanges. Then
+// forms partial sums of S~^T k and S~^T q over its rows (S~ = decayed state), and the row
+// groups combine them with log2(RG) cross-lane exchanges. Then
 //     delta = beta (v - S~^T k),   o = scale (S~^T q + delta (k . q)),   S = S~ + k delta^T
 // which is o = scale S_t^T q without a second pass over the state.
 //
-// The grid is flat and 1-D (four wavefronts per 256-thread block), so N * HV * V/64 may
-// exceed 65,535. States may be laid out [K][V] or transposed, [V][K] (fla's state_v_first);
-// the state after every token can be written out as well (fla's
-// return_intermediate_states). Packed offsets are validated per slot on every call: a slot with
-// bos < 0, bos > eos, eos > T, or slot 0 not starting at 0, is skipped and flagged.
+// States stored [K][V] give each row group a contiguous run of rows, d = rg R + i: every
+// access of the CG column-group lanes is then one contiguous run of a state row. States
+// stored transposed ([V][K], fla's state_v_first) deal rows to the row groups four at a
+// time, d = 4 RG (i / 4) + 4 rg + i % 4, so the RG row-group lanes of a column read one
+// contiguous run of it. The two layouts thus sum rows in different orders, and their
+// outputs agree to fp32 rounding, not bitwise.
+//
+// BV = 64 (K = 128: 128 fp32 of state per lane, one wave per SIMD) when every sequence
+// carries about one token and the states are [K][V]: that launch is a pure state stream
+// and the longer row runs keep it closest to a plain copy. Otherwise BV = 32 (half the
+// registers, three waves per SIMD), which hides the per-token dependency chain of longer
+// sequences and, for transposed states, makes each column access a full 128-byte run.
+//
+// The grid is flat and 1-D (four wavefronts per 256-thread block), so N * HV * V/BV may
+// exceed 65,535. The state layout and whether the state after every token is written
+// out as well (fla's return_intermediate_states) are compile-time choices, so the plain
+// decode kernel carries neither. Packed offsets are validated per slot on every call: a
+// slot with bos < 0, bos > eos, eos > T, or slot 0 not starting at 0, is skipped and
+// flagged.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
 namespace {
-
-__device__ __forceinline__ void load_row_block(const __bf16* p, float* out, int n) {
-    // n consecutive bf16 values (n a multiple of 8, 16-byte aligned)
-    for (int i = 0; i < n; i += 8) {
-        bf16x8 x = *reinterpret_cast<const bf16x8*>(p + i);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) out[i + j] = (float)x[j];
-    }
-}
-
-__device__ __forceinline__ void load_row_block(const float* p, float* out, int n) {
-    for (int i = 0; i < n; i += 4) {
-        f32x4 x = *reinterpret_cast<const f32x4*>(p + i);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) out[i + j] = x[j];
-    }
-}
 
 __device__ __forceinline__ void load4(const __bf16* p, float* out) {
     bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
@@ -73,67 +70,108 @@ __device__ __forceinline__ void store4(float* p, const float* x) {
     *reinterpret_cast<f32x4*>(p) = y;
 }
 
+// Sum over the row groups: lanes CG, 2 CG, ... apart hold the same columns.
+template <int CG>
 __device__ __forceinline__ float sum_row_groups(float x) {
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
+#pragma unroll
+    for (int off = CG; off < 64; off *= 2) x += __shfl_xor(x, off, 64);
     return x;
 }
 
-// The lane's block of a state (rows d0 .. d0+R-1, columns c0 .. c0+3) in either layout:
-// [K][V] (row d at base + d V) or, with vk, [V][K] (column c at base + c K); 16-byte
-// accesses in both.
-template <int R>
-__device__ __forceinline__ void load_state(const float* base, int K, int V, bool vk, int d0, int c0,
-                                           float (&S)[R][4]) {
-    if (!vk) {
+// Row i of a lane's block in row group rg of RG, R rows each: contiguous (rg R + i), or
+// dealt four at a time (ILV) (see the work decomposition above). Rows i .. i+3, i a
+// multiple of 4, are consecutive in both.
+template <int RG, int R, bool ILV>
+__device__ __forceinline__ int block_row(int rg, int i) {
+    return ILV ? 4 * RG * (i >> 2) + 4 * rg + (i & 3) : rg * R + i;
+}
+
+// The lane's R entries of one K-vector (q, k, a gate row, dt_bias), in block-row order:
+// 16-byte accesses of 8 (bf16) or 4 (fp32) elements where the rows are contiguous, else
+// four consecutive elements at a time.
+template <int RG, int R, bool ILV>
+__device__ __forceinline__ void load_rows(const __bf16* p, int rg, float (&out)[R]) {
+    if (!ILV) {
+        p += rg * R;
 #pragma unroll
-        for (int i = 0; i < R; ++i) load4(base + (size_t)(d0 + i) * V + c0, S[i]);
+        for (int i = 0; i < R; i += 8) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(p + i);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[i + e] = (float)x[e];
+        }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < R; i += 4) load4(p + block_row<RG, R, true>(rg, i), out + i);
+    }
+}
+
+template <int RG, int R, bool ILV>
+__device__ __forceinline__ void load_rows(const float* p, int rg, float (&out)[R]) {
 #pragma unroll
-            for (int i = 0; i < R; i += 4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(base + (size_t)(c0 + j) * K + d0 + i);
+    for (int i = 0; i < R; i += 4) load4(p + block_row<RG, R, ILV>(rg, i), out + i);
+}
+
+// The lane's block of a state, columns c0 .. c0+3: [K][V] (row d at base + d V, rows
+// contiguous per row group) or, with VK, [V][K] (column c at base + c K, rows dealt four
+// at a time); 16-byte accesses in both.
+template <int RG, int R, bool VK>
+__device__ __forceinline__ void load_state(const float* base, int K, int V, int rg, int c0,
+                                           float (&S)[R][4]) {
+#pragma unroll
+    for (int i = 0; i < R; i += 4) {
+        const int d = block_row<RG, R, VK>(rg, i);
+        if (!VK) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) load4(base + (size_t)(d + e) * V + c0, S[i + e]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(base + (size_t)(c0 + j) * K + d);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[i + e][j] = x[e];
             }
+        }
     }
 }
 
-template <int R>
-__device__ __forceinline__ void store_state(float* base, int K, int V, bool vk, int d0, int c0,
+template <int RG, int R, bool VK>
+__device__ __forceinline__ void store_state(float* base, int K, int V, int rg, int c0,
                                             const float (&S)[R][4]) {
-    if (!vk) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) store4(base + (size_t)(d0 + i) * V + c0, S[i]);
-    } else {
+    for (int i = 0; i < R; i += 4) {
+        const int d = block_row<RG, R, VK>(rg, i);
+        if (!VK) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int e = 0; e < 4; ++e) store4(base + (size_t)(d + e) * V + c0, S[i + e]);
+        } else {
 #pragma unroll
-            for (int i = 0; i < R; i += 4)
-                *reinterpret_cast<f32x4*>(base + (size_t)(c0 + j) * K + d0 + i) =
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(base + (size_t)(c0 + j) * K + d) =
                     f32x4{S[i][j], S[i + 1][j], S[i + 2][j], S[i + 3][j]};
+        }
     }
 }
 
-template <int R>
+template <int CG, int R>
 __device__ __forceinline__ void l2norm_rows(float (&x)[R]) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < R; ++i) ss = fmaf(x[i], x[i], ss);
-    const float rn = l2norm_rstd(sum_row_groups(ss));
+    const float rn = l2norm_rstd(sum_row_groups<CG>(ss));
 #pragma unroll
     for (int i = 0; i < R; ++i) x[i] *= rn;
 }
 
-template <int K, typename TIn, typename TB>
+template <int K, int BV, typename TIn, typename TB, bool VK, bool INTER>
 __global__ __launch_bounds__(256) void recurrent_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ g, const InputSpec in, const TB* __restrict__ beta,
     const float* initial_state, const int32_t* __restrict__ cu_seqlens,
-    TIn* __restrict__ o, float* final_state, float* inter_states, int state_vk, int T, int H,
+    TIn* __restrict__ o, float* final_state, float* inter_states, int T, int H,
     int HV, int V, int nvt, long long n_items, float scale, int32_t* dev_status) {
-    constexpr int R = K / 4;  // rows per lane
+    constexpr int CG = BV / 4;   // column groups: lanes along the wave's BV columns
+    constexpr int RG = 64 / CG;  // row groups: lanes along K
+    constexpr int R = K / RG;    // rows per lane
     const int lane = threadIdx.x & 63;
     const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= n_items) return;
@@ -143,10 +181,9 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     const int hv = (int)(chain % HV);
     const int n = (int)(chain / HV);
     const int h = hv / (HV / H);
-    const int cg = lane & 15;
-    const int rg = lane >> 4;
-    const int c0 = vt * 64 + 4 * cg;
-    const int d0 = rg * R;
+    const int cg = lane % CG;
+    const int rg = lane / CG;
+    const int c0 = vt * BV + 4 * cg;
 
     long long row0;
     int bos, eos;
@@ -168,7 +205,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     const size_t sbase = ((size_t)n * HV + hv) * (size_t)K * V;
     float S[R][4];
     if (initial_state) {
-        load_state<R>(initial_state + sbase, K, V, state_vk, d0, c0, S);
+        load_state<RG, R, VK>(initial_state + sbase, K, V, rg, c0, S);
     } else {
 #pragma unroll
         for (int i = 0; i < R; ++i)
@@ -181,20 +218,20 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     for (int t = bos; t < eos; ++t) {
         const long long r = row0 + t;
         float kk[R], qq[R], ee[R], vv[4];
-        load_row_block(k + ((size_t)r * H + h) * K + d0, kk, R);
-        load_row_block(q + ((size_t)r * H + h) * K + d0, qq, R);
-        const size_t gofs = ((size_t)r * HV + hv) * K + d0;
+        load_rows<RG, R, VK>(k + ((size_t)r * H + h) * K, rg, kk);
+        load_rows<RG, R, VK>(q + ((size_t)r * H + h) * K, rg, qq);
+        const size_t gofs = ((size_t)r * HV + hv) * K;
         if (in.gate_mode == GATE_LOG2) {
-            load_row_block(g + gofs, ee, R);
+            load_rows<RG, R, VK>(g + gofs, rg, ee);
         } else {
             // the fused gate activation on the raw gate input
             if (in.gate_mode == GATE_RAW_BF16)
-                load_row_block(static_cast<const __bf16*>(in.g_raw) + gofs, ee, R);
+                load_rows<RG, R, VK>(static_cast<const __bf16*>(in.g_raw) + gofs, rg, ee);
             else
-                load_row_block(static_cast<const float*>(in.g_raw) + gofs, ee, R);
+                load_rows<RG, R, VK>(static_cast<const float*>(in.g_raw) + gofs, rg, ee);
             if (in.dt_bias) {
                 float db[R];
-                load_row_block(in.dt_bias + (size_t)hv * K + d0, db, R);
+                load_rows<RG, R, VK>(in.dt_bias + (size_t)hv * K, rg, db);
 #pragma unroll
                 for (int i = 0; i < R; ++i) ee[i] += db[i];
             }
@@ -205,8 +242,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
         float b = to_f32(beta[(size_t)r * HV + hv]);
         if (in.beta_sig != 0.f) b = beta_from_logit(b, in.beta_sig);
         // optional L2 normalisation of q / k (the four row groups hold a row between them)
-        if (in.l2norm_q) l2norm_rows(qq);
-        if (in.l2norm_k) l2norm_rows(kk);
+        if (in.l2norm_q) l2norm_rows<CG>(qq);
+        if (in.l2norm_k) l2norm_rows<CG>(kk);
 
         float p[4] = {0.f, 0.f, 0.f, 0.f};
         float rq[4] = {0.f, 0.f, 0.f, 0.f};
@@ -223,12 +260,12 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
                 rq[j] = fmaf(qq[i], s, rq[j]);
             }
         }
-        kq = sum_row_groups(kq);
+        kq = sum_row_groups<CG>(kq);
         float delta[4], out[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            p[j] = sum_row_groups(p[j]);
-            rq[j] = sum_row_groups(rq[j]);
+            p[j] = sum_row_groups<CG>(p[j]);
+            rq[j] = sum_row_groups<CG>(rq[j]);
             delta[j] = b * (vv[j] - p[j]);
             out[j] = scale * fmaf(delta[j], kq, rq[j]);
         }
@@ -238,24 +275,35 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
             for (int j = 0; j < 4; ++j) S[i][j] = fmaf(kk[i], delta[j], S[i][j]);
         if (rg == 0) store4(o + ((size_t)r * HV + hv) * V + c0, out);
         // the state after this token, in the states' layout
-        if (inter_states) store_state<R>(inter_states + ((size_t)r * HV + hv) * (size_t)K * V, K, V, state_vk, d0, c0, S);
+        if (INTER) store_state<RG, R, VK>(inter_states + ((size_t)r * HV + hv) * (size_t)K * V, K, V, rg, c0, S);
     }
 
-    if (final_state) store_state<R>(final_state + sbase, K, V, state_vk, d0, c0, S);
+    if (final_state) store_state<RG, R, VK>(final_state + sbase, K, V, rg, c0, S);
+}
+
+template <int K, int BV, typename TIn, typename TB, bool VK, bool INTER>
+hipError_t launch_v(const RecurrentArgs& a) {
+    const int nvt = a.V / BV;
+    const long long n_items = (long long)a.N * a.HV * nvt;
+    if (n_items == 0) return hipSuccess;
+    const long long blocks = (n_items + 3) / 4;
+    hipLaunchKernelGGL((recurrent_kernel<K, BV, TIn, TB, VK, INTER>), dim3((unsigned)blocks), dim3(256), 0,
+                       a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.in,
+                       (const TB*)a.beta, a.initial_state, a.cu_seqlens, (TIn*)a.o,
+                       a.final_state, a.inter_states, a.T, a.H, a.HV, a.V, nvt, n_items, a.scale,
+                       a.dev_status);
+    return hipGetLastError();
 }
 
 template <int K, typename TIn, typename TB>
 hipError_t launch_t(const RecurrentArgs& a) {
-    const int nvt = a.V / 64;
-    const long long n_items = (long long)a.N * a.HV * nvt;
-    if (n_items == 0) return hipSuccess;
-    const long long blocks = (n_items + 3) / 4;
-    hipLaunchKernelGGL((recurrent_kernel<K, TIn, TB>), dim3((unsigned)blocks), dim3(256), 0,
-                       a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.in,
-                       (const TB*)a.beta, a.initial_state, a.cu_seqlens, (TIn*)a.o,
-                       a.final_state, a.inter_states, a.state_vk, a.T, a.H, a.HV, a.V, nvt, n_items, a.scale,
-                       a.dev_status);
-    return hipGetLastError();
+    if (a.state_vk)
+        return a.inter_states ? launch_v<K, 32, TIn, TB, true, true>(a) : launch_v<K, 32, TIn, TB, true, false>(a);
+    // about one token per sequence: B T rows over N sequences, at most 1.5 on average
+    const bool one_token = 2LL * a.B * a.T <= 3LL * a.N;
+    if (one_token)
+        return a.inter_states ? launch_v<K, 64, TIn, TB, false, true>(a) : launch_v<K, 64, TIn, TB, false, false>(a);
+    return a.inter_states ? launch_v<K, 32, TIn, TB, false, true>(a) : launch_v<K, 32, TIn, TB, false, false>(a);
 }
 
 template <int K>
