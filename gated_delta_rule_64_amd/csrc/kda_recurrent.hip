@@ -101,14 +101,22 @@ __device__ __forceinline__ void load_rows(const __bf16* p, int rg, float (&out)[
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < R; i += 4) load4(p + block_row<RG, R, true>(rg, i), out + i);
+        for (int i = 0; i < R; i += 4) {
+            const bf16x4 x = *reinterpret_cast<const bf16x4*>(p + block_row<RG, R, true>(rg, i));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[i + e] = (float)x[e];
+        }
     }
 }
 
 template <int RG, int R, bool ILV>
 __device__ __forceinline__ void load_rows(const float* p, int rg, float (&out)[R]) {
 #pragma unroll
-    for (int i = 0; i < R; i += 4) load4(p + block_row<RG, R, ILV>(rg, i), out + i);
+    for (int i = 0; i < R; i += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(p + block_row<RG, R, ILV>(rg, i));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[i + e] = x[e];
+    }
 }
 
 // The lane's block of a state, columns c0 .. c0+3: [K][V] (row d at base + d V, rows
@@ -116,13 +124,13 @@ __device__ __forceinline__ void load_rows(const float* p, int rg, float (&out)[R
 // at a time); 16-byte accesses in both.
 template <int RG, int R, bool VK>
 __device__ __forceinline__ void load_state(const float* base, int K, int V, int rg, int c0,
-                                           float (&S)[R][4]) {
+                                           f32x4 (&S)[R]) {
 #pragma unroll
     for (int i = 0; i < R; i += 4) {
         const int d = block_row<RG, R, VK>(rg, i);
         if (!VK) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) load4(base + (size_t)(d + e) * V + c0, S[i + e]);
+            for (int e = 0; e < 4; ++e) S[i + e] = *reinterpret_cast<const f32x4*>(base + (size_t)(d + e) * V + c0);
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -136,13 +144,13 @@ __device__ __forceinline__ void load_state(const float* base, int K, int V, int 
 
 template <int RG, int R, bool VK>
 __device__ __forceinline__ void store_state(float* base, int K, int V, int rg, int c0,
-                                            const float (&S)[R][4]) {
+                                            const f32x4 (&S)[R]) {
 #pragma unroll
     for (int i = 0; i < R; i += 4) {
         const int d = block_row<RG, R, VK>(rg, i);
         if (!VK) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) store4(base + (size_t)(d + e) * V + c0, S[i + e]);
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<f32x4*>(base + (size_t)(d + e) * V + c0) = S[i + e];
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -203,14 +211,12 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     }
 
     const size_t sbase = ((size_t)n * HV + hv) * (size_t)K * V;
-    float S[R][4];
+    f32x4 S[R];   // row i of the lane's block, columns c0 .. c0+3
     if (initial_state) {
         load_state<RG, R, VK>(initial_state + sbase, K, V, rg, c0, S);
     } else {
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) S[i][j] = 0.0f;
+        for (int i = 0; i < R; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     const float amp = in.gate_mode != GATE_LOG2 ? -expf(in.A_log[hv]) : 0.f;
