@@ -11,6 +11,8 @@ Also reported on the same JSON line:
   * roofline  -- the dominant kernel (the one with the largest average duration, timed
                  live with HIP events recorded by kda_chunk_fwd_timed on the library's
                  stream) against HBM peak, with that kernel's algorithmic bytes;
+  * flushed   -- the headline forward timed one rep at a time with a 512 MB write between
+                 reps (so its inputs come from HBM, not the 256 MB MALL): median, p10, p90;
   * path      -- the whole step against the HBM floor of the workload's own inputs and
                  outputs (336.1 MB), and the matrix-core fractions;
   * gated     -- the same forward with the gate activation fused into Stage 1 (raw bf16
@@ -19,7 +21,8 @@ Also reported on the same JSON line:
                  sigmoid x2); the decode line carries the same for the recurrent path;
   * backward  -- the chunked backward of the headline forward (every input gradient);
   * decode    -- the per-token recurrent forward on 4096 sequences x 32 heads (one token
-                 each, fp32 states in and out): state GB/s and fraction of HBM peak;
+                 each, fp32 states in and out): state GB/s and fraction of HBM peak,
+                 and a plain-stream ceiling (torch.neg over the same state bytes);
   * cpu_baseline -- the fp64 CPU oracle on the full headline workload, host threads.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
@@ -107,12 +110,34 @@ def traffic_from_profiles(kernel_key):
     return d.get("bytes_per_launch", {}).get(kernel_key)
 
 
+def flushed_reps(call, reps, tokens, hip, sptr, dev):
+    """Time ``call`` one rep at a time with a 512 MB write between reps (outside the
+    events); median, p10, p90 of the reps."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    rev = Events(hip, 2 * reps)
+    for r in range(reps):
+        flush.fill_(r & 0xFF)
+        hip.hipEventRecord(rev.ev[2 * r], sptr)
+        call(None)
+        hip.hipEventRecord(rev.ev[2 * r + 1], sptr)
+    torch.cuda.synchronize()
+    reps_ms = sorted(rev.ms(2 * r, 2 * r + 1) for r in range(reps))
+    rev.close()
+    del flush
+    pct = lambda q: reps_ms[min(len(reps_ms) - 1, int(q * len(reps_ms)))]
+    return {"reps": reps, "median_ms": pct(0.5), "p10_ms": pct(0.1), "p90_ms": pct(0.9),
+            "tokens_per_s_median": tokens / (pct(0.5) * 1e-3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=10)
+    ap.add_argument("--flushed-reps", type=int, default=50,
+                    help="reps of the headline forward timed one at a time with a cache flush between")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain elementwise kernel that reads and writes 1 GiB "
@@ -187,6 +212,13 @@ def main():
     ms_per_step = total_ms / steps
     tokens = B * T
     tok_s = tokens / (ms_per_step * 1e-3)
+
+    # the same forward timed one rep at a time with a 512 MB write between reps (outside
+    # the events), so the inputs (336 MB) are not served from the 256 MB MALL: median,
+    # p10, p90 over the reps
+    flushed = None
+    if args.flushed_reps > 0:
+        flushed = flushed_reps(call, args.flushed_reps, tokens, hip, sptr, dev)
 
     # algorithmic quantities of the workload (inputs + outputs once, flops of the method)
     path_bytes = (2 * B * T * H * K * 2 + B * T * HV * V * 2 * 2 + B * T * HV * K * 4 + B * T * HV * 2)
@@ -372,6 +404,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": dom_bytes, "avg_launch_ms": dom_ms,
                      "kernels_ms": {"intra": intra_ms, "scan": scan_ms}},
+        "flushed": flushed,
         "path": {"hbm_floor_bytes": path_bytes, "achieved_GBs": path_bytes / (ms_per_step * 1e-3) / 1e9,
                  "hbm_frac": path_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "mfma_frac_exact_flops": flops_exact / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
