@@ -522,6 +522,142 @@ __global__ __launch_bounds__(BT, 2) void bwd_state_kernel(BwdParams p) {
     }
 }
 
+// The same products for bf16 inputs on the bf16 matrix cores: every fp32 operand is
+// carried as a hi + lo bf16 pair and a product is hi*hi + lo*hi + hi*lo (do, a bf16
+// input, is exact in bf16 and has no residual). Contraction over V in slices of 32: one
+// v_mfma_f32_16x16x32_bf16 step per slice. The operands sit in LDS as bf16 rows of
+// 32 values padded to 40 (80 bytes), so the 16 rows of a fragment read start in 16
+// distinct four-bank groups. Sixteen waves (four per SIMD): wave w owns row band w % 4
+// and a quarter of the 16-column tiles of K (part w / 4), and the band's dAqk tile
+// J = part when J <= band.
+constexpr int SB_LD = 40;          // bf16 row stride of the operand tiles
+constexpr int SB_THREADS = 1024;
+
+// Rows [0, R) x columns [0, W) of a row-major fp32 array into hi / lo bf16 LDS rows.
+template <int R, int W>
+__device__ __forceinline__ void stage_split(const float* src, size_t gstride, __bf16* hi, __bf16* lo, int tid) {
+    constexpr int W4 = W / 4;
+#pragma unroll 2
+    for (int q = tid; q < R * W4; q += SB_THREADS) {
+        const int r = q / W4, c4 = 4 * (q % W4);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + (size_t)r * gstride + c4);
+        bf16x4 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = (__bf16)x[e];
+            l[e] = (__bf16)(x[e] - (float)h[e]);
+        }
+        *reinterpret_cast<bf16x4*>(hi + r * SB_LD + c4) = h;
+        *reinterpret_cast<bf16x4*>(lo + r * SB_LD + c4) = l;
+    }
+}
+
+// Rows of a bf16 input into LDS (row r at src + r * rstride), zeros from row `len` on.
+template <int R, int W>
+__device__ __forceinline__ void stage_rows_bf16(const __bf16* src, size_t rstride, int len, __bf16* dst, int tid) {
+    constexpr int W4 = W / 4;
+    for (int q = tid; q < R * W4; q += SB_THREADS) {
+        const int r = q / W4, c4 = 4 * (q % W4);
+        bf16x4 h = {};
+        if (r < len) h = *reinterpret_cast<const bf16x4*>(src + (size_t)r * rstride + c4);
+        *reinterpret_cast<bf16x4*>(dst + r * SB_LD + c4) = h;
+    }
+}
+
+// The operand fragment of tile row `row`: lane (lq, lr) of a 16-row band reads values
+// 8 lq .. 8 lq + 7 of its row.
+__device__ __forceinline__ bf16x8 sb_frag(const __bf16* t, int row, int lq) {
+    return *reinterpret_cast<const bf16x8*>(t + row * SB_LD + 8 * lq);
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(SB_THREADS, 4) void bwd_state_bf16_kernel(BwdParams p) {
+    constexpr int VC = 32, NKH = K / 64;   // 16-column tiles of K per part
+    typedef GsLayout<K> GL;
+    typedef Mma<__bf16> M;
+    __shared__ __attribute__((aligned(16))) __bf16 hH[K * SB_LD], hLo[K * SB_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 dhH[K * SB_LD], dhLo[K * SB_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 doH[C * SB_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 vnH[C * SB_LD], vnLo[C * SB_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 dvH[C * SB_LD], dvLo[C * SB_LD];
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int band = wave & 3, part = wave >> 2;
+    int c, hv;
+    int2 pos;
+    if (!bwd_chunk(p, c, hv, pos)) return;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const float* hC = p.h + ci * (size_t)K * V;
+    const float* dhC = p.dh + ci * (size_t)K * V;
+    const float* vnC = p.vn + ci * (size_t)C * V;
+    const float* dvC = p.dvn + ci * (size_t)C * V;
+    const __bf16* dout = reinterpret_cast<const __bf16*>(p.dout);
+    const int r0 = 16 * band;
+    const int j0 = NKH * part;
+
+    f32x4 aq[NKH], aw[NKH], ak[NKH], aA;
+#pragma unroll
+    for (int j = 0; j < NKH; ++j) { aq[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aw[j] = aq[j]; ak[j] = aq[j]; }
+    aA = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dgacc = 0.f;   // thread d < K: sum_v dS[d][v] S[d][v]
+    for (int vb = 0; vb < V; vb += VC) {
+        stage_split<K, VC>(hC + vb, V, hH, hLo, tid);
+        stage_split<K, VC>(dhC + vb, V, dhH, dhLo, tid);
+        stage_rows_bf16<C, VC>(dout + ((size_t)pos.x * p.HV + hv) * V + vb, (size_t)p.HV * V, pos.y, doH, tid);
+        stage_split<C, VC>(vnC + vb, V, vnH, vnLo, tid);
+        stage_split<C, VC>(dvC + vb, V, dvH, dvLo, tid);
+        __syncthreads();
+        if (tid < K)
+            for (int vv = 0; vv < VC; ++vv) {
+                const int e = tid * SB_LD + vv;
+                dgacc = fmaf((float)dhH[e] + (float)dhLo[e], (float)hH[e] + (float)hLo[e], dgacc);
+            }
+        const bf16x8 a_do = sb_frag(doH, r0 + lr, lq);
+        const bf16x8 a_dvh = sb_frag(dvH, r0 + lr, lq), a_dvl = sb_frag(dvLo, r0 + lr, lq);
+        const bf16x8 a_vnh = sb_frag(vnH, r0 + lr, lq), a_vnl = sb_frag(vnLo, r0 + lr, lq);
+#pragma unroll
+        for (int j = 0; j < NKH; ++j) {
+            const int row = 16 * (j0 + j) + lr;
+            const bf16x8 bh = sb_frag(hH, row, lq), bl = sb_frag(hLo, row, lq);
+            const bf16x8 dh = sb_frag(dhH, row, lq), dl = sb_frag(dhLo, row, lq);
+            aq[j] = M::mma(a_do, bh, aq[j]);
+            aq[j] = M::mma(a_do, bl, aq[j]);
+            aw[j] = M::mma(a_dvh, bh, aw[j]);
+            aw[j] = M::mma(a_dvl, bh, aw[j]);
+            aw[j] = M::mma(a_dvh, bl, aw[j]);
+            ak[j] = M::mma(a_vnh, dh, ak[j]);
+            ak[j] = M::mma(a_vnl, dh, ak[j]);
+            ak[j] = M::mma(a_vnh, dl, ak[j]);
+        }
+        // dAqk tile (band, J = part), J <= band
+        if (part <= band) {
+            const bf16x8 vh = sb_frag(vnH, 16 * part + lr, lq), vl = sb_frag(vnLo, 16 * part + lr, lq);
+            aA = M::mma(a_do, vh, aA);
+            aA = M::mma(a_do, vl, aA);
+        }
+        __syncthreads();
+    }
+    float* out = p.gs + ci * (size_t)GL::FLOATS;
+#pragma unroll
+    for (int j = 0; j < NKH; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = r0 + 4 * lq + r, d = 16 * (j0 + j) + lr;
+            out[GL::DQG + row * K + d] = aq[j][r];
+            out[GL::DW + row * K + d] = -aw[j][r];
+            out[GL::DKG + row * K + d] = ak[j][r];
+        }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 4 * lq + r, s = 16 * part + lr;
+        out[GL::DA + row * C + s] = (part <= band && s <= row) ? aA[r] : 0.f;
+    }
+    if (tid < K) {
+        const float eg = reinterpret_cast<const float*>(p.rec + ci * p.rec_bytes + p.off_eg)[tid];
+        out[GL::DG + tid] = LN2F * eg * dgacc;
+    }
+}
+
 // ------------------------------------------------------------------------------------
 // backward of the WY inverse, per (chunk, value head): with M and T from the recompute,
 // writes dv and dbeta (final) and dkd, dM for the pair kernel. Eight waves; every product
@@ -979,7 +1115,10 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (nchunk_items > 0) {
-        hipLaunchKernelGGL((bwd_state_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
+        if constexpr (sizeof(TIn) == 2)
+            hipLaunchKernelGGL((bwd_state_bf16_kernel<K, V>), dim3((unsigned)nchunk_items), dim3(SB_THREADS), 0, a.stream, p);
+        else
+            hipLaunchKernelGGL((bwd_state_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(WY_THREADS), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
