@@ -442,6 +442,115 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_kernel(BwdParams p) {
     }
 }
 
+// The same prep for bf16 inputs on the bf16 matrix cores. The records carry Aqk and qg
+// as hi + lo bf16 pairs and do is a bf16 input, so P1 = Aqk_hi^T do + Aqk_lo^T do and
+// P2 likewise are exact products accumulated in fp32 (the fp32 prep's result up to
+// summation order). The contraction runs over the chunk's rows, so Aqk, qg and do are
+// staged transposed into bf16 LDS rows of 64 padded to 72 (144 bytes: the 16 rows of a
+// fragment read start in 16 distinct four-bank groups). The same LDS then stages w and
+// kg^T in fp32 for the fragment-order copies, as in the fp32 prep.
+constexpr int PT_LD = 72;
+
+template <int K, int V>
+__global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
+    constexpr int LA = C + 1, LK = K + 1;
+    typedef ScanOps<K, V> SO;
+    typedef FragTile<float, C, K> FKG;
+    typedef FragTile<float, K, C> FWT;
+    typedef Mma<__bf16> M;
+    constexpr int T_BYTES = (2 * C + 2 * K + V) * PT_LD * 2;
+    constexpr int F_BYTES = (C * LK + K * LA) * 4;
+    __shared__ __attribute__((aligned(16))) char smem[T_BYTES > F_BYTES ? T_BYTES : F_BYTES];
+    __bf16* aTh = reinterpret_cast<__bf16*>(smem);   // Aqk^T [s][r], hi
+    __bf16* aTl = aTh + C * PT_LD;                   //                lo
+    __bf16* qTh = aTl + C * PT_LD;                   // qg^T [d][r], hi
+    __bf16* qTl = qTh + K * PT_LD;                   //               lo
+    __bf16* dT = qTl + K * PT_LD;                    // do^T [v][r]
+    float* R0 = reinterpret_cast<float*>(smem);      // w [r][d]        (second phase)
+    float* R1 = R0 + C * LK;                         // kg^T [d][s]
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int c, hv;
+    int2 pos;
+    if (!bwd_chunk(p, c, hv, pos)) return;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const char* rec = p.rec + ci * p.rec_bytes;
+    const __bf16* dout = reinterpret_cast<const __bf16*>(p.dout);
+    float* ops = p.sops + ci * (size_t)SO::FLOATS;
+
+    // a fragment-order record tile (R rows, KC contraction; residual at + R*KC), each
+    // lane run of 8 transposed into column-major LDS: dst[col * PT_LD + row]
+    auto stage_t = [&](const __bf16* t, int R, int KC, __bf16* dh, __bf16* dl) {
+        const int NS = KC / M::KS;
+        for (int q = tid; q < R * KC / 8; q += BT) {
+            const int e0 = 8 * q;
+            const int l = q % 64, blk = q / 64;
+            const int row = 16 * (blk / NS) + (l & 15);
+            const int col = (blk % NS) * M::KS + (l >> 4) * M::KPL;
+            const bf16x8 h = *reinterpret_cast<const bf16x8*>(t + e0);
+            const bf16x8 lo = *reinterpret_cast<const bf16x8*>(t + e0 + R * KC);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                dh[(col + x) * PT_LD + row] = h[x];
+                dl[(col + x) * PT_LD + row] = lo[x];
+            }
+        }
+    };
+    stage_t(reinterpret_cast<const __bf16*>(rec + p.off_aqk), C, C, aTh, aTl);
+    stage_t(reinterpret_cast<const __bf16*>(rec + p.off_qg), C, K, qTh, qTl);
+    // do rows r < len (zeros after), 8 values per thread and step, transposed
+    for (int q = tid; q < C * V / 8; q += BT) {
+        const int r = q / (V / 8), v0 = 8 * (q % (V / 8));
+        bf16x8 x = {};
+        if (r < pos.y) x = *reinterpret_cast<const bf16x8*>(dout + ((size_t)(pos.x + r) * p.HV + hv) * V + v0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dT[(v0 + e) * PT_LD + r] = x[e];
+    }
+    __syncthreads();
+    auto frag = [&](const __bf16* t, int row, int ks) {
+        return *reinterpret_cast<const bf16x8*>(t + row * PT_LD + 32 * ks + 8 * lq);
+    };
+    // P1[s][v] = sum_r Aqk[r][s] do[r][v]: wave w owns rows 16w ..
+    for (int nt = 0; nt < V / 16; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C / 32; ++ks) {
+            const bf16x8 b = frag(dT, 16 * nt + lr, ks);
+            acc = M::mma(frag(aTh, 16 * wave + lr, ks), b, acc);
+            acc = M::mma(frag(aTl, 16 * wave + lr, ks), b, acc);
+        }
+        *reinterpret_cast<f32x4*>(ops + SO::P1 + AccTile::quad(16 * nt + lr, 16 * wave + 4 * lq)) = acc;
+    }
+    // P2[d][v] = sum_r qg[r][d] do[r][v]: wave w owns bands w, w + 4, ..
+    for (int db = wave; db < K / 16; db += 4)
+        for (int nt = 0; nt < V / 16; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < C / 32; ++ks) {
+                const bf16x8 b = frag(dT, 16 * nt + lr, ks);
+                acc = M::mma(frag(qTh, 16 * db + lr, ks), b, acc);
+                acc = M::mma(frag(qTl, 16 * db + lr, ks), b, acc);
+            }
+            *reinterpret_cast<f32x4*>(ops + SO::P2 + acc_kv<K>(16 * nt + lr, 16 * db + 4 * lq)) = acc;
+        }
+    __syncthreads();
+    stage_record<__bf16, C, K>(reinterpret_cast<const __bf16*>(rec + p.off_w), false, R0, LK, tid);
+    stage_record<__bf16, K, C>(reinterpret_cast<const __bf16*>(rec + p.off_kgT), true, R1, LA, tid);
+    __syncthreads();
+    // kg in fragment order (rows s, contraction d) and w^T (rows d, contraction r)
+    for (int e = tid; e < C * K; e += BT) {
+        const int l = e % 64, blk = e / 64;
+        {
+            const int row = 16 * (blk / FKG::NS) + (l & 15), col = 4 * (blk % FKG::NS) + (l >> 4);
+            ops[SO::KG + e] = R1[col * LA + row];
+        }
+        {
+            const int row = 16 * (blk / FWT::NS) + (l & 15), col = 4 * (blk % FWT::NS) + (l >> 4);
+            ops[SO::WT + e] = R0[col * LK + row];
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------------
 // products with the state checkpoints, per (chunk, value head): dqg = do S^T,
 // dw = -dv' S^T, dkg = v' dS^T, dAqk = do v'^T (s <= r), dG = ln2 2^G rowsum(dS S).
@@ -1107,7 +1216,10 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
     const long long nchunk_items = (long long)L.fwd.NCmax * a.HV;
     if (nchunk_items > 0) {
         // the records are in the input type (bf16 hi/lo pairs, or fp32)
-        hipLaunchKernelGGL((bwd_prep_kernel<K, V, TIn, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
+        if constexpr (sizeof(TIn) == 2)
+            hipLaunchKernelGGL((bwd_prep_bf16_kernel<K, V>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
+        else
+            hipLaunchKernelGGL((bwd_prep_kernel<K, V, TIn, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (chains > 0) {
