@@ -241,11 +241,12 @@ __device__ __forceinline__ int acc_kv(int v, int d) {
     return (((v >> 4) * (K / 16) + (d >> 4)) * 64 + (v & 15) + 16 * ((d & 15) >> 2)) * 4 + (d & 3);
 }
 
-// Per (value head, chunk) operands of the reverse scan, fp32: kg in fragment order as
-// the A operand of kg dS ([64][K]), w^T in fragment order as the A operand of w^T dv'
+// Per (value head, chunk) operands of the reverse scan: kg in fragment order as the A
+// operand of kg dS ([64][K]), w^T in fragment order as the A operand of w^T dv'
 // ([K][64]), P1 = Aqk^T do ([64][V], AccTile order) and P2 = qg^T do ([K][V], acc_kv
-// order). P1 and P2 do not depend on the state gradient, so they are formed in
-// parallel before the scan.
+// order), all fp32 for fp32 inputs; for bf16 inputs kg is a hi + lo pair and w^T one
+// bf16 tile in 16x16x32 fragment order, in the same slots. P1 and P2 do not depend on
+// the state gradient, so they are formed in parallel before the scan.
 template <int K, int V>
 struct ScanOps {
     static constexpr int KG = 0, WT = C * K, P1 = 2 * C * K, P2 = 2 * C * K + C * V;
@@ -442,32 +443,179 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_kernel(BwdParams p) {
     }
 }
 
+// The reverse scan for bf16 inputs: kg (hi, lo) and w^T in bf16 fragment order from the
+// bf16 prep, dS and dv' exchanged through LDS as hi + lo bf16 rows, products on
+// v_mfma_f32_16x16x32_bf16 (hi*hi + lo*hi + hi*lo; w^T is exact, two products). The
+// chain per chunk is 4 + 2 dependent steps per wave instead of 32 + 16 fp32 ones.
+template <int K, int V>
+struct DscanFragsB {
+    static constexpr int NKS = K / 32, NJS = C / 32, NDT = K / 64;
+    bf16x8 kg[2][NKS];        // hi, lo
+    bf16x8 wt[NDT][NJS];
+    f32x4 p1;
+    f32x4 p2[NDT];
+    f32x4 e[NDT];
+};
+
+template <int K, int V>
+__device__ __forceinline__ void load_dscan_b(DscanFragsB<K, V>& F, const BwdParams& p, int hv, int c,
+                                             int wave, int lane, int v0) {
+    typedef ScanOps<K, V> SO;
+    typedef FragTile<__bf16, C, K> FKG;
+    typedef FragTile<__bf16, K, C> FWT;
+    typedef DscanFragsB<K, V> DF;
+    const int lr = lane & 15, lq = lane >> 4;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const float* ops = p.sops + ci * (size_t)SO::FLOATS;
+    const __bf16* kg = reinterpret_cast<const __bf16*>(ops + SO::KG);
+    const __bf16* wt = reinterpret_cast<const __bf16*>(ops + SO::WT);
+    const float* eg = reinterpret_cast<const float*>(p.rec + ci * p.rec_bytes + p.off_eg);
+#pragma unroll
+    for (int kk = 0; kk < DF::NKS; ++kk) {
+        F.kg[0][kk] = *reinterpret_cast<const bf16x8*>(kg + FKG::frag(wave, kk, lane));
+        F.kg[1][kk] = *reinterpret_cast<const bf16x8*>(kg + C * K + FKG::frag(wave, kk, lane));
+    }
+#pragma unroll
+    for (int a = 0; a < DF::NDT; ++a) {
+#pragma unroll
+        for (int jj = 0; jj < DF::NJS; ++jj)
+            F.wt[a][jj] = *reinterpret_cast<const bf16x8*>(wt + FWT::frag(wave + 4 * a, jj, lane));
+        F.p2[a] = *reinterpret_cast<const f32x4*>(ops + SO::P2 + acc_kv<K>(v0 + lr, 16 * (wave + 4 * a) + 4 * lq));
+        F.e[a] = *reinterpret_cast<const f32x4*>(eg + 16 * (wave + 4 * a) + 4 * lq);
+    }
+    F.p1 = *reinterpret_cast<const f32x4*>(ops + SO::P1 + AccTile::quad(v0 + lr, 16 * wave + 4 * lq));
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
+    constexpr int BV = 16, NVT = V / BV, NDT = K / 64;
+    constexpr int LDK = K + 8, LDC = C + 8;   // bf16 row strides (16 distinct bank groups per fragment)
+    typedef DscanFragsB<K, V> DF;
+    typedef Mma<__bf16> M;
+    __shared__ __attribute__((aligned(16))) __bf16 dSh[BV * LDK], dSl[BV * LDK];   // dS^T [v][d]
+    __shared__ __attribute__((aligned(16))) __bf16 dvh[BV * LDC], dvl[BV * LDC];   // dv'^T [v][r]
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = p.N * p.HV * NVT;
+    const int item = xcd_remap(blockIdx.x, G);
+    const int vt = item % NVT, chain = item / NVT;
+    const int hv = chain % p.HV, n = chain / p.HV;
+    const int v0 = vt * BV;
+    if (!p.dense && !p.slot_ok[n]) return;
+    const int c0 = p.dense ? n * p.NT : p.coff[n];
+    const int c1 = p.dense ? c0 + p.NT : p.cend[n];
+    const size_t sbase = ((size_t)n * p.HV + hv) * (size_t)K * V;
+
+    // four consecutive rows (d or r) of column lr: hi and lo
+    auto put4 = [&](__bf16* hi, __bf16* lo, int off, f32x4 x) {
+        bf16x4 h, l;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            h[r] = (__bf16)x[r];
+            l[r] = (__bf16)(x[r] - (float)h[r]);
+        }
+        *reinterpret_cast<bf16x4*>(hi + off) = h;
+        *reinterpret_cast<bf16x4*>(lo + off) = l;
+    };
+    f32x4 dS[NDT];
+#pragma unroll
+    for (int a = 0; a < NDT; ++a) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d = 16 * (wave + 4 * a) + 4 * lq + r;
+            dS[a][r] = p.dht ? p.dht[sbase + (size_t)d * V + v0 + lr] : 0.f;
+        }
+        put4(dSh, dSl, lr * LDK + 16 * (wave + 4 * a) + 4 * lq, dS[a]);
+    }
+    // two-chunk ring: F0 holds chunk c, F1 chunk c - 1; past the first chunk a buffer
+    // re-reads chunk c0 (in bounds, never used)
+    auto clampc = [&](int c) { return c >= c0 ? c : c0; };
+    DF F0, F1;
+    if (c0 < c1) {
+        load_dscan_b<K, V>(F0, p, hv, c1 - 1, wave, lane, v0);
+        load_dscan_b<K, V>(F1, p, hv, clampc(c1 - 2), wave, lane, v0);
+    }
+    __syncthreads();
+    auto step = [&](DF& F, int c) {
+        const size_t ci = (size_t)hv * p.NCmax + c;
+        float* dhb = p.dh + ci * (size_t)K * V;
+#pragma unroll
+        for (int a = 0; a < NDT; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dhb[(size_t)(16 * (wave + 4 * a) + 4 * lq + r) * V + v0 + lr] = dS[a][r];
+        // dv' = P1 + kg dS (rows 16 wave + 4 lq + r, column lr of the slice)
+        f32x4 acc = F.p1, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < DF::NKS; ++kk) {
+            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(dSh + lr * LDK + 32 * kk + 8 * lq);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(dSl + lr * LDK + 32 * kk + 8 * lq);
+            acc = M::mma(F.kg[0][kk], bh, acc);
+            acc2 = M::mma(F.kg[1][kk], bh, acc2);
+            acc2 = M::mma(F.kg[0][kk], bl, acc2);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += acc2[r];
+        float* dvb = p.dvn + ci * (size_t)C * V;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dvb[(size_t)(16 * wave + 4 * lq + r) * V + v0 + lr] = acc[r];
+        put4(dvh, dvl, lr * LDC + 16 * wave + 4 * lq, acc);
+        __syncthreads();
+        // dS <- 2^G dS + P2 - w^T dv'
+#pragma unroll
+        for (int a = 0; a < NDT; ++a) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < DF::NJS; ++jj) {
+                x = M::mma(F.wt[a][jj], *reinterpret_cast<const bf16x8*>(dvh + lr * LDC + 32 * jj + 8 * lq), x);
+                x = M::mma(F.wt[a][jj], *reinterpret_cast<const bf16x8*>(dvl + lr * LDC + 32 * jj + 8 * lq), x);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dS[a][r] = fmaf(F.e[a][r], dS[a][r], F.p2[a][r] - x[r]);
+            put4(dSh, dSl, lr * LDK + 16 * (wave + 4 * a) + 4 * lq, dS[a]);
+        }
+        __syncthreads();
+    };
+    const int nsteps = c1 - c0;
+    int c = c1 - 1;
+    for (int t = 0; t < nsteps / 2; ++t, c -= 2) {
+        step(F0, c);
+        load_dscan_b<K, V>(F0, p, hv, clampc(c - 2), wave, lane, v0);
+        step(F1, c - 1);
+        load_dscan_b<K, V>(F1, p, hv, clampc(c - 3), wave, lane, v0);
+    }
+    if (nsteps & 1) step(F0, c);
+    if (p.dh0) {
+#pragma unroll
+        for (int a = 0; a < NDT; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                p.dh0[sbase + (size_t)(16 * (wave + 4 * a) + 4 * lq + r) * V + v0 + lr] = dS[a][r];
+    }
+}
+
 // The same prep for bf16 inputs on the bf16 matrix cores. The records carry Aqk and qg
 // as hi + lo bf16 pairs and do is a bf16 input, so P1 = Aqk_hi^T do + Aqk_lo^T do and
 // P2 likewise are exact products accumulated in fp32 (the fp32 prep's result up to
 // summation order). The contraction runs over the chunk's rows, so Aqk, qg and do are
 // staged transposed into bf16 LDS rows of 64 padded to 72 (144 bytes: the 16 rows of a
 // fragment read start in 16 distinct four-bank groups). The same LDS then stages w and
-// kg^T in fp32 for the fragment-order copies, as in the fp32 prep.
+// kg^T for the reverse scan's operands, here in bf16 fragment order for
+// v_mfma_f32_16x16x32_bf16: kg as hi + lo (rows s, contraction d), w^T (rows d,
+// contraction r; w is a single bf16 in the record, so this copy is exact).
 constexpr int PT_LD = 72;
 
 template <int K, int V>
 __global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
-    constexpr int LA = C + 1, LK = K + 1;
     typedef ScanOps<K, V> SO;
-    typedef FragTile<float, C, K> FKG;
-    typedef FragTile<float, K, C> FWT;
     typedef Mma<__bf16> M;
-    constexpr int T_BYTES = (2 * C + 2 * K + V) * PT_LD * 2;
-    constexpr int F_BYTES = (C * LK + K * LA) * 4;
+    constexpr int T_BYTES = (2 * C + 2 * K + V) * PT_LD * 2;     // first phase
+    constexpr int F_BYTES = 2 * K * PT_LD * 2 + C * (K + 8) * 2;  // second phase
     __shared__ __attribute__((aligned(16))) char smem[T_BYTES > F_BYTES ? T_BYTES : F_BYTES];
     __bf16* aTh = reinterpret_cast<__bf16*>(smem);   // Aqk^T [s][r], hi
     __bf16* aTl = aTh + C * PT_LD;                   //                lo
     __bf16* qTh = aTl + C * PT_LD;                   // qg^T [d][r], hi
     __bf16* qTl = qTh + K * PT_LD;                   //               lo
     __bf16* dT = qTl + K * PT_LD;                    // do^T [v][r]
-    float* R0 = reinterpret_cast<float*>(smem);      // w [r][d]        (second phase)
-    float* R1 = R0 + C * LK;                         // kg^T [d][s]
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int c, hv;
@@ -534,19 +682,49 @@ __global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
             *reinterpret_cast<f32x4*>(ops + SO::P2 + acc_kv<K>(16 * nt + lr, 16 * db + 4 * lq)) = acc;
         }
     __syncthreads();
-    stage_record<__bf16, C, K>(reinterpret_cast<const __bf16*>(rec + p.off_w), false, R0, LK, tid);
-    stage_record<__bf16, K, C>(reinterpret_cast<const __bf16*>(rec + p.off_kgT), true, R1, LA, tid);
+    // kg^T (rows d, contraction s; hi, lo) and w (rows r, contraction d) as row-major bf16
+    auto stage_rm = [&](const __bf16* t, int R, int KC, bool split, __bf16* dh, __bf16* dl, int ld) {
+        const int NS = KC / M::KS;
+        for (int q = tid; q < R * KC / 8; q += BT) {
+            const int l = q % 64, blk = q / 64;
+            const int row = 16 * (blk / NS) + (l & 15);
+            const int col = (blk % NS) * M::KS + (l >> 4) * M::KPL;
+            *reinterpret_cast<bf16x8*>(dh + row * ld + col) = *reinterpret_cast<const bf16x8*>(t + 8 * q);
+            if (split)
+                *reinterpret_cast<bf16x8*>(dl + row * ld + col) = *reinterpret_cast<const bf16x8*>(t + 8 * q + R * KC);
+        }
+    };
+    __bf16* kTh = reinterpret_cast<__bf16*>(smem);   // kg^T [d][s], hi
+    __bf16* kTl = kTh + K * PT_LD;                   //                lo
+    __bf16* wR = kTl + K * PT_LD;                    // w [r][d]
+    constexpr int WLD = K + 8;
+    stage_rm(reinterpret_cast<const __bf16*>(rec + p.off_kgT), K, C, true, kTh, kTl, PT_LD);
+    stage_rm(reinterpret_cast<const __bf16*>(rec + p.off_w), C, K, false, wR, nullptr, WLD);
     __syncthreads();
-    // kg in fragment order (rows s, contraction d) and w^T (rows d, contraction r)
-    for (int e = tid; e < C * K; e += BT) {
-        const int l = e % 64, blk = e / 64;
+    // kg (rows s, contraction d) and w^T (rows d, contraction r) in bf16 fragment order:
+    // kg hi at KG, lo at KG + C K (bf16 elements); w^T at WT
+    typedef FragTile<__bf16, C, K> FKGB;
+    typedef FragTile<__bf16, K, C> FWTB;
+    __bf16* okg = reinterpret_cast<__bf16*>(ops + SO::KG);
+    __bf16* owt = reinterpret_cast<__bf16*>(ops + SO::WT);
+    for (int q = tid; q < C * K / 8; q += BT) {
+        const int l = q % 64, blk = q / 64;
         {
-            const int row = 16 * (blk / FKG::NS) + (l & 15), col = 4 * (blk % FKG::NS) + (l >> 4);
-            ops[SO::KG + e] = R1[col * LA + row];
+            const int srow = 16 * (blk / FKGB::NS) + (l & 15);
+            const int d0 = (blk % FKGB::NS) * M::KS + (l >> 4) * M::KPL;
+            bf16x8 h, lo;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) { h[x] = kTh[(d0 + x) * PT_LD + srow]; lo[x] = kTl[(d0 + x) * PT_LD + srow]; }
+            *reinterpret_cast<bf16x8*>(okg + 8 * q) = h;
+            *reinterpret_cast<bf16x8*>(okg + C * K + 8 * q) = lo;
         }
         {
-            const int row = 16 * (blk / FWT::NS) + (l & 15), col = 4 * (blk % FWT::NS) + (l >> 4);
-            ops[SO::WT + e] = R0[col * LK + row];
+            const int drow = 16 * (blk / FWTB::NS) + (l & 15);
+            const int r0 = (blk % FWTB::NS) * M::KS + (l >> 4) * M::KPL;
+            bf16x8 h;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) h[x] = wR[(r0 + x) * WLD + drow];
+            *reinterpret_cast<bf16x8*>(owt + 8 * q) = h;
         }
     }
 }
@@ -1223,7 +1401,10 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (chains > 0) {
-        hipLaunchKernelGGL((bwd_scan_kernel<K, V>), dim3((unsigned)(chains * (V / 16))), dim3(BT), 0, a.stream, p);
+        if constexpr (sizeof(TIn) == 2)
+            hipLaunchKernelGGL((bwd_scan_bf16_kernel<K, V>), dim3((unsigned)(chains * (V / 16))), dim3(BT), 0, a.stream, p);
+        else
+            hipLaunchKernelGGL((bwd_scan_kernel<K, V>), dim3((unsigned)(chains * (V / 16))), dim3(BT), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (nchunk_items > 0) {
