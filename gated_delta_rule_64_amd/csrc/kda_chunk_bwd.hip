@@ -1246,8 +1246,13 @@ __global__ __launch_bounds__(4 * K, 1) void bwd_pair_kernel(BwdParams p) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int s = 16 * I + j;
-                    const float er = exp2_fast(fminf(gr - gb[j], 0.f));   // row side: s <= r
-                    const float ec = exp2_fast(fminf(gb[j] - gr, 0.f));   // column side: s >= r
+                    // row side (s <= r): 2^min(x, 0); column side (s >= r): 2^min(-x, 0),
+                    // x = Gamma_r - Gamma_s; both are 2^-|x| on their own side and 1 on the
+                    // other, so one exp2 serves the pair
+                    const float x = gr - gb[j];
+                    const float t2 = exp2_fast(-fabsf(x));
+                    const float er = x <= 0.f ? t2 : 1.f;
+                    const float ec = x >= 0.f ? t2 : 1.f;
                     const float ek = kb[j] * er;
                     xq = fmaf(dAL[r * LA + s], ek, xq);
                     xk = fmaf(dML[r * LA + s], ek, xk);
