@@ -23,6 +23,8 @@ Also reported on the same JSON line:
   * decode    -- the per-token recurrent forward on 4096 sequences x 32 heads (one token
                  each, fp32 states in and out): state GB/s and fraction of HBM peak,
                  and a plain-stream ceiling (torch.neg over the same state bytes);
+  * varlen    -- the packed-sequence forward (64 slots, ~31k tokens, 4 empty slots,
+                 initial and final states);
   * cpu_baseline -- the fp64 CPU oracle on the full headline workload, host threads.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
@@ -385,6 +387,35 @@ def main():
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
     del dd, dout, dstate
 
+    # packed varlen forward: 64 slots, lengths U[1, 1024] with 4 empty slots (~31k tokens),
+    # H=HV=16, K=V=128 bf16, fp32 initial and final states (timed like the headline)
+    wv = inputs.WORKLOADS["vl"]
+    dv_ = inputs.make(wv, device=dev)
+    Bv, Tv = dv_["q"].shape[0], dv_["q"].shape[1]
+    Nv = dv_["cu_seqlens"].numel() - 1
+    vtokens = int(dv_["cu_seqlens"][-1].item())
+    vws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(Bv, Tv, wv.H, wv.HV, wv.K, wv.V, Nv, 1, kda.KDA_BF16),
+                      dtype=torch.uint8, device=dev)
+    vout = torch.empty_like(dv_["v"])
+    vstate = torch.empty_like(dv_["initial_state"])
+
+    def vcall():
+        kda.kda_chunk_fwd(dv_["q"], dv_["k"], dv_["v"], dv_["g"], dv_["beta"], dv_["initial_state"],
+                          dv_["cu_seqlens"], output_final_state=True, out=vout, final_state=vstate,
+                          workspace=vws)
+    for _ in range(args.warmup):
+        vcall()
+    torch.cuda.synchronize()
+    vev = Events(hip, 2)
+    hip.hipEventRecord(vev.ev[0], sptr)
+    for _ in range(steps):
+        vcall()
+    hip.hipEventRecord(vev.ev[1], sptr)
+    torch.cuda.synchronize()
+    var_ms = vev.ms(0, 1) / steps
+    vev.close()
+    del dv_, vws, vout, vstate
+
     result = {
         "metric": "KDA fwd tokens/s + % bf16 MFMA peak at T=8192; decode state GB/s % HBM",
         "value": tok_s,
@@ -415,6 +446,8 @@ def main():
                          "ms_per_step": fused_ms, "tokens_per_s": tokens / (fused_ms * 1e-3)},
         "backward": {"workload": "kda_chunk_bwd of the headline forward (dq, dk, dv, dg, dbeta; do ~ N(0,1) bf16, no dht)",
                      "ms_per_step": bwd_ms, "tokens_per_s": tokens / (bwd_ms * 1e-3), "steps": bsteps},
+        "varlen": {"workload": f"chunk_kda fwd packed: 64 slots (4 empty), {vtokens} tokens, H=HV=16 K=V=128 bf16, fp32 initial and final states",
+                   "ms_per_step": var_ms, "tokens_per_s": vtokens / (var_ms * 1e-3)},
         "decode": {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
                    "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
                    "bytes": dec_bytes, "fused_inputs_ms": dec_fused_ms, "state_vk_ms": dec_vk_ms,

@@ -42,7 +42,11 @@ constexpr float SPREAD_LIMIT = 100.0f;
 // decrease always break some slot's check; the slots that pass may then overlap, so the
 // chunk count is also capped at the table's capacity NCmax: a slot whose chunks would
 // not fit is skipped and flagged like a malformed one. Entries past n_chunks are never
-// read.
+// read. The slot order lists the slots by descending chunk count (ties by index; skipped
+// slots count 0) for the serial scans to take the longest chains first; past
+// SORT_SLOTS slots it is the identity.
+constexpr int SORT_SLOTS = 2048;
+
 __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* __restrict__ cu, int N,
                                                      int T, int NCmax,
                                                      int32_t* __restrict__ coff,
@@ -50,8 +54,10 @@ __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ slot_ok,
                                                      int32_t* __restrict__ nchunks,
                                                      int2* __restrict__ table,
+                                                     int32_t* __restrict__ order,
                                                      int32_t* dev_status) {
     __shared__ int scan[1024];
+    __shared__ int cnts[SORT_SLOTS];
     __shared__ int used;
     const int tid = threadIdx.x;
     if (tid == 0) used = 0;
@@ -87,6 +93,7 @@ __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* __restrict__
             slot_ok[n] = ok;
             coff[n] = ok ? (int)first : 0;
             cend[n] = ok ? (int)(first + cnt) : 0;
+            if (n < SORT_SLOTS) cnts[n] = ok ? cnt : 0;
             if (ok) {
                 for (int i = 0; i < cnt; ++i) {
                     const int l = len - i * C < C ? len - i * C : C;
@@ -100,6 +107,20 @@ __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* __restrict__
     }
     __syncthreads();
     if (tid == 0) nchunks[0] = used;
+    // the slot order: rank = number of slots ahead (more chunks, or as many and a lower index)
+    for (int n = tid; n < N; n += 1024) {
+        if (N > SORT_SLOTS) {
+            order[n] = n;
+            continue;
+        }
+        const int cn = cnts[n];
+        int rank = 0;
+        for (int j = 0; j < N; ++j) {
+            const int cj = cnts[j];
+            rank += (cj > cn) || (cj == cn && j < n);
+        }
+        order[rank] = n;
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -1250,6 +1271,7 @@ struct ScanParams {
     const int32_t* cend;     // one past the last chunk of each sequence [N]
     const int32_t* slot_ok;  // sequence validity (packed offsets checked per slot)
     const int2* table;       // chunk table: (first row, rows)
+    const int32_t* order;    // slots by descending chunk count (packed), or NULL
     int N, T, HV, NT, NCmax;
     int dense;               // no offsets: sequence n is chunks n NT .. n NT + NT - 1, no schedule
     // checkpoints for the backward (kernels instantiated with CKPT, which write no o),
@@ -1360,11 +1382,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
     const int wave = tid >> 6;
     const int lr = lane & 15, lq = lane >> 4;
     const int G = p.N * p.HV * NVT;
-    const int item = xcd_remap(blockIdx.x, G);
-    const int vt = item % NVT;
-    const int chain = item / NVT;
-    const int hv = chain % p.HV;
-    const int n = chain / p.HV;
+    int vt, hv, n;
+    scan_item(blockIdx.x, G, NVT, p.HV, p.dense ? nullptr : p.order, vt, hv, n);
     const int v0 = vt * BV;
     // Aqk rows 16*wave.. are zero past column 16*wave+15: fewer contraction steps
     const int njs_w = (16 * wave + 16 + KS - 1) / KS;
@@ -1678,11 +1697,8 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;
     const int G = p.N * p.HV * NVT;
-    const int item = xcd_remap(blockIdx.x, G);
-    const int vt = item % NVT;
-    const int chain = item / NVT;
-    const int hv = chain % p.HV;
-    const int n = chain / p.HV;
+    int vt, hv, n;
+    scan_item(blockIdx.x, G, NVT, p.HV, p.dense ? nullptr : p.order, vt, hv, n);
     const int v0 = vt * BV;
 
     if (!p.dense && !p.slot_ok[n]) return;    // malformed offsets: leave this slot untouched
@@ -1914,7 +1930,7 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     // kernel computes chunk positions itself and the schedule kernel is not launched
     const bool dense = a.cu_seqlens == nullptr;
     const int NT = (a.T + C - 1) / C;
-    int32_t *coff = nullptr, *cend = nullptr, *slot_ok = nullptr, *nch = nullptr;
+    int32_t *coff = nullptr, *cend = nullptr, *slot_ok = nullptr, *nch = nullptr, *order = nullptr;
     int2* table = nullptr;
     if (a.events) {
         hipError_t err = hipEventRecord(a.events[0], a.stream);
@@ -1926,8 +1942,9 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
         slot_ok = cend + a.N;
         nch = slot_ok + a.N;
         table = reinterpret_cast<int2*>(ws + sched_table_offset(a.N));
+        order = reinterpret_cast<int32_t*>(ws + sched_order_offset(a.N, L.NCmax));
         hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.N,
-                           a.T, L.NCmax, coff, cend, slot_ok, nch, table, a.dev_status);
+                           a.T, L.NCmax, coff, cend, slot_ok, nch, table, order, a.dev_status);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -1974,7 +1991,7 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     sp.rec = recs; sp.rec_bytes = L.rec_bytes; sp.off_w = L.off_w; sp.off_u = L.off_u;
     sp.off_qg = L.off_qg; sp.off_kgT = L.off_kgT; sp.off_aqk = L.off_aqk; sp.off_eg = L.off_eg;
     sp.initial_state = a.initial_state; sp.final_state = a.final_state; sp.o = a.o;
-    sp.coff = coff; sp.cend = cend; sp.slot_ok = slot_ok; sp.table = table;
+    sp.coff = coff; sp.cend = cend; sp.slot_ok = slot_ok; sp.table = table; sp.order = order;
     sp.N = a.N; sp.T = a.T; sp.HV = a.HV; sp.NT = NT; sp.NCmax = L.NCmax;
     sp.dense = dense;
     sp.h_out = a.h_out; sp.vn_out = a.vn_out;
@@ -2046,9 +2063,8 @@ bool chunk_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qk
     L.off_eg = off;  off += (size_t)K * 4;
     L.rec_bytes = align256(off);
     {
-        size_t s = sched_table_offset(N);                      // coff, cend, slot_ok, n_chunks
-        s += (size_t)L.NCmax * 8;                              // chunk table
-        L.sched_bytes = align256(s);
+        // coff, cend, slot_ok, n_chunks, the chunk table, then the slot order
+        L.sched_bytes = align256(sched_order_offset(N, L.NCmax) + (size_t)N * 4);
     }
     L.total = L.sched_bytes + (size_t)HV * L.NCmax * L.rec_bytes;
     *out = L;

@@ -152,6 +152,7 @@ struct BwdParams {
     const int32_t* coff;
     const int32_t* cend;
     const int32_t* slot_ok;
+    const int32_t* order;     // slots by descending chunk count (packed), or NULL
     int dense, NT, T, N, H, HV, NCmax;
     float scale;
     // forward records
@@ -363,9 +364,8 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = p.N * p.HV * NVT;
-    const int item = xcd_remap(blockIdx.x, G);
-    const int vt = item % NVT, chain = item / NVT;
-    const int hv = chain % p.HV, n = chain / p.HV;
+    int vt, hv, n;
+    scan_item(blockIdx.x, G, NVT, p.HV, p.dense ? nullptr : p.order, vt, hv, n);
     const int v0 = vt * BV;
     if (!p.dense && !p.slot_ok[n]) return;
     const int c0 = p.dense ? n * p.NT : p.coff[n];
@@ -497,9 +497,8 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = p.N * p.HV * NVT;
-    const int item = xcd_remap(blockIdx.x, G);
-    const int vt = item % NVT, chain = item / NVT;
-    const int hv = chain % p.HV, n = chain / p.HV;
+    int vt, hv, n;
+    scan_item(blockIdx.x, G, NVT, p.HV, p.dense ? nullptr : p.order, vt, hv, n);
     const int v0 = vt * BV;
     if (!p.dense && !p.slot_ok[n]) return;
     const int c0 = p.dense ? n * p.NT : p.coff[n];
@@ -1373,8 +1372,9 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
         const int32_t* coff = reinterpret_cast<const int32_t*>(ws);
         p.coff = coff; p.cend = coff + a.N; p.slot_ok = coff + 2 * a.N; p.nchunks = coff + 3 * a.N;
         p.table = reinterpret_cast<const int2*>(ws + sched_table_offset(a.N));
+        p.order = reinterpret_cast<const int32_t*>(ws + sched_order_offset(a.N, L.fwd.NCmax));
     } else {
-        p.coff = p.cend = p.slot_ok = p.nchunks = nullptr;
+        p.coff = p.cend = p.slot_ok = p.nchunks = p.order = nullptr;
         p.table = nullptr;
     }
     p.dense = dense; p.NT = NT; p.T = a.T; p.N = a.N; p.H = a.H; p.HV = a.HV; p.NCmax = L.fwd.NCmax;

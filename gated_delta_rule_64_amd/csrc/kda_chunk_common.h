@@ -29,4 +29,35 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
     return (b % 8) * (G / 8) + b / 8;
 }
 
+// Offset of the packed schedule's slot order (int32 [N], slots by descending chunk count)
+// in the schedule region: after the chunk table.
+inline size_t sched_order_offset(int N, int NCmax) { return sched_table_offset(N) + (size_t)NCmax * 8; }
+
+// Work item of a serial scan block b (G = chains * NVT blocks, NVT column slices per
+// chain): its column slice vt, value head hv and sequence n. Without an order (dense
+// mode) items follow xcd_remap. With the packed schedule's order, chains are walked
+// longest sequence first, their ranks dealt round-robin to the 8 XCDs (block b runs on
+// XCD b % 8) and each chain's slices kept on one XCD: the blocks dispatched first hold
+// the longest chains, so short ones fill in behind them instead of a long one starting
+// last.
+__device__ __forceinline__ void scan_item(int b, int G, int NVT, int HV, const int32_t* order, int& vt,
+                                          int& hv, int& n) {
+    int chain;
+    if (order == nullptr) {
+        const int item = xcd_remap(b, G);
+        vt = item % NVT;
+        chain = item / NVT;
+    } else if (G % 8 == 0 && (G / 8) % NVT == 0) {
+        const int j = b / 8;
+        vt = j % NVT;
+        chain = (j / NVT) * 8 + b % 8;
+    } else {
+        vt = b % NVT;
+        chain = b / NVT;
+    }
+    hv = chain % HV;
+    n = chain / HV;
+    if (order != nullptr) n = order[n];
+}
+
 }  // namespace kda

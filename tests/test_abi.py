@@ -75,8 +75,9 @@ def _rec_bytes(K, V, elem):
 
 
 def _sched_bytes(N, ncmax):
-    # first/end chunk and validity per sequence, chunk count, then the chunk table
-    s = ((3 * N + 1) * 4 + 15) // 16 * 16 + ncmax * 8
+    # first/end chunk and validity per sequence, chunk count, the chunk table, then the
+    # slot order
+    s = ((3 * N + 1) * 4 + 15) // 16 * 16 + ncmax * 8 + N * 4
     return (s + 255) // 256 * 256
 
 
