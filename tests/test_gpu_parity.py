@@ -660,6 +660,31 @@ def _check_bwd(d, do, dht, dtype, rows=None, label=""):
     return got, ref
 
 
+def test_chunk_many_slots():
+    """Packed offsets with more slots (2,100) than the schedule sorts by length (2,048),
+    so the scans take the slots in index order: lengths 0..70 (every tenth slot empty,
+    some crossing a chunk boundary), forward and backward against the oracle, empty
+    slots' states passed through bitwise."""
+    rng = np.random.default_rng(96)
+    lens = rng.integers(1, 71, size=2100)
+    lens[::10] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    Tp = int(cu[-1]) + 8
+    d = small(1, Tp, 1, 2, 64, 64, torch.bfloat16, seed=97)
+    d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    d["initial_state"] = torch.randn(len(lens), 2, 64, 64, generator=torch.Generator().manual_seed(98)).mul(0.05).to(DEV)
+    log(f"[many slots] 2100 slots, {int(cu[-1])} tokens, HV2 K=V=64 bf16")
+    o, ht = run("chunk", d)
+    o_ref, ht_ref = oracle_of(d)
+    m = valid_rows(cu, Tp)
+    check("o", o[:, m], o_ref[:, m], torch.bfloat16)
+    check("final_state", ht, ht_ref, torch.bfloat16)
+    for n in np.nonzero(lens == 0)[0][:20]:
+        assert torch.equal(ht[n], d["initial_state"][n]), f"empty slot {n} state must pass through bitwise"
+    do, dht = _bwd_inputs(d, 99)
+    _check_bwd(d, do, dht, torch.bfloat16, rows=torch.from_numpy(m), label="many slots ")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_chunk_bwd_dense_gva(dtype):
     """B=2, T=200 (a short last chunk), H=2, HV=4 (GVA), K=V=128, initial state and a
