@@ -158,7 +158,7 @@ int recurrent_impl(const void* q, const void* k, const void* v, const void* g, i
         return fail(KDA_ERR_UNSUPPORTED, "K must be 64 or 128, got %d", K);
     if (V % 64 != 0)
         return fail(KDA_ERR_UNSUPPORTED, "V must be a multiple of 64, got %d", V);
-    if ((long long)N * HV * (V / 32) > 0x7fffffffLL * 4LL)
+    if ((long long)N * HV * (V / 16) > 0x7fffffffLL * 4LL)
         return fail(KDA_ERR_SHAPE, "grid too large");
     if (state_layout != KDA_STATE_KV && state_layout != KDA_STATE_VK)
         return fail(KDA_ERR_ARG, "state_layout must be KDA_STATE_KV (0) or KDA_STATE_VK (1), got %d", state_layout);

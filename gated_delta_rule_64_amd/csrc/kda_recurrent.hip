@@ -27,11 +27,12 @@
 // contiguous run of it. The two layouts thus sum rows in different orders, and their
 // outputs agree to fp32 rounding, not bitwise.
 //
-// BV = 64 (K = 128: 128 fp32 of state per lane, one wave per SIMD) when every sequence
-// carries about one token and the states are [K][V]: that launch is a pure state stream
-// and the longer row runs keep it closest to a plain copy. Otherwise BV = 32 (half the
+// States stored [K][V]: BV = 64 (K = 128: 128 fp32 of state per lane, one wave per SIMD)
+// when every sequence carries about one token: that launch is a pure state stream and
+// the longer row runs keep it closest to a plain copy. Otherwise BV = 32 (half the
 // registers, three waves per SIMD), which hides the per-token dependency chain of longer
-// sequences and, for transposed states, makes each column access a full 128-byte run.
+// sequences. Transposed states: BV = 16 (16 row groups, four waves per SIMD), so each
+// column access of a row-group set is one 256-byte run, the length of the [K][V] rows'.
 //
 // The grid is flat and 1-D (four wavefronts per 256-thread block), so N * HV * V/BV may
 // exceed 65,535. The state layout and whether the state after every token is written
@@ -304,7 +305,7 @@ hipError_t launch_v(const RecurrentArgs& a) {
 template <int K, typename TIn, typename TB>
 hipError_t launch_t(const RecurrentArgs& a) {
     if (a.state_vk)
-        return a.inter_states ? launch_v<K, 32, TIn, TB, true, true>(a) : launch_v<K, 32, TIn, TB, true, false>(a);
+        return a.inter_states ? launch_v<K, 16, TIn, TB, true, true>(a) : launch_v<K, 16, TIn, TB, true, false>(a);
     // about one token per sequence: B T rows over N sequences, at most 1.5 on average
     const bool one_token = 2LL * a.B * a.T <= 3LL * a.N;
     if (one_token)

@@ -746,26 +746,27 @@ def test_chunk_bwd_c3_full():
 # ------------------------------------------------------------------------------------
 # decode serving: transposed state layout, intermediate states, graph replay
 # ------------------------------------------------------------------------------------
-def _packed_case(lens, HV=4, seed=70, dtype=torch.bfloat16):
+def _packed_case(lens, HV=4, seed=70, dtype=torch.bfloat16, KV=128):
     cu = [0]
     for n in lens:
         cu.append(cu[-1] + n)
     Tp = cu[-1] + 8
-    d = small(1, Tp, 2, HV, 128, 128, dtype, seed=seed)
+    d = small(1, Tp, 2, HV, KV, KV, dtype, seed=seed)
     d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=DEV)
-    d["initial_state"] = torch.randn(len(lens), HV, 128, 128, generator=torch.Generator().manual_seed(seed + 1)).mul(0.05).to(DEV)
+    d["initial_state"] = torch.randn(len(lens), HV, KV, KV, generator=torch.Generator().manual_seed(seed + 1)).mul(0.05).to(DEV)
     return d, cu
 
 
-@pytest.mark.parametrize("lens", [[5, 0, 1, 9], [1] * 18 + [0, 2, 3, 0, 1, 1]], ids=["packed", "about_one_token"])
-def test_recurrent_state_layout_vk(lens):
+@pytest.mark.parametrize("lens,KV", [([5, 0, 1, 9], 128), ([1] * 18 + [0, 2, 3, 0, 1, 1], 128), ([5, 0, 1, 9], 64)],
+                         ids=["packed", "about_one_token", "packed_k64"])
+def test_recurrent_state_layout_vk(lens, KV):
     """States stored transposed ([V][K] per head): both layouts within the tolerance of
     the oracle, and within fp32 rounding of each other (the layouts sum a state's rows in
     different orders, so agreement is to a rounding step, not bitwise). The second case
     has at most 1.5 rows per sequence (33 rows, 24 slots), which takes the decode launch
     of the [K][V] layout."""
     import gated_delta_rule_64_amd as kda
-    d, cu = _packed_case(lens)
+    d, cu = _packed_case(lens, KV=KV)
     o1, s1 = kda.kda_recurrent_fwd_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
                                       d["cu_seqlens"], output_final_state=True)
     h0t = d["initial_state"].transpose(-1, -2).contiguous()
