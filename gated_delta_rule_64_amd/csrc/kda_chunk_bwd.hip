@@ -1130,6 +1130,9 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
 // tile w (K / 16 waves); each lane holds its results in the matrix-core layout (rows
 // 16I + 4lq .. +3 of channel 16w + lr) through the elementwise step.
 // ------------------------------------------------------------------------------------
+// largest decay spread (log2 units) of a 16-row block that the pair kernel anchors
+constexpr float PAIR_SPREAD = 64.f;
+
 template <int K>
 constexpr int pair_threads() { return 4 * K; }   // one wave per 16-channel tile
 
@@ -1223,43 +1226,74 @@ __global__ __launch_bounds__(4 * K, 1) void bwd_pair_kernel(BwdParams p) {
                 akc[t][J][rr] = fmaf(f, z[rr], akc[t][J][rr]);
             }
         }
-        // pairs inside a block: one one-sided factor each. All 16 rows of the block are
-        // visited (fixed trip counts, fully unrolled); pairs on the wrong side of the
-        // diagonal meet a zero dAqk / dM, and their exponent is clamped at 0 so nothing
-        // overflows.
+        // pairs inside a block. Where the block's decay spread (Gamma of its first row minus
+        // Gamma of its last, in every channel of the tile) is at most PAIR_SPREAD, anchor
+        // the factors at a block boundary row and use the matrix cores:
+        //   row side    2^(G_r - G_s) = 2^(G_r - G_last) 2^(G_last - G_s),
+        //   column side 2^(G_s - G_r) = 2^(G_first - G_r) 2^(G_s - G_first),
+        // the second factor (<= 1) scaling the operand and the first (<= 2^spread) the
+        // finished sum. Otherwise one one-sided factor per pair (exact at any decay). In
+        // both, pairs on the wrong side of the diagonal meet a zero dAqk / dM.
 #pragma unroll 1
         for (int I = 0; I < 4; ++I) {
-            float kb[16], qb[16], gb[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                kb[j] = kL[(16 * I + j) * LK + d];
-                qb[j] = qL[(16 * I + j) * LK + d];
-                gb[j] = GmL[(16 * I + j) * LK + d];
-            }
             f32x4 xq4, xk4, xc4;
+            const float gfirst = GmL[(16 * I) * LK + d], glast = GmL[(16 * I + 15) * LK + d];
+            const bool steep = __builtin_amdgcn_ballot_w64(gfirst - glast > PAIR_SPREAD) != 0;   // wave-uniform
+            if (!steep) {
+                f32x4 yq = {0.f, 0.f, 0.f, 0.f}, yk = yq, yc = yq;
+                const int ri = 16 * I + lr;   // A operand row of this lane
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = 16 * I + 4 * lq + rr;
-                const float gr = GmL[r * LK + d];
-                float xq = 0.f, xk = 0.f, xc = 0.f;
+                for (int s0 = 0; s0 < 16; s0 += 4) {
+                    const int s = 16 * I + s0 + lq;   // contraction index of this lane
+                    const float gs = GmL[s * LK + d];
+                    const float ks = kL[s * LK + d];
+                    const float br = ks * exp2_fast(glast - gs);
+                    const float fc = exp2_fast(gs - gfirst);
+                    yq = __builtin_amdgcn_mfma_f32_16x16x4f32(dAL[ri * LA + s], br, yq, 0, 0, 0);
+                    yk = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[ri * LA + s], br, yk, 0, 0, 0);
+                    yc = __builtin_amdgcn_mfma_f32_16x16x4f32(sc * dAL[s * LA + ri], qL[s * LK + d] * fc, yc, 0, 0, 0);
+                    yc = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[s * LA + ri], ks * fc, yc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float gr = GmL[(16 * I + 4 * lq + rr) * LK + d];
+                    const float fr = exp2_fast(gr - glast), fcol = exp2_fast(gfirst - gr);
+                    xq4[rr] = sc * fr * yq[rr];
+                    xk4[rr] = fr * yk[rr];
+                    xc4[rr] = fcol * yc[rr];
+                }
+            } else {
+                float kb[16], qb[16], gb[16];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int s = 16 * I + j;
-                    // row side (s <= r): 2^min(x, 0); column side (s >= r): 2^min(-x, 0),
-                    // x = Gamma_r - Gamma_s; both are 2^-|x| on their own side and 1 on the
-                    // other, so one exp2 serves the pair
-                    const float x = gr - gb[j];
-                    const float t2 = exp2_fast(-fabsf(x));
-                    const float er = x <= 0.f ? t2 : 1.f;
-                    const float ec = x >= 0.f ? t2 : 1.f;
-                    const float ek = kb[j] * er;
-                    xq = fmaf(dAL[r * LA + s], ek, xq);
-                    xk = fmaf(dML[r * LA + s], ek, xk);
-                    xc = fmaf(fmaf(sc * dAL[s * LA + r], qb[j], dML[s * LA + r] * kb[j]), ec, xc);
+                    kb[j] = kL[(16 * I + j) * LK + d];
+                    qb[j] = qL[(16 * I + j) * LK + d];
+                    gb[j] = GmL[(16 * I + j) * LK + d];
                 }
-                xq4[rr] = sc * xq;
-                xk4[rr] = xk;
-                xc4[rr] = xc;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 16 * I + 4 * lq + rr;
+                    const float gr = GmL[r * LK + d];
+                    float xq = 0.f, xk = 0.f, xc = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int s = 16 * I + j;
+                        // row side (s <= r): 2^min(x, 0); column side (s >= r): 2^min(-x, 0),
+                        // x = Gamma_r - Gamma_s; both are 2^-|x| on their own side and 1 on
+                        // the other, so one exp2 serves the pair
+                        const float x = gr - gb[j];
+                        const float t2 = exp2_fast(-fabsf(x));
+                        const float er = x <= 0.f ? t2 : 1.f;
+                        const float ec = x >= 0.f ? t2 : 1.f;
+                        const float ek = kb[j] * er;
+                        xq = fmaf(dAL[r * LA + s], ek, xq);
+                        xk = fmaf(dML[r * LA + s], ek, xk);
+                        xc = fmaf(fmaf(sc * dAL[s * LA + r], qb[j], dML[s * LA + r] * kb[j]), ec, xc);
+                    }
+                    xq4[rr] = sc * xq;
+                    xk4[rr] = xk;
+                    xc4[rr] = xc;
+                }
             }
 #pragma unroll
             for (int Ib = 0; Ib < 4; ++Ib)
