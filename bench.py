@@ -27,7 +27,7 @@ Also reported on the same JSON line:
                  initial and final states);
   * cpu_baseline -- the fp64 CPU oracle on the full headline workload, host threads.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50]
 """
 from __future__ import annotations
 
@@ -135,8 +135,8 @@ def flushed_reps(call, reps, tokens, hip, sptr, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=10)
     ap.add_argument("--flushed-reps", type=int, default=50,
                     help="reps of the headline forward timed one at a time with a cache flush between")
@@ -198,17 +198,28 @@ def main():
         call(None)
     torch.cuda.synchronize()
     steps = args.steps
-    ev = Events(hip, 4 * steps)
+    # two events per step: after Stage 1+2 (mid) and after the scan (end); a step starts
+    # where the previous one ended (the first at the outer start event), so the kernels
+    # run back to back with one marker between them
+    ev = Events(hip, 2 * steps)
     outer = Events(hip, 2)
+    slots = [(vp * 4)(None, None, ev.ev[2 * s], ev.ev[2 * s + 1]) for s in range(steps)]
     torch.cuda.synchronize()
     hip.hipEventRecord(outer.ev[0], sptr)
     for s in range(steps):
-        call(ctypes.cast(ctypes.byref(ev.ev, 4 * s * ctypes.sizeof(vp)), vp))
+        call(ctypes.cast(slots[s], vp))
     hip.hipEventRecord(outer.ev[1], sptr)
     torch.cuda.synchronize()
     total_ms = outer.ms(0, 1)
-    intra_ms = sum(ev.ms(4 * s + 1, 4 * s + 2) for s in range(steps)) / steps
-    scan_ms = sum(ev.ms(4 * s + 2, 4 * s + 3) for s in range(steps)) / steps
+
+    def span(a, b):
+        out_ = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(out_), a, b) == 0
+        return float(out_.value)
+
+    starts = [outer.ev[0]] + [ev.ev[2 * s + 1] for s in range(steps - 1)]
+    intra_ms = sum(span(starts[s], ev.ev[2 * s]) for s in range(steps)) / steps
+    scan_ms = sum(ev.ms(2 * s, 2 * s + 1) for s in range(steps)) / steps
     ev.close()
     outer.close()
     ms_per_step = total_ms / steps

@@ -1598,6 +1598,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
 constexpr int SCAN8_THREADS = 512;
 constexpr int ROW_PREFETCH = 2;     // row waves: chunks in flight
 constexpr int STATE_PREFETCH = 3;   // state waves: chunks in flight
+constexpr int SCAN_L2_AHEAD = 4;    // chunks ahead of the one being scanned that the L2 prefetch touches
 
 template <int K, int BV>
 struct RowFrags {
@@ -1846,8 +1847,21 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
             }
         lds_barrier();   // initial S^T
         int cur = 0;
+        // L2 prefetch: the chain's NVT column-slice blocks share one XCD (scan_item), and
+        // block vt touches its share of the record SCAN_L2_AHEAD chunks ahead, one line per
+        // lane, so the register rings' loads of that record hit in L2. The loaded word is
+        // folded into `sink` when the same ring slot comes round (after the loads that
+        // follow it have been waited for), and sink is stored only for an impossible N.
+        const int lines = (int)(p.rec_bytes / 128);
+        const int l0 = vt * lines / NVT, nl = (vt + 1) * lines / NVT - l0;
+        const int li = sw * 64 + lane;
+        uint32_t sink = 0, pf0 = 0, pf1 = 0, pf2 = 0;
+        auto prefetch = [&](uint32_t& pf, int cn) {
+            sink ^= pf;
+            if (li < nl) pf = *reinterpret_cast<const uint32_t*>(record(cn + SCAN_L2_AHEAD - STATE_PREFETCH) + (size_t)(l0 + li) * 128);
+        };
         // one chunk; F is refilled with chunk cn as its registers die
-        auto step = [&](StateFrags<K, BV>& F, int cn) {
+        auto step = [&](StateFrags<K, BV>& F, int cn, uint32_t& pf) {
             if constexpr (CKPT) {   // the state at the start of the chunk F holds
                 float* hb = p.h_out + ((size_t)hv * p.NCmax + (cn - STATE_PREFETCH)) * (size_t)K * V;
 #pragma unroll
@@ -1890,6 +1904,7 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                 }
             }
             load_state_g<K, BV>(F, record(cn), p, sw, lane);
+            prefetch(pf, cn);
             lds_barrier();   // B: S_(c+1) complete
             cur ^= 1;
         };
@@ -1897,12 +1912,14 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
         const int nsteps = c1 > c0 ? c1 - c0 : 0;
         int c = c0;
         for (int t = 0; t < nsteps / 3; ++t, c += 3) {
-            step(G0, c + 3);
-            step(G1, c + 4);
-            step(G2, c + 5);
+            step(G0, c + 3, pf0);
+            step(G1, c + 4, pf1);
+            step(G2, c + 5, pf2);
         }
-        if (nsteps % 3 >= 1) step(G0, c + 3);
-        if (nsteps % 3 >= 2) step(G1, c + 4);
+        if (nsteps % 3 >= 1) step(G0, c + 3, pf0);
+        if (nsteps % 3 >= 2) step(G1, c + 4, pf1);
+        sink ^= pf0 ^ pf1 ^ pf2;
+        if (p.N < 0 && sink == 0x9e3779b9u) reinterpret_cast<uint32_t*>(p.o)[0] = sink;
         if (p.final_state) {
 #pragma unroll
             for (int a = 0; a < NDT; ++a)
@@ -1932,7 +1949,7 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     const int NT = (a.T + C - 1) / C;
     int32_t *coff = nullptr, *cend = nullptr, *slot_ok = nullptr, *nch = nullptr, *order = nullptr;
     int2* table = nullptr;
-    if (a.events) {
+    if (a.events && a.events[0]) {
         hipError_t err = hipEventRecord(a.events[0], a.stream);
         if (err != hipSuccess) return err;
     }
@@ -1948,7 +1965,7 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (a.events) {
+    if (a.events && a.events[1]) {
         hipError_t err = hipEventRecord(a.events[1], a.stream);
         if (err != hipSuccess) return err;
     }
@@ -1995,12 +2012,12 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     sp.N = a.N; sp.T = a.T; sp.HV = a.HV; sp.NT = NT; sp.NCmax = L.NCmax;
     sp.dense = dense;
     sp.h_out = a.h_out; sp.vn_out = a.vn_out;
-    if (a.events) {
+    if (a.events && a.events[2]) {
         hipError_t err = hipEventRecord(a.events[2], a.stream);
         if (err != hipSuccess) return err;
     }
     hipError_t err = launch_scan<K, V, TIn>(a, sp);
-    if (err == hipSuccess && a.events) err = hipEventRecord(a.events[3], a.stream);
+    if (err == hipSuccess && a.events && a.events[3]) err = hipEventRecord(a.events[3], a.stream);
     return err;
 }
 

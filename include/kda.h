@@ -131,7 +131,10 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
  * `stream` before the first kernel (events[0]), after the packed-mode scheduler
  * (events[1]; same point as events[0] in dense mode), after the Stage 1+2 kernel
  * (events[2]) and after the Stage 3+4 scan (events[3]), so the caller can read each
- * kernel's duration with hipEventElapsedTime. events == NULL behaves like kda_chunk_fwd.
+ * kernel's duration with hipEventElapsedTime. A NULL entry is not recorded (each
+ * record is a marker on the stream; a caller timing steps back to back can record only
+ * events[2] and events[3] and take the previous step's events[3] as the start).
+ * events == NULL behaves like kda_chunk_fwd.
  * For profiling callers (benchmarks); nothing is synchronised.
  */
 int kda_chunk_fwd_timed(const void* q, const void* k, const void* v, const float* g,
