@@ -607,7 +607,7 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
     }
     if (nsteps & 1) step(F0, c);
     sink ^= pf0 ^ pf1;
-    if (p.N < 0 && sink == 0x9e3779b9u) p.dh[0] = (float)sink;
+    asm volatile("" ::"v"(sink));   // keeps the prefetch loads; emits no instruction
     if (p.dh0) {
 #pragma unroll
         for (int a = 0; a < NDT; ++a)
