@@ -981,3 +981,39 @@ def test_chunk_bwd_ex(case):
             assert x is None, name
             continue
         check(name, x, np.asarray(y).reshape(tuple(x.shape)), dtype)
+
+
+# ------------------------------------------------------------------------------------
+# the in-place timing entry point: NULL event slots are skipped, results unchanged
+# ------------------------------------------------------------------------------------
+def test_timed_entry_null_event_slots():
+    import ctypes
+
+    import bench
+    import gated_delta_rule_64_amd as kda
+    d = small(1, 1000, 4, 8, 128, 128, torch.bfloat16, seed=12, h0=False)
+    o_ref, _ = run("chunk", d, final=False)
+    lib = kda.load_library()
+    vp = ctypes.c_void_p
+    lib.kda_chunk_fwd_timed.restype = ctypes.c_int
+    lib.kda_chunk_fwd_timed.argtypes = list(lib.kda_chunk_fwd.argtypes) + [vp]
+    hip = bench.hip_runtime()
+    ev = bench.Events(hip, 4)
+    B, T, H, K = d["q"].shape
+    HV, V = d["v"].shape[2], d["v"].shape[3]
+    ws_bytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, kda.KDA_BF16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    sptr = vp(torch.cuda.current_stream().cuda_stream)
+    for slots in ((None, None, ev.ev[2], ev.ev[3]), tuple(ev.ev[i] for i in range(4))):
+        log(f"[timed entry] events recorded: {[s is not None for s in slots]}")
+        out = torch.full_like(d["v"], float("nan"))
+        arr = (vp * 4)(*slots)
+        rc = lib.kda_chunk_fwd_timed(
+            vp(d["q"].data_ptr()), vp(d["k"].data_ptr()), vp(d["v"].data_ptr()), vp(d["g"].data_ptr()),
+            vp(d["beta"].data_ptr()), None, None, B, vp(out.data_ptr()), None, B, T, H, HV, K, V,
+            kda.KDA_BF16, kda.KDA_BF16, 0.0, 64, vp(ws.data_ptr()), ws_bytes, None, sptr, ctypes.cast(arr, vp))
+        assert rc == 0, lib.kda_last_error().decode()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref)
+        assert ev.ms(2, 3) > 0.0
+    ev.close()
