@@ -817,31 +817,24 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
     const int i_row = 16 * w + lr;
     const bool live = i_row < len;
     const size_t r_g = (size_t)(rs + i_row);
-    bf16x8 qv[NKS], kv[NKS], vv[NVS];
+    bf16x8 qv[NKS], kv[NKS];
     float loc[NKS][8];
     float beta_i = 0.f;
     if (live) {
         beta_i = load_beta<TB>(p, r_g, hv);
         const TW* qp = reinterpret_cast<const TW*>(p.q) + (r_g * p.H + h) * K + 8 * lq;
         const TW* kp = reinterpret_cast<const TW*>(p.k) + (r_g * p.H + h) * K + 8 * lq;
-        const TW* vp = reinterpret_cast<const TW*>(p.v) + (r_g * p.HV + hv) * V + 8 * lq;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             qv[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
             kv[s] = *reinterpret_cast<const bf16x8*>(kp + 32 * s);
             load_gate8<K>(p, r_g, hv, 32 * s + 8 * lq, loc[s]);
         }
-#pragma unroll
-        for (int s = 0; s < NVS; ++s) vv[s] = *reinterpret_cast<const bf16x8*>(vp + 32 * s);
     } else {
 #pragma unroll
         for (int s = 0; s < NKS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) { qv[s][e] = (__bf16)0.f; kv[s][e] = (__bf16)0.f; loc[s][e] = 0.f; }
-#pragma unroll
-        for (int s = 0; s < NVS; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vv[s][e] = (__bf16)0.f;
     }
     if (lq == 0) betas[i_row] = beta_i;
     // optional L2 normalisation of the q / k rows: each lane's row is x * rn, with the row
@@ -868,19 +861,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
         }
     }
     const bool exact_diag = __builtin_amdgcn_ballot_w64(wide) != 0;   // wave-uniform
-
-    // v^T into LDS: the selection products turn each lane's 8 columns of one row into
-    // 4 consecutive rows of one column
-#pragma unroll
-    for (int s = 0; s < NVS; ++s)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const f32x4 x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[s], eye_frag(lane, hh),
-                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            const int col = 32 * s + 16 * hh + lr;
-            *reinterpret_cast<bf16x4*>(VTt + TVT::idx(col, 16 * w + 4 * lq)) =
-                bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-        }
 
     // diagonal block, exact at any gate (blocks that decay too fast for one anchor): a
     // pair j < i is split at the highest bit b where i and j differ; the row
@@ -1009,6 +989,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
         }
     }
     lds_barrier();
+
+    // v is first needed by the u product: its rows are loaded here, behind Stage 1's loads,
+    // so its latency overlaps Stage 2
+    bf16x8 vv[NVS];
+    if (live) {
+        const TW* vp = reinterpret_cast<const TW*>(p.v) + (r_g * p.HV + hv) * V + 8 * lq;
+#pragma unroll
+        for (int s = 0; s < NVS; ++s) vv[s] = *reinterpret_cast<const bf16x8*>(vp + 32 * s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < NVS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[s][e] = (__bf16)0.f;
+    }
 
     // ---- records from registers: qg, kg^T, eG; (k 2^Gamma)^T into LDS ----
     const float* ew = table + tab_ew(w) * K + 8 * lq;
@@ -1139,6 +1133,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
                 f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
+    // v^T into LDS: the selection products turn each lane's 8 columns of one row into
+    // 4 consecutive rows of one column
+#pragma unroll
+    for (int s = 0; s < NVS; ++s)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const f32x4 x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[s], eye_frag(lane, hh),
+                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const int col = 32 * s + 16 * hh + lr;
+            *reinterpret_cast<bf16x4*>(VTt + TVT::idx(col, 16 * w + 4 * lq)) =
+                bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+        }
     lds_barrier();
 
     // ---- WY inverse T = (I + L)^-1 by 16-row blocks ----
