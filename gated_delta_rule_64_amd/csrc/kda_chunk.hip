@@ -1103,6 +1103,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
     };
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+        // rows 16w .. 16w + 15 are zero from column 16w + 16 on: the forward scan never
+        // reads such a fragment (the backward's prep stages the whole tile)
+        if (!CKPT && 32 * s >= 16 * w + 16) continue;
         f32x4 x, y;
 #pragma unroll
         for (int r = 0; r < 4; ++r) { x[r] = tile_aqk(2 * s, r); y[r] = tile_aqk(2 * s + 1, r); }

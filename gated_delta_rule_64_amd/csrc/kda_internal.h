@@ -88,7 +88,9 @@ struct ChunkArgs {
 //              Aqk    [NS][64][64]  TW, scale folded in, zero above the diagonal
 //              u      [64][V]       fp32, accumulator order (AccTile)
 //              eG     [K]           fp32, 2^(chunk's total log2 decay)
-//            w, qg, kgT and Aqk are in matrix-core fragment order (FragTile).
+//            w, qg, kgT and Aqk are in matrix-core fragment order (FragTile). The
+//            forward leaves Aqk's two all-zero fragments (rows 0-31, columns 32-63)
+//            unwritten, as its scan never reads them; the backward's records hold them.
 //            NS = 2 on the bf16 path (tile 1 holds x - bf16(x) rounded to bf16, so
 //            hi + lo carries about 16 significant bits), NS = 1 on the fp32 path.
 //            records are ordered hv-major: record(hv, c) = hv * NCmax + c.
