@@ -355,6 +355,8 @@ def test_chunk_stage2_records_bf16(steep):
     B, T, H, _ = d["q"].shape
     HV = 4
     nbytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, torch.bfloat16)
+    # zero-filled: the forward does not write Aqk's all-zero fragments (rows 0-31,
+    # columns 32-63), which its scan never reads
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
     run("chunk", d, workspace=ws)
     _, _, stages = chunked_ref.chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
