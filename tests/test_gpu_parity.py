@@ -1019,3 +1019,44 @@ def test_timed_entry_null_event_slots():
         assert torch.equal(out, o_ref)
         assert ev.ms(2, 3) > 0.0
     ev.close()
+
+
+# ------------------------------------------------------------------------------------
+# degenerate inputs: no rows at all (dense T = 0) and packed offsets whose every slot is
+# empty; states pass through bitwise, o is never written
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["chunk", "recurrent"])
+def test_degenerate_inputs(path):
+    import gated_delta_rule_64_amd as kda
+    gen = torch.Generator().manual_seed(21)
+    H, HV, K, V = 2, 4, 128, 128
+    fn = kda.kda_chunk_fwd if path == "chunk" else kda.kda_recurrent_fwd
+
+    def tensors(B, T, N):
+        q = torch.randn(B, T, H, K, generator=gen).to(torch.bfloat16).to(DEV)
+        k = torch.randn(B, T, H, K, generator=gen).to(torch.bfloat16).to(DEV)
+        v = torch.randn(B, T, HV, V, generator=gen).to(torch.bfloat16).to(DEV)
+        g = (-torch.rand(B, T, HV, K, generator=gen)).to(DEV)
+        beta = torch.rand(B, T, HV, generator=gen).to(torch.bfloat16).to(DEV)
+        h0 = (torch.randn(N, HV, K, V, generator=gen) * 0.05).to(DEV)
+        return q, k, v, g, beta, h0
+
+    log(f"[degenerate {path}] dense B=2 T=0")
+    q, k, v, g, beta, h0 = tensors(2, 0, 2)
+    o, ht = fn(q, k, v, g, beta, h0, None, output_final_state=True)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(ht, h0)
+    o, ht = fn(q, k, v, g, beta, None, None, output_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ht, torch.zeros_like(h0))
+
+    log(f"[degenerate {path}] packed N=3, every slot empty, 70 unowned rows")
+    q, k, v, g, beta, h0 = tensors(1, 70, 3)
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    out = torch.full_like(v, float("nan"))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o, ht = fn(q, k, v, g, beta, h0, cu, output_final_state=True, out=out, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.isnan(o.float()).all(), "rows outside every sequence are not written"
+    assert torch.equal(ht, h0), "empty slots pass their states through bitwise"
