@@ -1060,3 +1060,38 @@ def test_degenerate_inputs(path):
     assert int(status.item()) == 0
     assert torch.isnan(o.float()).all(), "rows outside every sequence are not written"
     assert torch.equal(ht, h0), "empty slots pass their states through bitwise"
+
+
+def test_degenerate_inputs_bwd():
+    """The backward on the same degenerate inputs: the final-state gradient passes to the
+    initial state's bitwise (the state does), and rows outside every sequence get zero
+    gradients."""
+    import gated_delta_rule_64_amd as kda
+    gen = torch.Generator().manual_seed(22)
+    H, HV, K, V = 2, 4, 128, 128
+
+    def tensors(B, T, N):
+        q = torch.randn(B, T, H, K, generator=gen).to(torch.bfloat16).to(DEV)
+        k = torch.randn(B, T, H, K, generator=gen).to(torch.bfloat16).to(DEV)
+        v = torch.randn(B, T, HV, V, generator=gen).to(torch.bfloat16).to(DEV)
+        g = (-torch.rand(B, T, HV, K, generator=gen)).to(DEV)
+        beta = torch.rand(B, T, HV, generator=gen).to(torch.bfloat16).to(DEV)
+        do = torch.randn(B, T, HV, V, generator=gen).to(torch.bfloat16).to(DEV)
+        h0 = (torch.randn(N, HV, K, V, generator=gen) * 0.05).to(DEV)
+        dht = torch.randn(N, HV, K, V, generator=gen).to(DEV)
+        return q, k, v, g, beta, do, h0, dht
+
+    log("[degenerate bwd] dense B=2 T=0")
+    q, k, v, g, beta, do, h0, dht = tensors(2, 0, 2)
+    dq, dk, dv, dg, db, dh0 = kda.kda_chunk_bwd(q, k, v, g, beta, do, h0, None, dht)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and torch.equal(dh0, dht)
+
+    log("[degenerate bwd] packed N=3, every slot empty, 70 unowned rows")
+    q, k, v, g, beta, do, h0, dht = tensors(1, 70, 3)
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    dq, dk, dv, dg, db, dh0 = kda.kda_chunk_bwd(q, k, v, g, beta, do, h0, cu, dht)
+    torch.cuda.synchronize()
+    assert torch.equal(dh0, dht)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg), ("dbeta", db)):
+        assert (t.float() == 0).all(), f"{name} must be zero outside every sequence"
