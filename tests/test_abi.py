@@ -327,3 +327,19 @@ def test_recurrent_ex_layout_and_intermediate_rejects(lib):
     assert b"state_layout" in lib.kda_last_error()
     assert _rec_ex(lib, inter=FAKE + 4) == -2
     assert _rec_ex(lib, lay=1, inter=FAKE, cu=FAKE, N=0, T=0) == 0
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128), (128, 64)])
+def test_bench_record_bytes_match_the_library_layout(lib, K, V):
+    """The bench prices the Stage 1+2 and scan kernels with its own count of one record's
+    bytes; it must equal the record stride of the library's workspace layout (the
+    workspace grows by exactly HV records per added chunk of a dense sequence)."""
+    import bench
+    B, H, HV, nt = 1, 2, 4, 41
+    total = lib.kda_chunk_fwd_workspace_bytes(B, 64 * nt, H, HV, K, V, B, 0, 1)
+    records = total - _sched_bytes(B, B * nt)
+    assert records % (HV * nt) == 0
+    rec = records // (HV * nt)
+    # the library pads each record to 256 bytes; the bench counts the bytes it holds
+    assert rec == (bench.record_bytes(K, V, 2) + 255) // 256 * 256
+    assert rec - bench.record_bytes(K, V, 2) < 256
