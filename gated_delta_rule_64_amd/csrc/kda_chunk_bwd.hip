@@ -25,6 +25,8 @@
 //   dT = dv' (beta v)^T + dw (beta kd)^T, dL = -(T^T dT T^T) strictly lower, dM = beta dL
 //   and the pair terms of Aqk and M with one one-sided 2^(Gamma_r - Gamma_s) <= 1 each.
 // All of it in fp32 (fp32 matrix cores for the dense products).
+#include <type_traits>
+
 #include "kda_chunk_common.h"
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -112,25 +114,83 @@ __device__ __forceinline__ void stage_f32(const float* src, size_t gstride, floa
 template <int R, int W, typename T, int NTH = BT>
 __device__ __forceinline__ void stage_rows(const T* src, size_t rstride, int len, float* dst, int ld, int tid) {
     constexpr int W4 = W / 4;
+    // rows past len read row len - 1 (in bounds) and are stored as zeros: no branch
+    // around the loads, so the unrolled loop issues them all before its first store
+    if (len <= 0) {   // (block-uniform) no row to read
+        for (int q = tid; q < R * W4; q += NTH)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(q / W4) * ld + 4 * (q % W4) + e] = 0.f;
+        return;
+    }
+    const int last = len - 1;
 #pragma unroll 4
     for (int q = tid; q < R * W4; q += NTH) {
         const int r = q / W4, c4 = 4 * (q % W4);
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (r < len) {
-            if constexpr (sizeof(T) == 2) {
-                const bf16x4 h = *reinterpret_cast<const bf16x4*>(src + (size_t)r * rstride + c4);
+        const int rl = r < len ? r : last;
+        float x[4];
+        if constexpr (sizeof(T) == 2) {
+            const bf16x4 h = *reinterpret_cast<const bf16x4*>(src + (size_t)rl * rstride + c4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (float)h[e];
-            } else {
-                const f32x4 f = *reinterpret_cast<const f32x4*>(src + (size_t)r * rstride + c4);
+            for (int e = 0; e < 4; ++e) x[e] = r < len ? (float)h[e] : 0.f;
+        } else {
+            const f32x4 f = *reinterpret_cast<const f32x4*>(src + (size_t)rl * rstride + c4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = f[e];
-            }
+            for (int e = 0; e < 4; ++e) x[e] = r < len ? f[e] : 0.f;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[r * ld + c4 + e] = x[e];
     }
 }
+
+// Rows of an input tensor (as stage_rows), in two steps: load() issues every load of
+// the calling thread into registers, store() converts and writes them to LDS. Staging
+// several tensors load-load-...-store-store keeps all their loads in flight together.
+template <int R, int W, typename T, int NTH>
+struct RowLoad {
+    static constexpr int W4 = W / 4, N = R * W4 / NTH;
+    static_assert(N * NTH == R * W4, "whole vectors per thread");
+    typedef typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type vec;
+    vec x[N];
+    __device__ __forceinline__ void load(const T* src, size_t rstride, int len, int tid) {
+        const int last = len > 0 ? len - 1 : 0;   // rows past len re-read row len - 1
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int q = tid + NTH * i, r = q / W4, c4 = 4 * (q % W4);
+            x[i] = len > 0 ? *reinterpret_cast<const vec*>(src + (size_t)(r < len ? r : last) * rstride + c4) : vec{};
+        }
+    }
+    __device__ __forceinline__ void store(int len, float* dst, int ld, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int q = tid + NTH * i, r = q / W4, c4 = 4 * (q % W4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[r * ld + c4 + e] = r < len ? (float)x[i][e] : 0.f;
+        }
+    }
+};
+
+// A fp32 [R][W] tile (as stage_f32), in the same two steps.
+template <int R, int W, int NTH>
+struct TileLoad {
+    static constexpr int W4 = W / 4, N = R * W4 / NTH;
+    static_assert(N * NTH == R * W4, "whole vectors per thread");
+    f32x4 x[N];
+    __device__ __forceinline__ void load(const float* src, size_t gstride, int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int q = tid + NTH * i;
+            x[i] = *reinterpret_cast<const f32x4*>(src + (size_t)(q / W4) * gstride + 4 * (q % W4));
+        }
+    }
+    __device__ __forceinline__ void store(float* dst, int ld, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int q = tid + NTH * i;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(q / W4) * ld + 4 * (q % W4) + e] = x[i][e];
+        }
+    }
+};
 
 struct BwdParams {
     const void* q;
@@ -1186,12 +1246,21 @@ __global__ __launch_bounds__(4 * K, 1) void bwd_pair_kernel(BwdParams p) {
     const float* wyC = p.wy + ci * (size_t)WL::FLOATS;
     const float sc = p.scale;
 
-    stage_rows<C, K, TIn, NTH>(qin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, qL, LK, tid);
-    stage_rows<C, K, TIn, NTH>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
-    stage_gate<K, NTH>(p, pos, hv, GmL, LK, tid);
-    stage_f32<C, C, NTH>(gsC + GL::DA, C, dAL, LA, tid);   // dAqk (the scale is applied at use)
-    stage_f32<C, C, NTH>(wyC + WL::DM, C, dML, LA, tid);
-    if (tid < K) dGL[tid] = gsC[GL::DG + tid];
+    {
+        // q, k, dAqk and dM loads go out together, the gate is staged meanwhile
+        RowLoad<C, K, TIn, NTH> lq_, lk_;
+        TileLoad<C, C, NTH> la_, lm_;
+        lq_.load(qin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid);
+        lk_.load(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid);
+        la_.load(gsC + GL::DA, C, tid);   // dAqk (the scale is applied at use)
+        lm_.load(wyC + WL::DM, C, tid);
+        stage_gate<K, NTH>(p, pos, hv, GmL, LK, tid);
+        if (tid < K) dGL[tid] = gsC[GL::DG + tid];
+        lq_.store(len, qL, LK, tid);
+        lk_.store(len, kL, LK, tid);
+        la_.store(dAL, LA, tid);
+        lm_.store(dML, LA, tid);
+    }
     __syncthreads();
     if (p.in.l2norm_q) l2norm_rows_lds<K>(qL, LK, tid);        // threads 0 .. 63
     if (p.in.l2norm_k) l2norm_rows_lds<K>(kL, LK, tid - C);    // threads 64 .. 127
