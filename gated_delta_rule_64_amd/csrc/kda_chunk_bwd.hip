@@ -1064,8 +1064,10 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
     const TB* bin = reinterpret_cast<const TB*>(p.beta);
 
     // ---- loads and the chunk-local cumsum of g ----
-    stage_rows<C, K, TIn, NTH>(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, kL, LK, tid);
+    RowLoad<C, K, TIn, NTH> lk_;
+    lk_.load(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid);
     stage_gate<K, NTH>(p, pos, hv, XL, LX, tid);
+    lk_.store(len, kL, LK, tid);
     if (tid < C) {
         float b = tid < len ? to_f32(bin[(size_t)(pos.x + tid) * p.HV + hv]) : 0.f;
         if (p.in.beta_sig != 0.f && tid < len) b = beta_from_logit(b, p.in.beta_sig);
@@ -1081,16 +1083,18 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
         for (int r = 0; r < C; ++r) { acc += XL[r * LX + tid]; XL[r * LX + tid] = acc; }
     }
     __syncthreads();
-    // kd = k 2^Gamma; M and T = (I + diag(beta) M)^-1 as Stage 2 of the recompute left them
-    for (int e = tid; e < C * K; e += NTH) {
-        const int r = e / K, d = e % K;
-        kL[r * LK + d] *= exp2_fast(XL[r * LX + d]);
-    }
+    // kd = k 2^Gamma; M and T = (I + diag(beta) M)^-1 as Stage 2 of the recompute left
+    // them (their loads issued first, stored after the kd loop)
     {
-        const float* Mg = p.mt + ci * (size_t)(C * C);
-        const float* Tg = p.mt + ((size_t)p.NCmax * p.HV + ci) * (C * C);
-        stage_f32<C, C, NTH>(Mg, C, ML, LA, tid);
-        stage_f32<C, C, NTH>(Tg, C, TL, LA, tid);
+        TileLoad<C, C, NTH> lm_, lt_;
+        lm_.load(p.mt + ci * (size_t)(C * C), C, tid);
+        lt_.load(p.mt + ((size_t)p.NCmax * p.HV + ci) * (C * C), C, tid);
+        for (int e = tid; e < C * K; e += NTH) {
+            const int r = e / K, d = e % K;
+            kL[r * LK + d] *= exp2_fast(XL[r * LX + d]);
+        }
+        lm_.store(ML, LA, tid);
+        lt_.store(TL, LA, tid);
     }
     __syncthreads();
     // row sums over one tile's columns (the 16 lanes of a row), added into dbL
@@ -1108,9 +1112,14 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
     for (int i = 0; i < NT_DT; ++i) dT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // ---- value side: dv = beta T^T dv', dbeta += rowsum((T^T dv') v), dT = dv' (beta v)^T ----
-    const float* dvC = p.dvn + ci * (size_t)C * V;
-    stage_f32<C, V, NTH>(dvC, V, XL, LX, tid);
-    stage_rows<C, V, TIn, NTH>(vin + ((size_t)pos.x * p.HV + hv) * V, (size_t)p.HV * V, len, YL, LY, tid);
+    {
+        TileLoad<C, V, NTH> ldv_;
+        RowLoad<C, V, TIn, NTH> lv_;
+        ldv_.load(p.dvn + ci * (size_t)C * V, V, tid);
+        lv_.load(vin + ((size_t)pos.x * p.HV + hv) * V, (size_t)p.HV * V, len, tid);
+        ldv_.store(XL, LX, tid);
+        lv_.store(len, YL, LY, tid);
+    }
     __syncthreads();
     TIn* dvout = reinterpret_cast<TIn*>(p.dv);
     for (int t = wave; t < 4 * (V / 16); t += NW) {
