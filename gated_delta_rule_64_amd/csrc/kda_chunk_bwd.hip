@@ -1121,6 +1121,10 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
         lv_.store(len, YL, LY, tid);
     }
     __syncthreads();
+    // dw (for the key side) is loaded now and lands in XL once the value side is done
+    const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
+    TileLoad<C, K, NTH> ldw_;
+    ldw_.load(gsC + GL::DW, K, tid);
     TIn* dvout = reinterpret_cast<TIn*>(p.dv);
     for (int t = wave; t < 4 * (V / 16); t += NW) {
         const int sb = t / (V / 16), nt = t % (V / 16);
@@ -1145,8 +1149,7 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
     }
     __syncthreads();
     // ---- key side: dkd = beta T^T dw, dbeta += rowsum((T^T dw) kd), dT += dw (beta kd)^T ----
-    const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
-    stage_f32<C, K, NTH>(gsC + GL::DW, K, XL, LX, tid);
+    ldw_.store(XL, LX, tid);
     __syncthreads();
     float* wyC = p.wy + ci * (size_t)WL::FLOATS;
     for (int t = wave; t < 4 * (K / 16); t += NW) {
