@@ -688,6 +688,66 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
 // contraction r; w is a single bf16 in the record, so this copy is exact).
 constexpr int PT_LD = 72;
 
+// A fragment-order bf16 record tile (R rows, KC contraction, its residual tile at
+// + R * KC) transposed into column-major LDS (dst[col * PT_LD + row]), in two steps:
+// load() issues the thread's loads, store() writes them, so several tiles' loads are in
+// flight together.
+template <int R, int KC, int NTH>
+struct FragTLoad {
+    typedef Mma<__bf16> M;
+    static constexpr int N = R * KC / 8 / NTH, NS = KC / M::KS;
+    static_assert(N * NTH * 8 == R * KC, "whole runs per thread");
+    bf16x8 h[N], l[N];
+    __device__ __forceinline__ void load(const __bf16* t, int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int e0 = 8 * (tid + NTH * i);
+            h[i] = *reinterpret_cast<const bf16x8*>(t + e0);
+            l[i] = *reinterpret_cast<const bf16x8*>(t + e0 + R * KC);
+        }
+    }
+    __device__ __forceinline__ void store(__bf16* dh, __bf16* dl, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int q = tid + NTH * i, ln = q % 64, blk = q / 64;
+            const int row = 16 * (blk / NS) + (ln & 15);
+            const int col = (blk % NS) * M::KS + (ln >> 4) * M::KPL;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                dh[(col + x) * PT_LD + row] = h[i][x];
+                dl[(col + x) * PT_LD + row] = l[i][x];
+            }
+        }
+    }
+};
+
+// R rows of W bf16 values (row r at src + r * rstride) transposed into LDS
+// (dst[col * PT_LD + r]), zeros from row len on, in the same two steps; rows past len
+// re-read row len - 1 (in bounds).
+template <int R, int W, int NTH>
+struct RowTLoad {
+    static constexpr int W8 = W / 8, N = R * W8 / NTH;
+    static_assert(N * NTH == R * W8, "whole runs per thread");
+    bf16x8 x[N];
+    __device__ __forceinline__ void load(const __bf16* src, size_t rstride, int len, int tid) {
+        const int last = len > 0 ? len - 1 : 0;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int q = tid + NTH * i, r = q / W8, c0 = 8 * (q % W8);
+            x[i] = len > 0 ? *reinterpret_cast<const bf16x8*>(src + (size_t)(r < len ? r : last) * rstride + c0)
+                           : bf16x8{};
+        }
+    }
+    __device__ __forceinline__ void store(int len, __bf16* dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int q = tid + NTH * i, r = q / W8, c0 = 8 * (q % W8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[(c0 + e) * PT_LD + r] = r < len ? x[i][e] : (__bf16)0.f;
+        }
+    }
+};
+
 template <int K, int V>
 __global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
     typedef ScanOps<K, V> SO;
@@ -710,33 +770,17 @@ __global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
     const __bf16* dout = reinterpret_cast<const __bf16*>(p.dout);
     float* ops = p.sops + ci * (size_t)SO::FLOATS;
 
-    // a fragment-order record tile (R rows, KC contraction; residual at + R*KC), each
-    // lane run of 8 transposed into column-major LDS: dst[col * PT_LD + row]
-    auto stage_t = [&](const __bf16* t, int R, int KC, __bf16* dh, __bf16* dl) {
-        const int NS = KC / M::KS;
-        for (int q = tid; q < R * KC / 8; q += BT) {
-            const int e0 = 8 * q;
-            const int l = q % 64, blk = q / 64;
-            const int row = 16 * (blk / NS) + (l & 15);
-            const int col = (blk % NS) * M::KS + (l >> 4) * M::KPL;
-            const bf16x8 h = *reinterpret_cast<const bf16x8*>(t + e0);
-            const bf16x8 lo = *reinterpret_cast<const bf16x8*>(t + e0 + R * KC);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                dh[(col + x) * PT_LD + row] = h[x];
-                dl[(col + x) * PT_LD + row] = lo[x];
-            }
-        }
-    };
-    stage_t(reinterpret_cast<const __bf16*>(rec + p.off_aqk), C, C, aTh, aTl);
-    stage_t(reinterpret_cast<const __bf16*>(rec + p.off_qg), C, K, qTh, qTl);
-    // do rows r < len (zeros after), 8 values per thread and step, transposed
-    for (int q = tid; q < C * V / 8; q += BT) {
-        const int r = q / (V / 8), v0 = 8 * (q % (V / 8));
-        bf16x8 x = {};
-        if (r < pos.y) x = *reinterpret_cast<const bf16x8*>(dout + ((size_t)(pos.x + r) * p.HV + hv) * V + v0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dT[(v0 + e) * PT_LD + r] = x[e];
+    {
+        // Aqk and qg (hi, lo) and the do rows: every load first, then the transposed stores
+        FragTLoad<C, C, BT> la_;
+        FragTLoad<C, K, BT> lq_;
+        RowTLoad<C, V, BT> ld_;
+        la_.load(reinterpret_cast<const __bf16*>(rec + p.off_aqk), tid);
+        lq_.load(reinterpret_cast<const __bf16*>(rec + p.off_qg), tid);
+        ld_.load(dout + ((size_t)pos.x * p.HV + hv) * V, (size_t)p.HV * V, pos.y, tid);
+        la_.store(aTh, aTl, tid);
+        lq_.store(qTh, qTl, tid);
+        ld_.store(pos.y, dT, tid);
     }
     __syncthreads();
     auto frag = [&](const __bf16* t, int row, int ks) {
