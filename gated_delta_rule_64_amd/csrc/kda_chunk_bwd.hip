@@ -721,6 +721,35 @@ struct FragTLoad {
     }
 };
 
+// A fragment-order bf16 record tile (R rows, KC contraction; with SPLIT its residual
+// tile at + R * KC too) copied into row-major LDS (dst[row * ld + col]), in two steps
+// like FragTLoad.
+template <int R, int KC, int NTH, bool SPLIT>
+struct FragRLoad {
+    typedef Mma<__bf16> M;
+    static constexpr int N = R * KC / 8 / NTH, NS = KC / M::KS;
+    static_assert(N * NTH * 8 == R * KC, "whole runs per thread");
+    bf16x8 h[N], l[SPLIT ? N : 1];
+    __device__ __forceinline__ void load(const __bf16* t, int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int e0 = 8 * (tid + NTH * i);
+            h[i] = *reinterpret_cast<const bf16x8*>(t + e0);
+            if constexpr (SPLIT) l[i] = *reinterpret_cast<const bf16x8*>(t + e0 + R * KC);
+        }
+    }
+    __device__ __forceinline__ void store(__bf16* dh, __bf16* dl, int ld, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int q = tid + NTH * i, ln = q % 64, blk = q / 64;
+            const int row = 16 * (blk / NS) + (ln & 15);
+            const int col = (blk % NS) * M::KS + (ln >> 4) * M::KPL;
+            *reinterpret_cast<bf16x8*>(dh + row * ld + col) = h[i];
+            if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(dl + row * ld + col) = l[i];
+        }
+    }
+};
+
 // R rows of W bf16 values (row r at src + r * rstride) transposed into LDS
 // (dst[col * PT_LD + r]), zeros from row len on, in the same two steps; rows past len
 // re-read row len - 1 (in bounds).
@@ -811,23 +840,19 @@ __global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
         }
     __syncthreads();
     // kg^T (rows d, contraction s; hi, lo) and w (rows r, contraction d) as row-major bf16
-    auto stage_rm = [&](const __bf16* t, int R, int KC, bool split, __bf16* dh, __bf16* dl, int ld) {
-        const int NS = KC / M::KS;
-        for (int q = tid; q < R * KC / 8; q += BT) {
-            const int l = q % 64, blk = q / 64;
-            const int row = 16 * (blk / NS) + (l & 15);
-            const int col = (blk % NS) * M::KS + (l >> 4) * M::KPL;
-            *reinterpret_cast<bf16x8*>(dh + row * ld + col) = *reinterpret_cast<const bf16x8*>(t + 8 * q);
-            if (split)
-                *reinterpret_cast<bf16x8*>(dl + row * ld + col) = *reinterpret_cast<const bf16x8*>(t + 8 * q + R * KC);
-        }
-    };
     __bf16* kTh = reinterpret_cast<__bf16*>(smem);   // kg^T [d][s], hi
     __bf16* kTl = kTh + K * PT_LD;                   //                lo
     __bf16* wR = kTl + K * PT_LD;                    // w [r][d]
     constexpr int WLD = K + 8;
-    stage_rm(reinterpret_cast<const __bf16*>(rec + p.off_kgT), K, C, true, kTh, kTl, PT_LD);
-    stage_rm(reinterpret_cast<const __bf16*>(rec + p.off_w), C, K, false, wR, nullptr, WLD);
+    {
+        // kg^T (hi, lo) and w from the record: every load first, then the LDS stores
+        FragRLoad<K, C, BT, true> lk_;
+        FragRLoad<C, K, BT, false> lw_;
+        lk_.load(reinterpret_cast<const __bf16*>(rec + p.off_kgT), tid);
+        lw_.load(reinterpret_cast<const __bf16*>(rec + p.off_w), tid);
+        lk_.store(kTh, kTl, PT_LD, tid);
+        lw_.store(wR, nullptr, WLD, tid);
+    }
     __syncthreads();
     // kg (rows s, contraction d) and w^T (rows d, contraction r) in bf16 fragment order:
     // kg hi at KG, lo at KG + C K (bf16 elements); w^T at WT
