@@ -1649,11 +1649,14 @@ __device__ __forceinline__ void load_row_wqu(RowFrags<K, BV>& F, const char* rec
         F.u[nt] = *reinterpret_cast<const f32x4*>(u + AccTile::quad(v0 + 16 * nt + lr, 16 * b + 4 * lq));
 }
 
+// i: the chunk's index within its sequence, whose rows are bos .. bos + slen - 1. The
+// position is formed from values loaded before the loop: a load here, into registers a
+// dense launch would fill by moves, makes the compiler wait for every load in flight.
 template <int K, int BV>
 __device__ __forceinline__ void load_row_a(RowFrags<K, BV>& F, const char* rec, const ScanParams& p,
-                                           int c, int b, int lane) {
+                                           int bos, int slen, int i, int b, int lane) {
     typedef FragTile<__bf16, C, C> FQ;
-    F.pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
+    F.pos = make_int2(bos + i * C, slen - i * C < C ? slen - i * C : C);
     const __bf16* aqk = reinterpret_cast<const __bf16*>(rec + p.off_aqk);
     // band b of the lower-triangular Aqk has nonzero columns only below 16b + 16
     const int njs = (16 * b + 16 + 31) / 32;
@@ -1736,11 +1739,22 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
         __bf16* o = reinterpret_cast<__bf16*>(p.o);
         RowFrags<K, BV> R0, R1;
         static_assert(ROW_PREFETCH == 2, "the row loop is unrolled for two buffers");
+        // the sequence's rows (chunk c0 + i starts at row bos + i C; the schedule's table
+        // holds exactly that for packed sequences)
+        int bos = 0, slen = 0;
         if (c0 < c1) {
+            if (p.dense) {
+                bos = n * p.T;
+                slen = p.T;
+            } else {
+                const int2 first = p.table[c0], last = p.table[c1 - 1];
+                bos = first.x;
+                slen = last.x + last.y - first.x;
+            }
             load_row_wqu<K, BV>(R0, record(c0), p, b, lane, v0);
-            load_row_a<K, BV>(R0, record(c0), p, c0, b, lane);
+            load_row_a<K, BV>(R0, record(c0), p, bos, slen, 0, b, lane);
             load_row_wqu<K, BV>(R1, record(c0 + 1), p, b, lane, v0);
-            load_row_a<K, BV>(R1, record(c0 + 1), p, clampc(c0 + 1), b, lane);
+            load_row_a<K, BV>(R1, record(c0 + 1), p, bos, slen, clampc(c0 + 1) - c0, b, lane);
         }
         lds_barrier();   // initial S^T
         int cur = 0;
@@ -1812,7 +1826,7 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                     *reinterpret_cast<vec4*>(o + ((size_t)(rs + i) * p.HV + hv) * V + v0 + 16 * nt + 4 * lq) = ov;
                 }
             }
-            load_row_a<K, BV>(F, record(cn), p, clampc(cn), b, lane);
+            load_row_a<K, BV>(F, record(cn), p, bos, slen, clampc(cn) - c0, b, lane);
             lds_barrier();   // B: S_(c+1) complete
             cur ^= 1;
         };
