@@ -3,31 +3,41 @@
 
 Headline: the chunked forward on the long-context workload (B=1, T=8192, H=16 q/k heads,
 HV=32 value heads, K=V=128, bf16 q/k/v/beta, fp32 log2 gates clamped at -5, no initial
-state, no final state): tokens/s over K timed steps with inputs resident in HBM, plus
-the fraction of bf16 matrix-core peak its flops represent. A step is one call of
-kda_chunk_fwd (scheduler-free dense mode: Stage 1+2 kernel, then the Stage 3+4 scan).
+state, no final state). A step is one call of kda_chunk_fwd (dense mode: the Stage 1+2
+kernel, then the Stage 3+4 scan) with its inputs resident in HBM. Before the timed steps
+the forward runs back to back for --preheat-s seconds (clocks at their working level),
+then --warmup untimed steps. Each of the --steps timed steps is preceded, outside its
+events, by a 512 MB write, so its 336 MB of inputs come from HBM and not the 256 MB
+MALL; `value` is tokens per second at the median step time, `ms_per_step` that median.
 
 Also reported on the same JSON line:
-  * roofline  -- the dominant kernel (the one with the largest average duration, timed
-                 live with HIP events recorded by kda_chunk_fwd_timed on the library's
-                 stream) against HBM peak, with that kernel's algorithmic bytes;
-  * flushed   -- the headline forward timed one rep at a time with a 512 MB write between
-                 reps (so its inputs come from HBM, not the 256 MB MALL): median, p10, p90;
-  * path      -- the whole step against the HBM floor of the workload's own inputs and
-                 outputs (336.1 MB), and the matrix-core fractions;
-  * gated     -- the same forward with the gate activation fused into Stage 1 (raw bf16
-                 gate input instead of the fp32 log2 decay);
-  * fused_inputs -- the same with every input fusion on (fused gate, q/k L2 norm, beta
-                 sigmoid x2); the decode line carries the same for the recurrent path;
-  * backward  -- the chunked backward of the headline forward (every input gradient);
-  * decode    -- the per-token recurrent forward on 4096 sequences x 32 heads (one token
-                 each, fp32 states in and out): state GB/s and fraction of HBM peak,
-                 and a plain-stream ceiling (torch.neg over the same state bytes);
-  * varlen    -- the packed-sequence forward (64 slots, ~31k tokens, 4 empty slots,
-                 initial and final states);
+  * roofline     -- the forward (both kernels) against HBM peak on the method's own bytes
+                    (inputs read once + o written once: 336,068,608 B per call), with the
+                    average launch duration of each kernel timed live on the library's
+                    stream (events recorded by kda_chunk_fwd_timed), each kernel's share of
+                    the method's bytes, the bytes its records add by design, and the HBM
+                    bytes the counters measured (committed rocprofv3 summary, when taken on
+                    the current kernel source);
+  * steps_ms     -- median, p10, p90, mean of the timed steps; back_to_back -- the same
+                    forward with no flush between steps (mean);
+  * path         -- matrix-core fractions (exact and dense-tile flop counts) against the
+                    published peak and against the measured ceiling (`ceilings`);
+  * ceilings     -- a bf16 matrix-core loop built here, the peak from the device's CU count
+                    and clock, and a plain HBM stream (the decode's);
+  * c2           -- the forward on B=2 T=4096 H=HV=16 with initial and final states
+                    (timed like the headline) against its 205.8 MB floor;
+  * gated, fused_inputs -- the headline with the gate activation (and the q/k norm and
+                    beta sigmoid) fused into the loads;
+  * backward     -- the chunked backward of the headline forward (every input gradient);
+  * varlen       -- the packed-sequence forward (64 slots, ~31k tokens, 4 empty slots,
+                    initial and final states);
+  * decode       -- the per-token recurrent forward on 4096 sequences x 32 heads (one token
+                    each, fp32 states in and out): state GB/s and fraction of HBM peak, and
+                    a plain-stream ceiling (torch.neg over the same state bytes);
   * cpu_baseline -- the fp64 CPU oracle on the full headline workload, host threads.
 
-Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--preheat-s 1.0]
+       [--only headline]   (the headline leg alone: for profiling its kernels)
 """
 from __future__ import annotations
 
@@ -97,9 +107,9 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_key):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, when it was taken
-    on the current kernel source (else None)."""
+def traffic_from_profiles():
+    """HBM bytes per launch of each forward kernel from the committed rocprofv3 counter
+    summary, when it was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_c3.json")
     if not os.path.exists(path):
         return None
@@ -109,37 +119,119 @@ def traffic_from_profiles(kernel_key):
         return None
     if d.get("source_hash") != source_hash():
         return None
-    return d.get("bytes_per_launch", {}).get(kernel_key)
+    return d.get("bytes_per_launch")
 
 
-def flushed_reps(call, reps, tokens, hip, sptr, dev):
-    """Time ``call`` one rep at a time with a 512 MB write between reps (outside the
-    events); median, p10, p90 of the reps."""
+def pctl(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(q * len(xs)))]
+
+
+def stats(xs):
+    return {"median": pctl(xs, 0.5), "p10": pctl(xs, 0.1), "p90": pctl(xs, 0.9),
+            "mean": sum(xs) / len(xs), "n": len(xs)}
+
+
+class Flusher:
+    """A 512 MB buffer written between timed reps (outside their events), so a rep's
+    inputs are read from HBM and not from the 256 MB MALL."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        self.r = 0
+
+    def __call__(self):
+        self.r += 1
+        self.buf.fill_(self.r & 0xFF)
+
+
+def timed_flushed(call, steps, hip, sptr, flush, nev=0):
+    """``steps`` reps of ``call(events)``, each after a flush; per rep the events are
+    [start, (nev inner events), end]. Returns the per-rep lists of event spans: the whole
+    rep, and one list per inner segment."""
     import torch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    rev = Events(hip, 2 * reps)
-    for r in range(reps):
-        flush.fill_(r & 0xFF)
-        hip.hipEventRecord(rev.ev[2 * r], sptr)
-        call(None)
-        hip.hipEventRecord(rev.ev[2 * r + 1], sptr)
+    per = nev + 2
+    ev = Events(hip, per * steps)
+    for r in range(steps):
+        flush()
+        base = per * r
+        hip.hipEventRecord(ev.ev[base], sptr)
+        call(ev.ev[base: base + per])
+        hip.hipEventRecord(ev.ev[base + per - 1], sptr)
     torch.cuda.synchronize()
-    reps_ms = sorted(rev.ms(2 * r, 2 * r + 1) for r in range(reps))
-    rev.close()
-    del flush
-    pct = lambda q: reps_ms[min(len(reps_ms) - 1, int(q * len(reps_ms)))]
-    return {"reps": reps, "median_ms": pct(0.5), "p10_ms": pct(0.1), "p90_ms": pct(0.9),
-            "tokens_per_s_median": tokens / (pct(0.5) * 1e-3)}
+    whole = [ev.ms(per * r, per * r + per - 1) for r in range(steps)]
+    segs = [[ev.ms(per * r + i, per * r + i + 1) for r in range(steps)] for i in range(per - 1)]
+    ev.close()
+    return whole, segs
+
+
+def back_to_back(call, steps, hip, sptr):
+    import torch
+    ev = Events(hip, 2)
+    torch.cuda.synchronize()
+    hip.hipEventRecord(ev.ev[0], sptr)
+    for _ in range(steps):
+        call()
+    hip.hipEventRecord(ev.ev[1], sptr)
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / steps
+    ev.close()
+    return ms
+
+
+def device_peak_tflops(hip, dev_index):
+    """bf16 dense matrix-core peak from the device's own CU count and peak shader clock:
+    CUs x clock x 4,096 flop per clock per CU (four SIMDs, one 16x16x32 bf16 product of
+    16,384 flops every 16 clocks each)."""
+    cus, khz = ctypes.c_int(), ctypes.c_int()
+    hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    # hipDeviceAttributeMultiprocessorCount = 63, hipDeviceAttributeClockRate = 5 (kHz)
+    if hip.hipDeviceGetAttribute(ctypes.byref(cus), 63, dev_index) != 0:
+        return None
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, dev_index) != 0:
+        return None
+    return {"cus": cus.value, "clock_mhz": khz.value / 1e3,
+            "bf16_tflops": cus.value * khz.value * 1e3 * 4096 / 1e12}
+
+
+def mfma_ceiling(hip, sptr, dev):
+    """Time the bf16 matrix-core loop of libkda_ceiling.so (every wave eight independent
+    16x16x32 products per trip, 16 waves per CU)."""
+    import torch
+    path = os.path.join(ROOT, "gated_delta_rule_64_amd", "libkda_ceiling.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.kda_ceiling_mfma_bf16.restype = ctypes.c_int
+    lib.kda_ceiling_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks, iters = 256 * 4, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        assert lib.kda_ceiling_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), sptr) == 0
+    torch.cuda.synchronize()
+    ev = Events(hip, 2)
+    hip.hipEventRecord(ev.ev[0], sptr)
+    assert lib.kda_ceiling_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), sptr) == 0
+    hip.hipEventRecord(ev.ev[1], sptr)
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1)
+    ev.close()
+    flops = blocks * 4 * iters * 8 * 16384.0
+    return {"kernel": "bf16 16x16x32 matrix-core loop (1,024 blocks x 4 waves, 8 independent chains)",
+            "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--preheat-s", type=float, default=1.0,
+                    help="seconds of back-to-back headline forwards before the warm-up steps")
     ap.add_argument("--decode-steps", type=int, default=10)
-    ap.add_argument("--flushed-reps", type=int, default=50,
-                    help="reps of the headline forward timed one at a time with a cache flush between")
+    ap.add_argument("--only", choices=["headline"], default=None,
+                    help="run the headline leg alone (for profiling its kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain elementwise kernel that reads and writes 1 GiB "
@@ -151,6 +243,7 @@ def main():
               "(sequences and heads shard across GPUs with no communication; run one "
               "process per GPU on its own share)", file=sys.stderr)
         sys.exit(2)
+    steps = max(1, args.steps)
 
     import torch
     from gated_delta_rule_64_amd import _lib
@@ -168,6 +261,28 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = vp(stream.cuda_stream)
+    flush = Flusher(dev)
+
+    def timed_call(d, out, ws, ws_bytes, B, T, H, HV, K, V, N, final=None):
+        """kda_chunk_fwd_timed on dense inputs; returns call(events) where events is a
+        4-slot list [start, mid, end] mapped to the library's slots 0, 2, 3."""
+        h0 = d["initial_state"]
+
+        def call(evs):
+            slots = None if evs is None else ctypes.cast((vp * 4)(evs[0], None, evs[1], evs[2]), vp)
+            rc = lib.kda_chunk_fwd_timed(
+                vp(d["q"].data_ptr()), vp(d["k"].data_ptr()), vp(d["v"].data_ptr()),
+                vp(d["g"].data_ptr()), vp(d["beta"].data_ptr()),
+                None if h0 is None else vp(h0.data_ptr()), None, N, vp(out.data_ptr()),
+                None if final is None else vp(final.data_ptr()), B, T, H, HV, K, V, kda.KDA_BF16,
+                kda.KDA_BF16, 0.0, 64, vp(ws.data_ptr()), ws_bytes, None, sptr, slots)
+            if rc != 0:
+                raise RuntimeError(lib.kda_last_error().decode())
+        return call
+
+    # ---------------- headline: c3 ----------------
     w = inputs.WORKLOADS["c3"]
     d = inputs.make(w, device=dev)
     B, T, H, HV, K, V = w.B, w.T, w.H, w.HV, w.K, w.V
@@ -175,17 +290,7 @@ def main():
     ws_bytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, N, 0, kda.KDA_BF16)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(d["v"])
-    stream = torch.cuda.current_stream(dev)
-    sptr = vp(stream.cuda_stream)
-
-    def call(events_ptr):
-        rc = lib.kda_chunk_fwd_timed(
-            vp(d["q"].data_ptr()), vp(d["k"].data_ptr()), vp(d["v"].data_ptr()),
-            vp(d["g"].data_ptr()), vp(d["beta"].data_ptr()), None, None, N,
-            vp(out.data_ptr()), None, B, T, H, HV, K, V, kda.KDA_BF16, kda.KDA_BF16,
-            0.0, 64, vp(ws.data_ptr()), ws_bytes, None, sptr, events_ptr)
-        if rc != 0:
-            raise RuntimeError(lib.kda_last_error().decode())
+    call = timed_call(d, out, ws, ws_bytes, B, T, H, HV, K, V, N)
 
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -194,61 +299,135 @@ def main():
         torch.neg(src, out=dst)          # 1 GiB read + 1 GiB written by one plain kernel
         torch.cuda.synchronize()
         del src, dst
+    # pre-heat: the forward back to back for a fixed wall time, so the timed steps run at
+    # the clocks a busy GPU holds (a cold start ran both kernels ~17% slower)
+    t_end = time.time() + max(0.0, args.preheat_s)
+    n_pre = 0
+    while True:
+        for _ in range(50):
+            call(None)
+        n_pre += 50
+        torch.cuda.synchronize()
+        if time.time() >= t_end:
+            break
     for _ in range(args.warmup):
         call(None)
     torch.cuda.synchronize()
-    steps = args.steps
-    # two events per step: after Stage 1+2 (mid) and after the scan (end); a step starts
-    # where the previous one ended (the first at the outer start event), so the kernels
-    # run back to back with one marker between them
-    ev = Events(hip, 2 * steps)
-    outer = Events(hip, 2)
-    slots = [(vp * 4)(None, None, ev.ev[2 * s], ev.ev[2 * s + 1]) for s in range(steps)]
-    torch.cuda.synchronize()
-    hip.hipEventRecord(outer.ev[0], sptr)
-    for s in range(steps):
-        call(ctypes.cast(slots[s], vp))
-    hip.hipEventRecord(outer.ev[1], sptr)
-    torch.cuda.synchronize()
-    total_ms = outer.ms(0, 1)
-
-    def span(a, b):
-        out_ = ctypes.c_float()
-        assert hip.hipEventElapsedTime(ctypes.byref(out_), a, b) == 0
-        return float(out_.value)
-
-    starts = [outer.ev[0]] + [ev.ev[2 * s + 1] for s in range(steps - 1)]
-    intra_ms = sum(span(starts[s], ev.ev[2 * s]) for s in range(steps)) / steps
-    scan_ms = sum(ev.ms(2 * s, 2 * s + 1) for s in range(steps)) / steps
-    ev.close()
-    outer.close()
-    ms_per_step = total_ms / steps
+    whole, (seg_intra, seg_scan) = timed_flushed(call, steps, hip, sptr, flush, nev=1)
+    st = stats(whole)
+    ms_per_step = st["median"]
     tokens = B * T
     tok_s = tokens / (ms_per_step * 1e-3)
+    intra_ms = sum(seg_intra) / steps
+    scan_ms = sum(seg_scan) / steps
+    fwd_ms = intra_ms + scan_ms
+    b2b_ms = back_to_back(lambda: call(None), steps, hip, sptr)
 
-    # the same forward timed one rep at a time with a 512 MB write between reps (outside
-    # the events), so the inputs (336 MB) are not served from the 256 MB MALL: median,
-    # p10, p90 over the reps
-    flushed = None
-    if args.flushed_reps > 0:
-        flushed = flushed_reps(call, args.flushed_reps, tokens, hip, sptr, dev)
-
-    # algorithmic quantities of the workload (inputs + outputs once, flops of the method)
-    path_bytes = (2 * B * T * H * K * 2 + B * T * HV * V * 2 * 2 + B * T * HV * K * 4 + B * T * HV * 2)
+    # the method's bytes: inputs read once, o written once (SURVEY's 1,282 B per
+    # token-head at GVA 2); which kernel moves which share of them; and what the records
+    # between the two kernels add by design
+    q_b = 2 * B * T * H * K * 2                 # q, k
+    v_b = B * T * HV * V * 2
+    g_b = B * T * HV * K * 4
+    beta_b = B * T * HV * 2
+    o_b = B * T * HV * V * 2
+    method_bytes = q_b + v_b + g_b + beta_b + o_b
+    in_bytes = method_bytes - o_b
     flops_exact = 141013.0 * B * T * HV
     flops_dense = 180224.0 * B * T * HV
     nchunks = B * ((T + 63) // 64)
     rec = record_bytes(K, V, 2) * nchunks * HV
-    intra_bytes = path_bytes - B * T * HV * V * 2 + rec     # reads inputs, writes records
-    scan_bytes = rec + B * T * HV * V * 2                    # reads records, writes o
-    kern = {"intra": (intra_ms, intra_bytes), "scan": (scan_ms, scan_bytes)}
-    dom = max(kern, key=lambda k_: kern[k_][0])
-    dom_ms, dom_bytes = kern[dom]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(dom)
+    counters = traffic_from_profiles()
+    traffic = None
+    if counters and "intra" in counters and "scan" in counters:
+        traffic = counters["intra"] + counters["scan"]
+    achieved = method_bytes / (fwd_ms * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm", "kernel": "chunk forward: Stage 1+2 kernel + scan kernel (one call)",
+        "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+        "traffic": traffic, "algorithmic_bytes": method_bytes, "avg_launch_ms": fwd_ms,
+        "dominant": "scan" if scan_ms >= intra_ms else "intra",
+        "kernels": {
+            "intra": {"avg_ms": intra_ms, "method_bytes": in_bytes,
+                      "method_GBs": in_bytes / (intra_ms * 1e-3) / 1e9,
+                      "design_bytes": in_bytes + rec,
+                      "counter_bytes": counters.get("intra") if counters else None},
+            "scan": {"avg_ms": scan_ms, "method_bytes": o_b,
+                     "method_GBs": o_b / (scan_ms * 1e-3) / 1e9,
+                     "design_bytes": rec + o_b,
+                     "counter_bytes": counters.get("scan") if counters else None},
+        },
+        "record_bytes_per_call": rec,
+    }
+    peak_dev = device_peak_tflops(hip, 0)
+    ceil = mfma_ceiling(hip, sptr, dev)
+    tflops_exact = flops_exact / (ms_per_step * 1e-3) / 1e12
+    path = {
+        "hbm_floor_bytes": method_bytes, "hbm_floor_us": method_bytes / HBM_PEAK_GBS / 1e3,
+        "achieved_GBs": method_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac": method_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "tflops_exact": tflops_exact,
+        "mfma_frac_exact_flops": tflops_exact / BF16_PEAK_TFLOPS,
+        "mfma_frac_dense_tile_flops": flops_dense / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "mfma_frac_exact_of_measured_ceiling": tflops_exact / ceil["tflops"] if ceil else None,
+    }
+    result = {
+        "metric": "KDA fwd tokens/s + % bf16 MFMA peak at T=8192; decode state GB/s % HBM",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=log2(sigmoid(N(2,1))) >= -5, beta=sigmoid(N(0,1)))",
+        "config": {"workload": "chunk_kda fwd B=1 T=8192 H=16 HV=32 K=V=128 bf16, h0=None, no final state",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "timing": {"per_step": "512 MB write before each step (outside its events); value at the median step",
+                   "preheat_s": args.preheat_s, "preheat_steps": n_pre},
+        "steps_ms": st,
+        "back_to_back": {"ms_per_step": b2b_ms, "tokens_per_s": tokens / (b2b_ms * 1e-3)},
+        "roofline": roofline,
+        "path": path,
+        "ceilings": {"mfma_bf16_measured": ceil,
+                     "mfma_bf16_device": peak_dev,
+                     "mfma_bf16_published_tflops": BF16_PEAK_TFLOPS,
+                     "hbm_published_GBs": HBM_PEAK_GBS},
+    }
+    if args.only == "headline":
+        print(json.dumps(result), flush=True)
+        return
 
-    # the same forward with the gate activation fused into Stage 1: raw bf16 gate input,
-    # A_log = log(U[1, 2]) per head, dt_bias N(0, 0.5^2) (timed like the headline)
+    # ---------------- c2: B=2 T=4096 H=HV=16, states in and out ----------------
+    w2 = inputs.WORKLOADS["c2"]
+    d2 = inputs.make(w2, device=dev)
+    ws2_bytes = kda.kda_chunk_fwd_workspace_bytes(w2.B, w2.T, w2.H, w2.HV, w2.K, w2.V, w2.B, 0, kda.KDA_BF16)
+    ws2 = torch.empty(ws2_bytes, dtype=torch.uint8, device=dev)
+    out2 = torch.empty_like(d2["v"])
+    fs2 = torch.empty_like(d2["initial_state"])
+    call2 = timed_call(d2, out2, ws2, ws2_bytes, w2.B, w2.T, w2.H, w2.HV, w2.K, w2.V, w2.B, final=fs2)
+    for _ in range(args.warmup):
+        call2(None)
+    whole2, (i2, s2) = timed_flushed(call2, steps, hip, sptr, flush, nev=1)
+    st2 = stats(whole2)
+    c2_bytes = (2 * w2.B * w2.T * w2.H * w2.K * 2 + 2 * w2.B * w2.T * w2.HV * w2.V * 2
+                + w2.B * w2.T * w2.HV * w2.K * 4 + w2.B * w2.T * w2.HV * 2
+                + 2 * d2["initial_state"].numel() * 4)
+    c2_fwd = (sum(i2) + sum(s2)) / steps
+    result["c2"] = {"workload": "chunk_kda fwd B=2 T=4096 H=HV=16 K=V=128 bf16, h0 N(0,0.05), final state",
+                    "ms_per_step": st2["median"], "steps_ms": st2,
+                    "tokens_per_s": w2.B * w2.T / (st2["median"] * 1e-3),
+                    "kernels_ms": {"intra": sum(i2) / steps, "scan": sum(s2) / steps},
+                    "algorithmic_bytes": c2_bytes, "hbm_floor_us": c2_bytes / HBM_PEAK_GBS / 1e3,
+                    "hbm_frac": c2_bytes / (c2_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del d2, ws2, out2, fs2
+
+    # ---------------- the headline with the fused input options ----------------
+    # the gate activation fused into Stage 1: raw bf16 gate input, A_log = log(U[1, 2])
+    # per head, dt_bias N(0, 0.5^2)
     gen = torch.Generator().manual_seed(w.seed + 100)
     g_raw = torch.randn(B, T, HV, K, generator=gen).mul(2.0).to(torch.bfloat16).to(dev)
     A_log = torch.rand(HV, generator=gen).add(1.0).log().to(dev)
@@ -259,15 +438,7 @@ def main():
                                 None, None, out=out, workspace=ws)
     for _ in range(args.warmup):
         gcall()
-    torch.cuda.synchronize()
-    gev = Events(hip, 2)
-    hip.hipEventRecord(gev.ev[0], sptr)
-    for _ in range(steps):
-        gcall()
-    hip.hipEventRecord(gev.ev[1], sptr)
-    torch.cuda.synchronize()
-    gated_ms = gev.ms(0, 1) / steps
-    gev.close()
+    gated_ms = back_to_back(gcall, steps, hip, sptr)
 
     # every input fusion at once: the fused gate as above, q / k L2-normalised in the
     # loads and beta = 2 sigmoid(beta) (the recipe's q, k and beta serve as the raw inputs)
@@ -278,19 +449,16 @@ def main():
                              workspace=ws)
     for _ in range(args.warmup):
         fcall()
-    torch.cuda.synchronize()
-    fev = Events(hip, 2)
-    hip.hipEventRecord(fev.ev[0], sptr)
-    for _ in range(steps):
-        fcall()
-    hip.hipEventRecord(fev.ev[1], sptr)
-    torch.cuda.synchronize()
-    fused_ms = fev.ms(0, 1) / steps
-    fev.close()
+    fused_ms = back_to_back(fcall, steps, hip, sptr)
     del g_raw, A_log, dt_bias
+    result["gated"] = {"workload": "the headline forward with the gate activation fused into Stage 1 (raw bf16 gate input, A_log, dt_bias)",
+                       "ms_per_step": gated_ms, "tokens_per_s": tokens / (gated_ms * 1e-3)}
+    result["fused_inputs"] = {"workload": "the headline forward with every input fusion: raw bf16 gate + A_log + dt_bias, q/k L2 norm in the loads, beta = 2 sigmoid(beta)",
+                              "ms_per_step": fused_ms, "tokens_per_s": tokens / (fused_ms * 1e-3)}
 
-    # the chunked backward of the headline forward: do ~ N(0, 1) bf16, no final-state
-    # gradient, no initial state (so no dh0); outputs and workspace allocated up front
+    # ---------------- backward of the headline forward ----------------
+    # do ~ N(0, 1) bf16, no final-state gradient, no initial state (so no dh0); outputs
+    # and workspace allocated up front
     bws_bytes = kda.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, 0, kda.KDA_BF16)
     bws = torch.empty(bws_bytes, dtype=torch.uint8, device=dev)
     gen = torch.Generator().manual_seed(w.seed + 200)
@@ -311,18 +479,16 @@ def main():
     bsteps = max(1, steps // 4)
     for _ in range(2):
         bcall()
-    torch.cuda.synchronize()
-    bev = Events(hip, 2)
-    hip.hipEventRecord(bev.ev[0], sptr)
-    for _ in range(bsteps):
-        bcall()
-    hip.hipEventRecord(bev.ev[1], sptr)
-    torch.cuda.synchronize()
-    bwd_ms = bev.ms(0, 1) / bsteps
-    bev.close()
+    bwd_ms = back_to_back(bcall, bsteps, hip, sptr)
+    # inputs, do and every gradient once (SURVEY's floor for the backward)
+    bwd_bytes = 2 * (q_b + v_b + g_b + beta_b) + o_b
+    result["backward"] = {"workload": "kda_chunk_bwd of the headline forward (dq, dk, dv, dg, dbeta; do ~ N(0,1) bf16, no dht)",
+                          "ms_per_step": bwd_ms, "tokens_per_s": tokens / (bwd_ms * 1e-3), "steps": bsteps,
+                          "algorithmic_bytes": bwd_bytes,
+                          "hbm_frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del bws, dout, gq, gk, gv, gg, gb
 
-    # decode: 4096 sequences x 32 heads, one token each, fp32 states in and out
+    # ---------------- decode: 4096 sequences x 32 heads ----------------
     del ws, out
     dd = inputs.make("dec", device=dev)
     dout = torch.empty_like(dd["v"])
@@ -333,15 +499,8 @@ def main():
                               dd["cu_seqlens"], output_final_state=True, out=dout, final_state=dstate)
     for _ in range(2):
         dcall()
-    torch.cuda.synchronize()
-    dev_ev = Events(hip, 2)
-    hip.hipEventRecord(dev_ev.ev[0], sptr)
-    for _ in range(args.decode_steps):
-        dcall()
-    hip.hipEventRecord(dev_ev.ev[1], sptr)
-    torch.cuda.synchronize()
-    dec_ms = dev_ev.ms(0, 1) / args.decode_steps
-    dev_ev.close()
+    dec_ms = back_to_back(dcall, args.decode_steps, hip, sptr)
+
     # the same decode with q / k normalisation and beta = sigmoid(beta) fused into the loads
     def dfcall():
         kda.kda_recurrent_fwd_ex(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["initial_state"],
@@ -350,15 +509,7 @@ def main():
                                  use_beta_sigmoid_in_kernel=True)
     for _ in range(2):
         dfcall()
-    torch.cuda.synchronize()
-    dev_ev = Events(hip, 2)
-    hip.hipEventRecord(dev_ev.ev[0], sptr)
-    for _ in range(args.decode_steps):
-        dfcall()
-    hip.hipEventRecord(dev_ev.ev[1], sptr)
-    torch.cuda.synchronize()
-    dec_fused_ms = dev_ev.ms(0, 1) / args.decode_steps
-    dev_ev.close()
+    dec_fused_ms = back_to_back(dfcall, args.decode_steps, hip, sptr)
     # the same decode with the states stored transposed ([V][K] per head)
     h0_vk = dd["initial_state"].transpose(-1, -2).contiguous()
     dstate_vk = torch.empty_like(h0_vk)
@@ -369,37 +520,29 @@ def main():
                                  final_state=dstate_vk, state_layout="vk")
     for _ in range(2):
         dvcall()
-    torch.cuda.synchronize()
-    dev_ev = Events(hip, 2)
-    hip.hipEventRecord(dev_ev.ev[0], sptr)
-    for _ in range(args.decode_steps):
-        dvcall()
-    hip.hipEventRecord(dev_ev.ev[1], sptr)
-    torch.cuda.synchronize()
-    dec_vk_ms = dev_ev.ms(0, 1) / args.decode_steps
-    dev_ev.close()
+    dec_vk_ms = back_to_back(dvcall, args.decode_steps, hip, sptr)
     del h0_vk, dstate_vk
     # what a plain elementwise stream achieves over the same bytes: torch.neg reading the
     # 8.6 GB state tensor and writing 8.6 GB (the practical HBM ceiling the decode is read against)
     for _ in range(2):
         torch.neg(dd["initial_state"], out=dstate)
-    torch.cuda.synchronize()
-    dev_ev = Events(hip, 2)
-    hip.hipEventRecord(dev_ev.ev[0], sptr)
-    for _ in range(args.decode_steps):
-        torch.neg(dd["initial_state"], out=dstate)
-    hip.hipEventRecord(dev_ev.ev[1], sptr)
-    torch.cuda.synchronize()
-    stream_ms = dev_ev.ms(0, 1) / args.decode_steps
-    dev_ev.close()
+    stream_ms = back_to_back(lambda: torch.neg(dd["initial_state"], out=dstate), args.decode_steps, hip, sptr)
     stream_gbs = 2 * dd["initial_state"].numel() * 4 / (stream_ms * 1e-3) / 1e9
     dec_bytes = (2 * dd["initial_state"].numel() * 4 + 3 * dd["q"].numel() * 2 + dd["g"].numel() * 4
                  + dd["beta"].numel() * 2 + dout.numel() * 2)
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
     del dd, dout, dstate
+    result["decode"] = {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
+                        "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
+                        "bytes": dec_bytes, "fused_inputs_ms": dec_fused_ms, "state_vk_ms": dec_vk_ms,
+                        "stream_ceiling": {"kernel": "torch.neg over the fp32 state tensor (8.59 GB read + 8.59 GB written)",
+                                           "ms": stream_ms, "GB_s": stream_gbs,
+                                           "decode_frac": dec_gbs / stream_gbs}}
+    result["ceilings"]["hbm_stream_GBs"] = stream_gbs
 
-    # packed varlen forward: 64 slots, lengths U[1, 1024] with 4 empty slots (~31k tokens),
-    # H=HV=16, K=V=128 bf16, fp32 initial and final states (timed like the headline)
+    # ---------------- packed varlen forward ----------------
+    # 64 slots, lengths U[1, 1024] with 4 empty slots (~31k tokens), H=HV=16, K=V=128
+    # bf16, fp32 initial and final states
     wv = inputs.WORKLOADS["vl"]
     dv_ = inputs.make(wv, device=dev)
     Bv, Tv = dv_["q"].shape[0], dv_["q"].shape[1]
@@ -416,56 +559,10 @@ def main():
                           workspace=vws)
     for _ in range(args.warmup):
         vcall()
-    torch.cuda.synchronize()
-    vev = Events(hip, 2)
-    hip.hipEventRecord(vev.ev[0], sptr)
-    for _ in range(steps):
-        vcall()
-    hip.hipEventRecord(vev.ev[1], sptr)
-    torch.cuda.synchronize()
-    var_ms = vev.ms(0, 1) / steps
-    vev.close()
+    var_ms = back_to_back(vcall, steps, hip, sptr)
     del dv_, vws, vout, vstate
-
-    result = {
-        "metric": "KDA fwd tokens/s + % bf16 MFMA peak at T=8192; decode state GB/s % HBM",
-        "value": tok_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=log2(sigmoid(N(2,1))) >= -5, beta=sigmoid(N(0,1)))",
-        "config": {"workload": "chunk_kda fwd B=1 T=8192 H=16 HV=32 K=V=128 bf16, h0=None, no final state",
-                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": dom_bytes, "avg_launch_ms": dom_ms,
-                     "kernels_ms": {"intra": intra_ms, "scan": scan_ms}},
-        "flushed": flushed,
-        "path": {"hbm_floor_bytes": path_bytes, "achieved_GBs": path_bytes / (ms_per_step * 1e-3) / 1e9,
-                 "hbm_frac": path_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                 "mfma_frac_exact_flops": flops_exact / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                 "mfma_frac_dense_tile_flops": flops_dense / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
-        "gated": {"workload": "the headline forward with the gate activation fused into Stage 1 (raw bf16 gate input, A_log, dt_bias)",
-                  "ms_per_step": gated_ms, "tokens_per_s": tokens / (gated_ms * 1e-3)},
-        "fused_inputs": {"workload": "the headline forward with every input fusion: raw bf16 gate + A_log + dt_bias, q/k L2 norm in the loads, beta = 2 sigmoid(beta)",
-                         "ms_per_step": fused_ms, "tokens_per_s": tokens / (fused_ms * 1e-3)},
-        "backward": {"workload": "kda_chunk_bwd of the headline forward (dq, dk, dv, dg, dbeta; do ~ N(0,1) bf16, no dht)",
-                     "ms_per_step": bwd_ms, "tokens_per_s": tokens / (bwd_ms * 1e-3), "steps": bsteps},
-        "varlen": {"workload": f"chunk_kda fwd packed: 64 slots (4 empty), {vtokens} tokens, H=HV=16 K=V=128 bf16, fp32 initial and final states",
-                   "ms_per_step": var_ms, "tokens_per_s": vtokens / (var_ms * 1e-3)},
-        "decode": {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
-                   "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
-                   "bytes": dec_bytes, "fused_inputs_ms": dec_fused_ms, "state_vk_ms": dec_vk_ms,
-                   "stream_ceiling": {"kernel": "torch.neg over the fp32 state tensor (8.59 GB read + 8.59 GB written)",
-                                      "ms": stream_ms, "GB_s": stream_gbs,
-                                      "decode_frac": dec_gbs / stream_gbs}},
-    }
+    result["varlen"] = {"workload": f"chunk_kda fwd packed: 64 slots (4 empty), {vtokens} tokens, H=HV=16 K=V=128 bf16, fp32 initial and final states",
+                        "ms_per_step": var_ms, "tokens_per_s": vtokens / (var_ms * 1e-3)}
 
     if not args.no_cpu_baseline:
         import oracle

@@ -19,6 +19,8 @@ Entry points (same names as the C ABI):
                                              (raw gate -> dA_log, ddt_bias; q/k norm; beta sigmoid)
   kda_chunk_fwd_workspace_bytes(...)         workspace size queries (also _bwd_)
   kda_last_error()                           reason for the last failure
+Every entry point takes ``debug=True``: wait for the call
+and raise KdaDeviceCheckError when a device-side check flagged the inputs.
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ from ._lib import (  # noqa: F401
     KDA_PRE_NEG_EIGVAL,
     KDA_STATE_KV,
     KDA_STATE_VK,
+    KdaDeviceCheckError,
     KdaError,
     kda_chunk_bwd,
     kda_chunk_bwd_ex,
@@ -53,7 +56,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "kda_chunk_fwd", "kda_chunk_bwd", "kda_chunk_bwd_ex", "kda_chunk_bwd_workspace_bytes", "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_recurrent_fwd",
     "kda_recurrent_fwd_ex", "kda_chunk_fwd_workspace_bytes",
-    "kda_last_error", "KdaError", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
+    "kda_last_error", "KdaError", "KdaDeviceCheckError", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
     "library_path", "KDA_GATE_LOG2", "KDA_GATE_RAW_F32", "KDA_GATE_RAW_BF16", "KDA_PRE_L2NORM_Q",
     "KDA_PRE_L2NORM_K", "KDA_PRE_BETA_SIGMOID", "KDA_PRE_NEG_EIGVAL", "KDA_STATE_KV", "KDA_STATE_VK",
 ]

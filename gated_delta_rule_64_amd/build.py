@@ -15,6 +15,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
+# measurement helper for the benchmark (a matrix-core loop), built beside the library
+CEILING_LIB = os.path.join(PKG, "libkda_ceiling.so")
+CEILING_SOURCE = "ceiling.hip"
 SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_bwd.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
@@ -54,6 +57,13 @@ def build(verbose: bool = False, jobs: int = 3) -> str:
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
         subprocess.run(cmd, check=True)
         os.replace(out_tmp, LIB)
+        out_tmp = CEILING_LIB + ".tmp%d" % os.getpid()
+        # accumulators in VGPRs: the default AGPR form rotated the loop's accumulators
+        # through copies (and measured half the matrix-core rate)
+        cmd = [cc, *flags(), "-mllvm", "-amdgpu-mfma-vgpr-form", "-x", "hip", "-shared",
+               os.path.join(CSRC, CEILING_SOURCE), "-o", out_tmp]
+        _wait((CEILING_SOURCE, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        os.replace(out_tmp, CEILING_LIB)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
     return LIB

@@ -190,8 +190,9 @@ int chunk_bwd_impl(const kda::ChunkBwdArgs& a0, const float* g, int chunk_size) 
     if (rc != KDA_OK) return rc;
     if ((long long)a.B * a.T > 0 && (!a.dout || !a.dq || !a.dk || !a.dv || !a.dg || !a.dbeta))
         return fail(KDA_ERR_NULL, "do, dq, dk, dv, dg and dbeta must be non-NULL");
-    if (!aligned16(a.dht))
-        return fail(KDA_ERR_SHAPE, "dht must be 16-byte aligned");
+    if (!aligned16(a.dht) || !aligned16(a.dout) || !aligned16(a.dq) || !aligned16(a.dk) ||
+        !aligned16(a.dg) || !aligned16(a.dbeta))
+        return fail(KDA_ERR_SHAPE, "dht, do, dq, dk, dg and dbeta must be 16-byte aligned");
     if (chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64, got %d", chunk_size);
     if (a.K != 64 && a.K != 128)
@@ -218,6 +219,16 @@ int chunk_bwd_impl(const kda::ChunkBwdArgs& a0, const float* g, int chunk_size) 
 }
 
 }  // namespace
+
+namespace kda {
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+}  // namespace kda
 
 extern "C" {
 
@@ -254,8 +265,9 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
         return fail(KDA_ERR_NULL, "dA_log must be non-NULL with a raw gate");
     if (gate != KDA_GATE_LOG2 && dt_bias && nonempty && !ddt_bias)
         return fail(KDA_ERR_NULL, "ddt_bias must be non-NULL when dt_bias is given");
-    if (!aligned16(dht))
-        return fail(KDA_ERR_SHAPE, "dht must be 16-byte aligned");
+    if (!aligned16(dht) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dg) || !aligned16(dbeta) || !aligned16(dA_log) || !aligned16(ddt_bias))
+        return fail(KDA_ERR_SHAPE, "dht, do, dq, dk, dg, dbeta, dA_log and ddt_bias must be 16-byte aligned");
     if (chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64, got %d", chunk_size);
     if (K != 64 && K != 128)

@@ -9,6 +9,10 @@
 
 namespace kda {
 
+// Records `fmt` as the thread's kda_last_error() reason and returns `code` (the C ABI
+// layer's error path, shared with the entry points that live in other files).
+int set_error(int code, const char* fmt, ...);
+
 // How the loads obtain the per-token log2 decay (the public kda_gate values).
 enum GateMode {
     GATE_LOG2 = KDA_GATE_LOG2,           // g: fp32 per-token log2 decay, as given

@@ -343,3 +343,82 @@ def test_bench_record_bytes_match_the_library_layout(lib, K, V):
     # the library pads each record to 256 bytes; the bench counts the bytes it holds
     assert rec == (bench.record_bytes(K, V, 2) + 255) // 256 * 256
     assert rec - bench.record_bytes(K, V, 2) < 256
+
+
+def test_bwd_rejects_misaligned_gradient_buffers(lib):
+    # every buffer the backward kernels read or write with vector accesses
+    for name in ("do", "dq", "dk", "dg", "db"):
+        assert _bwd(lib, **{name: FAKE + 4}) == -2, name
+        assert b"16-byte aligned" in lib.kda_last_error()
+
+
+def test_binding_checks_caller_buffers():
+    """Buffers the caller passes in (out, final_state, intermediate states, workspace,
+    dev_status) must fit the problem exactly: the C ABI cannot see their sizes."""
+    import torch
+    from gated_delta_rule_64_amd import _lib
+    dev = torch.device("cuda:0")   # never touched: the shape and dtype checks come first
+    q = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16)
+    v = torch.zeros(1, 64, 4, 128, dtype=torch.bfloat16)
+    N, HV, K, V = 1, 4, 128, 128
+    ok_out = torch.zeros_like(v)
+    # o: v's shape in q's dtype
+    with pytest.raises(ValueError, match="out"):
+        _lib._fwd_outputs(q, v, N, HV, K, V, dev, torch.zeros(1, 64, 4, 64, dtype=torch.bfloat16), None, False)
+    with pytest.raises(TypeError, match="out"):
+        _lib._fwd_outputs(q, v, N, HV, K, V, dev, torch.zeros(1, 64, 4, 128), None, False)
+    # final state: fp32 [N, HV, K, V], or the transposed layout when asked for
+    with pytest.raises(ValueError, match="final_state"):
+        _lib._fwd_outputs(q, v, N, HV, K, V, dev, ok_out, torch.zeros(N, HV, V, K + 1), True)
+    with pytest.raises(TypeError, match="final_state"):
+        _lib._fwd_outputs(q, v, N, HV, K, V, dev, ok_out, torch.zeros(N, HV, K, V, dtype=torch.float64), True)
+    with pytest.raises(ValueError, match="final_state"):
+        _lib._fwd_outputs(q, v, N, HV, K, V, dev, ok_out, torch.zeros(N, HV, K, V), True,
+                          state_shape=(N, HV, V, K + 1))
+    # intermediate states, dev_status
+    with pytest.raises(ValueError, match="intermediate_states"):
+        _lib._check_buffers(dev, [("intermediate_states", torch.zeros(63, HV, K, V), (64, HV, K, V), torch.float32)])
+    with pytest.raises(TypeError, match="dev_status"):
+        _lib._check_buffers(dev, [], dev_status=torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(TypeError, match="dev_status"):
+        _lib._check_buffers(dev, [], dev_status=torch.zeros(0, dtype=torch.int32))
+    # host tensors are refused once shapes and dtypes pass
+    with pytest.raises(ValueError, match="workspace"):
+        _lib._check_buffers(dev, [], workspace=torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="dev_status"):
+        _lib._check_buffers(dev, [], dev_status=torch.zeros(1, dtype=torch.int32))
+
+
+def test_binding_input_table_messages():
+    """Each input is checked against its layout and named in the error."""
+    import torch
+    from gated_delta_rule_64_amd import kda_chunk_fwd, kda_recurrent_fwd_ex
+    bf = torch.bfloat16
+    q = torch.zeros(1, 64, 2, 128, dtype=bf)
+    v = torch.zeros(1, 64, 4, 128, dtype=bf)
+    g = torch.zeros(1, 64, 4, 128)
+    b = torch.zeros(1, 64, 4, dtype=bf)
+    with pytest.raises(ValueError, match="^k:"):
+        kda_chunk_fwd(q, torch.zeros(1, 64, 2, 64, dtype=bf), v, g, b)
+    with pytest.raises(TypeError, match="^v:"):
+        kda_chunk_fwd(q, q, v.float(), g, b)
+    with pytest.raises(ValueError, match="^g:"):
+        kda_chunk_fwd(q, q, v, torch.zeros(1, 64, 2, 128), b)
+    with pytest.raises(TypeError, match="^g:"):
+        kda_chunk_fwd(q, q, v, g.to(bf), b)
+    with pytest.raises(ValueError, match="^beta:"):
+        kda_chunk_fwd(q, q, v, g, torch.zeros(1, 64, 2, dtype=bf))
+    with pytest.raises(ValueError, match="^initial_state:"):
+        kda_chunk_fwd(q, q, v, g, b, torch.zeros(1, 4, 128, 64))
+    with pytest.raises(TypeError, match="^cu_seqlens:"):
+        kda_chunk_fwd(q, q, v, g, b, None, torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(ValueError, match="B must be 1"):
+        kda_chunk_fwd(q.expand(2, -1, -1, -1), q.expand(2, -1, -1, -1), v.expand(2, -1, -1, -1),
+                      g.expand(2, -1, -1, -1), b.expand(2, -1, -1), None, torch.zeros(2, dtype=torch.int32))
+    # the transposed decode layout checks the initial state as [N, HV, V, K]
+    vv = torch.zeros(1, 64, 4, 64, dtype=bf)
+    with pytest.raises(ValueError, match="^initial_state:"):
+        kda_recurrent_fwd_ex(q, q, vv, g, b, torch.zeros(1, 4, 128, 64), state_layout="vk")
+    # all shapes right: then the host tensors are refused
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda_recurrent_fwd_ex(q, q, vv, g, b, torch.zeros(1, 4, 64, 128), state_layout="vk")

@@ -109,23 +109,62 @@ def test_chunk_varlen_full():
     assert tail.numel() > 0 and torch.isnan(tail).all(), "rows past the last offset must stay untouched"
 
 
-def test_recurrent_decode_full_sampled():
+def _decode_vs_oracle_batched(d, o, ht, batch=512):
+    """Every (sequence, head) pair of a one-token decode against the oracle, run on
+    batches of sequences so host memory stays bounded (the fp64 states of all 4096
+    sequences would take 17 GB). The bound is the workload's: 2e-2 x RMS over all pairs."""
+    from tests.util import half_ulp_bf16
+    N = d["cu_seqlens"].numel() - 1
+    worst_o = worst_s = 0.0
+    ss_o = ss_s = 0.0
+    n_o = n_s = 0
+    for a in range(0, N, batch):
+        idx = torch.arange(a, min(N, a + batch), device=DEV)
+        sub = dict(q=d["q"][0, idx].unsqueeze(1), k=d["k"][0, idx].unsqueeze(1),
+                   v=d["v"][0, idx].unsqueeze(1), g=d["g"][0, idx].unsqueeze(1),
+                   beta=d["beta"][0, idx].unsqueeze(1), initial_state=d["initial_state"][idx],
+                   cu_seqlens=None)
+        o_ref, ht_ref = oracle_of(sub)
+        go = to64(o[0, idx].unsqueeze(1))
+        assert np.isfinite(go).all()
+        worst_o = max(worst_o, float((np.abs(go - o_ref) - half_ulp_bf16(o_ref)).max()))
+        gs = to64(ht[idx])
+        worst_s = max(worst_s, float(np.abs(gs - ht_ref).max()))
+        ss_o += float((o_ref ** 2).sum()); n_o += o_ref.size
+        ss_s += float((ht_ref ** 2).sum()); n_s += ht_ref.size
+        del sub, o_ref, ht_ref, go, gs
+    bound_o = 2e-2 * (ss_o / n_o) ** 0.5
+    bound_s = 2e-2 * (ss_s / n_s) ** 0.5
+    log(f"  o: max err beyond output rounding {worst_o:.3e}, bound {bound_o:.3e}, "
+        f"ratio {worst_o / bound_o:.3f}  ({n_o} values)")
+    log(f"  final_state: max err {worst_s:.3e}, bound {bound_s:.3e}, ratio {worst_s / bound_s:.3f}")
+    assert worst_o <= bound_o and worst_s <= bound_s
+
+
+def test_recurrent_decode_full():
     """The decode workload at full size (4096 sequences x 32 heads: a flat grid of
-    262,144 waves), checked against the oracle on 96 sampled sequences (all heads)."""
+    262,144 waves): every (sequence, head) pair against the oracle, and bitwise
+    determinism of two runs."""
     d = inputs.make("dec", device=DEV)
-    log("[dec recurrent] N=4096 HV=32 K=V=128, 1 token each, fp32 states")
+    log("[dec recurrent] N=4096 HV=32 K=V=128, 1 token each, fp32 states; all pairs vs the oracle")
     o, ht = run("recurrent", d)
     o2, ht2 = run("recurrent", d)
     assert torch.equal(o, o2) and torch.equal(ht, ht2), "decode must be deterministic"
-    rng = np.random.default_rng(0)
-    sample = np.sort(rng.choice(4096, size=96, replace=False))
-    idx = torch.as_tensor(sample, device=DEV)
-    sub = dict(q=d["q"][0, idx].unsqueeze(1), k=d["k"][0, idx].unsqueeze(1), v=d["v"][0, idx].unsqueeze(1),
-               g=d["g"][0, idx].unsqueeze(1), beta=d["beta"][0, idx].unsqueeze(1),
-               initial_state=d["initial_state"][idx], cu_seqlens=None)
-    o_ref, ht_ref = oracle_of(sub)
-    check("o (sampled)", o[0, idx].unsqueeze(1), o_ref, torch.bfloat16)
-    check("final_state (sampled)", ht[idx], ht_ref, torch.bfloat16)
+    del o2, ht2
+    _decode_vs_oracle_batched(d, o, ht)
+
+
+def test_retrieval_identity_decode_full():
+    """beta = 1 and q = k give o = scale * v whatever the state, for every one of the
+    131,072 (sequence, head) pairs of the decode workload: an indexing check of the flat
+    grid at full size with no oracle run."""
+    d = inputs.make("dec", device=DEV)
+    d["q"] = d["k"]
+    d["beta"] = torch.ones_like(d["beta"])
+    log("[dec retrieval identity] N=4096 HV=32 K=V=128, beta = 1, q = k")
+    o, ht = run("recurrent", d)
+    want = to64(d["v"]) * 128 ** -0.5
+    check("o vs scale*v (all pairs)", o, want, torch.bfloat16)
 
 
 # ------------------------------------------------------------------------------------
@@ -240,6 +279,38 @@ def test_invalid_cu_seqlens_flagged_not_faulting(path):
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     run(path, d, dev_status=status)
     assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("path", ["chunk", "recurrent", "chunk_bwd"])
+def test_debug_mode_raises_on_bad_offsets(path):
+    """debug=True waits for the call and raises KdaDeviceCheckError when the device-side
+    offset check fires (a fresh status word when the caller gives none); well-formed
+    offsets pass, and without debug the same malformed call returns normally."""
+    import gated_delta_rule_64_amd as kda
+    T = 300
+    d = small(1, T, 2, 2, 128, 128, torch.bfloat16, seed=4)
+    d["initial_state"] = torch.randn(3, 2, 128, 128, generator=torch.Generator().manual_seed(3)).to(DEV) * 0.05
+    do = torch.randn(1, T, 2, 128, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+
+    def call(cu, **kw):
+        args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+        if path == "chunk_bwd":
+            return kda.kda_chunk_bwd(*args, do, d["initial_state"], cu, **kw)
+        fn = kda.kda_chunk_fwd if path == "chunk" else kda.kda_recurrent_fwd
+        return fn(*args, d["initial_state"], cu, output_final_state=True, **kw)
+
+    bad = torch.tensor([0, 100, 50, 200], dtype=torch.int32, device=DEV)
+    good = torch.tensor([0, 100, 150, 300], dtype=torch.int32, device=DEV)
+    with pytest.raises(kda.KdaDeviceCheckError) as e:
+        call(bad, debug=True)
+    assert e.value.status & kda.KDA_DEV_BAD_CU_SEQLENS and isinstance(e.value, kda.KdaError)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    with pytest.raises(kda.KdaDeviceCheckError):
+        call(bad, debug=True, dev_status=status)
+    assert int(status.item()) & kda.KDA_DEV_BAD_CU_SEQLENS
+    call(good, debug=True)
+    call(bad)                 # no debug: no exception, nothing synchronised
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("path", ["chunk", "recurrent"])
