@@ -18,8 +18,11 @@ Entry points (same names as the C ABI):
   kda_chunk_bwd_ex(...)                      the same through the fused input options
                                              (raw gate -> dA_log, ddt_bias; q/k norm; beta sigmoid)
   kda_chunk_fwd_workspace_bytes(...)         workspace size queries (also _bwd_)
+  kda_chunk_fwd_noalloc(...)                 kda_chunk_fwd with no allocation at all: the
+                                             intermediates live in a per-GPU scratch array
+                                             (problems up to kda_noalloc_scratch_bytes())
   kda_last_error()                           reason for the last failure
-Every entry point takes ``debug=True``: wait for the call
+Every entry point takes ``debug=True`` (except the allocation-free one): wait for the call
 and raise KdaDeviceCheckError when a device-side check flagged the inputs.
 """
 from __future__ import annotations
@@ -45,8 +48,10 @@ from ._lib import (  # noqa: F401
     kda_chunk_fwd,
     kda_chunk_fwd_ex,
     kda_chunk_fwd_gated,
+    kda_chunk_fwd_noalloc,
     kda_chunk_fwd_workspace_bytes,
     kda_last_error,
+    kda_noalloc_scratch_bytes,
     kda_recurrent_fwd,
     kda_recurrent_fwd_ex,
     library_path,
@@ -56,7 +61,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "kda_chunk_fwd", "kda_chunk_bwd", "kda_chunk_bwd_ex", "kda_chunk_bwd_workspace_bytes", "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_recurrent_fwd",
     "kda_recurrent_fwd_ex", "kda_chunk_fwd_workspace_bytes",
-    "kda_last_error", "KdaError", "KdaDeviceCheckError", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
+    "kda_last_error", "KdaError", "KdaDeviceCheckError", "kda_chunk_fwd_noalloc",
+    "kda_noalloc_scratch_bytes", "KDA_BF16", "KDA_F32", "KDA_DEV_BAD_CU_SEQLENS", "load_library",
     "library_path", "KDA_GATE_LOG2", "KDA_GATE_RAW_F32", "KDA_GATE_RAW_BF16", "KDA_PRE_L2NORM_Q",
     "KDA_PRE_L2NORM_K", "KDA_PRE_BETA_SIGMOID", "KDA_PRE_NEG_EIGVAL", "KDA_STATE_KV", "KDA_STATE_VK",
 ]

@@ -88,6 +88,12 @@ def load_library():
         lib.kda_last_error.argtypes = []
         lib.kda_abi_version.restype = i32
         lib.kda_abi_version.argtypes = []
+        lib.kda_chunk_fwd_noalloc.restype = i32
+        lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                              i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                              vp, vp]
+        lib.kda_noalloc_scratch_bytes.restype = sz
+        lib.kda_noalloc_scratch_bytes.argtypes = []
         _lib = lib
         return lib
 
@@ -286,6 +292,34 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
         raise KdaError(rc, lib.kda_last_error().decode())
     _debug_raise(debug, dev_status, dev)
     return out, final_state
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                          output_final_state=False, scale=None, *, out, final_state=None,
+                          dev_status=None):
+    """``kda_chunk_fwd`` through the library's entry point that allocates nothing: the
+    caller passes ``out`` (and ``final_state`` when requested); the per-chunk
+    intermediates live in the library's per-device scratch array, so problems needing
+    more than ``kda_noalloc_scratch_bytes()`` bytes are rejected, and calls that
+    overlap on one GPU race on it."""
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens)
+    if out is None or (output_final_state and final_state is None):
+        raise ValueError("kda_chunk_fwd_noalloc allocates nothing: pass out (and final_state)")
+    out, final_state = _fwd_outputs(q, v, N, HV, K, V, dev, out, final_state, output_final_state)
+    _check_buffers(dev, [], dev_status=dev_status)
+    rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(initial_state), _ptr(cu_seqlens), N, _ptr(out),
+                                   _ptr(final_state), B, T, H, HV, K, V, qkv, bdt,
+                                   float(scale or 0.0), 64, _ptr(dev_status), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    return out, final_state
+
+
+def kda_noalloc_scratch_bytes() -> int:
+    """Bytes of the per-device scratch array behind ``kda_chunk_fwd_noalloc``."""
+    return int(load_library().kda_noalloc_scratch_bytes())
 
 
 def kda_chunk_fwd_gated(q, k, v, g_raw, beta, A_log, dt_bias=None, lower_bound=None,

@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "libkda.so")
 # measurement helper for the benchmark (a matrix-core loop), built beside the library
 CEILING_LIB = os.path.join(PKG, "libkda_ceiling.so")
 CEILING_SOURCE = "ceiling.hip"
-SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_bwd.hip",
+           "kda_noalloc.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 

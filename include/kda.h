@@ -308,12 +308,36 @@ int kda_recurrent_fwd_ex(const void* q, const void* k, const void* v, const void
                          int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
                          float scale, int32_t* dev_status, hipStream_t stream);
 
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments,
+ * results and errors minus the workspace. The per-chunk intermediates go to a scratch
+ * array of KDA_NOALLOC_SCRATCH_MB MiB that the library's code object holds in device
+ * memory, one copy per GPU, kept until the process ends. Nothing is allocated or freed.
+ *   - Problems whose kda_chunk_fwd_workspace_bytes() exceeds kda_noalloc_scratch_bytes()
+ *     are rejected with KDA_ERR_WORKSPACE before anything is enqueued (e.g. at K = V =
+ *     128 in bf16 about 500 (value head, 64-token chunk) pairs fit).
+ *   - Every call on one GPU shares that GPU's array and leaves its intermediates there:
+ *     calls that may overlap on one GPU (other streams, other host threads) race and
+ *     must be serialised by the caller.
+ *   - The first call on each GPU looks the array's address up (with that GPU current).
+ */
+#define KDA_NOALLOC_SCRATCH_MB 64
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                          const void* beta, const float* initial_state,
+                          const int32_t* cu_seqlens, int N, void* o, float* final_state, int B,
+                          int T, int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
+                          float scale, int chunk_size, int32_t* dev_status, hipStream_t stream);
+
+/* Bytes of the scratch array behind kda_chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_MB MiB). */
+size_t kda_noalloc_scratch_bytes(void);
+
 /* Reason for the last non-KDA_OK return on this thread ("" if none). */
 const char* kda_last_error(void);
 
 /* ABI version of this header (bumped on any signature change or added entry point);
  * the library returns the KDA_ABI_VERSION it was built with. */
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 int kda_abi_version(void);
 
 #ifdef __cplusplus

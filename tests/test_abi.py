@@ -352,6 +352,35 @@ def test_bwd_rejects_misaligned_gradient_buffers(lib):
         assert b"16-byte aligned" in lib.kda_last_error()
 
 
+def _noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, N=1, o=FAKE, ht=None,
+             B=1, T=64, H=2, HV=2, K=128, V=128, qd=1, bd=1, scale=0.0, cs=64, st=None,
+             stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"],
+                                     a["N"], a["o"], a["ht"], a["B"], a["T"], a["H"], a["HV"],
+                                     a["K"], a["V"], a["qd"], a["bd"], a["scale"], a["cs"],
+                                     a["st"], a["stream"])
+
+
+def test_noalloc_scratch_limit(lib):
+    """The allocation-free entry point holds KDA_NOALLOC_SCRATCH_MB MiB per GPU; a problem
+    whose intermediates exceed it is rejected on the host before any GPU call."""
+    cap = lib.kda_noalloc_scratch_bytes()
+    assert cap == _header_int("KDA_NOALLOC_SCRATCH_MB") << 20
+    # the long-context problem (538 MB of records) is far beyond it
+    assert _noalloc(lib, T=8192, H=16, HV=32) == -5
+    assert b"allocation-free" in lib.kda_last_error()
+    # the largest dense T at H=2 HV=8 that fits, and the next chunk that does not
+    fits = [T for T in range(64, 1 << 16, 64)
+            if lib.kda_chunk_fwd_workspace_bytes(1, T, 2, 8, 128, 128, 1, 0, 1) <= cap]
+    assert _noalloc(lib, T=fits[-1] + 64, HV=8) == -5
+    # argument errors inside the limit are the forward's own (checked before any GPU call)
+    assert _noalloc(lib, q=None) == -1
+    assert _noalloc(lib, cs=32) == -4
+    assert _noalloc(lib, cu=FAKE, N=0, T=0) == 0
+
+
 def test_binding_checks_caller_buffers():
     """Buffers the caller passes in (out, final_state, intermediate states, workspace,
     dev_status) must fit the problem exactly: the C ABI cannot see their sizes."""
