@@ -52,6 +52,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+LEGS = ["headline", "c2", "gated", "backward", "decode", "varlen"]
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak
 
@@ -230,8 +231,9 @@ def main():
     ap.add_argument("--preheat-s", type=float, default=1.0,
                     help="seconds of back-to-back headline forwards before the warm-up steps")
     ap.add_argument("--decode-steps", type=int, default=10)
-    ap.add_argument("--only", choices=["headline"], default=None,
-                    help="run the headline leg alone (for profiling its kernels)")
+    ap.add_argument("--only", choices=LEGS, default=None,
+                    help="run one leg alone (for profiling its kernels); the headline leg "
+                         "always runs first unless another leg is named")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain elementwise kernel that reads and writes 1 GiB "
@@ -282,6 +284,9 @@ def main():
                 raise RuntimeError(lib.kda_last_error().decode())
         return call
 
+    def want(leg):
+        return args.only is None or args.only == leg
+
     # ---------------- headline: c3 ----------------
     w = inputs.WORKLOADS["c3"]
     d = inputs.make(w, device=dev)
@@ -292,6 +297,18 @@ def main():
     out = torch.empty_like(d["v"])
     call = timed_call(d, out, ws, ws_bytes, B, T, H, HV, K, V, N)
 
+    # the method's bytes: inputs read once, o written once (SURVEY's 1,282 B per
+    # token-head at GVA 2); which kernel moves which share of them; and what the records
+    # between the two kernels add by design
+    q_b = 2 * B * T * H * K * 2                 # q, k
+    v_b = B * T * HV * V * 2
+    g_b = B * T * HV * K * 4
+    beta_b = B * T * HV * 2
+    o_b = B * T * HV * V * 2
+    method_bytes = q_b + v_b + g_b + beta_b + o_b
+    in_bytes = method_bytes - o_b
+    tokens = B * T
+
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -301,6 +318,8 @@ def main():
         del src, dst
     # pre-heat: the forward back to back for a fixed wall time, so the timed steps run at
     # the clocks a busy GPU holds (a cold start ran both kernels ~17% slower)
+    if not want("headline"):
+        args.preheat_s = min(args.preheat_s, 0.2)
     t_end = time.time() + max(0.0, args.preheat_s)
     n_pre = 0
     while True:
@@ -313,258 +332,254 @@ def main():
     for _ in range(args.warmup):
         call(None)
     torch.cuda.synchronize()
-    whole, (seg_intra, seg_scan) = timed_flushed(call, steps, hip, sptr, flush, nev=1)
-    st = stats(whole)
-    ms_per_step = st["median"]
-    tokens = B * T
-    tok_s = tokens / (ms_per_step * 1e-3)
-    intra_ms = sum(seg_intra) / steps
-    scan_ms = sum(seg_scan) / steps
-    fwd_ms = intra_ms + scan_ms
-    b2b_ms = back_to_back(lambda: call(None), steps, hip, sptr)
+    result = {"leg": args.only, "note": "a single leg for profiling its kernels; no headline figures in this run"}
+    if want("headline"):
+        whole, (seg_intra, seg_scan) = timed_flushed(call, steps, hip, sptr, flush, nev=1)
+        st = stats(whole)
+        ms_per_step = st["median"]
+        tok_s = tokens / (ms_per_step * 1e-3)
+        intra_ms = sum(seg_intra) / steps
+        scan_ms = sum(seg_scan) / steps
+        fwd_ms = intra_ms + scan_ms
+        b2b_ms = back_to_back(lambda: call(None), steps, hip, sptr)
 
-    # the method's bytes: inputs read once, o written once (SURVEY's 1,282 B per
-    # token-head at GVA 2); which kernel moves which share of them; and what the records
-    # between the two kernels add by design
-    q_b = 2 * B * T * H * K * 2                 # q, k
-    v_b = B * T * HV * V * 2
-    g_b = B * T * HV * K * 4
-    beta_b = B * T * HV * 2
-    o_b = B * T * HV * V * 2
-    method_bytes = q_b + v_b + g_b + beta_b + o_b
-    in_bytes = method_bytes - o_b
-    flops_exact = 141013.0 * B * T * HV
-    flops_dense = 180224.0 * B * T * HV
-    nchunks = B * ((T + 63) // 64)
-    rec = record_bytes(K, V, 2) * nchunks * HV
-    counters = traffic_from_profiles()
-    traffic = None
-    if counters and "intra" in counters and "scan" in counters:
-        traffic = counters["intra"] + counters["scan"]
-    achieved = method_bytes / (fwd_ms * 1e-3) / 1e9
-    roofline = {
-        "bound": "hbm", "kernel": "chunk forward: Stage 1+2 kernel + scan kernel (one call)",
-        "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-        "traffic": traffic, "algorithmic_bytes": method_bytes, "avg_launch_ms": fwd_ms,
-        "dominant": "scan" if scan_ms >= intra_ms else "intra",
-        "kernels": {
-            "intra": {"avg_ms": intra_ms, "method_bytes": in_bytes,
-                      "method_GBs": in_bytes / (intra_ms * 1e-3) / 1e9,
-                      "design_bytes": in_bytes + rec,
-                      "counter_bytes": counters.get("intra") if counters else None},
-            "scan": {"avg_ms": scan_ms, "method_bytes": o_b,
-                     "method_GBs": o_b / (scan_ms * 1e-3) / 1e9,
-                     "design_bytes": rec + o_b,
-                     "counter_bytes": counters.get("scan") if counters else None},
-        },
-        "record_bytes_per_call": rec,
-    }
-    peak_dev = device_peak_tflops(hip, 0)
-    ceil = mfma_ceiling(hip, sptr, dev)
-    tflops_exact = flops_exact / (ms_per_step * 1e-3) / 1e12
-    path = {
-        "hbm_floor_bytes": method_bytes, "hbm_floor_us": method_bytes / HBM_PEAK_GBS / 1e3,
-        "achieved_GBs": method_bytes / (ms_per_step * 1e-3) / 1e9,
-        "hbm_frac": method_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "tflops_exact": tflops_exact,
-        "mfma_frac_exact_flops": tflops_exact / BF16_PEAK_TFLOPS,
-        "mfma_frac_dense_tile_flops": flops_dense / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        "mfma_frac_exact_of_measured_ceiling": tflops_exact / ceil["tflops"] if ceil else None,
-    }
-    result = {
-        "metric": "KDA fwd tokens/s + % bf16 MFMA peak at T=8192; decode state GB/s % HBM",
-        "value": tok_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=log2(sigmoid(N(2,1))) >= -5, beta=sigmoid(N(0,1)))",
-        "config": {"workload": "chunk_kda fwd B=1 T=8192 H=16 HV=32 K=V=128 bf16, h0=None, no final state",
-                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "timing": {"per_step": "512 MB write before each step (outside its events); value at the median step",
-                   "preheat_s": args.preheat_s, "preheat_steps": n_pre},
-        "steps_ms": st,
-        "back_to_back": {"ms_per_step": b2b_ms, "tokens_per_s": tokens / (b2b_ms * 1e-3)},
-        "roofline": roofline,
-        "path": path,
-        "ceilings": {"mfma_bf16_measured": ceil,
-                     "mfma_bf16_device": peak_dev,
-                     "mfma_bf16_published_tflops": BF16_PEAK_TFLOPS,
-                     "hbm_published_GBs": HBM_PEAK_GBS},
-    }
+        flops_exact = 141013.0 * B * T * HV
+        flops_dense = 180224.0 * B * T * HV
+        nchunks = B * ((T + 63) // 64)
+        rec = record_bytes(K, V, 2) * nchunks * HV
+        counters = traffic_from_profiles()
+        traffic = None
+        if counters and "intra" in counters and "scan" in counters:
+            traffic = counters["intra"] + counters["scan"]
+        achieved = method_bytes / (fwd_ms * 1e-3) / 1e9
+        roofline = {
+            "bound": "hbm", "kernel": "chunk forward: Stage 1+2 kernel + scan kernel (one call)",
+            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic, "algorithmic_bytes": method_bytes, "avg_launch_ms": fwd_ms,
+            "dominant": "scan" if scan_ms >= intra_ms else "intra",
+            "kernels": {
+                "intra": {"avg_ms": intra_ms, "method_bytes": in_bytes,
+                          "method_GBs": in_bytes / (intra_ms * 1e-3) / 1e9,
+                          "design_bytes": in_bytes + rec,
+                          "counter_bytes": counters.get("intra") if counters else None},
+                "scan": {"avg_ms": scan_ms, "method_bytes": o_b,
+                         "method_GBs": o_b / (scan_ms * 1e-3) / 1e9,
+                         "design_bytes": rec + o_b,
+                         "counter_bytes": counters.get("scan") if counters else None},
+            },
+            "record_bytes_per_call": rec,
+        }
+        peak_dev = device_peak_tflops(hip, 0)
+        ceil = mfma_ceiling(hip, sptr, dev)
+        tflops_exact = flops_exact / (ms_per_step * 1e-3) / 1e12
+        path = {
+            "hbm_floor_bytes": method_bytes, "hbm_floor_us": method_bytes / HBM_PEAK_GBS / 1e3,
+            "achieved_GBs": method_bytes / (ms_per_step * 1e-3) / 1e9,
+            "hbm_frac": method_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tflops_exact": tflops_exact,
+            "mfma_frac_exact_flops": tflops_exact / BF16_PEAK_TFLOPS,
+            "mfma_frac_dense_tile_flops": flops_dense / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "mfma_frac_exact_of_measured_ceiling": tflops_exact / ceil["tflops"] if ceil else None,
+        }
+        result = {
+            "metric": "KDA fwd tokens/s + % bf16 MFMA peak at T=8192; decode state GB/s % HBM",
+            "value": tok_s,
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms_per_step,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=log2(sigmoid(N(2,1))) >= -5, beta=sigmoid(N(0,1)))",
+            "config": {"workload": "chunk_kda fwd B=1 T=8192 H=16 HV=32 K=V=128 bf16, h0=None, no final state",
+                       "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+            "timing": {"per_step": "512 MB write before each step (outside its events); value at the median step",
+                       "preheat_s": args.preheat_s, "preheat_steps": n_pre},
+            "steps_ms": st,
+            "back_to_back": {"ms_per_step": b2b_ms, "tokens_per_s": tokens / (b2b_ms * 1e-3)},
+            "roofline": roofline,
+            "path": path,
+            "ceilings": {"mfma_bf16_measured": ceil,
+                         "mfma_bf16_device": peak_dev,
+                         "mfma_bf16_published_tflops": BF16_PEAK_TFLOPS,
+                         "hbm_published_GBs": HBM_PEAK_GBS},
+        }
     if args.only == "headline":
         print(json.dumps(result), flush=True)
         return
 
     # ---------------- c2: B=2 T=4096 H=HV=16, states in and out ----------------
-    w2 = inputs.WORKLOADS["c2"]
-    d2 = inputs.make(w2, device=dev)
-    ws2_bytes = kda.kda_chunk_fwd_workspace_bytes(w2.B, w2.T, w2.H, w2.HV, w2.K, w2.V, w2.B, 0, kda.KDA_BF16)
-    ws2 = torch.empty(ws2_bytes, dtype=torch.uint8, device=dev)
-    out2 = torch.empty_like(d2["v"])
-    fs2 = torch.empty_like(d2["initial_state"])
-    call2 = timed_call(d2, out2, ws2, ws2_bytes, w2.B, w2.T, w2.H, w2.HV, w2.K, w2.V, w2.B, final=fs2)
-    for _ in range(args.warmup):
-        call2(None)
-    whole2, (i2, s2) = timed_flushed(call2, steps, hip, sptr, flush, nev=1)
-    st2 = stats(whole2)
-    c2_bytes = (2 * w2.B * w2.T * w2.H * w2.K * 2 + 2 * w2.B * w2.T * w2.HV * w2.V * 2
-                + w2.B * w2.T * w2.HV * w2.K * 4 + w2.B * w2.T * w2.HV * 2
-                + 2 * d2["initial_state"].numel() * 4)
-    c2_fwd = (sum(i2) + sum(s2)) / steps
-    result["c2"] = {"workload": "chunk_kda fwd B=2 T=4096 H=HV=16 K=V=128 bf16, h0 N(0,0.05), final state",
-                    "ms_per_step": st2["median"], "steps_ms": st2,
-                    "tokens_per_s": w2.B * w2.T / (st2["median"] * 1e-3),
-                    "kernels_ms": {"intra": sum(i2) / steps, "scan": sum(s2) / steps},
-                    "algorithmic_bytes": c2_bytes, "hbm_floor_us": c2_bytes / HBM_PEAK_GBS / 1e3,
-                    "hbm_frac": c2_bytes / (c2_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    del d2, ws2, out2, fs2
+    if want("c2"):
+        w2 = inputs.WORKLOADS["c2"]
+        d2 = inputs.make(w2, device=dev)
+        ws2_bytes = kda.kda_chunk_fwd_workspace_bytes(w2.B, w2.T, w2.H, w2.HV, w2.K, w2.V, w2.B, 0, kda.KDA_BF16)
+        ws2 = torch.empty(ws2_bytes, dtype=torch.uint8, device=dev)
+        out2 = torch.empty_like(d2["v"])
+        fs2 = torch.empty_like(d2["initial_state"])
+        call2 = timed_call(d2, out2, ws2, ws2_bytes, w2.B, w2.T, w2.H, w2.HV, w2.K, w2.V, w2.B, final=fs2)
+        for _ in range(args.warmup):
+            call2(None)
+        whole2, (i2, s2) = timed_flushed(call2, steps, hip, sptr, flush, nev=1)
+        st2 = stats(whole2)
+        c2_bytes = (2 * w2.B * w2.T * w2.H * w2.K * 2 + 2 * w2.B * w2.T * w2.HV * w2.V * 2
+                    + w2.B * w2.T * w2.HV * w2.K * 4 + w2.B * w2.T * w2.HV * 2
+                    + 2 * d2["initial_state"].numel() * 4)
+        c2_fwd = (sum(i2) + sum(s2)) / steps
+        result["c2"] = {"workload": "chunk_kda fwd B=2 T=4096 H=HV=16 K=V=128 bf16, h0 N(0,0.05), final state",
+                        "ms_per_step": st2["median"], "steps_ms": st2,
+                        "tokens_per_s": w2.B * w2.T / (st2["median"] * 1e-3),
+                        "kernels_ms": {"intra": sum(i2) / steps, "scan": sum(s2) / steps},
+                        "algorithmic_bytes": c2_bytes, "hbm_floor_us": c2_bytes / HBM_PEAK_GBS / 1e3,
+                        "hbm_frac": c2_bytes / (c2_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del d2, ws2, out2, fs2
 
     # ---------------- the headline with the fused input options ----------------
-    # the gate activation fused into Stage 1: raw bf16 gate input, A_log = log(U[1, 2])
-    # per head, dt_bias N(0, 0.5^2)
-    gen = torch.Generator().manual_seed(w.seed + 100)
-    g_raw = torch.randn(B, T, HV, K, generator=gen).mul(2.0).to(torch.bfloat16).to(dev)
-    A_log = torch.rand(HV, generator=gen).add(1.0).log().to(dev)
-    dt_bias = torch.randn(HV * K, generator=gen).mul(0.5).to(dev)
+    if want("gated"):
+        # the gate activation fused into Stage 1: raw bf16 gate input, A_log = log(U[1, 2])
+        # per head, dt_bias N(0, 0.5^2)
+        gen = torch.Generator().manual_seed(w.seed + 100)
+        g_raw = torch.randn(B, T, HV, K, generator=gen).mul(2.0).to(torch.bfloat16).to(dev)
+        A_log = torch.rand(HV, generator=gen).add(1.0).log().to(dev)
+        dt_bias = torch.randn(HV * K, generator=gen).mul(0.5).to(dev)
 
-    def gcall():
-        kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], g_raw, d["beta"], A_log, dt_bias, None,
-                                None, None, out=out, workspace=ws)
-    for _ in range(args.warmup):
-        gcall()
-    gated_ms = back_to_back(gcall, steps, hip, sptr)
+        def gcall():
+            kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], g_raw, d["beta"], A_log, dt_bias, None,
+                                    None, None, out=out, workspace=ws)
+        for _ in range(args.warmup):
+            gcall()
+        gated_ms = back_to_back(gcall, steps, hip, sptr)
 
-    # every input fusion at once: the fused gate as above, q / k L2-normalised in the
-    # loads and beta = 2 sigmoid(beta) (the recipe's q, k and beta serve as the raw inputs)
-    def fcall():
-        kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], g_raw, d["beta"], use_gate_in_kernel=True,
-                             A_log=A_log, dt_bias=dt_bias, use_qk_l2norm_in_kernel=True,
-                             use_beta_sigmoid_in_kernel=True, allow_neg_eigval=True, out=out,
-                             workspace=ws)
-    for _ in range(args.warmup):
-        fcall()
-    fused_ms = back_to_back(fcall, steps, hip, sptr)
-    del g_raw, A_log, dt_bias
-    result["gated"] = {"workload": "the headline forward with the gate activation fused into Stage 1 (raw bf16 gate input, A_log, dt_bias)",
-                       "ms_per_step": gated_ms, "tokens_per_s": tokens / (gated_ms * 1e-3)}
-    result["fused_inputs"] = {"workload": "the headline forward with every input fusion: raw bf16 gate + A_log + dt_bias, q/k L2 norm in the loads, beta = 2 sigmoid(beta)",
-                              "ms_per_step": fused_ms, "tokens_per_s": tokens / (fused_ms * 1e-3)}
+        # every input fusion at once: the fused gate as above, q / k L2-normalised in the
+        # loads and beta = 2 sigmoid(beta) (the recipe's q, k and beta serve as the raw inputs)
+        def fcall():
+            kda.kda_chunk_fwd_ex(d["q"], d["k"], d["v"], g_raw, d["beta"], use_gate_in_kernel=True,
+                                 A_log=A_log, dt_bias=dt_bias, use_qk_l2norm_in_kernel=True,
+                                 use_beta_sigmoid_in_kernel=True, allow_neg_eigval=True, out=out,
+                                 workspace=ws)
+        for _ in range(args.warmup):
+            fcall()
+        fused_ms = back_to_back(fcall, steps, hip, sptr)
+        del g_raw, A_log, dt_bias
+        result["gated"] = {"workload": "the headline forward with the gate activation fused into Stage 1 (raw bf16 gate input, A_log, dt_bias)",
+                           "ms_per_step": gated_ms, "tokens_per_s": tokens / (gated_ms * 1e-3)}
+        result["fused_inputs"] = {"workload": "the headline forward with every input fusion: raw bf16 gate + A_log + dt_bias, q/k L2 norm in the loads, beta = 2 sigmoid(beta)",
+                                  "ms_per_step": fused_ms, "tokens_per_s": tokens / (fused_ms * 1e-3)}
 
     # ---------------- backward of the headline forward ----------------
-    # do ~ N(0, 1) bf16, no final-state gradient, no initial state (so no dh0); outputs
-    # and workspace allocated up front
-    bws_bytes = kda.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, 0, kda.KDA_BF16)
-    bws = torch.empty(bws_bytes, dtype=torch.uint8, device=dev)
-    gen = torch.Generator().manual_seed(w.seed + 200)
-    dout = torch.randn(tuple(d["v"].shape), generator=gen).to(torch.bfloat16).to(dev)
-    gq, gk, gv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
-    gg = torch.empty(B, T, HV, K, dtype=torch.float32, device=dev)
-    gb = torch.empty_like(d["beta"])
+    if want("backward"):
+        # do ~ N(0, 1) bf16, no final-state gradient, no initial state (so no dh0); outputs
+        # and workspace allocated up front
+        bws_bytes = kda.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, 0, kda.KDA_BF16)
+        bws = torch.empty(bws_bytes, dtype=torch.uint8, device=dev)
+        gen = torch.Generator().manual_seed(w.seed + 200)
+        dout = torch.randn(tuple(d["v"].shape), generator=gen).to(torch.bfloat16).to(dev)
+        gq, gk, gv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        gg = torch.empty(B, T, HV, K, dtype=torch.float32, device=dev)
+        gb = torch.empty_like(d["beta"])
 
-    def bcall():
-        rc = lib.kda_chunk_bwd(
-            vp(d["q"].data_ptr()), vp(d["k"].data_ptr()), vp(d["v"].data_ptr()),
-            vp(d["g"].data_ptr()), vp(d["beta"].data_ptr()), None, None, N,
-            vp(dout.data_ptr()), None, vp(gq.data_ptr()), vp(gk.data_ptr()), vp(gv.data_ptr()),
-            vp(gg.data_ptr()), vp(gb.data_ptr()), None, B, T, H, HV, K, V, kda.KDA_BF16,
-            kda.KDA_BF16, 0.0, 64, vp(bws.data_ptr()), bws_bytes, None, sptr)
-        if rc != 0:
-            raise RuntimeError(lib.kda_last_error().decode())
-    bsteps = max(1, steps // 4)
-    for _ in range(2):
-        bcall()
-    bwd_ms = back_to_back(bcall, bsteps, hip, sptr)
-    # inputs, do and every gradient once (SURVEY's floor for the backward)
-    bwd_bytes = 2 * (q_b + v_b + g_b + beta_b) + o_b
-    result["backward"] = {"workload": "kda_chunk_bwd of the headline forward (dq, dk, dv, dg, dbeta; do ~ N(0,1) bf16, no dht)",
-                          "ms_per_step": bwd_ms, "tokens_per_s": tokens / (bwd_ms * 1e-3), "steps": bsteps,
-                          "algorithmic_bytes": bwd_bytes,
-                          "hbm_frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    del bws, dout, gq, gk, gv, gg, gb
+        def bcall():
+            rc = lib.kda_chunk_bwd(
+                vp(d["q"].data_ptr()), vp(d["k"].data_ptr()), vp(d["v"].data_ptr()),
+                vp(d["g"].data_ptr()), vp(d["beta"].data_ptr()), None, None, N,
+                vp(dout.data_ptr()), None, vp(gq.data_ptr()), vp(gk.data_ptr()), vp(gv.data_ptr()),
+                vp(gg.data_ptr()), vp(gb.data_ptr()), None, B, T, H, HV, K, V, kda.KDA_BF16,
+                kda.KDA_BF16, 0.0, 64, vp(bws.data_ptr()), bws_bytes, None, sptr)
+            if rc != 0:
+                raise RuntimeError(lib.kda_last_error().decode())
+        bsteps = max(1, steps // 4)
+        for _ in range(2):
+            bcall()
+        bwd_ms = back_to_back(bcall, bsteps, hip, sptr)
+        # inputs, do and every gradient once (SURVEY's floor for the backward)
+        bwd_bytes = 2 * (q_b + v_b + g_b + beta_b) + o_b
+        result["backward"] = {"workload": "kda_chunk_bwd of the headline forward (dq, dk, dv, dg, dbeta; do ~ N(0,1) bf16, no dht)",
+                              "ms_per_step": bwd_ms, "tokens_per_s": tokens / (bwd_ms * 1e-3), "steps": bsteps,
+                              "algorithmic_bytes": bwd_bytes,
+                              "hbm_frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del bws, dout, gq, gk, gv, gg, gb
 
     # ---------------- decode: 4096 sequences x 32 heads ----------------
     del ws, out
-    dd = inputs.make("dec", device=dev)
-    dout = torch.empty_like(dd["v"])
-    dstate = torch.empty_like(dd["initial_state"])
+    if want("decode"):
+        dd = inputs.make("dec", device=dev)
+        dout = torch.empty_like(dd["v"])
+        dstate = torch.empty_like(dd["initial_state"])
 
-    def dcall():
-        kda.kda_recurrent_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["initial_state"],
-                              dd["cu_seqlens"], output_final_state=True, out=dout, final_state=dstate)
-    for _ in range(2):
-        dcall()
-    dec_ms = back_to_back(dcall, args.decode_steps, hip, sptr)
+        def dcall():
+            kda.kda_recurrent_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["initial_state"],
+                                  dd["cu_seqlens"], output_final_state=True, out=dout, final_state=dstate)
+        for _ in range(2):
+            dcall()
+        dec_ms = back_to_back(dcall, args.decode_steps, hip, sptr)
 
-    # the same decode with q / k normalisation and beta = sigmoid(beta) fused into the loads
-    def dfcall():
-        kda.kda_recurrent_fwd_ex(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["initial_state"],
-                                 dd["cu_seqlens"], output_final_state=True, out=dout,
-                                 final_state=dstate, use_qk_l2norm_in_kernel=True,
-                                 use_beta_sigmoid_in_kernel=True)
-    for _ in range(2):
-        dfcall()
-    dec_fused_ms = back_to_back(dfcall, args.decode_steps, hip, sptr)
-    # the same decode with the states stored transposed ([V][K] per head)
-    h0_vk = dd["initial_state"].transpose(-1, -2).contiguous()
-    dstate_vk = torch.empty_like(h0_vk)
+        # the same decode with q / k normalisation and beta = sigmoid(beta) fused into the loads
+        def dfcall():
+            kda.kda_recurrent_fwd_ex(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["initial_state"],
+                                     dd["cu_seqlens"], output_final_state=True, out=dout,
+                                     final_state=dstate, use_qk_l2norm_in_kernel=True,
+                                     use_beta_sigmoid_in_kernel=True)
+        for _ in range(2):
+            dfcall()
+        dec_fused_ms = back_to_back(dfcall, args.decode_steps, hip, sptr)
+        # the same decode with the states stored transposed ([V][K] per head)
+        h0_vk = dd["initial_state"].transpose(-1, -2).contiguous()
+        dstate_vk = torch.empty_like(h0_vk)
 
-    def dvcall():
-        kda.kda_recurrent_fwd_ex(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], h0_vk,
-                                 dd["cu_seqlens"], output_final_state=True, out=dout,
-                                 final_state=dstate_vk, state_layout="vk")
-    for _ in range(2):
-        dvcall()
-    dec_vk_ms = back_to_back(dvcall, args.decode_steps, hip, sptr)
-    del h0_vk, dstate_vk
-    # what a plain elementwise stream achieves over the same bytes: torch.neg reading the
-    # 8.6 GB state tensor and writing 8.6 GB (the practical HBM ceiling the decode is read against)
-    for _ in range(2):
-        torch.neg(dd["initial_state"], out=dstate)
-    stream_ms = back_to_back(lambda: torch.neg(dd["initial_state"], out=dstate), args.decode_steps, hip, sptr)
-    stream_gbs = 2 * dd["initial_state"].numel() * 4 / (stream_ms * 1e-3) / 1e9
-    dec_bytes = (2 * dd["initial_state"].numel() * 4 + 3 * dd["q"].numel() * 2 + dd["g"].numel() * 4
-                 + dd["beta"].numel() * 2 + dout.numel() * 2)
-    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
-    del dd, dout, dstate
-    result["decode"] = {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
-                        "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
-                        "bytes": dec_bytes, "fused_inputs_ms": dec_fused_ms, "state_vk_ms": dec_vk_ms,
-                        "stream_ceiling": {"kernel": "torch.neg over the fp32 state tensor (8.59 GB read + 8.59 GB written)",
-                                           "ms": stream_ms, "GB_s": stream_gbs,
-                                           "decode_frac": dec_gbs / stream_gbs}}
-    result["ceilings"]["hbm_stream_GBs"] = stream_gbs
+        def dvcall():
+            kda.kda_recurrent_fwd_ex(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], h0_vk,
+                                     dd["cu_seqlens"], output_final_state=True, out=dout,
+                                     final_state=dstate_vk, state_layout="vk")
+        for _ in range(2):
+            dvcall()
+        dec_vk_ms = back_to_back(dvcall, args.decode_steps, hip, sptr)
+        del h0_vk, dstate_vk
+        # what a plain elementwise stream achieves over the same bytes: torch.neg reading the
+        # 8.6 GB state tensor and writing 8.6 GB (the practical HBM ceiling the decode is read against)
+        for _ in range(2):
+            torch.neg(dd["initial_state"], out=dstate)
+        stream_ms = back_to_back(lambda: torch.neg(dd["initial_state"], out=dstate), args.decode_steps, hip, sptr)
+        stream_gbs = 2 * dd["initial_state"].numel() * 4 / (stream_ms * 1e-3) / 1e9
+        dec_bytes = (2 * dd["initial_state"].numel() * 4 + 3 * dd["q"].numel() * 2 + dd["g"].numel() * 4
+                     + dd["beta"].numel() * 2 + dout.numel() * 2)
+        dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+        del dd, dout, dstate
+        result["decode"] = {"workload": "recurrent decode N=4096 HV=32 K=V=128, 1 bf16 token each, fp32 states in+out",
+                            "ms": dec_ms, "GB_s": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
+                            "bytes": dec_bytes, "fused_inputs_ms": dec_fused_ms, "state_vk_ms": dec_vk_ms,
+                            "stream_ceiling": {"kernel": "torch.neg over the fp32 state tensor (8.59 GB read + 8.59 GB written)",
+                                               "ms": stream_ms, "GB_s": stream_gbs,
+                                               "decode_frac": dec_gbs / stream_gbs}}
+        result.setdefault("ceilings", {})["hbm_stream_GBs"] = stream_gbs
 
     # ---------------- packed varlen forward ----------------
-    # 64 slots, lengths U[1, 1024] with 4 empty slots (~31k tokens), H=HV=16, K=V=128
-    # bf16, fp32 initial and final states
-    wv = inputs.WORKLOADS["vl"]
-    dv_ = inputs.make(wv, device=dev)
-    Bv, Tv = dv_["q"].shape[0], dv_["q"].shape[1]
-    Nv = dv_["cu_seqlens"].numel() - 1
-    vtokens = int(dv_["cu_seqlens"][-1].item())
-    vws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(Bv, Tv, wv.H, wv.HV, wv.K, wv.V, Nv, 1, kda.KDA_BF16),
-                      dtype=torch.uint8, device=dev)
-    vout = torch.empty_like(dv_["v"])
-    vstate = torch.empty_like(dv_["initial_state"])
+    if want("varlen"):
+        # 64 slots, lengths U[1, 1024] with 4 empty slots (~31k tokens), H=HV=16, K=V=128
+        # bf16, fp32 initial and final states
+        wv = inputs.WORKLOADS["vl"]
+        dv_ = inputs.make(wv, device=dev)
+        Bv, Tv = dv_["q"].shape[0], dv_["q"].shape[1]
+        Nv = dv_["cu_seqlens"].numel() - 1
+        vtokens = int(dv_["cu_seqlens"][-1].item())
+        vws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(Bv, Tv, wv.H, wv.HV, wv.K, wv.V, Nv, 1, kda.KDA_BF16),
+                          dtype=torch.uint8, device=dev)
+        vout = torch.empty_like(dv_["v"])
+        vstate = torch.empty_like(dv_["initial_state"])
 
-    def vcall():
-        kda.kda_chunk_fwd(dv_["q"], dv_["k"], dv_["v"], dv_["g"], dv_["beta"], dv_["initial_state"],
-                          dv_["cu_seqlens"], output_final_state=True, out=vout, final_state=vstate,
-                          workspace=vws)
-    for _ in range(args.warmup):
-        vcall()
-    var_ms = back_to_back(vcall, steps, hip, sptr)
-    del dv_, vws, vout, vstate
-    result["varlen"] = {"workload": f"chunk_kda fwd packed: 64 slots (4 empty), {vtokens} tokens, H=HV=16 K=V=128 bf16, fp32 initial and final states",
-                        "ms_per_step": var_ms, "tokens_per_s": vtokens / (var_ms * 1e-3)}
+        def vcall():
+            kda.kda_chunk_fwd(dv_["q"], dv_["k"], dv_["v"], dv_["g"], dv_["beta"], dv_["initial_state"],
+                              dv_["cu_seqlens"], output_final_state=True, out=vout, final_state=vstate,
+                              workspace=vws)
+        for _ in range(args.warmup):
+            vcall()
+        var_ms = back_to_back(vcall, steps, hip, sptr)
+        del dv_, vws, vout, vstate
+        result["varlen"] = {"workload": f"chunk_kda fwd packed: 64 slots (4 empty), {vtokens} tokens, H=HV=16 K=V=128 bf16, fp32 initial and final states",
+                            "ms_per_step": var_ms, "tokens_per_s": vtokens / (var_ms * 1e-3)}
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and want("headline"):
         import oracle
         host = inputs.make(w)   # same recipe on the host (the oracle's cost does not depend on values)
         threads = oracle.default_threads()
