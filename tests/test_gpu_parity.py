@@ -109,6 +109,28 @@ def test_chunk_varlen_full():
     assert tail.numel() > 0 and torch.isnan(tail).all(), "rows past the last offset must stay untouched"
 
 
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (128, 64)])
+def test_chunk_packed_many_chains(K, V):
+    """Packed batches with many more chains than CUs (the wide-slice scan instance where
+    V = 128): 160 slots of 1..200 tokens (10 empty) x HV = 8 heads with GVA 2, initial
+    states, a NaN sentinel tail; every slot against the oracle, empty slots bitwise."""
+    w = inputs.Workload("many", 1, 0, 4, 8, K, V, torch.bfloat16, torch.bfloat16, 41, -5.0, 0.05, True,
+                        n_slots=160, len_lo=1, len_hi=200, n_empty=10)
+    d = to_device(inputs.make(w))
+    cu = d["cu_seqlens"].cpu()
+    T = d["q"].shape[1]
+    log(f"[packed many chains] 160 slots, {int(cu[-1])} tokens, H=4 HV=8 K={K} V={V} bf16")
+    o, ht = run("chunk", d, out=torch.full_like(d["v"], float("nan")))
+    o_ref, ht_ref = oracle_of(d)
+    m = valid_rows(cu, T)
+    check("o", o[:, m], o_ref[:, m], torch.bfloat16)
+    check("final_state", ht, ht_ref, torch.bfloat16)
+    lens = (cu[1:] - cu[:-1]).numpy()
+    for n in np.nonzero(lens == 0)[0]:
+        assert torch.equal(ht[n], d["initial_state"][n]), f"empty slot {n} state must pass through bitwise"
+    assert torch.isnan(o[:, ~m]).all(), "rows past the last offset must stay untouched"
+
+
 def _decode_vs_oracle_batched(d, o, ht, batch=512):
     """Every (sequence, head) pair of a one-token decode against the oracle, run on
     batches of sequences so host memory stays bounded (the fp64 states of all 4096
