@@ -239,9 +239,13 @@ struct BwdParams {
 template <int K>
 __device__ __forceinline__ void l2norm_rows_lds(float* X, int ld, int t) {
     if (t >= 0 && t < C) {
+        // two passes over LDS, neither fully unrolled: fully unrolled, the pair kept the
+        // whole row in registers between them (and spilled)
         float ss = 0.f;
+#pragma unroll 8
         for (int d = 0; d < K; ++d) ss = fmaf(X[t * ld + d], X[t * ld + d], ss);
         const float rn = l2norm_rstd(ss);
+#pragma unroll 8
         for (int d = 0; d < K; ++d) X[t * ld + d] *= rn;
     }
 }
@@ -1048,6 +1052,7 @@ __global__ __launch_bounds__(SB_THREADS, 4) void bwd_state_bf16_kernel(BwdParams
         stage_split<C, VC>(dvC + vb, V, dvH, dvLo, tid);
         __syncthreads();
         if (tid < K)
+#pragma unroll 8   // (fully unrolled, its 128 LDS reads were all held in registers)
             for (int vv = 0; vv < VC; ++vv) {
                 const int e = tid * SB_LD + vv;
                 dgacc = fmaf((float)dhH[e] + (float)dhLo[e], (float)hH[e] + (float)hLo[e], dgacc);
