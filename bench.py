@@ -94,11 +94,18 @@ class Events:
             self.hip.hipEventDestroy(e)
 
 
-def record_bytes(K, V, elem):
-    """Algorithmic bytes of one Stage 2 record (see the workspace layout in the library):
-    w, qg(hi, lo), kg^T(hi, lo), Aqk(hi, lo) in the operand type, u and 2^G in fp32."""
-    ns = 2 if elem == 2 else 1
-    return 64 * K * elem + ns * (2 * 64 * K * elem + 64 * 64 * elem) + 64 * V * 4 + K * 4
+def record_bytes(K, V, elem, compact=False):
+    """Bytes of one Stage 2 record (see the workspace layout in the library): w, qg, kg^T,
+    Aqk in the operand type, u and 2^G in fp32; on the bf16 path the residuals of qg,
+    kg^T and Aqk as a second bf16 tile each, or, in compact records (the layout of
+    launches with many chains), as fp8 tiles (a byte per value) with one 32-bit scale
+    word per 16-row band and lane."""
+    b = 64 * K * elem + 2 * 64 * K * elem + 64 * 64 * elem + 64 * V * 4 + K * 4
+    if elem == 2 and compact:
+        b += 2 * 64 * K + 64 * 64 + (64 // 16 + K // 16 + 64 // 16) * 64 * 4
+    elif elem == 2:
+        b += 2 * 64 * K * elem + 64 * 64 * elem
+    return b
 
 
 def source_hash():

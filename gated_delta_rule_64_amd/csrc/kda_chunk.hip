@@ -136,6 +136,7 @@ struct IntraParams {
     const int2* table;        // chunk table: (first row, rows)
     char* rec;                // record base
     size_t rec_bytes, off_w, off_u, off_qg, off_kgT, off_aqk, off_eg;
+    size_t off_qg_lo, off_kgT_lo, off_aqk_lo, off_qg_sc, off_kgT_sc, off_aqk_sc;
     int T, H, HV, NT, NCmax;
     int dense;                // no offsets: chunk c is chunk c % NT of sequence c / NT
     float scale;
@@ -750,8 +751,9 @@ __device__ __forceinline__ float frag_row_rstd(const bf16x8 (&x)[NS]) {
     return l2norm_rstd(ss);
 }
 
-template <int K, int V, typename TB, bool CKPT>
+template <int K, int V, typename TB, bool CKPT, bool LO8>
 __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) {
+    static_assert(!(CKPT && LO8), "the backward's recompute keeps bf16 residual tiles");
     typedef __bf16 TW;
     constexpr int NKS = K / 32, NVS = V / 32;   // 32-column steps of q/k/g and of v
     typedef Tile<TW, C, C> TB64;                // T beta
@@ -809,6 +811,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
     TW* out_aqk = reinterpret_cast<TW*>(rec + p.off_aqk);
     float* out_u = reinterpret_cast<float*>(rec + p.off_u);
     float* out_eg = reinterpret_cast<float*>(rec + p.off_eg);
+    // compact records (LO8): residuals of qg, kg^T and Aqk as fp8 tiles
+    typedef Lo8Tile<C, K> LA8;                  // qg
+    typedef Lo8Tile<C, C> LQ8;                  // Aqk
+    typedef Lo8Tile<K, C> LG8;                  // kg^T
+    uint2* out_qg8 = reinterpret_cast<uint2*>(rec + p.off_qg_lo);
+    uint2* out_kg8 = reinterpret_cast<uint2*>(rec + p.off_kgT_lo);
+    uint2* out_aqk8 = reinterpret_cast<uint2*>(rec + p.off_aqk_lo);
+    uint8_t* out_qgs = reinterpret_cast<uint8_t*>(rec + p.off_qg_sc);
+    uint8_t* out_kgs = reinterpret_cast<uint8_t*>(rec + p.off_kgT_sc);
+    uint8_t* out_aqks = reinterpret_cast<uint8_t*>(rec + p.off_aqk_sc);
 
     // swizzled fp32 64 x 64: 16-byte chunk index XOR (row % 16)
     auto sw = [](int row, int col) { return row * C + ((((col >> 2) ^ (row & 15))) << 2) + (col & 3); };
@@ -1024,9 +1036,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
             xg[e] = kap_own[s][e] * kgv[e];
         }
         bf16x8 hi8, lo8;
-        split8(xq, hi8, lo8);
+        if constexpr (LO8) {
+            uint2 l8;
+            uint32_t sb;
+            split8_lo8(xq, hi8, l8, sb);
+            out_qg8[LA8::frag(w, s, lane)] = l8;
+            out_qgs[4 * LA8::scale(w, lane) + s] = (uint8_t)sb;
+        } else {
+            split8(xq, hi8, lo8);
+            *reinterpret_cast<bf16x8*>(out_qg + C * K + FA::frag(w, s, lane)) = lo8;
+        }
         *reinterpret_cast<bf16x8*>(out_qg + FA::frag(w, s, lane)) = hi8;
-        *reinterpret_cast<bf16x8*>(out_qg + C * K + FA::frag(w, s, lane)) = lo8;
         // (k 2^Gamma)^T: four consecutive rows of one column per lane
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -1038,23 +1058,31 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
         // kg^T in fragment order (rows = channels, contraction = rows of the chunk):
         // selection products give 4 consecutive rows per lane, the lane swaps 8
         split8(xg, hi8, lo8);
-#pragma unroll
+        // (with the fp8 encode, the unrolled pair made the kernel spill)
+#pragma unroll (LO8 ? 1 : 2)
         for (int part = 0; part < 2; ++part) {
             const bf16x8 a = part ? lo8 : hi8;
             const f32x4 x0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, eye_frag(lane, 0), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             const f32x4 x1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, eye_frag(lane, 1), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             float o8[8];
             acc_pair_to_frag(x0, x1, o8);
-            bf16x8 ov;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ov[e] = (__bf16)o8[e];
             // lanes lq 0-1 hold channel 32s + lr, lanes lq 2-3 channel 32s + 16 + lr; rows
             // 16w + 8(lq & 1) .. +7 of the chunk
             const int band = 2 * s + (lq >> 1);
             const int fl = lr + 16 * (2 * (w & 1) + (lq & 1));
-            *reinterpret_cast<bf16x8*>(out_kgT + part * K * C + FG::frag(band, w >> 1, fl)) = ov;
+            if (LO8 && part == 1) {   // the bf16 residual, re-rounded to fp8
+                uint32_t sb;
+                out_kg8[LG8::frag(band, w >> 1, fl)] = lo8_encode(o8, sb);
+                out_kgs[4 * LG8::scale(band, fl) + (w >> 1)] = (uint8_t)sb;
+            } else {
+                bf16x8 ov;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ov[e] = (__bf16)o8[e];
+                *reinterpret_cast<bf16x8*>(out_kgT + part * K * C + FG::frag(band, w >> 1, fl)) = ov;
+            }
         }
     }
+
     for (int t = tid; t < K / 4; t += NTHREADS)
         *reinterpret_cast<f32x4*>(out_eg + 4 * t) = *reinterpret_cast<const f32x4*>(table + TAB_EG * K + 4 * t);
 
@@ -1112,10 +1140,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
         float o8[8];
         acc_pair_to_frag(x, y, o8);
         bf16x8 hi8, lo8;
-        split8(o8, hi8, lo8);
+        if constexpr (LO8) {
+            uint2 l8;
+            uint32_t sb;
+            split8_lo8(o8, hi8, l8, sb);
+            out_aqk8[LQ8::frag(w, s, lane)] = l8;
+            out_aqks[4 * LQ8::scale(w, lane) + s] = (uint8_t)sb;
+        } else {
+            split8(o8, hi8, lo8);
+            *reinterpret_cast<bf16x8*>(out_aqk + C * C + FQ::frag(w, s, lane)) = lo8;
+        }
         *reinterpret_cast<bf16x8*>(out_aqk + FQ::frag(w, s, lane)) = hi8;
-        *reinterpret_cast<bf16x8*>(out_aqk + C * C + FQ::frag(w, s, lane)) = lo8;
     }
+
     // L rows of block w (beta_i, strictly lower) -> LDS
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
@@ -1273,6 +1310,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
 struct ScanParams {
     const char* rec;
     size_t rec_bytes, off_w, off_u, off_qg, off_kgT, off_aqk, off_eg;
+    size_t off_qg_lo, off_kgT_lo, off_aqk_lo, off_qg_sc, off_kgT_sc, off_aqk_sc;
+    int lo8;                 // compact records (fp8 residuals)
     const float* initial_state;
     float* final_state;
     void* o;
@@ -1609,88 +1648,125 @@ constexpr int ROW_PREFETCH = 2;     // row waves: chunks in flight
 constexpr int STATE_PREFETCH = 3;   // state waves: chunks in flight
 constexpr int SCAN_L2_AHEAD = 4;    // chunks ahead of the one being scanned that the L2 prefetch touches
 
-template <int K, int BV>
+// The residual halves of qg, Aqk and kg^T: a bf16 fragment (the backward's recompute
+// records) or the eight fp8 bytes of one (the forward's compact records), decoded with
+// the fragment's scale byte just before its product.
+template <bool LO8> struct LoFrag;
+template <> struct LoFrag<false> {
+    bf16x8 x;
+    __device__ __forceinline__ bf16x8 get(uint32_t) const { return x; }
+};
+template <> struct LoFrag<true> {
+    uint2 x;
+    __device__ __forceinline__ bf16x8 get(uint32_t sbyte) const { return lo8_decode(x, sbyte); }
+};
+
+template <int K, int BV, bool LO8>
 struct RowFrags {
     static constexpr int NKS = K / 32, NJS = C / 32, NNT = BV / 16;
     bf16x8 w[NKS];
-    bf16x8 q[2][NKS];      // qg hi, lo
-    bf16x8 a[2][NJS];      // Aqk hi, lo
+    bf16x8 q[NKS];         // qg hi
+    LoFrag<LO8> ql[NKS];   // qg lo
+    bf16x8 a[NJS];         // Aqk hi
+    LoFrag<LO8> al[NJS];   // Aqk lo
+    uint32_t qs, as;       // scale words of qg and Aqk lo (compact records)
     f32x4 u[NNT];
     int2 pos;              // (first row of the chunk, rows in it)
 };
 
-template <int K, int BV>
+template <int K, int BV, bool LO8>
 struct StateFrags {
     static constexpr int NDT = K / 64, NJS = C / 32;
-    bf16x8 g[NDT][2][NJS]; // kg^T hi, lo of the wave's state bands
-    f32x4 e[NDT];          // 2^G of those bands
+    bf16x8 g[NDT][NJS];        // kg^T hi of the wave's state bands
+    LoFrag<LO8> gl[NDT][NJS];  // kg^T lo
+    uint32_t gs[NDT];          // scale words of kg^T lo (compact records)
+    f32x4 e[NDT];              // 2^G of those bands
 };
 
 // Row operands are loaded in two parts, each as soon as the previous chunk's values of
 // those registers are dead: w, qg, u (used before the v' barrier) and Aqk, the chunk
 // position (used after it).
-template <int K, int BV>
-__device__ __forceinline__ void load_row_wqu(RowFrags<K, BV>& F, const char* rec, const ScanParams& p,
+template <int K, int BV, bool LO8>
+__device__ __forceinline__ void load_row_wqu(RowFrags<K, BV, LO8>& F, const char* rec, const ScanParams& p,
                                              int b, int lane, int v0) {
     typedef FragTile<__bf16, C, K> FA;
+    typedef Lo8Tile<C, K> LA8;
     const int lr = lane & 15, lq = lane >> 4;
     const __bf16* w = reinterpret_cast<const __bf16*>(rec + p.off_w);
     const __bf16* qg = reinterpret_cast<const __bf16*>(rec + p.off_qg);
     const float* u = reinterpret_cast<const float*>(rec + p.off_u);
 #pragma unroll
-    for (int kk = 0; kk < RowFrags<K, BV>::NKS; ++kk) {
+    for (int kk = 0; kk < RowFrags<K, BV, LO8>::NKS; ++kk) {
         F.w[kk] = *reinterpret_cast<const bf16x8*>(w + FA::frag(b, kk, lane));
-#pragma unroll
-        for (int sx = 0; sx < 2; ++sx)
-            F.q[sx][kk] = *reinterpret_cast<const bf16x8*>(qg + (size_t)sx * C * K + FA::frag(b, kk, lane));
+        F.q[kk] = *reinterpret_cast<const bf16x8*>(qg + FA::frag(b, kk, lane));
+        if constexpr (LO8)
+            F.ql[kk].x = reinterpret_cast<const uint2*>(rec + p.off_qg_lo)[LA8::frag(b, kk, lane)];
+        else
+            F.ql[kk].x = *reinterpret_cast<const bf16x8*>(qg + (size_t)C * K + FA::frag(b, kk, lane));
     }
+    if constexpr (LO8) F.qs = reinterpret_cast<const uint32_t*>(rec + p.off_qg_sc)[LA8::scale(b, lane)];
 #pragma unroll
-    for (int nt = 0; nt < RowFrags<K, BV>::NNT; ++nt)
+    for (int nt = 0; nt < RowFrags<K, BV, LO8>::NNT; ++nt)
         F.u[nt] = *reinterpret_cast<const f32x4*>(u + AccTile::quad(v0 + 16 * nt + lr, 16 * b + 4 * lq));
 }
 
 // i: the chunk's index within its sequence, whose rows are bos .. bos + slen - 1. The
 // position is formed from values loaded before the loop: a load here, into registers a
 // dense launch would fill by moves, makes the compiler wait for every load in flight.
-template <int K, int BV>
-__device__ __forceinline__ void load_row_a(RowFrags<K, BV>& F, const char* rec, const ScanParams& p,
+template <int K, int BV, bool LO8>
+__device__ __forceinline__ void load_row_a(RowFrags<K, BV, LO8>& F, const char* rec, const ScanParams& p,
                                            int bos, int slen, int i, int b, int lane) {
     typedef FragTile<__bf16, C, C> FQ;
+    typedef Lo8Tile<C, C> LQ8;
     F.pos = make_int2(bos + i * C, slen - i * C < C ? slen - i * C : C);
     const __bf16* aqk = reinterpret_cast<const __bf16*>(rec + p.off_aqk);
     // band b of the lower-triangular Aqk has nonzero columns only below 16b + 16
     const int njs = (16 * b + 16 + 31) / 32;
 #pragma unroll
-    for (int jj = 0; jj < RowFrags<K, BV>::NJS; ++jj)
-#pragma unroll
-        for (int sx = 0; sx < 2; ++sx)
-            F.a[sx][jj] = jj < njs ? *reinterpret_cast<const bf16x8*>(aqk + (size_t)sx * C * C + FQ::frag(b, jj, lane))
-                                   : bf16x8{};
+    for (int jj = 0; jj < RowFrags<K, BV, LO8>::NJS; ++jj) {
+        F.a[jj] = jj < njs ? *reinterpret_cast<const bf16x8*>(aqk + FQ::frag(b, jj, lane)) : bf16x8{};
+        if constexpr (LO8)
+            F.al[jj].x = jj < njs ? reinterpret_cast<const uint2*>(rec + p.off_aqk_lo)[LQ8::frag(b, jj, lane)]
+                                  : make_uint2(0u, 0u);
+        else
+            F.al[jj].x = jj < njs ? *reinterpret_cast<const bf16x8*>(aqk + (size_t)C * C + FQ::frag(b, jj, lane))
+                                  : bf16x8{};
+    }
+    if constexpr (LO8) F.as = reinterpret_cast<const uint32_t*>(rec + p.off_aqk_sc)[LQ8::scale(b, lane)];
 }
 
 // State operands in two parts: 2^G (used by the decay, before the v' barrier) and kg^T.
-template <int K, int BV>
-__device__ __forceinline__ void load_state_e(StateFrags<K, BV>& F, const char* rec, const ScanParams& p,
+template <int K, int BV, bool LO8>
+__device__ __forceinline__ void load_state_e(StateFrags<K, BV, LO8>& F, const char* rec, const ScanParams& p,
                                              int sw, int lane) {
     const int lq = lane >> 4;
     const float* eg = reinterpret_cast<const float*>(rec + p.off_eg);
 #pragma unroll
-    for (int a = 0; a < StateFrags<K, BV>::NDT; ++a)
+    for (int a = 0; a < StateFrags<K, BV, LO8>::NDT; ++a)
         F.e[a] = *reinterpret_cast<const f32x4*>(eg + 16 * (sw + 4 * a) + 4 * lq);
 }
 
-template <int K, int BV>
-__device__ __forceinline__ void load_state_g(StateFrags<K, BV>& F, const char* rec, const ScanParams& p,
+template <int K, int BV, bool LO8>
+__device__ __forceinline__ void load_state_g(StateFrags<K, BV, LO8>& F, const char* rec, const ScanParams& p,
                                              int sw, int lane) {
     typedef FragTile<__bf16, K, C> FG;
+    typedef Lo8Tile<K, C> LG8;
     const __bf16* kgT = reinterpret_cast<const __bf16*>(rec + p.off_kgT);
 #pragma unroll
-    for (int jj = 0; jj < StateFrags<K, BV>::NJS; ++jj)
+    for (int jj = 0; jj < StateFrags<K, BV, LO8>::NJS; ++jj)
 #pragma unroll
-        for (int a = 0; a < StateFrags<K, BV>::NDT; ++a)
+        for (int a = 0; a < StateFrags<K, BV, LO8>::NDT; ++a) {
+            F.g[a][jj] = *reinterpret_cast<const bf16x8*>(kgT + FG::frag(sw + 4 * a, jj, lane));
+            if constexpr (LO8)
+                F.gl[a][jj].x = reinterpret_cast<const uint2*>(rec + p.off_kgT_lo)[LG8::frag(sw + 4 * a, jj, lane)];
+            else
+                F.gl[a][jj].x = *reinterpret_cast<const bf16x8*>(kgT + (size_t)K * C + FG::frag(sw + 4 * a, jj, lane));
+        }
+    if constexpr (LO8) {
 #pragma unroll
-            for (int sx = 0; sx < 2; ++sx)
-                F.g[a][sx][jj] = *reinterpret_cast<const bf16x8*>(kgT + (size_t)sx * K * C + FG::frag(sw + 4 * a, jj, lane));
+        for (int a = 0; a < StateFrags<K, BV, LO8>::NDT; ++a)
+            F.gs[a] = reinterpret_cast<const uint32_t*>(rec + p.off_kgT_sc)[LG8::scale(sw + 4 * a, lane)];
+    }
 }
 
 template <int K, int V, int BV, bool CKPT>
@@ -1701,6 +1777,8 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
     typedef Tile<TW, BV, C> TV;      // v'^T [BV][64]
     typedef __attribute__((ext_vector_type(4))) TW vec4;
     constexpr int NKS = K / 32, NJS = C / 32, NDT = K / 64, NNT = BV / 16, NVT = V / BV;
+    // compact records (fp8 residuals) go with the 32-column slices (scan_slice_width)
+    constexpr bool LO8 = !CKPT && BV == 32;
 
     __shared__ __attribute__((aligned(16))) TW St[2][2][TS::ELEMS];   // [buffer][hi, lo]
     __shared__ __attribute__((aligned(16))) TW Vt[2][TV::ELEMS];      // [hi, lo]
@@ -1737,7 +1815,7 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
         const int b = wave;
         const int njs_b = (16 * b + 16 + 31) / 32;   // Aqk steps with nonzero columns
         __bf16* o = reinterpret_cast<__bf16*>(p.o);
-        RowFrags<K, BV> R0, R1;
+        RowFrags<K, BV, LO8> R0, R1;
         static_assert(ROW_PREFETCH == 2, "the row loop is unrolled for two buffers");
         // the sequence's rows (chunk c0 + i starts at row bos + i C; the schedule's table
         // holds exactly that for packed sequences)
@@ -1751,15 +1829,15 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                 bos = first.x;
                 slen = last.x + last.y - first.x;
             }
-            load_row_wqu<K, BV>(R0, record(c0), p, b, lane, v0);
-            load_row_a<K, BV>(R0, record(c0), p, bos, slen, 0, b, lane);
-            load_row_wqu<K, BV>(R1, record(c0 + 1), p, b, lane, v0);
-            load_row_a<K, BV>(R1, record(c0 + 1), p, bos, slen, clampc(c0 + 1) - c0, b, lane);
+            load_row_wqu<K, BV, LO8>(R0, record(c0), p, b, lane, v0);
+            load_row_a<K, BV, LO8>(R0, record(c0), p, bos, slen, 0, b, lane);
+            load_row_wqu<K, BV, LO8>(R1, record(c0 + 1), p, b, lane, v0);
+            load_row_a<K, BV, LO8>(R1, record(c0 + 1), p, bos, slen, clampc(c0 + 1) - c0, b, lane);
         }
         lds_barrier();   // initial S^T
         int cur = 0;
         // one chunk; F is refilled with chunk cn as its registers die
-        auto step = [&](RowFrags<K, BV>& F, int cn) {
+        auto step = [&](RowFrags<K, BV, LO8>& F, int cn) {
             const int c = cn - ROW_PREFETCH;   // the chunk F holds
             bf16x8 sb[NNT][2][NKS];
 #pragma unroll
@@ -1796,12 +1874,12 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                 oacc2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < NKS; ++kk) {
-                    oacc[nt] = M::mma(sb[nt][0][kk], F.q[0][kk], oacc[nt]);
-                    oacc2[nt] = M::mma(sb[nt][0][kk], F.q[1][kk], oacc2[nt]);
-                    oacc2[nt] = M::mma(sb[nt][1][kk], F.q[0][kk], oacc2[nt]);
+                    oacc[nt] = M::mma(sb[nt][0][kk], F.q[kk], oacc[nt]);
+                    oacc2[nt] = M::mma(sb[nt][0][kk], F.ql[kk].get(lo8_byte(F.qs, kk)), oacc2[nt]);
+                    oacc2[nt] = M::mma(sb[nt][1][kk], F.q[kk], oacc2[nt]);
                 }
             }
-            load_row_wqu<K, BV>(F, record(cn), p, b, lane, v0);
+            load_row_wqu<K, BV, LO8>(F, record(cn), p, b, lane, v0);
             lds_barrier();   // A: v' complete
             // o^T, second part: v'^T Aqk^T; lane (lq, lr) holds row 16b + lr, columns 16nt + 4lq ..
             const long long rs = F.pos.x;
@@ -1813,9 +1891,9 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                     if (jj < njs_b) {
                         const bf16x8 vh = TV::frag(Vt[0], 16 * nt + lr, jj * 32 + lq * 8);
                         const bf16x8 vl = TV::frag(Vt[1], 16 * nt + lr, jj * 32 + lq * 8);
-                        oacc[nt] = M::mma(vh, F.a[0][jj], oacc[nt]);
-                        oacc2[nt] = M::mma(vh, F.a[1][jj], oacc2[nt]);
-                        oacc2[nt] = M::mma(vl, F.a[0][jj], oacc2[nt]);
+                        oacc[nt] = M::mma(vh, F.a[jj], oacc[nt]);
+                        oacc2[nt] = M::mma(vh, F.al[jj].get(lo8_byte(F.as, jj)), oacc2[nt]);
+                        oacc2[nt] = M::mma(vl, F.a[jj], oacc2[nt]);
                     }
                 }
                 const int i = 16 * b + lr;
@@ -1826,7 +1904,7 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                     *reinterpret_cast<vec4*>(o + ((size_t)(rs + i) * p.HV + hv) * V + v0 + 16 * nt + 4 * lq) = ov;
                 }
             }
-            load_row_a<K, BV>(F, record(cn), p, bos, slen, clampc(cn) - c0, b, lane);
+            load_row_a<K, BV, LO8>(F, record(cn), p, bos, slen, clampc(cn) - c0, b, lane);
             lds_barrier();   // B: S_(c+1) complete
             cur ^= 1;
         };
@@ -1843,15 +1921,15 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
         const int sw = wave - 4;
         f32x4 S[NDT][NNT];
         const size_t sbase = ((size_t)n * p.HV + hv) * (size_t)K * V;
-        StateFrags<K, BV> G0, G1, G2;
+        StateFrags<K, BV, LO8> G0, G1, G2;
         static_assert(STATE_PREFETCH == 3, "the state loop is unrolled for three buffers");
         if (c0 < c1) {
-            load_state_e<K, BV>(G0, record(c0), p, sw, lane);
-            load_state_g<K, BV>(G0, record(c0), p, sw, lane);
-            load_state_e<K, BV>(G1, record(c0 + 1), p, sw, lane);
-            load_state_g<K, BV>(G1, record(c0 + 1), p, sw, lane);
-            load_state_e<K, BV>(G2, record(c0 + 2), p, sw, lane);
-            load_state_g<K, BV>(G2, record(c0 + 2), p, sw, lane);
+            load_state_e<K, BV, LO8>(G0, record(c0), p, sw, lane);
+            load_state_g<K, BV, LO8>(G0, record(c0), p, sw, lane);
+            load_state_e<K, BV, LO8>(G1, record(c0 + 1), p, sw, lane);
+            load_state_g<K, BV, LO8>(G1, record(c0 + 1), p, sw, lane);
+            load_state_e<K, BV, LO8>(G2, record(c0 + 2), p, sw, lane);
+            load_state_g<K, BV, LO8>(G2, record(c0 + 2), p, sw, lane);
         }
 #pragma unroll
         for (int a = 0; a < NDT; ++a)
@@ -1884,7 +1962,7 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
             if (li < nl) pf = *reinterpret_cast<const uint32_t*>(record(cn + SCAN_L2_AHEAD - STATE_PREFETCH) + (size_t)(l0 + li) * 128);
         };
         // one chunk; F is refilled with chunk cn as its registers die
-        auto step = [&](StateFrags<K, BV>& F, int cn, uint32_t& pf) {
+        auto step = [&](StateFrags<K, BV, LO8>& F, int cn, uint32_t& pf) {
             if constexpr (CKPT) {   // the state at the start of the chunk F holds
                 float* hb = p.h_out + ((size_t)hv * p.NCmax + (cn - STATE_PREFETCH)) * (size_t)K * V;
 #pragma unroll
@@ -1902,7 +1980,15 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                 for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) S[a][nt][r] *= F.e[a][r];
-            load_state_e<K, BV>(F, record(cn), p, sw, lane);
+            load_state_e<K, BV, LO8>(F, record(cn), p, sw, lane);
+            // compact records: kg^T residuals decoded in the wait for v' (off the update's path)
+            bf16x8 glo[NDT][NJS];
+            if constexpr (LO8) {
+#pragma unroll
+                for (int a = 0; a < NDT; ++a)
+#pragma unroll
+                    for (int jj = 0; jj < NJS; ++jj) glo[a][jj] = F.gl[a][jj].get(lo8_byte(F.gs[a], jj));
+            }
             lds_barrier();   // A: v' complete
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt) {
@@ -1917,16 +2003,16 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                     f32x4 acc = S[a][nt], acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int jj = 0; jj < NJS; ++jj) {
-                        acc = M::mma(F.g[a][0][jj], vh[jj], acc);
-                        acc2 = M::mma(F.g[a][1][jj], vh[jj], acc2);
-                        acc2 = M::mma(F.g[a][0][jj], vl[jj], acc2);
+                        acc = M::mma(F.g[a][jj], vh[jj], acc);
+                        acc2 = M::mma(LO8 ? glo[a][jj] : F.gl[a][jj].get(0), vh[jj], acc2);
+                        acc2 = M::mma(F.g[a][jj], vl[jj], acc2);
                     }
                     acc += acc2;
                     S[a][nt] = acc;
                     put4(St[cur ^ 1][0], St[cur ^ 1][1], TS::idx(16 * nt + lr, 16 * (sw + 4 * a) + 4 * lq), acc);
                 }
             }
-            load_state_g<K, BV>(F, record(cn), p, sw, lane);
+            load_state_g<K, BV, LO8>(F, record(cn), p, sw, lane);
             prefetch(pf, cn);
             lds_barrier();   // B: S_(c+1) complete
             cur ^= 1;
@@ -1999,6 +2085,8 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     ip.nchunks = nch; ip.table = table; ip.rec = recs;
     ip.rec_bytes = L.rec_bytes; ip.off_w = L.off_w; ip.off_u = L.off_u; ip.off_qg = L.off_qg;
     ip.off_kgT = L.off_kgT; ip.off_aqk = L.off_aqk; ip.off_eg = L.off_eg;
+    ip.off_qg_lo = L.off_qg_lo; ip.off_kgT_lo = L.off_kgT_lo; ip.off_aqk_lo = L.off_aqk_lo;
+    ip.off_qg_sc = L.off_qg_sc; ip.off_kgT_sc = L.off_kgT_sc; ip.off_aqk_sc = L.off_aqk_sc;
     ip.T = a.T; ip.H = a.H; ip.HV = a.HV; ip.NCmax = L.NCmax;
     ip.dense = dense;   // then NCmax = B * NT chunks, all present
     ip.NT = NT;
@@ -2010,10 +2098,13 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
         const bool ckpt = a.m_out != nullptr;
         if constexpr (sizeof(TIn) == 2) {
             if (ckpt)
-                hipLaunchKernelGGL((intra_bf16_kernel<K, V, TB, true>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
+                hipLaunchKernelGGL((intra_bf16_kernel<K, V, TB, true, false>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
+                                   a.stream, ip);
+            else if (L.lo8)
+                hipLaunchKernelGGL((intra_bf16_kernel<K, V, TB, false, true>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
                                    a.stream, ip);
             else
-                hipLaunchKernelGGL((intra_bf16_kernel<K, V, TB, false>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
+                hipLaunchKernelGGL((intra_bf16_kernel<K, V, TB, false, false>), dim3((unsigned)nintra), dim3(NTHREADS), 0,
                                    a.stream, ip);
         } else {
             if (ckpt)
@@ -2030,6 +2121,9 @@ hipError_t launch_kv(const ChunkArgs& a, const ChunkLayout& L) {
     ScanParams sp;
     sp.rec = recs; sp.rec_bytes = L.rec_bytes; sp.off_w = L.off_w; sp.off_u = L.off_u;
     sp.off_qg = L.off_qg; sp.off_kgT = L.off_kgT; sp.off_aqk = L.off_aqk; sp.off_eg = L.off_eg;
+    sp.off_qg_lo = L.off_qg_lo; sp.off_kgT_lo = L.off_kgT_lo; sp.off_aqk_lo = L.off_aqk_lo;
+    sp.off_qg_sc = L.off_qg_sc; sp.off_kgT_sc = L.off_kgT_sc; sp.off_aqk_sc = L.off_aqk_sc;
+    sp.lo8 = L.lo8;
     sp.initial_state = a.initial_state; sp.final_state = a.final_state; sp.o = a.o;
     sp.coff = coff; sp.cend = cend; sp.slot_ok = slot_ok; sp.table = table; sp.order = order;
     sp.N = a.N; sp.T = a.T; sp.HV = a.HV; sp.NT = NT; sp.NCmax = L.NCmax;
@@ -2048,13 +2142,12 @@ template <int K, int V, typename TIn>
 hipError_t launch_scan(const ChunkArgs& a, const ScanParams& sp) {
     const long long chains = (long long)a.N * a.HV;
     if (chains == 0) return hipSuccess;
-    // pick the slice width: enough blocks to cover the chip, wide slices when chains abound
-    // (the fp32 path keeps 16-column slices: its operand tiles take twice the LDS;
-    //  the bf16 path's hi/lo pairs cap it at 32)
-    int BV = 16;
-    if (sizeof(TIn) == 2 && chains * (V / 32) >= 512) BV = 32;
+    // the slice width: enough blocks to cover the chip, wide slices when chains abound
+    const int BV = scan_slice_width(chains, V, sizeof(TIn) == 2);
     const unsigned nscan = (unsigned)(chains * (V / BV));
     const bool ckpt = sp.h_out != nullptr;   // backward re-scan: checkpoints, no o
+    // the records' format was chosen with the same rule (chunk_layout)
+    if (sp.lo8 != (!ckpt && BV == 32)) return hipErrorInvalidValue;
     if constexpr (sizeof(TIn) == 2) {
         if (ckpt)
             hipLaunchKernelGGL((scan_bf16_kernel<K, V, 16, true>), dim3((unsigned)(chains * (V / 16))),
@@ -2083,7 +2176,7 @@ hipError_t launch_t(const ChunkArgs& a, const ChunkLayout& L) {
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 bool chunk_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qkv_dtype,
-                  ChunkLayout* out) {
+                  ChunkLayout* out, bool ckpt_records) {
     ChunkLayout L{};
     if (packed) {
         L.NCmax = T / C + N;
@@ -2092,13 +2185,27 @@ bool chunk_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qk
         N = B;
     }
     L.elem = qkv_dtype == KDA_BF16 ? 2 : 4;
-    // bf16 path: qg, kg^T and Aqk carry a second tile with their bf16 rounding residual
-    const size_t ns = qkv_dtype == KDA_BF16 ? 2 : 1;
+    // bf16 path: qg, kg^T and Aqk carry their rounding residual, as a second bf16 tile
+    // (the backward's recompute) or as an fp8 tile with scale words (the forward)
+    const bool bf16 = qkv_dtype == KDA_BF16;
+    L.lo8 = bf16 && !ckpt_records && scan_slice_width((long long)N * HV, V, true) == 32;
+    const size_t ns = bf16 && !L.lo8 ? 2 : 1;
     size_t off = 0;
     L.off_w = off;   off += (size_t)C * K * L.elem;
     L.off_qg = off;  off += ns * C * K * L.elem;
     L.off_kgT = off; off += ns * K * C * L.elem;
     L.off_aqk = off; off += ns * C * C * L.elem;
+    L.off_qg_lo = L.off_qg + (size_t)C * K * L.elem;
+    L.off_kgT_lo = L.off_kgT + (size_t)K * C * L.elem;
+    L.off_aqk_lo = L.off_aqk + (size_t)C * C * L.elem;
+    if (L.lo8) {
+        L.off_qg_lo = off;  off += (size_t)C * K;
+        L.off_kgT_lo = off; off += (size_t)K * C;
+        L.off_aqk_lo = off; off += (size_t)C * C;
+        L.off_qg_sc = off;  off += (size_t)(C / 16) * 64 * 4;
+        L.off_kgT_sc = off; off += (size_t)(K / 16) * 64 * 4;
+        L.off_aqk_sc = off; off += (size_t)(C / 16) * 64 * 4;
+    }
     L.off_u = off;   off += (size_t)C * V * 4;        // u^T [V][64], fp32 (used outside the MFMAs)
     L.off_eg = off;  off += (size_t)K * 4;
     L.rec_bytes = align256(off);

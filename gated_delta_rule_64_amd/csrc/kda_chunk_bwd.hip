@@ -1845,7 +1845,7 @@ hipError_t launch_bwd_ex_k(const ChunkBwdExArgs& x, const ChunkBwdExLayout& L) {
 bool chunk_bwd_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qkv_dtype,
                       ChunkBwdLayout* out) {
     ChunkBwdLayout L{};
-    if (!chunk_layout(B, T, HV, K, V, N, packed, qkv_dtype, &L.fwd)) return false;
+    if (!chunk_layout(B, T, HV, K, V, N, packed, qkv_dtype, &L.fwd, true)) return false;
     const size_t items = (size_t)HV * L.fwd.NCmax;
     const size_t rows = (size_t)B * T;
     size_t off = align256b(L.fwd.total);

@@ -127,6 +127,21 @@ template <typename TW, int R, int KC> struct FragTile {
     }
 };
 
+// The fp8 residual (lo8_encode) of a bf16 FragTile<__bf16, R, KC>: the eight bytes of
+// fragment lane (band b, step st, lane) at uint2 index frag(b, st, lane), in the same
+// order as the bf16 tile, and per (band, lane) one 32-bit word whose byte st is that
+// fragment's scale byte (at most four steps per band).
+template <int R, int KC> struct Lo8Tile {
+    static constexpr int NS = KC / 32, BANDS = R / 16;
+    static_assert(R % 16 == 0 && KC % 32 == 0 && NS <= 4, "whole bands, at most 4 steps");
+    static constexpr size_t LO_BYTES = (size_t)R * KC;
+    static constexpr size_t SC_BYTES = (size_t)BANDS * 64 * 4;
+    __device__ __forceinline__ static int frag(int b, int st, int lane) { return (b * NS + st) * 64 + lane; }
+    __device__ __forceinline__ static int scale(int b, int lane) { return b * 64 + lane; }
+};
+// scale byte st of a word
+__device__ __forceinline__ uint32_t lo8_byte(uint32_t word, int st) { return (word >> (8 * st)) & 0xFFu; }
+
 // Accumulator-order tile of fp32 values [R][64] read back as four consecutive rows of
 // one column: block (column tile ct = col/16, row band rb = row/16), lane
 // l = (col % 16) + 16 * ((row % 16) / 4) holds rows 16rb + 4(l/16) .. +3 of column
@@ -264,6 +279,50 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
         lo[e] = (__bf16)(x[e] - (float)hi[e]);
     }
 }
+// Rounding residuals in fp8 (OCP e4m3: 4 significant bits, largest finite value 448) with
+// one power-of-two scale per fragment lane: the lane's eight residuals r are stored as
+// e4m3(r 2^s), s set from their largest magnitude m so that m 2^s lies in [128, 256)
+// (nothing reaches 448, where the conversion would give NaN), and beside them the byte
+// 127 - s, which is the exponent field of the decoding factor 2^-s. hi + lo then
+// carries about 12 significant bits of each value, relative to the largest of its
+// lane's eight; residuals of zero rows are stored as zeros.
+__device__ __forceinline__ uint2 lo8_encode(const float* r, uint32_t& sbyte) {
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(r[e]));
+    // m < 2^(eb - 126) for the biased exponent eb of m, so m 2^(134 - eb) < 256
+    const int eb = (int)((__float_as_uint(m) >> 23) & 0xFFu);
+    const int s = min(134 - eb, 126);
+    const float mul = __uint_as_float((uint32_t)(127 + s) << 23);
+    uint32_t w0 = 0, w1 = 0;
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0] * mul, r[1] * mul, w0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[2] * mul, r[3] * mul, w0, true);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[4] * mul, r[5] * mul, w1, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6] * mul, r[7] * mul, w1, true);
+    sbyte = (uint32_t)(127 - s);
+    return make_uint2(w0, w1);
+}
+// The inverse: eight e4m3 residuals times 2^(sbyte - 127), as a bf16 fragment (exact:
+// a 4-bit significand times a power of two).
+__device__ __forceinline__ bf16x8 lo8_decode(uint2 raw, uint32_t sbyte) {
+    const float f = __uint_as_float(sbyte << 23);
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+// hi and the fp8 residual of eight fp32 values
+__device__ __forceinline__ void split8_lo8(const float* x, bf16x8& hi, uint2& lo, uint32_t& sbyte) {
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = (__bf16)x[e];
+        r[e] = x[e] - (float)hi[e];
+    }
+    lo = lo8_encode(r, sbyte);
+}
+
 __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

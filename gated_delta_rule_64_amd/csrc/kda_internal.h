@@ -98,16 +98,36 @@ struct ChunkArgs {
 //            NS = 2 on the bf16 path (tile 1 holds x - bf16(x) rounded to bf16, so
 //            hi + lo carries about 16 significant bits), NS = 1 on the fp32 path.
 //            records are ordered hv-major: record(hv, c) = hv * NCmax + c.
+//            The bf16 forward's own records, where its scan takes 32-column slices
+//            (scan_slice_width: many chains), are compact:
+//            qg, kgT and Aqk keep only their bf16 tile in place (NS = 1) and their
+//            residuals follow as fp8 tiles with per-lane scale words (Lo8Tile):
+//              qg lo [64][K], kgT lo [K][64], Aqk lo [64][64]   1 byte per value
+//              qg, kgT, Aqk scale words                         [bands][64] uint32
+//            then u and eG as above (hi + lo carries about 12 significant bits).
 struct ChunkLayout {
     int NCmax;            // chunk slots (dense: B * ceil(T/64); packed: T/64 + N)
     size_t elem;          // bytes per intermediate element (2 bf16, 4 fp32)
     size_t off_w, off_u, off_qg, off_kgT, off_aqk, off_eg, rec_bytes;
+    // residual tiles (the bf16 tile's offset + its size unless compact) and, in compact
+    // records, the fp8 residuals' scale words
+    size_t off_qg_lo, off_kgT_lo, off_aqk_lo, off_qg_sc, off_kgT_sc, off_aqk_sc;
+    bool lo8;             // compact records (fp8 residuals)
     size_t sched_bytes;   // bytes of the chunk schedule
     size_t total;
 };
 
+// Column-slice width of the scan: 16 while chains are few (so that chains x V / 16
+// blocks cover the chip), 32 on the bf16 path once chains x V / 32 reaches 512 blocks
+// (the fp32 path keeps 16: its operand tiles take twice the LDS).
+inline int scan_slice_width(long long chains, int V, bool bf16) {
+    return bf16 && chains * (V / 32) >= 512 ? 32 : 16;
+}
+
+// ckpt_records: the layout of the backward's recompute (bf16 residual tiles); otherwise
+// the forward's, compact where the scan takes 32-column slices (bf16 path, many chains)
 bool chunk_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qkv_dtype,
-                  ChunkLayout* out);
+                  ChunkLayout* out, bool ckpt_records = false);
 
 // The chunked backward: forward inputs, the output gradient and the gradients out.
 struct ChunkBwdArgs {

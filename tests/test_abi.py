@@ -66,11 +66,16 @@ def test_abi_version(lib):
     assert lib.kda_abi_version() == _header_int("KDA_ABI_VERSION")
 
 
-def _rec_bytes(K, V, elem):
-    # w in the compute type; qg, kg^T and Aqk each with a bf16 residual tile on the bf16
-    # path; u and 2^G in fp32
-    ns = 2 if elem == 2 else 1
-    b = 64 * K * elem + ns * (2 * 64 * K * elem + 64 * 64 * elem) + 64 * V * 4 + 4 * K
+def _rec_bytes(K, V, elem, compact=False):
+    # w, qg, kg^T and Aqk in the compute type; u and 2^G in fp32. On the bf16 path qg,
+    # kg^T and Aqk carry their residual as a second bf16 tile, or, in compact records
+    # (launches whose scan takes 32-column slices: chains x V / 32 >= 512), as fp8 tiles
+    # (a byte per value) with a 32-bit scale word per 16-row band and lane
+    b = 64 * K * elem + 2 * 64 * K * elem + 64 * 64 * elem + 64 * V * 4 + 4 * K
+    if elem == 2 and compact:
+        b += 2 * 64 * K + 64 * 64 + (64 // 16 + K // 16 + 64 // 16) * 64 * 4
+    elif elem == 2:
+        b += 2 * 64 * K * elem + 64 * 64 * elem
     return (b + 255) // 256 * 256
 
 
@@ -90,10 +95,26 @@ def test_workspace_bytes_dense(lib, K, V, dt, elem):
 
 
 def test_workspace_bytes_packed(lib):
+    # 64 x 16 chains: the compact records of the 32-column scan
     N, T, HV = 64, 33000, 16
     got = lib.kda_chunk_fwd_workspace_bytes(1, T, 16, HV, 128, 128, N, 1, 1)
     ncmax = T // 64 + N
-    assert got == _sched_bytes(N, ncmax) + HV * ncmax * _rec_bytes(128, 128, 2)
+    assert got == _sched_bytes(N, ncmax) + HV * ncmax * _rec_bytes(128, 128, 2, compact=True)
+
+
+@pytest.mark.parametrize("B,HV,V,compact", [(16, 8, 128, True), (1, 127, 128, False),
+                                            (1, 128, 128, True), (2, 128, 64, True),
+                                            (1, 255, 64, False)])
+def test_workspace_bytes_compact_threshold(lib, B, HV, V, compact):
+    """bf16 records are compact exactly where the scan takes 32-column slices:
+    chains x V / 32 >= 512 blocks."""
+    T, K = 200, 128
+    nt = (T + 63) // 64
+    got = lib.kda_chunk_fwd_workspace_bytes(B, T, 2, HV, K, V, B, 0, 1)
+    assert got == _sched_bytes(B, B * nt) + HV * B * nt * _rec_bytes(K, V, 2, compact=compact)
+    # the fp32 path never is
+    got32 = lib.kda_chunk_fwd_workspace_bytes(B, T, 2, HV, K, V, B, 0, 0)
+    assert got32 == _sched_bytes(B, B * nt) + HV * B * nt * _rec_bytes(K, V, 4)
 
 
 def test_workspace_bytes_invalid(lib):
@@ -306,13 +327,15 @@ def test_bwd_specific_rejects(lib):
 
 
 def test_bwd_workspace_bytes(lib):
-    """The forward's workspace, then per (value head, chunk) fp32 checkpoints,
-    reverse-scan operands and intermediates, then per-value-head dq, dk."""
+    """The forward's schedule and records (in the recompute's layout), then per (value
+    head, chunk) fp32 checkpoints, reverse-scan operands and intermediates, then
+    per-value-head dq, dk."""
     B, T, H, HV, K, V = 2, 4096 + 17, 4, 8, 128, 128
     nt = (T + 63) // 64
     items = HV * B * nt
     al = lambda x: (x + 255) // 256 * 256
-    off = al(lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, 1))
+    # the recompute's schedule and records (bf16 residual tiles)
+    off = al(_sched_bytes(B, B * nt) + items * _rec_bytes(K, V, 2))
     for per in (K * V, 64 * V, 2 * 64 * 64, K * V, 64 * V, 2 * 64 * K + 64 * V + K * V,
                 3 * 64 * K + 64 * 64 + K, 64 * K + 64 * 64):
         off = al(off + items * per * 4)

@@ -12,7 +12,7 @@ import torch
 import oracle
 from oracle import chunked as chunked_ref
 from gated_delta_rule_64_amd import inputs
-from tests.util import acc_tile_index, check, frag_tile_index, log, to64, to_device, valid_rows
+from tests.util import E4M3_VALUES, acc_tile_index, check, frag_tile_index, log, to64, to_device, valid_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -129,6 +129,27 @@ def test_chunk_packed_many_chains(K, V):
     for n in np.nonzero(lens == 0)[0]:
         assert torch.equal(ht[n], d["initial_state"][n]), f"empty slot {n} state must pass through bitwise"
     assert torch.isnan(o[:, ~m]).all(), "rows past the last offset must stay untouched"
+
+
+@pytest.mark.parametrize("V,HV", [(128, 32), (64, 64)])
+def test_chunk_dense_many_chains(V, HV):
+    """Dense batches with exactly enough chains for the wide-slice scan and its compact
+    records (chains x V / 32 = 512 blocks): B = 4 sequences of 213 tokens, GVA 4,
+    initial and final states, against the oracle; and the same problem one chain short
+    of the threshold (the other record layout) must agree with it to the tolerance."""
+    K, B, T = 128, 4, 3 * 64 + 21
+    d = small(B, T, HV // 4, HV, K, V, torch.bfloat16, seed=43)
+    log(f"[dense many chains] B={B} T={T} H={HV // 4} HV={HV} K={K} V={V} bf16, {B * HV} chains")
+    o, ht = run("chunk", d)
+    o_ref, ht_ref = oracle_of(d)
+    check("o", o, o_ref, torch.bfloat16)
+    check("final_state", ht, ht_ref, torch.bfloat16)
+    # the first 3 sequences alone: 3 x HV chains, below the threshold
+    d3 = dict(d, q=d["q"][:3], k=d["k"][:3], v=d["v"][:3], g=d["g"][:3], beta=d["beta"][:3],
+              initial_state=d["initial_state"][:3])
+    o3, ht3 = run("chunk", d3)
+    check("o (narrow slices)", o3, to64(o[:3]), torch.bfloat16, want_rounded=True)
+    check("final_state (narrow slices)", ht3, to64(ht[:3]), torch.bfloat16)
 
 
 def _decode_vs_oracle_batched(d, o, ht, batch=512):
@@ -431,22 +452,25 @@ def test_chunk_stage2_records_fp32(seed):
         assert np.abs(aqk[L:]).max(initial=0) == 0 and np.abs(w[L:]).max(initial=0) == 0
 
 
+@pytest.mark.parametrize("HV", [4, 128], ids=["bf16-residuals", "fp8-residuals"])
 @pytest.mark.parametrize("steep", [False, True])
-def test_chunk_stage2_records_bf16(steep):
+def test_chunk_stage2_records_bf16(steep, HV):
     """The bf16 intra kernel's records against the fp64 chunk algebra of the same (bf16)
-    inputs, K = V = 128, GVA 2 -> 4 value heads, a short last chunk. Each stored quantity
-    is decoded from its layout (hi + lo where it carries a residual tile). ``steep``
-    puts gates down to -15 into the second chunk so its diagonal blocks take the exact
-    one-sided branch."""
+    inputs, K = V = 128, two q/k heads shared by HV value heads, a short last chunk. Each
+    stored quantity is decoded from its layout (hi + lo where it carries a residual). With
+    4 value heads the records hold bf16 residual tiles; with 128 (chains x V / 32 = 512
+    scan blocks) they are compact, the residuals fp8 tiles with per-lane scale words.
+    ``steep`` puts gates down to -15 into the second chunk so its diagonal blocks take
+    the exact one-sided branch."""
     import gated_delta_rule_64_amd as kda
     K = V = 128
-    d = small(1, 128 + 37, 2, 4, K, V, torch.bfloat16, seed=21)
+    compact = HV == 128
+    d = small(1, 128 + 37, 2, HV, K, V, torch.bfloat16, seed=21)
     if steep:
         g = d["g"].clone()
         g[:, 64:128, 1] = -15.0
         d["g"] = g
     B, T, H, _ = d["q"].shape
-    HV = 4
     nbytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, torch.bfloat16)
     # zero-filled: the forward does not write Aqk's all-zero fragments (rows 0-31,
     # columns 32-63), which its scan never reads
@@ -454,15 +478,28 @@ def test_chunk_stage2_records_bf16(steep):
     run("chunk", d, workspace=ws)
     _, _, stages = chunked_ref.chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
                                        None, None, return_stages=True)
-    e2 = 2
-    rec = (64 * K * e2 * 5 + 64 * 64 * e2 * 2 + 64 * V * 4 + 4 * K + 255) // 256 * 256
+    # record: w, qg, kg^T, Aqk (bf16, fragment order), then either their residuals as a
+    # second bf16 tile each (in place after each) or, compact, the fp8 residuals of qg,
+    # kg^T, Aqk (same order, a byte per value) and their scale words [bands][64]; u; 2^G
+    if compact:
+        lo_at = 64 * K * 2 * 3 + 64 * 64 * 2
+        sc_at = lo_at + 2 * 64 * K + 64 * 64
+        u_at = sc_at + (4 + K // 16 + 4) * 64 * 4
+    else:
+        u_at = 64 * K * 2 * 5 + 64 * 64 * 2 * 2
+    rec = (u_at + 64 * V * 4 + 4 * K + 255) // 256 * 256
+    assert nbytes == (((3 * B + 1) * 4 + 15) // 16 * 16 + B * ((T + 63) // 64) * 8 + B * 4 + 255) // 256 * 256 \
+        + HV * B * ((T + 63) // 64) * rec
     raw = ws.cpu()
     NT = (T + 63) // 64
     sched = (((3 * B + 1) * 4 + 15) // 16 * 16 + B * NT * 8 + 255) // 256 * 256
     scale = K ** -0.5
     # relative bounds: single-bf16 tiles (w) and the fp32 u built from the bf16 T beta
-    # carry bf16 rounding; the hi + lo tiles and 2^G are fp32-level
-    bounds = {"Aqk": 2e-5, "w": 1e-2, "u": 1e-2, "qg": 2e-5, "kgT": 2e-5, "2^G": 2e-5}
+    # carry bf16 rounding; hi + lo in bf16 is fp32-level, a bf16 tile plus its fp8
+    # residual carries about 12 bits of each value relative to the largest of the eight
+    # its lane holds; 2^G is fp32
+    split = 2e-4 if compact else 2e-5
+    bounds = {"Aqk": split, "w": 1e-2, "u": 1e-2, "qg": split, "kgT": split, "2^G": 2e-5}
     worst = {}
     for st in stages:
         hv, c = st["hv"], st["start"] // 64
@@ -472,18 +509,30 @@ def test_chunk_stage2_records_bf16(steep):
         def bf(off, n):
             return raw[base + off: base + off + 2 * n].view(torch.bfloat16).double().numpy()
 
-        def frag(off, R, KC, split):
-            x = bf(off, R * KC)
-            if split:
-                x = x + bf(off + 2 * R * KC, R * KC)
-            return x[frag_tile_index(R, KC, 32, 8)]
-        off = 0
-        w = frag(off, 64, K, False); off += 64 * K * 2
-        qg = frag(off, 64, K, True); off += 2 * 64 * K * 2
-        kgT = frag(off, K, 64, True); off += 2 * K * 64 * 2
-        aqk = frag(off, 64, 64, True); off += 2 * 64 * 64 * 2
-        u = raw[base + off: base + off + 4 * 64 * V].view(torch.float32).double().numpy()[acc_tile_index(64, V)]
-        off += 64 * V * 4
+        def frag(off, R, KC):
+            return bf(off, R * KC)[frag_tile_index(R, KC, 32, 8)]
+
+        def lo8(off, sc_off, R, KC):
+            codes = raw[base + off: base + off + R * KC].numpy()
+            vals = E4M3_VALUES[codes][frag_tile_index(R, KC, 32, 8)]
+            words = raw[base + sc_off: base + sc_off + (R // 16) * 64 * 4].numpy().view(np.uint32)
+            row, col = np.arange(R)[:, None], np.arange(KC)[None, :]
+            lane = row % 16 + 16 * ((col % 32) // 8)
+            sbyte = (words[(row // 16) * 64 + lane] >> (8 * (col // 32)).astype(np.uint32)) & 0xFF
+            return vals * np.exp2(sbyte.astype(np.float64) - 127.0)
+        if compact:
+            w = frag(0, 64, K)
+            qg = frag(64 * K * 2, 64, K) + lo8(lo_at, sc_at, 64, K)
+            kgT = frag(2 * 64 * K * 2, K, 64) + lo8(lo_at + 64 * K, sc_at + 4 * 64 * 4, K, 64)
+            aqk = frag(3 * 64 * K * 2, 64, 64) + lo8(lo_at + 2 * 64 * K, sc_at + (4 + K // 16) * 64 * 4, 64, 64)
+        else:
+            off = 0
+            w = frag(off, 64, K); off += 64 * K * 2
+            qg = frag(off, 64, K) + frag(off + 64 * K * 2, 64, K); off += 2 * 64 * K * 2
+            kgT = frag(off, K, 64) + frag(off + K * 64 * 2, K, 64); off += 2 * K * 64 * 2
+            aqk = frag(off, 64, 64) + frag(off + 64 * 64 * 2, 64, 64)
+        u = raw[base + u_at: base + u_at + 4 * 64 * V].view(torch.float32).double().numpy()[acc_tile_index(64, V)]
+        off = u_at + 64 * V * 4
         eg = raw[base + off: base + off + 4 * K].view(torch.float32).double().numpy()
         for name, got, want in (("Aqk", aqk[:L, :L], st["Aqk"]), ("w", w[:L], st["w"]),
                                 ("u", u[:L], st["u"]), ("qg", qg[:L], scale * st["qg"]),

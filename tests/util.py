@@ -99,3 +99,18 @@ def acc_tile_index(R, NCOL):
     row = np.arange(R)[:, None]
     col = np.arange(NCOL)[None, :]
     return (((col // 16) * 4 + row // 16) * 64 + col % 16 + 16 * ((row % 16) // 4)) * 4 + row % 4
+
+
+def _e4m3_value(code):
+    """OCP FP8 E4M3 (exponent bias 7, no infinities, S.1111.111 is NaN)."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+# value of each of the 256 e4m3 codes (decoding residual tiles stored in fp8)
+E4M3_VALUES = np.array([_e4m3_value(c) for c in range(256)])
