@@ -1109,7 +1109,7 @@ __global__ __launch_bounds__(SB_THREADS, 4) void bwd_state_bf16_kernel(BwdParams
 // is split into 16x16 output tiles dealt round-robin to the waves, and the row sums
 // that make dbeta are added into LDS.
 // ------------------------------------------------------------------------------------
-constexpr int WY_THREADS = 512;
+constexpr int WY_THREADS = 1024;
 
 template <int K, int V, typename TIn, typename TB>
 __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
@@ -1297,19 +1297,21 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
 // with e(r,s) = 2^(Gamma_r - Gamma_s) per channel. Pairs in different 16-row blocks run on
 // the matrix cores, factored through a boundary row between them (both factors <= 1): the
 // row side of block I through row 16I - 1, the column side of block J through row
-// 16J + 15. Pairs inside a block keep one one-sided factor each. Wave w owns channel
-// tile w (K / 16 waves); each lane holds its results in the matrix-core layout (rows
-// 16I + 4lq .. +3 of channel 16w + lr) through the elementwise step.
+// 16J + 15. Pairs inside a block keep one one-sided factor each. Two waves share each
+// 16-channel tile (2K / 16 waves): one takes row blocks 0 and 1, the other 2 and 3 --
+// block I's row side (8I products), column side (8(3 - I)) and diagonal (16) cost the
+// same for every I -- and each lane holds its results in the matrix-core layout (rows
+// 16I + 4lq .. +3 of channel 16 tile + lr) through the elementwise step.
 // ------------------------------------------------------------------------------------
 // largest decay spread (log2 units) of a 16-row block that the pair kernel anchors
 constexpr float PAIR_SPREAD = 64.f;
 
 template <int K>
-constexpr int pair_threads() { return 4 * K; }   // one wave per 16-channel tile
+constexpr int pair_threads() { return 8 * K; }   // two waves per 16-channel tile
 
 template <int K, int V, typename TIn>
-__global__ __launch_bounds__(4 * K, 1) void bwd_pair_kernel(BwdParams p) {
-    constexpr int LA = C + 1, LK = K + 1, NDW = 1, NTH = pair_threads<K>();
+__global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParams p) {
+    constexpr int LA = C + 1, LK = K + 1, NTH = pair_threads<K>();
     typedef GsLayout<K> GL;
     typedef WyLayout<K> WL;
     __shared__ float qL[C * LK];     // q, then dGamma
@@ -1320,6 +1322,7 @@ __global__ __launch_bounds__(4 * K, 1) void bwd_pair_kernel(BwdParams p) {
     __shared__ float dGL[K];
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = wave % (K / 16), half = wave / (K / 16);   // channel tile; row blocks 2 half, 2 half + 1
     int c, hv;
     int2 pos;
     if (!bwd_chunk(p, c, hv, pos)) return;
@@ -1358,150 +1361,145 @@ __global__ __launch_bounds__(4 * K, 1) void bwd_pair_kernel(BwdParams p) {
     }
     __syncthreads();
 
-    f32x4 aq[NDW][4], akr[NDW][4], akc[NDW][4];   // [channel tile][row block]
+    // accumulators of the wave's two row blocks I = 2 half + ib
+    f32x4 aq[2], akr[2], akc[2];
 #pragma unroll
-    for (int t = 0; t < NDW; ++t)
+    for (int ib = 0; ib < 2; ++ib) {
+        aq[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+        akr[ib] = aq[ib];
+        akc[ib] = aq[ib];
+    }
+    const int d = 16 * tile + lr;
+    // row side, pairs across blocks: block I against rows s < 16I, through row 16I - 1
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            aq[t][I] = f32x4{0.f, 0.f, 0.f, 0.f};
-            akr[t][I] = aq[t][I];
-            akc[t][I] = aq[t][I];
+    for (int ib = 0; ib < 2; ++ib) {
+        const int I = 2 * half + ib;
+        if (I == 0) continue;
+        const float P = GmL[(16 * I - 1) * LK + d];
+        f32x4 yq = {0.f, 0.f, 0.f, 0.f}, yk = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < 16 * I; s0 += 4) {
+            const int s = s0 + lq;
+            const float b = kL[s * LK + d] * exp2_fast(P - GmL[s * LK + d]);
+            yq = __builtin_amdgcn_mfma_f32_16x16x4f32(sc * dAL[(16 * I + lr) * LA + s], b, yq, 0, 0, 0);
+            yk = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[(16 * I + lr) * LA + s], b, yk, 0, 0, 0);
         }
 #pragma unroll
-    for (int t = 0; t < NDW; ++t) {
-        const int d = 16 * (wave + t) + lr;
-        // row side, pairs across blocks: block I against rows s < 16I, through row 16I - 1
-#pragma unroll
-        for (int I = 1; I < 4; ++I) {
-            const float P = GmL[(16 * I - 1) * LK + d];
-            f32x4 yq = {0.f, 0.f, 0.f, 0.f}, yk = {0.f, 0.f, 0.f, 0.f};
-            for (int s0 = 0; s0 < 16 * I; s0 += 4) {
-                const int s = s0 + lq;
-                const float b = kL[s * LK + d] * exp2_fast(P - GmL[s * LK + d]);
-                yq = __builtin_amdgcn_mfma_f32_16x16x4f32(sc * dAL[(16 * I + lr) * LA + s], b, yq, 0, 0, 0);
-                yk = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[(16 * I + lr) * LA + s], b, yk, 0, 0, 0);
-            }
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const float f = exp2_fast(GmL[(16 * I + 4 * lq + rr) * LK + d] - P);
-                aq[t][I][rr] = fmaf(f, yq[rr], aq[t][I][rr]);
-                akr[t][I][rr] = fmaf(f, yk[rr], akr[t][I][rr]);
-            }
-        }
-        // column side, pairs across blocks: block J against rows r >= 16J + 16, through
-        // row 16J + 15
-#pragma unroll
-        for (int J = 0; J < 3; ++J) {
-            const float Q = GmL[(16 * J + 15) * LK + d];
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            for (int r0 = 16 * (J + 1); r0 < C; r0 += 4) {
-                const int r = r0 + lq;
-                const float e = exp2_fast(GmL[r * LK + d] - Q);
-                z = __builtin_amdgcn_mfma_f32_16x16x4f32(sc * dAL[r * LA + 16 * J + lr], qL[r * LK + d] * e, z, 0, 0, 0);
-                z = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[r * LA + 16 * J + lr], kL[r * LK + d] * e, z, 0, 0, 0);
-            }
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const float f = exp2_fast(Q - GmL[(16 * J + 4 * lq + rr) * LK + d]);
-                akc[t][J][rr] = fmaf(f, z[rr], akc[t][J][rr]);
-            }
-        }
-        // pairs inside a block. Where the block's decay spread (Gamma of its first row minus
-        // Gamma of its last, in every channel of the tile) is at most PAIR_SPREAD, anchor
-        // the factors at a block boundary row and use the matrix cores:
-        //   row side    2^(G_r - G_s) = 2^(G_r - G_last) 2^(G_last - G_s),
-        //   column side 2^(G_s - G_r) = 2^(G_first - G_r) 2^(G_s - G_first),
-        // the second factor (<= 1) scaling the operand and the first (<= 2^spread) the
-        // finished sum. Otherwise one one-sided factor per pair (exact at any decay). In
-        // both, pairs on the wrong side of the diagonal meet a zero dAqk / dM.
-#pragma unroll 1
-        for (int I = 0; I < 4; ++I) {
-            f32x4 xq4, xk4, xc4;
-            const float gfirst = GmL[(16 * I) * LK + d], glast = GmL[(16 * I + 15) * LK + d];
-            const bool steep = __builtin_amdgcn_ballot_w64(gfirst - glast > PAIR_SPREAD) != 0;   // wave-uniform
-            if (!steep) {
-                f32x4 yq = {0.f, 0.f, 0.f, 0.f}, yk = yq, yc = yq;
-                const int ri = 16 * I + lr;   // A operand row of this lane
-#pragma unroll
-                for (int s0 = 0; s0 < 16; s0 += 4) {
-                    const int s = 16 * I + s0 + lq;   // contraction index of this lane
-                    const float gs = GmL[s * LK + d];
-                    const float ks = kL[s * LK + d];
-                    const float br = ks * exp2_fast(glast - gs);
-                    const float fc = exp2_fast(gs - gfirst);
-                    yq = __builtin_amdgcn_mfma_f32_16x16x4f32(dAL[ri * LA + s], br, yq, 0, 0, 0);
-                    yk = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[ri * LA + s], br, yk, 0, 0, 0);
-                    yc = __builtin_amdgcn_mfma_f32_16x16x4f32(sc * dAL[s * LA + ri], qL[s * LK + d] * fc, yc, 0, 0, 0);
-                    yc = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[s * LA + ri], ks * fc, yc, 0, 0, 0);
-                }
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const float gr = GmL[(16 * I + 4 * lq + rr) * LK + d];
-                    const float fr = exp2_fast(gr - glast), fcol = exp2_fast(gfirst - gr);
-                    xq4[rr] = sc * fr * yq[rr];
-                    xk4[rr] = fr * yk[rr];
-                    xc4[rr] = fcol * yc[rr];
-                }
-            } else {
-                float kb[16], qb[16], gb[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    kb[j] = kL[(16 * I + j) * LK + d];
-                    qb[j] = qL[(16 * I + j) * LK + d];
-                    gb[j] = GmL[(16 * I + j) * LK + d];
-                }
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int r = 16 * I + 4 * lq + rr;
-                    const float gr = GmL[r * LK + d];
-                    float xq = 0.f, xk = 0.f, xc = 0.f;
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int s = 16 * I + j;
-                        // row side (s <= r): 2^min(x, 0); column side (s >= r): 2^min(-x, 0),
-                        // x = Gamma_r - Gamma_s; both are 2^-|x| on their own side and 1 on
-                        // the other, so one exp2 serves the pair
-                        const float x = gr - gb[j];
-                        const float t2 = exp2_fast(-fabsf(x));
-                        const float er = x <= 0.f ? t2 : 1.f;
-                        const float ec = x >= 0.f ? t2 : 1.f;
-                        const float ek = kb[j] * er;
-                        xq = fmaf(dAL[r * LA + s], ek, xq);
-                        xk = fmaf(dML[r * LA + s], ek, xk);
-                        xc = fmaf(fmaf(sc * dAL[s * LA + r], qb[j], dML[s * LA + r] * kb[j]), ec, xc);
-                    }
-                    xq4[rr] = sc * xq;
-                    xk4[rr] = xk;
-                    xc4[rr] = xc;
-                }
-            }
-#pragma unroll
-            for (int Ib = 0; Ib < 4; ++Ib)
-                if (Ib == I) { aq[t][Ib] += xq4; akr[t][Ib] += xk4; akc[t][Ib] += xc4; }
+        for (int rr = 0; rr < 4; ++rr) {
+            const float f = exp2_fast(GmL[(16 * I + 4 * lq + rr) * LK + d] - P);
+            aq[ib][rr] = fmaf(f, yq[rr], aq[ib][rr]);
+            akr[ib][rr] = fmaf(f, yk[rr], akr[ib][rr]);
         }
     }
-    // elementwise terms of qg, kd, kg; dGamma; dq, dk per value head
-    float dgam[NDW][4][4];
+    // column side, pairs across blocks: block J against rows r >= 16J + 16, through
+    // row 16J + 15
 #pragma unroll
-    for (int t = 0; t < NDW; ++t) {
-        const int d = 16 * (wave + t) + lr;
-        const float Gd = GmL[(C - 1) * LK + d];
-        float dgk = 0.f;
+    for (int ib = 0; ib < 2; ++ib) {
+        const int J = 2 * half + ib;
+        if (J == 3) continue;
+        const float Q = GmL[(16 * J + 15) * LK + d];
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int r0 = 16 * (J + 1); r0 < C; r0 += 4) {
+            const int r = r0 + lq;
+            const float e = exp2_fast(GmL[r * LK + d] - Q);
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(sc * dAL[r * LA + 16 * J + lr], qL[r * LK + d] * e, z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[r * LA + 16 * J + lr], kL[r * LK + d] * e, z, 0, 0, 0);
+        }
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+        for (int rr = 0; rr < 4; ++rr) {
+            const float f = exp2_fast(Q - GmL[(16 * J + 4 * lq + rr) * LK + d]);
+            akc[ib][rr] = fmaf(f, z[rr], akc[ib][rr]);
+        }
+    }
+    // pairs inside a block. Where the block's decay spread (Gamma of its first row minus
+    // Gamma of its last, in every channel of the tile) is at most PAIR_SPREAD, anchor
+    // the factors at a block boundary row and use the matrix cores:
+    //   row side    2^(G_r - G_s) = 2^(G_r - G_last) 2^(G_last - G_s),
+    //   column side 2^(G_s - G_r) = 2^(G_first - G_r) 2^(G_s - G_first),
+    // the second factor (<= 1) scaling the operand and the first (<= 2^spread) the
+    // finished sum. Otherwise one one-sided factor per pair (exact at any decay). In
+    // both, pairs on the wrong side of the diagonal meet a zero dAqk / dM.
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+        const int I = 2 * half + ib;
+        f32x4 xq4, xk4, xc4;
+        const float gfirst = GmL[(16 * I) * LK + d], glast = GmL[(16 * I + 15) * LK + d];
+        const bool steep = __builtin_amdgcn_ballot_w64(gfirst - glast > PAIR_SPREAD) != 0;   // wave-uniform
+        if (!steep) {
+            f32x4 yq = {0.f, 0.f, 0.f, 0.f}, yk = yq, yc = yq;
+            const int ri = 16 * I + lr;   // A operand row of this lane
+#pragma unroll
+            for (int s0 = 0; s0 < 16; s0 += 4) {
+                const int s = 16 * I + s0 + lq;   // contraction index of this lane
+                const float gs = GmL[s * LK + d];
+                const float ks = kL[s * LK + d];
+                const float br = ks * exp2_fast(glast - gs);
+                const float fc = exp2_fast(gs - gfirst);
+                yq = __builtin_amdgcn_mfma_f32_16x16x4f32(dAL[ri * LA + s], br, yq, 0, 0, 0);
+                yk = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[ri * LA + s], br, yk, 0, 0, 0);
+                yc = __builtin_amdgcn_mfma_f32_16x16x4f32(sc * dAL[s * LA + ri], qL[s * LK + d] * fc, yc, 0, 0, 0);
+                yc = __builtin_amdgcn_mfma_f32_16x16x4f32(dML[s * LA + ri], ks * fc, yc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const float gr = GmL[(16 * I + 4 * lq + rr) * LK + d];
+                const float fr = exp2_fast(gr - glast), fcol = exp2_fast(gfirst - gr);
+                xq4[rr] = sc * fr * yq[rr];
+                xk4[rr] = fr * yk[rr];
+                xc4[rr] = fcol * yc[rr];
+            }
+        } else {
+            // (the rows' k, q and Gamma are read from LDS inside the loop: this branch is
+            // rare, and holding them in registers would crowd the 128-register budget)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int r = 16 * I + 4 * lq + rr;
+                const float gr = GmL[r * LK + d];
+                float xq = 0.f, xk = 0.f, xc = 0.f;
+#pragma unroll 4
+                for (int j = 0; j < 16; ++j) {
+                    const int s = 16 * I + j;
+                    const float kb = kL[s * LK + d], qb = qL[s * LK + d];
+                    // row side (s <= r): 2^min(x, 0); column side (s >= r): 2^min(-x, 0),
+                    // x = Gamma_r - Gamma_s; both are 2^-|x| on their own side and 1 on
+                    // the other, so one exp2 serves the pair
+                    const float x = gr - GmL[s * LK + d];
+                    const float t2 = exp2_fast(-fabsf(x));
+                    const float er = x <= 0.f ? t2 : 1.f;
+                    const float ec = x >= 0.f ? t2 : 1.f;
+                    const float ek = kb * er;
+                    xq = fmaf(dAL[r * LA + s], ek, xq);
+                    xk = fmaf(dML[r * LA + s], ek, xk);
+                    xc = fmaf(fmaf(sc * dAL[s * LA + r], qb, dML[s * LA + r] * kb), ec, xc);
+                }
+                xq4[rr] = sc * xq;
+                xk4[rr] = xk;
+                xc4[rr] = xc;
+            }
+        }
+        aq[ib] += xq4;
+        akr[ib] += xk4;
+        akc[ib] += xc4;
+    }
+    // elementwise terms of qg, kd, kg; dGamma; dq, dk per value head
+    float dgam[2][4];
+    {
+        const float Gd = GmL[(C - 1) * LK + d];
+        float dgk = 0.f;
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 16 * (2 * half + ib) + 4 * lq + rr;
                 const float qv = qL[r * LK + d], kv = kL[r * LK + d], gr = GmL[r * LK + d];
                 const float e1 = exp2_fast(gr), e2 = exp2_fast(Gd - gr);
                 const float dqg = gsC[GL::DQG + r * K + d];
                 const float dkg = gsC[GL::DKG + r * K + d];
                 const float dkd = wyC[WL::DKD + r * K + d];
-                const float dqi = aq[t][I][rr], dkr = akr[t][I][rr], dkc = akc[t][I][rr];
+                const float dqi = aq[ib][rr], dkr = akr[ib][rr], dkc = akc[ib][rr];
                 const float dq = fmaf(sc * e1, dqg, dqi);
                 const float dk = dkr + dkc + e1 * dkd + e2 * dkg;
                 const float kge = kv * e2 * dkg;
-                dgam[t][I][rr] = LN2F * (qv * dq + kv * (dkr - dkc + e1 * dkd) - kge);
+                dgam[ib][rr] = LN2F * (qv * dq + kv * (dkr - dkc + e1 * dkd) - kge);
                 if (r < len) {
                     dgk += kge;
                     const size_t row = (size_t)(pos.x + r);
@@ -1513,12 +1511,10 @@ __global__ __launch_bounds__(4 * K, 1) void bwd_pair_kernel(BwdParams p) {
     }
     __syncthreads();   // qL becomes dGamma
 #pragma unroll
-    for (int t = 0; t < NDW; ++t)
+    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                qL[(16 * I + 4 * lq + rr) * LK + 16 * (wave + t) + lr] = dgam[t][I][rr];
+        for (int rr = 0; rr < 4; ++rr)
+            qL[(16 * (2 * half + ib) + 4 * lq + rr) * LK + d] = dgam[ib][rr];
     __syncthreads();
     // dg = reverse cumsum of dGamma over the chunk's rows; dG joins at the last row
     if (tid < K && len > 0) {
