@@ -28,7 +28,9 @@ Also reported on the same JSON line:
                     (timed like the headline) against its 205.8 MB floor;
   * gated, fused_inputs -- the headline with the gate activation (and the q/k norm and
                     beta sigmoid) fused into the loads;
-  * backward     -- the chunked backward of the headline forward (every input gradient);
+  * backward     -- the chunked backward of the headline forward (every input gradient),
+                    and a training step split into kda_chunk_fwd_train (the forward keeping
+                    the backward's checkpoints) and kda_chunk_bwd_saved (no recompute);
   * varlen       -- the packed-sequence forward (64 slots, ~31k tokens, 4 empty slots,
                     initial and final states);
   * decode       -- the per-token recurrent forward on 4096 sequences x 32 heads (one token
@@ -500,13 +502,46 @@ def main():
         for _ in range(2):
             bcall()
         bwd_ms = back_to_back(bcall, bsteps, hip, sptr)
+        # a training step's split: the forward keeping the backward's checkpoints
+        # (kda_chunk_fwd_train, o written as well), then the backward from them
+        # (kda_chunk_bwd_saved, no recompute)
+        tws = torch.empty(bws_bytes, dtype=torch.uint8, device=dev)
+        o_t = torch.empty_like(d["v"])
+
+        def tcall():
+            rc = lib.kda_chunk_fwd_train(
+                vp(d["q"].data_ptr()), vp(d["k"].data_ptr()), vp(d["v"].data_ptr()),
+                vp(d["g"].data_ptr()), vp(d["beta"].data_ptr()), None, None, N,
+                vp(o_t.data_ptr()), None, B, T, H, HV, K, V, kda.KDA_BF16, kda.KDA_BF16, 0.0, 64,
+                vp(tws.data_ptr()), bws_bytes, None, sptr)
+            if rc != 0:
+                raise RuntimeError(lib.kda_last_error().decode())
+
+        def scall():
+            rc = lib.kda_chunk_bwd_saved(
+                vp(d["q"].data_ptr()), vp(d["k"].data_ptr()), vp(d["v"].data_ptr()),
+                vp(d["g"].data_ptr()), vp(d["beta"].data_ptr()), None, None, N,
+                vp(dout.data_ptr()), None, vp(gq.data_ptr()), vp(gk.data_ptr()), vp(gv.data_ptr()),
+                vp(gg.data_ptr()), vp(gb.data_ptr()), None, B, T, H, HV, K, V, kda.KDA_BF16,
+                kda.KDA_BF16, 0.0, 64, vp(tws.data_ptr()), bws_bytes, None, sptr)
+            if rc != 0:
+                raise RuntimeError(lib.kda_last_error().decode())
+        for _ in range(2):
+            tcall()
+        train_fwd_ms = back_to_back(tcall, bsteps, hip, sptr)
+        for _ in range(2):
+            scall()
+        saved_bwd_ms = back_to_back(scall, bsteps, hip, sptr)
         # inputs, do and every gradient once (SURVEY's floor for the backward)
         bwd_bytes = 2 * (q_b + v_b + g_b + beta_b) + o_b
         result["backward"] = {"workload": "kda_chunk_bwd of the headline forward (dq, dk, dv, dg, dbeta; do ~ N(0,1) bf16, no dht)",
                               "ms_per_step": bwd_ms, "tokens_per_s": tokens / (bwd_ms * 1e-3), "steps": bsteps,
                               "algorithmic_bytes": bwd_bytes,
-                              "hbm_frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del bws, dout, gq, gk, gv, gg, gb
+                              "hbm_frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "train_split": {"forward_keeping_checkpoints_ms": train_fwd_ms,
+                                              "backward_from_checkpoints_ms": saved_bwd_ms,
+                                              "step_ms": train_fwd_ms + saved_bwd_ms}}
+        del bws, tws, o_t, dout, gq, gk, gv, gg, gb
 
     # ---------------- decode: 4096 sequences x 32 heads ----------------
     del ws, out

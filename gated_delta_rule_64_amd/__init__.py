@@ -17,6 +17,9 @@ Entry points (same names as the C ABI):
   kda_chunk_bwd(q, k, v, g, beta, do, ...)  chunked backward: dq, dk, dv, dg, dbeta, dh0
   kda_chunk_bwd_ex(...)                      the same through the fused input options
                                              (raw gate -> dA_log, ddt_bias; q/k norm; beta sigmoid)
+  kda_chunk_fwd_train(q, k, v, g, beta, ...) a training forward: o and the final state, with
+                                             the backward's checkpoints kept in a workspace
+  kda_chunk_bwd_saved(..., do, workspace, ...)  kda_chunk_bwd from that workspace (no recompute)
   kda_chunk_fwd_workspace_bytes(...)         workspace size queries (also _bwd_)
   kda_chunk_fwd_noalloc(...)                 kda_chunk_fwd with no allocation at all: the
                                              intermediates live in a per-GPU scratch array
@@ -44,11 +47,13 @@ from ._lib import (  # noqa: F401
     KdaError,
     kda_chunk_bwd,
     kda_chunk_bwd_ex,
+    kda_chunk_bwd_saved,
     kda_chunk_bwd_workspace_bytes,
     kda_chunk_fwd,
     kda_chunk_fwd_ex,
     kda_chunk_fwd_gated,
     kda_chunk_fwd_noalloc,
+    kda_chunk_fwd_train,
     kda_chunk_fwd_workspace_bytes,
     kda_last_error,
     kda_noalloc_scratch_bytes,

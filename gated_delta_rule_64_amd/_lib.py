@@ -71,6 +71,12 @@ def load_library():
         lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
                                       sz, vp, vp]
+        lib.kda_chunk_bwd_saved.restype = i32
+        lib.kda_chunk_bwd_saved.argtypes = lib.kda_chunk_bwd.argtypes
+        lib.kda_chunk_fwd_train.restype = i32
+        lib.kda_chunk_fwd_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                            i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                            vp, sz, vp, vp]
         lib.kda_chunk_bwd_ex.restype = i32
         lib.kda_chunk_bwd_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp, vp, i32,
                                          vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
@@ -512,6 +518,12 @@ def kda_chunk_bwd(q, k, v, g, beta, do, initial_state=None, cu_seqlens=None, dht
     (with respect to the per-token log2 decay g), dbeta in beta's dtype, dh0 float32
     [N, HV, K, V] (None unless ``want_dh0``). Rows outside every sequence are zero.
     ``debug`` as in ``kda_chunk_fwd``."""
+    return _chunk_bwd(False, q, k, v, g, beta, do, initial_state, cu_seqlens, dht, scale,
+                      want_dh0, workspace, dev_status, debug)
+
+
+def _chunk_bwd(saved, q, k, v, g, beta, do, initial_state, cu_seqlens, dht, scale, want_dh0,
+               workspace, dev_status, debug):
     lib = load_library()
     B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens)
     _bwd_inputs(q, v, do, dht, N, HV, K, V, dev)
@@ -526,15 +538,49 @@ def kda_chunk_bwd(q, k, v, g, beta, do, initial_state=None, cu_seqlens=None, dht
         need = lib.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, int(cu_seqlens is not None), qkv)
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
     dev_status = _debug_status(debug, dev_status, dev)
-    rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                           _ptr(cu_seqlens), N, _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv),
-                           _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, HV, K, V, qkv, bdt,
-                           float(scale or 0.0), 64, _ptr(workspace), _nbytes(workspace),
-                           _ptr(dev_status), _stream(dev))
+    fn = lib.kda_chunk_bwd_saved if saved else lib.kda_chunk_bwd
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+            _ptr(cu_seqlens), N, _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(dg), _ptr(dbeta), _ptr(dh0), B, T, H, HV, K, V, qkv, bdt,
+            float(scale or 0.0), 64, _ptr(workspace), _nbytes(workspace),
+            _ptr(dev_status), _stream(dev))
     if rc != 0:
         raise KdaError(rc, lib.kda_last_error().decode())
     _debug_raise(debug, dev_status, dev)
     return dq, dk, dv, dg, dbeta, dh0
+
+
+def kda_chunk_fwd_train(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                        output_final_state=False, scale=None, *, out=None, final_state=None,
+                        workspace=None, dev_status=None, debug=False):
+    """Training forward: ``kda_chunk_fwd``'s outputs, with the forward's checkpoints
+    for the backward kept in a workspace. Returns ``(o, final_state or None, workspace)``;
+    pass the workspace to ``kda_chunk_bwd_saved`` with the same inputs. ``workspace``
+    (uint8, at least ``kda_chunk_bwd_workspace_bytes`` bytes) may be given to reuse one."""
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens)
+    out, final_state = _fwd_outputs(q, v, N, HV, K, V, dev, out, final_state, output_final_state)
+    need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, int(cu_seqlens is not None), qkv))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_buffers(dev, [], workspace=workspace, dev_status=dev_status)
+    dev_status = _debug_status(debug, dev_status, dev)
+    rc = lib.kda_chunk_fwd_train(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                 _ptr(cu_seqlens), N, _ptr(out), _ptr(final_state), B, T, H, HV, K, V,
+                                 qkv, bdt, float(scale or 0.0), 64, _ptr(workspace), _nbytes(workspace),
+                                 _ptr(dev_status), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    _debug_raise(debug, dev_status, dev)
+    return out, final_state, workspace
+
+
+def kda_chunk_bwd_saved(q, k, v, g, beta, do, workspace, initial_state=None, cu_seqlens=None,
+                        dht=None, scale=None, *, want_dh0=True, dev_status=None, debug=False):
+    """``kda_chunk_bwd`` from the workspace a ``kda_chunk_fwd_train`` call with the same
+    inputs left: the same results, without the forward recompute."""
+    return _chunk_bwd(True, q, k, v, g, beta, do, initial_state, cu_seqlens, dht, scale,
+                      want_dh0, workspace, dev_status, debug)
 
 
 def kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, N, packed, dtype=KDA_BF16) -> int:

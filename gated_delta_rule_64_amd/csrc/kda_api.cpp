@@ -183,16 +183,23 @@ int recurrent_impl(const void* q, const void* k, const void* v, const void* g, i
     return KDA_OK;
 }
 
+// the backward (a.mode BWD_FULL or BWD_FROM_SAVED) or a training forward (BWD_FORWARD)
 int chunk_bwd_impl(const kda::ChunkBwdArgs& a0, const float* g, int chunk_size) {
     kda::ChunkBwdArgs a = a0;
-    int rc = check_common(a.q, a.k, a.v, g, a.beta, a.initial_state, a.cu_seqlens, a.N, a.dv,
-                          a.dh0, a.B, a.T, a.H, a.HV, a.K, a.V, a.qkv_dtype, a.beta_dtype);
+    const bool fwd = a.mode == kda::BWD_FORWARD;
+    int rc = check_common(a.q, a.k, a.v, g, a.beta, a.initial_state, a.cu_seqlens, a.N,
+                          fwd ? a.fwd_o : a.dv, fwd ? a.fwd_final_state : a.dh0, a.B, a.T, a.H,
+                          a.HV, a.K, a.V, a.qkv_dtype, a.beta_dtype);
     if (rc != KDA_OK) return rc;
-    if ((long long)a.B * a.T > 0 && (!a.dout || !a.dq || !a.dk || !a.dv || !a.dg || !a.dbeta))
-        return fail(KDA_ERR_NULL, "do, dq, dk, dv, dg and dbeta must be non-NULL");
-    if (!aligned16(a.dht) || !aligned16(a.dout) || !aligned16(a.dq) || !aligned16(a.dk) ||
-        !aligned16(a.dg) || !aligned16(a.dbeta))
-        return fail(KDA_ERR_SHAPE, "dht, do, dq, dk, dg and dbeta must be 16-byte aligned");
+    if (fwd) {
+        if ((long long)a.B * a.T > 0 && !a.fwd_o) return fail(KDA_ERR_NULL, "o must be non-NULL");
+    } else {
+        if ((long long)a.B * a.T > 0 && (!a.dout || !a.dq || !a.dk || !a.dv || !a.dg || !a.dbeta))
+            return fail(KDA_ERR_NULL, "do, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (!aligned16(a.dht) || !aligned16(a.dout) || !aligned16(a.dq) || !aligned16(a.dk) ||
+            !aligned16(a.dg) || !aligned16(a.dbeta))
+            return fail(KDA_ERR_SHAPE, "dht, do, dq, dk, dg and dbeta must be 16-byte aligned");
+    }
     if (chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64, got %d", chunk_size);
     if (a.K != 64 && a.K != 128)
@@ -335,6 +342,46 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
     a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype; a.scale = scale;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.dev_status = dev_status; a.stream = stream;
+    return chunk_bwd_impl(a, g, chunk_size);
+}
+
+int kda_chunk_fwd_train(const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                        int N, void* o, float* final_state, int B, int T, int H, int HV, int K,
+                        int V, int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                        void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                        hipStream_t stream) {
+    clear_error();
+    kda::ChunkBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
+    a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype; a.scale = scale;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.dev_status = dev_status; a.stream = stream;
+    a.mode = kda::BWD_FORWARD;
+    a.fwd_o = o;
+    a.fwd_final_state = final_state;
+    return chunk_bwd_impl(a, g, chunk_size);
+}
+
+int kda_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                        const float* initial_state, const int32_t* cu_seqlens, int N, const void* dout,
+                        const float* dht, void* dq, void* dk, void* dv, float* dg, void* dbeta,
+                        float* dh0, int B, int T, int H, int HV, int K, int V, int qkv_dtype,
+                        int beta_dtype, float scale, int chunk_size, void* workspace,
+                        size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+    clear_error();
+    kda::ChunkBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
+    a.dout = dout; a.dht = dht;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    a.N = N; a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.qkv_dtype = qkv_dtype; a.beta_dtype = beta_dtype; a.scale = scale;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.dev_status = dev_status; a.stream = stream;
+    a.mode = kda::BWD_FROM_SAVED;
     return chunk_bwd_impl(a, g, chunk_size);
 }
 

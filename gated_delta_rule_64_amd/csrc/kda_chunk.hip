@@ -1307,6 +1307,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
 // ------------------------------------------------------------------------------------
 // scan: Stage 3+4 for one (sequence, value head, BV-column slice)
 // ------------------------------------------------------------------------------------
+// scan instances: the forward (o), the backward's re-scan (checkpoints, no o), and a
+// training forward (checkpoints and o)
+constexpr int SCAN_FWD = 0, SCAN_CKPT = 1, SCAN_CKPT_O = 2;
+
 struct ScanParams {
     const char* rec;
     size_t rec_bytes, off_w, off_u, off_qg, off_kgT, off_aqk, off_eg;
@@ -1322,9 +1326,9 @@ struct ScanParams {
     const int32_t* order;    // slots by descending chunk count (packed), or NULL
     int N, T, HV, NT, NCmax;
     int dense;               // no offsets: sequence n is chunks n NT .. n NT + NT - 1, no schedule
-    // checkpoints for the backward (kernels instantiated with CKPT, which write no o),
-    // per (value head, chunk) like the records: the state at the chunk's start [K][V]
-    // and v' [64][V], fp32
+    // checkpoints for the backward (kernels instantiated with CKPT, which write o only in
+    // a training forward, CKPT == SCAN_CKPT_O), per (value head, chunk) like the records:
+    // the state at the chunk's start [K][V] and v' [64][V], fp32
     float* h_out;
     float* vn_out;
 };
@@ -1406,7 +1410,7 @@ __device__ __forceinline__ void load_frags(ScanFrags<K, V, BV, TW>& F, const cha
         F.e[a] = *reinterpret_cast<const f32x4*>(eg + 16 * (wave + 4 * a) + 4 * lq);
 }
 
-template <int K, int V, int BV, typename TIn, bool CKPT>
+template <int K, int V, int BV, typename TIn, int CKPT>
 __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
     typedef TIn TW;
     typedef ScanFrags<K, V, BV, TW> SF;
@@ -1571,7 +1575,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void scan_kernel(ScanParams p) {
             }
             acc += acc2;
             const int i = 16 * wave + lr;
-            if (!CKPT && i < len) {
+            if (CKPT != SCAN_CKPT && i < len) {
                 typedef __attribute__((ext_vector_type(4))) TIn ovec;
                 ovec ov;
 #pragma unroll
@@ -1769,7 +1773,7 @@ __device__ __forceinline__ void load_state_g(StateFrags<K, BV, LO8>& F, const ch
     }
 }
 
-template <int K, int V, int BV, bool CKPT>
+template <int K, int V, int BV, int CKPT>
 __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams p) {
     typedef __bf16 TW;
     typedef Mma<TW> M;
@@ -1897,7 +1901,7 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
                     }
                 }
                 const int i = 16 * b + lr;
-                if (!CKPT && i < len) {
+                if (CKPT != SCAN_CKPT && i < len) {
                     vec4 ov;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) ov[r] = (__bf16)(oacc[nt][r] + oacc2[nt][r]);
@@ -2145,23 +2149,28 @@ hipError_t launch_scan(const ChunkArgs& a, const ScanParams& sp) {
     // the slice width: enough blocks to cover the chip, wide slices when chains abound
     const int BV = scan_slice_width(chains, V, sizeof(TIn) == 2);
     const unsigned nscan = (unsigned)(chains * (V / BV));
-    const bool ckpt = sp.h_out != nullptr;   // backward re-scan: checkpoints, no o
+    // checkpoints for the backward (its re-scan: no o; a training forward: with o)
+    const bool ckpt = sp.h_out != nullptr;
     // the records' format was chosen with the same rule (chunk_layout)
     if (sp.lo8 != (!ckpt && BV == 32)) return hipErrorInvalidValue;
     if constexpr (sizeof(TIn) == 2) {
-        if (ckpt)
-            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 16, true>), dim3((unsigned)(chains * (V / 16))),
-                               dim3(SCAN8_THREADS), 0, a.stream, sp);
+        const unsigned nck = (unsigned)(chains * (V / 16));
+        if (ckpt && sp.o)
+            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 16, SCAN_CKPT_O>), dim3(nck), dim3(SCAN8_THREADS), 0, a.stream, sp);
+        else if (ckpt)
+            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 16, SCAN_CKPT>), dim3(nck), dim3(SCAN8_THREADS), 0, a.stream, sp);
         else if (BV == 32)
-            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 32, false>), dim3(nscan), dim3(SCAN8_THREADS), 0, a.stream, sp);
+            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 32, SCAN_FWD>), dim3(nscan), dim3(SCAN8_THREADS), 0, a.stream, sp);
         else
-            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 16, false>), dim3(nscan), dim3(SCAN8_THREADS), 0, a.stream, sp);
+            hipLaunchKernelGGL((scan_bf16_kernel<K, V, 16, SCAN_FWD>), dim3(nscan), dim3(SCAN8_THREADS), 0, a.stream, sp);
         return hipGetLastError();
     }
-    if (ckpt)
-        hipLaunchKernelGGL((scan_kernel<K, V, 16, TIn, true>), dim3(nscan), dim3(NTHREADS), 0, a.stream, sp);
+    if (ckpt && sp.o)
+        hipLaunchKernelGGL((scan_kernel<K, V, 16, TIn, SCAN_CKPT_O>), dim3(nscan), dim3(NTHREADS), 0, a.stream, sp);
+    else if (ckpt)
+        hipLaunchKernelGGL((scan_kernel<K, V, 16, TIn, SCAN_CKPT>), dim3(nscan), dim3(NTHREADS), 0, a.stream, sp);
     else
-        hipLaunchKernelGGL((scan_kernel<K, V, 16, TIn, false>), dim3(nscan), dim3(NTHREADS), 0, a.stream, sp);
+        hipLaunchKernelGGL((scan_kernel<K, V, 16, TIn, SCAN_FWD>), dim3(nscan), dim3(NTHREADS), 0, a.stream, sp);
     return hipGetLastError();
 }
 

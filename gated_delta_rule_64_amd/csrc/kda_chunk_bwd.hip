@@ -1124,7 +1124,7 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
     __shared__ float TL[C * LA];
     __shared__ float dTL[C * LA];
     __shared__ float bL[C];
-    __shared__ float dbL[C];
+    __shared__ float dbP[NW][C];     // each wave's row sums for dbeta (added in wave order at the end)
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int c, hv;
@@ -1146,8 +1146,8 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
         float b = tid < len ? to_f32(bin[(size_t)(pos.x + tid) * p.HV + hv]) : 0.f;
         if (p.in.beta_sig != 0.f && tid < len) b = beta_from_logit(b, p.in.beta_sig);
         bL[tid] = b;
-        dbL[tid] = 0.f;
     }
+    for (int e = tid; e < NW * C; e += NTH) dbP[e / C][e % C] = 0.f;
     __syncthreads();
     if (p.in.l2norm_k) l2norm_rows_lds<K>(kL, LK, tid);
     if (p.in.gate_mode != GATE_LOG2) gate_rows_lds<K, NTH>(XL, LX, len, p.in, hv, tid);
@@ -1171,12 +1171,13 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
         lt_.store(TL, LA, tid);
     }
     __syncthreads();
-    // row sums over one tile's columns (the 16 lanes of a row), added into dbL
+    // row sums over one tile's columns (the 16 lanes of a row), added into the wave's own
+    // partials (one lane per row: no atomics, so the sums do not depend on wave timing)
     auto add_rows = [&](int row0, const float (&x)[4]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float y = sum16(x[r]);
-            if (lr == 0) atomicAdd(&dbL[row0 + 4 * lq + r], y);
+            if (lr == 0) dbP[wave][row0 + 4 * lq + r] += y;
         }
     };
     // dT tiles (I, J) owned by this wave: t = wave + NW i, I = t / 4, J = t % 4
@@ -1283,9 +1284,12 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
     }
     __syncthreads();
     if (tid < len) {
+        float db = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) db += dbP[w][tid];
         const size_t e = (size_t)(pos.x + tid) * p.HV + hv;
-        if (p.dbeta_f32) reinterpret_cast<float*>(p.dbeta)[e] = dbL[tid];
-        else reinterpret_cast<TB*>(p.dbeta)[e] = from_f32<TB>(dbL[tid]);
+        if (p.dbeta_f32) reinterpret_cast<float*>(p.dbeta)[e] = db;
+        else reinterpret_cast<TB*>(p.dbeta)[e] = from_f32<TB>(db);
     }
 }
 
@@ -1319,7 +1323,8 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParam
     __shared__ float GmL[C * LK];    // Gamma
     __shared__ float dAL[C * LA];    // dAqk (s <= r)
     __shared__ float dML[C * LA];    // dM (s < r)
-    __shared__ float dGL[K];
+    __shared__ float dGL[K];         // dG of the chunk end, from the state products
+    __shared__ float dGP[2][K];      // each half's kg term of dG (added in a fixed order)
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = wave % (K / 16), half = wave / (K / 16);   // channel tile; row blocks 2 half, 2 half + 1
@@ -1507,7 +1512,10 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParam
                     p.dk_hv[(row * p.HV + hv) * K + d] = dk;
                 }
             }
-        atomicAdd(&dGL[d], LN2F * dgk);
+        // the four lanes of channel d (lq = 0..3) summed in a fixed order
+        dgk += __shfl_xor(dgk, 16, 64);
+        dgk += __shfl_xor(dgk, 32, 64);
+        if (lq == 0) dGP[half][d] = LN2F * dgk;
     }
     __syncthreads();   // qL becomes dGamma
 #pragma unroll
@@ -1518,7 +1526,7 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParam
     __syncthreads();
     // dg = reverse cumsum of dGamma over the chunk's rows; dG joins at the last row
     if (tid < K && len > 0) {
-        float acc = dGL[tid];
+        float acc = dGL[tid] + dGP[0][tid] + dGP[1][tid];
         for (int rr = len - 1; rr >= 0; --rr) {
             acc += qL[rr * LK + tid];
             p.dg[((size_t)(pos.x + rr) * p.HV + hv) * K + tid] = acc;
@@ -1558,22 +1566,29 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
     char* ws = reinterpret_cast<char*>(a.workspace);
     const bool dense = a.cu_seqlens == nullptr;
     const int NT = (a.T + C - 1) / C;
-    // forward recompute: schedule (packed), records, and the re-scan with checkpoints
-    ChunkArgs f;
-    f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
-    f.in = a.in;   // the recompute runs with the forward's fused options
-    f.initial_state = a.initial_state; f.cu_seqlens = a.cu_seqlens;
-    f.o = nullptr; f.final_state = nullptr;
-    f.N = a.N; f.B = a.B; f.T = a.T; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
-    f.qkv_dtype = a.qkv_dtype; f.beta_dtype = a.beta_dtype; f.scale = a.scale;
-    f.workspace = a.workspace; f.workspace_bytes = a.workspace_bytes;
-    f.dev_status = a.dev_status; f.stream = a.stream; f.events = nullptr;
-    f.h_out = reinterpret_cast<float*>(ws + L.off_h);
-    f.vn_out = reinterpret_cast<float*>(ws + L.off_vn);
-    f.m_out = reinterpret_cast<float*>(ws + L.off_mt);                        // [items][64][64]
-    f.t_out = f.m_out + (size_t)L.fwd.NCmax * a.HV * (C * C);                  // [items][64][64]
-    hipError_t err = launch_chunk(f, L.fwd);
-    if (err != hipSuccess) return err;
+    // forward recompute: schedule (packed), records, and the re-scan with checkpoints (a
+    // training forward also writes o and the final state; a backward from its workspace
+    // skips this)
+    if (a.mode != BWD_FROM_SAVED) {
+        ChunkArgs f;
+        f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
+        f.in = a.in;   // the recompute runs with the forward's fused options
+        f.initial_state = a.initial_state; f.cu_seqlens = a.cu_seqlens;
+        const bool fwd = a.mode == BWD_FORWARD;
+        f.o = fwd ? a.fwd_o : nullptr;
+        f.final_state = fwd ? a.fwd_final_state : nullptr;
+        f.N = a.N; f.B = a.B; f.T = a.T; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
+        f.qkv_dtype = a.qkv_dtype; f.beta_dtype = a.beta_dtype; f.scale = a.scale;
+        f.workspace = a.workspace; f.workspace_bytes = a.workspace_bytes;
+        f.dev_status = a.dev_status; f.stream = a.stream; f.events = nullptr;
+        f.h_out = reinterpret_cast<float*>(ws + L.off_h);
+        f.vn_out = reinterpret_cast<float*>(ws + L.off_vn);
+        f.m_out = reinterpret_cast<float*>(ws + L.off_mt);                        // [items][64][64]
+        f.t_out = f.m_out + (size_t)L.fwd.NCmax * a.HV * (C * C);                  // [items][64][64]
+        hipError_t err = launch_chunk(f, L.fwd);
+        if (err != hipSuccess || fwd) return err;
+    }
+    hipError_t err = hipSuccess;
 
     BwdParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.dout = a.dout; p.dht = a.dht;

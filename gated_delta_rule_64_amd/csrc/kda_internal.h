@@ -129,6 +129,8 @@ inline int scan_slice_width(long long chains, int V, bool bf16) {
 bool chunk_layout(int B, int T, int HV, int K, int V, int N, bool packed, int qkv_dtype,
                   ChunkLayout* out, bool ckpt_records = false);
 
+constexpr int BWD_FULL = 0, BWD_FORWARD = 1, BWD_FROM_SAVED = 2;
+
 // The chunked backward: forward inputs, the output gradient and the gradients out.
 struct ChunkBwdArgs {
     const void* q;
@@ -154,6 +156,14 @@ struct ChunkBwdArgs {
     int32_t* dev_status;
     hipStream_t stream;
     bool skip_reduce = false;   // leave dq, dk per value head (fp32) in the workspace
+    // BWD_FULL: the backward, the forward recomputed first into the workspace;
+    // BWD_FORWARD: only that forward, writing o (fwd_o) and the final state
+    // (fwd_final_state, or NULL) as well: a training forward whose workspace then holds
+    // everything the backward recomputes; BWD_FROM_SAVED: the backward from such a
+    // workspace (same inputs), without the recompute
+    int mode = 0;
+    void* fwd_o = nullptr;
+    float* fwd_final_state = nullptr;
     // fused input options of the forward being differentiated (g unused for a raw gate);
     // the gradients then are with respect to the transformed inputs (q, k normalised,
     // the log2 gate, the activated beta), the last one written fp32 when dbeta_f32

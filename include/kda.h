@@ -232,6 +232,41 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                   hipStream_t stream);
 
 /*
+ * Training forward: kda_chunk_fwd's outputs (o, and the final state when final_state is
+ * non-NULL) computed the way kda_chunk_bwd recomputes the forward (the method's backward
+ * in "kernel-fun 0.2.0.dev1 sdist", ALGORITHM.md, section Backward, starts with that
+ * recompute), leaving in the workspace everything that recompute produces: the
+ * schedule, the per-chunk records, Stage 2's M and T, the state at every chunk start
+ * and v'. A kda_chunk_bwd_saved call with the same inputs and this workspace then skips
+ * the recompute. Arguments as kda_chunk_fwd, except:
+ *   workspace    at least kda_chunk_bwd_workspace_bytes(...) bytes (the backward's
+ *                size), 256-byte aligned; it belongs to this forward and its backward
+ *                until that backward has run.
+ * o agrees with kda_chunk_fwd's to the tolerance of the bf16 path (bit for bit where
+ * kda_chunk_fwd's scan takes 16-column slices: chains x V / 32 < 512).
+ */
+int kda_chunk_fwd_train(const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                        int N, void* o, float* final_state, int B, int T, int H, int HV, int K,
+                        int V, int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                        void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                        hipStream_t stream);
+
+/*
+ * kda_chunk_bwd from a kda_chunk_fwd_train workspace: the same arguments and results
+ * (bit for bit), without the forward recompute. The inputs must be those of that
+ * forward and the workspace untouched since; the workspace is then used as
+ * kda_chunk_bwd uses its own.
+ */
+int kda_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                        int N, const void* dout, const float* dht, void* dq, void* dk, void* dv,
+                        float* dg, void* dbeta, float* dh0, int B, int T, int H, int HV, int K,
+                        int V, int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                        void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                        hipStream_t stream);
+
+/*
  * kda_chunk_bwd for a forward run with the options of kda_chunk_fwd_ex: the same `g`,
  * `gate`, A_log, dt_bias, has_lower_bound, lower_bound, beta and `preprocess` arguments
  * (and rules) as that forward. The gradients are with respect to the raw inputs:
@@ -337,7 +372,7 @@ const char* kda_last_error(void);
 
 /* ABI version of this header (bumped on any signature change or added entry point);
  * the library returns the KDA_ABI_VERSION it was built with. */
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 int kda_abi_version(void);
 
 #ifdef __cplusplus

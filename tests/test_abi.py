@@ -181,15 +181,26 @@ def _rec_ex(lib, **kw):
                                     a["st"], a["stream"])
 
 
-def _bwd(lib, **kw):
+def _bwd(lib, fn="kda_chunk_bwd", **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, N=1, do=FAKE, dht=None,
              dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, db=FAKE, dh0=None, B=1, T=64, H=2, HV=2, K=128,
              V=128, qd=1, bd=1, scale=0.0, cs=64, ws=FAKE, wsb=1 << 40, st=None, stream=None)
     a.update(kw)
-    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["N"],
-                             a["do"], a["dht"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"],
-                             a["dh0"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["qd"],
-                             a["bd"], a["scale"], a["cs"], a["ws"], a["wsb"], a["st"], a["stream"])
+    return getattr(lib, fn)(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["N"],
+                            a["do"], a["dht"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"],
+                            a["dh0"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["qd"],
+                            a["bd"], a["scale"], a["cs"], a["ws"], a["wsb"], a["st"], a["stream"])
+
+
+def _train(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, N=1, o=FAKE, fs=None,
+             B=1, T=64, H=2, HV=2, K=128, V=128, qd=1, bd=1, scale=0.0, cs=64, ws=FAKE,
+             wsb=1 << 40, st=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_train(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["N"],
+                                   a["o"], a["fs"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"],
+                                   a["qd"], a["bd"], a["scale"], a["cs"], a["ws"], a["wsb"], a["st"],
+                                   a["stream"])
 
 
 CASES = [
@@ -306,23 +317,51 @@ def test_binding_rejects_bad_tensors():
                       torch.zeros(1, 64, 2))
 
 
+@pytest.mark.parametrize("fn", ["kda_chunk_bwd", "kda_chunk_bwd_saved"])
 @pytest.mark.parametrize("name,kw,code", CASES, ids=[c[0] for c in CASES])
-def test_bwd_rejects_common(lib, name, kw, code):
-    assert _bwd(lib, **kw) == code
+def test_bwd_rejects_common(lib, name, kw, code, fn):
+    assert _bwd(lib, fn, **kw) == code
     assert lib.kda_last_error().decode() != ""
 
 
-def test_bwd_specific_rejects(lib):
+@pytest.mark.parametrize("fn", ["kda_chunk_bwd", "kda_chunk_bwd_saved"])
+def test_bwd_specific_rejects(lib, fn):
     for out in ("do", "dq", "dk", "dv", "dg", "db"):
-        assert _bwd(lib, **{out: None}) == -1, out
-    assert _bwd(lib, dht=FAKE + 4) == -2
-    assert _bwd(lib, cs=32) == -4
-    assert _bwd(lib, K=96) == -4
-    assert _bwd(lib, V=256) == -4
-    assert _bwd(lib, ws=None) == -5
-    assert _bwd(lib, wsb=16) == -5
-    assert _bwd(lib, ws=FAKE + 16) == -5
-    assert _bwd(lib, cu=FAKE, N=0, T=0) == 0
+        assert _bwd(lib, fn, **{out: None}) == -1, out
+    assert _bwd(lib, fn, dht=FAKE + 4) == -2
+    assert _bwd(lib, fn, cs=32) == -4
+    assert _bwd(lib, fn, K=96) == -4
+    assert _bwd(lib, fn, V=256) == -4
+    assert _bwd(lib, fn, ws=None) == -5
+    assert _bwd(lib, fn, wsb=16) == -5
+    assert _bwd(lib, fn, ws=FAKE + 16) == -5
+    assert _bwd(lib, fn, cu=FAKE, N=0, T=0) == 0
+    assert lib.kda_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("name,kw,code", CASES, ids=[c[0] for c in CASES])
+def test_train_forward_rejects_common(lib, name, kw, code):
+    assert _train(lib, **kw) == code
+    assert lib.kda_last_error().decode() != ""
+
+
+def test_train_forward_specific_rejects(lib):
+    """The training forward takes the backward's workspace (its size, not the forward's),
+    needs o, and checks o and the final state like kda_chunk_fwd."""
+    B, T, H, HV, K, V = 1, 64, 2, 2, 128, 128
+    fwd_bytes = lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, B, 0, 1)
+    bwd_bytes = lib.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, B, 0, 1)
+    assert bwd_bytes > fwd_bytes
+    assert _train(lib, o=None) == -1
+    assert _train(lib, o=FAKE + 4) == -2
+    assert _train(lib, fs=FAKE + 4) == -2
+    assert _train(lib, cs=32) == -4
+    assert _train(lib, K=96) == -4
+    assert _train(lib, ws=None) == -5
+    assert _train(lib, wsb=fwd_bytes) == -5
+    assert b"need %d" % bwd_bytes in lib.kda_last_error()
+    assert _train(lib, ws=FAKE + 16) == -5
+    assert _train(lib, cu=FAKE, N=0, T=0) == 0
     assert lib.kda_last_error().decode() == ""
 
 

@@ -804,6 +804,73 @@ def _check_bwd(d, do, dht, dtype, rows=None, label=""):
     return got, ref
 
 
+def test_chunk_bwd_deterministic():
+    """The backward's gradients are the same bits on every call: its row and channel sums
+    (dbeta, the chunk-end dG term) are added in a fixed order, not by LDS atomics whose
+    order follows the waves' timing. Three calls at the c2 shape (with dht) and a packed
+    batch."""
+    import gated_delta_rule_64_amd as kda
+    for d in (small(2, 1024 + 37, 4, 8, 128, 128, torch.bfloat16, seed=68), _train_case("packed_many_chains")):
+        do, dht = _bwd_inputs(d, 69)
+        runs = [kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["initial_state"],
+                                  d["cu_seqlens"], dht) for _ in range(3)]
+        torch.cuda.synchronize()
+        for rep in runs[1:]:
+            for name, x, y in zip(["dq", "dk", "dv", "dg", "dbeta", "dh0"], rep, runs[0]):
+                assert torch.equal(x, y), f"{name} differs between calls"
+    log("  three backward calls bitwise equal (dense and packed)")
+
+
+def _train_case(case):
+    if case == "dense_gva_bf16":
+        return small(2, 200, 2, 4, 128, 128, torch.bfloat16, seed=64)
+    if case == "dense_fp32_k64":
+        return small(1, 300, 2, 2, 64, 128, torch.float32, seed=65)
+    # packed, 160 slots x 8 heads: kda_chunk_fwd takes 32-column slices (compact records)
+    w = inputs.Workload("many", 1, 0, 4, 8, 128, 128, torch.bfloat16, torch.bfloat16, 66, -5.0, 0.05, True,
+                        n_slots=160, len_lo=1, len_hi=200, n_empty=10)
+    return to_device(inputs.make(w))
+
+
+@pytest.mark.parametrize("case", ["dense_gva_bf16", "dense_fp32_k64", "packed_many_chains"])
+def test_chunk_train_forward_and_saved_backward(case):
+    """The training forward's o and final state against kda_chunk_fwd (bit for bit where
+    that forward's scan also takes 16-column slices, else to the tolerance) and the
+    oracle; the backward from its workspace bit for bit equal to the full backward's,
+    twice in a row from the same workspace."""
+    import gated_delta_rule_64_amd as kda
+    d = _train_case(case)
+    dtype = d["q"].dtype
+    cu = d["cu_seqlens"]
+    log(f"[train forward + saved backward] {case}")
+    o, ht, ws = kda.kda_chunk_fwd_train(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], cu,
+                                        output_final_state=True)
+    o_f, ht_f = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], cu,
+                                  output_final_state=True)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle_of(d)
+    rows = valid_rows(cu.cpu(), d["q"].shape[1]) if cu is not None else None
+    if rows is None:
+        check("o", o, o_ref, dtype)
+    else:
+        check("o", o[:, rows], o_ref[:, rows], dtype)
+    check("final_state", ht, ht_ref, dtype)
+    if case == "packed_many_chains":
+        check("o (vs kda_chunk_fwd)", o[:, rows], to64(o_f[:, rows]), dtype, want_rounded=True)
+        check("final_state (vs kda_chunk_fwd)", ht, to64(ht_f), dtype)
+    else:
+        assert torch.equal(o, o_f) and torch.equal(ht, ht_f), "16-column slices: same bits as kda_chunk_fwd"
+    do, dht = _bwd_inputs(d, 67)
+    full = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["initial_state"], cu, dht)
+    for rep in range(2):
+        saved = kda.kda_chunk_bwd_saved(d["q"], d["k"], d["v"], d["g"], d["beta"], do, ws,
+                                        d["initial_state"], cu, dht)
+        torch.cuda.synchronize()
+        for name, x, y in zip(["dq", "dk", "dv", "dg", "dbeta", "dh0"], saved, full):
+            assert torch.equal(x, y), f"{name} differs from kda_chunk_bwd's (call {rep})"
+    log("  saved backward == full backward bitwise (two calls)")
+
+
 def test_chunk_many_slots():
     """Packed offsets with more slots (2,100) than the schedule sorts by length (2,048),
     so the scans take the slots in index order: lengths 0..70 (every tenth slot empty,
