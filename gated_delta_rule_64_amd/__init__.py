@@ -20,6 +20,7 @@ Entry points (same names as the C ABI):
   kda_chunk_fwd_train(q, k, v, g, beta, ...) a training forward: o and the final state, with
                                              the backward's checkpoints kept in a workspace
   kda_chunk_bwd_saved(..., do, workspace, ...)  kda_chunk_bwd from that workspace (no recompute)
+  kda_chunk_fwd_ex_train / kda_chunk_bwd_ex_saved   the same with kda_chunk_fwd_ex's options
   kda_chunk_fwd_workspace_bytes(...)         workspace size queries (also _bwd_)
   kda_chunk_fwd_noalloc(...)                 kda_chunk_fwd with no allocation at all: the
                                              intermediates live in a per-GPU scratch array
@@ -47,10 +48,12 @@ from ._lib import (  # noqa: F401
     KdaError,
     kda_chunk_bwd,
     kda_chunk_bwd_ex,
+    kda_chunk_bwd_ex_saved,
     kda_chunk_bwd_saved,
     kda_chunk_bwd_workspace_bytes,
     kda_chunk_fwd,
     kda_chunk_fwd_ex,
+    kda_chunk_fwd_ex_train,
     kda_chunk_fwd_gated,
     kda_chunk_fwd_noalloc,
     kda_chunk_fwd_train,

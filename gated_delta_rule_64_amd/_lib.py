@@ -81,6 +81,12 @@ def load_library():
         lib.kda_chunk_bwd_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp, vp, i32,
                                          vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                          i32, i32, i32, i32, f32, i32, vp, sz, vp, vp]
+        lib.kda_chunk_bwd_ex_saved.restype = i32
+        lib.kda_chunk_bwd_ex_saved.argtypes = lib.kda_chunk_bwd_ex.argtypes
+        lib.kda_chunk_fwd_ex_train.restype = i32
+        lib.kda_chunk_fwd_ex_train.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, i32, vp, vp, i32,
+                                               vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                               vp, sz, vp, vp]
         lib.kda_chunk_bwd_ex_workspace_bytes.restype = sz
         lib.kda_chunk_bwd_ex_workspace_bytes.argtypes = [i32] * 9
         lib.kda_chunk_bwd_workspace_bytes.restype = sz
@@ -524,6 +530,8 @@ def kda_chunk_bwd(q, k, v, g, beta, do, initial_state=None, cu_seqlens=None, dht
 
 def _chunk_bwd(saved, q, k, v, g, beta, do, initial_state, cu_seqlens, dht, scale, want_dh0,
                workspace, dev_status, debug):
+    if saved and workspace is None:
+        raise ValueError("the backward from saved checkpoints needs the training forward's workspace")
     lib = load_library()
     B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens)
     _bwd_inputs(q, v, do, dht, N, HV, K, V, dev)
@@ -597,6 +605,63 @@ def kda_chunk_bwd_ex(q, k, v, g, beta, do, initial_state=None, cu_seqlens=None, 
     """Gradients of ``kda_chunk_fwd_ex`` with the same options, with respect to the raw
     inputs. Returns ``(dq, dk, dv, dg, dbeta, dh0, dA_log, ddt_bias)``; the last two are
     None unless the gate is raw (``ddt_bias`` also needs ``dt_bias``)."""
+    return _chunk_bwd_ex(False, q, k, v, g, beta, do, initial_state, cu_seqlens, dht, scale,
+                         use_gate_in_kernel, A_log, dt_bias, lower_bound, use_qk_l2norm_in_kernel,
+                         l2norm_q, l2norm_k, use_beta_sigmoid_in_kernel, allow_neg_eigval, want_dh0,
+                         workspace, dev_status, debug)
+
+
+def kda_chunk_bwd_ex_saved(q, k, v, g, beta, do, workspace, initial_state=None, cu_seqlens=None,
+                           dht=None, scale=None, *, use_gate_in_kernel=False, A_log=None,
+                           dt_bias=None, lower_bound=None, use_qk_l2norm_in_kernel=False,
+                           l2norm_q=None, l2norm_k=None, use_beta_sigmoid_in_kernel=False,
+                           allow_neg_eigval=False, want_dh0=True, dev_status=None, debug=False):
+    """``kda_chunk_bwd_ex`` from the workspace a ``kda_chunk_fwd_ex_train`` call with the
+    same inputs and options left: the same results, without the forward recompute."""
+    return _chunk_bwd_ex(True, q, k, v, g, beta, do, initial_state, cu_seqlens, dht, scale,
+                         use_gate_in_kernel, A_log, dt_bias, lower_bound, use_qk_l2norm_in_kernel,
+                         l2norm_q, l2norm_k, use_beta_sigmoid_in_kernel, allow_neg_eigval, want_dh0,
+                         workspace, dev_status, debug)
+
+
+def kda_chunk_fwd_ex_train(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                           output_final_state=False, scale=None, *, use_gate_in_kernel=False,
+                           A_log=None, dt_bias=None, lower_bound=None, use_qk_l2norm_in_kernel=False,
+                           l2norm_q=None, l2norm_k=None, use_beta_sigmoid_in_kernel=False,
+                           allow_neg_eigval=False, out=None, final_state=None, workspace=None,
+                           dev_status=None, debug=False):
+    """``kda_chunk_fwd_train`` with the options of ``kda_chunk_fwd_ex``. Returns
+    ``(o, final_state or None, workspace)`` for ``kda_chunk_bwd_ex_saved``."""
+    lib = load_library()
+    B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens,
+                                                  raw_gate=use_gate_in_kernel)
+    gate, pre = _options(g, HV, K, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                         use_qk_l2norm_in_kernel, l2norm_q, l2norm_k, use_beta_sigmoid_in_kernel,
+                         allow_neg_eigval)
+    out, final_state = _fwd_outputs(q, v, N, HV, K, V, dev, out, final_state, output_final_state)
+    if workspace is None:
+        need = lib.kda_chunk_bwd_ex_workspace_bytes(B, T, H, HV, K, V, N, int(cu_seqlens is not None), qkv)
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    _check_buffers(dev, [], workspace=workspace, dev_status=dev_status)
+    dev_status = _debug_status(debug, dev_status, dev)
+    rc = lib.kda_chunk_fwd_ex_train(_ptr(q), _ptr(k), _ptr(v), _ptr(g), gate, _ptr(A_log), _ptr(dt_bias),
+                                    int(lower_bound is not None),
+                                    float(lower_bound if lower_bound is not None else 0.0), _ptr(beta), pre,
+                                    _ptr(initial_state), _ptr(cu_seqlens), N, _ptr(out), _ptr(final_state),
+                                    B, T, H, HV, K, V, qkv, bdt, float(scale or 0.0), 64, _ptr(workspace),
+                                    _nbytes(workspace), _ptr(dev_status), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    _debug_raise(debug, dev_status, dev)
+    return out, final_state, workspace
+
+
+def _chunk_bwd_ex(saved, q, k, v, g, beta, do, initial_state, cu_seqlens, dht, scale,
+                  use_gate_in_kernel, A_log, dt_bias, lower_bound, use_qk_l2norm_in_kernel,
+                  l2norm_q, l2norm_k, use_beta_sigmoid_in_kernel, allow_neg_eigval, want_dh0,
+                  workspace, dev_status, debug):
+    if saved and workspace is None:
+        raise ValueError("the backward from saved checkpoints needs the training forward's workspace")
     lib = load_library()
     B, T, H, HV, K, V, N, qkv, bdt, dev = _common(q, k, v, g, beta, initial_state, cu_seqlens,
                                                   raw_gate=use_gate_in_kernel)
@@ -615,13 +680,14 @@ def kda_chunk_bwd_ex(q, k, v, g, beta, do, initial_state=None, cu_seqlens=None, 
         need = lib.kda_chunk_bwd_ex_workspace_bytes(B, T, H, HV, K, V, N, int(cu_seqlens is not None), qkv)
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
     dev_status = _debug_status(debug, dev_status, dev)
-    rc = lib.kda_chunk_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), gate, _ptr(A_log), _ptr(dt_bias),
-                              int(lower_bound is not None),
-                              float(lower_bound if lower_bound is not None else 0.0), _ptr(beta), pre,
-                              _ptr(initial_state), _ptr(cu_seqlens), N, _ptr(do), _ptr(dht), _ptr(dq),
-                              _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(dA), _ptr(ddt),
-                              B, T, H, HV, K, V, qkv, bdt, float(scale or 0.0), 64, _ptr(workspace),
-                              _nbytes(workspace), _ptr(dev_status), _stream(dev))
+    fn = lib.kda_chunk_bwd_ex_saved if saved else lib.kda_chunk_bwd_ex
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), gate, _ptr(A_log), _ptr(dt_bias),
+            int(lower_bound is not None),
+            float(lower_bound if lower_bound is not None else 0.0), _ptr(beta), pre,
+            _ptr(initial_state), _ptr(cu_seqlens), N, _ptr(do), _ptr(dht), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(dA), _ptr(ddt),
+            B, T, H, HV, K, V, qkv, bdt, float(scale or 0.0), 64, _ptr(workspace),
+            _nbytes(workspace), _ptr(dev_status), _stream(dev))
     if rc != 0:
         raise KdaError(rc, lib.kda_last_error().decode())
     _debug_raise(debug, dev_status, dev)

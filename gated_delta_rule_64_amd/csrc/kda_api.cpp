@@ -249,32 +249,43 @@ size_t kda_chunk_bwd_ex_workspace_bytes(int B, int T, int H, int HV, int K, int 
     return L.total;
 }
 
-int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
-                     const float* A_log, const float* dt_bias, int has_lower_bound,
-                     float lower_bound, const void* beta, int preprocess,
-                     const float* initial_state, const int32_t* cu_seqlens, int N,
-                     const void* dout, const float* dht, void* dq, void* dk, void* dv, float* dg,
-                     void* dbeta, float* dh0, float* dA_log, float* ddt_bias, int B, int T,
-                     int H, int HV, int K, int V, int qkv_dtype, int beta_dtype, float scale,
-                     int chunk_size, void* workspace, size_t workspace_bytes,
-                     int32_t* dev_status, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_chunk_bwd_ex (mode BWD_FULL or BWD_FROM_SAVED) or its training forward (BWD_FORWARD:
+// o and final_state are written, the gradient pointers are unused)
+int chunk_bwd_ex_impl(int mode, const void* q, const void* k, const void* v, const void* g, int gate,
+                      const float* A_log, const float* dt_bias, int has_lower_bound,
+                      float lower_bound, const void* beta, int preprocess,
+                      const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                      float* final_state, const void* dout, const float* dht, void* dq, void* dk,
+                      void* dv, float* dg, void* dbeta, float* dh0, float* dA_log, float* ddt_bias,
+                      int B, int T, int H, int HV, int K, int V, int qkv_dtype, int beta_dtype,
+                      float scale, int chunk_size, void* workspace, size_t workspace_bytes,
+                      int32_t* dev_status, hipStream_t stream) {
     clear_error();
+    const bool fwd = mode == kda::BWD_FORWARD;
     int rc = check_common(q, k, v, static_cast<const float*>(g), beta, initial_state, cu_seqlens, N,
-                          dv, dh0, B, T, H, HV, K, V, qkv_dtype, beta_dtype);
+                          fwd ? o : dv, fwd ? final_state : dh0, B, T, H, HV, K, V, qkv_dtype, beta_dtype);
     if (rc != KDA_OK) return rc;
     kda::InputSpec in;
     const bool nonempty = (long long)B * T > 0;
     rc = make_input_spec(g, gate, A_log, dt_bias, has_lower_bound, lower_bound, preprocess, nonempty, &in);
     if (rc != KDA_OK) return rc;
-    if (nonempty && (!dout || !dq || !dk || !dv || !dg || !dbeta))
-        return fail(KDA_ERR_NULL, "do, dq, dk, dv, dg and dbeta must be non-NULL");
-    if (gate != KDA_GATE_LOG2 && nonempty && !dA_log)
-        return fail(KDA_ERR_NULL, "dA_log must be non-NULL with a raw gate");
-    if (gate != KDA_GATE_LOG2 && dt_bias && nonempty && !ddt_bias)
-        return fail(KDA_ERR_NULL, "ddt_bias must be non-NULL when dt_bias is given");
-    if (!aligned16(dht) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
-        !aligned16(dg) || !aligned16(dbeta) || !aligned16(dA_log) || !aligned16(ddt_bias))
-        return fail(KDA_ERR_SHAPE, "dht, do, dq, dk, dg, dbeta, dA_log and ddt_bias must be 16-byte aligned");
+    if (fwd) {
+        if (nonempty && !o) return fail(KDA_ERR_NULL, "o must be non-NULL");
+    } else {
+        if (nonempty && (!dout || !dq || !dk || !dv || !dg || !dbeta))
+            return fail(KDA_ERR_NULL, "do, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (gate != KDA_GATE_LOG2 && nonempty && !dA_log)
+            return fail(KDA_ERR_NULL, "dA_log must be non-NULL with a raw gate");
+        if (gate != KDA_GATE_LOG2 && dt_bias && nonempty && !ddt_bias)
+            return fail(KDA_ERR_NULL, "ddt_bias must be non-NULL when dt_bias is given");
+        if (!aligned16(dht) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+            !aligned16(dg) || !aligned16(dbeta) || !aligned16(dA_log) || !aligned16(ddt_bias))
+            return fail(KDA_ERR_SHAPE, "dht, do, dq, dk, dg, dbeta, dA_log and ddt_bias must be 16-byte aligned");
+    }
     if (chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64, got %d", chunk_size);
     if (K != 64 && K != 128)
@@ -303,6 +314,9 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
     a.scale = scale == 0.0f ? 1.0f / sqrtf((float)K) : scale;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.dev_status = dev_status; a.stream = stream;
+    a.mode = mode;
+    a.fwd_o = o;
+    a.fwd_final_state = final_state;
     x.g = g;
     x.gate_bf16 = gate == KDA_GATE_RAW_BF16 ? 1 : 0;
     x.in = in;
@@ -312,6 +326,58 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
     if (err != hipSuccess)
         return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g, int gate,
+                     const float* A_log, const float* dt_bias, int has_lower_bound,
+                     float lower_bound, const void* beta, int preprocess,
+                     const float* initial_state, const int32_t* cu_seqlens, int N,
+                     const void* dout, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                     void* dbeta, float* dh0, float* dA_log, float* ddt_bias, int B, int T,
+                     int H, int HV, int K, int V, int qkv_dtype, int beta_dtype, float scale,
+                     int chunk_size, void* workspace, size_t workspace_bytes,
+                     int32_t* dev_status, hipStream_t stream) {
+    return chunk_bwd_ex_impl(kda::BWD_FULL, q, k, v, g, gate, A_log, dt_bias, has_lower_bound,
+                             lower_bound, beta, preprocess, initial_state, cu_seqlens, N, nullptr,
+                             nullptr, dout, dht, dq, dk, dv, dg, dbeta, dh0, dA_log, ddt_bias, B, T,
+                             H, HV, K, V, qkv_dtype, beta_dtype, scale, chunk_size, workspace,
+                             workspace_bytes, dev_status, stream);
+}
+
+int kda_chunk_bwd_ex_saved(const void* q, const void* k, const void* v, const void* g, int gate,
+                           const float* A_log, const float* dt_bias, int has_lower_bound,
+                           float lower_bound, const void* beta, int preprocess,
+                           const float* initial_state, const int32_t* cu_seqlens, int N,
+                           const void* dout, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                           void* dbeta, float* dh0, float* dA_log, float* ddt_bias, int B, int T,
+                           int H, int HV, int K, int V, int qkv_dtype, int beta_dtype, float scale,
+                           int chunk_size, void* workspace, size_t workspace_bytes,
+                           int32_t* dev_status, hipStream_t stream) {
+    return chunk_bwd_ex_impl(kda::BWD_FROM_SAVED, q, k, v, g, gate, A_log, dt_bias, has_lower_bound,
+                             lower_bound, beta, preprocess, initial_state, cu_seqlens, N, nullptr,
+                             nullptr, dout, dht, dq, dk, dv, dg, dbeta, dh0, dA_log, ddt_bias, B, T,
+                             H, HV, K, V, qkv_dtype, beta_dtype, scale, chunk_size, workspace,
+                             workspace_bytes, dev_status, stream);
+}
+
+int kda_chunk_fwd_ex_train(const void* q, const void* k, const void* v, const void* g, int gate,
+                           const float* A_log, const float* dt_bias, int has_lower_bound,
+                           float lower_bound, const void* beta, int preprocess,
+                           const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                           float* final_state, int B, int T, int H, int HV, int K, int V,
+                           int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                           hipStream_t stream) {
+    return chunk_bwd_ex_impl(kda::BWD_FORWARD, q, k, v, g, gate, A_log, dt_bias, has_lower_bound,
+                             lower_bound, beta, preprocess, initial_state, cu_seqlens, N, o,
+                             final_state, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, nullptr, nullptr, nullptr, B, T, H, HV, K, V, qkv_dtype,
+                             beta_dtype, scale, chunk_size, workspace, workspace_bytes, dev_status,
+                             stream);
 }
 
 const char* kda_last_error(void) { return g_last_error; }

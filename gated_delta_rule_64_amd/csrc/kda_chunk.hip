@@ -1059,7 +1059,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_bf16_kernel(IntraParams p) 
         // selection products give 4 consecutive rows per lane, the lane swaps 8
         split8(xg, hi8, lo8);
         // (with the fp8 encode, the unrolled pair made the kernel spill)
-#pragma unroll (LO8 ? 1 : 2)
+        constexpr int PART_UNROLL = LO8 ? 1 : 2;
+#pragma unroll PART_UNROLL
         for (int part = 0; part < 2; ++part) {
             const bf16x8 a = part ? lo8 : hi8;
             const f32x4 x0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, eye_frag(lane, 0), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);

@@ -1820,7 +1820,7 @@ hipError_t launch_bwd_ex_k(const ChunkBwdExArgs& x, const ChunkBwdExLayout& L) {
     }
     c.skip_reduce = true;
     err = launch_chunk_bwd(c, L.core);
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || a.mode == BWD_FORWARD) return err;   // a training forward ends there
 
     PostParams q;
     q.q = a.q; q.k = a.k; q.g = x.g; q.beta = a.beta; q.in = x.in; q.gate_bf16 = x.gate_bf16;

@@ -294,6 +294,31 @@ int kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
                      int chunk_size, void* workspace, size_t workspace_bytes,
                      int32_t* dev_status, hipStream_t stream);
 
+/*
+ * kda_chunk_fwd_train with the options of kda_chunk_fwd_ex (the same g, gate, A_log,
+ * dt_bias, has_lower_bound, lower_bound, beta and preprocess arguments and rules), and
+ * kda_chunk_bwd_ex from its workspace (at least kda_chunk_bwd_ex_workspace_bytes bytes):
+ * the same arguments and results as kda_chunk_bwd_ex, without the forward recompute.
+ * Everything else as kda_chunk_fwd_train and kda_chunk_bwd_saved.
+ */
+int kda_chunk_fwd_ex_train(const void* q, const void* k, const void* v, const void* g, int gate,
+                           const float* A_log, const float* dt_bias, int has_lower_bound,
+                           float lower_bound, const void* beta, int preprocess,
+                           const float* initial_state, const int32_t* cu_seqlens, int N, void* o,
+                           float* final_state, int B, int T, int H, int HV, int K, int V,
+                           int qkv_dtype, int beta_dtype, float scale, int chunk_size,
+                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                           hipStream_t stream);
+int kda_chunk_bwd_ex_saved(const void* q, const void* k, const void* v, const void* g, int gate,
+                           const float* A_log, const float* dt_bias, int has_lower_bound,
+                           float lower_bound, const void* beta, int preprocess,
+                           const float* initial_state, const int32_t* cu_seqlens, int N,
+                           const void* dout, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                           void* dbeta, float* dh0, float* dA_log, float* ddt_bias, int B, int T,
+                           int H, int HV, int K, int V, int qkv_dtype, int beta_dtype, float scale,
+                           int chunk_size, void* workspace, size_t workspace_bytes,
+                           int32_t* dev_status, hipStream_t stream);
+
 /* Workspace bytes kda_chunk_bwd_ex needs; 0 for invalid sizes. */
 size_t kda_chunk_bwd_ex_workspace_bytes(int B, int T, int H, int HV, int K, int V, int N,
                                         int packed, int qkv_dtype);

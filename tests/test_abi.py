@@ -365,6 +365,78 @@ def test_train_forward_specific_rejects(lib):
     assert lib.kda_last_error().decode() == ""
 
 
+def _bwd_ex(lib, fn="kda_chunk_bwd_ex", **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gate=0, A=None, dt=None, hlb=0, lb=0.0, beta=FAKE,
+             pre=0, h0=None, cu=None, N=1, do=FAKE, dht=None, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE,
+             db=FAKE, dh0=None, dA=None, ddt=None, B=1, T=64, H=2, HV=2, K=128, V=128, qd=1, bd=1,
+             scale=0.0, cs=64, ws=FAKE, wsb=1 << 40, st=None, stream=None)
+    a.update(kw)
+    return getattr(lib, fn)(a["q"], a["k"], a["v"], a["g"], a["gate"], a["A"], a["dt"], a["hlb"],
+                            a["lb"], a["beta"], a["pre"], a["h0"], a["cu"], a["N"], a["do"], a["dht"],
+                            a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dh0"], a["dA"], a["ddt"],
+                            a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["qd"], a["bd"],
+                            a["scale"], a["cs"], a["ws"], a["wsb"], a["st"], a["stream"])
+
+
+def _train_ex(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gate=0, A=None, dt=None, hlb=0, lb=0.0, beta=FAKE,
+             pre=0, h0=None, cu=None, N=1, o=FAKE, ht=None, B=1, T=64, H=2, HV=2, K=128, V=128,
+             qd=1, bd=1, scale=0.0, cs=64, ws=FAKE, wsb=1 << 40, st=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_ex_train(a["q"], a["k"], a["v"], a["g"], a["gate"], a["A"], a["dt"],
+                                      a["hlb"], a["lb"], a["beta"], a["pre"], a["h0"], a["cu"], a["N"],
+                                      a["o"], a["ht"], a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"],
+                                      a["qd"], a["bd"], a["scale"], a["cs"], a["ws"], a["wsb"],
+                                      a["st"], a["stream"])
+
+
+@pytest.mark.parametrize("call", ["kda_chunk_bwd_ex", "kda_chunk_bwd_ex_saved", "kda_chunk_fwd_ex_train"])
+@pytest.mark.parametrize("name,kw,code", CASES, ids=[c[0] for c in CASES])
+def test_bwd_ex_and_train_ex_reject_common(lib, name, kw, code, call):
+    f = _train_ex if call == "kda_chunk_fwd_ex_train" else (lambda l, **k: _bwd_ex(l, call, **k))
+    assert f(lib, **kw) == code
+    assert lib.kda_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("fn", ["kda_chunk_bwd_ex", "kda_chunk_bwd_ex_saved"])
+def test_bwd_ex_specific_rejects(lib, fn):
+    for out in ("do", "dq", "dk", "dv", "dg", "db"):
+        assert _bwd_ex(lib, fn, **{out: None}) == -1, out
+    raw = dict(gate=2, A=FAKE, dA=FAKE)
+    assert _bwd_ex(lib, fn, **dict(raw, dA=None)) == -1           # dA_log with a raw gate
+    assert _bwd_ex(lib, fn, **dict(raw, dt=FAKE)) == -1           # ddt_bias with dt_bias
+    assert _bwd_ex(lib, fn, **dict(raw, dt=FAKE, ddt=FAKE + 4)) == -2
+    assert _bwd_ex(lib, fn, gate=3) == -7
+    assert _bwd_ex(lib, fn, pre=8) == -7
+    assert _bwd_ex(lib, fn, cs=32) == -4
+    assert _bwd_ex(lib, fn, K=96) == -4
+    assert _bwd_ex(lib, fn, ws=None) == -5
+    assert _bwd_ex(lib, fn, wsb=16) == -5
+    assert _bwd_ex(lib, fn, ws=FAKE + 16) == -5
+    assert _bwd_ex(lib, fn, cu=FAKE, N=0, T=0, **dict(raw, dt=FAKE, ddt=FAKE, pre=15)) == 0
+    assert lib.kda_last_error().decode() == ""
+
+
+def test_train_ex_forward_specific_rejects(lib):
+    """The fused-option training forward takes kda_chunk_bwd_ex's workspace and needs o;
+    no gradient outputs are asked for."""
+    B, T, H, HV, K, V = 1, 64, 2, 2, 128, 128
+    need = lib.kda_chunk_bwd_ex_workspace_bytes(B, T, H, HV, K, V, B, 0, 1)
+    assert need > lib.kda_chunk_bwd_workspace_bytes(B, T, H, HV, K, V, B, 0, 1)
+    assert _train_ex(lib, o=None) == -1
+    assert _train_ex(lib, o=FAKE + 4) == -2
+    assert _train_ex(lib, ht=FAKE + 4) == -2
+    assert _train_ex(lib, gate=3) == -7
+    assert _train_ex(lib, gate=2, A=None) == -1
+    assert _train_ex(lib, cs=32) == -4
+    assert _train_ex(lib, ws=None) == -5
+    assert _train_ex(lib, wsb=need - 1) == -5
+    assert b"need %d" % need in lib.kda_last_error()
+    ok = dict(gate=2, A=FAKE, dt=FAKE, hlb=1, lb=-5.0, pre=15)
+    assert _train_ex(lib, cu=FAKE, N=0, T=0, **ok) == 0
+    assert lib.kda_last_error().decode() == ""
+
+
 def test_bwd_workspace_bytes(lib):
     """The forward's schedule and records (in the recompute's layout), then per (value
     head, chunk) fp32 checkpoints, reverse-scan operands and intermediates, then

@@ -1194,6 +1194,48 @@ def test_chunk_bwd_ex(case):
         check(name, x, np.asarray(y).reshape(tuple(x.shape)), dtype)
 
 
+@pytest.mark.parametrize("case", BWD_EX, ids=lambda c: f"gate{int(c[0])}_lb{c[1]}_q{int(c[2])}k{int(c[3])}_sig{int(c[4])}{int(c[5])}_{str(c[6])[6:]}")
+def test_chunk_train_ex_forward_and_saved_backward(case):
+    """The training split with the fused options: the forward's o and final state against
+    the composed oracle and kda_chunk_fwd_ex; the backward from its workspace bit for bit
+    equal to kda_chunk_bwd_ex's, twice in a row from the same workspace."""
+    import gated_delta_rule_64_amd as kda
+    raw, bound, lq, lk, sig, neg, dtype = case
+    d = small(1, 200, 2, 4, 128, 128, dtype, seed=90)
+    r = _raw_inputs(d, 91, lq, lk, sig, zero_rows=False, span=0.5)
+    g_raw = A_log = dt_bias = None
+    if raw:
+        g_raw, A_log, dt_bias = _gate_params(1, 200, 4, 128, torch.bfloat16 if dtype == torch.bfloat16 else torch.float32, seed=92)
+    opts = dict(use_gate_in_kernel=raw, A_log=A_log, dt_bias=dt_bias, lower_bound=bound, l2norm_q=lq,
+                l2norm_k=lk, use_beta_sigmoid_in_kernel=sig, allow_neg_eigval=neg)
+    g_in = g_raw if raw else r["g"]
+    log(f"[train ex] gate raw={raw} bound={bound} l2norm q={lq} k={lk} sigmoid={sig} neg={neg} {dtype}")
+    o, ht, ws = kda.kda_chunk_fwd_ex_train(r["q"], r["k"], r["v"], g_in, r["beta"], r["initial_state"],
+                                           None, output_final_state=True, **opts)
+    o_f, ht_f = kda.kda_chunk_fwd_ex(r["q"], r["k"], r["v"], g_in, r["beta"], r["initial_state"], None,
+                                     output_final_state=True, **opts)
+    torch.cuda.synchronize()
+    g2 = oracle.gate_activation(g_raw, A_log, dt_bias, bound) if raw else None
+    o_ref, ht_ref = _pre_oracle(r, lq, lk, sig, neg, g2=g2)
+    check("o", o, o_ref, dtype)
+    check("final_state", ht, ht_ref, dtype)
+    check("o (vs kda_chunk_fwd_ex)", o, to64(o_f), dtype, want_rounded=True)
+    check("final_state (vs kda_chunk_fwd_ex)", ht, to64(ht_f), dtype)
+    do, dht = _bwd_inputs(d, 93)
+    full = kda.kda_chunk_bwd_ex(r["q"], r["k"], r["v"], g_in, r["beta"], do, r["initial_state"], None,
+                                dht, **opts)
+    for rep in range(2):
+        saved = kda.kda_chunk_bwd_ex_saved(r["q"], r["k"], r["v"], g_in, r["beta"], do, ws,
+                                           r["initial_state"], None, dht, **opts)
+        torch.cuda.synchronize()
+        for name, x, y in zip(["dq", "dk", "dv", "dg", "dbeta", "dh0", "dA_log", "ddt_bias"], saved, full):
+            if y is None:
+                assert x is None, name
+                continue
+            assert torch.equal(x, y), f"{name} differs from kda_chunk_bwd_ex's (call {rep})"
+    log("  saved backward == full backward bitwise (two calls)")
+
+
 # ------------------------------------------------------------------------------------
 # the in-place timing entry point: NULL event slots are skipped, results unchanged
 # ------------------------------------------------------------------------------------
