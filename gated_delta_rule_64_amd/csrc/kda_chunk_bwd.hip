@@ -24,7 +24,10 @@
 //   dbeta = rowsum(Gu v) + rowsum(Gw kd) + rowsum(dL M),
 //   dT = dv' (beta v)^T + dw (beta kd)^T, dL = -(T^T dT T^T) strictly lower, dM = beta dL
 //   and the pair terms of Aqk and M with one one-sided 2^(Gamma_r - Gamma_s) <= 1 each.
-// All of it in fp32 (fp32 matrix cores for the dense products).
+// All of it in fp32 arithmetic. With bf16 inputs the dense products of the prep, reverse
+// scan, state and WY stages run on the bf16 matrix cores, each fp32 operand carried as
+// a hi + lo bf16 pair (three products per step); the pair terms and the fp32-input
+// path use the fp32 matrix cores.
 #include <type_traits>
 
 #include "kda_chunk_common.h"
@@ -262,6 +265,29 @@ __device__ __forceinline__ void gate_rows_lds(float* X, int ld, int len, const I
             X[r * ld + d] = gate_log2_from_raw(x, amp, in.has_lower_bound, lb2);
         }
     }
+}
+
+// In-place cumulative sum down the C rows of a C x K fp32 tile in LDS (X[r * ld + d]):
+// NTH threads, each a run of C / (NTH / K) rows of one column; the runs' totals go
+// through `tot` (NTH floats) and each run adds those above it. The caller's writes of X
+// must be visible (a barrier) before the call; one barrier inside, none at the end.
+template <int K, int NTH>
+__device__ __forceinline__ void cumsum_rows_lds(float* X, int ld, float* tot, int tid) {
+    constexpr int NS = NTH / K, RL = C / NS;
+    static_assert(NTH % K == 0 && C % NS == 0, "runs must tile the chunk");
+    const int d = tid % K, s = tid / K;
+    float x[RL];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < RL; ++i) x[i] = X[(s * RL + i) * ld + d];
+#pragma unroll
+    for (int i = 0; i < RL; ++i) { acc += x[i]; x[i] = acc; }
+    tot[s * K + d] = acc;
+    __syncthreads();
+    float off = 0.f;
+    for (int j = 0; j < s; ++j) off += tot[j * K + d];
+#pragma unroll
+    for (int i = 0; i < RL; ++i) X[(s * RL + i) * ld + d] = x[i] + off;
 }
 
 // rows of g (log2 decay, or the raw gate input by the options) into LDS
@@ -1294,6 +1320,320 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------
+// The same backward of the WY inverse for bf16 inputs, its dense products on the bf16
+// matrix cores. Each fp32 operand is split once into a hi + lo bf16 pair in LDS, laid
+// out so that a lane's eight contraction values are one 16-byte read: T^T (for
+// T^T dv', T^T dw, T^T dT) and T (for X T^T), dv' and dw both as rows (dT) and
+// transposed (T^T dv', T^T dw), kd, v (a bf16 input, exact). A product is then
+// hi*hi + lo*hi + hi*lo per 32-wide contraction step (hi*hi + lo*hi against v, and beta
+// applied to the finished dT column). Sixteen waves, the tiles dealt as in the fp32
+// kernel; the row sums for dbeta in per-wave partials.
+// ------------------------------------------------------------------------------------
+// An fp32 [C][W] tile (row stride W) into registers, lane l of each wave taking row l:
+// the transposed bf16 stores below then put a wave's 64 lanes on 32 distinct banks
+// (lanes along a row would share four).
+template <int W, int NTH>
+struct ColLoad {
+    static constexpr int WAVES = NTH / 64, N = C * W / (4 * NTH);
+    static_assert(N * 4 * NTH == C * W, "whole vectors per thread");
+    f32x4 x[N];
+    __device__ __forceinline__ static int col(int tid, int i) { return 4 * ((tid >> 6) + WAVES * i); }
+    __device__ __forceinline__ void load(const float* src, int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = *reinterpret_cast<const f32x4*>(src + (tid & 63) * W + col(tid, i));
+    }
+};
+
+// That tile split into hi + lo bf16 rows (row r at r * ldr) and transposed rows (column
+// c at c * ldt).
+template <int W, int NTH>
+__device__ __forceinline__ void store_split_rt(const ColLoad<W, NTH>& t, __bf16* rh, __bf16* rl, int ldr,
+                                              __bf16* th, __bf16* tl, int ldt, int tid) {
+#pragma unroll
+    for (int i = 0; i < ColLoad<W, NTH>::N; ++i) {
+        const int r = tid & 63, c4 = ColLoad<W, NTH>::col(tid, i);
+        bf16x4 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = (__bf16)t.x[i][e];
+            l[e] = (__bf16)(t.x[i][e] - (float)h[e]);
+            th[(c4 + e) * ldt + r] = h[e];
+            tl[(c4 + e) * ldt + r] = l[e];
+        }
+        *reinterpret_cast<bf16x4*>(rh + r * ldr + c4) = h;
+        *reinterpret_cast<bf16x4*>(rl + r * ldr + c4) = l;
+    }
+}
+
+// The 16x16x32 operand fragment of row `row` at contraction offset k (k = k0 + 8 lq).
+__device__ __forceinline__ bf16x8 wy_frag(const __bf16* t, int row, int ld, int k) {
+    return *reinterpret_cast<const bf16x8*>(t + row * ld + k);
+}
+
+template <int K, int V, typename TB>
+__global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p) {
+    constexpr int NTH = WY_THREADS, NW = NTH / 64;
+    constexpr int MKV = K > V ? K : V;
+    // bf16 row strides: 144 or 272 bytes, so the 16 rows of a fragment read start in 16
+    // distinct four-bank groups
+    constexpr int TP = C + 8, KP = K + 8, VP = V + 8, XP = MKV + 8, LK = K + 1;
+    constexpr int A_ELEMS = 2 * C * XP, B_ELEMS = 4 * C * TP;
+    static_assert(NTH == C * C / 4 && NTH / 64 == C / 4, "one float4 of T per thread");
+    static_assert(2 * MKV * TP <= B_ELEMS, "transposed operand fits region B");
+    static_assert(C * LK * 2 <= A_ELEMS && C * LK * 2 <= B_ELEMS, "fp32 staging fits regions A and B");
+    static_assert(NW == 16, "one 16x16 tile of a 64x64 product per wave");
+    typedef GsLayout<K> GL;
+    typedef WyLayout<K> WL;
+    typedef Mma<__bf16> M;
+    __shared__ __attribute__((aligned(16))) __bf16 TtH[C * TP], TtL[C * TP];   // T^T
+    __shared__ __attribute__((aligned(16))) __bf16 kdH[C * KP], kdL[C * KP];   // kd = k 2^Gamma
+    __shared__ __attribute__((aligned(16))) __bf16 vB[C * VP];                // v
+    // region A: Gamma (fp32), then dv' rows, then dw rows (hi, lo), then X = T^T dT
+    // region B: k (fp32), then dv'^T, then dw^T (hi, lo), then T rows and dT^T
+    __shared__ __attribute__((aligned(16))) __bf16 regA[A_ELEMS];
+    __shared__ __attribute__((aligned(16))) __bf16 regB[B_ELEMS];
+    __shared__ float bL[C];
+    __shared__ float dbP[NW][C];     // each wave's row sums for dbeta (added in wave order at the end)
+    __shared__ float runT[NTH];      // run totals of the gate cumsum
+    float* GS = reinterpret_cast<float*>(regA);
+    float* kS = reinterpret_cast<float*>(regB);
+    __bf16 *AH = regA, *AL = regA + C * XP;
+    __bf16 *BtH = regB, *BtL = regB + MKV * TP;
+    __bf16 *ThH = regB, *ThL = regB + C * TP, *dTH = regB + 2 * C * TP, *dTL = regB + 3 * C * TP;
+    __bf16 *XH = regA, *XLo = regA + C * TP;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tI = wave >> 2, tJ = wave & 3;   // this wave's tile of the 64 x 64 products
+    int c, hv;
+    int2 pos;
+    if (!bwd_chunk(p, c, hv, pos)) return;
+    const int h = hv / (p.HV / p.H);
+    const int len = pos.y;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const __bf16* kin = reinterpret_cast<const __bf16*>(p.k);
+    const __bf16* vin = reinterpret_cast<const __bf16*>(p.v);
+    const TB* bin = reinterpret_cast<const TB*>(p.beta);
+    const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
+    float* wyC = p.wy + ci * (size_t)WL::FLOATS;
+
+    // ---- loads: k, v, the gate and beta first (the stages right after need them), then T,
+    // dv' and M at this lane's dL elements into registers (memory counters complete in
+    // order, so those land while the gate cumsum and kd run) ----
+    RowLoad<C, K, __bf16, NTH> lk_;
+    RowLoad<C, V, __bf16, NTH> lv_;
+    lk_.load(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid);
+    lv_.load(vin + ((size_t)pos.x * p.HV + hv) * V, (size_t)p.HV * V, len, tid);
+    stage_gate<K, NTH>(p, pos, hv, GS, LK, tid);
+    lk_.store(len, kS, LK, tid);
+#pragma unroll
+    for (int i = 0; i < RowLoad<C, V, __bf16, NTH>::N; ++i) {
+        const int q = tid + NTH * i, r = q / (V / 4), c4 = 4 * (q % (V / 4));
+        *reinterpret_cast<bf16x4*>(vB + r * VP + c4) = r < len ? lv_.x[i] : bf16x4{};
+    }
+    if (tid < C) {
+        float b = tid < len ? to_f32(bin[(size_t)(pos.x + tid) * p.HV + hv]) : 0.f;
+        if (p.in.beta_sig != 0.f && tid < len) b = beta_from_logit(b, p.in.beta_sig);
+        bL[tid] = b;
+    }
+    // T[tr][tc .. tc + 3], lane l of each wave taking row l
+    const int tr = tid & 63, tc = 4 * (tid >> 6);
+    const f32x4 tq = *reinterpret_cast<const f32x4*>(p.mt + ((size_t)p.NCmax * p.HV + ci) * (C * C) + tr * C + tc);
+    ColLoad<V, NTH> ldv_;
+    ldv_.load(p.dvn + ci * (size_t)C * V, tid);
+    float mR[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mR[r] = p.mt[ci * (size_t)(C * C) + (16 * tI + 4 * lq + r) * C + 16 * tJ + lr];
+    for (int e = tid; e < NW * C; e += NTH) dbP[e / C][e % C] = 0.f;
+    __syncthreads();
+    if (p.in.l2norm_k) l2norm_rows_lds<K>(kS, LK, tid);
+    if (p.in.gate_mode != GATE_LOG2) gate_rows_lds<K, NTH>(GS, LK, len, p.in, hv, tid);
+    __syncthreads();
+    cumsum_rows_lds<K, NTH>(GS, LK, runT, tid);
+    __syncthreads();
+    // kd = k 2^Gamma and T^T, split
+    for (int e = tid; e < C * K; e += NTH) {
+        const int r = e / K, d = e % K;
+        const float x = kS[r * LK + d] * exp2_fast(GS[r * LK + d]);
+        const __bf16 hx = (__bf16)x;
+        kdH[r * KP + d] = hx;
+        kdL[r * KP + d] = (__bf16)(x - (float)hx);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const __bf16 hx = (__bf16)tq[e];
+        TtH[(tc + e) * TP + tr] = hx;
+        TtL[(tc + e) * TP + tr] = (__bf16)(tq[e] - (float)hx);
+    }
+    __syncthreads();
+    store_split_rt<V, NTH>(ldv_, AH, AL, XP, BtH, BtL, TP, tid);
+    // dw (for the key side) is loaded now and lands during the value side
+    ColLoad<K, NTH> ldw_;
+    ldw_.load(gsC + GL::DW, tid);
+    __syncthreads();
+
+    auto add_rows = [&](int row0, const float (&x)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float y = sum16(x[r]);
+            if (lr == 0) dbP[wave][row0 + 4 * lq + r] += y;
+        }
+    };
+    // T^T X for X = dv' or dw held transposed in region B: tile (sb, nt)
+    auto tt_prod = [&](int sb, int nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32) {
+            const int k = k0 + 8 * lq;
+            const bf16x8 ah = wy_frag(TtH, 16 * sb + lr, TP, k), al = wy_frag(TtL, 16 * sb + lr, TP, k);
+            const bf16x8 bh = wy_frag(BtH, 16 * nt + lr, TP, k), bl = wy_frag(BtL, 16 * nt + lr, TP, k);
+            acc = M::mma(ah, bh, acc);
+            acc = M::mma(al, bh, acc);
+            acc = M::mma(ah, bl, acc);
+        }
+        return acc;
+    };
+    f32x4 dT = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- value side: dv = beta T^T dv', dbeta += rowsum((T^T dv') v), dT = dv' (beta v)^T ----
+    __bf16* dvout = reinterpret_cast<__bf16*>(p.dv);
+    for (int t = wave; t < 4 * (V / 16); t += NW) {
+        const int sb = t / (V / 16), nt = t % (V / 16);
+        const f32x4 acc = tt_prod(sb, nt);
+        float db[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int s = 16 * sb + 4 * lq + r, vv = 16 * nt + lr;
+            db[r] = acc[r] * (float)vB[s * VP + vv];
+            if (s < len) dvout[((size_t)(pos.x + s) * p.HV + hv) * V + vv] = (__bf16)(bL[s] * acc[r]);
+        }
+        add_rows(16 * sb, db);
+    }
+    if (tJ <= tI) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < V; k0 += 32) {
+            const int k = k0 + 8 * lq;
+            const bf16x8 ah = wy_frag(AH, 16 * tI + lr, XP, k), al = wy_frag(AL, 16 * tI + lr, XP, k);
+            const bf16x8 b = wy_frag(vB, 16 * tJ + lr, VP, k);
+            acc = M::mma(ah, b, acc);
+            acc = M::mma(al, b, acc);
+        }
+        const float bj = bL[16 * tJ + lr];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dT[r] = bj * acc[r];
+    }
+    __syncthreads();
+    store_split_rt<K, NTH>(ldw_, AH, AL, XP, BtH, BtL, TP, tid);
+    __syncthreads();
+    // ---- key side: dkd = beta T^T dw, dbeta += rowsum((T^T dw) kd), dT += dw (beta kd)^T ----
+    for (int t = wave; t < 4 * (K / 16); t += NW) {
+        const int sb = t / (K / 16), nt = t % (K / 16);
+        const f32x4 acc = tt_prod(sb, nt);
+        float db[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int s = 16 * sb + 4 * lq + r, d = 16 * nt + lr;
+            db[r] = acc[r] * ((float)kdH[s * KP + d] + (float)kdL[s * KP + d]);
+            wyC[WL::DKD + s * K + d] = bL[s] * acc[r];
+        }
+        add_rows(16 * sb, db);
+    }
+    if (tJ <= tI) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += 32) {
+            const int k = k0 + 8 * lq;
+            const bf16x8 ah = wy_frag(AH, 16 * tI + lr, XP, k), al = wy_frag(AL, 16 * tI + lr, XP, k);
+            const bf16x8 bh = wy_frag(kdH, 16 * tJ + lr, KP, k), bl = wy_frag(kdL, 16 * tJ + lr, KP, k);
+            acc = M::mma(ah, bh, acc);
+            acc = M::mma(al, bh, acc);
+            acc = M::mma(ah, bl, acc);
+        }
+        const float bj = bL[16 * tJ + lr];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dT[r] = fmaf(bj, acc[r], dT[r]);
+    }
+    __syncthreads();
+    // ---- dT (strictly lower) transposed and T as rows, split, into region B ----
+    {
+        bf16x4 hv4, lv4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * tI + 4 * lq + r, s = 16 * tJ + lr;
+            const float x = (tJ <= tI && s < row) ? dT[r] : 0.f;
+            hv4[r] = (__bf16)x;
+            lv4[r] = (__bf16)(x - (float)hv4[r]);
+        }
+        const int s = 16 * tJ + lr;
+        *reinterpret_cast<bf16x4*>(dTH + s * TP + 16 * tI + 4 * lq) = hv4;
+        *reinterpret_cast<bf16x4*>(dTL + s * TP + 16 * tI + 4 * lq) = lv4;
+        bf16x4 th, tl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            th[e] = (__bf16)tq[e];
+            tl[e] = (__bf16)(tq[e] - (float)th[e]);
+        }
+        *reinterpret_cast<bf16x4*>(ThH + tr * TP + tc) = th;
+        *reinterpret_cast<bf16x4*>(ThL + tr * TP + tc) = tl;
+    }
+    __syncthreads();
+    // ---- X = T^T dT (all tiles), split into region A ----
+    {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32) {
+            const int k = k0 + 8 * lq;
+            const bf16x8 ah = wy_frag(TtH, 16 * tI + lr, TP, k), al = wy_frag(TtL, 16 * tI + lr, TP, k);
+            const bf16x8 bh = wy_frag(dTH, 16 * tJ + lr, TP, k), bl = wy_frag(dTL, 16 * tJ + lr, TP, k);
+            x = M::mma(ah, bh, x);
+            x = M::mma(al, bh, x);
+            x = M::mma(ah, bl, x);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = (16 * tI + 4 * lq + r) * TP + 16 * tJ + lr;
+            const __bf16 hx = (__bf16)x[r];
+            XH[e] = hx;
+            XLo[e] = (__bf16)(x[r] - (float)hx);
+        }
+    }
+    __syncthreads();
+    // ---- dL = -(X T^T) strictly lower; dM = beta dL, dbeta += rowsum(dL M) ----
+    {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (tJ <= tI) {
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += 32) {
+                const int k = k0 + 8 * lq;
+                const bf16x8 ah = wy_frag(XH, 16 * tI + lr, TP, k), al = wy_frag(XLo, 16 * tI + lr, TP, k);
+                const bf16x8 bh = wy_frag(ThH, 16 * tJ + lr, TP, k), bl = wy_frag(ThL, 16 * tJ + lr, TP, k);
+                x = M::mma(ah, bh, x);
+                x = M::mma(al, bh, x);
+                x = M::mma(ah, bl, x);
+            }
+        }
+        float db[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * tI + 4 * lq + r, s = 16 * tJ + lr;
+            const float dl = (tJ <= tI && s < row) ? -x[r] : 0.f;
+            db[r] = dl * mR[r];
+            wyC[WL::DM + row * C + s] = bL[row] * dl;
+        }
+        add_rows(16 * tI, db);
+    }
+    __syncthreads();
+    if (tid < len) {
+        float db = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) db += dbP[w][tid];
+        const size_t e = (size_t)(pos.x + tid) * p.HV + hv;
+        if (p.dbeta_f32) reinterpret_cast<float*>(p.dbeta)[e] = db;
+        else reinterpret_cast<TB*>(p.dbeta)[e] = from_f32<TB>(db);
+    }
+}
+
+// ------------------------------------------------------------------------------------
 // pair terms and the elementwise ones, per (chunk, value head): dq, dk (per value head,
 // summed later) and dg (the chunk-local reverse cumsum of dGamma).
 //   row side    dq_r  = sum_(s<=r) scale dAqk[r,s] k_s e(r,s),  dkr_r = sum_(s<r) dM[r,s] k_s e(r,s)
@@ -1325,6 +1665,7 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParam
     __shared__ float dML[C * LA];    // dM (s < r)
     __shared__ float dGL[K];         // dG of the chunk end, from the state products
     __shared__ float dGP[2][K];      // each half's kg term of dG (added in a fixed order)
+    __shared__ float runT[NTH];      // run totals of the two cumsums
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = wave % (K / 16), half = wave / (K / 16);   // channel tile; row blocks 2 half, 2 half + 1
@@ -1360,11 +1701,22 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParam
     if (p.in.l2norm_k) l2norm_rows_lds<K>(kL, LK, tid - C);    // threads 64 .. 127
     if (p.in.gate_mode != GATE_LOG2) gate_rows_lds<K, NTH>(GmL, LK, len, p.in, hv, tid);
     __syncthreads();
-    if (tid < K) {
-        float acc = 0.f;
-        for (int r = 0; r < C; ++r) { acc += GmL[r * LK + tid]; GmL[r * LK + tid] = acc; }
-    }
+    cumsum_rows_lds<K, NTH>(GmL, LK, runT, tid);
     __syncthreads();
+
+    const int d = 16 * tile + lr;
+    // the state products' and the WY backward's gradients at this lane's elements (rows
+    // 16 I + 4 lq + rr of channel d), loaded now so that they land during the products
+    float dqgR[2][4], dkgR[2][4], dkdR[2][4];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = 16 * (2 * half + ib) + 4 * lq + rr;
+            dqgR[ib][rr] = gsC[GL::DQG + r * K + d];
+            dkgR[ib][rr] = gsC[GL::DKG + r * K + d];
+            dkdR[ib][rr] = wyC[WL::DKD + r * K + d];
+        }
 
     // accumulators of the wave's two row blocks I = 2 half + ib
     f32x4 aq[2], akr[2], akc[2];
@@ -1374,7 +1726,6 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParam
         akr[ib] = aq[ib];
         akc[ib] = aq[ib];
     }
-    const int d = 16 * tile + lr;
     // row side, pairs across blocks: block I against rows s < 16I, through row 16I - 1
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
@@ -1497,9 +1848,7 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParam
                 const int r = 16 * (2 * half + ib) + 4 * lq + rr;
                 const float qv = qL[r * LK + d], kv = kL[r * LK + d], gr = GmL[r * LK + d];
                 const float e1 = exp2_fast(gr), e2 = exp2_fast(Gd - gr);
-                const float dqg = gsC[GL::DQG + r * K + d];
-                const float dkg = gsC[GL::DKG + r * K + d];
-                const float dkd = wyC[WL::DKD + r * K + d];
+                const float dqg = dqgR[ib][rr], dkg = dkgR[ib][rr], dkd = dkdR[ib][rr];
                 const float dqi = aq[ib][rr], dkr = akr[ib][rr], dkc = akc[ib][rr];
                 const float dq = fmaf(sc * e1, dqg, dqi);
                 const float dk = dkr + dkc + e1 * dkd + e2 * dkg;
@@ -1524,12 +1873,27 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParam
         for (int rr = 0; rr < 4; ++rr)
             qL[(16 * (2 * half + ib) + 4 * lq + rr) * LK + d] = dgam[ib][rr];
     __syncthreads();
-    // dg = reverse cumsum of dGamma over the chunk's rows; dG joins at the last row
-    if (tid < K && len > 0) {
-        float acc = dGL[tid] + dGP[0][tid] + dGP[1][tid];
-        for (int rr = len - 1; rr >= 0; --rr) {
-            acc += qL[rr * LK + tid];
-            p.dg[((size_t)(pos.x + rr) * p.HV + hv) * K + tid] = acc;
+    // dg = reverse cumsum of dGamma over the chunk's rows (rows >= len left out); dG
+    // joins at the last row. Runs of RL rows per thread, as in the forward cumsum.
+    {
+        constexpr int NS = NTH / K, RL = C / NS;
+        const int dc = tid % K, sg = tid / K;
+        float x[RL];
+        float acc = 0.f;
+#pragma unroll
+        for (int i = RL - 1; i >= 0; --i) {
+            const int r = sg * RL + i;
+            acc += r < len ? qL[r * LK + dc] : 0.f;
+            x[i] = acc;
+        }
+        runT[sg * K + dc] = acc;
+        __syncthreads();
+        float off = dGL[dc] + dGP[0][dc] + dGP[1][dc];
+        for (int j = NS - 1; j > sg; --j) off += runT[j * K + dc];
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+            const int r = sg * RL + i;
+            if (r < len) p.dg[((size_t)(pos.x + r) * p.HV + hv) * K + dc] = x[i] + off;
         }
     }
 }
@@ -1643,7 +2007,10 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
         else
             hipLaunchKernelGGL((bwd_state_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(WY_THREADS), 0, a.stream, p);
+        if constexpr (sizeof(TIn) == 2)
+            hipLaunchKernelGGL((bwd_wy_bf16_kernel<K, V, TB>), dim3((unsigned)nchunk_items), dim3(WY_THREADS), 0, a.stream, p);
+        else
+            hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(WY_THREADS), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((bwd_pair_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(pair_threads<K>()), 0,
                            a.stream, p);
