@@ -1899,6 +1899,335 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_kernel(BwdParam
 }
 
 // ------------------------------------------------------------------------------------
+// The pair terms for bf16 inputs on the bf16 matrix cores (16x16x16: a 16-row block is
+// one contraction step). scale dAqk and dM are split once into hi + lo bf16 tiles, as
+// rows (the row side: contraction over s) and transposed (the column side: contraction
+// over r); each lane's decayed k / q operand values are split as they are formed, and a
+// product is hi*hi + lo*hi + hi*lo. q and k stay bf16 in LDS (exact) with the rows'
+// normalisation factors beside them; the tiling, the anchoring and the elementwise
+// step are those of the fp32 kernel.
+// ------------------------------------------------------------------------------------
+// 16x16x16 operand fragment: row `row`, contraction values k .. k + 3 (k = k0 + 4 lq)
+__device__ __forceinline__ bf16x4 pair_frag(const __bf16* t, int row, int k) {
+    return *reinterpret_cast<const bf16x4*>(t + row * (C + 8) + k);
+}
+__device__ __forceinline__ f32x4 mma16_3(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, f32x4 c) {
+    c = mma16(ah, bl, c);
+    c = mma16(al, bh, c);
+    return mma16(ah, bh, c);
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_bf16_kernel(BwdParams p) {
+    constexpr int NTH = pair_threads<K>(), LK = K + 1, KP = K + 8, TP = C + 8;
+    typedef GsLayout<K> GL;
+    typedef WyLayout<K> WL;
+    __shared__ __attribute__((aligned(16))) __bf16 qB[C * KP], kB[C * KP];   // q, k (bf16 inputs)
+    __shared__ float rnq[C], rnk[C];     // row normalisation factors (1 without the option)
+    __shared__ float GmL[C * LK];        // Gamma
+    // scale dAqk (s <= r) and dM (s < r): hi / lo, as rows then transposed; after the
+    // products the region holds dGamma [C][LK] fp32
+    __shared__ __attribute__((aligned(16))) __bf16 At[8 * C * TP];
+    __shared__ float dGL[K];             // dG of the chunk end, from the state products
+    __shared__ float dGP[2][K];          // each half's kg term of dG (added in a fixed order)
+    __shared__ float runT[NTH];          // run totals of the two cumsums
+    static_assert(C * LK * 4 <= 8 * C * TP * 2, "dGamma fits the operand region");
+    __bf16 *aH = At, *aL = At + C * TP, *mH = At + 2 * C * TP, *mL = At + 3 * C * TP;
+    __bf16 *atH = At + 4 * C * TP, *atL = At + 5 * C * TP, *mtH = At + 6 * C * TP, *mtL = At + 7 * C * TP;
+    float* dGam = reinterpret_cast<float*>(At);
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = wave % (K / 16), half = wave / (K / 16);   // channel tile; row blocks 2 half, 2 half + 1
+    int c, hv;
+    int2 pos;
+    if (!bwd_chunk(p, c, hv, pos)) return;
+    const int h = hv / (p.HV / p.H);
+    const int len = pos.y;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const __bf16* qin = reinterpret_cast<const __bf16*>(p.q);
+    const __bf16* kin = reinterpret_cast<const __bf16*>(p.k);
+    const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
+    const float* wyC = p.wy + ci * (size_t)WL::FLOATS;
+    const float sc = p.scale;
+
+    {
+        // q, k, dAqk and dM loads go out together, the gate is staged meanwhile
+        RowLoad<C, K, __bf16, NTH> lq_, lk_;
+        ColLoad<C, NTH> la_, lm_;
+        lq_.load(qin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid);
+        lk_.load(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid);
+        la_.load(gsC + GL::DA, tid);
+        lm_.load(wyC + WL::DM, tid);
+        stage_gate<K, NTH>(p, pos, hv, GmL, LK, tid);
+        if (tid < K) dGL[tid] = gsC[GL::DG + tid];
+#pragma unroll
+        for (int i = 0; i < RowLoad<C, K, __bf16, NTH>::N; ++i) {
+            const int q = tid + NTH * i, r = q / (K / 4), c4 = 4 * (q % (K / 4));
+            *reinterpret_cast<bf16x4*>(qB + r * KP + c4) = r < len ? lq_.x[i] : bf16x4{};
+            *reinterpret_cast<bf16x4*>(kB + r * KP + c4) = r < len ? lk_.x[i] : bf16x4{};
+        }
+#pragma unroll
+        for (int i = 0; i < ColLoad<C, NTH>::N; ++i) {
+            f32x4 x = la_.x[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] *= sc;
+            const int r = tid & 63, c4 = ColLoad<C, NTH>::col(tid, i);
+            bf16x4 hh, ll;
+            split4(x, hh, ll);
+            *reinterpret_cast<bf16x4*>(aH + r * TP + c4) = hh;
+            *reinterpret_cast<bf16x4*>(aL + r * TP + c4) = ll;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                atH[(c4 + e) * TP + r] = hh[e];
+                atL[(c4 + e) * TP + r] = ll[e];
+            }
+            split4(lm_.x[i], hh, ll);
+            *reinterpret_cast<bf16x4*>(mH + r * TP + c4) = hh;
+            *reinterpret_cast<bf16x4*>(mL + r * TP + c4) = ll;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                mtH[(c4 + e) * TP + r] = hh[e];
+                mtL[(c4 + e) * TP + r] = ll[e];
+            }
+        }
+    }
+    __syncthreads();
+    // row normalisation factors: threads 0 .. 63 the q rows, 64 .. 127 the k rows (the
+    // sum of squares in channel order, as the fp32 kernel's)
+    if (tid < 2 * C) {
+        const int r = tid & 63;
+        const bool isq = tid < C;
+        float f = 1.f;
+        if (isq ? p.in.l2norm_q : p.in.l2norm_k) {
+            const __bf16* row = (isq ? qB : kB) + r * KP;
+            float ss = 0.f;
+#pragma unroll 8
+            for (int d = 0; d < K; ++d) ss = fmaf((float)row[d], (float)row[d], ss);
+            f = l2norm_rstd(ss);
+        }
+        (isq ? rnq : rnk)[r] = f;
+    }
+    if (p.in.gate_mode != GATE_LOG2) gate_rows_lds<K, NTH>(GmL, LK, len, p.in, hv, tid);
+    __syncthreads();
+    cumsum_rows_lds<K, NTH>(GmL, LK, runT, tid);
+    __syncthreads();
+
+    const int d = 16 * tile + lr;
+    auto qval = [&](int r) { return (float)qB[r * KP + d] * rnq[r]; };
+    auto kval = [&](int r) { return (float)kB[r * KP + d] * rnk[r]; };
+    // The wave's two row blocks I = 2 half + ib one after the other: products, then the
+    // elementwise step of the block's rows. The state products' and the WY backward's
+    // gradients at a block's elements (rows 16 I + 4 lq + rr of channel d) are loaded
+    // one block ahead, so they land during the products.
+    float dgam[2][4];
+    float dgk = 0.f;
+    const float Gd = GmL[(C - 1) * LK + d];
+    float dqgR[4], dkgR[4], dkdR[4];
+    auto load_grads = [&](int I) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = 16 * I + 4 * lq + rr;
+            dqgR[rr] = gsC[GL::DQG + r * K + d];
+            dkgR[rr] = gsC[GL::DKG + r * K + d];
+            dkdR[rr] = wyC[WL::DKD + r * K + d];
+        }
+    };
+    load_grads(2 * half);
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+        const int I = 2 * half + ib;
+        f32x4 aq = {0.f, 0.f, 0.f, 0.f}, akr = aq, akc = aq;
+        // row side, pairs across blocks: block I against the blocks S < I, through row 16I - 1
+        if (I > 0) {
+            const float P = GmL[(16 * I - 1) * LK + d];
+            f32x4 yq = {0.f, 0.f, 0.f, 0.f}, yk = {0.f, 0.f, 0.f, 0.f};
+            for (int S = 0; S < I; ++S) {
+                f32x4 b;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s = 16 * S + 4 * lq + j;
+                    b[j] = kval(s) * exp2_fast(P - GmL[s * LK + d]);
+                }
+                bf16x4 bh, bl;
+                split4(b, bh, bl);
+                const int k = 16 * S + 4 * lq;
+                yq = mma16_3(pair_frag(aH, 16 * I + lr, k), pair_frag(aL, 16 * I + lr, k), bh, bl, yq);
+                yk = mma16_3(pair_frag(mH, 16 * I + lr, k), pair_frag(mL, 16 * I + lr, k), bh, bl, yk);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const float f = exp2_fast(GmL[(16 * I + 4 * lq + rr) * LK + d] - P);
+                aq[rr] = f * yq[rr];
+                akr[rr] = f * yk[rr];
+            }
+        }
+        // column side, pairs across blocks: block I against the blocks R > I, through row
+        // 16I + 15
+        if (I < 3) {
+            const float Q = GmL[(16 * I + 15) * LK + d];
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            for (int R = I + 1; R < 4; ++R) {
+                f32x4 bq, bk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * R + 4 * lq + j;
+                    const float e = exp2_fast(GmL[r * LK + d] - Q);
+                    bq[j] = qval(r) * e;
+                    bk[j] = kval(r) * e;
+                }
+                bf16x4 bqh, bql, bkh, bkl;
+                split4(bq, bqh, bql);
+                split4(bk, bkh, bkl);
+                const int k = 16 * R + 4 * lq;
+                z = mma16_3(pair_frag(atH, 16 * I + lr, k), pair_frag(atL, 16 * I + lr, k), bqh, bql, z);
+                z = mma16_3(pair_frag(mtH, 16 * I + lr, k), pair_frag(mtL, 16 * I + lr, k), bkh, bkl, z);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                akc[rr] = exp2_fast(Q - GmL[(16 * I + 4 * lq + rr) * LK + d]) * z[rr];
+        }
+        // pairs inside the block: anchored at a block boundary row on the matrix cores
+        // where the block's decay spread is at most PAIR_SPREAD, else one one-sided factor
+        // per pair (exact at any decay); pairs on the wrong side of the diagonal meet a
+        // zero dAqk / dM.
+        const float gfirst = GmL[(16 * I) * LK + d], glast = GmL[(16 * I + 15) * LK + d];
+        const bool steep = __builtin_amdgcn_ballot_w64(gfirst - glast > PAIR_SPREAD) != 0;   // wave-uniform
+        if (!steep) {
+            // row side (anchored at the block's last row), then the column side (at its
+            // first row), each operand split just before its products
+            const int row = 16 * I + lr, k = 16 * I + 4 * lq;
+            {
+                f32x4 br;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s = 16 * I + 4 * lq + j;
+                    br[j] = kval(s) * exp2_fast(glast - GmL[s * LK + d]);
+                }
+                bf16x4 bh, bl;
+                split4(br, bh, bl);
+                f32x4 yq = {0.f, 0.f, 0.f, 0.f}, yk = yq;
+                yq = mma16_3(pair_frag(aH, row, k), pair_frag(aL, row, k), bh, bl, yq);
+                yk = mma16_3(pair_frag(mH, row, k), pair_frag(mL, row, k), bh, bl, yk);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float fr = exp2_fast(GmL[(16 * I + 4 * lq + rr) * LK + d] - glast);
+                    aq[rr] = fmaf(fr, yq[rr], aq[rr]);
+                    akr[rr] = fmaf(fr, yk[rr], akr[rr]);
+                }
+            }
+            {
+                f32x4 bq, bk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s = 16 * I + 4 * lq + j;
+                    const float fc = exp2_fast(GmL[s * LK + d] - gfirst);
+                    bq[j] = qval(s) * fc;
+                    bk[j] = kval(s) * fc;
+                }
+                bf16x4 bqh, bql, bkh, bkl;
+                split4(bq, bqh, bql);
+                split4(bk, bkh, bkl);
+                f32x4 yc = {0.f, 0.f, 0.f, 0.f};
+                yc = mma16_3(pair_frag(atH, row, k), pair_frag(atL, row, k), bqh, bql, yc);
+                yc = mma16_3(pair_frag(mtH, row, k), pair_frag(mtL, row, k), bkh, bkl, yc);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    akc[rr] = fmaf(exp2_fast(gfirst - GmL[(16 * I + 4 * lq + rr) * LK + d]), yc[rr], akc[rr]);
+            }
+        } else {
+            // (rare: operands read from LDS inside the loop, dAqk and dM as hi + lo)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 16 * I + 4 * lq + rr;
+                const float gr = GmL[r * LK + d];
+                float xq = 0.f, xk = 0.f, xc = 0.f;
+#pragma unroll 4
+                for (int j = 0; j < 16; ++j) {
+                    const int s = 16 * I + j;
+                    const float kb = kval(s), qb = qval(s);
+                    // row side (s <= r): 2^min(x, 0); column side (s >= r): 2^min(-x, 0)
+                    const float x = gr - GmL[s * LK + d];
+                    const float t2 = exp2_fast(-fabsf(x));
+                    const float er = x <= 0.f ? t2 : 1.f;
+                    const float ec = x >= 0.f ? t2 : 1.f;
+                    const float ek = kb * er;
+                    const float a_rs = (float)aH[r * TP + s] + (float)aL[r * TP + s];
+                    const float m_rs = (float)mH[r * TP + s] + (float)mL[r * TP + s];
+                    const float a_sr = (float)aH[s * TP + r] + (float)aL[s * TP + r];
+                    const float m_sr = (float)mH[s * TP + r] + (float)mL[s * TP + r];
+                    xq = fmaf(a_rs, ek, xq);
+                    xk = fmaf(m_rs, ek, xk);
+                    xc = fmaf(fmaf(a_sr, qb, m_sr * kb), ec, xc);
+                }
+                aq[rr] += xq;
+                akr[rr] += xk;
+                akc[rr] += xc;
+            }
+        }
+        // elementwise terms of qg, kd, kg; dGamma; dq, dk per value head
+        float dqg[4], dkg[4], dkd[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            dqg[rr] = dqgR[rr];
+            dkg[rr] = dkgR[rr];
+            dkd[rr] = dkdR[rr];
+        }
+        if (ib == 0) load_grads(I + 1);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = 16 * I + 4 * lq + rr;
+            const float qv = qval(r), kv = kval(r), gr = GmL[r * LK + d];
+            const float e1 = exp2_fast(gr), e2 = exp2_fast(Gd - gr);
+            const float dqi = aq[rr], dkr = akr[rr], dkc = akc[rr];
+            const float dq = fmaf(sc * e1, dqg[rr], dqi);
+            const float dk = dkr + dkc + e1 * dkd[rr] + e2 * dkg[rr];
+            const float kge = kv * e2 * dkg[rr];
+            dgam[ib][rr] = LN2F * (qv * dq + kv * (dkr - dkc + e1 * dkd[rr]) - kge);
+            if (r < len) {
+                dgk += kge;
+                const size_t row = (size_t)(pos.x + r);
+                p.dq_hv[(row * p.HV + hv) * K + d] = dq;
+                p.dk_hv[(row * p.HV + hv) * K + d] = dk;
+            }
+        }
+    }
+    // the four lanes of channel d (lq = 0..3) summed in a fixed order
+    dgk += __shfl_xor(dgk, 16, 64);
+    dgk += __shfl_xor(dgk, 32, 64);
+    if (lq == 0) dGP[half][d] = LN2F * dgk;
+    __syncthreads();   // the operand tiles become dGamma
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            dGam[(16 * (2 * half + ib) + 4 * lq + rr) * LK + d] = dgam[ib][rr];
+    __syncthreads();
+    // dg = reverse cumsum of dGamma over the chunk's rows (rows >= len left out); dG
+    // joins at the last row. Runs of RL rows per thread, as in the forward cumsum.
+    {
+        constexpr int NS = NTH / K, RL = C / NS;
+        const int dc = tid % K, sg = tid / K;
+        float x[RL];
+        float acc = 0.f;
+#pragma unroll
+        for (int i = RL - 1; i >= 0; --i) {
+            const int r = sg * RL + i;
+            acc += r < len ? dGam[r * LK + dc] : 0.f;
+            x[i] = acc;
+        }
+        runT[sg * K + dc] = acc;
+        __syncthreads();
+        float off = dGL[dc] + dGP[0][dc] + dGP[1][dc];
+        for (int j = NS - 1; j > sg; --j) off += runT[j * K + dc];
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+            const int r = sg * RL + i;
+            if (r < len) p.dg[((size_t)(pos.x + r) * p.HV + hv) * K + dc] = x[i] + off;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
 // GVA: dq, dk of a q/k head are the sums over its value heads; per (chunk, q/k head)
 // ------------------------------------------------------------------------------------
 template <int K, typename TIn>
@@ -2012,8 +2341,12 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
         else
             hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(WY_THREADS), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL((bwd_pair_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(pair_threads<K>()), 0,
-                           a.stream, p);
+        if constexpr (sizeof(TIn) == 2)
+            hipLaunchKernelGGL((bwd_pair_bf16_kernel<K, V>), dim3((unsigned)nchunk_items), dim3(pair_threads<K>()), 0,
+                               a.stream, p);
+        else
+            hipLaunchKernelGGL((bwd_pair_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(pair_threads<K>()), 0,
+                               a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         if (!a.skip_reduce) {
             hipLaunchKernelGGL((bwd_reduce_kernel<K, TIn>), dim3((unsigned)((long long)L.fwd.NCmax * a.H)), dim3(BT), 0,
