@@ -1003,42 +1003,60 @@ __global__ __launch_bounds__(BT, 2) void bwd_state_kernel(BwdParams p) {
 constexpr int SB_LD = 40;          // bf16 row stride of the operand tiles
 constexpr int SB_THREADS = 1024;
 
-// Rows [0, R) x columns [0, W) of a row-major fp32 array into hi / lo bf16 LDS rows.
-template <int R, int W>
-__device__ __forceinline__ void stage_split(const float* src, size_t gstride, __bf16* hi, __bf16* lo, int tid) {
-    constexpr int W4 = W / 4;
-#pragma unroll 2
-    for (int q = tid; q < R * W4; q += SB_THREADS) {
-        const int r = q / W4, c4 = 4 * (q % W4);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + (size_t)r * gstride + c4);
-        bf16x4 h, l;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            h[e] = (__bf16)x[e];
-            l[e] = (__bf16)(x[e] - (float)h[e]);
-        }
-        *reinterpret_cast<bf16x4*>(hi + r * SB_LD + c4) = h;
-        *reinterpret_cast<bf16x4*>(lo + r * SB_LD + c4) = l;
-    }
-}
-
-// Rows of a bf16 input into LDS (row r at src + r * rstride), zeros from row `len` on.
-template <int R, int W>
-__device__ __forceinline__ void stage_rows_bf16(const __bf16* src, size_t rstride, int len, __bf16* dst, int tid) {
-    constexpr int W4 = W / 4;
-    for (int q = tid; q < R * W4; q += SB_THREADS) {
-        const int r = q / W4, c4 = 4 * (q % W4);
-        bf16x4 h = {};
-        if (r < len) h = *reinterpret_cast<const bf16x4*>(src + (size_t)r * rstride + c4);
-        *reinterpret_cast<bf16x4*>(dst + r * SB_LD + c4) = h;
-    }
-}
-
 // The operand fragment of tile row `row`: lane (lq, lr) of a 16-row band reads values
 // 8 lq .. 8 lq + 7 of its row.
 __device__ __forceinline__ bf16x8 sb_frag(const __bf16* t, int row, int lq) {
     return *reinterpret_cast<const bf16x8*>(t + row * SB_LD + 8 * lq);
 }
+
+// One 32-column slice of the state kernel's operands, held in registers between its
+// loads and its split stores (so that a slice's loads are in flight together, and the
+// next slice's during this one's products): S and dS fp32 [K][32], v' and dv' fp32
+// [64][32], do bf16 [64][32] (rows >= len zero). Thread t takes row t / 8, columns
+// 4 (t % 8) .. + 3 of each tile, as stage_split and stage_rows_bf16 do.
+__device__ __forceinline__ void put_split4(f32x4 x, __bf16* hi, __bf16* lo, int off) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = (__bf16)x[e];
+        l[e] = (__bf16)(x[e] - (float)h[e]);
+    }
+    *reinterpret_cast<bf16x4*>(hi + off) = h;
+    *reinterpret_cast<bf16x4*>(lo + off) = l;
+}
+template <int K, int V>
+struct StateSlice {
+    static_assert(K * 8 <= SB_THREADS && C * 8 <= SB_THREADS, "one vector per thread and tile");
+    f32x4 h, dh, vn, dv;
+    bf16x4 dO;
+    __device__ __forceinline__ void load(const float* hC, const float* dhC, const float* vnC, const float* dvC,
+                                         const __bf16* dorow, size_t dstride, int len, int vb, int tid) {
+        const int r = tid >> 3, c4 = 4 * (tid & 7);
+        if (r < K) {
+            h = *reinterpret_cast<const f32x4*>(hC + (size_t)r * V + vb + c4);
+            dh = *reinterpret_cast<const f32x4*>(dhC + (size_t)r * V + vb + c4);
+        }
+        if (r < C) {
+            vn = *reinterpret_cast<const f32x4*>(vnC + (size_t)r * V + vb + c4);
+            dv = *reinterpret_cast<const f32x4*>(dvC + (size_t)r * V + vb + c4);
+            dO = bf16x4{};
+            if (r < len) dO = *reinterpret_cast<const bf16x4*>(dorow + (size_t)r * dstride + vb + c4);
+        }
+    }
+    __device__ __forceinline__ void store(__bf16* hH, __bf16* hLo, __bf16* dhH, __bf16* dhLo, __bf16* doH,
+                                          __bf16* vnH, __bf16* vnLo, __bf16* dvH, __bf16* dvLo, int tid) const {
+        const int r = tid >> 3, c4 = 4 * (tid & 7), o = r * SB_LD + c4;
+        if (r < K) {
+            put_split4(h, hH, hLo, o);
+            put_split4(dh, dhH, dhLo, o);
+        }
+        if (r < C) {
+            put_split4(vn, vnH, vnLo, o);
+            put_split4(dv, dvH, dvLo, o);
+            *reinterpret_cast<bf16x4*>(doH + o) = dO;
+        }
+    }
+};
 
 template <int K, int V>
 __global__ __launch_bounds__(SB_THREADS, 4) void bwd_state_bf16_kernel(BwdParams p) {
@@ -1070,13 +1088,15 @@ __global__ __launch_bounds__(SB_THREADS, 4) void bwd_state_bf16_kernel(BwdParams
     for (int j = 0; j < NKH; ++j) { aq[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aw[j] = aq[j]; ak[j] = aq[j]; }
     aA = f32x4{0.f, 0.f, 0.f, 0.f};
     float dgacc = 0.f;   // thread d < K: sum_v dS[d][v] S[d][v]
+    const __bf16* dorow = dout + ((size_t)pos.x * p.HV + hv) * V;
+    StateSlice<K, V> cur, nxt;
+    cur.load(hC, dhC, vnC, dvC, dorow, (size_t)p.HV * V, pos.y, 0, tid);
+#pragma unroll
     for (int vb = 0; vb < V; vb += VC) {
-        stage_split<K, VC>(hC + vb, V, hH, hLo, tid);
-        stage_split<K, VC>(dhC + vb, V, dhH, dhLo, tid);
-        stage_rows_bf16<C, VC>(dout + ((size_t)pos.x * p.HV + hv) * V + vb, (size_t)p.HV * V, pos.y, doH, tid);
-        stage_split<C, VC>(vnC + vb, V, vnH, vnLo, tid);
-        stage_split<C, VC>(dvC + vb, V, dvH, dvLo, tid);
+        cur.store(hH, hLo, dhH, dhLo, doH, vnH, vnLo, dvH, dvLo, tid);
         __syncthreads();
+        // the next slice's loads go out now and land during this slice's products
+        if (vb + VC < V) nxt.load(hC, dhC, vnC, dvC, dorow, (size_t)p.HV * V, pos.y, vb + VC, tid);
         if (tid < K)
 #pragma unroll 8   // (fully unrolled, its 128 LDS reads were all held in registers)
             for (int vv = 0; vv < VC; ++vv) {
@@ -1107,6 +1127,7 @@ __global__ __launch_bounds__(SB_THREADS, 4) void bwd_state_bf16_kernel(BwdParams
             aA = M::mma(a_do, vl, aA);
         }
         __syncthreads();
+        cur = nxt;
     }
     float* out = p.gs + ci * (size_t)GL::FLOATS;
 #pragma unroll
