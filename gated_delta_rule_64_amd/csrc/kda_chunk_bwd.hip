@@ -28,6 +28,7 @@
 // scan, state and WY stages run on the bf16 matrix cores, each fp32 operand carried as
 // a hi + lo bf16 pair (three products per step); the pair terms and the fp32-input
 // path use the fp32 matrix cores.
+#include <atomic>
 #include <type_traits>
 
 #include "kda_chunk_common.h"
@@ -312,6 +313,16 @@ struct WyLayout {
     static constexpr int DKD = 0, DM = C * K;
     static constexpr int FLOATS = C * K + C * C;
 };
+
+// Work item b of a per-chunk-head kernel (G = NCmax * HV items, dealt to the XCDs by
+// xcd_remap): its chunk c and value head hv, and whether it exists (nch = the number of
+// chunks: NCmax in dense mode, the packed schedule's count otherwise).
+__device__ __forceinline__ bool bwd_item(const BwdParams& p, int b, int nch, int& c, int& hv) {
+    const int item = xcd_remap(b, p.NCmax * p.HV);
+    hv = item % p.HV;
+    c = item / p.HV;
+    return c < nch;
+}
 
 // the chunk this block handles, or false when it is past the packed schedule's end
 __device__ __forceinline__ bool bwd_chunk(const BwdParams& p, int& c, int& hv, int2& pos) {
@@ -1340,6 +1351,62 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_kernel(BwdParams p) {
     }
 }
 
+// A chunk-head's k, v and gate rows and its beta, held in registers between their loads
+// and their LDS stores (so that the next chunk-head's are in flight during this one's
+// products). TG is the gate's element type (fp32 log2 decay or raw input, or a bf16 raw
+// input). A scheduled chunk has at least one row: rows past its end re-read its last
+// row (no branch around the loads) and are stored as zeros.
+template <int K, int V, int NTH, typename TB, typename TG>
+struct WyInputs {
+    static constexpr int NK = C * K / (4 * NTH), NV = C * V / (4 * NTH);
+    static_assert(NK * 4 * NTH == C * K && NV * 4 * NTH == C * V, "whole vectors per thread");
+    typedef typename std::conditional<sizeof(TG) == 2, bf16x4, f32x4>::type gvec;
+    bf16x4 k[NK], v[NV];
+    gvec g[NK];
+    TB b;
+    __device__ __forceinline__ void load(const BwdParams& p, const TG* gsrc, int2 ps, int hv, int tid) {
+        const int last = ps.y > 0 ? ps.y - 1 : 0, h = hv / (p.HV / p.H);
+        const __bf16* kin = reinterpret_cast<const __bf16*>(p.k);
+        const __bf16* vin = reinterpret_cast<const __bf16*>(p.v);
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int q = tid + NTH * i, r = min(q / (K / 4), last), c4 = 4 * (q % (K / 4));
+            k[i] = *reinterpret_cast<const bf16x4*>(kin + ((size_t)(ps.x + r) * p.H + h) * K + c4);
+            g[i] = *reinterpret_cast<const gvec*>(gsrc + ((size_t)(ps.x + r) * p.HV + hv) * K + c4);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int q = tid + NTH * i, r = min(q / (V / 4), last), c4 = 4 * (q % (V / 4));
+            v[i] = *reinterpret_cast<const bf16x4*>(vin + ((size_t)(ps.x + r) * p.HV + hv) * V + c4);
+        }
+        if (tid < C) b = reinterpret_cast<const TB*>(p.beta)[(size_t)(ps.x + min(tid, last)) * p.HV + hv];
+    }
+    // k and the gate as fp32 rows (row stride ld), v as bf16 rows (stride ldv), beta
+    // (through its sigmoid with the option) into bL
+    __device__ __forceinline__ void store(const BwdParams& p, int len, float* kS, float* GS, int ld, __bf16* vB,
+                                          int ldv, float* bL, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int q = tid + NTH * i, r = q / (K / 4), c4 = 4 * (q % (K / 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kS[r * ld + c4 + e] = r < len ? (float)k[i][e] : 0.f;
+                GS[r * ld + c4 + e] = r < len ? (float)g[i][e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int q = tid + NTH * i, r = q / (V / 4), c4 = 4 * (q % (V / 4));
+            *reinterpret_cast<bf16x4*>(vB + r * ldv + c4) = r < len ? v[i] : bf16x4{};
+        }
+        if (tid < C) {
+            float bt = tid < len ? to_f32(b) : 0.f;
+            if (p.in.beta_sig != 0.f && tid < len) bt = beta_from_logit(bt, p.in.beta_sig);
+            bL[tid] = bt;
+        }
+    }
+};
+
 // ------------------------------------------------------------------------------------
 // The same backward of the WY inverse for bf16 inputs, its dense products on the bf16
 // matrix cores. Each fp32 operand is split once into a hi + lo bf16 pair in LDS, laid
@@ -1391,7 +1458,7 @@ __device__ __forceinline__ bf16x8 wy_frag(const __bf16* t, int row, int ld, int 
     return *reinterpret_cast<const bf16x8*>(t + row * ld + k);
 }
 
-template <int K, int V, typename TB>
+template <int K, int V, typename TB, typename TG>
 __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p) {
     constexpr int NTH = WY_THREADS, NW = NTH / 64;
     constexpr int MKV = K > V ? K : V;
@@ -1422,48 +1489,42 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
     __bf16 *BtH = regB, *BtL = regB + MKV * TP;
     __bf16 *ThH = regB, *ThL = regB + C * TP, *dTH = regB + 2 * C * TP, *dTL = regB + 3 * C * TP;
     __bf16 *XH = regA, *XLo = regA + C * TP;
-    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int tid0 = threadIdx.x;
+    const int G = p.NCmax * p.HV;
+    const int nch = p.dense ? p.NCmax : p.nchunks[0];
+    const TG* gsrc = static_cast<const TG*>(p.in.gate_mode == GATE_LOG2 ? static_cast<const void*>(p.g) : p.in.g_raw);
+    // The block takes chunk-heads b, b + gridDim.x, ... and loads the next one's inputs
+    // during this one's products.
+    WyInputs<K, V, NTH, TB, TG> in_;
+    int b = blockIdx.x, c = 0, hv = 0;
+    while (b < G && !bwd_item(p, b, nch, c, hv)) b += gridDim.x;
+    if (b < G) in_.load(p, gsrc, chunk_pos(p.dense, p.NT, p.T, p.table, c), hv, tid0);
+    while (b < G) {
+    // the lane indices re-derived from an opaque copy each chunk-head, so that the
+    // compiler recomputes the lane-dependent LDS addresses in the body instead of keeping
+    // them all live across the loop
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tI = wave >> 2, tJ = wave & 3;   // this wave's tile of the 64 x 64 products
-    int c, hv;
-    int2 pos;
-    if (!bwd_chunk(p, c, hv, pos)) return;
-    const int h = hv / (p.HV / p.H);
+    const int2 pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
     const int len = pos.y;
     const size_t ci = (size_t)hv * p.NCmax + c;
-    const __bf16* kin = reinterpret_cast<const __bf16*>(p.k);
-    const __bf16* vin = reinterpret_cast<const __bf16*>(p.v);
-    const TB* bin = reinterpret_cast<const TB*>(p.beta);
     const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
     float* wyC = p.wy + ci * (size_t)WL::FLOATS;
+    // the next chunk-head this block takes
+    int bn = b + gridDim.x, cn = 0, hvn = 0;
+    while (bn < G && !bwd_item(p, bn, nch, cn, hvn)) bn += gridDim.x;
 
-    // ---- loads: k, v, the gate and beta first (the stages right after need them), then T,
-    // dv' and M at this lane's dL elements into registers (memory counters complete in
-    // order, so those land while the gate cumsum and kd run) ----
-    RowLoad<C, K, __bf16, NTH> lk_;
-    RowLoad<C, V, __bf16, NTH> lv_;
-    lk_.load(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid);
-    lv_.load(vin + ((size_t)pos.x * p.HV + hv) * V, (size_t)p.HV * V, len, tid);
-    stage_gate<K, NTH>(p, pos, hv, GS, LK, tid);
-    lk_.store(len, kS, LK, tid);
-#pragma unroll
-    for (int i = 0; i < RowLoad<C, V, __bf16, NTH>::N; ++i) {
-        const int q = tid + NTH * i, r = q / (V / 4), c4 = 4 * (q % (V / 4));
-        *reinterpret_cast<bf16x4*>(vB + r * VP + c4) = r < len ? lv_.x[i] : bf16x4{};
-    }
-    if (tid < C) {
-        float b = tid < len ? to_f32(bin[(size_t)(pos.x + tid) * p.HV + hv]) : 0.f;
-        if (p.in.beta_sig != 0.f && tid < len) b = beta_from_logit(b, p.in.beta_sig);
-        bL[tid] = b;
-    }
+    // ---- this chunk-head's k, v, gate and beta into LDS; T and dv' into registers (they
+    // land while the gate cumsum and kd run) ----
+    in_.store(p, len, kS, GS, LK, vB, VP, bL, tid);
     // T[tr][tc .. tc + 3], lane l of each wave taking row l
     const int tr = tid & 63, tc = 4 * (tid >> 6);
-    const f32x4 tq = *reinterpret_cast<const f32x4*>(p.mt + ((size_t)p.NCmax * p.HV + ci) * (C * C) + tr * C + tc);
+    const f32x4 tq0 = *reinterpret_cast<const f32x4*>(p.mt + ((size_t)p.NCmax * p.HV + ci) * (C * C) + tr * C + tc);
     ColLoad<V, NTH> ldv_;
     ldv_.load(p.dvn + ci * (size_t)C * V, tid);
-    float mR[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mR[r] = p.mt[ci * (size_t)(C * C) + (16 * tI + 4 * lq + r) * C + 16 * tJ + lr];
     for (int e = tid; e < NW * C; e += NTH) dbP[e / C][e % C] = 0.f;
     __syncthreads();
     if (p.in.l2norm_k) l2norm_rows_lds<K>(kS, LK, tid);
@@ -1481,15 +1542,17 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const __bf16 hx = (__bf16)tq[e];
+        const __bf16 hx = (__bf16)tq0[e];
         TtH[(tc + e) * TP + tr] = hx;
-        TtL[(tc + e) * TP + tr] = (__bf16)(tq[e] - (float)hx);
+        TtL[(tc + e) * TP + tr] = (__bf16)(tq0[e] - (float)hx);
     }
     __syncthreads();
     store_split_rt<V, NTH>(ldv_, AH, AL, XP, BtH, BtL, TP, tid);
-    // dw (for the key side) is loaded now and lands during the value side
+    // dw (for the key side) is loaded now and lands during the value side, then the next
+    // chunk-head's inputs
     ColLoad<K, NTH> ldw_;
     ldw_.load(gsC + GL::DW, tid);
+    if (bn < G) in_.load(p, gsrc, chunk_pos(p.dense, p.NT, p.T, p.table, cn), hvn, tid);
     __syncthreads();
 
     auto add_rows = [&](int row0, const float (&x)[4]) {
@@ -1514,6 +1577,7 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
         return acc;
     };
     f32x4 dT = {0.f, 0.f, 0.f, 0.f};
+    float mR[4];
 
     // ---- value side: dv = beta T^T dv', dbeta += rowsum((T^T dv') v), dT = dv' (beta v)^T ----
     __bf16* dvout = reinterpret_cast<__bf16*>(p.dv);
@@ -1577,6 +1641,11 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
     __syncthreads();
     // ---- dT (strictly lower) transposed and T as rows, split, into region B ----
     {
+        // T again (from cache), and M at this lane's dL elements: loaded here rather
+        // than held in registers through the products
+        const f32x4 tq = *reinterpret_cast<const f32x4*>(p.mt + ((size_t)p.NCmax * p.HV + ci) * (C * C) + tr * C + tc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mR[r] = p.mt[ci * (size_t)(C * C) + (16 * tI + 4 * lq + r) * C + 16 * tJ + lr];
         bf16x4 hv4, lv4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1651,6 +1720,11 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
         const size_t e = (size_t)(pos.x + tid) * p.HV + hv;
         if (p.dbeta_f32) reinterpret_cast<float*>(p.dbeta)[e] = db;
         else reinterpret_cast<TB*>(p.dbeta)[e] = from_f32<TB>(db);
+    }
+    __syncthreads();   // this chunk-head's LDS reads are done before the next one's stores
+    b = bn;
+    c = cn;
+    hv = hvn;
     }
 }
 
@@ -2275,6 +2349,21 @@ __global__ __launch_bounds__(BT) void bwd_reduce_kernel(BwdParams p) {
     }
 }
 
+
+// Grid of a persistent kernel (one block per CU, each looping over its items): the
+// current device's CU count, at most `items`.
+long long persistent_blocks(long long items) {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    int n = dev >= 0 && dev < 64 ? cus[dev].load(std::memory_order_relaxed) : 0;
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        if (dev >= 0 && dev < 64) cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return items < n ? items : n;
+}
+
 template <int K, int V, typename TIn, typename TB>
 hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
     char* ws = reinterpret_cast<char*>(a.workspace);
@@ -2357,8 +2446,14 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
         else
             hipLaunchKernelGGL((bwd_state_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(BT), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if constexpr (sizeof(TIn) == 2)
-            hipLaunchKernelGGL((bwd_wy_bf16_kernel<K, V, TB>), dim3((unsigned)nchunk_items), dim3(WY_THREADS), 0, a.stream, p);
+        if constexpr (sizeof(TIn) == 2) {
+            if (p.in.gate_mode == GATE_RAW_BF16)
+                hipLaunchKernelGGL((bwd_wy_bf16_kernel<K, V, TB, __bf16>), dim3((unsigned)persistent_blocks(nchunk_items)),
+                                   dim3(WY_THREADS), 0, a.stream, p);
+            else
+                hipLaunchKernelGGL((bwd_wy_bf16_kernel<K, V, TB, float>), dim3((unsigned)persistent_blocks(nchunk_items)),
+                                   dim3(WY_THREADS), 0, a.stream, p);
+        }
         else
             hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(WY_THREADS), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
