@@ -560,24 +560,37 @@ struct DscanFragsB {
     f32x4 e[NDT];
 };
 
+// The operands of chunk c in two groups: those of the dv' products (kg, P1) and those
+// of the dS update (w^T, P2, 2^G). The scan issues each group right after the products
+// that last read it, so the loads queue up behind work in flight instead of in one burst.
 template <int K, int V>
-__device__ __forceinline__ void load_dscan_b(DscanFragsB<K, V>& F, const BwdParams& p, int hv, int c,
-                                             int wave, int lane, int v0) {
+__device__ __forceinline__ void load_dscan_b_kg(DscanFragsB<K, V>& F, const BwdParams& p, int hv, int c,
+                                                int wave, int lane, int v0) {
     typedef ScanOps<K, V> SO;
     typedef FragTile<__bf16, C, K> FKG;
-    typedef FragTile<__bf16, K, C> FWT;
     typedef DscanFragsB<K, V> DF;
     const int lr = lane & 15, lq = lane >> 4;
     const size_t ci = (size_t)hv * p.NCmax + c;
     const float* ops = p.sops + ci * (size_t)SO::FLOATS;
     const __bf16* kg = reinterpret_cast<const __bf16*>(ops + SO::KG);
-    const __bf16* wt = reinterpret_cast<const __bf16*>(ops + SO::WT);
-    const float* eg = reinterpret_cast<const float*>(p.rec + ci * p.rec_bytes + p.off_eg);
 #pragma unroll
     for (int kk = 0; kk < DF::NKS; ++kk) {
         F.kg[0][kk] = *reinterpret_cast<const bf16x8*>(kg + FKG::frag(wave, kk, lane));
         F.kg[1][kk] = *reinterpret_cast<const bf16x8*>(kg + C * K + FKG::frag(wave, kk, lane));
     }
+    F.p1 = *reinterpret_cast<const f32x4*>(ops + SO::P1 + AccTile::quad(v0 + lr, 16 * wave + 4 * lq));
+}
+template <int K, int V>
+__device__ __forceinline__ void load_dscan_b_wt(DscanFragsB<K, V>& F, const BwdParams& p, int hv, int c,
+                                                int wave, int lane, int v0) {
+    typedef ScanOps<K, V> SO;
+    typedef FragTile<__bf16, K, C> FWT;
+    typedef DscanFragsB<K, V> DF;
+    const int lr = lane & 15, lq = lane >> 4;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const float* ops = p.sops + ci * (size_t)SO::FLOATS;
+    const __bf16* wt = reinterpret_cast<const __bf16*>(ops + SO::WT);
+    const float* eg = reinterpret_cast<const float*>(p.rec + ci * p.rec_bytes + p.off_eg);
 #pragma unroll
     for (int a = 0; a < DF::NDT; ++a) {
 #pragma unroll
@@ -586,7 +599,12 @@ __device__ __forceinline__ void load_dscan_b(DscanFragsB<K, V>& F, const BwdPara
         F.p2[a] = *reinterpret_cast<const f32x4*>(ops + SO::P2 + acc_kv<K>(v0 + lr, 16 * (wave + 4 * a) + 4 * lq));
         F.e[a] = *reinterpret_cast<const f32x4*>(eg + 16 * (wave + 4 * a) + 4 * lq);
     }
-    F.p1 = *reinterpret_cast<const f32x4*>(ops + SO::P1 + AccTile::quad(v0 + lr, 16 * wave + 4 * lq));
+}
+template <int K, int V>
+__device__ __forceinline__ void load_dscan_b(DscanFragsB<K, V>& F, const BwdParams& p, int hv, int c,
+                                             int wave, int lane, int v0) {
+    load_dscan_b_kg<K, V>(F, p, hv, c, wave, lane, v0);
+    load_dscan_b_wt<K, V>(F, p, hv, c, wave, lane, v0);
 }
 
 template <int K, int V>
@@ -657,7 +675,9 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
         }
     };
     __syncthreads();
-    auto step = [&](DF& F, int c) {
+    // one chunk of the walk; F's operands are then reloaded with chunk cn's, each group
+    // right after its last use
+    auto step = [&](DF& F, int c, int cn) {
         const size_t ci = (size_t)hv * p.NCmax + c;
         float* dhb = p.dh + ci * (size_t)K * V;
 #pragma unroll
@@ -676,6 +696,7 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] += acc2[r];
+        load_dscan_b_kg<K, V>(F, p, hv, cn, wave, lane, v0);
         float* dvb = p.dvn + ci * (size_t)C * V;
 #pragma unroll
         for (int r = 0; r < 4; ++r) dvb[(size_t)(16 * wave + 4 * lq + r) * V + v0 + lr] = acc[r];
@@ -694,19 +715,18 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
             for (int r = 0; r < 4; ++r) dS[a][r] = fmaf(F.e[a][r], dS[a][r], F.p2[a][r] - x[r]);
             put4(dSh, dSl, lr * LDK + 16 * (wave + 4 * a) + 4 * lq, dS[a]);
         }
+        load_dscan_b_wt<K, V>(F, p, hv, cn, wave, lane, v0);
         __syncthreads();
     };
     const int nsteps = c1 - c0;
     int c = c1 - 1;
     for (int t = 0; t < nsteps / 2; ++t, c -= 2) {
-        step(F0, c);
-        load_dscan_b<K, V>(F0, p, hv, clampc(c - 2), wave, lane, v0);
+        step(F0, c, clampc(c - 2));
         prefetch(pf0, c);
-        step(F1, c - 1);
-        load_dscan_b<K, V>(F1, p, hv, clampc(c - 3), wave, lane, v0);
+        step(F1, c - 1, clampc(c - 3));
         prefetch(pf1, c - 1);
     }
-    if (nsteps & 1) step(F0, c);
+    if (nsteps & 1) step(F0, c, clampc(c - 2));
     sink ^= pf0 ^ pf1;
     asm volatile("" ::"v"(sink));   // keeps the prefetch loads; emits no instruction
     if (p.dh0) {
