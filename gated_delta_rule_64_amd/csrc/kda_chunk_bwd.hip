@@ -1435,7 +1435,9 @@ struct WyInputs {
 // transposed (T^T dv', T^T dw), kd, v (a bf16 input, exact). A product is then
 // hi*hi + lo*hi + hi*lo per 32-wide contraction step (hi*hi + lo*hi against v, and beta
 // applied to the finished dT column). Sixteen waves, the tiles dealt as in the fp32
-// kernel; the row sums for dbeta in per-wave partials.
+// kernel; the row sums for dbeta in per-wave partials. The blocks are persistent (one
+// per CU, each looping over chunk-heads) and load the next chunk-head's k, v, gate and
+// beta into registers during this one's products.
 // ------------------------------------------------------------------------------------
 // An fp32 [C][W] tile (row stride W) into registers, lane l of each wave taking row l:
 // the transposed bf16 stores below then put a wave's 64 lanes on 32 distinct banks
