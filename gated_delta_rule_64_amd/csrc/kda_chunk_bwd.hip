@@ -235,6 +235,7 @@ struct BwdParams {
     float* dk_hv;
     InputSpec in;        // fused options of the forward (applied to the staged inputs)
     int dbeta_f32;       // dbeta written as fp32
+    int pair_gva;        // the bf16 pair kernel sums dq, dk over each q/k head's value heads itself
 };
 
 // The fused options applied to staged rows in LDS (64 rows of K, rows >= len zero):
@@ -2052,37 +2053,73 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_bf16_kernel(Bwd
     __bf16 *aH = At, *aL = At + C * TP, *mH = At + 2 * C * TP, *mL = At + 3 * C * TP;
     __bf16 *atH = At + 4 * C * TP, *atL = At + 5 * C * TP, *mtH = At + 6 * C * TP, *mtL = At + 7 * C * TP;
     float* dGam = reinterpret_cast<float*>(At);
-    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tile = wave % (K / 16), half = wave / (K / 16);   // channel tile; row blocks 2 half, 2 half + 1
-    int c, hv;
-    int2 pos;
-    if (!bwd_chunk(p, c, hv, pos)) return;
-    const int h = hv / (p.HV / p.H);
+    // A block takes one chunk and, with pair_gva, one q/k head and all of its value
+    // heads in turn (q, k and their normalisation factors staged once; dq, dk summed over
+    // the value heads in the first one's slot of the per-value-head buffers, the last one
+    // writing the bf16 results), else one (chunk, value head).
+    const int grp = p.HV / p.H;
+    const int nh = p.pair_gva ? p.H : p.HV;
+    const int item = xcd_remap(blockIdx.x, p.NCmax * nh);
+    const int c = item / nh, hh = item % nh;
+    if (!p.dense && c >= p.nchunks[0]) return;
+    const int2 pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
+    const int h = p.pair_gva ? hh : hh / grp;
+    const int ng = p.pair_gva ? grp : 1;
     const int len = pos.y;
-    const size_t ci = (size_t)hv * p.NCmax + c;
     const __bf16* qin = reinterpret_cast<const __bf16*>(p.q);
     const __bf16* kin = reinterpret_cast<const __bf16*>(p.k);
+    __bf16* dqo = reinterpret_cast<__bf16*>(p.dq);
+    __bf16* dko = reinterpret_cast<__bf16*>(p.dk);
+    const float sc = p.scale;
+    const int tid0 = threadIdx.x;
+    {
+        // q, k (bf16, exact) and their rows' normalisation factors, once for the block
+        RowLoad<C, K, __bf16, NTH> lq_, lk_;
+        lq_.load(qin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid0);
+        lk_.load(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid0);
+#pragma unroll
+        for (int i = 0; i < RowLoad<C, K, __bf16, NTH>::N; ++i) {
+            const int q = tid0 + NTH * i, r = q / (K / 4), c4 = 4 * (q % (K / 4));
+            *reinterpret_cast<bf16x4*>(qB + r * KP + c4) = r < len ? lq_.x[i] : bf16x4{};
+            *reinterpret_cast<bf16x4*>(kB + r * KP + c4) = r < len ? lk_.x[i] : bf16x4{};
+        }
+        __syncthreads();
+        // threads 0 .. 63 the q rows, 64 .. 127 the k rows (the sum of squares in channel
+        // order, as the fp32 kernel's)
+        if (tid0 < 2 * C) {
+            const int r = tid0 & 63;
+            const bool isq = tid0 < C;
+            float f = 1.f;
+            if (isq ? p.in.l2norm_q : p.in.l2norm_k) {
+                const __bf16* row = (isq ? qB : kB) + r * KP;
+                float ss = 0.f;
+#pragma unroll 8
+                for (int d = 0; d < K; ++d) ss = fmaf((float)row[d], (float)row[d], ss);
+                f = l2norm_rstd(ss);
+            }
+            (isq ? rnq : rnk)[r] = f;
+        }
+    }
+    for (int g = 0; g < ng; ++g) {
+    // lane indices from an opaque copy each value head (the lane-dependent LDS addresses
+    // are then recomputed in the body, not held live across the loop)
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = wave % (K / 16), half = wave / (K / 16);   // channel tile; row blocks 2 half, 2 half + 1
+    const int hv = p.pair_gva ? h * grp + g : hh;
+    const size_t ci = (size_t)hv * p.NCmax + c;
     const float* gsC = p.gs + ci * (size_t)GL::FLOATS;
     const float* wyC = p.wy + ci * (size_t)WL::FLOATS;
-    const float sc = p.scale;
 
     {
-        // q, k, dAqk and dM loads go out together, the gate is staged meanwhile
-        RowLoad<C, K, __bf16, NTH> lq_, lk_;
+        // dAqk and dM loads go out together, the gate is staged meanwhile
         ColLoad<C, NTH> la_, lm_;
-        lq_.load(qin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid);
-        lk_.load(kin + ((size_t)pos.x * p.H + h) * K, (size_t)p.H * K, len, tid);
         la_.load(gsC + GL::DA, tid);
         lm_.load(wyC + WL::DM, tid);
         stage_gate<K, NTH>(p, pos, hv, GmL, LK, tid);
         if (tid < K) dGL[tid] = gsC[GL::DG + tid];
-#pragma unroll
-        for (int i = 0; i < RowLoad<C, K, __bf16, NTH>::N; ++i) {
-            const int q = tid + NTH * i, r = q / (K / 4), c4 = 4 * (q % (K / 4));
-            *reinterpret_cast<bf16x4*>(qB + r * KP + c4) = r < len ? lq_.x[i] : bf16x4{};
-            *reinterpret_cast<bf16x4*>(kB + r * KP + c4) = r < len ? lk_.x[i] : bf16x4{};
-        }
 #pragma unroll
         for (int i = 0; i < ColLoad<C, NTH>::N; ++i) {
             f32x4 x = la_.x[i];
@@ -2109,21 +2146,6 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_bf16_kernel(Bwd
         }
     }
     __syncthreads();
-    // row normalisation factors: threads 0 .. 63 the q rows, 64 .. 127 the k rows (the
-    // sum of squares in channel order, as the fp32 kernel's)
-    if (tid < 2 * C) {
-        const int r = tid & 63;
-        const bool isq = tid < C;
-        float f = 1.f;
-        if (isq ? p.in.l2norm_q : p.in.l2norm_k) {
-            const __bf16* row = (isq ? qB : kB) + r * KP;
-            float ss = 0.f;
-#pragma unroll 8
-            for (int d = 0; d < K; ++d) ss = fmaf((float)row[d], (float)row[d], ss);
-            f = l2norm_rstd(ss);
-        }
-        (isq ? rnq : rnk)[r] = f;
-    }
     if (p.in.gate_mode != GATE_LOG2) gate_rows_lds<K, NTH>(GmL, LK, len, p.in, hv, tid);
     __syncthreads();
     cumsum_rows_lds<K, NTH>(GmL, LK, runT, tid);
@@ -2303,8 +2325,23 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_bf16_kernel(Bwd
             if (r < len) {
                 dgk += kge;
                 const size_t row = (size_t)(pos.x + r);
-                p.dq_hv[(row * p.HV + hv) * K + d] = dq;
-                p.dk_hv[(row * p.HV + hv) * K + d] = dk;
+                if (p.pair_gva) {
+                    // the running sum over the value heads (each lane reads back only
+                    // what it wrote for the value head before)
+                    float* sq = p.dq_hv + (row * p.HV + h * grp) * K + d;
+                    float* sk = p.dk_hv + (row * p.HV + h * grp) * K + d;
+                    const float aq_ = g > 0 ? *sq + dq : dq, ak_ = g > 0 ? *sk + dk : dk;
+                    if (g + 1 < ng) {
+                        *sq = aq_;
+                        *sk = ak_;
+                    } else {
+                        dqo[(row * p.H + h) * K + d] = (__bf16)aq_;
+                        dko[(row * p.H + h) * K + d] = (__bf16)ak_;
+                    }
+                } else {
+                    p.dq_hv[(row * p.HV + hv) * K + d] = dq;
+                    p.dk_hv[(row * p.HV + hv) * K + d] = dk;
+                }
             }
         }
     }
@@ -2341,6 +2378,8 @@ __global__ __launch_bounds__(pair_threads<K>(), 1) void bwd_pair_bf16_kernel(Bwd
             const int r = sg * RL + i;
             if (r < len) p.dg[((size_t)(pos.x + r) * p.HV + hv) * K + dc] = x[i] + off;
         }
+    }
+    __syncthreads();   // this value head's LDS reads are done before the next one's stores
     }
 }
 
@@ -2479,14 +2518,19 @@ hipError_t launch_bwd_kv(const ChunkBwdArgs& a, const ChunkBwdLayout& L) {
         else
             hipLaunchKernelGGL((bwd_wy_kernel<K, V, TIn, TB>), dim3((unsigned)nchunk_items), dim3(WY_THREADS), 0, a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
+        // bf16 inputs without a following chain rule: the pair kernel sums dq, dk over the
+        // value heads itself (one block per chunk and q/k head), no separate reduction
+        const bool pair_gva = sizeof(TIn) == 2 && !a.skip_reduce;
+        p.pair_gva = pair_gva ? 1 : 0;
         if constexpr (sizeof(TIn) == 2)
-            hipLaunchKernelGGL((bwd_pair_bf16_kernel<K, V>), dim3((unsigned)nchunk_items), dim3(pair_threads<K>()), 0,
-                               a.stream, p);
+            hipLaunchKernelGGL((bwd_pair_bf16_kernel<K, V>),
+                               dim3((unsigned)(pair_gva ? (long long)L.fwd.NCmax * a.H : nchunk_items)),
+                               dim3(pair_threads<K>()), 0, a.stream, p);
         else
             hipLaunchKernelGGL((bwd_pair_kernel<K, V, TIn>), dim3((unsigned)nchunk_items), dim3(pair_threads<K>()), 0,
                                a.stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if (!a.skip_reduce) {
+        if (!a.skip_reduce && !pair_gva) {
             hipLaunchKernelGGL((bwd_reduce_kernel<K, TIn>), dim3((unsigned)((long long)L.fwd.NCmax * a.H)), dim3(BT), 0,
                                a.stream, p);
             if ((err = hipGetLastError()) != hipSuccess) return err;
