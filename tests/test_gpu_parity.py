@@ -1094,6 +1094,10 @@ BWD_EDGE = [  # (label, B, T, H, HV, K, V, dtype, h0, dht)
     ("one_chunk", 1, 64, 2, 4, 128, 64, torch.bfloat16, True, False),
     ("chunk_plus_one", 2, 65, 1, 2, 64, 128, torch.float32, False, True),
     ("fp32_k64", 1, 130, 2, 2, 64, 64, torch.float32, True, True),
+    # bf16 kernels at K = 64 (the pair kernel's eight-wave shape), four value heads per
+    # q/k head summed in the pair kernel, a ragged last chunk
+    ("bf16_k64_gva4", 1, 150, 1, 4, 64, 128, torch.bfloat16, True, True),
+    ("bf16_k64_v64", 2, 100, 2, 2, 64, 64, torch.bfloat16, False, True),
 ]
 
 
