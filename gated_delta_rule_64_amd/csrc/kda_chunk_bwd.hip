@@ -1599,14 +1599,44 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
         }
         return acc;
     };
+    // tiles (sb, nt) and (sb + 2, nt) together: one read of the X fragments serves both
+    auto tt_prod2 = [&](int sb, int nt, f32x4& a0, f32x4& a1) {
+        a0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        a1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32) {
+            const int k = k0 + 8 * lq;
+            const bf16x8 bh = wy_frag(BtH, 16 * nt + lr, TP, k), bl = wy_frag(BtL, 16 * nt + lr, TP, k);
+            const bf16x8 ah0 = wy_frag(TtH, 16 * sb + lr, TP, k), al0 = wy_frag(TtL, 16 * sb + lr, TP, k);
+            const bf16x8 ah1 = wy_frag(TtH, 16 * sb + 32 + lr, TP, k), al1 = wy_frag(TtL, 16 * sb + 32 + lr, TP, k);
+            a0 = M::mma(ah0, bh, a0);
+            a1 = M::mma(ah1, bh, a1);
+            a0 = M::mma(al0, bh, a0);
+            a1 = M::mma(al1, bh, a1);
+            a0 = M::mma(ah0, bl, a0);
+            a1 = M::mma(ah1, bl, a1);
+        }
+    };
+    // every tile of T^T X (N / 16 column tiles) through epi(sb, nt, acc); with two tiles
+    // per wave, wave w takes (w / (N / 16), w % (N / 16)) and the tile two row blocks down
+    auto tt_all = [&](auto ncols, auto&& epi) {
+        constexpr int NC = decltype(ncols)::value;
+        if constexpr (4 * NC == 2 * NW) {
+            const int sb = wave / NC, nt = wave % NC;
+            f32x4 a0, a1;
+            tt_prod2(sb, nt, a0, a1);
+            epi(sb, nt, a0);
+            epi(sb + 2, nt, a1);
+        } else {
+            for (int t = wave; t < 4 * NC; t += NW) epi(t / NC, t % NC, tt_prod(t / NC, t % NC));
+        }
+    };
     f32x4 dT = {0.f, 0.f, 0.f, 0.f};
     float mR[4];
 
     // ---- value side: dv = beta T^T dv', dbeta += rowsum((T^T dv') v), dT = dv' (beta v)^T ----
     __bf16* dvout = reinterpret_cast<__bf16*>(p.dv);
-    for (int t = wave; t < 4 * (V / 16); t += NW) {
-        const int sb = t / (V / 16), nt = t % (V / 16);
-        const f32x4 acc = tt_prod(sb, nt);
+    tt_all(std::integral_constant<int, V / 16>(), [&](int sb, int nt, const f32x4& acc) {
         float db[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1615,7 +1645,7 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
             if (s < len) dvout[((size_t)(pos.x + s) * p.HV + hv) * V + vv] = (__bf16)(bL[s] * acc[r]);
         }
         add_rows(16 * sb, db);
-    }
+    });
     if (tJ <= tI) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1634,9 +1664,7 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
     store_split_rt<K, NTH>(ldw_, AH, AL, XP, BtH, BtL, TP, tid);
     __syncthreads();
     // ---- key side: dkd = beta T^T dw, dbeta += rowsum((T^T dw) kd), dT += dw (beta kd)^T ----
-    for (int t = wave; t < 4 * (K / 16); t += NW) {
-        const int sb = t / (K / 16), nt = t % (K / 16);
-        const f32x4 acc = tt_prod(sb, nt);
+    tt_all(std::integral_constant<int, K / 16>(), [&](int sb, int nt, const f32x4& acc) {
         float db[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1645,7 +1673,7 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
             wyC[WL::DKD + s * K + d] = bL[s] * acc[r];
         }
         add_rows(16 * sb, db);
-    }
+    });
     if (tJ <= tI) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
