@@ -344,16 +344,27 @@ __device__ __forceinline__ int acc_kv(int v, int d) {
     return (((v >> 4) * (K / 16) + (d >> 4)) * 64 + (v & 15) + 16 * ((d & 15) >> 2)) * 4 + (d & 3);
 }
 
-// Per (value head, chunk) operands of the reverse scan: kg in fragment order as the A
-// operand of kg dS ([64][K]), w^T in fragment order as the A operand of w^T dv'
-// ([K][64]), P1 = Aqk^T do ([64][V], AccTile order) and P2 = qg^T do ([K][V], acc_kv
-// order), all fp32 for fp32 inputs; for bf16 inputs kg is a hi + lo pair and w^T one
-// bf16 tile in 16x16x32 fragment order, in the same slots. P1 and P2 do not depend on
-// the state gradient, so they are formed in parallel before the scan.
+// Per (value head, chunk) operands of the reverse scan, fp32 inputs: kg in fragment
+// order as the A operand of kg dS ([64][K]), w^T in fragment order as the A operand of
+// w^T dv' ([K][64]), P1 = Aqk^T do ([64][V], AccTile order) and P2 = qg^T do ([K][V],
+// acc_kv order), all fp32. P1 and P2 do not depend on the state gradient, so they are
+// formed in parallel before the scan.
 template <int K, int V>
 struct ScanOps {
     static constexpr int KG = 0, WT = C * K, P1 = 2 * C * K, P2 = 2 * C * K + C * V;
     static constexpr int FLOATS = 2 * C * K + C * V + K * V;
+};
+// The same slot for bf16 inputs, in bf16 elements, every tile in 16x16x32 fragment
+// order: kg (hi, lo), w^T, then the operands of P1 and P2, which the reverse scan forms
+// on the matrix cores as it goes (64 KB of bf16 operands per chunk-head instead of 96 KB
+// of fp32 products): Aqk^T (rows s, contraction r; hi, lo), qg^T (rows d, contraction
+// r; hi, lo) and do^T (rows v, contraction r).
+template <int K, int V>
+struct ScanOpsB {
+    static constexpr int KG = 0, WT = 2 * C * K, AQT = 3 * C * K, QGT = 3 * C * K + 2 * C * C;
+    static constexpr int DOT = 5 * C * K + 2 * C * C, ELEMS = 5 * C * K + 2 * C * C + V * C;
+    static_assert(ELEMS * 2 <= ScanOps<K, V>::FLOATS * 4, "fits the per-chunk slot");
+    static_assert(ELEMS * 2 % 128 == 0, "whole 128-byte lines");
 };
 
 // ------------------------------------------------------------------------------------
@@ -548,7 +559,10 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_kernel(BwdParams p) {
 // The reverse scan for bf16 inputs: kg (hi, lo) and w^T in bf16 fragment order from the
 // bf16 prep, dS and dv' exchanged through LDS as hi + lo bf16 rows, products on
 // v_mfma_f32_16x16x32_bf16 (hi*hi + lo*hi + hi*lo; w^T is exact, two products). The
-// chain per chunk is 4 + 2 dependent steps per wave instead of 32 + 16 fp32 ones.
+// chain per chunk is 4 + 2 dependent steps per wave instead of 32 + 16 fp32 ones. P1 and
+// P2 of the slice's columns are formed from the prep's Aqk^T, qg^T (hi, lo) and do^T
+// fragments (hi then lo per contraction step, in one accumulator): P1 as the start of
+// the dv' accumulation, P2 after the v' barrier, where it overlaps the dv'^T reads.
 constexpr int BWD_L2_AHEAD = 4;   // chunks beyond the current one the reverse scan's L2 prefetch touches
 
 template <int K, int V>
@@ -556,48 +570,81 @@ struct DscanFragsB {
     static constexpr int NKS = K / 32, NJS = C / 32, NDT = K / 64;
     bf16x8 kg[2][NKS];        // hi, lo
     bf16x8 wt[NDT][NJS];
-    f32x4 p1;
-    f32x4 p2[NDT];
     f32x4 e[NDT];
 };
+template <int K, int V>
+struct DscanPB {
+    static constexpr int NJS = C / 32, NDT = K / 64;
+    bf16x8 aq[2][NJS];        // Aqk^T band `wave`: hi, lo
+    bf16x8 dt[NJS];           // do^T band of the slice
+    bf16x8 qt[NDT][2][NJS];   // qg^T bands wave + 4a: hi, lo
+};
 
-// The operands of chunk c in two groups: those of the dv' products (kg, P1) and those
-// of the dS update (w^T, P2, 2^G). The scan issues each group right after the products
-// that last read it, so the loads queue up behind work in flight instead of in one burst.
+// The operands of chunk c in two groups, two chunks ahead: those of the dv' products
+// (kg) and those of the dS update (w^T, 2^G); the scan issues each group right after the
+// products that last read it, so the loads queue up behind work in flight instead of in
+// one burst. The operands of P1 and P2 (Aqk^T, do^T, qg^T) are held one chunk ahead
+// only (their loads hit the lines the L2 prefetch touched), which keeps the scan within
+// its registers.
 template <int K, int V>
 __device__ __forceinline__ void load_dscan_b_kg(DscanFragsB<K, V>& F, const BwdParams& p, int hv, int c,
                                                 int wave, int lane, int v0) {
     typedef ScanOps<K, V> SO;
+    typedef ScanOpsB<K, V> SB;
     typedef FragTile<__bf16, C, K> FKG;
+    typedef FragTile<__bf16, C, C> FAT;
+    typedef FragTile<__bf16, V, C> FDT;
     typedef DscanFragsB<K, V> DF;
-    const int lr = lane & 15, lq = lane >> 4;
     const size_t ci = (size_t)hv * p.NCmax + c;
-    const float* ops = p.sops + ci * (size_t)SO::FLOATS;
-    const __bf16* kg = reinterpret_cast<const __bf16*>(ops + SO::KG);
+    const __bf16* ops = reinterpret_cast<const __bf16*>(p.sops + ci * (size_t)SO::FLOATS);
 #pragma unroll
     for (int kk = 0; kk < DF::NKS; ++kk) {
-        F.kg[0][kk] = *reinterpret_cast<const bf16x8*>(kg + FKG::frag(wave, kk, lane));
-        F.kg[1][kk] = *reinterpret_cast<const bf16x8*>(kg + C * K + FKG::frag(wave, kk, lane));
+        F.kg[0][kk] = *reinterpret_cast<const bf16x8*>(ops + SB::KG + FKG::frag(wave, kk, lane));
+        F.kg[1][kk] = *reinterpret_cast<const bf16x8*>(ops + SB::KG + C * K + FKG::frag(wave, kk, lane));
     }
-    F.p1 = *reinterpret_cast<const f32x4*>(ops + SO::P1 + AccTile::quad(v0 + lr, 16 * wave + 4 * lq));
+}
+template <int K, int V>
+__device__ __forceinline__ void load_dscan_b_p(DscanPB<K, V>& F, const BwdParams& p, int hv, int c,
+                                               int wave, int lane, int v0) {
+    typedef ScanOps<K, V> SO;
+    typedef ScanOpsB<K, V> SB;
+    typedef FragTile<__bf16, C, C> FAT;
+    typedef FragTile<__bf16, V, C> FDT;
+    typedef FragTile<__bf16, K, C> FQT;
+    typedef DscanPB<K, V> PF;
+    const size_t ci = (size_t)hv * p.NCmax + c;
+    const __bf16* ops = reinterpret_cast<const __bf16*>(p.sops + ci * (size_t)SO::FLOATS);
+#pragma unroll
+    for (int jj = 0; jj < PF::NJS; ++jj) {
+        F.dt[jj] = *reinterpret_cast<const bf16x8*>(ops + SB::DOT + FDT::frag(v0 / 16, jj, lane));
+        F.aq[0][jj] = *reinterpret_cast<const bf16x8*>(ops + SB::AQT + FAT::frag(wave, jj, lane));
+        F.aq[1][jj] = *reinterpret_cast<const bf16x8*>(ops + SB::AQT + C * C + FAT::frag(wave, jj, lane));
+    }
+#pragma unroll
+    for (int a = 0; a < PF::NDT; ++a)
+#pragma unroll
+        for (int jj = 0; jj < PF::NJS; ++jj) {
+            F.qt[a][0][jj] = *reinterpret_cast<const bf16x8*>(ops + SB::QGT + FQT::frag(wave + 4 * a, jj, lane));
+            F.qt[a][1][jj] = *reinterpret_cast<const bf16x8*>(ops + SB::QGT + K * C + FQT::frag(wave + 4 * a, jj, lane));
+        }
 }
 template <int K, int V>
 __device__ __forceinline__ void load_dscan_b_wt(DscanFragsB<K, V>& F, const BwdParams& p, int hv, int c,
                                                 int wave, int lane, int v0) {
     typedef ScanOps<K, V> SO;
+    typedef ScanOpsB<K, V> SB;
     typedef FragTile<__bf16, K, C> FWT;
     typedef DscanFragsB<K, V> DF;
-    const int lr = lane & 15, lq = lane >> 4;
+    const int lq = lane >> 4;
     const size_t ci = (size_t)hv * p.NCmax + c;
-    const float* ops = p.sops + ci * (size_t)SO::FLOATS;
-    const __bf16* wt = reinterpret_cast<const __bf16*>(ops + SO::WT);
+    const __bf16* ops = reinterpret_cast<const __bf16*>(p.sops + ci * (size_t)SO::FLOATS);
     const float* eg = reinterpret_cast<const float*>(p.rec + ci * p.rec_bytes + p.off_eg);
 #pragma unroll
     for (int a = 0; a < DF::NDT; ++a) {
 #pragma unroll
-        for (int jj = 0; jj < DF::NJS; ++jj)
-            F.wt[a][jj] = *reinterpret_cast<const bf16x8*>(wt + FWT::frag(wave + 4 * a, jj, lane));
-        F.p2[a] = *reinterpret_cast<const f32x4*>(ops + SO::P2 + acc_kv<K>(v0 + lr, 16 * (wave + 4 * a) + 4 * lq));
+        for (int jj = 0; jj < DF::NJS; ++jj) {
+            F.wt[a][jj] = *reinterpret_cast<const bf16x8*>(ops + SB::WT + FWT::frag(wave + 4 * a, jj, lane));
+        }
         F.e[a] = *reinterpret_cast<const f32x4*>(eg + 16 * (wave + 4 * a) + 4 * lq);
     }
 }
@@ -652,21 +699,22 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
     // re-reads chunk c0 (in bounds, never used)
     auto clampc = [&](int c) { return c >= c0 ? c : c0; };
     DF F0, F1;
+    DscanPB<K, V> PF;   // one chunk ahead (its loads hit the L2 lines the prefetch touched)
     if (c0 < c1) {
+        load_dscan_b_p<K, V>(PF, p, hv, c1 - 1, wave, lane, v0);
         load_dscan_b<K, V>(F0, p, hv, c1 - 1, wave, lane, v0);
         load_dscan_b<K, V>(F1, p, hv, clampc(c1 - 2), wave, lane, v0);
     }
     // L2 prefetch of the operands BWD_L2_AHEAD chunks further down the walk: the chain's
     // NVT slice blocks share one XCD (scan_item) and block vt touches one word per
-    // 128-byte line of its share of the bytes this kernel reads (kg hi + lo and w^T, then
-    // P1 and P2); a loaded word is folded into `sink` when its ring slot comes round
+    // 128-byte line of its share of the bytes this kernel reads (the whole bf16 operand
+    // slot); a loaded word is folded into `sink` when its ring slot comes round
     typedef ScanOps<K, V> SO;
-    constexpr int LINES_A = (2 * C * K * 2 + K * C * 2) / 128;        // kg hi + lo, w^T
-    constexpr int LINES = LINES_A + (C * V + K * V) * 4 / 128;        // + P1, P2
+    constexpr int LINES = ScanOpsB<K, V>::ELEMS * 2 / 128;
+    static_assert((LINES + NVT - 1) / NVT <= BT, "one line per lane");
     const int l0 = vt * LINES / NVT, nl = (vt + 1) * LINES / NVT - l0;
     const int li = 64 * wave + lane;
-    const int pl = l0 + li;
-    const size_t pbyte = pl < LINES_A ? (size_t)pl * 128 : (size_t)SO::P1 * 4 + (size_t)(pl - LINES_A) * 128;
+    const size_t pbyte = (size_t)(l0 + li) * 128;
     uint32_t sink = 0, pf0 = 0, pf1 = 0;
     auto prefetch = [&](uint32_t& pf, int c) {
         sink ^= pf;
@@ -685,8 +733,15 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
         for (int a = 0; a < NDT; ++a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) dhb[(size_t)(16 * (wave + 4 * a) + 4 * lq + r) * V + v0 + lr] = dS[a][r];
+        // P1 = Aqk^T do at this wave's rows and the slice's columns (Aqk^T as hi + lo; do
+        // is exact in bf16)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc, p2[NDT];
+#pragma unroll
+        for (int jj = 0; jj < DF::NJS; ++jj) {
+            acc = M::mma(PF.aq[0][jj], PF.dt[jj], acc);
+            acc = M::mma(PF.aq[1][jj], PF.dt[jj], acc);
+        }
         // dv' = P1 + kg dS (rows 16 wave + 4 lq + r, column lr of the slice)
-        f32x4 acc = F.p1, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < DF::NKS; ++kk) {
             const bf16x8 bh = *reinterpret_cast<const bf16x8*>(dSh + lr * LDK + 32 * kk + 8 * lq);
@@ -703,7 +758,18 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
         for (int r = 0; r < 4; ++r) dvb[(size_t)(16 * wave + 4 * lq + r) * V + v0 + lr] = acc[r];
         put4(dvh, dvl, lr * LDC + 16 * wave + 4 * lq, acc);
         __syncthreads();
-        // dS <- 2^G dS + P2 - w^T dv'
+        // P2 = qg^T do (qg^T as hi + lo), then the next chunk's P operands; dS <- 2^G dS +
+        // P2 - w^T dv'
+#pragma unroll
+        for (int a = 0; a < NDT; ++a) {
+            p2[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < DF::NJS; ++jj) {
+                p2[a] = M::mma(PF.qt[a][0][jj], PF.dt[jj], p2[a]);
+                p2[a] = M::mma(PF.qt[a][1][jj], PF.dt[jj], p2[a]);
+            }
+        }
+        load_dscan_b_p<K, V>(PF, p, hv, clampc(c - 1), wave, lane, v0);
 #pragma unroll
         for (int a = 0; a < NDT; ++a) {
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -713,7 +779,7 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
                 x = M::mma(F.wt[a][jj], *reinterpret_cast<const bf16x8*>(dvl + lr * LDC + 32 * jj + 8 * lq), x);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dS[a][r] = fmaf(F.e[a][r], dS[a][r], F.p2[a][r] - x[r]);
+            for (int r = 0; r < 4; ++r) dS[a][r] = fmaf(F.e[a][r], dS[a][r], p2[a][r] - x[r]);
             put4(dSh, dSl, lr * LDK + 16 * (wave + 4 * a) + 4 * lq, dS[a]);
         }
         load_dscan_b_wt<K, V>(F, p, hv, cn, wave, lane, v0);
@@ -739,15 +805,16 @@ __global__ __launch_bounds__(BT, 1) void bwd_scan_bf16_kernel(BwdParams p) {
     }
 }
 
-// The same prep for bf16 inputs on the bf16 matrix cores. The records carry Aqk and qg
-// as hi + lo bf16 pairs and do is a bf16 input, so P1 = Aqk_hi^T do + Aqk_lo^T do and
-// P2 likewise are exact products accumulated in fp32 (the fp32 prep's result up to
-// summation order). The contraction runs over the chunk's rows, so Aqk, qg and do are
+// The prep for bf16 inputs: the reverse scan's operands as bf16 fragments for
+// v_mfma_f32_16x16x32_bf16, no products. The records carry Aqk and qg as hi + lo bf16
+// pairs and do is a bf16 input, so the scan's P1 = Aqk_hi^T do + Aqk_lo^T do and P2
+// likewise are exact products accumulated in fp32 (the fp32 prep's result up to
+// summation order). Their contraction runs over the chunk's rows, so Aqk, qg and do are
 // staged transposed into bf16 LDS rows of 64 padded to 72 (144 bytes: the 16 rows of a
-// fragment read start in 16 distinct four-bank groups). The same LDS then stages w and
-// kg^T for the reverse scan's operands, here in bf16 fragment order for
-// v_mfma_f32_16x16x32_bf16: kg as hi + lo (rows s, contraction d), w^T (rows d,
-// contraction r; w is a single bf16 in the record, so this copy is exact).
+// fragment read start in 16 distinct four-bank groups) and copied out as Aqk^T, qg^T
+// (hi, lo) and do^T fragments. The same LDS then stages w and kg^T: kg as hi + lo (rows
+// s, contraction d), w^T (rows d, contraction r; w is a single bf16 in the record, so
+// this copy is exact).
 constexpr int PT_LD = 72;
 
 // A fragment-order bf16 record tile (R rows, KC contraction, its residual tile at
@@ -842,6 +909,7 @@ struct RowTLoad {
 template <int K, int V>
 __global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
     typedef ScanOps<K, V> SO;
+    typedef ScanOpsB<K, V> SB;
     typedef Mma<__bf16> M;
     constexpr int T_BYTES = (2 * C + 2 * K + V) * PT_LD * 2;     // first phase
     constexpr int F_BYTES = 2 * K * PT_LD * 2 + C * (K + 8) * 2;  // second phase
@@ -874,32 +942,28 @@ __global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
         ld_.store(pos.y, dT, tid);
     }
     __syncthreads();
-    auto frag = [&](const __bf16* t, int row, int ks) {
-        return *reinterpret_cast<const bf16x8*>(t + row * PT_LD + 32 * ks + 8 * lq);
+    // Aqk^T, qg^T (hi, lo) and do^T copied out in 16x16x32 fragment order (lane l of block
+    // (band b, step st) holds row 16b + l % 16, columns 32st + 8(l / 16) ..): the reverse
+    // scan's operands of P1 = Aqk^T do and P2 = qg^T do
+    __bf16* ob = reinterpret_cast<__bf16*>(ops);
+    auto copy_frags = [&](auto rows, const __bf16* t, __bf16* dst) {
+        constexpr int N = decltype(rows)::value * C / 8 / BT;
+        static_assert(N * BT * 8 == decltype(rows)::value * C, "whole runs per thread");
+        bf16x8 x[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int q = tid + BT * i, ln = q % 64, blk = q / 64;
+            x[i] = *reinterpret_cast<const bf16x8*>(t + (16 * (blk / (C / 32)) + (ln & 15)) * PT_LD +
+                                                    32 * (blk % (C / 32)) + 8 * (ln >> 4));
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) *reinterpret_cast<bf16x8*>(dst + 8 * (tid + BT * i)) = x[i];
     };
-    // P1[s][v] = sum_r Aqk[r][s] do[r][v]: wave w owns rows 16w ..
-    for (int nt = 0; nt < V / 16; ++nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < C / 32; ++ks) {
-            const bf16x8 b = frag(dT, 16 * nt + lr, ks);
-            acc = M::mma(frag(aTh, 16 * wave + lr, ks), b, acc);
-            acc = M::mma(frag(aTl, 16 * wave + lr, ks), b, acc);
-        }
-        *reinterpret_cast<f32x4*>(ops + SO::P1 + AccTile::quad(16 * nt + lr, 16 * wave + 4 * lq)) = acc;
-    }
-    // P2[d][v] = sum_r qg[r][d] do[r][v]: wave w owns bands w, w + 4, ..
-    for (int db = wave; db < K / 16; db += 4)
-        for (int nt = 0; nt < V / 16; ++nt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < C / 32; ++ks) {
-                const bf16x8 b = frag(dT, 16 * nt + lr, ks);
-                acc = M::mma(frag(qTh, 16 * db + lr, ks), b, acc);
-                acc = M::mma(frag(qTl, 16 * db + lr, ks), b, acc);
-            }
-            *reinterpret_cast<f32x4*>(ops + SO::P2 + acc_kv<K>(16 * nt + lr, 16 * db + 4 * lq)) = acc;
-        }
+    copy_frags(std::integral_constant<int, C>(), aTh, ob + SB::AQT);
+    copy_frags(std::integral_constant<int, C>(), aTl, ob + SB::AQT + C * C);
+    copy_frags(std::integral_constant<int, K>(), qTh, ob + SB::QGT);
+    copy_frags(std::integral_constant<int, K>(), qTl, ob + SB::QGT + K * C);
+    copy_frags(std::integral_constant<int, V>(), dT, ob + SB::DOT);
     __syncthreads();
     // kg^T (rows d, contraction s; hi, lo) and w (rows r, contraction d) as row-major bf16
     __bf16* kTh = reinterpret_cast<__bf16*>(smem);   // kg^T [d][s], hi
@@ -920,8 +984,8 @@ __global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
     // kg hi at KG, lo at KG + C K (bf16 elements); w^T at WT
     typedef FragTile<__bf16, C, K> FKGB;
     typedef FragTile<__bf16, K, C> FWTB;
-    __bf16* okg = reinterpret_cast<__bf16*>(ops + SO::KG);
-    __bf16* owt = reinterpret_cast<__bf16*>(ops + SO::WT);
+    __bf16* okg = ob + SB::KG;
+    __bf16* owt = ob + SB::WT;
     for (int q = tid; q < C * K / 8; q += BT) {
         const int l = q % 64, blk = q / 64;
         {
