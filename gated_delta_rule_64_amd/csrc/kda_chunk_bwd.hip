@@ -9,7 +9,8 @@
 // input gradients: the products with the state checkpoints (its wy_dqkg h/dh
 // consumers), the backward of the WY inverse, and the intra-chunk pair terms with a
 // reverse cumsum of the gate gradient folded in (its intra stage and dg cumsum). GVA
-// gradients of q and k are summed over each q/k head's value heads at the end.
+// gradients of q and k are summed over each q/k head's value heads (by the bf16 pair
+// kernel itself, else by a last kernel).
 //
 // Per chunk (rows r, s of the chunk, Gamma the chunk-local cumsum of g, G its last
 // row, S the state at the chunk start, dS the gradient at the chunk end, do the output
@@ -24,10 +25,11 @@
 //   dbeta = rowsum(Gu v) + rowsum(Gw kd) + rowsum(dL M),
 //   dT = dv' (beta v)^T + dw (beta kd)^T, dL = -(T^T dT T^T) strictly lower, dM = beta dL
 //   and the pair terms of Aqk and M with one one-sided 2^(Gamma_r - Gamma_s) <= 1 each.
-// All of it in fp32 arithmetic. With bf16 inputs the dense products of the prep, reverse
-// scan, state and WY stages run on the bf16 matrix cores, each fp32 operand carried as
-// a hi + lo bf16 pair (three products per step); the pair terms and the fp32-input
-// path use the fp32 matrix cores.
+// All of it in fp32 arithmetic. With bf16 inputs the dense products of the reverse scan
+// (P1 and P2 included), the state, WY and pair stages run on the bf16 matrix cores, each
+// fp32 operand carried as a hi + lo bf16 pair (three products per step; two where one
+// operand is exact in bf16), and the prep only lays their operands out; the fp32-input
+// path uses the fp32 matrix cores.
 #include <atomic>
 #include <type_traits>
 
