@@ -4,11 +4,14 @@
 Headline: the chunked forward on the long-context workload (B=1, T=8192, H=16 q/k heads,
 HV=32 value heads, K=V=128, bf16 q/k/v/beta, fp32 log2 gates clamped at -5, no initial
 state, no final state). A step is one call of kda_chunk_fwd (dense mode: the Stage 1+2
-kernel, then the Stage 3+4 scan) with its inputs resident in HBM. Before the timed steps
-the forward runs back to back for --preheat-s seconds (clocks at their working level),
-then --warmup untimed steps. Each of the --steps timed steps is preceded, outside its
-events, by a 512 MB write, so its 336 MB of inputs come from HBM and not the 256 MB
-MALL; `value` is tokens per second at the median step time, `ms_per_step` that median.
+kernel, then the Stage 3+4 scan) with its inputs resident in HBM. Each of the --steps
+timed steps is preceded, outside its events, by a 512 MB write, so its 336 MB of inputs
+come from HBM and not the 256 MB MALL; `value` is tokens per second at the median step
+time, `ms_per_step` that median. Before them the same pattern (write, step) runs for
+--preheat-s seconds, so the clocks have settled at the level that pattern holds (a short
+timed window right after other work read up to 10% slow), then --warmup untimed steps.
+Every other timed window (back-to-back reps of one call) first runs its own call for a
+quarter second (at most --preheat-s).
 
 Also reported on the same JSON line:
   * roofline     -- the forward (both kernels) against HBM peak on the method's own bytes
@@ -325,20 +328,29 @@ def main():
         torch.neg(src, out=dst)          # 1 GiB read + 1 GiB written by one plain kernel
         torch.cuda.synchronize()
         del src, dst
-    # pre-heat: the forward back to back for a fixed wall time, so the timed steps run at
-    # the clocks a busy GPU holds (a cold start ran both kernels ~17% slower)
+    # pre-heat: a timed window's own pattern for a fixed wall time before it, so its reps
+    # run at the clocks the GPU settles at under that pattern (a cold start ran both
+    # kernels ~17% slower, and 20 flushed steps right after back-to-back calls 5-10%)
     if not want("headline"):
         args.preheat_s = min(args.preheat_s, 0.2)
-    t_end = time.time() + max(0.0, args.preheat_s)
-    n_pre = 0
-    while True:
-        for _ in range(50):
-            call(None)
-        n_pre += 50
-        torch.cuda.synchronize()
-        if time.time() >= t_end:
-            break
+    leg_pre_s = min(0.25, max(0.0, args.preheat_s))
+
+    def preheat(fn, seconds, flushed=False):
+        t_end = time.time() + max(0.0, seconds)
+        n = 0
+        while True:
+            for _ in range(10):
+                if flushed:
+                    flush()
+                fn()
+            n += 10
+            torch.cuda.synchronize()
+            if time.time() >= t_end:
+                return n
+
+    n_pre = preheat(lambda: call(None), args.preheat_s, flushed=True)
     for _ in range(args.warmup):
+        flush()
         call(None)
     torch.cuda.synchronize()
     result = {"leg": args.only, "note": "a single leg for profiling its kernels; no headline figures in this run"}
@@ -350,6 +362,7 @@ def main():
         intra_ms = sum(seg_intra) / steps
         scan_ms = sum(seg_scan) / steps
         fwd_ms = intra_ms + scan_ms
+        preheat(lambda: call(None), leg_pre_s)
         b2b_ms = back_to_back(lambda: call(None), steps, hip, sptr)
 
         flops_exact = 141013.0 * B * T * HV
@@ -406,6 +419,7 @@ def main():
             "config": {"workload": "chunk_kda fwd B=1 T=8192 H=16 HV=32 K=V=128 bf16, h0=None, no final state",
                        "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
             "timing": {"per_step": "512 MB write before each step (outside its events); value at the median step",
+                       "preheat": "the same write + step pattern for preheat_s seconds, then the warm-up steps",
                        "preheat_s": args.preheat_s, "preheat_steps": n_pre},
             "steps_ms": st,
             "back_to_back": {"ms_per_step": b2b_ms, "tokens_per_s": tokens / (b2b_ms * 1e-3)},
@@ -429,7 +443,9 @@ def main():
         out2 = torch.empty_like(d2["v"])
         fs2 = torch.empty_like(d2["initial_state"])
         call2 = timed_call(d2, out2, ws2, ws2_bytes, w2.B, w2.T, w2.H, w2.HV, w2.K, w2.V, w2.B, final=fs2)
+        preheat(lambda: call2(None), leg_pre_s, flushed=True)
         for _ in range(args.warmup):
+            flush()
             call2(None)
         whole2, (i2, s2) = timed_flushed(call2, steps, hip, sptr, flush, nev=1)
         st2 = stats(whole2)
@@ -457,6 +473,7 @@ def main():
         def gcall():
             kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], g_raw, d["beta"], A_log, dt_bias, None,
                                     None, None, out=out, workspace=ws)
+        preheat(gcall, leg_pre_s)
         for _ in range(args.warmup):
             gcall()
         gated_ms = back_to_back(gcall, steps, hip, sptr)
@@ -468,6 +485,7 @@ def main():
                                  A_log=A_log, dt_bias=dt_bias, use_qk_l2norm_in_kernel=True,
                                  use_beta_sigmoid_in_kernel=True, allow_neg_eigval=True, out=out,
                                  workspace=ws)
+        preheat(fcall, leg_pre_s)
         for _ in range(args.warmup):
             fcall()
         fused_ms = back_to_back(fcall, steps, hip, sptr)
@@ -499,6 +517,7 @@ def main():
             if rc != 0:
                 raise RuntimeError(lib.kda_last_error().decode())
         bsteps = max(1, steps // 4)
+        preheat(bcall, leg_pre_s)
         for _ in range(2):
             bcall()
         bwd_ms = back_to_back(bcall, bsteps, hip, sptr)
@@ -526,9 +545,11 @@ def main():
                 kda.KDA_BF16, 0.0, 64, vp(tws.data_ptr()), bws_bytes, None, sptr)
             if rc != 0:
                 raise RuntimeError(lib.kda_last_error().decode())
+        preheat(tcall, leg_pre_s)
         for _ in range(2):
             tcall()
         train_fwd_ms = back_to_back(tcall, bsteps, hip, sptr)
+        preheat(scall, leg_pre_s)
         for _ in range(2):
             scall()
         saved_bwd_ms = back_to_back(scall, bsteps, hip, sptr)
@@ -614,6 +635,7 @@ def main():
             kda.kda_chunk_fwd(dv_["q"], dv_["k"], dv_["v"], dv_["g"], dv_["beta"], dv_["initial_state"],
                               dv_["cu_seqlens"], output_final_state=True, out=vout, final_state=vstate,
                               workspace=vws)
+        preheat(vcall, leg_pre_s)
         for _ in range(args.warmup):
             vcall()
         var_ms = back_to_back(vcall, steps, hip, sptr)
