@@ -594,8 +594,6 @@ __device__ __forceinline__ void load_dscan_b_kg(DscanFragsB<K, V>& F, const BwdP
     typedef ScanOps<K, V> SO;
     typedef ScanOpsB<K, V> SB;
     typedef FragTile<__bf16, C, K> FKG;
-    typedef FragTile<__bf16, C, C> FAT;
-    typedef FragTile<__bf16, V, C> FDT;
     typedef DscanFragsB<K, V> DF;
     const size_t ci = (size_t)hv * p.NCmax + c;
     const __bf16* ops = reinterpret_cast<const __bf16*>(p.sops + ci * (size_t)SO::FLOATS);
@@ -921,8 +919,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_prep_bf16_kernel(BwdParams p) {
     __bf16* qTh = aTl + C * PT_LD;                   // qg^T [d][r], hi
     __bf16* qTl = qTh + K * PT_LD;                   //               lo
     __bf16* dT = qTl + K * PT_LD;                    // do^T [v][r]
-    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x;
     int c, hv;
     int2 pos;
     if (!bwd_chunk(p, c, hv, pos)) return;
