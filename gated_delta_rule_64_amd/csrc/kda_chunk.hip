@@ -199,10 +199,10 @@ __device__ __forceinline__ float load_beta(const IntraParams& p, size_t r, int h
 // Thread mapping for the elementwise work: thread (cg, rg) owns columns 8cg .. 8cg+7 of
 // rows rg*RPT .. rg*RPT+RPT-1, so every global access is a 16- or 32-byte vector. The
 // Stage 2 products run on fp32 matrix cores (v_mfma_f32_16x16x4_f32) in two K-halves to
-// keep the LDS footprint under 80 KB (two blocks per CU). All record tiles are written
-// in the scan's fragment order.
+// keep the LDS footprint under 80 KB; its registers (one wave per SIMD) allow one block
+// per CU. All record tiles are written in the scan's fragment order.
 template <int K, int V, typename TIn, typename TB, bool CKPT>
-__global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
+__global__ __launch_bounds__(NTHREADS, 1) void intra_kernel(IntraParams p) {
     typedef TIn TW;                        // operand type of the record
     constexpr bool SPLIT = sizeof(TW) == 2;
     constexpr int CG = K / 8, RG = NTHREADS / CG, RPT = C / RG;
@@ -267,7 +267,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
     const TIn* q = reinterpret_cast<const TIn*>(p.q);
     const TIn* k = reinterpret_cast<const TIn*>(p.k);
     const TIn* v = reinterpret_cast<const TIn*>(p.v);
-    const TB* beta = reinterpret_cast<const TB*>(p.beta);
     char* rec = p.rec + ((size_t)hv * p.NCmax + c) * p.rec_bytes;
     TW* out_w = reinterpret_cast<TW*>(rec + p.off_w);
     TW* out_qg = reinterpret_cast<TW*>(rec + p.off_qg);
@@ -276,12 +275,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void intra_kernel(IntraParams p) {
     float* out_u = reinterpret_cast<float*>(rec + p.off_u);
     float* out_eg = reinterpret_cast<float*>(rec + p.off_eg);
 
-    // write x as hi (and lo = x - hi on the bf16 path) at element idx of two tiles
-    auto put_split = [&](TW* hi_t, TW* lo_t, int idx, float x) {
-        const TW hi = from_f32<TW>(x);
-        hi_t[idx] = hi;
-        if constexpr (SPLIT) lo_t[idx] = from_f32<TW>(x - to_f32(hi));
-    };
     // 8 consecutive fp32 values -> one bf16 fragment lane (hi and lo, 16 bytes each)
     auto put_split8 = [&](TW* hi_t, TW* lo_t, int idx, const float* x) {
         if constexpr (SPLIT) {
@@ -1373,7 +1366,6 @@ __device__ __forceinline__ void load_frags(ScanFrags<K, V, BV, TW>& F, const cha
     F.pos = chunk_pos(p.dense, p.NT, p.T, p.table, c);
     typedef ScanFrags<K, V, BV, TW> SF;
     typedef typename SF::frag frag;
-    constexpr int KS = SF::M::KS, KPL = SF::M::KPL;
     const TW* w = reinterpret_cast<const TW*>(rec + p.off_w);
     const TW* qg = reinterpret_cast<const TW*>(rec + p.off_qg);
     const TW* aqk = reinterpret_cast<const TW*>(rec + p.off_aqk);
