@@ -1755,9 +1755,8 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
     __syncthreads();
     // ---- dT (strictly lower) transposed and T as rows, split, into region B ----
     {
-        // T again (from cache), and M at this lane's dL elements: loaded here rather
-        // than held in registers through the products
-        const f32x4 tq = *reinterpret_cast<const f32x4*>(p.mt + ((size_t)p.NCmax * p.HV + ci) * (C * C) + tr * C + tc);
+        // M at this lane's dL elements: loaded here rather than held in registers through
+        // the products
 #pragma unroll
         for (int r = 0; r < 4; ++r) mR[r] = p.mt[ci * (size_t)(C * C) + (16 * tI + 4 * lq + r) * C + 16 * tJ + lr];
         bf16x4 hv4, lv4;
@@ -1771,11 +1770,12 @@ __global__ __launch_bounds__(WY_THREADS, 1) void bwd_wy_bf16_kernel(BwdParams p)
         const int s = 16 * tJ + lr;
         *reinterpret_cast<bf16x4*>(dTH + s * TP + 16 * tI + 4 * lq) = hv4;
         *reinterpret_cast<bf16x4*>(dTL + s * TP + 16 * tI + 4 * lq) = lv4;
+        // T as rows (hi, lo): T^T's split read transposed (the same bits as splitting T)
         bf16x4 th, tl;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            th[e] = (__bf16)tq[e];
-            tl[e] = (__bf16)(tq[e] - (float)th[e]);
+            th[e] = TtH[(tc + e) * TP + tr];
+            tl[e] = TtL[(tc + e) * TP + tr];
         }
         *reinterpret_cast<bf16x4*>(ThH + tr * TP + tc) = th;
         *reinterpret_cast<bf16x4*>(ThL + tr * TP + tc) = tl;
