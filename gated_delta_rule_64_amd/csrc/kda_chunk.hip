@@ -1950,13 +1950,27 @@ __global__ __launch_bounds__(SCAN8_THREADS, 1) void scan_bf16_kernel(ScanParams 
         // lane, so the register rings' loads of that record hit in L2. The loaded word is
         // folded into `sink` when the same ring slot comes round (after the loads that
         // follow it have been waited for), and sink is consumed by an empty asm statement.
-        const int lines = (int)(p.rec_bytes / 128);
+        // Without o (the backward's re-scan) only the lines of w, kg^T (hi, lo), u and 2^G
+        // are touched: qg and Aqk are never read there.
+        constexpr int LW = C * K * 2 / 128, LG = 2 * K * C * 2 / 128, LU = C * V * 4 / 128, LE = K * 4 / 128;
+        const int lines = CKPT == SCAN_CKPT ? LW + LG + LU + LE : (int)(p.rec_bytes / 128);
         const int l0 = vt * lines / NVT, nl = (vt + 1) * lines / NVT - l0;
         const int li = sw * 64 + lane;
+        size_t ck_byte = 0;
+        if constexpr (CKPT == SCAN_CKPT) {
+            const int L = l0 + li;
+            ck_byte = L < LW             ? p.off_w + (size_t)L * 128
+                      : L < LW + LG      ? p.off_kgT + (size_t)(L - LW) * 128
+                      : L < LW + LG + LU ? p.off_u + (size_t)(L - LW - LG) * 128
+                                         : p.off_eg + (size_t)(L - LW - LG - LU) * 128;
+        }
         uint32_t sink = 0, pf0 = 0, pf1 = 0, pf2 = 0;
         auto prefetch = [&](uint32_t& pf, int cn) {
             sink ^= pf;
-            if (li < nl) pf = *reinterpret_cast<const uint32_t*>(record(cn + SCAN_L2_AHEAD - STATE_PREFETCH) + (size_t)(l0 + li) * 128);
+            if (li < nl) {
+                const size_t off = CKPT == SCAN_CKPT ? ck_byte : (size_t)(l0 + li) * 128;
+                pf = *reinterpret_cast<const uint32_t*>(record(cn + SCAN_L2_AHEAD - STATE_PREFETCH) + off);
+            }
         };
         // one chunk; F is refilled with chunk cn as its registers die
         auto step = [&](StateFrags<K, BV, LO8>& F, int cn, uint32_t& pf) {
